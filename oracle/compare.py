@@ -1,0 +1,114 @@
+"""Per-element comparison metric for device results (test infrastructure).
+
+The bars: max relative error per element <= 8e-3 where the output is bf16
+(MATCH, and wide-internal with bf16 output), <= 1e-4 for wide-internal with
+float32 output.  A plain ``|y - r| / |r|`` is undefined at ``r = 0`` and
+meaningless where the gate or up dot product has cancelled far below its
+terms, so the denominator is floored:
+
+    err_i = |y_i - r_i| / max(|r_i|, tau_i, tau_0)
+    tau_i = 2^-4 * ( |silu(g_i)| * nu_u,i + |silu'(g_i) * u_i| * nu_g,i )
+    tau_0 = 2^-24 * RMS(r)
+
+``nu = sqrt(sum_k (x_k w_k)^2)`` is the cancellation-free scale of a dot
+product; ``tau_i`` is first-order error propagation of a gate/up error of
+1/16 of that scale.  Where no cancellation happened the floor does not bind and
+the test is plain relative error.
+
+In MATCH the gate and up are rounded to bf16 before the nonlinearity.  Where
+the exact value lies within ``eta * nu`` (eta = 2^-12) of a bf16 rounding
+midpoint, a correct float32 accumulation may round to either neighbour; both
+are admissible, and the candidate nearest the device value is used.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import bf16_rne, bf16_value, silu
+
+TOL = {0: 8e-3, 1: 1e-4, 2: 8e-3}
+ETA = 2.0 ** -12
+FLOOR = 2.0 ** -4
+TAU0 = 2.0 ** -24
+
+
+def _sigmoid(t):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-t))
+
+
+def silu_prime(t):
+    s = _sigmoid(t)
+    return s * (1.0 + t * (1.0 - s))
+
+
+def bf16_candidates(v, nu, eta=ETA):
+    """(primary, alternative) bf16 roundings of float64 ``v`` as float64.
+
+    primary = RNE(v).  alternative = the other bf16 neighbour of ``v`` when
+    ``v`` lies within ``eta * nu`` of the midpoint between the two; otherwise
+    it equals primary."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), -1.0, 1.0)
+    pb = bf16_rne(a).astype(np.int64)
+    pv = bf16_value(pb.astype(np.uint16))
+    above = pv > a
+    ob = np.where(above, np.maximum(pb - 1, 0), pb + 1)
+    ov = bf16_value(ob.astype(np.uint16))
+    exact = pv == a
+    mid = 0.5 * (pv + ov)
+    admissible = (~exact) & (np.abs(a - mid) <= eta * np.asarray(nu, dtype=np.float64))
+    alt = np.where(admissible, ov, pv)
+    return sign * pv, sign * alt
+
+
+def reference_values(o, mode):
+    """Primary reference r and its gate/up (rounded in MATCH)."""
+    g, u = o["g"], o["u"]
+    if mode == 0:
+        g = bf16_value(bf16_rne(g))
+        u = bf16_value(bf16_rne(u))
+    return silu(g) * u, g, u
+
+
+def evaluate(y, o, mode, eta=ETA):
+    """Compare device output ``y`` (any float dtype, same element order as the
+    oracle dict ``o``) against the oracle.  Returns a dict of statistics with
+    ``ok`` set when the bar of ``mode`` holds."""
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    g, u = o["g"].reshape(-1), o["u"].reshape(-1)
+    nug, nuu = o["nu_g"].reshape(-1), o["nu_u"].reshape(-1)
+    r0, gp, up = reference_values({"g": g, "u": u}, mode)
+    if mode == 0:
+        g_a, g_b = bf16_candidates(g, nug, eta)
+        u_a, u_b = bf16_candidates(u, nuu, eta)
+        cands = [silu(gc) * uc for gc in (g_a, g_b) for uc in (u_a, u_b)]
+        dist = np.stack([np.abs(y - c) for c in cands])
+        pick = np.argmin(dist, axis=0)
+        r = np.choose(pick, cands)
+    else:
+        r = r0
+    tau = FLOOR * (np.abs(silu(gp)) * nuu + np.abs(silu_prime(gp) * up) * nug)
+    rms = float(np.sqrt(np.mean(r0 * r0))) if r0.size else 0.0
+    tau0 = TAU0 * rms
+    denom = np.maximum(np.maximum(np.abs(r), tau), tau0)
+    diff = np.abs(y - r)
+    finite = np.isfinite(y)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(denom > 0, diff / np.where(denom > 0, denom, 1.0),
+                       np.where(diff == 0, 0.0, np.inf))
+    err = np.where(finite, err, np.inf)
+    n = y.size
+    worst = int(np.argmax(err)) if n else -1
+    stats = {
+        "n": n,
+        "max_err": float(err[worst]) if n else 0.0,
+        "worst_index": worst,
+        "floor_fraction": float(np.mean(np.maximum(tau, tau0) > np.abs(r))) if n else 0.0,
+        "max_abs_over_rms": float(np.max(diff) / rms) if (n and rms > 0) else 0.0,
+        "nonfinite": int(np.sum(~finite)),
+        "tol": TOL[mode],
+    }
+    stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= TOL[mode]))
+    return stats
