@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused quantized SwiGLU expansion on one MI355X.
+
+Headline workload (one "step"): the decode configuration -- M=1, H=2048,
+I=5632, 4-bit gs64 gate and up -- run as 1000 calls, each with a fresh x and
+one of 40 distinct weight sets in rotation (about 520 MB, more than the
+256 MB last-level cache, so every call streams its weights from HBM).
+``value`` is weight GB/s over the timed steps.  The 1000 calls of a step are
+recorded once into a HIP graph and replayed.
+
+Also reported on the same JSON line: the roofline fraction of the decode
+kernel, the CPU oracle on a bounded sample (the baseline), and the
+matrix-matrix path on the three prefill configurations (TFLOP/s and fraction
+of the bf16/f16 dense MFMA peak).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|c2|c3|c4]
+                    [--no-prefill] [--no-cpu] [--eager]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused quant-SwiGLU TFLOP/s (prefill) + weight GB/s (M=1 decode), % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/f16 MFMA
+ROTATING_SETS = 40
+CALLS = 1000
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(c):
+    wg = c.I * c.H * c.bits_g // 8 + 2 * 2 * c.I * (c.H // c.gs_g)
+    wu = c.I * c.H * c.bits_u // 8 + 2 * 2 * c.I * (c.H // c.gs_u)
+    return wg + wu
+
+
+def algorithmic_bytes(c, out_bytes=2):
+    return weight_bytes(c) + c.M * c.H * 2 + c.M * c.I * out_bytes
+
+
+def rotating_weight_sets(c, base_dev, n_sets, seed):
+    """Set 0 is the seeded problem; the others are drawn on the GPU from the
+    same distributions (uniform codes, scales U[0.005,0.02] in bf16, biases
+    -8*s*U[0.9,1.1] in bf16), seeded."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    sets = [base_dev[1:]]
+    ng = c.H // c.gs_g
+    for _ in range(n_sets - 1):
+        one = []
+        for bits in (c.bits_g, c.bits_u):
+            words = torch.randint(-2**31, 2**31 - 1, (c.I, c.H * bits // 32), generator=gen, device="cuda",
+                                  dtype=torch.int64).to(torch.int32)
+            s = (torch.rand((c.I, ng), generator=gen, device="cuda") * (c.s_hi - c.s_lo) + c.s_lo)
+            s = s.to(torch.bfloat16)
+            f = torch.rand((c.I, ng), generator=gen, device="cuda") * 0.2 + 0.9
+            b = (-8.0 * s.float() * f).to(torch.bfloat16)
+            one += [words, s, b]
+        sets.append(tuple(one))
+    return sets
+
+
+def bench_decode(args):
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import CONFIGS, make_problem
+
+    c = CONFIGS[1]
+    p = make_problem(1)
+    dev = swq.to_device(p)
+    sets = rotating_weight_sets(c, dev, ROTATING_SETS, seed=101)
+    import numpy as np
+    xs = torch.from_numpy(np.ascontiguousarray(p.xs).view(np.int16)).cuda().view(torch.bfloat16)  # [1000, H]
+    out = torch.empty((CALLS, c.I), dtype=torch.bfloat16, device="cuda")
+    L = swq.lib()
+    H, I = c.H, c.I
+    xrow = H * 2
+    orow = I * 2
+    ptr_sets = [tuple(t.data_ptr() for t in s) for s in sets]
+    x0, o0 = xs.data_ptr(), out.data_ptr()
+    assert swq.swiglu_q_get_m_threshold() > 1, "decode must take the matrix-vector path"
+
+    def step(stream_handle):
+        for i in range(CALLS):
+            wg, sg, bg, wu, su, bu = ptr_sets[i % ROTATING_SETS]
+            rc = L.swiglu_q_forward(x0 + i * xrow, wg, sg, bg, wu, su, bu, 1, H, I, c.bits_g, c.gs_g,
+                                    c.bits_u, c.gs_u, 0, o0 + i * orow, stream_handle)
+            if rc != 0:
+                raise RuntimeError(f"swiglu_q_forward failed: {swq.swiglu_q_strerror(rc)}")
+
+    stream = torch.cuda.Stream()
+    graph = None
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)               # eager warm-up (also first-use setup)
+    torch.cuda.synchronize()
+    if not args.eager:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step(torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+        except Exception as e:                 # noqa: BLE001
+            log(f"graph capture failed ({e}); timing eager launches")
+            graph = None
+
+    def run_one():
+        if graph is not None:
+            graph.replay()
+        else:
+            with torch.cuda.stream(stream):
+                step(stream.cuda_stream)
+
+    before = swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV)
+    for _ in range(args.warmup):
+        run_one()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            run_one()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    launches = args.steps * CALLS
+    if graph is None:
+        assert swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV) - before == (args.warmup + args.steps) * CALLS
+    wb = weight_bytes(c)
+    value = wb * CALLS / (ms_step * 1e-3) / 1e9
+    avg_launch_us = ms * 1e3 / launches
+    achieved = algorithmic_bytes(c) / (avg_launch_us * 1e-6) / 1e9
+    res = {
+        "value": round(value, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 4),
+        "dtype": "f16",
+        "config": {"workload": "decode GEMV M=1 H=2048 I=5632, 4-bit gs64 gate and up, "
+                               "1000 calls per step with fresh x, 40 rotating weight sets",
+                   "M": 1, "H": H, "I": I, "bits_g": c.bits_g, "gs_g": c.gs_g, "bits_u": c.bits_u,
+                   "gs_u": c.gs_u, "calls_per_step": CALLS, "weight_sets": ROTATING_SETS,
+                   "precision_mode": "MATCH", "launch": "hip graph" if graph is not None else "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_launch_us, 3),
+                     "bytes_per_launch": algorithmic_bytes(c)},
+        "wall_s": round(wall, 3),
+    }
+    return res
+
+
+def bench_prefill_one(cfg, steps, warmup, mode=0):
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import CONFIGS, make_problem
+
+    c = CONFIGS[cfg]
+    p = make_problem(cfg)
+    dev = swq.to_device(p)
+    del p
+    out = torch.empty((c.M, c.I), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            swq.forward(*dev, c.bits_g, c.gs_g, c.bits_u, c.gs_u, mode=mode, out=out, stream=stream)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            swq.forward(*dev, c.bits_g, c.gs_g, c.bits_u, c.gs_u, mode=mode, out=out, stream=stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    flops = 4.0 * c.M * c.H * c.I
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"config": c.describe, "ms_per_call": round(ms, 4), "tflops": round(tflops, 2),
+            "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
+
+
+def cpu_baseline_decode(max_seconds=20.0):
+    """The oracle as it stands, on a bounded sample of the decode workload:
+    whole calls (all 5632 columns) on fresh x rows, until about max_seconds."""
+    import oracle
+    from synth import CONFIGS, make_problem
+
+    c = CONFIGS[1]
+    p = make_problem(1)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        p.x = p.xs[calls:calls + 1]
+        oracle.swiglu_pairs(p, 0, nthreads=cores, want=("h",))
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= max_seconds or calls >= 200:
+            break
+    gbs = weight_bytes(c) * calls / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{calls} decode calls (M=1, H=2048, I=5632, all columns, MATCH) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the fused SwiGLU path has no multi-GPU component in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import quantized_swiglu_forward_amd as swq
+    swq.lib()
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    if args.workload == "decode":
+        log("decode: timing ...")
+        line.update(bench_decode(args))
+    else:
+        cfg = int(args.workload[1])
+        from synth import CONFIGS
+        r = bench_prefill_one(cfg, args.steps, args.warmup)
+        c = CONFIGS[cfg]
+        line.update({"value": r["tflops"], "unit": "TFLOP/s", "ms_per_step": r["ms_per_call"], "dtype": "f16",
+                     "config": {"workload": c.describe, "M": c.M, "H": c.H, "I": c.I,
+                                "precision_mode": "MATCH"},
+                     "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None}})
+    if not args.no_prefill:
+        pre = {}
+        for cfg, mode in ((2, 0), (2, 1), (3, 0), (4, 0)):
+            log(f"prefill c{cfg} mode {mode}: timing ...")
+            pre[f"c{cfg}_{['match', 'f32'][mode]}"] = bench_prefill_one(cfg, steps=10, warmup=3, mode=mode)
+            torch.cuda.empty_cache()
+        line["prefill"] = pre
+    if not args.no_cpu:
+        log("cpu baseline: oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_decode()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

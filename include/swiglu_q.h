@@ -1,0 +1,148 @@
+/*
+ * swiglu_q — fused quantized SwiGLU expansion for AMD Instinct MI355X (gfx950).
+ *
+ *   hidden[M, I] = silu(x · Wgᵀ) ⊙ (x · Wuᵀ),   silu(t) = t · σ(t),  σ(t) = 1 / (1 + e^(−t))
+ *
+ * Wg and Wu are affine group-quantized: each weight is stored as an unsigned
+ * integer code q of `bits` bits, and every group of `gs` consecutive codes
+ * along K (the hidden dimension H) has one bf16 scale s and one bf16 bias b,
+ * so that w = s·q + b.  The down projection is not part of this call.
+ *
+ * Sources (pages of the "mlx-bun" package diffs):
+ *  - the operation, one dispatch computing both projections from one read of
+ *    x, and the down projection left as a separate call:
+ *    "mlx-bun 0.0.7 -> 0.0.9" (page 42), fused-swiglu-kernel.ts, header comment;
+ *  - the host entry (x, then gate weight/scales/biases, then up
+ *    weight/scales/biases, then the two quantization specs, gate and up
+ *    specs independent), its shapes and "caller owns the result":
+ *    same file, host entry and its docstring;
+ *  - the two precision variants: same file, precision-variants comment;
+ *  - the support predicate (bf16 activations, affine biases present, group
+ *    size a multiple of 32, H a multiple of 32): same file, support predicate;
+ *  - the M threshold below which the caller keeps the matrix-vector path:
+ *    same file, M-threshold function and the "where the win is" comment.
+ *
+ * Memory layout (all row-major, contiguous, no strides):
+ *   x        bf16    [M, H]
+ *   Wg, Wu   uint32  [I, H·bits/32]   codes along K, 32/bits per word, code j of
+ *                                     a word in bits [bits·j, bits·j + bits)
+ *                                     (least significant first)
+ *   sg,bg,su,bu bf16 [I, H/gs]        scale and bias of each group
+ *   out      [M, I]  bf16 for SWQ_MATCH and SWQ_F32_BF16OUT, float32 for SWQ_F32
+ *
+ * Ownership and synchronisation: every pointer passed to the forward calls
+ * is a DEVICE pointer owned by the caller; the library never frees or keeps
+ * them.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ * and the call returns without synchronising.  The matrix-matrix path needs
+ * a device workspace: the library keeps one per (device, stream), allocated
+ * on first use and grown (never shrunk) when a call needs more; growth
+ * synchronises that stream once.  swiglu_q_release_workspace() frees them.
+ *
+ * Exactness: the weights are dequantized exactly (no rounding of s·q + b);
+ * gate and up are float32 dot products.  This holds when every scale and
+ * bias is zero or has magnitude in [2^-17, 2^12) (the range in which a bf16
+ * value times a code offset of at most 2^(bits-1) stays exactly
+ * representable in binary16); outside that range the dequantized weight is
+ * rounded to binary16.
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * HIP call and returns a status; nothing is launched on error.
+ */
+#ifndef SWIGLU_Q_H
+#define SWIGLU_Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SWQ_OK               0
+#define SWQ_ERR_NULL         1  /* a required pointer is NULL                       */
+#define SWQ_ERR_SHAPE        2  /* M < 0, H <= 0, I <= 0, H % gs != 0, H % 32 != 0  */
+#define SWQ_ERR_UNSUPPORTED  3  /* bits not in {4, 8}, gs not in {32, 64, 128},
+                                   unknown precision mode or path                   */
+#define SWQ_ERR_ALIGN        4  /* a pointer is not 16-byte aligned                 */
+#define SWQ_ERR_HIP          5  /* a HIP call or kernel launch failed               */
+#define SWQ_ERR_WORKSPACE    6  /* the workspace could not be allocated             */
+
+/* Precision modes (the pages' two variants; the wide one with two output types). */
+#define SWQ_MATCH        0  /* gate and up rounded to bf16 (RNE) before silu·up;
+                               product computed in float32, rounded once to bf16   */
+#define SWQ_F32          1  /* gate, up, silu and product in float32; float32 out  */
+#define SWQ_F32_BF16OUT  2  /* as SWQ_F32, rounded once to bf16 at the store       */
+
+/* Kernel paths chosen by the M-threshold dispatcher. */
+#define SWQ_PATH_GEMV    0  /* M < threshold: wavefront-reduction matrix-vector    */
+#define SWQ_PATH_MFMA    1  /* M >= threshold: dequantizing bf16/f16 MFMA GEMM      */
+#define SWQ_PATH_AUTO   -1
+
+/*
+ * Fused forward: out = silu(x·Wgᵀ) ⊙ (x·Wuᵀ) in the given precision mode.
+ *   x            bf16 [M, H] device pointer
+ *   Wg, sg, bg   gate codes [I, H·bits_g/32], scales and biases [I, H/gs_g]
+ *   Wu, su, bu   up codes [I, H·bits_u/32], scales and biases [I, H/gs_u]
+ *   M, H, I      rows of x, hidden size, intermediate size
+ *   bits_*, gs_* quantization spec of each matrix: bits in {4, 8},
+ *                gs in {32, 64, 128}, H a multiple of gs and of 32
+ *   precision_mode  SWQ_MATCH, SWQ_F32 or SWQ_F32_BF16OUT
+ *   out          [M, I] device pointer, bf16 or float32 by mode
+ *   stream       hipStream_t (NULL = null stream)
+ * M == 0 returns SWQ_OK with nothing launched.  All pointers 16-byte aligned.
+ */
+int swiglu_q_forward(const void *x,
+                     const uint32_t *Wg, const void *sg, const void *bg,
+                     const uint32_t *Wu, const void *su, const void *bu,
+                     int64_t M, int64_t H, int64_t I,
+                     int bits_g, int gs_g, int bits_u, int gs_u,
+                     int precision_mode, void *out, void *stream);
+
+/* 1 if the combination is supported by swiglu_q_forward, else 0 (mirrors the
+ * pages' support predicate, restricted to what this library implements). */
+int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
+                       int precision_mode);
+
+/* M threshold T of the dispatcher: M < T takes SWQ_PATH_GEMV, M >= T takes
+ * SWQ_PATH_MFMA.  The default comes from the environment variable
+ * SWIGLU_Q_MMIN when set to a positive integer, else the built-in default.
+ * T <= 1 sends every M >= 1 to the MFMA path. */
+void swiglu_q_set_m_threshold(int T);
+int swiglu_q_get_m_threshold(void);
+
+/* Number of forward (and debug) calls that launched each path since load
+ * or the last reset.  path: SWQ_PATH_GEMV or SWQ_PATH_MFMA. */
+uint64_t swiglu_q_call_count(int path);
+void swiglu_q_reset_counts(void);
+
+/* Human-readable text of a status code (static storage). */
+const char *swiglu_q_strerror(int status);
+
+/*
+ * Test hook: the pre-epilogue gate and up projections in float32,
+ * gate_out[M, I] and up_out[M, I] (device pointers, caller-owned), computed
+ * by the kernel of `path` (SWQ_PATH_AUTO = what the dispatcher would pick).
+ * Same validation and status codes as swiglu_q_forward.
+ */
+int swiglu_q_debug_gemm(const void *x,
+                        const uint32_t *Wg, const void *sg, const void *bg,
+                        const uint32_t *Wu, const void *su, const void *bu,
+                        int64_t M, int64_t H, int64_t I,
+                        int bits_g, int gs_g, int bits_u, int gs_u,
+                        int path, float *gate_out, float *up_out, void *stream);
+
+/* Bytes of workspace the MFMA path uses for this shape (0 when M == 0). */
+int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int bits_g, int gs_g,
+                                 int bits_u, int gs_u);
+
+/* Free every cached workspace (synchronises the device first). */
+int swiglu_q_release_workspace(void);
+
+/* Library version string. */
+const char *swiglu_q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_Q_H */

@@ -1,0 +1,192 @@
+"""Fused quantized SwiGLU expansion for AMD Instinct MI355X (gfx950).
+
+``hidden = silu(x Wg^T) * (x Wu^T)`` with affine group-quantized Wg/Wu, computed
+by the hand-written HIP kernels of ``libswiglu_q.so``.  This module only
+marshals arguments into the library's C ABI (``include/swiglu_q.h``): every
+step of the computation runs in the HIP kernels, and nothing here falls back
+to another implementation.  PyTorch supplies device memory and streams.
+
+Functions with the C names take raw device pointers (ints) or tensors and
+return the integer status; ``forward`` / ``debug_gemm_tensors`` are tensor
+conveniences that allocate outputs with torch and raise ``SwigluQError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libswiglu_q.so")
+
+SWQ_OK, SWQ_ERR_NULL, SWQ_ERR_SHAPE, SWQ_ERR_UNSUPPORTED, SWQ_ERR_ALIGN, SWQ_ERR_HIP, SWQ_ERR_WORKSPACE = range(7)
+SWQ_MATCH, SWQ_F32, SWQ_F32_BF16OUT = 0, 1, 2
+SWQ_PATH_GEMV, SWQ_PATH_MFMA, SWQ_PATH_AUTO = 0, 1, -1
+
+_lib = None
+
+
+class SwigluQError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({strerror(status)})" if what else
+                         f"status {status} ({strerror(status)})")
+
+
+def lib():
+    """Load ``libswiglu_q.so``; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_swiglu_forward_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
+    L.swiglu_q_forward.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
+    L.swiglu_q_forward.restype = i32
+    L.swiglu_q_debug_gemm.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.swiglu_q_debug_gemm.restype = i32
+    L.swiglu_q_supported.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.swiglu_q_supported.restype = i32
+    L.swiglu_q_set_m_threshold.argtypes = [i32]
+    L.swiglu_q_set_m_threshold.restype = None
+    L.swiglu_q_get_m_threshold.argtypes = []
+    L.swiglu_q_get_m_threshold.restype = i32
+    L.swiglu_q_call_count.argtypes = [i32]
+    L.swiglu_q_call_count.restype = u64
+    L.swiglu_q_reset_counts.argtypes = []
+    L.swiglu_q_reset_counts.restype = None
+    L.swiglu_q_strerror.argtypes = [i32]
+    L.swiglu_q_strerror.restype = ctypes.c_char_p
+    L.swiglu_q_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    L.swiglu_q_workspace_bytes.restype = i64
+    L.swiglu_q_release_workspace.argtypes = []
+    L.swiglu_q_release_workspace.restype = i32
+    L.swiglu_q_version.argtypes = []
+    L.swiglu_q_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- the C entry points, same names ---------------------------------------
+
+def swiglu_q_forward(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u,
+                     precision_mode, out, stream=None) -> int:
+    return lib().swiglu_q_forward(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
+                                  M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
+                                  _stream(stream))
+
+
+def swiglu_q_debug_gemm(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, path,
+                        gate_out, up_out, stream=None) -> int:
+    return lib().swiglu_q_debug_gemm(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
+                                     M, H, I, bits_g, gs_g, bits_u, gs_u, path, _ptr(gate_out),
+                                     _ptr(up_out), _stream(stream))
+
+
+def swiglu_q_supported(H, bits_g, gs_g, bits_u, gs_u, precision_mode) -> int:
+    return lib().swiglu_q_supported(H, bits_g, gs_g, bits_u, gs_u, precision_mode)
+
+
+def swiglu_q_set_m_threshold(T: int) -> None:
+    lib().swiglu_q_set_m_threshold(T)
+
+
+def swiglu_q_get_m_threshold() -> int:
+    return lib().swiglu_q_get_m_threshold()
+
+
+def swiglu_q_call_count(path: int) -> int:
+    return lib().swiglu_q_call_count(path)
+
+
+def swiglu_q_reset_counts() -> None:
+    lib().swiglu_q_reset_counts()
+
+
+def swiglu_q_strerror(status: int) -> str:
+    return lib().swiglu_q_strerror(status).decode()
+
+
+def swiglu_q_workspace_bytes(M, H, bits_g, gs_g, bits_u, gs_u) -> int:
+    return lib().swiglu_q_workspace_bytes(M, H, bits_g, gs_g, bits_u, gs_u)
+
+
+def swiglu_q_release_workspace() -> int:
+    return lib().swiglu_q_release_workspace()
+
+
+def swiglu_q_version() -> str:
+    return lib().swiglu_q_version().decode()
+
+
+strerror = swiglu_q_strerror
+
+
+# ---- tensor conveniences ----------------------------------------------------
+
+def forward(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_u=None,
+            mode=SWQ_MATCH, out=None, stream=None):
+    """``hidden`` for device tensors: x [M, H] (bf16 or int16/uint16 bit
+    patterns), packed codes int32/uint32 [I, H*bits/32], scales/biases bf16
+    [I, H/gs].  Returns ``out`` ([M, I], bf16 or float32 by mode)."""
+    import torch
+    bits_u = bits_g if bits_u is None else bits_u
+    gs_u = gs_g if gs_u is None else gs_u
+    M, H = int(x.shape[0]), int(x.shape[1])
+    I = int(wg.shape[0])
+    if out is None:
+        dt = torch.float32 if mode == SWQ_F32 else torch.bfloat16
+        out = torch.empty((M, I), dtype=dt, device=x.device)
+    rc = swiglu_q_forward(x, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
+    if rc != SWQ_OK:
+        raise SwigluQError(rc, "swiglu_q_forward")
+    return out
+
+
+def debug_gemm_tensors(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_u=None,
+                       path=SWQ_PATH_AUTO, stream=None):
+    """Pre-epilogue float32 (gate, up) from the kernel of ``path``."""
+    import torch
+    bits_u = bits_g if bits_u is None else bits_u
+    gs_u = gs_g if gs_u is None else gs_u
+    M, H = int(x.shape[0]), int(x.shape[1])
+    I = int(wg.shape[0])
+    g = torch.empty((M, I), dtype=torch.float32, device=x.device)
+    u = torch.empty((M, I), dtype=torch.float32, device=x.device)
+    rc = swiglu_q_debug_gemm(x, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, path, g, u, stream)
+    if rc != SWQ_OK:
+        raise SwigluQError(rc, "swiglu_q_debug_gemm")
+    return g, u
+
+
+def to_device(prob, device="cuda"):
+    """Copy a host problem (numpy bit patterns) to device tensors; returns the
+    tuple (x, wg, sg, bg, wu, su, bu)."""
+    import numpy as np
+    import torch
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    def t32(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device)
+
+    return (t16(prob.x), t32(prob.wg), t16(prob.sg), t16(prob.bg),
+            t32(prob.wu), t16(prob.su), t16(prob.bu))

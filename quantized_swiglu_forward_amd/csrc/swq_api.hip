@@ -1,0 +1,281 @@
+// C-ABI boundary of the fused quantized SwiGLU library (declared in
+// include/swiglu_q.h): argument validation, the M-threshold dispatcher,
+// per-path call counters, and the per-(device, stream) workspace of the
+// matrix-matrix path.
+//
+// The dispatcher mirrors the pages' M threshold ("mlx-bun 0.0.7 -> 0.0.9"
+// diff, page 42, fused-swiglu-kernel.ts: below a small row count the
+// projections are matrix-vector products and a different path runs; the
+// threshold defaults to 2 there and can be set from the environment) and the
+// support predicate of the same file (bf16 activations, affine biases,
+// group size a multiple of 32, H a multiple of 32).
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/swiglu_q.h"
+#include "swq_kernels.h"
+
+using namespace swq;
+
+namespace {
+
+constexpr int kDefaultThreshold = 2;
+
+std::atomic<int> g_threshold{-1};
+std::atomic<uint64_t> g_calls[2];
+std::mutex g_ws_mutex;
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+int threshold_now() {
+  int t = g_threshold.load(std::memory_order_relaxed);
+  if (t >= 0) return t;
+  t = kDefaultThreshold;
+  if (const char* s = getenv("SWIGLU_Q_MMIN")) {
+    char* end = nullptr;
+    long v = strtol(s, &end, 10);
+    if (end != s && v > 0 && v < (1L << 30)) t = (int)v;
+  }
+  int expected = -1;
+  g_threshold.compare_exchange_strong(expected, t);
+  return g_threshold.load();
+}
+
+bool logging() {
+  static const bool on = [] {
+    const char* s = getenv("SWIGLU_Q_LOG");
+    return s && s[0] == '1';
+  }();
+  return on;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool spec_ok(int bits, int gs) {
+  return (bits == 4 || bits == 8) && (gs == 32 || gs == 64 || gs == 128);
+}
+
+// Validation shared by every entry point; nothing touches HIP here.
+int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
+             const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
+             int bits_u, int gs_u) {
+  if (!x || !Wg || !sg || !bg || !Wu || !su || !bu) return SWQ_ERR_NULL;
+  if (!spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return SWQ_ERR_UNSUPPORTED;
+  if (M < 0 || H <= 0 || I <= 0) return SWQ_ERR_SHAPE;
+  if (H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0) return SWQ_ERR_SHAPE;
+  // kernels index with 32-bit row/column counters
+  if (M > (1LL << 30) || H > (1LL << 24) || I > (1LL << 30)) return SWQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16)) return SWQ_ERR_ALIGN;
+  if (!aligned(sg, 2) || !aligned(bg, 2) || !aligned(su, 2) || !aligned(bu, 2)) return SWQ_ERR_ALIGN;
+  return SWQ_OK;
+}
+
+bool gemv_fits(int64_t M, int64_t H) {
+  return M >= 1 && M <= kGemvMaxM && gemv_lds_bytes(M, H) <= kGemvLdsBytes;
+}
+
+int choose_mfma_config(int64_t M, int64_t I) {
+  if (const char* s = getenv("SWIGLU_Q_MFMA_CFG")) {
+    int v = atoi(s);
+    if (v >= 0 && v < kMfmaConfigs) return v;
+  }
+  const int64_t tiles_big = ((M + kMfmaBM[1] - 1) / kMfmaBM[1]) * ((I + kMfmaBN[1] - 1) / kMfmaBN[1]);
+  return tiles_big >= 512 ? 1 : 0;
+}
+
+int64_t ws_bytes(int64_t M, int64_t H, int gs_g, int gs_u) {
+  const int64_t ldx = H + kext_columns(H, gs_g) + kext_columns(H, gs_u);
+  const int64_t xa = (M * ldx * 2 + 255) / 256 * 256;
+  const int64_t ex = (M * 4 + 255) / 256 * 256;
+  return xa + ex;
+}
+
+int get_workspace(hipStream_t stream, size_t need, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SWQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // the old buffer may still be read by work queued on this stream
+      if (hipStreamSynchronize(stream) != hipSuccess) return SWQ_ERR_HIP;
+      if (hipFree(w.ptr) != hipSuccess) return SWQ_ERR_HIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t grain = 2u << 20;
+    const size_t bytes = (need + grain - 1) / grain * grain;
+    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return SWQ_ERR_WORKSPACE;
+    }
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return SWQ_OK;
+}
+
+int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
+        const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
+        int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u, int path,
+        void* stream_v) {
+  hipStream_t stream = (hipStream_t)stream_v;
+  if (M == 0) return SWQ_OK;
+  if (path == SWQ_PATH_AUTO) {
+    path = (M < threshold_now() && gemv_fits(M, H)) ? SWQ_PATH_GEMV : SWQ_PATH_MFMA;
+  }
+  if (path == SWQ_PATH_GEMV && !gemv_fits(M, H)) return SWQ_ERR_UNSUPPORTED;
+
+  if (path == SWQ_PATH_GEMV) {
+    GemvParams p;
+    p.x = (const uint16_t*)x;
+    p.wg = Wg; p.sg = (const uint16_t*)sg; p.bg = (const uint16_t*)bg;
+    p.wu = Wu; p.su = (const uint16_t*)su; p.bu = (const uint16_t*)bu;
+    p.M = (int)M; p.H = (int)H; p.I = (int)I;
+    p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
+    p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+    if (logging())
+      fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
+              (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
+    (void)hipGetLastError();
+    if (launch_gemv(p, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
+    g_calls[SWQ_PATH_GEMV].fetch_add(1, std::memory_order_relaxed);
+    return SWQ_OK;
+  }
+
+  void* ws = nullptr;
+  int rc = get_workspace(stream, (size_t)ws_bytes(M, H, gs_g, gs_u), &ws);
+  if (rc != SWQ_OK) return rc;
+  const int kext_g = kext_columns(H, gs_g), kext_u = kext_columns(H, gs_u);
+  const int ldx = (int)H + kext_g + kext_u;
+  _Float16* xa = (_Float16*)ws;
+  int* xexp = (int*)((char*)ws + (M * ldx * 2 + 255) / 256 * 256);
+
+  PrepParams pp;
+  pp.x = (const uint16_t*)x;
+  pp.M = (int)M; pp.H = (int)H; pp.gs_g = gs_g; pp.gs_u = gs_u;
+  pp.z_g = bits_g == 8 ? 136.0f : 8.0f;
+  pp.z_u = bits_u == 8 ? 136.0f : 8.0f;
+  pp.ldx = ldx; pp.kext_g = kext_g; pp.kext_u = kext_u;
+  pp.xa = xa; pp.xexp = xexp;
+
+  MfmaParams p;
+  p.xa = xa; p.xexp = xexp;
+  p.wg = Wg; p.sg = (const uint16_t*)sg; p.bg = (const uint16_t*)bg;
+  p.wu = Wu; p.su = (const uint16_t*)su; p.bu = (const uint16_t*)bu;
+  p.M = (int)M; p.H = (int)H; p.I = (int)I;
+  p.gs_g = gs_g; p.gs_u = gs_u;
+  p.ldx = ldx; p.kext_g = kext_g; p.kext_u = kext_u;
+  p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+  const int cfg = choose_mfma_config(M, I);
+  if (logging())
+    fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
+            cfg, kMfmaBM[cfg], kMfmaBN[cfg], (long long)M, (long long)H, (long long)I, bits_g, bits_u,
+            gs_g, gs_u, mode);
+  (void)hipGetLastError();
+  if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
+  if (launch_mfma(p, cfg, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
+  g_calls[SWQ_PATH_MFMA].fetch_add(1, std::memory_order_relaxed);
+  return SWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int swiglu_q_forward(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
+                     const uint32_t* Wu, const void* su, const void* bu, int64_t M, int64_t H, int64_t I,
+                     int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode, void* out,
+                     void* stream) {
+  int rc = validate(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u);
+  if (rc != SWQ_OK) return rc;
+  if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return SWQ_ERR_UNSUPPORTED;
+  if (!out) return SWQ_ERR_NULL;
+  if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
+             nullptr, nullptr, SWQ_PATH_AUTO, stream);
+}
+
+int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
+                        const uint32_t* Wu, const void* su, const void* bu, int64_t M, int64_t H,
+                        int64_t I, int bits_g, int gs_g, int bits_u, int gs_u, int path, float* gate_out,
+                        float* up_out, void* stream) {
+  int rc = validate(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u);
+  if (rc != SWQ_OK) return rc;
+  if (path != SWQ_PATH_AUTO && path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return SWQ_ERR_UNSUPPORTED;
+  if (!gate_out || !up_out) return SWQ_ERR_NULL;
+  if (!aligned(gate_out, 4) || !aligned(up_out, 4)) return SWQ_ERR_ALIGN;
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, SWQ_F32, nullptr, gate_out,
+             up_out, path, stream);
+}
+
+int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode) {
+  if (!spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
+  if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return 0;
+  if (H <= 0 || H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0 || H > (1LL << 24)) return 0;
+  return 1;
+}
+
+void swiglu_q_set_m_threshold(int T) { g_threshold.store(T < 0 ? 0 : T); }
+
+int swiglu_q_get_m_threshold(void) { return threshold_now(); }
+
+uint64_t swiglu_q_call_count(int path) {
+  if (path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return 0;
+  return g_calls[path].load();
+}
+
+void swiglu_q_reset_counts(void) {
+  g_calls[0].store(0);
+  g_calls[1].store(0);
+}
+
+const char* swiglu_q_strerror(int status) {
+  switch (status) {
+    case SWQ_OK: return "ok";
+    case SWQ_ERR_NULL: return "a required pointer is NULL";
+    case SWQ_ERR_SHAPE: return "invalid shape (M<0, H<=0, I<=0, H not a multiple of 32 or of a group size)";
+    case SWQ_ERR_UNSUPPORTED: return "unsupported bits, group size, precision mode or path";
+    case SWQ_ERR_ALIGN: return "misaligned pointer (x, Wg, Wu need 16 bytes; others their element size)";
+    case SWQ_ERR_HIP: return "HIP launch or runtime error";
+    case SWQ_ERR_WORKSPACE: return "workspace allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int bits_g, int gs_g, int bits_u, int gs_u) {
+  if (M <= 0 || H <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
+  if (H % gs_g != 0 || H % gs_u != 0) return 0;
+  return ws_bytes(M, H, gs_g, gs_u);
+}
+
+int swiglu_q_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int rc = SWQ_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  for (auto& kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    if (hipSetDevice(kv.first.first) != hipSuccess) { rc = SWQ_ERR_HIP; continue; }
+    if (hipDeviceSynchronize() != hipSuccess) rc = SWQ_ERR_HIP;
+    if (hipFree(kv.second.ptr) != hipSuccess) rc = SWQ_ERR_HIP;
+  }
+  (void)hipSetDevice(prev);
+  g_ws.clear();
+  return rc;
+}
+
+const char* swiglu_q_version(void) { return "swiglu_q 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device helpers shared by the HIP kernels of the fused quantized SwiGLU.
+//
+// Dequantization scheme.  A weight is w = s*q + b (affine group quantization;
+// "mlx-bun 0.0.7 -> 0.0.9" diff, page 42, gemma4-base.ts QuantizedLinear and
+// fused-swiglu-kernel.ts support predicate).  The kernels rewrite it as
+//
+//     w = s*(q - z) + (b + z*s),        z = 8 for 4-bit codes
+//     w = 16s*(hi - 8) + s*(lo - 8) + (b + 136*s)   for 8-bit codes q = 16*hi + lo
+//
+// Every code offset (q - 8), (hi - 8), (lo - 8) lies in [-8, 7], so with a
+// bf16 scale (8 significant bits) the product s*(q - 8) has at most 11
+// significant bits and is EXACT in binary16 as long as |s| is in
+// [2^-17, 2^8).  The sum over K therefore runs on f16 MFMA / dot2 with exact
+// products and float32 accumulation, and the per-group constant (b + z*s)
+// multiplies the per-group sum of x, which is carried separately.
+//
+// Code extraction places a nibble into the mantissa of a binary16 "magic"
+// number: nibble bits [0,4) OR 0x6400 is 1024 + q, nibble bits [4,8) OR 0x5400
+// is 64 + q.  Subtracting 1032 or 72 (exact) gives q - 8.  A 32-bit word
+// holds two f16 lanes, so one AND/OR pair extracts two codes at once; the
+// pairs come out as (code j, code j+4) of an 8-code block, and every x
+// operand is stored in the matching order [0,4,1,5,2,6,3,7] within each
+// block of 8 consecutive k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ float round_to_bf16(float f) {
+  return bf16_to_f32(f32_to_bf16(f));
+}
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// bf16 value -> (v, v) as two binary16 lanes (exact inside the documented range).
+__device__ __forceinline__ f16x2 bf16_to_h2(uint16_t b) {
+  _Float16 h = (_Float16)bf16_to_f32(b);
+  return (f16x2){h, h};
+}
+
+// Eight 4-bit codes of one word -> s*(q-8) as four f16 pairs in the order
+// (q0,q4) (q1,q5) (q2,q6) (q3,q7).
+__device__ __forceinline__ void dequant4(uint32_t w, f16x2 s2, uint32_t out[4]) {
+  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t w8 = w >> 8;
+  f16x2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - c1032;
+  f16x2 p1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - c72;
+  f16x2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - c1032;
+  f16x2 p3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - c72;
+  out[0] = as_u32(p0 * s2);
+  out[1] = as_u32(p1 * s2);
+  out[2] = as_u32(p2 * s2);
+  out[3] = as_u32(p3 * s2);
+}
+
+// Eight 4-bit codes of one word -> (q-8) as four f16 pairs, same order, no scale.
+__device__ __forceinline__ void codes4(uint32_t w, uint32_t out[4]) {
+  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t w8 = w >> 8;
+  out[0] = as_u32(as_h2((w & 0x000F000Fu) | 0x64006400u) - c1032);
+  out[1] = as_u32(as_h2((w & 0x00F000F0u) | 0x54005400u) - c72);
+  out[2] = as_u32(as_h2((w8 & 0x000F000Fu) | 0x64006400u) - c1032);
+  out[3] = as_u32(as_h2((w8 & 0x00F000F0u) | 0x54005400u) - c72);
+}
+
+// Eight 8-bit codes in two words (wa: codes 0..3, wb: codes 4..7) -> the low
+// and high nibble planes (lo-8) and (hi-8) as f16 pairs in the order
+// (c0,c4) (c1,c5) (c2,c6) (c3,c7).  v_perm_b32 gathers byte j of wa and byte j
+// of wb into bytes 0 and 2 of one register.
+__device__ __forceinline__ void codes8(uint32_t wa, uint32_t wb, uint32_t lo[4], uint32_t hi[4]) {
+  const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
+    const uint32_t t = __builtin_amdgcn_perm(wb, wa, sel);
+    lo[j] = as_u32(as_h2((t & 0x000F000Fu) | 0x64006400u) - c1032);
+    hi[j] = as_u32(as_h2((t & 0x00F000F0u) | 0x54005400u) - c72);
+  }
+}
+
+// Offset z of the rewrite w = s*(q - z) + (b + z*s).
+template <int BITS>
+struct CodeOffset;
+template <>
+struct CodeOffset<4> { static constexpr float z = 8.0f; };
+template <>
+struct CodeOffset<8> { static constexpr float z = 136.0f; };
+
+// sigma(t) = 1 / (1 + e^-t) with the hardware exp2 and reciprocal
+// (about 1 ulp each); e^-t overflows to +inf for t < about -88, giving
+// sigma = 0 and silu = -0.
+__device__ __forceinline__ float sigmoid_fast(float t) {
+  const float e = __builtin_amdgcn_exp2f(-t * 1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Precision modes (values fixed by the public header).
+enum : int { kMatch = 0, kF32 = 1, kF32Bf16Out = 2 };
+
+// The epilogue on one element: gate g and up u in float32.
+__device__ __forceinline__ float swiglu_epilogue(float g, float u, int mode) {
+  if (mode == kMatch) {
+    g = round_to_bf16(g);
+    u = round_to_bf16(u);
+  }
+  return g * sigmoid_fast(g) * u;
+}
+
+}  // namespace swq

@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swq {
+
+// Row staging of x for the matrix-matrix path.
+struct PrepParams {
+  const uint16_t* x;   // bf16 [M, H]
+  int M, H;
+  int gs_g, gs_u;
+  float z_g, z_u;      // code offsets of the gate / up rewrite w = s(q-z) + (b+zs)
+  int ldx;             // row pitch of xa in halves: H + kext_g + kext_u
+  int kext_g, kext_u;  // extra K columns per matrix (4 per group, padded to 32)
+  _Float16* xa;        // out: [M, ldx]
+  int* xexp;           // out: [M] row exponents e (x' = x * 2^-e)
+};
+
+struct MfmaParams {
+  const _Float16* xa;
+  const int* xexp;
+  const uint32_t* wg;
+  const uint16_t* sg;
+  const uint16_t* bg;
+  const uint32_t* wu;
+  const uint16_t* su;
+  const uint16_t* bu;
+  int M, H, I;
+  int gs_g, gs_u;
+  int ldx, kext_g, kext_u;
+  int mode;
+  void* out;
+  float* dbg_g;        // non-null: write float32 gate/up instead of hidden
+  float* dbg_u;
+};
+
+struct GemvParams {
+  const uint16_t* x;   // bf16 [M, H]
+  const uint32_t* wg;
+  const uint16_t* sg;
+  const uint16_t* bg;
+  const uint32_t* wu;
+  const uint16_t* su;
+  const uint16_t* bu;
+  int M, H, I;
+  int gs_g, gs_u;
+  int mode;
+  void* out;
+  float* dbg_g;
+  float* dbg_u;
+};
+
+// Number of MFMA tile configurations and their shapes (rows, columns per matrix).
+constexpr int kMfmaConfigs = 2;
+constexpr int kMfmaBM[kMfmaConfigs] = {128, 256};
+constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
+
+// Largest M the matrix-vector kernel takes, and its LDS budget for x.
+constexpr int kGemvMaxM = 16;
+constexpr int kGemvLdsBytes = 64 * 1024;
+
+inline int64_t gemv_lds_bytes(int64_t M, int64_t H) {
+  // binary16 x' plus one float32 partial sum per 32 inputs, per row
+  return M * (H * 2 + (H / 32) * 4);
+}
+
+inline int kext_columns(int64_t H, int gs) {
+  const int64_t c = 4 * (H / gs);
+  return (int)((c + 31) / 32 * 32);
+}
+
+hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
+hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream);
+hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
+
+}  // namespace swq

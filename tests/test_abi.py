@@ -1,0 +1,147 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/swiglu_q.h declares, and rejects bad arguments before any HIP call."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_swiglu_forward_amd as swq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swiglu_q.h")
+
+# fake, 256-byte aligned "device" addresses: validation never dereferences them
+P = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swiglu_q_\w+)\s*\(", text)))
+
+
+def _exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", swq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert "swiglu_q_forward" in declared and len(declared) >= 10
+    missing = [f for f in declared if f not in _exported()]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(swq.lib(), f)
+        assert hasattr(swq, f), f"binding lacks {f}"
+
+
+def _fwd(**kw):
+    a = dict(x=P, Wg=P, sg=P, bg=P, Wu=P, su=P, bu=P, M=4, H=256, I=64, bits_g=4, gs_g=64, bits_u=4,
+             gs_u=64, precision_mode=0, out=P, stream=0)
+    a.update(kw)
+    return swq.swiglu_q_forward(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), swq.SWQ_ERR_NULL),
+    (dict(Wg=None), swq.SWQ_ERR_NULL),
+    (dict(bu=None), swq.SWQ_ERR_NULL),
+    (dict(out=None), swq.SWQ_ERR_NULL),
+    (dict(bits_g=3), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(bits_u=2), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(gs_g=16), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(gs_u=96), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(precision_mode=3), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(precision_mode=-1), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(M=-1), swq.SWQ_ERR_SHAPE),
+    (dict(H=0), swq.SWQ_ERR_SHAPE),
+    (dict(I=0), swq.SWQ_ERR_SHAPE),
+    (dict(H=96, gs_g=64), swq.SWQ_ERR_SHAPE),
+    (dict(H=200, gs_g=32, gs_u=32), swq.SWQ_ERR_SHAPE),
+    (dict(x=P + 8), swq.SWQ_ERR_ALIGN),
+    (dict(Wg=P + 4), swq.SWQ_ERR_ALIGN),
+    (dict(Wu=P + 2), swq.SWQ_ERR_ALIGN),
+    (dict(sg=P + 1), swq.SWQ_ERR_ALIGN),
+    (dict(out=P + 1), swq.SWQ_ERR_ALIGN),
+    (dict(out=P + 2, precision_mode=1), swq.SWQ_ERR_ALIGN),
+])
+def test_forward_validation(kw, status):
+    before = (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1))
+    assert _fwd(**kw) == status
+    assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
+
+
+def test_m_zero_is_ok_and_launches_nothing():
+    before = (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1))
+    assert _fwd(M=0) == swq.SWQ_OK
+    assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
+
+
+def test_debug_gemm_validation():
+    base = dict(x=P, Wg=P, sg=P, bg=P, Wu=P, su=P, bu=P, M=4, H=256, I=64, bits_g=4, gs_g=64,
+                bits_u=4, gs_u=64, path=-1, gate_out=P, up_out=P, stream=0)
+    assert swq.swiglu_q_debug_gemm(**{**base, "path": 2}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_debug_gemm(**{**base, "gate_out": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_debug_gemm(**{**base, "up_out": P + 2}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_debug_gemm(**{**base, "bits_g": 5}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_debug_gemm(**{**base, "M": 0}) == swq.SWQ_OK
+    # the matrix-vector path cannot take this many rows
+    assert swq.swiglu_q_debug_gemm(**{**base, "M": 4096, "path": 0}) == swq.SWQ_ERR_UNSUPPORTED
+
+
+def test_supported_predicate():
+    assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 0) == 1
+    assert swq.swiglu_q_supported(2560, 8, 32, 4, 64, 1) == 1
+    assert swq.swiglu_q_supported(4096, 4, 128, 8, 128, 2) == 1
+    assert swq.swiglu_q_supported(2048, 2, 64, 4, 64, 0) == 0
+    assert swq.swiglu_q_supported(2048, 4, 48, 4, 64, 0) == 0
+    assert swq.swiglu_q_supported(96, 4, 64, 4, 32, 0) == 0
+    assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 7) == 0
+
+
+def test_threshold_roundtrip():
+    old = swq.swiglu_q_get_m_threshold()
+    try:
+        swq.swiglu_q_set_m_threshold(9)
+        assert swq.swiglu_q_get_m_threshold() == 9
+        swq.swiglu_q_set_m_threshold(-5)
+        assert swq.swiglu_q_get_m_threshold() == 0
+    finally:
+        swq.swiglu_q_set_m_threshold(old)
+
+
+def test_threshold_default_from_environment():
+    code = ("import quantized_swiglu_forward_amd as s; print(s.swiglu_q_get_m_threshold())")
+    env = dict(os.environ, SWIGLU_Q_MMIN="13")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                         check=True).stdout.strip()
+    assert out == "13"
+    env = dict(os.environ, SWIGLU_Q_MMIN="junk")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                         check=True).stdout.strip()
+    assert out == "2"
+
+
+def test_strerror_and_version():
+    for s in range(7):
+        assert swq.swiglu_q_strerror(s)
+    assert swq.swiglu_q_strerror(99) == "unknown status"
+    assert "gfx950" in swq.swiglu_q_version()
+
+
+def test_workspace_bytes():
+    # rows of H + extra columns (4 per group, padded to 32) halves, + row exponents
+    H, M = 2048, 512
+    ext = 2 * ((4 * (H // 64) + 31) // 32 * 32)
+    expect = (M * (H + ext) * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
+    assert swq.swiglu_q_workspace_bytes(M, H, 4, 64, 4, 64) == expect
+    assert swq.swiglu_q_workspace_bytes(0, H, 4, 64, 4, 64) == 0
+    assert swq.swiglu_q_workspace_bytes(M, H, 3, 64, 4, 64) == 0
+
+
+def test_binding_has_no_fallback():
+    """The binding only marshals: it never imports the oracle."""
+    src = open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "__init__.py")).read()
+    assert "oracle" not in src

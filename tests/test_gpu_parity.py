@@ -1,0 +1,232 @@
+"""GPU parity of the HIP library (called through its C ABI) against the CPU
+oracle, element by element, on seeded synthetic problems: the five workload
+configurations (full sizes sampled), a sweep of ragged shapes and
+quantization specs through both kernels, the pre-epilogue projections, and
+invariants that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_swiglu_forward_amd as swq
+from gpu_helpers import (check, device_forward, device_gemm, forced_path, oracle_full, oracle_pairs,
+                         sample_pairs, say)
+from synth import CONFIGS, bf16_bits_to_f32, make_custom, make_problem, pack_codes, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+GEMV, MFMA = swq.SWQ_PATH_GEMV, swq.SWQ_PATH_MFMA
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    swq.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- config 0 --
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_config0_full(mode, path):
+    p = make_problem(0)
+    say("config0", "mode", mode, "path", path)
+    y = device_forward(p, mode, path)
+    check(y, oracle_full(p, mode), mode, f"c0 mode{mode} path{path}")
+
+
+def test_config0_default_dispatch():
+    p = make_problem(0)
+    say("config0 default dispatch")
+    expect = GEMV if p.M < swq.swiglu_q_get_m_threshold() else MFMA
+    y = device_forward(p, 0, None, expect_path=expect)
+    check(y, oracle_full(p, 0), 0, "c0 default")
+
+
+# ------------------------------------------------------------ shape sweep --
+
+SPECS = [(4, 64, 4, 64), (4, 32, 4, 32), (4, 128, 4, 128), (8, 32, 4, 64), (8, 64, 8, 64),
+         (4, 64, 8, 128), (8, 128, 8, 32)]
+SHAPES = [(1, 256, 129), (2, 512, 200), (3, 256, 97), (4, 1024, 130), (5, 256, 64), (6, 384, 77),
+          (7, 512, 129), (8, 256, 255), (16, 512, 100), (31, 256, 129), (32, 256, 96), (33, 512, 257),
+          (63, 256, 65), (64, 128, 64), (65, 512, 300), (127, 256, 129), (128, 256, 128),
+          (129, 512, 257), (257, 256, 400)]
+SWEEP = []
+for i, (M, H, I) in enumerate(SHAPES):
+    spec = SPECS[i % len(SPECS)]
+    if H % spec[1] or H % spec[3]:
+        spec = SPECS[0]
+    paths = [GEMV, MFMA] if M <= 16 else [MFMA]
+    for path in paths:
+        SWEEP.append((M, H, I, spec, i % 3, path))
+
+
+@pytest.mark.parametrize("M,H,I,spec,mode,path", SWEEP,
+                         ids=[f"M{c[0]}-H{c[1]}-I{c[2]}-{c[3][0]}b{c[3][1]}-{c[3][2]}b{c[3][3]}-m{c[4]}-p{c[5]}"
+                              for c in SWEEP])
+def test_shape_sweep(M, H, I, spec, mode, path):
+    bg, gg, bu, gu = spec
+    p = make_custom(M, H, I, bg, gg, bu, gu, seed=1000 + M * 7 + I, bias_mode="factor")
+    say("sweep", M, H, I, spec, "mode", mode, "path", path)
+    y = device_forward(p, mode, path)
+    check(y, oracle_full(p, mode), mode, f"sweep M{M} H{H} I{I} {spec} mode{mode} path{path}")
+
+
+# ------------------------------------------------------- full-size configs --
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_config1_decode_full(mode):
+    p = make_problem(1)
+    say("config1 decode full", "mode", mode)
+    y = device_forward(p, mode, None, expect_path=GEMV if 1 < swq.swiglu_q_get_m_threshold() else MFMA)
+    check(y, oracle_full(p, mode), mode, f"c1 mode{mode}")
+
+
+def test_config1_fresh_inputs():
+    """Three of the 1000 fresh decode inputs, on one resident weight set."""
+    p = make_problem(1)
+    dev = list(swq.to_device(p))
+    for call in (0, 499, 999):
+        q = make_problem(1, with_calls=False)
+        q.x = p.xs[call:call + 1].copy()
+        dev[0] = swq.to_device(q)[0]
+        say("config1 fresh x call", call)
+        y = device_forward(q, 0, None, dev=tuple(dev))
+        check(y, oracle_full(q, 0), 0, f"c1 call {call}")
+
+
+@pytest.mark.parametrize("cfg,mode", [(2, 0), (2, 1), (2, 2), (3, 0), (3, 1), (4, 0), (4, 1)])
+def test_full_size_sampled(cfg, mode):
+    p = make_problem(cfg)
+    c = CONFIGS[cfg]
+    say(f"config{cfg} full size", "mode", mode)
+    y = device_forward(p, mode, None, expect_path=MFMA)
+    ms, ns = sample_pairs(c.M, c.I, 3000, seed=cfg * 10 + mode)
+    o = oracle_pairs(p, mode, ms, ns)
+    check(y[ms, ns], o, mode, f"c{cfg} mode{mode} sampled")
+    assert np.all(np.isfinite(y))
+
+
+# -------------------------------------------------- pre-epilogue gate / up --
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+@pytest.mark.parametrize("spec", [(4, 64, 4, 64), (8, 32, 4, 64), (4, 128, 8, 64)])
+def test_debug_gemm_matches_oracle(spec, path):
+    M = 5 if path == GEMV else 70
+    p = make_custom(M, 1024, 193, *spec, seed=31)
+    say("debug gemm", spec, "path", path)
+    g, u = device_gemm(p, path)
+    o = oracle_full(p, 1)
+    eg = np.max(np.abs(g - o["g"]) / o["nu_g"])
+    eu = np.max(np.abs(u - o["u"]) / o["nu_u"])
+    print(f"  max |dg|/nu_g={eg:.3g} |du|/nu_u={eu:.3g}")
+    assert eg <= 1e-5 and eu <= 1e-5
+
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_integer_special_case_is_exact(path):
+    """s = 1, b in {0, -8}, small-integer x: gate and up are integers below
+    2^24 and must come out bit-exact."""
+    rng = np.random.default_rng(5)
+    M, H, I = (3, 512, 70) if path == GEMV else (40, 512, 70)
+    p = make_custom(M, H, I, 8, 32, 4, 64, seed=2)
+    xi = rng.integers(-7, 8, size=(M, H))
+    p.x = to_bf16_bits(xi.astype(np.float32))
+    cg = rng.integers(0, 256, size=(I, H), dtype=np.uint8)
+    cu = rng.integers(0, 16, size=(I, H), dtype=np.uint8)
+    p.wg, p.wu = pack_codes(cg, 8), pack_codes(cu, 4)
+    p.sg = to_bf16_bits(np.ones((I, H // 32), np.float32))
+    p.bg = to_bf16_bits(np.zeros((I, H // 32), np.float32))
+    p.su = to_bf16_bits(np.ones((I, H // 64), np.float32))
+    p.bu = to_bf16_bits(np.full((I, H // 64), -8.0, np.float32))
+    say("integer exact", "path", path)
+    g, u = device_gemm(p, path)
+    ref_g = xi @ cg.astype(np.int64).T
+    ref_u = xi @ (cu.astype(np.int64) - 8).T
+    assert np.array_equal(g, ref_g.astype(np.float64))
+    assert np.array_equal(u, ref_u.astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_gemv_and_mfma_agree(M):
+    p = make_custom(M, 2048, 300, 4, 64, seed=M)
+    say("gemv vs mfma", M)
+    yg = device_forward(p, 1, GEMV)
+    ym = device_forward(p, 1, MFMA)
+    o = oracle_full(p, 1)
+    check(yg, o, 1, f"gemv M{M}")
+    check(ym, o, 1, f"mfma M{M}")
+
+
+# -------------------------------------------------------------- invariants --
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_bitwise_repeatable(path):
+    p = make_custom(8 if path == GEMV else 300, 1024, 500, 4, 64, seed=12)
+    dev = swq.to_device(p)
+    say("repeatability", path)
+    a = device_forward(p, 0, path, dev=dev)
+    b = device_forward(p, 0, path, dev=dev)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_row_and_column_permutation(path):
+    M = 6 if path == GEMV else 200
+    p = make_custom(M, 512, 160, 8, 32, 4, 64, seed=13)
+    say("permutation", path)
+    y = device_forward(p, 1, path)
+    rng = np.random.default_rng(0)
+    pr = rng.permutation(M)
+    pc = rng.permutation(160)
+    q = make_custom(M, 512, 160, 8, 32, 4, 64, seed=13)
+    q.x = p.x[pr].copy()
+    for k in ("wg", "sg", "bg", "wu", "su", "bu"):
+        setattr(q, k, getattr(p, k)[pc].copy())
+    yq = device_forward(q, 1, path)
+    assert np.array_equal(yq, y[pr][:, pc])
+
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_power_of_two_scaling_of_x(path):
+    M = 4 if path == GEMV else 100
+    p = make_custom(M, 1024, 96, 4, 64, seed=14)
+    say("x scaling", path)
+    g1, u1 = device_gemm(p, path)
+    q = make_custom(M, 1024, 96, 4, 64, seed=14)
+    q.x = to_bf16_bits(bf16_bits_to_f32(p.x) * np.float32(8.0))
+    g8, u8 = device_gemm(q, path)
+    assert np.array_equal(g8, 8.0 * g1) and np.array_equal(u8, 8.0 * u1)
+
+
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_zero_gate_weights(path):
+    """Constant codes c per group with b = -s*c: every gate weight is zero, so
+    hidden is zero up to float32 rounding of the terms that cancel."""
+    M = 3 if path == GEMV else 64
+    p = make_custom(M, 512, 90, 4, 64, seed=15)
+    rng = np.random.default_rng(15)
+    c = rng.choice(np.array([1, 2, 4, 8]), size=(90, 512 // 64))
+    p.wg = pack_codes(np.repeat(c, 64, axis=1).astype(np.uint8), 4)
+    s = bf16_bits_to_f32(p.sg)
+    p.bg = to_bf16_bits((-s * c).astype(np.float32))
+    say("zero gate", path)
+    g, _ = device_gemm(p, path)
+    scale = np.abs(bf16_bits_to_f32(p.x)).astype(np.float64).sum(axis=1, keepdims=True) * float(s.max()) * 8
+    assert np.all(np.abs(g) <= 2.0 ** -20 * scale)
+    y = device_forward(p, 1, path)
+    o = oracle_full(p, 1)
+    assert np.all(o["h"] == 0.0)
+    assert np.all(np.abs(y) <= 2.0 ** -18 * scale * np.abs(o["u"]).max())
+
+
+def test_m_zero_launches_nothing():
+    p = make_custom(1, 256, 64, 4, 64, seed=1)
+    dev = swq.to_device(p)
+    out = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    before = [swq.swiglu_q_call_count(k) for k in (0, 1)]
+    rc = swq.swiglu_q_forward(dev[0], *dev[1:], 0, 256, 64, 4, 64, 4, 64, 0, out.data_ptr() or 256, None)
+    assert rc == swq.SWQ_OK
+    assert [swq.swiglu_q_call_count(k) for k in (0, 1)] == before
