@@ -40,7 +40,7 @@
  *
  * Exactness: the weights are dequantized exactly (no rounding of s·q + b);
  * gate and up are float32 dot products.  This holds when every scale and
- * bias is zero or has magnitude in [2^-17, 2^12) (the range in which a bf16
+ * bias is zero or has magnitude in [2^-17, 2^8) (the range in which a bf16
  * value times a code offset of at most 2^(bits-1) stays exactly
  * representable in binary16); outside that range the dequantized weight is
  * rounded to binary16.
@@ -131,8 +131,9 @@ int swiglu_q_debug_gemm(const void *x,
                         int bits_g, int gs_g, int bits_u, int gs_u,
                         int path, float *gate_out, float *up_out, void *stream);
 
-/* Bytes of workspace the MFMA path uses for this shape (0 when M == 0). */
-int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int bits_g, int gs_g,
+/* Bytes of workspace the MFMA path uses for this shape (0 when M == 0 or
+ * the arguments are invalid). */
+int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
                                  int bits_u, int gs_u);
 
 /* Free every cached workspace (synchronises the device first). */

@@ -57,7 +57,7 @@ def lib():
     L.swiglu_q_reset_counts.restype = None
     L.swiglu_q_strerror.argtypes = [i32]
     L.swiglu_q_strerror.restype = ctypes.c_char_p
-    L.swiglu_q_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    L.swiglu_q_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
     L.swiglu_q_workspace_bytes.restype = i64
     L.swiglu_q_release_workspace.argtypes = []
     L.swiglu_q_release_workspace.restype = i32
@@ -124,8 +124,8 @@ def swiglu_q_strerror(status: int) -> str:
     return lib().swiglu_q_strerror(status).decode()
 
 
-def swiglu_q_workspace_bytes(M, H, bits_g, gs_g, bits_u, gs_u) -> int:
-    return lib().swiglu_q_workspace_bytes(M, H, bits_g, gs_g, bits_u, gs_u)
+def swiglu_q_workspace_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u) -> int:
+    return lib().swiglu_q_workspace_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u)
 
 
 def swiglu_q_release_workspace() -> int:

@@ -85,19 +85,33 @@ bool gemv_fits(int64_t M, int64_t H) {
 }
 
 int choose_mfma_config(int64_t M, int64_t I) {
-  if (const char* s = getenv("SWIGLU_Q_MFMA_CFG")) {
-    int v = atoi(s);
-    if (v >= 0 && v < kMfmaConfigs) return v;
-  }
-  const int64_t tiles_big = ((M + kMfmaBM[1] - 1) / kMfmaBM[1]) * ((I + kMfmaBN[1] - 1) / kMfmaBN[1]);
-  return tiles_big >= 512 ? 1 : 0;
+  (void)M;
+  (void)I;
+  return 0;
 }
 
-int64_t ws_bytes(int64_t M, int64_t H, int gs_g, int gs_u) {
-  const int64_t ldx = H + kext_columns(H, gs_g) + kext_columns(H, gs_u);
-  const int64_t xa = (M * ldx * 2 + 255) / 256 * 256;
-  const int64_t ex = (M * 4 + 255) / 256 * 256;
-  return xa + ex;
+// Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
+// (binary16), row exponents [M] (int32), then the extra-column B rows
+// [I, kext] (binary16) of the gate, of its second plane (8-bit gate only),
+// of the up matrix and of its second plane (8-bit up only).
+struct WsLayout {
+  int64_t xa, xexp, eg, eg2, eu, eu2, total;
+};
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bits_u, int gs_u) {
+  const int64_t kext = kext_columns(H, gs_g < gs_u ? gs_g : gs_u);
+  const int64_t plane = align256(I * kext * 2);
+  WsLayout w;
+  w.xa = 0;
+  w.xexp = align256(M * (H + kext) * 2);
+  w.eg = w.xexp + align256(M * 4);
+  w.eg2 = w.eg + plane;
+  w.eu = w.eg2 + (bits_g == 8 ? plane : 0);
+  w.eu2 = w.eu + plane;
+  w.total = w.eu2 + (bits_u == 8 ? plane : 0);
+  return w;
 }
 
 int get_workspace(hipStream_t stream, size_t need, void** out) {
@@ -154,29 +168,40 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     return SWQ_OK;
   }
 
+  const WsLayout L = ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u);
   void* ws = nullptr;
-  int rc = get_workspace(stream, (size_t)ws_bytes(M, H, gs_g, gs_u), &ws);
+  int rc = get_workspace(stream, (size_t)L.total, &ws);
   if (rc != SWQ_OK) return rc;
-  const int kext_g = kext_columns(H, gs_g), kext_u = kext_columns(H, gs_u);
-  const int ldx = (int)H + kext_g + kext_u;
-  _Float16* xa = (_Float16*)ws;
-  int* xexp = (int*)((char*)ws + (M * ldx * 2 + 255) / 256 * 256);
+  char* wsb = (char*)ws;
+  const int g0 = gs_g < gs_u ? gs_g : gs_u;
+  const int kext = kext_columns(H, g0);
+  const int ldx = (int)H + kext;
+  _Float16* xa = (_Float16*)(wsb + L.xa);
+  int* xexp = (int*)(wsb + L.xexp);
+  _Float16* eg = (_Float16*)(wsb + L.eg);
+  _Float16* eg2 = bits_g == 8 ? (_Float16*)(wsb + L.eg2) : nullptr;
+  _Float16* eu = (_Float16*)(wsb + L.eu);
+  _Float16* eu2 = bits_u == 8 ? (_Float16*)(wsb + L.eu2) : nullptr;
 
   PrepParams pp;
   pp.x = (const uint16_t*)x;
-  pp.M = (int)M; pp.H = (int)H; pp.gs_g = gs_g; pp.gs_u = gs_u;
-  pp.z_g = bits_g == 8 ? 136.0f : 8.0f;
-  pp.z_u = bits_u == 8 ? 136.0f : 8.0f;
-  pp.ldx = ldx; pp.kext_g = kext_g; pp.kext_u = kext_u;
+  pp.sg = (const uint16_t*)sg; pp.bg = (const uint16_t*)bg;
+  pp.su = (const uint16_t*)su; pp.bu = (const uint16_t*)bu;
+  pp.M = (int)M; pp.H = (int)H; pp.I = (int)I;
+  pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
+  pp.g0 = g0; pp.ldx = ldx; pp.kext = kext;
   pp.xa = xa; pp.xexp = xexp;
+  pp.bext_g = eg; pp.bext_g2 = eg2; pp.bext_u = eu; pp.bext_u2 = eu2;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;
   p.wg = Wg; p.sg = (const uint16_t*)sg; p.bg = (const uint16_t*)bg;
   p.wu = Wu; p.su = (const uint16_t*)su; p.bu = (const uint16_t*)bu;
   p.M = (int)M; p.H = (int)H; p.I = (int)I;
-  p.gs_g = gs_g; p.gs_u = gs_u;
-  p.ldx = ldx; p.kext_g = kext_g; p.kext_u = kext_u;
+  p.gs_g = gs_g; p.gs_u = gs_u; p.g0 = g0;
+  p.ldx = ldx; p.kext = kext;
+  p.bext_g = eg; p.bext_g2 = eg2; p.bext_u = eu; p.bext_u2 = eu2;
+  p.ext_plane = (int)(L.eg2 - L.eg);
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
   const int cfg = choose_mfma_config(M, I);
   if (logging())
@@ -254,10 +279,11 @@ const char* swiglu_q_strerror(int status) {
   }
 }
 
-int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int bits_g, int gs_g, int bits_u, int gs_u) {
-  if (M <= 0 || H <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
+int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bits_u,
+                                 int gs_u) {
+  if (M <= 0 || H <= 0 || I <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
   if (H % gs_g != 0 || H % gs_u != 0) return 0;
-  return ws_bytes(M, H, gs_g, gs_u);
+  return ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u).total;
 }
 
 int swiglu_q_release_workspace(void) {

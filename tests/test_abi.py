@@ -132,13 +132,21 @@ def test_strerror_and_version():
 
 
 def test_workspace_bytes():
-    # rows of H + extra columns (4 per group, padded to 32) halves, + row exponents
-    H, M = 2048, 512
-    ext = 2 * ((4 * (H // 64) + 31) // 32 * 32)
-    expect = (M * (H + ext) * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
-    assert swq.swiglu_q_workspace_bytes(M, H, 4, 64, 4, 64) == expect
-    assert swq.swiglu_q_workspace_bytes(0, H, 4, 64, 4, 64) == 0
-    assert swq.swiglu_q_workspace_bytes(M, H, 3, 64, 4, 64) == 0
+    # x' rows of H + extra columns (4 per group of the finer group size,
+    # padded to 32) halves, row exponents, then one [I, kext] binary16 plane
+    # of extra-column B rows per matrix, two for an 8-bit matrix
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    def expect(M, H, I, bg, gg, bu, gu):
+        ext = (4 * (H // min(gg, gu)) + 31) // 32 * 32
+        planes = (2 if bg == 8 else 1) + (2 if bu == 8 else 1)
+        return a256(M * (H + ext) * 2) + a256(M * 4) + planes * a256(I * ext * 2)
+
+    assert swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64) == expect(512, 2048, 8192, 4, 64, 4, 64)
+    assert swq.swiglu_q_workspace_bytes(8192, 2560, 10240, 8, 32, 4, 64) == expect(8192, 2560, 10240, 8, 32, 4, 64)
+    assert swq.swiglu_q_workspace_bytes(0, 2048, 64, 4, 64, 4, 64) == 0
+    assert swq.swiglu_q_workspace_bytes(4, 2048, 64, 3, 64, 4, 64) == 0
 
 
 def test_binding_has_no_fallback():
