@@ -13,8 +13,12 @@ kernel, the CPU oracle on a bounded sample (the baseline), and the
 matrix-matrix path on the three prefill configurations (TFLOP/s and fraction
 of the bf16/f16 dense MFMA peak).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|c2|c3|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|c2|c3|c4|copy]
                     [--no-prefill] [--no-cpu] [--eager]
+
+``--workload copy`` times a plain device-to-device copy of one decode call's
+algorithmic byte count, 1000 copies per step over 40 rotating sources: the
+known-size reference against which the HBM traffic counters are scaled.
 """
 import argparse
 import json
@@ -45,6 +49,35 @@ def weight_bytes(c):
 
 def algorithmic_bytes(c, out_bytes=2):
     return weight_bytes(c) + c.M * c.H * 2 + c.M * c.I * out_bytes
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_gemv_M1_H2048_I5632_hbm_traffic.md")
+GEMV_SOURCES = ["swq_gemv.hip", "swq_device.h", "swq_kernels.h"]
+
+
+def gemv_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or
+    None when the decode kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source") == gemv_source_digest():
+                        return int(rec["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def rotating_weight_sets(c, base_dev, n_sets, seed):
@@ -154,7 +187,7 @@ def bench_decode(args):
                    "gs_u": c.gs_u, "calls_per_step": CALLS, "weight_sets": ROTATING_SETS,
                    "precision_mode": "MATCH", "launch": "hip graph" if graph is not None else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(avg_launch_us, 3),
                      "bytes_per_launch": algorithmic_bytes(c)},
         "wall_s": round(wall, 3),
@@ -193,6 +226,44 @@ def bench_prefill_one(cfg, steps, warmup, mode=0):
             "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
 
 
+def bench_copy(args):
+    """Plain copy kernel of a known size: 1000 copies of 12,991,488 bytes per
+    step, sources rotating over 40 buffers, recorded into one HIP graph."""
+    import torch
+
+    nbytes = 12991488
+    srcs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i) for i in range(ROTATING_SETS)]
+    dst = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            dst.copy_(srcs[i])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(CALLS):
+            dst.copy_(srcs[i % ROTATING_SETS])
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    us = ms_step * 1e3 / CALLS
+    return {"value": round(2 * nbytes / (us * 1e-6) / 1e9, 2), "unit": "GB/s (read+write)",
+            "ms_per_step": round(ms_step, 4), "dtype": "u8",
+            "config": {"workload": f"device copy of {nbytes} bytes, 1000 per step, 40 rotating sources",
+                       "bytes_read": nbytes, "bytes_written": nbytes, "avg_launch_us": round(us, 3)}}
+
+
 def cpu_baseline_decode(max_seconds=20.0):
     """The oracle as it stands, on a bounded sample of the decode workload:
     whole calls (all 5632 columns) on fresh x rows, until about max_seconds."""
@@ -225,7 +296,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
@@ -247,6 +318,11 @@ def main():
     if args.workload == "decode":
         log("decode: timing ...")
         line.update(bench_decode(args))
+    elif args.workload == "copy":
+        line.update(bench_copy(args))
+        line["metric"] = "plain copy (traffic-counter reference)"
+        print(json.dumps(line), flush=True)
+        return
     else:
         cfg = int(args.workload[1])
         from synth import CONFIGS

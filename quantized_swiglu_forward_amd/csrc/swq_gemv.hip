@@ -12,7 +12,7 @@
 // epilogue as the matrix-matrix path writes hidden.
 //
 // x is used as x' = x * 2^-e in binary16 (e = exponent of the row maximum;
-// exact for every element at least 2^-18 of the maximum), in the
+// exact for every element at least 2^-17 of the maximum), in the
 // [0,4,1,5,2,6,3,7] order of the code pairs.
 //
 // Work split: a column group of `lpc` lanes (a power of two, at most 64)

@@ -12,15 +12,15 @@
 //     the dequantized weight pairs, and appends, per group of
 //     g0 = min(gs_g, gs_u) inputs, the group sum Sx of x' split as hi + lo
 //     binary16 values, in four extra K columns (hi, lo, hi, lo).  Every bf16
-//     x whose magnitude is at least 2^-18 of the row maximum converts
+//     x whose magnitude is at least 2^-17 of the row maximum converts
 //     exactly.  The remaining blocks write the B rows of those extra
 //     columns for every output feature: (b, b, 8s, 8s) per group (exact in
 //     binary16), and for an 8-bit matrix a second plane (128s, 128s, 0, 0),
 //     so that the extra columns add sum_g Sx[m,g] * (b[n,g] + z*s[n,g]).
 //  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators.  The K
-//     loop first runs over the extra columns, then streams the packed codes,
-//     dequantizes them to the exact binary16 values s*(q - z) and feeds them
-//     to the MFMA.  The epilogue multiplies by 2^e (exact), then computes
+//     loop streams the packed codes, dequantizes them to the exact binary16
+//     values s*(q - z) and feeds them to the MFMA, then runs over the extra
+//     columns.  The epilogue multiplies by 2^e (exact), then computes
 //     silu(g) * u per precision mode.
 #include "swq_device.h"
 #include "swq_kernels.h"
