@@ -5,28 +5,27 @@
 // fused-swiglu-kernel.ts, the comment on where the fusion pays off, and the
 // M-threshold function below which the caller keeps this path).  No MFMA
 // here: lanes stream packed rows with 16-byte loads, turn codes into exact
-// binary16 (q - 8) pairs and accumulate x'(q - 8) with v_dot2_f32_f16; per
-// 32-input chunk (always inside one quantization group) the partial sum P
-// and the chunk's sum of x' give  s*P + (b + z*s)*Sx  in float32.  A
+// binary16 operands and accumulate x'q with v_dot2_f32_f16; per 32-input
+// chunk (always inside one quantization group) the partial sum P and the
+// chunk's sum of x' give the chunk's share of sum_k x'(s q + b) in float32.  A
 // cross-lane reduction per column then yields gate and up, and the same
 // epilogue as the matrix-matrix path writes hidden.
 //
-// x is used as x' = x * 2^-e in binary16 (e = exponent of the row maximum;
-// exact for every element at least 2^-17 of the maximum), in the
-// [0,4,1,5,2,6,3,7] order of the code pairs.
-//
 // Work split: a column group of `lpc` lanes (a power of two, at most 64)
 // owns one output column at a time; lane sl of the group handles the
-// 32-input chunks sl, sl + lpc, ...  Every lane issues its weight loads
-// before anything else, so the whole weight stream is in flight while x is
-// prepared.
+// 32-input chunks sl, sl + lpc, ...  Every lane issues its loads before
+// anything else, so the whole weight stream is in flight at once.
 //
 // Two kernels:
-//  * swq_gemv1_kernel: M = 1 with at most two chunks per lane.  Each lane
-//    keeps its own x chunks in registers; the row maximum is a reduction over
-//    the column group, which covers the whole row.  No LDS, no barriers.
-//  * swq_gemvm_kernel: 1 <= M <= 16.  The block stages x' and per-chunk sums
-//    in LDS; the loads of the next (column, chunk) item are in flight while
+//  * swq_gemv1_kernel: M = 1 with at most two chunks per lane (H <= 4096).
+//    Codes enter the dot products as exact binary16 subnormals with no
+//    offset, and each lane scales its own x chunk by a power of two; no LDS,
+//    no barrier (described above the kernel).
+//  * swq_gemvm_kernel: 1 <= M <= 16.  The block stages x' = x * 2^-e in
+//    binary16 (e = exponent of the row maximum; exact for every element at
+//    least 2^-17 of the maximum) in the [0,4,1,5,2,6,3,7] order of the code
+//    pairs, with per-chunk sums, in LDS; codes become exact binary16 (q - z)
+//    pairs; the loads of the next (column, chunk) item are in flight while
 //    the current one is computed.
 #include "swq_device.h"
 #include "swq_kernels.h"
@@ -96,34 +95,6 @@ __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, flo
   }
 }
 
-// bf16 x chunk (32 values) -> x' = x * 2^-e as binary16 pairs in code-pair order, and its sum.
-__device__ __forceinline__ float convert_chunk(const u32x4 raw[4], int e, uint32_t xv[16]) {
-  float sum = 0.0f;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {            // block of 8 values
-    float f[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(raw[b][j] & 0xFFFFu)), -e);
-      f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(raw[b][j] >> 16)), -e);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += f[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xv[4 * b + j] = as_u32((f16x2){(_Float16)f[j], (_Float16)f[j + 4]});
-  }
-  return sum;
-}
-
-__device__ __forceinline__ uint32_t chunk_absmax(const u32x4 raw[4]) {
-  uint32_t a = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a = max(a, max(raw[b][j] & 0x7FFFu, (raw[b][j] >> 16) & 0x7FFFu));
-  return a;
-}
-
 __device__ __forceinline__ int row_exponent(uint32_t amax_bits) {
   if (amax_bits == 0) return 0;
   const int field = (int)(amax_bits >> 7);
@@ -131,7 +102,162 @@ __device__ __forceinline__ int row_exponent(uint32_t amax_bits) {
 }
 
 // ------------------------------------------------------------- M == 1 ----
+//
+// Codes as binary16 subnormals.  A 4-bit code q in bits [0,4) of a binary16
+// lane, with the exponent field zero, is the subnormal q * 2^-24; in bits
+// [4,8) it is 16q * 2^-24.  So one AND per code pair of a word yields exact
+// binary16 operands (no magic constant, no offset), and v_dot2_f32_f16
+// forms exact products x' * q in float32.  The x' pairs that meet a code in
+// bits [0,4) are stored pre-multiplied by 16 (exact: a power of two, and
+// 16 max|x'| < 32), so every product lands in the same unit 2^-20:
+//
+//   P = sum_k 16 x'_k q_k 2^-24 = 2^-20 sum_k x'_k q_k
+//
+// and a 32-code chunk adds s * P + b * Sx'' with Sx'' = 2^-20 * sum x' over
+// the chunk (the same unit).  x' = x * 2^-e uses the exponent e of the
+// chunk's own largest magnitude; the chunk's scale and the unit are removed
+// with one ldexp by (e + 20) per chunk.  No offset is subtracted, so nothing
+// cancels beyond what w = s*q + b itself does.
+//
+// 8-bit codes: v_perm_b32 gathers byte j of the word holding codes 0..3 and
+// byte j of the word holding codes 4..7 into one register; its low nibbles
+// (mask 0x000F000F) and high nibbles (mask 0x00F000F0, worth 16 * lo units)
+// both meet 16 x', which is what q = 16 hi + lo needs.
+//
 
+// Unscaled dot of one chunk in units of 2^-20: xa holds the 16x pairs
+// (codes at bits [0,4)), xb the 1x pairs (codes at bits [4,8)).
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const uint32_t xa[8], const uint32_t xb[8]) {
+  float p = 0.0f;
+  if (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = r.w[0][j];
+      const uint32_t w8 = w >> 8;
+      p = __builtin_amdgcn_fdot2(as_h2(xa[2 * j]), as_h2(w & 0x000F000Fu), p, false);
+      p = __builtin_amdgcn_fdot2(as_h2(xb[2 * j]), as_h2(w & 0x00F000F0u), p, false);
+      p = __builtin_amdgcn_fdot2(as_h2(xa[2 * j + 1]), as_h2(w8 & 0x000F000Fu), p, false);
+      p = __builtin_amdgcn_fdot2(as_h2(xb[2 * j + 1]), as_h2(w8 & 0x00F000F0u), p, false);
+    }
+  } else {
+    // xa / xb interleave as (pair 0, pair 2) / (pair 1, pair 3) of each 8-block;
+    // 8-bit needs 16x' on every pair: xb pairs are scaled here
+    const f16x2 c16 = {(_Float16)16.0f, (_Float16)16.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4& wv = r.w[j / 2];
+      const uint32_t wa = wv[2 * (j & 1)], wb = wv[2 * (j & 1) + 1];
+      uint32_t xq[4] = {xa[2 * j], as_u32(as_h2(xb[2 * j]) * c16), xa[2 * j + 1],
+                        as_u32(as_h2(xb[2 * j + 1]) * c16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + t) << 16) | (uint32_t)t;
+        const uint32_t v = __builtin_amdgcn_perm(wb, wa, sel);
+        p = __builtin_amdgcn_fdot2(as_h2(xq[t]), as_h2(v & 0x000F000Fu), p, false);
+        p = __builtin_amdgcn_fdot2(as_h2(xq[t]), as_h2(v & 0x00F000F0u), p, false);
+      }
+    }
+  }
+  return p;
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const uint32_t xa[8], const uint32_t xb[8],
+                                            float sx) {
+  const float P = chunk_dot_sub<BITS>(r, xa, xb);
+  const float s = __uint_as_float(r.sb << 16);
+  const float b = __uint_as_float(r.sb & 0xFFFF0000u);
+  return fmaf(s, P, b * sx);
+}
+
+// Sum over aligned groups of `width` lanes (a power of two); every lane of a
+// group ends with the group's sum.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v += __shfl_xor(v, 1);
+  if (width >= 4) v += __shfl_xor(v, 2);
+  if (width >= 8) v += __shfl_xor(v, 4);
+  if (width >= 16) v += __shfl_xor(v, 8);
+  if (width >= 32) v += __shfl_xor(v, 16);
+  if (width >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Sum over the whole wavefront, uniform result: DPP within rows of 16
+// lanes (xor 1, xor 2, half-row mirror, row mirror), then the four row sums.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false);   // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// One lane's x chunk (32 bf16 values) as exact binary16 pairs for the
+// subnormal-code dot products, scaled by its own power of two: x' = x 2^-e
+// with e the exponent of the chunk's largest magnitude (every element at
+// least 2^-17 of that maximum converts exactly).  xa holds the pairs that
+// meet codes in bits [0,4) as 16x', xb the others as x'; sx is the chunk's
+// sum of x' in the dot products' unit 2^-20.
+struct XChunk {
+  uint32_t xa[8], xb[8];
+  float sx;
+  int e;
+};
+
+__device__ __forceinline__ void load_x_chunk(const uint16_t* x, int kc, u32x4 raw[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) raw[q] = *reinterpret_cast<const u32x4*>(x + kc * 32 + 8 * q);
+}
+
+__device__ __forceinline__ void make_x_chunk(const u32x4 raw[4], XChunk& c) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(raw[q][j] & 0x7FFFu, (raw[q][j] >> 16) & 0x7FFFu));
+  c.e = row_exponent(amax);
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float sx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {            // 8-block q: values 8q .. 8q+7
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16_to_f32((uint16_t)(raw[q][j] & 0xFFFFu));
+      f[2 * j + 1] = bf16_to_f32((uint16_t)(raw[q][j] >> 16));
+    }
+    // pairs (0,4) and (2,6) meet codes in bits [0,4): 16x'; (1,5), (3,7): x'
+    c.xa[2 * q] = as_u32((f16x2){(_Float16)ldexpf(f[0], 4 - c.e), (_Float16)ldexpf(f[4], 4 - c.e)});
+    c.xb[2 * q] = as_u32((f16x2){(_Float16)ldexpf(f[1], -c.e), (_Float16)ldexpf(f[5], -c.e)});
+    c.xa[2 * q + 1] = as_u32((f16x2){(_Float16)ldexpf(f[2], 4 - c.e), (_Float16)ldexpf(f[6], 4 - c.e)});
+    c.xb[2 * q + 1] = as_u32((f16x2){(_Float16)ldexpf(f[3], -c.e), (_Float16)ldexpf(f[7], -c.e)});
+    sx = __builtin_amdgcn_fdot2(as_h2(c.xa[2 * q]), sixteenth, sx, false);
+    sx = __builtin_amdgcn_fdot2(as_h2(c.xb[2 * q]), one, sx, false);
+    sx = __builtin_amdgcn_fdot2(as_h2(c.xa[2 * q + 1]), sixteenth, sx, false);
+    sx = __builtin_amdgcn_fdot2(as_h2(c.xb[2 * q + 1]), one, sx, false);
+  }
+  c.sx = ldexpf(sx, -20);
+}
+
+// The chunk's share of sum_k x_k (s q_k + b), in the chunk's own scale 2^(e+20).
+template <int BITS>
+__device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChunk& x) {
+  const float P = chunk_dot_sub<BITS>(r, x.xa, x.xb);
+  const float s = __uint_as_float(r.sb << 16);
+  const float b = __uint_as_float(r.sb & 0xFFFF0000u);
+  return fmaf(s, P, b * x.sx);
+}
+
+// M = 1.  Lane sl of a column group of lpc lanes owns the 32-code chunks
+// sl, sl + lpc, ... of its column; a wave owns R rounds of 64/lpc columns.
+// Every lane loads its x chunks first, then its whole weight stream, then
+// converts x while the weights arrive; no LDS, no barrier.
 template <int BITS_G, int BITS_U, int CPL, int R>
 __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lpc) {
   const int lane = threadIdx.x & 63;
@@ -142,13 +268,18 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lpc) {
   const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
 
-  // 1. all weight loads of this lane's R columns x CPL chunks
+  // 1. x chunks (loads complete in issue order: x first, so it is not held
+  //    up behind the weight stream)
+  u32x4 raw[CPL][4];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) load_x_chunk(p.x, min(sl + c * lpc, nchunk - 1), raw[c]);
+
+  // 2. all weight loads of this lane: R columns x CPL chunks x 2 matrices
   RawChunk<BITS_G> rg[R][CPL];
   RawChunk<BITS_U> ru[R][CPL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int n = (wave_global * R + r) * cpw + sub;
-    const int nn = min(n, p.I - 1);
+    const int nn = min((wave_global * R + r) * cpw + sub, p.I - 1);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int kc = min(sl + c * lpc, nchunk - 1);
@@ -157,45 +288,31 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lpc) {
     }
   }
 
-  // 2. this lane's x chunks, the row exponent, x' and chunk sums
-  u32x4 raw[CPL][4];
-  uint32_t amax = 0;
+  // 3. x' of this lane's chunks
+  XChunk xc[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int kc = sl + c * lpc;
-    if (kc < nchunk) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) raw[c][b] = *reinterpret_cast<const u32x4*>(p.x + kc * 32 + 8 * b);
-      amax = max(amax, chunk_absmax(raw[c]));
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) raw[c][b] = (u32x4){0u, 0u, 0u, 0u};
-    }
-  }
-  for (int off = lpc >> 1; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-  const int e = row_exponent(amax);
-  uint32_t xv[CPL][16];
-  float sx[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) sx[c] = convert_chunk(raw[c], e, xv[c]);
+  for (int c = 0; c < CPL; ++c) make_x_chunk(raw[c], xc[c]);
 
-  // 3. per column: dot products, group reduction, epilogue
+  // 4. per column: chunk terms, reduction over the column group, epilogue
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       if (sl + c * lpc < nchunk) {
-        ag += chunk_dot<BITS_G>(rg[r][c], xv[c], sx[c]);
-        au += chunk_dot<BITS_U>(ru[r][c], xv[c], sx[c]);
+        ag += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
+        au += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
       }
     }
-    for (int off = lpc >> 1; off > 0; off >>= 1) {
-      ag += __shfl_xor(ag, off);
-      au += __shfl_xor(au, off);
+    if (lpc == 64) {
+      ag = wave_sum(ag);
+      au = wave_sum(au);
+    } else {
+      ag = group_sum(ag, lpc);
+      au = group_sum(au, lpc);
     }
     const int n = (wave_global * R + r) * cpw + sub;
-    if (sl == 0 && n < p.I) store_out(p, 0, n, ldexpf(ag, e), ldexpf(au, e));
+    if (sl == 0 && n < p.I) store_out(p, 0, n, ag, au);
   }
 }
 
