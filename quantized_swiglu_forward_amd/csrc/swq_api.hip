@@ -73,8 +73,10 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
   if (!spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return SWQ_ERR_UNSUPPORTED;
   if (M < 0 || H <= 0 || I <= 0) return SWQ_ERR_SHAPE;
   if (H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0) return SWQ_ERR_SHAPE;
-  // kernels index with 32-bit row/column counters
-  if (M > (1LL << 30) || H > (1LL << 24) || I > (1LL << 30)) return SWQ_ERR_SHAPE;
+  // kernels index rows, columns and tiles with 32-bit counters, and address a
+  // block's rows of x' and of the weights with 32-bit buffer offsets
+  if (M > (1LL << 30) || H > (1LL << 20) || I > (1LL << 30)) return SWQ_ERR_SHAPE;
+  if (((M + 127) / 128) * ((I + 127) / 128) >= (1LL << 31)) return SWQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16)) return SWQ_ERR_ALIGN;
   if (!aligned(sg, 2) || !aligned(bg, 2) || !aligned(su, 2) || !aligned(bu, 2)) return SWQ_ERR_ALIGN;
   return SWQ_OK;
@@ -84,18 +86,19 @@ bool gemv_fits(int64_t M, int64_t H) {
   return M >= 1 && M <= kGemvMaxM && gemv_lds_bytes(M, H) <= kGemvLdsBytes;
 }
 
+// Row tile of the MFMA kernel: 256 rows unless that leaves CUs idle (fewer
+// than two tiles per CU of the 256), then 128.
 int choose_mfma_config(int64_t M, int64_t I) {
-  (void)M;
-  (void)I;
-  return 0;
+  const int64_t ntiles = (I + kMfmaBN - 1) / kMfmaBN;
+  const int64_t tiles256 = ((M + 255) / 256) * ntiles;
+  return tiles256 >= 512 ? 0 : 1;
 }
 
 // Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
 // (binary16), row exponents [M] (int32), then the extra-column B rows
-// [I, kext] (binary16) of the gate, of its second plane (8-bit gate only),
-// of the up matrix and of its second plane (8-bit up only).
+// [I, kext] (binary16) of the gate and of the up matrix.
 struct WsLayout {
-  int64_t xa, xexp, eg, eg2, eu, eu2, total;
+  int64_t xa, xexp, eg, eu, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -107,10 +110,10 @@ WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bi
   w.xa = 0;
   w.xexp = align256(M * (H + kext) * 2);
   w.eg = w.xexp + align256(M * 4);
-  w.eg2 = w.eg + plane;
-  w.eu = w.eg2 + (bits_g == 8 ? plane : 0);
-  w.eu2 = w.eu + plane;
-  w.total = w.eu2 + (bits_u == 8 ? plane : 0);
+  w.eu = w.eg + plane;
+  w.total = w.eu + plane;
+  (void)bits_g;
+  (void)bits_u;
   return w;
 }
 
@@ -179,9 +182,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   _Float16* xa = (_Float16*)(wsb + L.xa);
   int* xexp = (int*)(wsb + L.xexp);
   _Float16* eg = (_Float16*)(wsb + L.eg);
-  _Float16* eg2 = bits_g == 8 ? (_Float16*)(wsb + L.eg2) : nullptr;
   _Float16* eu = (_Float16*)(wsb + L.eu);
-  _Float16* eu2 = bits_u == 8 ? (_Float16*)(wsb + L.eu2) : nullptr;
 
   PrepParams pp;
   pp.x = (const uint16_t*)x;
@@ -191,22 +192,21 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
   pp.g0 = g0; pp.ldx = ldx; pp.kext = kext;
   pp.xa = xa; pp.xexp = xexp;
-  pp.bext_g = eg; pp.bext_g2 = eg2; pp.bext_u = eu; pp.bext_u2 = eu2;
+  pp.bext_g = eg; pp.bext_u = eu;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;
-  p.wg = Wg; p.sg = (const uint16_t*)sg; p.bg = (const uint16_t*)bg;
-  p.wu = Wu; p.su = (const uint16_t*)su; p.bu = (const uint16_t*)bu;
+  p.wg = Wg; p.sg = (const uint16_t*)sg;
+  p.wu = Wu; p.su = (const uint16_t*)su;
   p.M = (int)M; p.H = (int)H; p.I = (int)I;
-  p.gs_g = gs_g; p.gs_u = gs_u; p.g0 = g0;
+  p.gs_g = gs_g; p.gs_u = gs_u;
   p.ldx = ldx; p.kext = kext;
-  p.bext_g = eg; p.bext_g2 = eg2; p.bext_u = eu; p.bext_u2 = eu2;
-  p.ext_plane = (int)(L.eg2 - L.eg);
+  p.bext_g = eg; p.bext_u = eu;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
   const int cfg = choose_mfma_config(M, I);
   if (logging())
     fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
-            cfg, kMfmaBM[cfg], kMfmaBN[cfg], (long long)M, (long long)H, (long long)I, bits_g, bits_u,
+            cfg, kMfmaBM[cfg], kMfmaBN, (long long)M, (long long)H, (long long)I, bits_g, bits_u,
             gs_g, gs_u, mode);
   (void)hipGetLastError();
   if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
@@ -248,7 +248,7 @@ int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const
 int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode) {
   if (!spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
   if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return 0;
-  if (H <= 0 || H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0 || H > (1LL << 24)) return 0;
+  if (H <= 0 || H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0 || H > (1LL << 20)) return 0;
   return 1;
 }
 

@@ -6,7 +6,8 @@
 
 namespace swq {
 
-// Row staging of x for the matrix-matrix path.
+// Row staging of x for the matrix-matrix path, and the extra-column rows
+// that carry the per-group bias term.
 struct PrepParams {
   const uint16_t* x;   // bf16 [M, H]
   const uint16_t* sg;  // scales and biases of both matrices (bf16 [I, H/gs])
@@ -17,13 +18,11 @@ struct PrepParams {
   int gs_g, gs_u, bits_g, bits_u;
   int g0;              // min(gs_g, gs_u): granularity of the group sums
   int ldx;             // row pitch of xa in halves: H + kext
-  int kext;            // extra K columns: 4 per g0-group, padded to 32
+  int kext;            // extra K columns: 3 per g0-group, padded to 32
   _Float16* xa;        // out: [M, ldx]
   int* xexp;           // out: [M] row exponents e (x' = x * 2^-e)
-  _Float16* bext_g;    // out: [I, kext] extra-column B rows of the gate (b, b, 8s, 8s)
-  _Float16* bext_g2;   // out: [I, kext] second plane (128s, 128s, 0, 0), 8-bit gate only
+  _Float16* bext_g;    // out: [I, kext] extra-column B rows of the gate (c_hi, c_lo, c_hi per group)
   _Float16* bext_u;    // out: same for the up matrix
-  _Float16* bext_u2;
 };
 
 struct MfmaParams {
@@ -31,18 +30,13 @@ struct MfmaParams {
   const int* xexp;
   const uint32_t* wg;
   const uint16_t* sg;
-  const uint16_t* bg;
   const uint32_t* wu;
   const uint16_t* su;
-  const uint16_t* bu;
   int M, H, I;
-  int gs_g, gs_u, g0;
+  int gs_g, gs_u;
   int ldx, kext;
   const _Float16* bext_g;
-  const _Float16* bext_g2;
   const _Float16* bext_u;
-  const _Float16* bext_u2;
-  int ext_plane;       // bytes from a first extra-column plane to its second plane
   int mode;
   void* out;
   float* dbg_g;        // non-null: write float32 gate/up instead of hidden
@@ -65,10 +59,10 @@ struct GemvParams {
   float* dbg_u;
 };
 
-// Number of MFMA tile configurations and their shapes (rows, columns per matrix).
-constexpr int kMfmaConfigs = 1;
-constexpr int kMfmaBM[kMfmaConfigs] = {256};
-constexpr int kMfmaBN[kMfmaConfigs] = {128};
+// Row-tile heights of the MFMA kernel (the column tile is 128 per matrix).
+constexpr int kMfmaConfigs = 2;
+constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
+constexpr int kMfmaBN = 128;
 
 // Largest M the matrix-vector kernel takes, and its LDS budget for x.
 constexpr int kGemvMaxM = 16;
@@ -80,7 +74,7 @@ inline int64_t gemv_lds_bytes(int64_t M, int64_t H) {
 }
 
 inline int kext_columns(int64_t H, int g0) {
-  const int64_t c = 4 * (H / g0);
+  const int64_t c = 3 * (H / g0);
   return (int)((c + 31) / 32 * 32);
 }
 

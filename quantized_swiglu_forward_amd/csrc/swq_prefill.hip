@@ -1,27 +1,34 @@
 // Matrix-matrix path (M >= threshold) of the fused quantized SwiGLU:
 //   hidden[M, I] = silu(x Wg^T) * (x Wu^T)
-// One dispatch produces a BM x BN tile of BOTH projections from one staged
+// One dispatch produces a BM x 128 tile of BOTH projections from one staged
 // x tile, then applies the epilogue in registers ("mlx-bun 0.0.7 -> 0.0.9"
 // diff, page 42, fused-swiglu-kernel.ts: header comment and kernel source,
 // where x is read once for two GEMMs and down_proj stays separate).
+//
+// Exactness.  A weight w = s*q + b is split as  s*(q - z) + c  with
+// c = b + z*s per group (z = 8 for 4-bit codes; for 8-bit codes
+// q = 16 hi + lo and s*q = 16s*(hi - 8) + s*(lo - 8) + 136 s).  Every
+// s*(code - 8) is exact in binary16 (a bf16 scale has 8 significant bits, the
+// offset code at most 4), so the K loop runs on f16 MFMA with exact products
+// and float32 accumulation.  The constant part sum_g Sx[m,g] * c[n,g] runs on
+// the same MFMAs as extra K columns: the group sum of x' (float32) split into
+// binary16 hi + lo, against c split into binary16 c_hi + c_lo, three columns
+// per group: (hi, hi, lo) x (c_hi, c_lo, c_hi); the dropped lo*c_lo term is
+// below 2^-22 of the group term.
 //
 // Two kernels:
 //  1. swq_prep_kernel.  Blocks [0, M): one row of x each.  It picks a
 //     power-of-two row scale 2^-e so that max|x'| lies in [1, 2), writes
 //     x' = x * 2^-e as binary16 in the [0,4,1,5,2,6,3,7] order that matches
-//     the dequantized weight pairs, and appends, per group of
-//     g0 = min(gs_g, gs_u) inputs, the group sum Sx of x' split as hi + lo
-//     binary16 values, in four extra K columns (hi, lo, hi, lo).  Every bf16
+//     the dequantized weight pairs, and appends the extra columns
+//     (hi, hi, lo) of every group of g0 = min(gs_g, gs_u) inputs.  Every bf16
 //     x whose magnitude is at least 2^-17 of the row maximum converts
-//     exactly.  The remaining blocks write the B rows of those extra
-//     columns for every output feature: (b, b, 8s, 8s) per group (exact in
-//     binary16), and for an 8-bit matrix a second plane (128s, 128s, 0, 0),
-//     so that the extra columns add sum_g Sx[m,g] * (b[n,g] + z*s[n,g]).
-//  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators.  The K
-//     loop streams the packed codes, dequantizes them to the exact binary16
-//     values s*(q - z) and feeds them to the MFMA, then runs over the extra
-//     columns.  The epilogue multiplies by 2^e (exact), then computes
-//     silu(g) * u per precision mode.
+//     exactly.  The remaining blocks write, for every output feature and
+//     matrix, the extra-column B rows (c_hi, c_lo, c_hi).
+//  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators over the
+//     H columns (packed codes, dequantized in registers) and then the extra
+//     columns (precomputed binary16 rows); epilogue 2^e, then silu(g) * u per
+//     precision mode.
 #include "swq_device.h"
 #include "swq_kernels.h"
 
@@ -92,40 +99,48 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
       const int g = c / gchunks;
       const _Float16 hi = (_Float16)part;
       const _Float16 lo = (_Float16)(part - (float)hi);
-      *reinterpret_cast<f16x2*>(ext + 4 * g) = (f16x2){hi, lo};
-      *reinterpret_cast<f16x2*>(ext + 4 * g + 2) = (f16x2){hi, lo};
+      ext[3 * g] = hi;
+      ext[3 * g + 1] = hi;
+      ext[3 * g + 2] = lo;
     }
   }
   // zero padding of the extra columns
-  for (int k = 4 * ngroups + tid; k < p.kext; k += 256) ext[k] = (_Float16)0.0f;
+  for (int k = 3 * ngroups + tid; k < p.kext; k += 256) ext[k] = (_Float16)0.0f;
 }
 
-// B rows of the extra columns for one matrix: thread (n, G) writes columns
-// [4G, 4G+4) of row n (zeros in the padding).
-__device__ __forceinline__ void prep_ext_rows(const uint16_t* S, const uint16_t* B, int gs, int bits, int g0,
-                                              int H, int I, int kext, _Float16* lo, _Float16* hi,
-                                              int64_t idx) {
-  const int per_row = kext / 4;
-  if (idx >= (int64_t)I * per_row) return;
-  const int n = (int)(idx / per_row), G = (int)(idx % per_row);
-  f16x2 v0 = {(_Float16)0.0f, (_Float16)0.0f}, v1 = v0, h0 = v0;
-  if (G < H / g0) {
-    const int g = G * g0 / gs;
-    const int ng = H / gs;
-    const float b = bf16_to_f32(B[(int64_t)n * ng + g]);
-    const float s = bf16_to_f32(S[(int64_t)n * ng + g]);
-    const _Float16 bb = (_Float16)b, s8 = (_Float16)(8.0f * s), s128 = (_Float16)(128.0f * s);
-    v0 = (f16x2){bb, bb};
-    v1 = (f16x2){s8, s8};
-    h0 = (f16x2){s128, s128};
+// Extra-column B row piece: thread (n, j) writes columns [32j, 32j + 32) of
+// row n of one matrix: (c_hi, c_lo, c_hi) per g0-group, c = b + z*s exactly
+// in float32 (b and z*s are bf16 values times small powers of two and 17),
+// zeros in the padding.
+__device__ __forceinline__ void prep_ext_piece(const uint16_t* S, const uint16_t* B, int gs, int bits, int g0,
+                                               int ngroups, int kext, _Float16* dst, int64_t n, int j) {
+  const int ng = ngroups * g0 / gs;                 // groups of this matrix per row
+  const float z = bits == 8 ? 136.0f : 8.0f;
+  f16x8 out[4];
+  int gprev = -1;
+  _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int k = 32 * j + t;
+    const int G = k / 3, role = k - 3 * G;
+    _Float16 v = (_Float16)0.0f;
+    if (G < ngroups) {
+      const int g = G * g0 / gs;
+      if (g != gprev) {
+        const float s = bf16_to_f32(S[n * ng + g]);
+        const float b = bf16_to_f32(B[n * ng + g]);   // n * ng is int64
+        const float c = fmaf(z, s, b);
+        chi = (_Float16)c;
+        clo = (_Float16)(c - (float)chi);
+        gprev = g;
+      }
+      v = role == 1 ? clo : chi;
+    }
+    out[t / 8][t % 8] = v;
   }
-  const int64_t o = (int64_t)n * kext + 4 * G;
-  *reinterpret_cast<f16x2*>(lo + o) = v0;
-  *reinterpret_cast<f16x2*>(lo + o + 2) = v1;
-  if (bits == 8) {
-    *reinterpret_cast<f16x2*>(hi + o) = h0;
-    *reinterpret_cast<f16x2*>(hi + o + 2) = (f16x2){(_Float16)0.0f, (_Float16)0.0f};
-  }
+  f16x8* d = reinterpret_cast<f16x8*>(dst + (int64_t)n * kext + 32 * j);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = out[q];
 }
 
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
@@ -133,40 +148,95 @@ __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
     prep_x_row(p, blockIdx.x);
     return;
   }
+  const int per_row = p.kext / 32;
   const int64_t idx = (int64_t)(blockIdx.x - p.M) * 256 + threadIdx.x;
-  const int64_t per_mat = (int64_t)p.I * (p.kext / 4);
-  if (idx < per_mat)
-    prep_ext_rows(p.sg, p.bg, p.gs_g, p.bits_g, p.g0, p.H, p.I, p.kext, p.bext_g, p.bext_g2, idx);
-  else
-    prep_ext_rows(p.su, p.bu, p.gs_u, p.bits_u, p.g0, p.H, p.I, p.kext, p.bext_u, p.bext_u2, idx - per_mat);
+  const int64_t per_mat = (int64_t)p.I * per_row;
+  const int ngroups = p.H / p.g0;
+  if (idx < per_mat) {
+    prep_ext_piece(p.sg, p.bg, p.gs_g, p.bits_g, p.g0, ngroups, p.kext, p.bext_g, idx / per_row,
+                   (int)(idx % per_row));
+  } else if (idx < 2 * per_mat) {
+    const int64_t i2 = idx - per_mat;
+    prep_ext_piece(p.su, p.bu, p.gs_u, p.bits_u, p.g0, ngroups, p.kext, p.bext_u, i2 / per_row,
+                   (int)(i2 % per_row));
+  }
 }
 
 // ----------------------------------------------------------- MFMA GEMM ----
 //
-// Work split.  A block of four wavefronts (one per SIMD) computes a 256 x 128
-// tile of both projections.  Wave (wm, wn) owns rows [128 wm, 128 wm + 128)
-// and columns [64 wn, 64 wn + 64) of the gate AND the up tile: 4 x 2 MFMA
-// 32x32x16 fragments per matrix, 256 float32 accumulators per lane.
-//  * x' (the A operand) goes through a 3-stage LDS ring; its global loads are
-//    issued two K-steps ahead and written to LDS one K-step ahead.
-//  * The B side is staged in LDS per super-step: four K-steps of packed codes
-//    (64 or 128 bytes per row) with their scales, or one K-step of the
-//    precomputed extra-column rows (64 bytes per plane).  Rows are read as
-//    whole segments, one super-step ahead.  Each lane then reads the codes
-//    of its columns and two 8-code blocks from LDS and dequantizes them in
-//    registers just before the MFMA: lane l holds column l%32 and blocks
-//    2(l/32), 2(l/32)+1 of the 32-wide K-step, one per MFMA k16 step (A is
-//    read for the same blocks).
-//  * Global accesses are buffer loads: per-lane offsets fixed for the whole
-//    loop, the K position as a scalar offset.
+// Work split.  A block of four wavefronts (one per SIMD) computes a BM x 128
+// tile of both projections.  Wave w owns all BM rows and columns
+// [32w, 32w + 32) of the gate AND the up tile: BM/32 MFMA 32x32x16
+// fragments per matrix.  Each column's codes are dequantized by exactly one
+// wave; every A fragment read from LDS feeds the gate and the up MFMA.
+//
+// Staging.  A ring of four LDS stages, each holding one K-step of 32: the x'
+// tile (BM rows x 64 bytes) and the B side (packed codes of both matrices, or
+// for the extra-column steps their binary16 rows).  Global data goes
+// straight to LDS with buffer loads that write LDS (no VGPR round trip),
+// issued three K-steps ahead; one barrier per K-step.  Rows of 64 bytes are
+// stored as four 16-byte chunks permuted by (row >> 2) & 3, so the MFMA
+// operand reads (32 rows, one chunk) spread over all banks.
+//
+// Software pipeline per K-step t (two k16 sub-steps): while the MFMAs of one
+// sub-step run, the A fragments of the next are read from LDS and its codes
+// dequantized in registers (lane l: column l % 32, 8-code blocks
+// 2 (l / 32) + ks, the MFMA's own K order).
+//
+// Tile order: blocks are dealt round-robin to the 8 XCDs; the kernel remaps
+// them so that each XCD runs a contiguous range of logical tiles, grouped four
+// (or eight) row tiles at a time, so the tiles running together on one XCD
+// share x' rows and weight rows in its L2.
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer descriptor in scalar registers: base, no stride, `bytes` records
+// (hardware bounds check: reads past the end return zero).
+__device__ __forceinline__ i32x4 make_srsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 
-// Dequantized B operands of one k-block (8 codes) of one matrix.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uint64_t)(lds_ptr_t)p;
+}
+
+// Buffer loads that write LDS: lane i's data lands at base + 16 i (16-byte
+// loads) or base + 4 i (2-byte loads, zero-extended).  They are issued from
+// inline assembly so that the compiler does not serialise every later LDS
+// read behind them (it cannot tell the stages apart); the kernel orders them
+// itself with explicit vmcnt waits and barriers.  m0 carries the LDS base.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds_base), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(i32x4 rs, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+               ::"s"(lds_base), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Barrier without the memory fence of __syncthreads (which would wait for the
+// loads in flight for later stages); the asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Dequantized B operands of one k16 sub-step (one 8-code block per lane) of one matrix.
 template <int BITS>
-__device__ __forceinline__ void code_operands(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1) {
+__device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1) {
   if (BITS == 4) {
     uint32_t o[4];
     dequant4(w[0], s2, o);
@@ -186,317 +256,278 @@ __device__ __forceinline__ void code_operands(const uint32_t* w, f16x2 s2, f16x8
   }
 }
 
-template <int BITS_G, int BITS_U>
+template <int BITS_G, int BITS_U, int BM>
 __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
-  constexpr int NT = 256;
-  constexpr int BM = 256, BN = 128;
-  constexpr int LDK = 40;                        // A row pitch in halves (80 bytes)
-  constexpr int A_IT = BM * 4 / NT;              // 16-byte x' chunks per thread per step
-  constexpr int RBG = BITS_G * 16, RBU = BITS_U * 16;   // staged bytes per row per super-step
-  constexpr int PG = RBG + 16, PU = RBU + 16;           // LDS row pitches
-  constexpr int CHG = RBG / 16, CHU = RBU / 16;         // 16-byte pieces per row
-  constexpr int SS_CH = BN * (CHG + CHU);
-  constexpr int SS_IT = SS_CH / NT;
-  constexpr int IT_G = BN * CHG / NT;            // slots [0, IT_G) stage gate rows, the rest up rows
-  static_assert(SS_IT * NT == SS_CH && IT_G * NT == BN * CHG, "staged pieces must divide evenly");
-  static_assert(A_IT * NT == BM * 4, "x' chunks must divide evenly");
+  constexpr int NT = 256, BN = 128, STAGES = 4;
+  constexpr int MF = BM / 32;                          // A fragments per wave
+  constexpr int A_BYTES = BM * 64;                     // x' rows of one K-step
+  constexpr int B_BYTES = 2 * BN * 64;                 // extra-column rows of both matrices
+  constexpr int S_BYTES = 2 * BN * 4;                  // one scale per row and matrix, a dword each
+  constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  constexpr int CG = BITS_G * 4, CU = BITS_U * 4;      // code bytes per row per K-step
+  constexpr int GATE_CHUNKS = BN * CG / 16;            // 16-byte pieces of gate codes per K-step
+  constexpr int CODE_CHUNKS = BN * (CG + CU) / 16;
+  constexpr int A_INSTR = BM * 4 / NT;
+  constexpr int B_CODE_INSTR = (CODE_CHUNKS + NT - 1) / NT;
+  constexpr int B_EXT_INSTR = B_BYTES / 16 / NT;
+  constexpr int N_MAIN = A_INSTR + B_CODE_INSTR + 1;   // buffer loads a thread issues per K-step
+  constexpr int N_EXT = A_INSTR + B_EXT_INSTR + 1;
+  constexpr int GM = BM == 256 ? 4 : 8;                // row tiles per group of the tile order
+  static_assert(GATE_CHUNKS % 64 == 0 && CODE_CHUNKS % 64 == 0, "a wave's DMA stays in one matrix");
+  static_assert(B_CODE_INSTR * NT - CODE_CHUNKS <= BN * CU / 16, "duplicate DMA pieces are up pieces");
+  static_assert(BM <= NT, "one row exponent per thread");
 
-  __shared__ __attribute__((aligned(16))) _Float16 As[3][BM * LDK];
-  __shared__ __attribute__((aligned(16))) unsigned char Bq[2][BN * (PG + PU)];
-  __shared__ __attribute__((aligned(16))) uint16_t Sq[2][2][BN * 4];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
+  __shared__ int rexp[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform (scalar)
   const int half = lane >> 5, l32 = lane & 31;
 
-  // XCD-aware tile order: consecutive tiles land on the same XCD (blocks are
-  // dealt round-robin to the 8 XCDs); within an XCD's range the row tile
-  // varies fastest, so concurrent blocks share weights and x' in its L2.
+  // ---- tile of this block
   const int T = gridDim.x;
   const int q8 = T / 8, r8 = T % 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int logical = xcd < r8 ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
-  const int mtiles = (p.M + BM - 1) / BM;
-  const int m0 = (logical % mtiles) * BM;
-  const int n0 = (logical / mtiles) * BN;
+  const int mtiles = (p.M + BM - 1) / BM, ntiles = (p.I + BN - 1) / BN;
+  const int per_group = GM * ntiles;
+  const int grp = logical / per_group;
+  const int first_m = grp * GM;
+  const int gsz = min(mtiles - first_m, GM);
+  const int in_grp = logical - grp * per_group;
+  const int m0 = (first_m + in_grp % gsz) * BM;
+  const int n0 = (in_grp / gsz) * BN;
   const int rows = min(BM, p.M - m0);
   const int cols = min(BN, p.I - n0);
 
-  const int s_main = p.H / 32;                   // multiple of 1; super-steps of 4
-  const int s_ext = p.kext / 32;
+  const int s_main = p.H / 32;
+  const int s_total = s_main + p.kext / 32;
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
   const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
 
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.xa + (int64_t)m0 * p.ldx, (uint32_t)rows * p.ldx * 2);
-  const __amdgpu_buffer_rsrc_t rs_wg = make_rsrc(p.wg + (int64_t)n0 * rw_g, (uint32_t)cols * rw_g * 4);
-  const __amdgpu_buffer_rsrc_t rs_wu = make_rsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols * rw_u * 4);
-  const __amdgpu_buffer_rsrc_t rs_sg = make_rsrc(p.sg + (int64_t)n0 * ng_g, (uint32_t)cols * ng_g * 2);
-  const __amdgpu_buffer_rsrc_t rs_su = make_rsrc(p.su + (int64_t)n0 * ng_u, (uint32_t)cols * ng_u * 2);
-  // the second plane of an 8-bit matrix follows its first plane at p.ext_plane bytes
-  const uint32_t ebytes = (uint32_t)cols * p.kext * 2;
-  const __amdgpu_buffer_rsrc_t rs_eg =
-      make_rsrc(p.bext_g + (int64_t)n0 * p.kext, ebytes + (BITS_G == 8 ? (uint32_t)p.ext_plane : 0u));
-  const __amdgpu_buffer_rsrc_t rs_eu =
-      make_rsrc(p.bext_u + (int64_t)n0 * p.kext, ebytes + (BITS_U == 8 ? (uint32_t)p.ext_plane : 0u));
+  const i32x4 rs_a = make_srsrc(p.xa + (int64_t)m0 * p.ldx, (uint32_t)rows * p.ldx * 2);
+  const i32x4 rs_wg = make_srsrc(p.wg + (int64_t)n0 * rw_g, (uint32_t)cols * rw_g * 4);
+  const i32x4 rs_wu = make_srsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols * rw_u * 4);
+  const i32x4 rs_sg = make_srsrc(p.sg + (int64_t)n0 * ng_g, (uint32_t)cols * ng_g * 2);
+  const i32x4 rs_su = make_srsrc(p.su + (int64_t)n0 * ng_u, (uint32_t)cols * ng_u * 2);
+  const i32x4 rs_eg = make_srsrc(p.bext_g + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
+  const i32x4 rs_eu = make_srsrc(p.bext_u + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
 
-  uint32_t aoff[A_IT];
+  // ---- per-thread DMA offsets (bytes)
+  // A: LDS piece L = j*NT + tid holds row L/4, chunk (L%4) ^ ((row>>2)&3)
+  uint32_t a_voff[A_INSTR];
 #pragma unroll
-  for (int it = 0; it < A_IT; ++it) {
-    const int c = tid + it * NT;
-    aoff[it] = (uint32_t)((min(c >> 2, rows - 1) * p.ldx + (c & 3) * 8) * 2);
+  for (int j = 0; j < A_INSTR; ++j) {
+    const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
+    a_voff[j] = (uint32_t)(row * p.ldx * 2 + c * 16);
   }
-  // staged B piece it of this thread: (matrix, row, 16-byte part)
-  uint32_t qoff[SS_IT];
+  // B codes: LDS piece L < GATE_CHUNKS is gate row L/(CG/16) part L%(CG/16), then up rows;
+  // pieces past CODE_CHUNKS repeat up pieces (same data to the same place)
+  uint32_t c_voff[B_CODE_INSTR];
 #pragma unroll
-  for (int it = 0; it < SS_IT; ++it) {
-    const bool g = it < IT_G;
-    const int cc = g ? tid + it * NT : tid + (it - IT_G) * NT;
-    const int per = g ? CHG : CHU;
-    const int row = min(cc / per, cols - 1), part = cc % per;
-    qoff[it] = (uint32_t)(row * (g ? rw_g : rw_u) * 4 + part * 16);
+  for (int j = 0; j < B_CODE_INSTR; ++j) {
+    int L = j * NT + tid;
+    if (L >= CODE_CHUNKS) L -= BN * CU / 16;
+    if (L < GATE_CHUNKS) c_voff[j] = (uint32_t)((L / (CG / 16)) * rw_g * 4 + (L % (CG / 16)) * 16);
+    else c_voff[j] = (uint32_t)(((L - GATE_CHUNKS) / (CU / 16)) * rw_u * 4 + ((L - GATE_CHUNKS) % (CU / 16)) * 16);
   }
-  // scale staging: thread t owns (matrix t / BN, row t % BN); uniform per wave
-  const bool s_gate = __builtin_amdgcn_readfirstlane(tid) < BN;
-  const int s_row = tid % BN;
-  const uint32_t s_off = (uint32_t)(min(s_row, cols - 1) * (s_gate ? ng_g : ng_u) * 2);
-  const int s_gs = s_gate ? p.gs_g : p.gs_u;
-
-  f32x16 acc_g[4][2], acc_u[4][2];
+  // B extra columns: piece L: matrix L/512, row (L%512)/4, chunk (L%4) ^ ((row>>2)&3)
+  uint32_t e_voff[B_EXT_INSTR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc_g[i][j][r] = 0.0f;
-        acc_u[i][j][r] = 0.0f;
-      }
-
-  u32x4 ra[3][A_IT];
-  u32x4 qs[SS_IT];          // staged codes of the next super-step
-  uint32_t ss_s[4];         // staged scales of the next super-step
-
-  // ---- loads (unconditional: past-the-end loads are harmless and unused)
-  auto issue_a = [&](int kcol, u32x4 (&a)[A_IT]) {
-#pragma unroll
-    for (int it = 0; it < A_IT; ++it) a[it] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoff[it], kcol * 2, 0);
-  };
-  auto issue_ss = [&](int ss) {
-#pragma unroll
-    for (int it = 0; it < SS_IT; ++it) {
-      if (it < IT_G) qs[it] = __builtin_amdgcn_raw_buffer_load_b128(rs_wg, qoff[it], ss * RBG, 0);
-      else qs[it] = __builtin_amdgcn_raw_buffer_load_b128(rs_wu, qoff[it], ss * RBU, 0);
-    }
-    const int g0i = (ss * 128) / s_gs;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      ss_s[q] = s_gate ? __builtin_amdgcn_raw_buffer_load_b16(rs_sg, s_off, (g0i + q) * 2, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b16(rs_su, s_off, (g0i + q) * 2, 0);
-  };
-  auto write_ss = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < SS_IT; ++it) {
-      const bool g = it < IT_G;
-      const int cc = g ? tid + it * NT : tid + (it - IT_G) * NT;
-      const int per = g ? CHG : CHU;
-      const int row = cc / per, part = cc % per;
-      const int o = g ? row * PG + part * 16 : BN * PG + row * PU + part * 16;
-      *reinterpret_cast<u32x4*>(&Bq[buf][o]) = qs[it];
-    }
-    uint16_t* d = &Sq[buf][s_gate ? 0 : 1][s_row * 4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = (uint16_t)ss_s[q];
-  };
-  auto write_a = [&](int stage, const u32x4 (&a)[A_IT]) {
-#pragma unroll
-    for (int it = 0; it < A_IT; ++it) {
-      const int c = tid + it * NT;
-      *reinterpret_cast<u32x4*>(&As[stage][(c >> 2) * LDK + (c & 3) * 8]) = a[it];
-    }
-  };
-
-  auto mfma4 = [&](const f16x8 (&a)[4], int f, const f16x8& bg0, const f16x8& bg1, const f16x8& bu0,
-                   const f16x8& bu1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bg0, acc_g[i][f], 0, 0, 0);
-      if (BITS_G == 8) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bg1, acc_g[i][f], 0, 0, 0);
-      acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bu0, acc_u[i][f], 0, 0, 0);
-      if (BITS_U == 8) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bu1, acc_u[i][f], 0, 0, 0);
-    }
-  };
-
-  // K-step with sub-step Q (0..3) of super-step buffer BUF, A stage STAGE
-  auto compute_main = [&]<int Q>(int stage, int buf) {
-    const _Float16* abase = &As[stage][(wm * 128 + l32) * LDK];
-    f16x2 sg2[2], su2[2];
-    uint32_t wgv[2][4], wuv[2][4];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int cl = wn * 64 + f * 32 + l32;
-      const unsigned char* qg = &Bq[buf][cl * PG + Q * (BITS_G * 4) + half * (BITS_G * 2)];
-      const unsigned char* qu = &Bq[buf][BN * PG + cl * PU + Q * (BITS_U * 4) + half * (BITS_U * 2)];
-      if (BITS_G == 4) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
-        wgv[f][0] = v[0]; wgv[f][1] = v[1];
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
-        wgv[f][0] = v[0]; wgv[f][1] = v[1]; wgv[f][2] = v[2]; wgv[f][3] = v[3];
-      }
-      if (BITS_U == 4) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
-        wuv[f][0] = v[0]; wuv[f][1] = v[1];
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
-        wuv[f][0] = v[0]; wuv[f][1] = v[1]; wuv[f][2] = v[2]; wuv[f][3] = v[3];
-      }
-      sg2[f] = bf16_to_h2(Sq[buf][0][cl * 4 + (Q * 32) / p.gs_g]);
-      su2[f] = bf16_to_h2(Sq[buf][1][cl * 4 + (Q * 32) / p.gs_u]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = (2 * half + ks) * 8;
-      f16x8 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const f16x8*>(abase + i * 32 * LDK + kk);
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        f16x8 bg0, bg1, bu0, bu1;
-        code_operands<BITS_G>(&wgv[f][ks * (BITS_G / 4)], sg2[f], bg0, bg1);
-        code_operands<BITS_U>(&wuv[f][ks * (BITS_U / 4)], su2[f], bu0, bu1);
-        mfma4(a, f, bg0, bg1, bu0, bu1);
-      }
-    }
-  };
-
-  // main K-step t = 12*it + K (K static): A stage K%3, super-step sub-step K%4
-  auto main_step = [&]<int K>(int t) {
-    constexpr int U = K % 3, Q = K % 4;
-    __syncthreads();
-    issue_a((t + 2) * 32, ra[(U + 2) % 3]);
-    const int j = t >> 2;                      // super-step of this K-step
-    if constexpr (Q == 0) issue_ss(j + 1);
-    compute_main.template operator()<Q>(U, j & 1);
-    write_a((U + 1) % 3, ra[(U + 1) % 3]);
-    if constexpr (Q == 3) write_ss((j + 1) & 1);
-  };
-
-  // prologue: steps 0, 1 of A, super-step 0 of B
-  issue_a(0, ra[0]);
-  issue_a(32, ra[1]);
-  issue_ss(0);
-  write_a(0, ra[0]);
-  write_ss(0);
-  const int full = s_main / 12;
-  int t = 0;
-  for (int it = 0; it < full; ++it, t += 12) {
-    main_step.template operator()<0>(t);
-    main_step.template operator()<1>(t + 1);
-    main_step.template operator()<2>(t + 2);
-    main_step.template operator()<3>(t + 3);
-    main_step.template operator()<4>(t + 4);
-    main_step.template operator()<5>(t + 5);
-    main_step.template operator()<6>(t + 6);
-    main_step.template operator()<7>(t + 7);
-    main_step.template operator()<8>(t + 8);
-    main_step.template operator()<9>(t + 9);
-    main_step.template operator()<10>(t + 10);
-    main_step.template operator()<11>(t + 11);
+  for (int j = 0; j < B_EXT_INSTR; ++j) {
+    const int L = j * NT + tid, row = (L & 511) >> 2, c = (L & 3) ^ ((row >> 2) & 3);
+    e_voff[j] = (uint32_t)(row * p.kext * 2 + c * 16);
   }
-  // tail: the remaining s_main % 12 steps (runs once)
-  {
-    const int rem = s_main - t;
-    if (rem > 0) main_step.template operator()<0>(t);
-    if (rem > 1) main_step.template operator()<1>(t + 1);
-    if (rem > 2) main_step.template operator()<2>(t + 2);
-    if (rem > 3) main_step.template operator()<3>(t + 3);
-    if (rem > 4) main_step.template operator()<4>(t + 4);
-    if (rem > 5) main_step.template operator()<5>(t + 5);
-    if (rem > 6) main_step.template operator()<6>(t + 6);
-    if (rem > 7) main_step.template operator()<7>(t + 7);
-    if (rem > 8) main_step.template operator()<8>(t + 8);
-    if (rem > 9) main_step.template operator()<9>(t + 9);
-    if (rem > 10) main_step.template operator()<10>(t + 10);
-  }
+  const int ncol = 32 * w + l32;                      // this lane's column in the tile
+  // scales: thread t < 128 loads gate row t, thread t >= 128 up row t - 128
+  const uint32_t s_voff = (uint32_t)(tid < BN ? tid * ng_g * 2 : (tid - BN) * ng_u * 2);
 
-  // ---- extra columns of the bias term: A = group sums of x', B = precomputed rows
-  // staged in As[0] and Bq[0] with one step of prefetch
-  {
-    constexpr int EP_G = BITS_G == 8 ? 2 : 1, EP_U = BITS_U == 8 ? 2 : 1;
-    u32x4 ea[A_IT];
-    u32x4 eb[SS_IT];
-    auto issue_e = [&](int e) {
-      issue_a(p.H + e * 32, ea);
-      // 64 bytes per plane-row per step: the same piece layout as the codes
+  // row exponents of the tile: loaded first, published through LDS after the K loop
+  const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;   // BM <= NT
+
+
+  // issue every load of K-step s into its stage (SLOT = s % STAGES)
+  const uint32_t smem0 = lds_addr(smem);
+  auto issue = [&]<int SLOT>(int s) {
+    const uint32_t st = smem0 + SLOT * STAGE;
+    const uint32_t soff_a = (uint32_t)s * 64;
 #pragma unroll
-      for (int it = 0; it < SS_IT; ++it) {
-        const bool g = it < IT_G;
-        const int cc = g ? tid + it * NT : tid + (it - IT_G) * NT;
-        const int per = g ? CHG : CHU;
-        const int row = min(cc / per, cols - 1), part = cc % per;
-        // plane part/4: the second plane starts p.ext_plane bytes after the first
-        const uint32_t off = (uint32_t)(row * p.kext * 2 + (part & 3) * 16 + (part >> 2) * p.ext_plane);
-        if (g) eb[it] = __builtin_amdgcn_raw_buffer_load_b128(rs_eg, off, e * 64, 0);
-        else eb[it] = __builtin_amdgcn_raw_buffer_load_b128(rs_eu, off, e * 64, 0);
+    for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j], soff_a);
+    const uint32_t sb = st + A_BYTES;
+    const uint32_t ss = sb + B_BYTES + w * 64 * 4;
+    if (s < s_main) {
+#pragma unroll
+      for (int j = 0; j < B_CODE_INSTR; ++j) {
+        int L0 = j * NT + w * 64;                      // wave-uniform first piece
+        if (L0 >= CODE_CHUNKS) L0 -= BN * CU / 16;
+        if (L0 < GATE_CHUNKS) dma16(rs_wg, sb + L0 * 16, c_voff[j], (uint32_t)s * CG);
+        else dma16(rs_wu, sb + L0 * 16, c_voff[j], (uint32_t)s * CU);
       }
-    };
-    issue_e(0);
-    for (int e = 0; e < s_ext; ++e) {
-      __syncthreads();                        // previous users of As[0] / Bq[0] are done
-      write_a(0, ea);
+      if (w < 2) dma2(rs_sg, ss, s_voff, (uint32_t)((s * 32) / p.gs_g) * 2);
+      else dma2(rs_su, ss, s_voff, (uint32_t)((s * 32) / p.gs_u) * 2);
+    } else {
+      const uint32_t soff_e = (uint32_t)(s - s_main) * 64;
 #pragma unroll
-      for (int it = 0; it < SS_IT; ++it) qs[it] = eb[it];
-      write_ss(0);
-      __syncthreads();
-      if (e + 1 < s_ext) issue_e(e + 1);
-      const _Float16* abase = &As[0][(wm * 128 + l32) * LDK];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kk = (2 * half + ks) * 8;
-        f16x8 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const f16x8*>(abase + i * 32 * LDK + kk);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int cl = wn * 64 + f * 32 + l32;
-          const unsigned char* rg = &Bq[0][cl * PG];
-          const unsigned char* ru = &Bq[0][BN * PG + cl * PU];
-          const int kb = (2 * half + ks) * 16;
-          const f16x8 bg0 = *reinterpret_cast<const f16x8*>(rg + kb);
-          const f16x8 bu0 = *reinterpret_cast<const f16x8*>(ru + kb);
-          f16x8 bg1 = bg0, bu1 = bu0;
-          if (EP_G == 2) bg1 = *reinterpret_cast<const f16x8*>(rg + 64 + kb);
-          if (EP_U == 2) bu1 = *reinterpret_cast<const f16x8*>(ru + 64 + kb);
-          mfma4(a, f, bg0, bg1, bu0, bu1);
-        }
+      for (int j = 0; j < B_EXT_INSTR; ++j) {
+        const int L0 = j * NT + w * 64;
+        if (L0 < 512) dma16(rs_eg, sb + L0 * 16, e_voff[j], soff_e);
+        else dma16(rs_eu, sb + L0 * 16, e_voff[j], soff_e);
       }
+      dma2(w < 2 ? rs_sg : rs_su, ss, s_voff, 0);      // unused: keeps the per-step load count fixed
     }
-  }
+  };
 
-  // epilogue: lane holds rows 8*(r/4) + 4*(lane/32) + r%4 of column lane%32
+  // wait until at most the loads of K-step s are still in flight
+  auto wait_all_but = [&](int s) {
+    if (s < s_main) wait_vmcnt<N_MAIN>();
+    else wait_vmcnt<N_EXT>();
+  };
+
+  f32x16 acc_g[MF], acc_u[MF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int ocol = n0 + wn * 64 + f * 32 + l32;
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int r = 0; r < 16; ++r) {
+      acc_g[i][r] = 0.0f;
+      acc_u[i][r] = 0.0f;
+    }
+
+  // operand registers of the two sub-steps of a K-step
+  f16x8 a0[MF], a1[MF];
+  f16x8 g0a, g0b, u0a, u0b;       // sub-step 0: gate planes, up planes
+  f16x8 g1a, g1b, u1a, u1b;       // sub-step 1
+  uint32_t cw_g[BITS_G / 2], cw_u[BITS_U / 2];   // this lane's codes of the current K-step
+
+  const uint32_t a_lds0 = (uint32_t)(l32 * 64 + (((2 * half) ^ ((l32 >> 2) & 3)) * 16));
+  const uint32_t a_lds1 = (uint32_t)(l32 * 64 + (((2 * half + 1) ^ ((l32 >> 2) & 3)) * 16));
+  const uint32_t e_lds0 = (uint32_t)(ncol * 64 + (((2 * half) ^ ((l32 >> 2) & 3)) * 16));
+  const uint32_t e_lds1 = (uint32_t)(ncol * 64 + (((2 * half + 1) ^ ((l32 >> 2) & 3)) * 16));
+
+  // A fragments of sub-step ks of K-step s
+  auto read_a = [&]<int SLOT>(int ks, f16x8 (&a)[MF]) {
+    const unsigned char* st = smem + SLOT * STAGE + (ks ? a_lds1 : a_lds0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (row >= p.M || ocol >= p.I) continue;
-        const int e = p.xexp[row];
-        const float g = ldexpf(acc_g[i][f][r], e);
-        const float u = ldexpf(acc_u[i][f][r], e);
-        const int64_t o = (int64_t)row * p.I + ocol;
-        if (p.dbg_g) {
-          p.dbg_g[o] = g;
-          p.dbg_u[o] = u;
+    for (int i = 0; i < MF; ++i) a[i] = *reinterpret_cast<const f16x8*>(st + i * 32 * 64);
+  };
+  // B operands of sub-step ks of K-step s (ks == 0 also fetches the step's codes)
+  auto read_b = [&]<int SLOT>(int s, int ks, f16x8& ga, f16x8& gb, f16x8& ua, f16x8& ub) {
+    const unsigned char* sb = smem + SLOT * STAGE + A_BYTES;
+    if (s < s_main) {
+      if (ks == 0) {
+        const unsigned char* qg = sb + ncol * CG + half * (CG / 2);
+        const unsigned char* qu = sb + BN * CG + ncol * CU + half * (CU / 2);
+        if (BITS_G == 4) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
+          cw_g[0] = v[0]; cw_g[1] = v[1];
         } else {
-          const float h = swiglu_epilogue(g, u, p.mode);
-          if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
-          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
+          cw_g[0] = v[0]; cw_g[1] = v[1]; cw_g[2] = v[2]; cw_g[3] = v[3];
         }
+        if (BITS_U == 4) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
+          cw_u[0] = v[0]; cw_u[1] = v[1];
+        } else {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
+          cw_u[0] = v[0]; cw_u[1] = v[1]; cw_u[2] = v[2]; cw_u[3] = v[3];
+        }
+      }
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(sb + B_BYTES);
+      const f16x2 sg2 = bf16_to_h2((uint16_t)sc[ncol]);
+      const f16x2 su2 = bf16_to_h2((uint16_t)sc[BN + ncol]);
+      dequant_block<BITS_G>(&cw_g[ks * (BITS_G / 4)], sg2, ga, gb);
+      dequant_block<BITS_U>(&cw_u[ks * (BITS_U / 4)], su2, ua, ub);
+    } else {
+      const uint32_t o = ks ? e_lds1 : e_lds0;
+      ga = *reinterpret_cast<const f16x8*>(sb + o);
+      ua = *reinterpret_cast<const f16x8*>(sb + BN * 64 + o);
+    }
+  };
+  auto mfma = [&](bool ext, const f16x8 (&a)[MF], const f16x8& ga, const f16x8& gb, const f16x8& ua,
+                  const f16x8& ub) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      acc_g[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga, acc_g[i], 0, 0, 0);
+      acc_u[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ua, acc_u[i], 0, 0, 0);
+    }
+    if (!ext) {
+      if (BITS_G == 8) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) acc_g[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], gb, acc_g[i], 0, 0, 0);
+      }
+      if (BITS_U == 8) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) acc_u[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ub, acc_u[i], 0, 0, 0);
+      }
+    }
+  };
+
+  // one K-step t with t % STAGES == PH: sub-step (t, 0) while (t, 1) is
+  // prepared from the same stage, then the barrier, then sub-step (t, 1)
+  // while (t+1, 0) is prepared
+  auto step = [&]<int PH>(int t) {
+    constexpr int NX = (PH + 1) % STAGES, IS = (PH + 3) % STAGES;
+    const bool ext = t >= s_main;
+    read_a.template operator()<PH>(1, a1);
+    read_b.template operator()<PH>(t, 1, g1a, g1b, u1a, u1b);
+    mfma(ext, a0, g0a, g0b, u0a, u0b);
+    // stage t+1 complete for every wave, and every wave is done with stage t-1
+    wait_all_but(t + 2);
+    block_barrier();
+    issue.template operator()<IS>(t + 3);
+    read_a.template operator()<NX>(0, a0);
+    read_b.template operator()<NX>(t + 1, 0, g0a, g0b, u0a, u0b);
+    mfma(ext, a1, g1a, g1b, u1a, u1b);
+  };
+
+  // ---- prologue: K-steps 0..2 in flight, step 0 complete, its first operands read
+  issue.template operator()<0>(0);
+  issue.template operator()<1>(1);
+  issue.template operator()<2>(2);
+  if (2 < s_main) {
+    wait_vmcnt<2 * N_MAIN>();
+  } else if (1 < s_main) {
+    wait_vmcnt<N_MAIN + N_EXT>();
+  } else {
+    wait_vmcnt<2 * N_EXT>();
+  }
+  block_barrier();
+  read_a.template operator()<0>(0, a0);
+  read_b.template operator()<0>(0, 0, g0a, g0b, u0a, u0b);
+
+  int t = 0;
+  for (; t + STAGES <= s_total; t += STAGES) {
+    step.template operator()<0>(t);
+    step.template operator()<1>(t + 1);
+    step.template operator()<2>(t + 2);
+    step.template operator()<3>(t + 3);
+  }
+  if (t < s_total) step.template operator()<0>(t);
+  if (t + 1 < s_total) step.template operator()<1>(t + 1);
+  if (t + 2 < s_total) step.template operator()<2>(t + 2);
+  wait_vmcnt<0>();                                   // nothing left in flight at exit
+  if (tid < BM) rexp[tid] = my_exp;
+  __syncthreads();
+
+  // ---- epilogue: lane holds rows 8*(r/4) + 4*half + r%4 of fragment i, column ncol
+  const int ocol = n0 + ncol;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+      if (lr >= rows || ocol >= p.I) continue;
+      const int e = rexp[lr];
+      const float g = ldexpf(acc_g[i][r], e);
+      const float u = ldexpf(acc_u[i][r], e);
+      const int64_t o = (int64_t)(m0 + lr) * p.I + ocol;
+      if (p.dbg_g) {
+        p.dbg_g[o] = g;
+        p.dbg_u[o] = u;
+      } else {
+        const float h = swiglu_epilogue(g, u, p.mode);
+        if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
+        else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
       }
     }
   }
@@ -505,18 +536,23 @@ __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const int64_t ext_threads = 2 * (int64_t)p.I * (p.kext / 4);
+  const int64_t ext_threads = 2 * (int64_t)p.I * (p.kext / 32);
   const int64_t blocks = p.M + (ext_threads + 255) / 256;
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int BG, int BU, int BM>
+static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.I + kMfmaBN - 1) / kMfmaBN);
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM>), dim3(tiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int BG, int BU>
 static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, hipStream_t stream) {
-  (void)cfg;
-  const int tiles = ((p.M + 255) / 256) * ((p.I + 127) / 128);
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU>), dim3(tiles), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (cfg == 1) return launch_mfma_t<BG, BU, 128>(p, stream);
+  return launch_mfma_t<BG, BU, 256>(p, stream);
 }
 
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream) {

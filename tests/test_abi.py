@@ -60,6 +60,9 @@ def _fwd(**kw):
     (dict(I=0), swq.SWQ_ERR_SHAPE),
     (dict(H=96, gs_g=64), swq.SWQ_ERR_SHAPE),
     (dict(H=200, gs_g=32, gs_u=32), swq.SWQ_ERR_SHAPE),
+    (dict(H=(1 << 20) + 64), swq.SWQ_ERR_SHAPE),
+    (dict(M=(1 << 30) + 1), swq.SWQ_ERR_SHAPE),
+    (dict(M=1 << 30, I=1 << 30), swq.SWQ_ERR_SHAPE),
     (dict(x=P + 8), swq.SWQ_ERR_ALIGN),
     (dict(Wg=P + 4), swq.SWQ_ERR_ALIGN),
     (dict(Wu=P + 2), swq.SWQ_ERR_ALIGN),
@@ -132,16 +135,15 @@ def test_strerror_and_version():
 
 
 def test_workspace_bytes():
-    # x' rows of H + extra columns (4 per group of the finer group size,
+    # x' rows of H + extra columns (3 per group of the finer group size,
     # padded to 32) halves, row exponents, then one [I, kext] binary16 plane
-    # of extra-column B rows per matrix, two for an 8-bit matrix
+    # of extra-column B rows per matrix
     def a256(v):
         return (v + 255) // 256 * 256
 
     def expect(M, H, I, bg, gg, bu, gu):
-        ext = (4 * (H // min(gg, gu)) + 31) // 32 * 32
-        planes = (2 if bg == 8 else 1) + (2 if bu == 8 else 1)
-        return a256(M * (H + ext) * 2) + a256(M * 4) + planes * a256(I * ext * 2)
+        ext = (3 * (H // min(gg, gu)) + 31) // 32 * 32
+        return a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2)
 
     assert swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64) == expect(512, 2048, 8192, 4, 64, 4, 64)
     assert swq.swiglu_q_workspace_bytes(8192, 2560, 10240, 8, 32, 4, 64) == expect(8192, 2560, 10240, 8, 32, 4, 64)
