@@ -86,11 +86,16 @@ bool gemv_fits(int64_t M, int64_t H) {
   return M >= 1 && M <= kGemvMaxM && gemv_lds_bytes(M, H) <= kGemvLdsBytes;
 }
 
-// Row tile of the MFMA kernel: 256 rows unless that leaves CUs idle (fewer
-// than two tiles per CU of the 256), then 128.
+// Tile shape of the MFMA kernel: 256 x 128 unless that leaves CUs idle
+// (fewer than two tiles per CU of the 256), then 128 x 128.  The environment
+// variable SWIGLU_Q_MFMA_CFG (0 .. kMfmaConfigs-1) overrides the choice.
 int choose_mfma_config(int64_t M, int64_t I) {
-  const int64_t ntiles = (I + kMfmaBN - 1) / kMfmaBN;
-  const int64_t tiles256 = ((M + 255) / 256) * ntiles;
+  if (const char* s = getenv("SWIGLU_Q_MFMA_CFG")) {
+    char* end = nullptr;
+    const long v = strtol(s, &end, 10);
+    if (end != s && v >= 0 && v < kMfmaConfigs) return (int)v;
+  }
+  const int64_t tiles256 = ((M + 255) / 256) * ((I + 127) / 128);
   return tiles256 >= 512 ? 0 : 1;
 }
 
@@ -206,7 +211,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   const int cfg = choose_mfma_config(M, I);
   if (logging())
     fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
-            cfg, kMfmaBM[cfg], kMfmaBN, (long long)M, (long long)H, (long long)I, bits_g, bits_u,
+            cfg, kMfmaBM[cfg], kMfmaBN[cfg], (long long)M, (long long)H, (long long)I, bits_g, bits_u,
             gs_g, gs_u, mode);
   (void)hipGetLastError();
   if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;

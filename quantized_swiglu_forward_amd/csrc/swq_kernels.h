@@ -59,10 +59,10 @@ struct GemvParams {
   float* dbg_u;
 };
 
-// Row-tile heights of the MFMA kernel (the column tile is 128 per matrix).
-constexpr int kMfmaConfigs = 2;
-constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
-constexpr int kMfmaBN = 128;
+// Tile shapes of the MFMA kernel: rows, and columns per matrix.
+constexpr int kMfmaConfigs = 5;
+constexpr int kMfmaBM[kMfmaConfigs] = {256, 128, 128, 128, 64};
+constexpr int kMfmaBN[kMfmaConfigs] = {128, 128, 128, 256, 256};
 
 // Largest M the matrix-vector kernel takes, and its LDS budget for x.
 constexpr int kGemvMaxM = 16;

@@ -108,39 +108,26 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   for (int k = 3 * ngroups + tid; k < p.kext; k += 256) ext[k] = (_Float16)0.0f;
 }
 
-// Extra-column B row piece: thread (n, j) writes columns [32j, 32j + 32) of
-// row n of one matrix: (c_hi, c_lo, c_hi) per g0-group, c = b + z*s exactly
+// Extra-column B rows: thread (n, G) writes columns 3G, 3G+1, 3G+2 of row n
+// of one matrix, (c_hi, c_lo, c_hi) for g0-group G with c = b + z*s exactly
 // in float32 (b and z*s are bf16 values times small powers of two and 17),
-// zeros in the padding.
-__device__ __forceinline__ void prep_ext_piece(const uint16_t* S, const uint16_t* B, int gs, int bits, int g0,
-                                               int ngroups, int kext, _Float16* dst, int64_t n, int j) {
-  const int ng = ngroups * g0 / gs;                 // groups of this matrix per row
-  const float z = bits == 8 ? 136.0f : 8.0f;
-  f16x8 out[4];
-  int gprev = -1;
+// zeros past the last group (the padding up to kext).
+__device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t* B, int gs, int bits, int g0,
+                                               int ngroups, int kext, _Float16* dst, int64_t n, int G) {
   _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const int k = 32 * j + t;
-    const int G = k / 3, role = k - 3 * G;
-    _Float16 v = (_Float16)0.0f;
-    if (G < ngroups) {
-      const int g = G * g0 / gs;
-      if (g != gprev) {
-        const float s = bf16_to_f32(S[n * ng + g]);
-        const float b = bf16_to_f32(B[n * ng + g]);   // n * ng is int64
-        const float c = fmaf(z, s, b);
-        chi = (_Float16)c;
-        clo = (_Float16)(c - (float)chi);
-        gprev = g;
-      }
-      v = role == 1 ? clo : chi;
-    }
-    out[t / 8][t % 8] = v;
+  if (G < ngroups) {
+    const int ng = ngroups * g0 / gs;               // groups of this matrix per row
+    const int64_t gi = n * ng + (G * g0) / gs;
+    const float z = bits == 8 ? 136.0f : 8.0f;
+    const float c = fmaf(z, bf16_to_f32(S[gi]), bf16_to_f32(B[gi]));
+    chi = (_Float16)c;
+    clo = (_Float16)(c - (float)chi);
   }
-  f16x8* d = reinterpret_cast<f16x8*>(dst + (int64_t)n * kext + 32 * j);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = out[q];
+  _Float16* d = dst + n * kext + 3 * G;
+  const int k = 3 * G;
+  if (k < kext) d[0] = chi;
+  if (k + 1 < kext) d[1] = clo;
+  if (k + 2 < kext) d[2] = chi;
 }
 
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
@@ -148,16 +135,16 @@ __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
     prep_x_row(p, blockIdx.x);
     return;
   }
-  const int per_row = p.kext / 32;
+  const int per_row = (p.kext + 2) / 3;               // triplets per row, the last ones padding
   const int64_t idx = (int64_t)(blockIdx.x - p.M) * 256 + threadIdx.x;
   const int64_t per_mat = (int64_t)p.I * per_row;
   const int ngroups = p.H / p.g0;
   if (idx < per_mat) {
-    prep_ext_piece(p.sg, p.bg, p.gs_g, p.bits_g, p.g0, ngroups, p.kext, p.bext_g, idx / per_row,
+    prep_ext_group(p.sg, p.bg, p.gs_g, p.bits_g, p.g0, ngroups, p.kext, p.bext_g, idx / per_row,
                    (int)(idx % per_row));
   } else if (idx < 2 * per_mat) {
     const int64_t i2 = idx - per_mat;
-    prep_ext_piece(p.su, p.bu, p.gs_u, p.bits_u, p.g0, ngroups, p.kext, p.bext_u, i2 / per_row,
+    prep_ext_group(p.su, p.bu, p.gs_u, p.bits_u, p.g0, ngroups, p.kext, p.bext_u, i2 / per_row,
                    (int)(i2 % per_row));
   }
 }
@@ -256,26 +243,31 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8
   }
 }
 
-template <int BITS_G, int BITS_U, int BM>
-__global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
-  constexpr int NT = 256, BN = 128, STAGES = 4;
-  constexpr int MF = BM / 32;                          // A fragments per wave
+template <int BITS_G, int BITS_U, int BM, int WN, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void swq_mfma_kernel(MfmaParams p) {
+  constexpr int NT = 256, STAGES = 4;
+  constexpr int BN = 4 * WN;                           // columns per matrix of the block tile
+  constexpr int MF = BM / 32, NF = WN / 32;            // A and B fragments per wave
+  constexpr int CG = BITS_G * 4, CU = BITS_U * 4;      // code bytes per row per K-step
   constexpr int A_BYTES = BM * 64;                     // x' rows of one K-step
-  constexpr int B_BYTES = 2 * BN * 64;                 // extra-column rows of both matrices
+  constexpr int CODE_BYTES = BN * (CG + CU);
+  constexpr int EXT_BYTES = BN * 64;                   // extra-column rows of one matrix
+  constexpr int B_BYTES = CODE_BYTES > EXT_BYTES ? CODE_BYTES : EXT_BYTES;
   constexpr int S_BYTES = 2 * BN * 4;                  // one scale per row and matrix, a dword each
   constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  constexpr int CG = BITS_G * 4, CU = BITS_U * 4;      // code bytes per row per K-step
   constexpr int GATE_CHUNKS = BN * CG / 16;            // 16-byte pieces of gate codes per K-step
-  constexpr int CODE_CHUNKS = BN * (CG + CU) / 16;
+  constexpr int CODE_CHUNKS = CODE_BYTES / 16;
   constexpr int A_INSTR = BM * 4 / NT;
   constexpr int B_CODE_INSTR = (CODE_CHUNKS + NT - 1) / NT;
-  constexpr int B_EXT_INSTR = B_BYTES / 16 / NT;
-  constexpr int N_MAIN = A_INSTR + B_CODE_INSTR + 1;   // buffer loads a thread issues per K-step
-  constexpr int N_EXT = A_INSTR + B_EXT_INSTR + 1;
-  constexpr int GM = BM == 256 ? 4 : 8;                // row tiles per group of the tile order
-  static_assert(GATE_CHUNKS % 64 == 0 && CODE_CHUNKS % 64 == 0, "a wave's DMA stays in one matrix");
+  constexpr int B_EXT_INSTR = EXT_BYTES / 16 / NT;
+  constexpr int S_INSTR = (2 * BN + NT - 1) / NT;
+  constexpr int N_MAIN = A_INSTR + B_CODE_INSTR + S_INSTR;   // buffer loads a thread issues per K-step
+  constexpr int N_EXT = A_INSTR + B_EXT_INSTR + S_INSTR;
+  constexpr int GM = 4;                                // row tiles per group of the tile order
+  static_assert(GATE_CHUNKS % 64 == 0 && CODE_CHUNKS % 64 == 0 && BN % 64 == 0,
+                "each wave's code or scale DMA instruction reads one matrix");
   static_assert(B_CODE_INSTR * NT - CODE_CHUNKS <= BN * CU / 16, "duplicate DMA pieces are up pieces");
-  static_assert(BM <= NT, "one row exponent per thread");
+  static_assert(BM <= NT && A_INSTR >= 1 && S_INSTR >= 1 && B_EXT_INSTR >= 1, "tile shape");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
   __shared__ int rexp[BM];
@@ -302,7 +294,8 @@ __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
   const int cols = min(BN, p.I - n0);
 
   const int s_main = p.H / 32;
-  const int s_total = s_main + p.kext / 32;
+  const int s_ext = p.kext / 32;
+  const int s_total = s_main + 2 * s_ext;              // extra-column steps: gate then up, per 32 columns
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
   const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
 
@@ -322,168 +315,228 @@ __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
     const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
     a_voff[j] = (uint32_t)(row * p.ldx * 2 + c * 16);
   }
-  // B codes: LDS piece L < GATE_CHUNKS is gate row L/(CG/16) part L%(CG/16), then up rows;
-  // pieces past CODE_CHUNKS repeat up pieces (same data to the same place)
+  // codes: LDS piece L < GATE_CHUNKS is gate row L/(CG/16) part L%(CG/16), then up rows;
+  // pieces past CODE_CHUNKS repeat up pieces (same data to the same place).
+  // Wave w's instruction j covers pieces code_l0(j) .. + 63 of one matrix.
+  auto code_l0 = [&](int j) {
+    const int L0 = j * NT + w * 64;
+    return L0 >= CODE_CHUNKS ? L0 - BN * CU / 16 : L0;
+  };
   uint32_t c_voff[B_CODE_INSTR];
 #pragma unroll
   for (int j = 0; j < B_CODE_INSTR; ++j) {
     int L = j * NT + tid;
     if (L >= CODE_CHUNKS) L -= BN * CU / 16;
-    if (L < GATE_CHUNKS) c_voff[j] = (uint32_t)((L / (CG / 16)) * rw_g * 4 + (L % (CG / 16)) * 16);
-    else c_voff[j] = (uint32_t)(((L - GATE_CHUNKS) / (CU / 16)) * rw_u * 4 + ((L - GATE_CHUNKS) % (CU / 16)) * 16);
+    c_voff[j] = L < GATE_CHUNKS
+                    ? (uint32_t)((L / (CG / 16)) * rw_g * 4 + (L % (CG / 16)) * 16)
+                    : (uint32_t)(((L - GATE_CHUNKS) / (CU / 16)) * rw_u * 4 + ((L - GATE_CHUNKS) % (CU / 16)) * 16);
   }
-  // B extra columns: piece L: matrix L/512, row (L%512)/4, chunk (L%4) ^ ((row>>2)&3)
+  // extra columns of one matrix: piece L = row*4 + phys, chunk phys ^ ((row>>2)&3)
   uint32_t e_voff[B_EXT_INSTR];
 #pragma unroll
   for (int j = 0; j < B_EXT_INSTR; ++j) {
-    const int L = j * NT + tid, row = (L & 511) >> 2, c = (L & 3) ^ ((row >> 2) & 3);
+    const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
     e_voff[j] = (uint32_t)(row * p.kext * 2 + c * 16);
   }
-  const int ncol = 32 * w + l32;                      // this lane's column in the tile
-  // scales: thread t < 128 loads gate row t, thread t >= 128 up row t - 128
-  const uint32_t s_voff = (uint32_t)(tid < BN ? tid * ng_g * 2 : (tid - BN) * ng_u * 2);
+  // scales: instruction j, thread t loads the scale of row (j*NT + t) mod BN of
+  // the gate (first BN rows) or the up matrix
+  uint32_t s_voff[S_INSTR];
+#pragma unroll
+  for (int j = 0; j < S_INSTR; ++j) {
+    const int r = j * NT + tid;
+    s_voff[j] = r < BN ? (uint32_t)(r * ng_g * 2) : (uint32_t)((r - BN) * ng_u * 2);
+  }
+  const int sh_g = __builtin_ctz(p.gs_g) - 5, sh_u = __builtin_ctz(p.gs_u) - 5;   // K-step -> group
 
   // row exponents of the tile: loaded first, published through LDS after the K loop
-  const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;   // BM <= NT
+  const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;
 
-
-  // issue every load of K-step s into its stage (SLOT = s % STAGES)
+  // issue every load of K-step s into stage `slot`
   const uint32_t smem0 = lds_addr(smem);
-  auto issue = [&]<int SLOT>(int s) {
-    const uint32_t st = smem0 + SLOT * STAGE;
-    const uint32_t soff_a = (uint32_t)s * 64;
+  auto issue = [&](int slot, int s, bool ext) {
+    const uint32_t st = smem0 + slot * STAGE;
+    const int es = s - s_main;                         // extra-column step: block es/2, matrix es%2
+    const uint32_t soff_a = (uint32_t)(ext ? s_main + (es >> 1) : s) * 64;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j], soff_a);
     const uint32_t sb = st + A_BYTES;
-    const uint32_t ss = sb + B_BYTES + w * 64 * 4;
-    if (s < s_main) {
+    const uint32_t ss = sb + B_BYTES;
+    if (!ext) {
 #pragma unroll
       for (int j = 0; j < B_CODE_INSTR; ++j) {
-        int L0 = j * NT + w * 64;                      // wave-uniform first piece
-        if (L0 >= CODE_CHUNKS) L0 -= BN * CU / 16;
-        if (L0 < GATE_CHUNKS) dma16(rs_wg, sb + L0 * 16, c_voff[j], (uint32_t)s * CG);
-        else dma16(rs_wu, sb + L0 * 16, c_voff[j], (uint32_t)s * CU);
+        const int L0 = code_l0(j);
+        const bool gate = L0 < GATE_CHUNKS;            // wave-uniform
+        dma16(gate ? rs_wg : rs_wu, sb + L0 * 16, c_voff[j], (uint32_t)s * (gate ? CG : CU));
       }
-      if (w < 2) dma2(rs_sg, ss, s_voff, (uint32_t)((s * 32) / p.gs_g) * 2);
-      else dma2(rs_su, ss, s_voff, (uint32_t)((s * 32) / p.gs_u) * 2);
-    } else {
-      const uint32_t soff_e = (uint32_t)(s - s_main) * 64;
 #pragma unroll
-      for (int j = 0; j < B_EXT_INSTR; ++j) {
-        const int L0 = j * NT + w * 64;
-        if (L0 < 512) dma16(rs_eg, sb + L0 * 16, e_voff[j], soff_e);
-        else dma16(rs_eu, sb + L0 * 16, e_voff[j], soff_e);
+      for (int j = 0; j < S_INSTR; ++j) {
+        const bool gate = j * NT + w * 64 < BN;        // wave-uniform
+        dma2(gate ? rs_sg : rs_su, ss + (j * NT + w * 64) * 4, s_voff[j], (uint32_t)(s >> (gate ? sh_g : sh_u)) * 2);
       }
-      dma2(w < 2 ? rs_sg : rs_su, ss, s_voff, 0);      // unused: keeps the per-step load count fixed
+    } else {
+      const i32x4 rs_e = (es & 1) ? rs_eu : rs_eg;
+      const uint32_t soff_e = (uint32_t)(es >> 1) * 64;
+#pragma unroll
+      for (int j = 0; j < B_EXT_INSTR; ++j) dma16(rs_e, sb + (j * NT + w * 64) * 16, e_voff[j], soff_e);
+#pragma unroll
+      for (int j = 0; j < S_INSTR; ++j)                  // unused: keeps the per-step load count fixed
+        dma2(j * NT + w * 64 < BN ? rs_sg : rs_su, ss + (j * NT + w * 64) * 4, s_voff[j], 0);
     }
   };
 
-  // wait until at most the loads of K-step s are still in flight
-  auto wait_all_but = [&](int s) {
-    if (s < s_main) wait_vmcnt<N_MAIN>();
-    else wait_vmcnt<N_EXT>();
-  };
-
-  f32x16 acc_g[MF], acc_u[MF];
+  f32x16 acc_g[MF][NF], acc_u[MF][NF];
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc_g[i][r] = 0.0f;
-      acc_u[i][r] = 0.0f;
-    }
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc_g[i][f][r] = 0.0f;
+        acc_u[i][f][r] = 0.0f;
+      }
 
   // operand registers of the two sub-steps of a K-step
   f16x8 a0[MF], a1[MF];
-  f16x8 g0a, g0b, u0a, u0b;       // sub-step 0: gate planes, up planes
-  f16x8 g1a, g1b, u1a, u1b;       // sub-step 1
-  uint32_t cw_g[BITS_G / 2], cw_u[BITS_U / 2];   // this lane's codes of the current K-step
+  f16x8 g0a[NF], g0b[NF], u0a[NF], u0b[NF];     // sub-step 0: gate planes, up planes
+  f16x8 g1a[NF], g1b[NF], u1a[NF], u1b[NF];     // sub-step 1
+  uint32_t cw_g[NF][BITS_G / 2], cw_u[NF][BITS_U / 2];   // this lane's codes of the current K-step
+  f16x2 sg2[NF], su2[NF];                                 // and its scales
 
-  const uint32_t a_lds0 = (uint32_t)(l32 * 64 + (((2 * half) ^ ((l32 >> 2) & 3)) * 16));
-  const uint32_t a_lds1 = (uint32_t)(l32 * 64 + (((2 * half + 1) ^ ((l32 >> 2) & 3)) * 16));
-  const uint32_t e_lds0 = (uint32_t)(ncol * 64 + (((2 * half) ^ ((l32 >> 2) & 3)) * 16));
-  const uint32_t e_lds1 = (uint32_t)(ncol * 64 + (((2 * half + 1) ^ ((l32 >> 2) & 3)) * 16));
+  const uint32_t sw = (uint32_t)((l32 >> 2) & 3);
+  const uint32_t a_lds0 = (uint32_t)(l32 * 64) + (((2 * half) ^ sw) * 16);
+  const uint32_t a_lds1 = (uint32_t)(l32 * 64) + (((2 * half + 1) ^ sw) * 16);
 
-  // A fragments of sub-step ks of K-step s
-  auto read_a = [&]<int SLOT>(int ks, f16x8 (&a)[MF]) {
-    const unsigned char* st = smem + SLOT * STAGE + (ks ? a_lds1 : a_lds0);
+  // A fragments of sub-step ks from stage `slot`
+  auto read_a = [&](int slot, int ks, f16x8 (&a)[MF]) {
+    const unsigned char* st = smem + slot * STAGE + (ks ? a_lds1 : a_lds0);
 #pragma unroll
     for (int i = 0; i < MF; ++i) a[i] = *reinterpret_cast<const f16x8*>(st + i * 32 * 64);
   };
-  // B operands of sub-step ks of K-step s (ks == 0 also fetches the step's codes)
-  auto read_b = [&]<int SLOT>(int s, int ks, f16x8& ga, f16x8& gb, f16x8& ua, f16x8& ub) {
-    const unsigned char* sb = smem + SLOT * STAGE + A_BYTES;
-    if (s < s_main) {
+  // B operands of sub-step ks from stage `slot` (ks == 0 also fetches the step's codes and scales)
+  auto read_b = [&](int slot, bool ext, int ks, f16x8 (&ga)[NF], f16x8 (&gb)[NF], f16x8 (&ua)[NF],
+                    f16x8 (&ub)[NF]) {
+    const unsigned char* sb = smem + slot * STAGE + A_BYTES;
+    if (!ext) {
       if (ks == 0) {
-        const unsigned char* qg = sb + ncol * CG + half * (CG / 2);
-        const unsigned char* qu = sb + BN * CG + ncol * CU + half * (CU / 2);
-        if (BITS_G == 4) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
-          cw_g[0] = v[0]; cw_g[1] = v[1];
-        } else {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
-          cw_g[0] = v[0]; cw_g[1] = v[1]; cw_g[2] = v[2]; cw_g[3] = v[3];
-        }
-        if (BITS_U == 4) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
-          cw_u[0] = v[0]; cw_u[1] = v[1];
-        } else {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
-          cw_u[0] = v[0]; cw_u[1] = v[1]; cw_u[2] = v[2]; cw_u[3] = v[3];
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(sb + B_BYTES);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int n = w * WN + f * 32 + l32;
+          sg2[f] = bf16_to_h2((uint16_t)sc[n]);
+          su2[f] = bf16_to_h2((uint16_t)sc[BN + n]);
+          const unsigned char* qg = sb + n * CG + half * (CG / 2);
+          const unsigned char* qu = sb + BN * CG + n * CU + half * (CU / 2);
+          if (BITS_G == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
+            cw_g[f][0] = v[0]; cw_g[f][1] = v[1];
+          } else {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
+            cw_g[f][0] = v[0]; cw_g[f][1] = v[1]; cw_g[f][2] = v[2]; cw_g[f][3] = v[3];
+          }
+          if (BITS_U == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
+            cw_u[f][0] = v[0]; cw_u[f][1] = v[1];
+          } else {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
+            cw_u[f][0] = v[0]; cw_u[f][1] = v[1]; cw_u[f][2] = v[2]; cw_u[f][3] = v[3];
+          }
         }
       }
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(sb + B_BYTES);
-      const f16x2 sg2 = bf16_to_h2((uint16_t)sc[ncol]);
-      const f16x2 su2 = bf16_to_h2((uint16_t)sc[BN + ncol]);
-      dequant_block<BITS_G>(&cw_g[ks * (BITS_G / 4)], sg2, ga, gb);
-      dequant_block<BITS_U>(&cw_u[ks * (BITS_U / 4)], su2, ua, ub);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        dequant_block<BITS_G>(&cw_g[f][ks * (BITS_G / 4)], sg2[f], ga[f], gb[f]);
+        dequant_block<BITS_U>(&cw_u[f][ks * (BITS_U / 4)], su2[f], ua[f], ub[f]);
+      }
     } else {
-      const uint32_t o = ks ? e_lds1 : e_lds0;
-      ga = *reinterpret_cast<const f16x8*>(sb + o);
-      ua = *reinterpret_cast<const f16x8*>(sb + BN * 64 + o);
+      // one matrix per extra-column step; its operands go to the gate slots
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int n = w * WN + f * 32 + l32;
+        ga[f] = *reinterpret_cast<const f16x8*>(sb + n * 64 + (((2 * half + ks) ^ sw) * 16));
+      }
     }
   };
-  auto mfma = [&](bool ext, const f16x8 (&a)[MF], const f16x8& ga, const f16x8& gb, const f16x8& ua,
-                  const f16x8& ub) {
+  // kind 0: code step (both matrices); 1: extra columns of the gate; 2: of the up matrix
+  auto mfma = [&](int kind, const f16x8 (&a)[MF], const f16x8 (&ga)[NF], const f16x8 (&gb)[NF],
+                  const f16x8 (&ua)[NF], const f16x8 (&ub)[NF]) {
+    if (kind == 0) {
 #pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      acc_g[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga, acc_g[i], 0, 0, 0);
-      acc_u[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ua, acc_u[i], 0, 0, 0);
-    }
-    if (!ext) {
-      if (BITS_G == 8) {
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int i = 0; i < MF; ++i) acc_g[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], gb, acc_g[i], 0, 0, 0);
-      }
-      if (BITS_U == 8) {
+        for (int i = 0; i < MF; ++i) {
+          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_g[i][f], 0, 0, 0);
+          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ua[f], acc_u[i][f], 0, 0, 0);
+          if (BITS_G == 8) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], gb[f], acc_g[i][f], 0, 0, 0);
+          if (BITS_U == 8) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ub[f], acc_u[i][f], 0, 0, 0);
+        }
+    } else if (kind == 1) {
 #pragma unroll
-        for (int i = 0; i < MF; ++i) acc_u[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ub, acc_u[i], 0, 0, 0);
-      }
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_g[i][f], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_u[i][f], 0, 0, 0);
     }
   };
 
-  // one K-step t with t % STAGES == PH: sub-step (t, 0) while (t, 1) is
+  // Order of one sub-step's instructions: the MFMAs interleaved with the LDS
+  // reads and the dequantization that prepare the next sub-step, so that the
+  // matrix pipe stays fed while the vector ALU works (the reads go with the
+  // first MFMAs, their results are needed by the dequantization).
+  constexpr int MF_MAIN = MF * NF * ((BITS_G / 4) + (BITS_U / 4));   // MFMAs of a code sub-step
+  constexpr int DQ_VALU = NF * (BITS_G == 8 ? 40 : 20) + NF * (BITS_U == 8 ? 40 : 20);
+  auto interleave = [&]<int NMFMA, int NDS, int NVALU>() {
+    constexpr int LEAD = NMFMA < 8 ? NMFMA / 2 : 4;
+    constexpr int DS_PER = (NDS + LEAD - 1) / LEAD;
+    constexpr int V_PER = (NVALU + (NMFMA - LEAD) - 1) / (NMFMA - LEAD);
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, DS_PER, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    }
+#pragma unroll
+    for (int i = LEAD; i < NMFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, V_PER, 0);    // VALU
+    }
+  };
+
+  // one K-step t in stage ph = t % STAGES: sub-step (t, 0) while (t, 1) is
   // prepared from the same stage, then the barrier, then sub-step (t, 1)
-  // while (t+1, 0) is prepared
-  auto step = [&]<int PH>(int t) {
-    constexpr int NX = (PH + 1) % STAGES, IS = (PH + 3) % STAGES;
-    const bool ext = t >= s_main;
-    read_a.template operator()<PH>(1, a1);
-    read_b.template operator()<PH>(t, 1, g1a, g1b, u1a, u1b);
-    mfma(ext, a0, g0a, g0b, u0a, u0b);
+  // while (t+1, 0) is prepared.  D = s_main - t for the last code steps
+  // (1..3: which of steps t+1, t+2, t+3 are extra-column steps), 0 for code
+  // steps further from the end, -1 / -2 for the extra-column steps of the
+  // gate / the up matrix; every kind is a compile-time constant.
+  auto step = [&]<int D>(int t, int ph) {
+    constexpr int KIND = D >= 0 ? 0 : -D;                      // MFMA kind of step t
+    constexpr bool NXT_EXT = D < 0 || D == 1;
+    constexpr bool W2_EXT = D < 0 || D == 1 || D == 2;
+    constexpr bool IS_EXT = D != 0;
+    const int nx = (ph + 1) & (STAGES - 1), is = (ph + 3) & (STAGES - 1);
+    read_a(ph, 1, a1);
+    read_b(ph, KIND != 0, 1, g1a, g1b, u1a, u1b);
+    mfma(KIND, a0, g0a, g0b, u0a, u0b);
+    if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
     // stage t+1 complete for every wave, and every wave is done with stage t-1
-    wait_all_but(t + 2);
+    if (W2_EXT) wait_vmcnt<N_EXT>();
+    else wait_vmcnt<N_MAIN>();
     block_barrier();
-    issue.template operator()<IS>(t + 3);
-    read_a.template operator()<NX>(0, a0);
-    read_b.template operator()<NX>(t + 1, 0, g0a, g0b, u0a, u0b);
-    mfma(ext, a1, g1a, g1b, u1a, u1b);
+    issue(is, t + 3, IS_EXT);
+    read_a(nx, 0, a0);
+    read_b(nx, NXT_EXT, 0, g0a, g0b, u0a, u0b);
+    mfma(KIND, a1, g1a, g1b, u1a, u1b);
+    if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
   };
 
   // ---- prologue: K-steps 0..2 in flight, step 0 complete, its first operands read
-  issue.template operator()<0>(0);
-  issue.template operator()<1>(1);
-  issue.template operator()<2>(2);
+  issue(0, 0, 0 >= s_main);
+  issue(1, 1, 1 >= s_main);
+  issue(2, 2, 2 >= s_main);
   if (2 < s_main) {
     wait_vmcnt<2 * N_MAIN>();
   } else if (1 < s_main) {
@@ -492,42 +545,52 @@ __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
     wait_vmcnt<2 * N_EXT>();
   }
   block_barrier();
-  read_a.template operator()<0>(0, a0);
-  read_b.template operator()<0>(0, 0, g0a, g0b, u0a, u0b);
+  read_a(0, 0, a0);
+  read_b(0, 0 >= s_main, 0, g0a, g0b, u0a, u0b);
 
+  // ---- K loop: code steps, the last three code steps, extra-column steps in gate/up pairs
+  const int t_code = max(0, s_main - 3);
   int t = 0;
-  for (; t + STAGES <= s_total; t += STAGES) {
-    step.template operator()<0>(t);
-    step.template operator()<1>(t + 1);
-    step.template operator()<2>(t + 2);
-    step.template operator()<3>(t + 3);
+  for (; t + STAGES <= t_code; t += STAGES) {
+    step.template operator()<0>(t, 0);
+    step.template operator()<0>(t + 1, 1);
+    step.template operator()<0>(t + 2, 2);
+    step.template operator()<0>(t + 3, 3);
   }
-  if (t < s_total) step.template operator()<0>(t);
-  if (t + 1 < s_total) step.template operator()<1>(t + 1);
-  if (t + 2 < s_total) step.template operator()<2>(t + 2);
+  for (; t < t_code; ++t) step.template operator()<0>(t, t & (STAGES - 1));
+  if (s_main >= 3) step.template operator()<3>(s_main - 3, (s_main - 3) & (STAGES - 1));
+  if (s_main >= 2) step.template operator()<2>(s_main - 2, (s_main - 2) & (STAGES - 1));
+  step.template operator()<1>(s_main - 1, (s_main - 1) & (STAGES - 1));
+  for (t = s_main; t < s_total; t += 2) {
+    step.template operator()<-1>(t, t & (STAGES - 1));
+    step.template operator()<-2>(t + 1, (t + 1) & (STAGES - 1));
+  }
   wait_vmcnt<0>();                                   // nothing left in flight at exit
   if (tid < BM) rexp[tid] = my_exp;
   __syncthreads();
 
-  // ---- epilogue: lane holds rows 8*(r/4) + 4*half + r%4 of fragment i, column ncol
-  const int ocol = n0 + ncol;
+  // ---- epilogue: lane holds rows 8*(r/4) + 4*half + r%4 of fragment i, column w*WN + 32f + l32
 #pragma unroll
-  for (int i = 0; i < MF; ++i) {
+  for (int f = 0; f < NF; ++f) {
+    const int ocol = n0 + w * WN + f * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      if (lr >= rows || ocol >= p.I) continue;
-      const int e = rexp[lr];
-      const float g = ldexpf(acc_g[i][r], e);
-      const float u = ldexpf(acc_u[i][r], e);
-      const int64_t o = (int64_t)(m0 + lr) * p.I + ocol;
-      if (p.dbg_g) {
-        p.dbg_g[o] = g;
-        p.dbg_u[o] = u;
-      } else {
-        const float h = swiglu_epilogue(g, u, p.mode);
-        if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
-        else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
+    for (int i = 0; i < MF; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        if (lr >= rows || ocol >= p.I) continue;
+        const int e = rexp[lr];
+        const float g = ldexpf(acc_g[i][f][r], e);
+        const float u = ldexpf(acc_u[i][f][r], e);
+        const int64_t o = (int64_t)(m0 + lr) * p.I + ocol;
+        if (p.dbg_g) {
+          p.dbg_g[o] = g;
+          p.dbg_u[o] = u;
+        } else {
+          const float h = swiglu_epilogue(g, u, p.mode);
+          if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
+          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
+        }
       }
     }
   }
@@ -536,23 +599,28 @@ __global__ __launch_bounds__(256) void swq_mfma_kernel(MfmaParams p) {
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const int64_t ext_threads = 2 * (int64_t)p.I * (p.kext / 32);
+  const int64_t ext_threads = 2 * (int64_t)p.I * ((p.kext + 2) / 3);
   const int64_t blocks = p.M + (ext_threads + 255) / 256;
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int BG, int BU, int BM>
+template <int BG, int BU, int BM, int WN, int OCC>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.I + kMfmaBN - 1) / kMfmaBN);
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM>), dim3(tiles), dim3(256), 0, stream, p);
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.I + 4 * WN - 1) / (4 * WN));
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC>), dim3(tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU>
 static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, hipStream_t stream) {
-  if (cfg == 1) return launch_mfma_t<BG, BU, 128>(p, stream);
-  return launch_mfma_t<BG, BU, 256>(p, stream);
+  switch (cfg) {
+    case 1: return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
+    case 2: return launch_mfma_t<BG, BU, 128, 32, 2>(p, stream);
+    case 3: return launch_mfma_t<BG, BU, 128, 64, 1>(p, stream);
+    case 4: return launch_mfma_t<BG, BU, 64, 64, 1>(p, stream);
+    default: return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
+  }
 }
 
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream) {
