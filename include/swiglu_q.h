@@ -61,7 +61,8 @@ extern "C" {
 #define SWQ_OK               0
 #define SWQ_ERR_NULL         1  /* a required pointer is NULL                       */
 #define SWQ_ERR_SHAPE        2  /* M < 0, H <= 0, I <= 0, H % gs != 0, H % 32 != 0,
-                                   H > 2^20, M or I > 2^30                         */
+                                   H > 2^20, M or I > 2^30, or a staged copy of x
+                                   (2 bytes x M x about 1.05 H) of 4 GiB or more   */
 #define SWQ_ERR_UNSUPPORTED  3  /* bits not in {4, 8}, gs not in {32, 64, 128},
                                    unknown precision mode or path                   */
 #define SWQ_ERR_ALIGN        4  /* a pointer is not 16-byte aligned                 */

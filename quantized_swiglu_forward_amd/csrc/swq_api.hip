@@ -77,6 +77,8 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
   // block's rows of x' and of the weights with 32-bit buffer offsets
   if (M > (1LL << 30) || H > (1LL << 20) || I > (1LL << 30)) return SWQ_ERR_SHAPE;
   if (((M + 127) / 128) * ((I + 127) / 128) >= (1LL << 31)) return SWQ_ERR_SHAPE;
+  // the staged x' ([H + extra columns] x M binary16) is addressed with 32-bit byte offsets
+  if (M * (H + kext_columns(H, gs_g < gs_u ? gs_g : gs_u)) * 2 >= (1LL << 32)) return SWQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16)) return SWQ_ERR_ALIGN;
   if (!aligned(sg, 2) || !aligned(bg, 2) || !aligned(su, 2) || !aligned(bu, 2)) return SWQ_ERR_ALIGN;
   return SWQ_OK;

@@ -17,9 +17,9 @@ struct PrepParams {
   int M, H, I;
   int gs_g, gs_u, bits_g, bits_u;
   int g0;              // min(gs_g, gs_u): granularity of the group sums
-  int ldx;             // row pitch of xa in halves: H + kext
+  int ldx;             // columns of x': H + kext (a multiple of 32)
   int kext;            // extra K columns: 3 per g0-group, padded to 32
-  _Float16* xa;        // out: [M, ldx]
+  _Float16* xa;        // out: [ldx / 32][M][32], K-step major
   int* xexp;           // out: [M] row exponents e (x' = x * 2^-e)
   _Float16* bext_g;    // out: [I, kext] extra-column B rows of the gate (c_hi, c_lo, c_hi per group)
   _Float16* bext_u;    // out: same for the up matrix
@@ -60,9 +60,9 @@ struct GemvParams {
 };
 
 // Tile shapes of the MFMA kernel: rows, and columns per matrix.
-constexpr int kMfmaConfigs = 5;
-constexpr int kMfmaBM[kMfmaConfigs] = {256, 128, 128, 128, 64};
-constexpr int kMfmaBN[kMfmaConfigs] = {128, 128, 128, 256, 256};
+constexpr int kMfmaConfigs = 2;
+constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
+constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
 // Largest M the matrix-vector kernel takes, and its LDS budget for x.
 constexpr int kGemvMaxM = 16;

@@ -29,6 +29,8 @@
 //     H columns (packed codes, dequantized in registers) and then the extra
 //     columns (precomputed binary16 rows); epilogue 2^e, then silu(g) * u per
 //     precision mode.
+#include <utility>
+
 #include "swq_device.h"
 #include "swq_kernels.h"
 
@@ -41,7 +43,9 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const uint16_t* xrow = p.x + (int64_t)m * p.H;
-  _Float16* arow = p.xa + (int64_t)m * p.ldx;
+  // x' is stored K-step major: the 32 columns [32s, 32s + 32) of row m at
+  // ((s * M) + m) * 32 halves, so a row tile of one K-step is contiguous
+  auto xa_at = [&](int k) { return p.xa + ((int64_t)(k >> 5) * p.M + m) * 32 + (k & 31); };
   const int nchunk = p.H / 8;
 
   // 1. row maximum of |x| (on the bf16 magnitude bits: monotone for finite values)
@@ -71,7 +75,6 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   // 2. scaled binary16 copy in pair order, and per-group sums
   const int gchunks = p.g0 / 8;
   const int ngroups = p.H / p.g0;
-  _Float16* ext = arow + p.H;
   for (int base = 0; base < nchunk; base += 256) {
     const int c = base + tid;
     float part = 0.0f;
@@ -91,7 +94,7 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
         h[2 * j] = (_Float16)f[j];
         h[2 * j + 1] = (_Float16)f[j + 4];
       }
-      *reinterpret_cast<f16x8*>(arow + 8 * c) = h;
+      *reinterpret_cast<f16x8*>(xa_at(8 * c)) = h;
     }
     // a group is g0/8 consecutive 8-value blocks = consecutive lanes
     for (int off = 1; off < gchunks; off <<= 1) part += __shfl_xor(part, off);
@@ -99,13 +102,13 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
       const int g = c / gchunks;
       const _Float16 hi = (_Float16)part;
       const _Float16 lo = (_Float16)(part - (float)hi);
-      ext[3 * g] = hi;
-      ext[3 * g + 1] = hi;
-      ext[3 * g + 2] = lo;
+      *xa_at(p.H + 3 * g) = hi;
+      *xa_at(p.H + 3 * g + 1) = hi;
+      *xa_at(p.H + 3 * g + 2) = lo;
     }
   }
   // zero padding of the extra columns
-  for (int k = 3 * ngroups + tid; k < p.kext; k += 256) ext[k] = (_Float16)0.0f;
+  for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
 }
 
 // Extra-column B rows: thread (n, G) writes columns 3G, 3G+1, 3G+2 of row n
@@ -243,9 +246,10 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8
   }
 }
 
-template <int BITS_G, int BITS_U, int BM, int WN, int OCC>
+template <int BITS_G, int BITS_U, int BM, int WN, int OCC, int STAGES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void swq_mfma_kernel(MfmaParams p) {
-  constexpr int NT = 256, STAGES = 4;
+  constexpr int NT = 256;
+  static_assert(STAGES >= 3 && STAGES <= 8, "stage ring");
   constexpr int BN = 4 * WN;                           // columns per matrix of the block tile
   constexpr int MF = BM / 32, NF = WN / 32;            // A and B fragments per wave
   constexpr int CG = BITS_G * 4, CU = BITS_U * 4;      // code bytes per row per K-step
@@ -299,7 +303,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
   const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
 
-  const i32x4 rs_a = make_srsrc(p.xa + (int64_t)m0 * p.ldx, (uint32_t)rows * p.ldx * 2);
+  // x' tile rows of K-step s: (s * M + m0 + row) * 64 bytes from the start of x'
+  const i32x4 rs_a = make_srsrc(p.xa + (int64_t)m0 * 32, (uint32_t)(((int64_t)(p.ldx / 32) * p.M - m0) * 64));
+  const uint32_t a_step = (uint32_t)p.M * 64;
   const i32x4 rs_wg = make_srsrc(p.wg + (int64_t)n0 * rw_g, (uint32_t)cols * rw_g * 4);
   const i32x4 rs_wu = make_srsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols * rw_u * 4);
   const i32x4 rs_sg = make_srsrc(p.sg + (int64_t)n0 * ng_g, (uint32_t)cols * ng_g * 2);
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
     const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
-    a_voff[j] = (uint32_t)(row * p.ldx * 2 + c * 16);
+    a_voff[j] = (uint32_t)(row * 64 + c * 16);
   }
   // codes: LDS piece L < GATE_CHUNKS is gate row L/(CG/16) part L%(CG/16), then up rows;
   // pieces past CODE_CHUNKS repeat up pieces (same data to the same place).
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   auto issue = [&](int slot, int s, bool ext) {
     const uint32_t st = smem0 + slot * STAGE;
     const int es = s - s_main;                         // extra-column step: block es/2, matrix es%2
-    const uint32_t soff_a = (uint32_t)(ext ? s_main + (es >> 1) : s) * 64;
+    const uint32_t soff_a = (uint32_t)(ext ? s_main + (es >> 1) : s) * a_step;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j], soff_a);
     const uint32_t sb = st + A_BYTES;
@@ -426,14 +432,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
           su2[f] = bf16_to_h2((uint16_t)sc[BN + n]);
           const unsigned char* qg = sb + n * CG + half * (CG / 2);
           const unsigned char* qu = sb + BN * CG + n * CU + half * (CU / 2);
-          if (BITS_G == 4) {
+          if constexpr (BITS_G == 4) {
             const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
             cw_g[f][0] = v[0]; cw_g[f][1] = v[1];
           } else {
             const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
             cw_g[f][0] = v[0]; cw_g[f][1] = v[1]; cw_g[f][2] = v[2]; cw_g[f][3] = v[3];
           }
-          if (BITS_U == 4) {
+          if constexpr (BITS_U == 4) {
             const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
             cw_u[f][0] = v[0]; cw_u[f][1] = v[1];
           } else {
@@ -506,64 +512,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
   };
 
+  // Loads of K-step s are issued STAGES - 1 steps ahead, at the start of step
+  // s - STAGES + 1.  vm_allowed(D, k0, k1): the loads a thread may still have
+  // in flight once steps t+k0 .. t+k1 are all that is outstanding, where D
+  // encodes which of them are extra-column steps (below).
+  auto vm_allowed = [](int D, int k0, int k1) constexpr {
+    int n = 0;
+    for (int k = k0; k <= k1; ++k) n += (D < 0 || (D >= 1 && D <= k)) ? N_EXT : N_MAIN;
+    return n;
+  };
+
   // one K-step t in stage ph = t % STAGES: sub-step (t, 0) while (t, 1) is
   // prepared from the same stage, then the barrier, then sub-step (t, 1)
-  // while (t+1, 0) is prepared.  D = s_main - t for the last code steps
-  // (1..3: which of steps t+1, t+2, t+3 are extra-column steps), 0 for code
-  // steps further from the end, -1 / -2 for the extra-column steps of the
-  // gate / the up matrix; every kind is a compile-time constant.
+  // while (t+1, 0) is prepared.  D = 0: every step up to t + STAGES - 1 is a
+  // code step; D in [1, STAGES): D = s_main - t (steps t+D and later are
+  // extra-column steps); D = -1 / -2: extra-column step of the gate / the up
+  // matrix.  Every kind is a compile-time constant.
   auto step = [&]<int D>(int t, int ph) {
     constexpr int KIND = D >= 0 ? 0 : -D;                      // MFMA kind of step t
     constexpr bool NXT_EXT = D < 0 || D == 1;
-    constexpr bool W2_EXT = D < 0 || D == 1 || D == 2;
     constexpr bool IS_EXT = D != 0;
-    const int nx = (ph + 1) & (STAGES - 1), is = (ph + 3) & (STAGES - 1);
+    constexpr int ALLOWED = vm_allowed(D, 2, STAGES - 2);
+    const int nx = (ph + 1) % STAGES, is = (ph + STAGES - 1) % STAGES;
     read_a(ph, 1, a1);
     read_b(ph, KIND != 0, 1, g1a, g1b, u1a, u1b);
     mfma(KIND, a0, g0a, g0b, u0a, u0b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
     // stage t+1 complete for every wave, and every wave is done with stage t-1
-    if (W2_EXT) wait_vmcnt<N_EXT>();
-    else wait_vmcnt<N_MAIN>();
+    wait_vmcnt<ALLOWED>();
     block_barrier();
-    issue(is, t + 3, IS_EXT);
+    issue(is, t + STAGES - 1, IS_EXT);
     read_a(nx, 0, a0);
     read_b(nx, NXT_EXT, 0, g0a, g0b, u0a, u0b);
     mfma(KIND, a1, g1a, g1b, u1a, u1b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
   };
 
-  // ---- prologue: K-steps 0..2 in flight, step 0 complete, its first operands read
-  issue(0, 0, 0 >= s_main);
-  issue(1, 1, 1 >= s_main);
-  issue(2, 2, 2 >= s_main);
-  if (2 < s_main) {
-    wait_vmcnt<2 * N_MAIN>();
-  } else if (1 < s_main) {
-    wait_vmcnt<N_MAIN + N_EXT>();
-  } else {
-    wait_vmcnt<2 * N_EXT>();
+  // ---- prologue: K-steps 0 .. STAGES-2 in flight, step 0 complete, its first operands read
+#pragma unroll
+  for (int k = 0; k < STAGES - 1; ++k) issue(k, k, k >= s_main);
+  {
+    // extra-column steps among steps 1 .. STAGES-2
+    const int n_ext = max(0, min(STAGES - 2, STAGES - 1 - max(s_main, 1)));
+    switch (n_ext) {
+      case 0: wait_vmcnt<(STAGES - 2) * N_MAIN>(); break;
+      case 1: wait_vmcnt<(STAGES - 3) * N_MAIN + N_EXT>(); break;
+      case 2: wait_vmcnt<(STAGES - 4 >= 0 ? STAGES - 4 : 0) * N_MAIN + 2 * N_EXT>(); break;
+      case 3: wait_vmcnt<(STAGES - 5 >= 0 ? STAGES - 5 : 0) * N_MAIN + 3 * N_EXT>(); break;
+      case 4: wait_vmcnt<(STAGES - 6 >= 0 ? STAGES - 6 : 0) * N_MAIN + 4 * N_EXT>(); break;
+      case 5: wait_vmcnt<(STAGES - 7 >= 0 ? STAGES - 7 : 0) * N_MAIN + 5 * N_EXT>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
   }
   block_barrier();
   read_a(0, 0, a0);
   read_b(0, 0 >= s_main, 0, g0a, g0b, u0a, u0b);
 
-  // ---- K loop: code steps, the last three code steps, extra-column steps in gate/up pairs
-  const int t_code = max(0, s_main - 3);
+  // ---- K loop: code steps, the last STAGES-1 code steps, extra-column steps in gate/up pairs
+  const int t_code = max(0, s_main - (STAGES - 1));
   int t = 0;
-  for (; t + STAGES <= t_code; t += STAGES) {
-    step.template operator()<0>(t, 0);
-    step.template operator()<0>(t + 1, 1);
-    step.template operator()<0>(t + 2, 2);
-    step.template operator()<0>(t + 3, 3);
-  }
-  for (; t < t_code; ++t) step.template operator()<0>(t, t & (STAGES - 1));
-  if (s_main >= 3) step.template operator()<3>(s_main - 3, (s_main - 3) & (STAGES - 1));
-  if (s_main >= 2) step.template operator()<2>(s_main - 2, (s_main - 2) & (STAGES - 1));
-  step.template operator()<1>(s_main - 1, (s_main - 1) & (STAGES - 1));
+  auto unrolled = [&]<int... PH>(int t0, std::integer_sequence<int, PH...>) {
+    (step.template operator()<0>(t0 + PH, PH), ...);
+  };
+  for (; t + STAGES <= t_code; t += STAGES) unrolled(t, std::make_integer_sequence<int, STAGES>{});
+  for (; t < t_code; ++t) step.template operator()<0>(t, t % STAGES);
+  auto boundary = [&]<int DD>() {
+    if constexpr (DD >= 1 && DD < STAGES)
+      if (s_main >= DD) step.template operator()<DD>(s_main - DD, (s_main - DD) % STAGES);
+  };
+  boundary.template operator()<7>();
+  boundary.template operator()<6>();
+  boundary.template operator()<5>();
+  boundary.template operator()<4>();
+  boundary.template operator()<3>();
+  boundary.template operator()<2>();
+  step.template operator()<1>(s_main - 1, (s_main - 1) % STAGES);
   for (t = s_main; t < s_total; t += 2) {
-    step.template operator()<-1>(t, t & (STAGES - 1));
-    step.template operator()<-2>(t + 1, (t + 1) & (STAGES - 1));
+    step.template operator()<-1>(t, t % STAGES);
+    step.template operator()<-2>(t + 1, (t + 1) % STAGES);
   }
   wait_vmcnt<0>();                                   // nothing left in flight at exit
   if (tid < BM) rexp[tid] = my_exp;
@@ -605,22 +631,17 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BG, int BU, int BM, int WN, int OCC>
+template <int BG, int BU, int BM, int WN, int OCC, int STAGES>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.I + 4 * WN - 1) / (4 * WN));
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC>), dim3(tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC, STAGES>), dim3(tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU>
 static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, hipStream_t stream) {
-  switch (cfg) {
-    case 1: return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
-    case 2: return launch_mfma_t<BG, BU, 128, 32, 2>(p, stream);
-    case 3: return launch_mfma_t<BG, BU, 128, 64, 1>(p, stream);
-    case 4: return launch_mfma_t<BG, BU, 64, 64, 1>(p, stream);
-    default: return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
-  }
+  if (cfg == 1) return launch_mfma_t<BG, BU, 128, 32, 1, 4>(p, stream);
+  return launch_mfma_t<BG, BU, 256, 32, 1, 4>(p, stream);
 }
 
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream) {

@@ -63,6 +63,7 @@ def _fwd(**kw):
     (dict(H=(1 << 20) + 64), swq.SWQ_ERR_SHAPE),
     (dict(M=(1 << 30) + 1), swq.SWQ_ERR_SHAPE),
     (dict(M=1 << 30, I=1 << 30), swq.SWQ_ERR_SHAPE),
+    (dict(M=1 << 20, H=2048), swq.SWQ_ERR_SHAPE),
     (dict(x=P + 8), swq.SWQ_ERR_ALIGN),
     (dict(Wg=P + 4), swq.SWQ_ERR_ALIGN),
     (dict(Wu=P + 2), swq.SWQ_ERR_ALIGN),
