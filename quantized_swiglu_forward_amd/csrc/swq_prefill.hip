@@ -246,35 +246,39 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8
   }
 }
 
-template <int BITS_G, int BITS_U, int BM, int WN, int OCC, int STAGES>
+template <int BITS_G, int BITS_U, int BM, int WN, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void swq_mfma_kernel(MfmaParams p) {
   constexpr int NT = 256;
-  static_assert(STAGES >= 3 && STAGES <= 8, "stage ring");
+  constexpr int STAGES = 4;                            // x' / extra-column ring: K-steps in flight
+  constexpr int SS = 4;                                // K-steps per code super-step (the code ring's unit)
   constexpr int BN = 4 * WN;                           // columns per matrix of the block tile
   constexpr int MF = BM / 32, NF = WN / 32;            // A and B fragments per wave
-  constexpr int CG = BITS_G * 4, CU = BITS_U * 4;      // code bytes per row per K-step
   constexpr int A_BYTES = BM * 64;                     // x' rows of one K-step
-  constexpr int CODE_BYTES = BN * (CG + CU);
-  constexpr int EXT_BYTES = BN * 64;                   // extra-column rows of one matrix
-  constexpr int B_BYTES = CODE_BYTES > EXT_BYTES ? CODE_BYTES : EXT_BYTES;
-  constexpr int S_BYTES = 2 * BN * 4;                  // one scale per row and matrix, a dword each
-  constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  constexpr int GATE_CHUNKS = BN * CG / 16;            // 16-byte pieces of gate codes per K-step
-  constexpr int CODE_CHUNKS = CODE_BYTES / 16;
+  constexpr int EXT_BYTES = BN * 64;                   // extra-column rows of one matrix, one K-step
+  constexpr int STAGE = A_BYTES + EXT_BYTES;
+  // code super-step: SS K-steps of codes per row = BITS 16-byte chunks per row and matrix,
+  // then the scales of its groups (4 slots per row and matrix, a dword each)
+  constexpr int CPR_G = BITS_G, CPR_U = BITS_U;
+  constexpr int SSG_BYTES = BN * CPR_G * 16, SSU_BYTES = BN * CPR_U * 16;
+  constexpr int SS_CODE_BYTES = SSG_BYTES + SSU_BYTES;
+  constexpr int SS_SLOT = SS_CODE_BYTES + 2 * BN * 16;
   constexpr int A_INSTR = BM * 4 / NT;
-  constexpr int B_CODE_INSTR = (CODE_CHUNKS + NT - 1) / NT;
   constexpr int B_EXT_INSTR = EXT_BYTES / 16 / NT;
-  constexpr int S_INSTR = (2 * BN + NT - 1) / NT;
-  constexpr int N_MAIN = A_INSTR + B_CODE_INSTR + S_INSTR;   // buffer loads a thread issues per K-step
-  constexpr int N_EXT = A_INSTR + B_EXT_INSTR + S_INSTR;
+  constexpr int SS_CODE_INSTR = SS_CODE_BYTES / 16 / NT;
+  constexpr int SS_SCALE_INSTR = 2 * BN * 4 / NT;
+  constexpr int N_SS = SS_CODE_INSTR + SS_SCALE_INSTR;  // buffer loads a thread issues per super-step
+  constexpr int N_MAIN = A_INSTR;                       // ... per code K-step
+  constexpr int N_EXT = A_INSTR + B_EXT_INSTR;          // ... per extra-column K-step
   constexpr int GM = 4;                                // row tiles per group of the tile order
-  static_assert(GATE_CHUNKS % 64 == 0 && CODE_CHUNKS % 64 == 0 && BN % 64 == 0,
-                "each wave's code or scale DMA instruction reads one matrix");
-  static_assert(B_CODE_INSTR * NT - CODE_CHUNKS <= BN * CU / 16, "duplicate DMA pieces are up pieces");
-  static_assert(BM <= NT && A_INSTR >= 1 && S_INSTR >= 1 && B_EXT_INSTR >= 1, "tile shape");
+  static_assert(SSG_BYTES % (16 * NT) == 0 && SSU_BYTES % (16 * NT) == 0 && (BN * 4) % NT == 0,
+                "each code or scale DMA instruction reads one matrix");
+  static_assert(BM <= NT && A_INSTR >= 1 && B_EXT_INSTR >= 1 && SS_SCALE_INSTR >= 1, "tile shape");
+  static_assert(STAGES == SS, "a stage slot and the super-step phase are both t % 4");
+  static_assert(STAGES * STAGE + 2 * SS_SLOT + BM * 4 <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE + 2 * SS_SLOT];
   __shared__ int rexp[BM];
+  unsigned char* const ssmem = smem + STAGES * STAGE;   // code ring: two super-step slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -321,21 +325,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
     a_voff[j] = (uint32_t)(row * 64 + c * 16);
   }
-  // codes: LDS piece L < GATE_CHUNKS is gate row L/(CG/16) part L%(CG/16), then up rows;
-  // pieces past CODE_CHUNKS repeat up pieces (same data to the same place).
-  // Wave w's instruction j covers pieces code_l0(j) .. + 63 of one matrix.
-  auto code_l0 = [&](int j) {
-    const int L0 = j * NT + w * 64;
-    return L0 >= CODE_CHUNKS ? L0 - BN * CU / 16 : L0;
-  };
-  uint32_t c_voff[B_CODE_INSTR];
+  // super-step codes: LDS piece L < BN*CPR_G is gate row r = L / CPR_G, chunk
+  // (L % CPR_G) ^ swz(r), then the up rows; the permutation spreads a K-step's
+  // reads over the banks
+  auto swz = [](int r, int cpr) { return (r * cpr / 16) % cpr; };
+  uint32_t c_voff[SS_CODE_INSTR];
 #pragma unroll
-  for (int j = 0; j < B_CODE_INSTR; ++j) {
-    int L = j * NT + tid;
-    if (L >= CODE_CHUNKS) L -= BN * CU / 16;
-    c_voff[j] = L < GATE_CHUNKS
-                    ? (uint32_t)((L / (CG / 16)) * rw_g * 4 + (L % (CG / 16)) * 16)
-                    : (uint32_t)(((L - GATE_CHUNKS) / (CU / 16)) * rw_u * 4 + ((L - GATE_CHUNKS) % (CU / 16)) * 16);
+  for (int j = 0; j < SS_CODE_INSTR; ++j) {
+    const int L = j * NT + tid;
+    if (j * NT < BN * CPR_G) {
+      const int r = L / CPR_G, c = (L % CPR_G) ^ swz(r, CPR_G);
+      c_voff[j] = (uint32_t)(r * rw_g * 4 + c * 16);
+    } else {
+      const int L2 = L - BN * CPR_G, r = L2 / CPR_U, c = (L2 % CPR_U) ^ swz(r, CPR_U);
+      c_voff[j] = (uint32_t)(r * rw_u * 4 + c * 16);
+    }
   }
   // extra columns of one matrix: piece L = row*4 + phys, chunk phys ^ ((row>>2)&3)
   uint32_t e_voff[B_EXT_INSTR];
@@ -344,20 +348,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
     e_voff[j] = (uint32_t)(row * p.kext * 2 + c * 16);
   }
-  // scales: instruction j, thread t loads the scale of row (j*NT + t) mod BN of
-  // the gate (first BN rows) or the up matrix
-  uint32_t s_voff[S_INSTR];
+  // super-step scales: 4 slots per row and matrix for the 128/gs groups the
+  // super-step touches (slots past the last one repeat it); piece L: matrix
+  // L / (4*BN), row (L % (4*BN)) / 4, slot L % 4
+  const int gps_g = 128 / p.gs_g, gps_u = 128 / p.gs_u;
+  uint32_t s_voff[SS_SCALE_INSTR];
 #pragma unroll
-  for (int j = 0; j < S_INSTR; ++j) {
-    const int r = j * NT + tid;
-    s_voff[j] = r < BN ? (uint32_t)(r * ng_g * 2) : (uint32_t)((r - BN) * ng_u * 2);
+  for (int j = 0; j < SS_SCALE_INSTR; ++j) {
+    const int L = j * NT + tid, rl = L % (4 * BN), r = rl / 4, k = rl % 4;
+    s_voff[j] = j * NT < 4 * BN ? (uint32_t)(r * ng_g * 2 + min(k, gps_g - 1) * 2)
+                                : (uint32_t)(r * ng_u * 2 + min(k, gps_u - 1) * 2);
   }
-  const int sh_g = __builtin_ctz(p.gs_g) - 5, sh_u = __builtin_ctz(p.gs_u) - 5;   // K-step -> group
+  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
 
   // row exponents of the tile: loaded first, published through LDS after the K loop
   const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;
 
-  // issue every load of K-step s into stage `slot`
+  // issue the x' (and for an extra-column step the B) loads of K-step s into stage `slot`
   const uint32_t smem0 = lds_addr(smem);
   auto issue = [&](int slot, int s, bool ext) {
     const uint32_t st = smem0 + slot * STAGE;
@@ -365,28 +372,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const uint32_t soff_a = (uint32_t)(ext ? s_main + (es >> 1) : s) * a_step;
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j], soff_a);
-    const uint32_t sb = st + A_BYTES;
-    const uint32_t ss = sb + B_BYTES;
-    if (!ext) {
-#pragma unroll
-      for (int j = 0; j < B_CODE_INSTR; ++j) {
-        const int L0 = code_l0(j);
-        const bool gate = L0 < GATE_CHUNKS;            // wave-uniform
-        dma16(gate ? rs_wg : rs_wu, sb + L0 * 16, c_voff[j], (uint32_t)s * (gate ? CG : CU));
-      }
-#pragma unroll
-      for (int j = 0; j < S_INSTR; ++j) {
-        const bool gate = j * NT + w * 64 < BN;        // wave-uniform
-        dma2(gate ? rs_sg : rs_su, ss + (j * NT + w * 64) * 4, s_voff[j], (uint32_t)(s >> (gate ? sh_g : sh_u)) * 2);
-      }
-    } else {
+    if (ext) {
+      const uint32_t sb = st + A_BYTES;
       const i32x4 rs_e = (es & 1) ? rs_eu : rs_eg;
       const uint32_t soff_e = (uint32_t)(es >> 1) * 64;
 #pragma unroll
       for (int j = 0; j < B_EXT_INSTR; ++j) dma16(rs_e, sb + (j * NT + w * 64) * 16, e_voff[j], soff_e);
+    }
+  };
+  // issue the codes and scales of super-step j (K-steps SS*j .. SS*j + SS-1) into its slot
+  const uint32_t ssmem0 = lds_addr(ssmem);
+  auto issue_ss = [&](int j) {
+    const uint32_t sl = ssmem0 + (j & 1) * SS_SLOT;
 #pragma unroll
-      for (int j = 0; j < S_INSTR; ++j)                  // unused: keeps the per-step load count fixed
-        dma2(j * NT + w * 64 < BN ? rs_sg : rs_su, ss + (j * NT + w * 64) * 4, s_voff[j], 0);
+    for (int q = 0; q < SS_CODE_INSTR; ++q) {
+      if (q * NT < BN * CPR_G) dma16(rs_wg, sl + (q * NT + w * 64) * 16, c_voff[q], (uint32_t)(j * CPR_G * 16));
+      else dma16(rs_wu, sl + (q * NT + w * 64) * 16, c_voff[q], (uint32_t)(j * CPR_U * 16));
+    }
+#pragma unroll
+    for (int q = 0; q < SS_SCALE_INSTR; ++q) {
+      if (q * NT < 4 * BN) dma2(rs_sg, sl + SS_CODE_BYTES + (q * NT + w * 64) * 4, s_voff[q], (uint32_t)((128 * j) >> lg_g) * 2);
+      else dma2(rs_su, sl + SS_CODE_BYTES + (q * NT + w * 64) * 4, s_voff[q], (uint32_t)((128 * j) >> lg_u) * 2);
     }
   };
 
@@ -418,20 +424,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
     for (int i = 0; i < MF; ++i) a[i] = *reinterpret_cast<const f16x8*>(st + i * 32 * 64);
   };
-  // B operands of sub-step ks from stage `slot` (ks == 0 also fetches the step's codes and scales)
-  auto read_b = [&](int slot, bool ext, int ks, f16x8 (&ga)[NF], f16x8 (&gb)[NF], f16x8 (&ua)[NF],
+  // B operands of sub-step ks of K-step t from stage `slot` (extra columns) or
+  // the code ring (ks == 0 also fetches the step's codes and scales)
+  auto read_b = [&](int slot, int t, bool ext, int ks, f16x8 (&ga)[NF], f16x8 (&gb)[NF], f16x8 (&ua)[NF],
                     f16x8 (&ub)[NF]) {
     const unsigned char* sb = smem + slot * STAGE + A_BYTES;
     if (!ext) {
       if (ks == 0) {
-        const uint32_t* sc = reinterpret_cast<const uint32_t*>(sb + B_BYTES);
+        const unsigned char* ring = ssmem + ((t / SS) & 1) * SS_SLOT;
+        const int q = t % SS;                          // K-step within the super-step
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(ring + SS_CODE_BYTES);
+        const int kg = (32 * q) >> lg_g, ku = (32 * q) >> lg_u;   // group slot of this K-step
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int n = w * WN + f * 32 + l32;
-          sg2[f] = bf16_to_h2((uint16_t)sc[n]);
-          su2[f] = bf16_to_h2((uint16_t)sc[BN + n]);
-          const unsigned char* qg = sb + n * CG + half * (CG / 2);
-          const unsigned char* qu = sb + BN * CG + n * CU + half * (CU / 2);
+          sg2[f] = bf16_to_h2((uint16_t)sc[4 * n + kg]);
+          su2[f] = bf16_to_h2((uint16_t)sc[4 * BN + 4 * n + ku]);
+          // 4-bit: chunk q holds the K-step, this lane's two 8-code blocks at half * 8;
+          // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half
+          const unsigned char* qg = BITS_G == 4
+              ? ring + n * (CPR_G * 16) + ((q ^ swz(n, CPR_G)) * 16) + half * 8
+              : ring + n * (CPR_G * 16) + (((2 * q + half) ^ swz(n, CPR_G)) * 16);
+          const unsigned char* qu = BITS_U == 4
+              ? ring + SSG_BYTES + n * (CPR_U * 16) + ((q ^ swz(n, CPR_U)) * 16) + half * 8
+              : ring + SSG_BYTES + n * (CPR_U * 16) + (((2 * q + half) ^ swz(n, CPR_U)) * 16);
           if constexpr (BITS_G == 4) {
             const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
             cw_g[f][0] = v[0]; cw_g[f][1] = v[1];
@@ -512,80 +528,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
   };
 
-  // Loads of K-step s are issued STAGES - 1 steps ahead, at the start of step
-  // s - STAGES + 1.  vm_allowed(D, k0, k1): the loads a thread may still have
-  // in flight once steps t+k0 .. t+k1 are all that is outstanding, where D
-  // encodes which of them are extra-column steps (below).
-  auto vm_allowed = [](int D, int k0, int k1) constexpr {
-    int n = 0;
-    for (int k = k0; k <= k1; ++k) n += (D < 0 || (D >= 1 && D <= k)) ? N_EXT : N_MAIN;
-    return n;
-  };
+  // Loads of K-step s are issued STAGES - 1 = 3 steps ahead, at the start of
+  // step s - 3, and the codes and scales of super-step j at the start of step
+  // SS*(j-1).  At the barrier of step t everything issued up to step t-2 must
+  // have landed; only the loads of step t-1 may still be in flight: the x'
+  // (and extra-column) loads of K-step t+2, and those of super-step t/SS + 1 if
+  // step t-1 started a super-step.
 
   // one K-step t in stage ph = t % STAGES: sub-step (t, 0) while (t, 1) is
   // prepared from the same stage, then the barrier, then sub-step (t, 1)
-  // while (t+1, 0) is prepared.  D = 0: every step up to t + STAGES - 1 is a
-  // code step; D in [1, STAGES): D = s_main - t (steps t+D and later are
-  // extra-column steps); D = -1 / -2: extra-column step of the gate / the up
-  // matrix.  Every kind is a compile-time constant.
+  // while (t+1, 0) is prepared.  D = 0: steps t+1 .. t+3 are code steps;
+  // D in [1, 3]: D = s_main - t (steps t+D and later are extra-column steps);
+  // D = -1 / -2: extra-column step of the gate / the up matrix.  Every kind is
+  // a compile-time constant.
   auto step = [&]<int D>(int t, int ph) {
     constexpr int KIND = D >= 0 ? 0 : -D;                      // MFMA kind of step t
     constexpr bool NXT_EXT = D < 0 || D == 1;
+    constexpr bool W2_EXT = D < 0 || D == 1 || D == 2;         // is step t+2 an extra-column step
     constexpr bool IS_EXT = D != 0;
-    constexpr int ALLOWED = vm_allowed(D, 2, STAGES - 2);
+    constexpr int NA = W2_EXT ? N_EXT : N_MAIN;
     const int nx = (ph + 1) % STAGES, is = (ph + STAGES - 1) % STAGES;
     read_a(ph, 1, a1);
-    read_b(ph, KIND != 0, 1, g1a, g1b, u1a, u1b);
+    read_b(ph, t, KIND != 0, 1, g1a, g1b, u1a, u1b);
     mfma(KIND, a0, g0a, g0b, u0a, u0b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
-    // stage t+1 complete for every wave, and every wave is done with stage t-1
-    wait_vmcnt<ALLOWED>();
+    // stage t+1 and its super-step complete for every wave, and every wave is done with stage t-1
+    if (ph == 1) wait_vmcnt<NA + N_SS>();
+    else wait_vmcnt<NA>();
     block_barrier();
     issue(is, t + STAGES - 1, IS_EXT);
+    if (ph == 0) issue_ss(t / SS + 1);
     read_a(nx, 0, a0);
-    read_b(nx, NXT_EXT, 0, g0a, g0b, u0a, u0b);
+    read_b(nx, t + 1, NXT_EXT, 0, g0a, g0b, u0a, u0b);
     mfma(KIND, a1, g1a, g1b, u1a, u1b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
   };
 
-  // ---- prologue: K-steps 0 .. STAGES-2 in flight, step 0 complete, its first operands read
-#pragma unroll
-  for (int k = 0; k < STAGES - 1; ++k) issue(k, k, k >= s_main);
-  {
-    // extra-column steps among steps 1 .. STAGES-2
-    const int n_ext = max(0, min(STAGES - 2, STAGES - 1 - max(s_main, 1)));
-    switch (n_ext) {
-      case 0: wait_vmcnt<(STAGES - 2) * N_MAIN>(); break;
-      case 1: wait_vmcnt<(STAGES - 3) * N_MAIN + N_EXT>(); break;
-      case 2: wait_vmcnt<(STAGES - 4 >= 0 ? STAGES - 4 : 0) * N_MAIN + 2 * N_EXT>(); break;
-      case 3: wait_vmcnt<(STAGES - 5 >= 0 ? STAGES - 5 : 0) * N_MAIN + 3 * N_EXT>(); break;
-      case 4: wait_vmcnt<(STAGES - 6 >= 0 ? STAGES - 6 : 0) * N_MAIN + 4 * N_EXT>(); break;
-      case 5: wait_vmcnt<(STAGES - 7 >= 0 ? STAGES - 7 : 0) * N_MAIN + 5 * N_EXT>(); break;
-      default: wait_vmcnt<0>(); break;
-    }
+  // ---- prologue: super-step 0 and K-steps 0 .. 2 in flight, step 0 complete, its first operands read
+  issue_ss(0);
+  issue(0, 0, 0 >= s_main);
+  issue(1, 1, 1 >= s_main);
+  issue(2, 2, 2 >= s_main);
+  if (2 < s_main) {
+    wait_vmcnt<2 * N_MAIN>();
+  } else if (1 < s_main) {
+    wait_vmcnt<N_MAIN + N_EXT>();
+  } else {
+    wait_vmcnt<2 * N_EXT>();
   }
   block_barrier();
   read_a(0, 0, a0);
-  read_b(0, 0 >= s_main, 0, g0a, g0b, u0a, u0b);
+  read_b(0, 0, 0 >= s_main, 0, g0a, g0b, u0a, u0b);
 
-  // ---- K loop: code steps, the last STAGES-1 code steps, extra-column steps in gate/up pairs
-  const int t_code = max(0, s_main - (STAGES - 1));
+  // ---- K loop: code steps, the last three code steps, extra-column steps in gate/up pairs
+  const int t_code = max(0, s_main - 3);
   int t = 0;
-  auto unrolled = [&]<int... PH>(int t0, std::integer_sequence<int, PH...>) {
-    (step.template operator()<0>(t0 + PH, PH), ...);
-  };
-  for (; t + STAGES <= t_code; t += STAGES) unrolled(t, std::make_integer_sequence<int, STAGES>{});
+  for (; t + STAGES <= t_code; t += STAGES) {
+    step.template operator()<0>(t, 0);
+    step.template operator()<0>(t + 1, 1);
+    step.template operator()<0>(t + 2, 2);
+    step.template operator()<0>(t + 3, 3);
+  }
   for (; t < t_code; ++t) step.template operator()<0>(t, t % STAGES);
-  auto boundary = [&]<int DD>() {
-    if constexpr (DD >= 1 && DD < STAGES)
-      if (s_main >= DD) step.template operator()<DD>(s_main - DD, (s_main - DD) % STAGES);
-  };
-  boundary.template operator()<7>();
-  boundary.template operator()<6>();
-  boundary.template operator()<5>();
-  boundary.template operator()<4>();
-  boundary.template operator()<3>();
-  boundary.template operator()<2>();
+  if (s_main >= 3) step.template operator()<3>(s_main - 3, (s_main - 3) % STAGES);
+  if (s_main >= 2) step.template operator()<2>(s_main - 2, (s_main - 2) % STAGES);
   step.template operator()<1>(s_main - 1, (s_main - 1) % STAGES);
   for (t = s_main; t < s_total; t += 2) {
     step.template operator()<-1>(t, t % STAGES);
@@ -631,17 +637,19 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BG, int BU, int BM, int WN, int OCC, int STAGES>
+template <int BG, int BU, int BM, int WN, int OCC>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.I + 4 * WN - 1) / (4 * WN));
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC, STAGES>), dim3(tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC>), dim3(tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU>
 static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, hipStream_t stream) {
-  if (cfg == 1) return launch_mfma_t<BG, BU, 128, 32, 1, 4>(p, stream);
-  return launch_mfma_t<BG, BU, 256, 32, 1, 4>(p, stream);
+  // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
+  if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
+  if constexpr (!(BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream) {
