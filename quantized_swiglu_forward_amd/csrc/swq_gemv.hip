@@ -45,7 +45,7 @@ __device__ __forceinline__ void load_chunk(RawChunk<BITS>& r, const uint32_t* W,
                                            int kc) {
   const uint32_t* base = W + row * rw + (int64_t)kc * (BITS);   // BITS words per 32-code chunk
 #pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) r.w[i] = *reinterpret_cast<const u32x4*>(base + 4 * i);
+  for (int i = 0; i < BITS / 4; ++i) r.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 4 * i));
   const int64_t gi = row * ng + (kc * 32) / gs;
   r.sb = (uint32_t)S[gi] | ((uint32_t)B[gi] << 16);
 }
@@ -197,7 +197,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// One lane's x chunk (32 bf16 values) as exact binary16 pairs for the
+// One lane's x chunk (32 values) as exact binary16 pairs for the
 // subnormal-code dot products, scaled by its own power of two: x' = x 2^-e
 // with e the exponent of the chunk's largest magnitude (every element at
 // least 2^-17 of that maximum converts exactly).  xa holds the pairs that
@@ -209,40 +209,61 @@ struct XChunk {
   int e;
 };
 
-__device__ __forceinline__ void load_x_chunk(const uint16_t* x, int kc, u32x4 raw[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) raw[q] = *reinterpret_cast<const u32x4*>(x + kc * 32 + 8 * q);
-}
+// Largest H of the M = 1 kernel: 64 lanes x 2 chunks of 32.
+constexpr int kGemv1MaxH = 4096;
 
-__device__ __forceinline__ void make_x_chunk(const u32x4 raw[4], XChunk& c) {
+// The block converts x once and shares it through LDS.  Thread t converts
+// the 8-value blocks t, t + 256, ...; the four blocks of a 32-value chunk
+// sit in four consecutive lanes, which agree on the chunk's exponent and
+// sum with two DPP steps.  Block j of a chunk is stored as the 16 bytes
+// (16x'0, 16x'4), (x'1, x'5), (16x'2, 16x'6), (x'3, x'7): the operands of
+// code word j in the order the dot products take them.  Lanes past the end
+// of x carry zeros (a quad is all in or all out: H is a multiple of 32).
+__device__ __forceinline__ void stage_x_block(const u32x4& raw, int blk, bool valid, u32x4* xs, float2* xinfo) {
   uint32_t amax = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int j = 0; j < 4; ++j) amax = max(amax, max(raw[j] & 0x7FFFu, (raw[j] >> 16) & 0x7FFFu));
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  const int e = row_exponent(amax);
+  float f[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) amax = max(amax, max(raw[q][j] & 0x7FFFu, (raw[q][j] >> 16) & 0x7FFFu));
-  c.e = row_exponent(amax);
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = bf16_to_f32((uint16_t)(raw[j] & 0xFFFFu));
+    f[2 * j + 1] = bf16_to_f32((uint16_t)(raw[j] >> 16));
+  }
+  u32x4 v;
+  v[0] = as_u32((f16x2){(_Float16)ldexpf(f[0], 4 - e), (_Float16)ldexpf(f[4], 4 - e)});
+  v[1] = as_u32((f16x2){(_Float16)ldexpf(f[1], -e), (_Float16)ldexpf(f[5], -e)});
+  v[2] = as_u32((f16x2){(_Float16)ldexpf(f[2], 4 - e), (_Float16)ldexpf(f[6], 4 - e)});
+  v[3] = as_u32((f16x2){(_Float16)ldexpf(f[3], -e), (_Float16)ldexpf(f[7], -e)});
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
   float sx = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {            // 8-block q: values 8q .. 8q+7
-    float f[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[2 * j] = bf16_to_f32((uint16_t)(raw[q][j] & 0xFFFFu));
-      f[2 * j + 1] = bf16_to_f32((uint16_t)(raw[q][j] >> 16));
-    }
-    // pairs (0,4) and (2,6) meet codes in bits [0,4): 16x'; (1,5), (3,7): x'
-    c.xa[2 * q] = as_u32((f16x2){(_Float16)ldexpf(f[0], 4 - c.e), (_Float16)ldexpf(f[4], 4 - c.e)});
-    c.xb[2 * q] = as_u32((f16x2){(_Float16)ldexpf(f[1], -c.e), (_Float16)ldexpf(f[5], -c.e)});
-    c.xa[2 * q + 1] = as_u32((f16x2){(_Float16)ldexpf(f[2], 4 - c.e), (_Float16)ldexpf(f[6], 4 - c.e)});
-    c.xb[2 * q + 1] = as_u32((f16x2){(_Float16)ldexpf(f[3], -c.e), (_Float16)ldexpf(f[7], -c.e)});
-    sx = __builtin_amdgcn_fdot2(as_h2(c.xa[2 * q]), sixteenth, sx, false);
-    sx = __builtin_amdgcn_fdot2(as_h2(c.xb[2 * q]), one, sx, false);
-    sx = __builtin_amdgcn_fdot2(as_h2(c.xa[2 * q + 1]), sixteenth, sx, false);
-    sx = __builtin_amdgcn_fdot2(as_h2(c.xb[2 * q + 1]), one, sx, false);
+  sx = __builtin_amdgcn_fdot2(as_h2(v[0]), sixteenth, sx, false);
+  sx = __builtin_amdgcn_fdot2(as_h2(v[1]), one, sx, false);
+  sx = __builtin_amdgcn_fdot2(as_h2(v[2]), sixteenth, sx, false);
+  sx = __builtin_amdgcn_fdot2(as_h2(v[3]), one, sx, false);
+  sx += __builtin_amdgcn_update_dpp(0.0f, sx, 0xB1, 0xF, 0xF, false);
+  sx += __builtin_amdgcn_update_dpp(0.0f, sx, 0x4E, 0xF, 0xF, false);
+  if (valid) {
+    xs[blk] = v;
+    if ((blk & 3) == 0) xinfo[blk >> 2] = make_float2(ldexpf(sx, -20), __int_as_float(e));
   }
-  c.sx = ldexpf(sx, -20);
+}
+
+__device__ __forceinline__ void read_x_chunk(const u32x4* xs, const float2* xinfo, int kc, XChunk& c) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = xs[4 * kc + q];
+    c.xa[2 * q] = v[0];
+    c.xb[2 * q] = v[1];
+    c.xa[2 * q + 1] = v[2];
+    c.xb[2 * q + 1] = v[3];
+  }
+  const float2 inf = xinfo[kc];
+  c.sx = inf.x;
+  c.e = __float_as_int(inf.y);
 }
 
 // The chunk's share of sum_k x_k (s q_k + b), in the chunk's own scale 2^(e+20).
@@ -254,25 +275,35 @@ __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChun
   return fmaf(s, P, b * x.sx);
 }
 
-// M = 1.  Lane sl of a column group of lpc lanes owns the 32-code chunks
-// sl, sl + lpc, ... of its column; a wave owns R rounds of 64/lpc columns.
-// Every lane loads its x chunks first, then its whole weight stream, then
-// converts x while the weights arrive; no LDS, no barrier.
+// M = 1.  Lane sl of a column group of lpc = 2^lg lanes owns the 32-code
+// chunks sl, sl + lpc, ... of its column; a wave owns R rounds of 64/lpc
+// columns.  Every thread issues its x load and then its whole weight stream
+// before any arithmetic; the block converts x into LDS while the weights
+// arrive (one barrier, which the weight loads stay in flight across).  With
+// a whole wave per column, the R columns' sums end wave-uniform and lane r
+// runs the epilogue of column r, so one pass serves all R columns.
 template <int BITS_G, int BITS_U, int CPL, int R>
-__global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lpc) {
-  const int lane = threadIdx.x & 63;
-  const int wave_global = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int sub = lane / lpc, sl = lane % lpc;
-  const int cpw = 64 / lpc;
-  const int nchunk = p.H / 32;
+__global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
+  __shared__ u32x4 xs[kGemv1MaxH / 8];
+  __shared__ float2 xinfo[kGemv1MaxH / 32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lpc = 1 << lg;
+  const int wave_global = blockIdx.x * 4 + (tid >> 6);
+  const int sub = lane >> lg, sl = lane & (lpc - 1);
+  const int cpw = 64 >> lg;
+  const int nchunk = p.H / 32, nblk = p.H / 8;
   const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
 
-  // 1. x chunks (loads complete in issue order: x first, so it is not held
-  //    up behind the weight stream)
-  u32x4 raw[CPL][4];
+  // 1. this thread's 8-value blocks of x (loads complete in issue order: x
+  //    first, so it is not held up behind the weight stream)
+  u32x4 xraw[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) load_x_chunk(p.x, min(sl + c * lpc, nchunk - 1), raw[c]);
+  for (int i = 0; i < CPL; ++i) {
+    const int blk = tid + 256 * i;
+    xraw[i] = *reinterpret_cast<const u32x4*>(p.x + 8 * min(blk, nblk - 1));
+  }
 
   // 2. all weight loads of this lane: R columns x CPL chunks x 2 matrices
   RawChunk<BITS_G> rg[R][CPL];
@@ -288,31 +319,52 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lpc) {
     }
   }
 
-  // 3. x' of this lane's chunks
+  // every load is issued before the first wait (for x) below
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. x' into LDS, shared by the block's four waves
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) stage_x_block(xraw[i], tid + 256 * i, tid + 256 * i < nblk, xs, xinfo);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   XChunk xc[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) make_x_chunk(raw[c], xc[c]);
+  for (int c = 0; c < CPL; ++c) read_x_chunk(xs, xinfo, min(sl + c * lpc, nchunk - 1), xc[c]);
 
   // 4. per column: chunk terms, reduction over the column group, epilogue
+  float ag[R], au[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float ag = 0.0f, au = 0.0f;
+    ag[r] = 0.0f;
+    au[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       if (sl + c * lpc < nchunk) {
-        ag += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
-        au += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
+        ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
+        au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
       }
     }
-    if (lpc == 64) {
-      ag = wave_sum(ag);
-      au = wave_sum(au);
-    } else {
-      ag = group_sum(ag, lpc);
-      au = group_sum(au, lpc);
+  }
+  if (lpc == 64) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float gr = wave_sum(ag[r]), ur = wave_sum(au[r]);
+      if (lane == r) {
+        g = gr;
+        u = ur;
+      }
     }
-    const int n = (wave_global * R + r) * cpw + sub;
-    if (sl == 0 && n < p.I) store_out(p, 0, n, ag, au);
+    const int n = wave_global * R + lane;
+    if (lane < R && n < p.I) store_out(p, 0, n, g, u);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
+      const int n = (wave_global * R + r) * cpw + sub;
+      if (sl == 0 && n < p.I) store_out(p, 0, n, g, u);
+    }
   }
 }
 
@@ -464,14 +516,17 @@ static int gemv_lanes_per_column(int H) {
 template <int BG, int BU, int CPL>
 static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
+  int lg = 0;
+  while ((1 << lg) < lpc) ++lg;
   const int cpw = 64 / lpc;
   const int cols_per_wave = cpw * R;
   const int waves = (p.I + cols_per_wave - 1) / cols_per_wave;
   const int blocks = (waves + 3) / 4;
+  if (p.H > kGemv1MaxH || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
   switch (R) {
-    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1>), dim3(blocks), dim3(256), 0, stream, p, lpc); break;
-    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2>), dim3(blocks), dim3(256), 0, stream, p, lpc); break;
-    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4>), dim3(blocks), dim3(256), 0, stream, p, lpc); break;
+    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
