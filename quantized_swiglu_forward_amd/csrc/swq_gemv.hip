@@ -50,6 +50,37 @@ __device__ __forceinline__ void load_chunk(RawChunk<BITS>& r, const uint32_t* W,
   r.sb = (uint32_t)S[gi] | ((uint32_t)B[gi] << 16);
 }
 
+// The same through buffer descriptors whose base is the wave's first column:
+// 32-bit offsets (one VALU op per address), and the descriptor's record count
+// returns zeros for columns past the end.
+struct MatBufs {
+  __amdgpu_buffer_rsrc_t w, s, b;
+  int rw, ng, lg_gs;
+};
+
+__device__ __forceinline__ MatBufs mat_bufs(const uint32_t* W, const uint16_t* S, const uint16_t* B, int64_t n0,
+                                            int ncols, int H, int bits, int gs) {
+  MatBufs m;
+  m.rw = H * bits / 32;
+  m.lg_gs = __builtin_ctz(gs);
+  m.ng = H >> m.lg_gs;
+  m.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + n0 * m.rw), (short)0, ncols * m.rw * 4, 0x00020000);
+  m.s = __builtin_amdgcn_make_buffer_rsrc((void*)(S + n0 * m.ng), (short)0, ncols * m.ng * 2, 0x00020000);
+  m.b = __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * m.ng), (short)0, ncols * m.ng * 2, 0x00020000);
+  return m;
+}
+
+// Chunk kc of column n0 + rel; code loads are nontemporal (each byte is read once).
+template <int BITS>
+__device__ __forceinline__ void load_chunk_buf(RawChunk<BITS>& r, const MatBufs& m, int rel, int kc) {
+  const int wo = (rel * m.rw + kc * BITS) * 4;
+#pragma unroll
+  for (int i = 0; i < BITS / 4; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(m.w, wo + 16 * i, 0, 2);
+  const int go = (rel * m.ng + ((kc * 32) >> m.lg_gs)) * 2;
+  r.sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m.s, go, 0, 0) |
+         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m.b, go, 0, 0) << 16);
+}
+
 // sum over the chunk of x'(q - z) as float32, split as  s*P + (b + z s)*Sx.
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const RawChunk<BITS>& r, const uint32_t xv[16], float sx) {
@@ -197,6 +228,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Row sum over 16 lanes; every lane of the row ends with it.
+__device__ __forceinline__ float row_sum(float v) {
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false);   // row_mirror
+  return v;
+}
+
+// v_permlane32_swap: a' = (a lanes 0-31, b lanes 0-31), b' = (a lanes 32-63,
+// b lanes 32-63), so a' + b' holds a's half-wave partial sums in lanes 0-31
+// and b's in lanes 32-63.  v_permlane16_swap does the same with the odd and
+// even 16-lane rows: a' = (a.r0, b.r0, a.r2, b.r2), b' = (a.r1, b.r1, a.r3, b.r3).
+__device__ __forceinline__ float fold32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float fold16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Lane i < 32 receives lane i + 32's value.
+__device__ __forceinline__ float upper_half(float a) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r[1]);
+}
+
 // One lane's x chunk (32 values) as exact binary16 pairs for the
 // subnormal-code dot products, scaled by its own power of two: x' = x 2^-e
 // with e the exponent of the chunk's largest magnitude (every element at
@@ -281,20 +339,20 @@ __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChun
 // before any arithmetic; the block converts x into LDS while the weights
 // arrive (one barrier, which the weight loads stay in flight across).  With
 // a whole wave per column, the R columns' sums end wave-uniform and lane r
-// runs the epilogue of column r, so one pass serves all R columns.
-template <int BITS_G, int BITS_U, int CPL, int R>
+// runs the epilogue of column r, so one pass serves all R columns.  FULL:
+// H = 2048 CPL exactly (64 lanes per column, every lane CPL chunks).
+template <int BITS_G, int BITS_U, int CPL, int R, bool FULL>
 __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
   __shared__ u32x4 xs[kGemv1MaxH / 8];
   __shared__ float2 xinfo[kGemv1MaxH / 32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  if constexpr (FULL) lg = 6;
   const int lpc = 1 << lg;
-  const int wave_global = blockIdx.x * 4 + (tid >> 6);
+  const int wave_global = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int sub = lane >> lg, sl = lane & (lpc - 1);
   const int cpw = 64 >> lg;
   const int nchunk = p.H / 32, nblk = p.H / 8;
-  const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
-  const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
 
   // 1. this thread's 8-value blocks of x (loads complete in issue order: x
   //    first, so it is not held up behind the weight stream)
@@ -306,16 +364,20 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
   }
 
   // 2. all weight loads of this lane: R columns x CPL chunks x 2 matrices
+  const int64_t n0 = (int64_t)wave_global * R * cpw;           // the wave's first column
+  const int ncols = (int)max((int64_t)0, min((int64_t)R * cpw, (int64_t)p.I - n0));
+  const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
+  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols, p.H, BITS_U, p.gs_u);
   RawChunk<BITS_G> rg[R][CPL];
   RawChunk<BITS_U> ru[R][CPL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int nn = min((wave_global * R + r) * cpw + sub, p.I - 1);
+    const int rel = r * cpw + sub;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int kc = min(sl + c * lpc, nchunk - 1);
-      load_chunk<BITS_G>(rg[r][c], p.wg, p.sg, p.bg, nn, rw_g, ng_g, p.gs_g, kc);
-      load_chunk<BITS_U>(ru[r][c], p.wu, p.su, p.bu, nn, rw_u, ng_u, p.gs_u, kc);
+      load_chunk_buf<BITS_G>(rg[r][c], mg, rel, kc);
+      load_chunk_buf<BITS_U>(ru[r][c], mu, rel, kc);
     }
   }
 
@@ -340,13 +402,24 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
     au[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      if (sl + c * lpc < nchunk) {
+      if (FULL || sl + c * lpc < nchunk) {
         ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
         au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
       }
     }
   }
-  if (lpc == 64) {
+  if (R <= 2 && (FULL || lpc == 64)) {
+    // Sums of the 2R values of the wave with two lane-swap folds and one row
+    // sum: row 0 ends with column 0's gate, row 2 with its up, rows 1 and 3
+    // with column 1's (R = 2); lane 16 r then runs column r's epilogue.
+    const float t0 = fold32(ag[0], au[0]);
+    const float t = R == 2 ? fold16(t0, fold32(ag[R - 1], au[R - 1])) : fold16(t0, t0);
+    const float g = row_sum(t);
+    const float u = upper_half(g);
+    const int col = lane >> 4;
+    const int64_t n = (int64_t)wave_global * R + col;
+    if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, 0, (int)n, g, u);
+  } else if (FULL || lpc == 64) {
     float g = 0.0f, u = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -358,7 +431,7 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
     }
     const int n = wave_global * R + lane;
     if (lane < R && n < p.I) store_out(p, 0, n, g, u);
-  } else {
+  } else if constexpr (!FULL) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
@@ -513,7 +586,7 @@ static int gemv_lanes_per_column(int H) {
   return l;
 }
 
-template <int BG, int BU, int CPL>
+template <int BG, int BU, int CPL, bool FULL>
 static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
   int lg = 0;
@@ -524,9 +597,9 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   const int blocks = (waves + 3) / 4;
   if (p.H > kGemv1MaxH || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
   switch (R) {
-    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
-    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
-    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -558,8 +631,13 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
   const int cpl = (p.H / 32 + lpc - 1) / lpc;
   if (p.M == 1 && cpl <= 2 && !getenv("SWIGLU_Q_GEMV_GENERAL")) {
-    if (cpl == 1) return launch_gemv1_t<BG, BU, 1>(p, gemv1_rounds(), stream);
-    return launch_gemv1_t<BG, BU, 2>(p, gemv1_rounds(), stream);
+    const bool full = lpc == 64 && p.H == 2048 * cpl;
+    if (cpl == 1) {
+      return full ? launch_gemv1_t<BG, BU, 1, true>(p, gemv1_rounds(), stream)
+                  : launch_gemv1_t<BG, BU, 1, false>(p, gemv1_rounds(), stream);
+    }
+    return full ? launch_gemv1_t<BG, BU, 2, true>(p, gemv1_rounds(), stream)
+                : launch_gemv1_t<BG, BU, 2, false>(p, gemv1_rounds(), stream);
   }
   if (p.M <= 1) return launch_gemvm_t<BG, BU, 1>(p, stream);
   if (p.M <= 2) return launch_gemvm_t<BG, BU, 2>(p, stream);
