@@ -341,25 +341,27 @@ __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChun
 // a whole wave per column, the R columns' sums end wave-uniform and lane r
 // runs the epilogue of column r, so one pass serves all R columns.  FULL:
 // H = 2048 CPL exactly (64 lanes per column, every lane CPL chunks).
-template <int BITS_G, int BITS_U, int CPL, int R, bool FULL>
-__global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
+template <int BITS_G, int BITS_U, int CPL, int R, bool FULL, int WPB>
+__global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int lg) {
+  constexpr int NT = 64 * WPB;
+  constexpr int XI = (256 * CPL + NT - 1) / NT;   // 8-value blocks of x per thread
   __shared__ u32x4 xs[kGemv1MaxH / 8];
   __shared__ float2 xinfo[kGemv1MaxH / 32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if constexpr (FULL) lg = 6;
   const int lpc = 1 << lg;
-  const int wave_global = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int wave_global = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int sub = lane >> lg, sl = lane & (lpc - 1);
   const int cpw = 64 >> lg;
   const int nchunk = p.H / 32, nblk = p.H / 8;
 
   // 1. this thread's 8-value blocks of x (loads complete in issue order: x
   //    first, so it is not held up behind the weight stream)
-  u32x4 xraw[CPL];
+  u32x4 xraw[XI];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int blk = tid + 256 * i;
+  for (int i = 0; i < XI; ++i) {
+    const int blk = tid + NT * i;
     xraw[i] = *reinterpret_cast<const u32x4*>(p.x + 8 * min(blk, nblk - 1));
   }
 
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256) void swq_gemv1_kernel(GemvParams p, int lg) {
 
   // 3. x' into LDS, shared by the block's four waves
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) stage_x_block(xraw[i], tid + 256 * i, tid + 256 * i < nblk, xs, xinfo);
+  for (int i = 0; i < XI; ++i) stage_x_block(xraw[i], tid + NT * i, tid + NT * i < nblk, xs, xinfo);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -594,12 +596,13 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   const int cpw = 64 / lpc;
   const int cols_per_wave = cpw * R;
   const int waves = (p.I + cols_per_wave - 1) / cols_per_wave;
-  const int blocks = (waves + 3) / 4;
   if (p.H > kGemv1MaxH || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
+  constexpr int WPB = 4;
+  const int blocks = (waves + WPB - 1) / WPB;
   switch (R) {
-    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
-    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
-    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL>), dim3(blocks), dim3(256), 0, stream, p, lg); break;
+    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
