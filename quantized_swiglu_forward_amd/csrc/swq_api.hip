@@ -101,6 +101,40 @@ int choose_mfma_config(int64_t M, int64_t I) {
   return tiles256 >= 512 ? 0 : 1;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+// With 256 x 128 tiles (one per CU at a time), a partly filled last round
+// leaves CUs idle for a whole tile time.  The columns past the last whole
+// round then go to a second launch of 128 x 128 tiles when that is at most
+// one round of them.  Returns the first column of the second launch, or 0
+// for a single launch.  SWIGLU_Q_MFMA_SPLIT=0 turns this off.
+int choose_column_split(int64_t M, int64_t I, int cfg, int bits_g, int bits_u) {
+  if (cfg != 0 || (bits_g == 8 && bits_u == 8)) return 0;
+  if (const char* s = getenv("SWIGLU_Q_MFMA_SPLIT"); s && s[0] == '0') return 0;
+  const int64_t cus = device_cus();
+  const int64_t mt = (M + 255) / 256, nt = (I + 127) / 128;
+  const int64_t full = mt * nt / cus;
+  if (full == 0 || mt * nt == full * cus) return 0;
+  const int64_t nt1 = full * cus / mt;
+  if (nt1 <= 0 || nt1 >= nt) return 0;
+  const int64_t rest = ((M + 127) / 128) * ((I - 128 * nt1 + 127) / 128);
+  if (rest > cus) return 0;
+  return (int)(128 * nt1);
+}
+
 // Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
 // (binary16), row exponents [M] (int32), then the extra-column B rows
 // [I, kext] (binary16) of the gate and of the up matrix.
@@ -206,18 +240,20 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.wg = Wg; p.sg = (const uint16_t*)sg;
   p.wu = Wu; p.su = (const uint16_t*)su;
   p.M = (int)M; p.H = (int)H; p.I = (int)I;
+  p.n_begin = 0; p.n_end = (int)I;
   p.gs_g = gs_g; p.gs_u = gs_u;
   p.ldx = ldx; p.kext = kext;
   p.bext_g = eg; p.bext_u = eu;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
   const int cfg = choose_mfma_config(M, I);
+  const int n_split = choose_column_split(M, I, cfg, bits_g, bits_u);
   if (logging())
-    fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
-            cfg, kMfmaBM[cfg], kMfmaBN[cfg], (long long)M, (long long)H, (long long)I, bits_g, bits_u,
+    fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) split %d M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
+            cfg, kMfmaBM[cfg], kMfmaBN[cfg], n_split, (long long)M, (long long)H, (long long)I, bits_g, bits_u,
             gs_g, gs_u, mode);
   (void)hipGetLastError();
   if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
-  if (launch_mfma(p, cfg, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
+  if (launch_mfma(p, cfg, n_split, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
   g_calls[SWQ_PATH_MFMA].fetch_add(1, std::memory_order_relaxed);
   return SWQ_OK;
 }

@@ -33,6 +33,7 @@ struct MfmaParams {
   const uint32_t* wu;
   const uint16_t* su;
   int M, H, I;
+  int n_begin, n_end;  // output columns [n_begin, n_end) of this launch
   int gs_g, gs_u;
   int ldx, kext;
   const _Float16* bext_g;
@@ -79,7 +80,9 @@ inline int kext_columns(int64_t H, int g0) {
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
-hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream);
+// cfg: tile shape (kMfmaBM/kMfmaBN); n_split > 0 with cfg 0: columns
+// [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
+hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
 
 }  // namespace swq

@@ -290,16 +290,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int q8 = T / 8, r8 = T % 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int logical = xcd < r8 ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
-  const int mtiles = (p.M + BM - 1) / BM, ntiles = (p.I + BN - 1) / BN;
+  const int mtiles = (p.M + BM - 1) / BM, ntiles = (p.n_end - p.n_begin + BN - 1) / BN;
   const int per_group = GM * ntiles;
   const int grp = logical / per_group;
   const int first_m = grp * GM;
   const int gsz = min(mtiles - first_m, GM);
   const int in_grp = logical - grp * per_group;
   const int m0 = (first_m + in_grp % gsz) * BM;
-  const int n0 = (in_grp / gsz) * BN;
+  const int n0 = p.n_begin + (in_grp / gsz) * BN;
   const int rows = min(BM, p.M - m0);
-  const int cols = min(BN, p.I - n0);
+  const int cols = min(BN, p.n_end - n0);
 
   const int s_main = p.H / 32;
   const int s_ext = p.kext / 32;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (lr >= rows || ocol >= p.I) continue;
+        if (lr >= rows || ocol >= p.n_end) continue;
         const int e = rexp[lr];
         const float g = ldexpf(acc_g[i][f][r], e);
         const float u = ldexpf(acc_u[i][f][r], e);
@@ -639,24 +639,34 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
 
 template <int BG, int BU, int BM, int WN, int OCC>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.I + 4 * WN - 1) / (4 * WN));
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.n_end - p.n_begin + 4 * WN - 1) / (4 * WN));
+  if (tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC>), dim3(tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU>
-static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, hipStream_t stream) {
+static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
   // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
   if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
-  if constexpr (!(BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
+  if constexpr (!(BG == 8 && BU == 8)) {
+    if (n_split <= 0 || n_split >= p.I) return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
+    // columns [0, n_split) in whole rounds of 256 x 128 tiles, the rest in 128 x 128 tiles
+    MfmaParams a = p, b = p;
+    a.n_end = n_split;
+    b.n_begin = n_split;
+    const hipError_t e = launch_mfma_t<BG, BU, 256, 32, 1>(a, stream);
+    if (e != hipSuccess) return e;
+    return launch_mfma_t<BG, BU, 128, 32, 1>(b, stream);
+  }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma(const MfmaParams& p, int cfg, int bits_g, int bits_u, hipStream_t stream) {
-  if (bits_g == 4 && bits_u == 4) return launch_mfma_bits<4, 4>(p, cfg, stream);
-  if (bits_g == 8 && bits_u == 4) return launch_mfma_bits<8, 4>(p, cfg, stream);
-  if (bits_g == 4 && bits_u == 8) return launch_mfma_bits<4, 8>(p, cfg, stream);
-  if (bits_g == 8 && bits_u == 8) return launch_mfma_bits<8, 8>(p, cfg, stream);
+hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream) {
+  if (bits_g == 4 && bits_u == 4) return launch_mfma_bits<4, 4>(p, cfg, n_split, stream);
+  if (bits_g == 8 && bits_u == 4) return launch_mfma_bits<8, 4>(p, cfg, n_split, stream);
+  if (bits_g == 4 && bits_u == 8) return launch_mfma_bits<4, 8>(p, cfg, n_split, stream);
+  if (bits_g == 8 && bits_u == 8) return launch_mfma_bits<8, 8>(p, cfg, n_split, stream);
   return hipErrorInvalidValue;
 }
 
