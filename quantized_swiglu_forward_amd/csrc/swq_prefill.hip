@@ -411,8 +411,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   f16x8 a0[MF], a1[MF];
   f16x8 g0a[NF], g0b[NF], u0a[NF], u0b[NF];     // sub-step 0: gate planes, up planes
   f16x8 g1a[NF], g1b[NF], u1a[NF], u1b[NF];     // sub-step 1
-  uint32_t cw_g[NF][BITS_G / 2], cw_u[NF][BITS_U / 2];   // this lane's codes of the current K-step
-  f16x2 sg2[NF], su2[NF];                                 // and its scales
+  // this lane's codes and scales of the current K-step (c) and of the next one (n)
+  uint32_t cw_gc[NF][BITS_G / 2], cw_uc[NF][BITS_U / 2], cw_gn[NF][BITS_G / 2], cw_un[NF][BITS_U / 2];
+  f16x2 sg_c[NF], su_c[NF], sg_n[NF], su_n[NF];
 
   const uint32_t sw = (uint32_t)((l32 >> 2) & 3);
   const uint32_t a_lds0 = (uint32_t)(l32 * 64) + (((2 * half) ^ sw) * 16);
@@ -424,58 +425,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
     for (int i = 0; i < MF; ++i) a[i] = *reinterpret_cast<const f16x8*>(st + i * 32 * 64);
   };
-  // B operands of sub-step ks of K-step t from stage `slot` (extra columns) or
-  // the code ring (ks == 0 also fetches the step's codes and scales)
-  auto read_b = [&](int slot, int t, bool ext, int ks, f16x8 (&ga)[NF], f16x8 (&gb)[NF], f16x8 (&ua)[NF],
-                    f16x8 (&ub)[NF]) {
+  // this lane's codes and scales of code K-step t, from the code ring
+  auto load_codes = [&](int t, uint32_t (&cg)[NF][BITS_G / 2], uint32_t (&cu)[NF][BITS_U / 2], f16x2 (&s_g)[NF],
+                        f16x2 (&s_u)[NF]) {
+    const unsigned char* ring = ssmem + ((t / SS) & 1) * SS_SLOT;
+    const int q = t % SS;                              // K-step within the super-step
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(ring + SS_CODE_BYTES);
+    const int kg = (32 * q) >> lg_g, ku = (32 * q) >> lg_u;   // group slot of this K-step
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int n = w * WN + f * 32 + l32;
+      s_g[f] = bf16_to_h2((uint16_t)sc[4 * n + kg]);
+      s_u[f] = bf16_to_h2((uint16_t)sc[4 * BN + 4 * n + ku]);
+      // 4-bit: chunk q holds the K-step, this lane's two 8-code blocks at half * 8;
+      // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half
+      const unsigned char* qg = BITS_G == 4
+          ? ring + n * (CPR_G * 16) + ((q ^ swz(n, CPR_G)) * 16) + half * 8
+          : ring + n * (CPR_G * 16) + (((2 * q + half) ^ swz(n, CPR_G)) * 16);
+      const unsigned char* qu = BITS_U == 4
+          ? ring + SSG_BYTES + n * (CPR_U * 16) + ((q ^ swz(n, CPR_U)) * 16) + half * 8
+          : ring + SSG_BYTES + n * (CPR_U * 16) + (((2 * q + half) ^ swz(n, CPR_U)) * 16);
+      if constexpr (BITS_G == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
+        cg[f][0] = v[0]; cg[f][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
+        cg[f][0] = v[0]; cg[f][1] = v[1]; cg[f][2] = v[2]; cg[f][3] = v[3];
+      }
+      if constexpr (BITS_U == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
+        cu[f][0] = v[0]; cu[f][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
+        cu[f][0] = v[0]; cu[f][1] = v[1]; cu[f][2] = v[2]; cu[f][3] = v[3];
+      }
+    }
+  };
+  // B operands of sub-step ks from codes and scales in registers
+  auto dequant = [&](int ks, const uint32_t (&cg)[NF][BITS_G / 2], const uint32_t (&cu)[NF][BITS_U / 2],
+                     const f16x2 (&s_g)[NF], const f16x2 (&s_u)[NF], f16x8 (&ga)[NF], f16x8 (&gb)[NF],
+                     f16x8 (&ua)[NF], f16x8 (&ub)[NF]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      dequant_block<BITS_G>(&cg[f][ks * (BITS_G / 4)], s_g[f], ga[f], gb[f]);
+      dequant_block<BITS_U>(&cu[f][ks * (BITS_U / 4)], s_u[f], ua[f], ub[f]);
+    }
+  };
+  // B operands of sub-step ks of an extra-column step from stage `slot` (one
+  // matrix per step; its operands go to the gate slots)
+  auto read_ext = [&](int slot, int ks, f16x8 (&ga)[NF]) {
     const unsigned char* sb = smem + slot * STAGE + A_BYTES;
-    if (!ext) {
-      if (ks == 0) {
-        const unsigned char* ring = ssmem + ((t / SS) & 1) * SS_SLOT;
-        const int q = t % SS;                          // K-step within the super-step
-        const uint32_t* sc = reinterpret_cast<const uint32_t*>(ring + SS_CODE_BYTES);
-        const int kg = (32 * q) >> lg_g, ku = (32 * q) >> lg_u;   // group slot of this K-step
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int n = w * WN + f * 32 + l32;
-          sg2[f] = bf16_to_h2((uint16_t)sc[4 * n + kg]);
-          su2[f] = bf16_to_h2((uint16_t)sc[4 * BN + 4 * n + ku]);
-          // 4-bit: chunk q holds the K-step, this lane's two 8-code blocks at half * 8;
-          // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half
-          const unsigned char* qg = BITS_G == 4
-              ? ring + n * (CPR_G * 16) + ((q ^ swz(n, CPR_G)) * 16) + half * 8
-              : ring + n * (CPR_G * 16) + (((2 * q + half) ^ swz(n, CPR_G)) * 16);
-          const unsigned char* qu = BITS_U == 4
-              ? ring + SSG_BYTES + n * (CPR_U * 16) + ((q ^ swz(n, CPR_U)) * 16) + half * 8
-              : ring + SSG_BYTES + n * (CPR_U * 16) + (((2 * q + half) ^ swz(n, CPR_U)) * 16);
-          if constexpr (BITS_G == 4) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
-            cw_g[f][0] = v[0]; cw_g[f][1] = v[1];
-          } else {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
-            cw_g[f][0] = v[0]; cw_g[f][1] = v[1]; cw_g[f][2] = v[2]; cw_g[f][3] = v[3];
-          }
-          if constexpr (BITS_U == 4) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
-            cw_u[f][0] = v[0]; cw_u[f][1] = v[1];
-          } else {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(qu);
-            cw_u[f][0] = v[0]; cw_u[f][1] = v[1]; cw_u[f][2] = v[2]; cw_u[f][3] = v[3];
-          }
-        }
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        dequant_block<BITS_G>(&cw_g[f][ks * (BITS_G / 4)], sg2[f], ga[f], gb[f]);
-        dequant_block<BITS_U>(&cw_u[f][ks * (BITS_U / 4)], su2[f], ua[f], ub[f]);
-      }
-    } else {
-      // one matrix per extra-column step; its operands go to the gate slots
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int n = w * WN + f * 32 + l32;
-        ga[f] = *reinterpret_cast<const f16x8*>(sb + n * 64 + (((2 * half + ks) ^ sw) * 16));
-      }
+    for (int f = 0; f < NF; ++f) {
+      const int n = w * WN + f * 32 + l32;
+      ga[f] = *reinterpret_cast<const f16x8*>(sb + n * 64 + (((2 * half + ks) ^ sw) * 16));
     }
   };
   // kind 0: code step (both matrices); 1: extra columns of the gate; 2: of the up matrix
@@ -549,9 +552,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     constexpr int NA = W2_EXT ? N_EXT : N_MAIN;
     const int nx = (ph + 1) % STAGES, is = (ph + STAGES - 1) % STAGES;
     read_a(ph, 1, a1);
-    read_b(ph, t, KIND != 0, 1, g1a, g1b, u1a, u1b);
+    if constexpr (KIND == 0) dequant(1, cw_gc, cw_uc, sg_c, su_c, g1a, g1b, u1a, u1b);
+    else read_ext(ph, 1, g1a);
+    // the next code step's codes: its super-step landed before the previous barrier
+    if constexpr (!NXT_EXT) load_codes(t + 1, cw_gn, cw_un, sg_n, su_n);
     mfma(KIND, a0, g0a, g0b, u0a, u0b);
-    if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
+    if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
     // stage t+1 and its super-step complete for every wave, and every wave is done with stage t-1
     if (ph == 1) wait_vmcnt<NA + N_SS>();
     else wait_vmcnt<NA>();
@@ -559,9 +565,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     issue(is, t + STAGES - 1, IS_EXT);
     if (ph == 0) issue_ss(t / SS + 1);
     read_a(nx, 0, a0);
-    read_b(nx, t + 1, NXT_EXT, 0, g0a, g0b, u0a, u0b);
+    if constexpr (!NXT_EXT) dequant(0, cw_gn, cw_un, sg_n, su_n, g0a, g0b, u0a, u0b);
+    else read_ext(nx, 0, g0a);
     mfma(KIND, a1, g1a, g1b, u1a, u1b);
-    if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
+    if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
+    if constexpr (!NXT_EXT) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int j = 0; j < BITS_G / 2; ++j) cw_gc[f][j] = cw_gn[f][j];
+#pragma unroll
+        for (int j = 0; j < BITS_U / 2; ++j) cw_uc[f][j] = cw_un[f][j];
+        sg_c[f] = sg_n[f];
+        su_c[f] = su_n[f];
+      }
+    }
   };
 
   // ---- prologue: super-step 0 and K-steps 0 .. 2 in flight, step 0 complete, its first operands read
@@ -578,7 +596,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   }
   block_barrier();
   read_a(0, 0, a0);
-  read_b(0, 0, 0 >= s_main, 0, g0a, g0b, u0a, u0b);
+  if (0 < s_main) {
+    load_codes(0, cw_gc, cw_uc, sg_c, su_c);
+    dequant(0, cw_gc, cw_uc, sg_c, su_c, g0a, g0b, u0a, u0b);
+  } else {
+    read_ext(0, 0, g0a);
+  }
 
   // ---- K loop: code steps, the last three code steps, extra-column steps in gate/up pairs
   const int t_code = max(0, s_main - 3);
