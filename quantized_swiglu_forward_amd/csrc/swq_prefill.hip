@@ -411,9 +411,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   f16x8 a0[MF], a1[MF];
   f16x8 g0a[NF], g0b[NF], u0a[NF], u0b[NF];     // sub-step 0: gate planes, up planes
   f16x8 g1a[NF], g1b[NF], u1a[NF], u1b[NF];     // sub-step 1
-  // this lane's codes and scales of the current K-step (c) and of the next one (n)
-  uint32_t cw_gc[NF][BITS_G / 2], cw_uc[NF][BITS_U / 2], cw_gn[NF][BITS_G / 2], cw_un[NF][BITS_U / 2];
-  f16x2 sg_c[NF], su_c[NF], sg_n[NF], su_n[NF];
+  // this lane's codes and scales of two consecutive code K-steps: step t
+  // uses set P and loads step t+1 into set P^1 (in the unrolled main loop P
+  // alternates; elsewhere P = 0 and set 1 is copied back after the step)
+  uint32_t cw_g[2][NF][BITS_G / 2], cw_u[2][NF][BITS_U / 2];
+  f16x2 s_g2[2][NF], s_u2[2][NF];
 
   const uint32_t sw = (uint32_t)((l32 >> 2) & 3);
   const uint32_t a_lds0 = (uint32_t)(l32 * 64) + (((2 * half) ^ sw) * 16);
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // D in [1, 3]: D = s_main - t (steps t+D and later are extra-column steps);
   // D = -1 / -2: extra-column step of the gate / the up matrix.  Every kind is
   // a compile-time constant.
-  auto step = [&]<int D>(int t, int ph) {
+  auto step = [&]<int D, int P = 0, bool COPY = true>(int t, int ph) {
     constexpr int KIND = D >= 0 ? 0 : -D;                      // MFMA kind of step t
     constexpr bool NXT_EXT = D < 0 || D == 1;
     constexpr bool W2_EXT = D < 0 || D == 1 || D == 2;         // is step t+2 an extra-column step
@@ -552,32 +554,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     constexpr int NA = W2_EXT ? N_EXT : N_MAIN;
     const int nx = (ph + 1) % STAGES, is = (ph + STAGES - 1) % STAGES;
     read_a(ph, 1, a1);
-    if constexpr (KIND == 0) dequant(1, cw_gc, cw_uc, sg_c, su_c, g1a, g1b, u1a, u1b);
+    if constexpr (KIND == 0) dequant(1, cw_g[P], cw_u[P], s_g2[P], s_u2[P], g1a, g1b, u1a, u1b);
     else read_ext(ph, 1, g1a);
     // the next code step's codes: its super-step landed before the previous barrier
-    if constexpr (!NXT_EXT) load_codes(t + 1, cw_gn, cw_un, sg_n, su_n);
+    if constexpr (!NXT_EXT) load_codes(t + 1, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1]);
     mfma(KIND, a0, g0a, g0b, u0a, u0b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
     // stage t+1 and its super-step complete for every wave, and every wave is done with stage t-1
+    // (scheduling fences keep the first half's MFMAs ahead of the wait)
+    __builtin_amdgcn_sched_barrier(0);
     if (ph == 1) wait_vmcnt<NA + N_SS>();
     else wait_vmcnt<NA>();
     block_barrier();
     issue(is, t + STAGES - 1, IS_EXT);
     if (ph == 0) issue_ss(t / SS + 1);
     read_a(nx, 0, a0);
-    if constexpr (!NXT_EXT) dequant(0, cw_gn, cw_un, sg_n, su_n, g0a, g0b, u0a, u0b);
+    if constexpr (!NXT_EXT) dequant(0, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1], g0a, g0b, u0a, u0b);
     else read_ext(nx, 0, g0a);
     mfma(KIND, a1, g1a, g1b, u1a, u1b);
     if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
-    if constexpr (!NXT_EXT) {
+    __builtin_amdgcn_sched_barrier(0);   // each step is its own scheduling region
+    if constexpr (COPY && !NXT_EXT) {
+      static_assert(P == 0, "copies go back to set 0");
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
 #pragma unroll
-        for (int j = 0; j < BITS_G / 2; ++j) cw_gc[f][j] = cw_gn[f][j];
+        for (int j = 0; j < BITS_G / 2; ++j) cw_g[0][f][j] = cw_g[1][f][j];
 #pragma unroll
-        for (int j = 0; j < BITS_U / 2; ++j) cw_uc[f][j] = cw_un[f][j];
-        sg_c[f] = sg_n[f];
-        su_c[f] = su_n[f];
+        for (int j = 0; j < BITS_U / 2; ++j) cw_u[0][f][j] = cw_u[1][f][j];
+        s_g2[0][f] = s_g2[1][f];
+        s_u2[0][f] = s_u2[1][f];
       }
     }
   };
@@ -597,8 +603,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   block_barrier();
   read_a(0, 0, a0);
   if (0 < s_main) {
-    load_codes(0, cw_gc, cw_uc, sg_c, su_c);
-    dequant(0, cw_gc, cw_uc, sg_c, su_c, g0a, g0b, u0a, u0b);
+    load_codes(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0]);
+    dequant(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0], g0a, g0b, u0a, u0b);
   } else {
     read_ext(0, 0, g0a);
   }
@@ -607,10 +613,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int t_code = max(0, s_main - 3);
   int t = 0;
   for (; t + STAGES <= t_code; t += STAGES) {
-    step.template operator()<0>(t, 0);
-    step.template operator()<0>(t + 1, 1);
-    step.template operator()<0>(t + 2, 2);
-    step.template operator()<0>(t + 3, 3);
+    step.template operator()<0, 0, false>(t, 0);
+    step.template operator()<0, 1, false>(t + 1, 1);
+    step.template operator()<0, 0, false>(t + 2, 2);
+    step.template operator()<0, 1, false>(t + 3, 3);
   }
   for (; t < t_code; ++t) step.template operator()<0>(t, t % STAGES);
   if (s_main >= 3) step.template operator()<3>(s_main - 3, (s_main - 3) % STAGES);
