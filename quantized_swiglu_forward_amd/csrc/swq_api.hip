@@ -136,10 +136,11 @@ int choose_column_split(int64_t M, int64_t I, int cfg, int bits_g, int bits_u) {
 }
 
 // Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
-// (binary16), row exponents [M] (int32), then the extra-column B rows
-// [I, kext] (binary16) of the gate and of the up matrix.
+// (binary16), row exponents [M] (int32), the extra-column B rows [I, kext]
+// (binary16) of the gate and of the up matrix, then the scale tiles
+// (4 KB per 128 columns and 128 inputs).
 struct WsLayout {
-  int64_t xa, xexp, eg, eu, total;
+  int64_t xa, xexp, eg, eu, sc, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -152,7 +153,9 @@ WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bi
   w.xexp = align256(M * (H + kext) * 2);
   w.eg = w.xexp + align256(M * 4);
   w.eu = w.eg + plane;
-  w.total = w.eu + plane;
+  w.sc = w.eu + plane;
+  const int64_t tiles = (I + kScaleTileCols - 1) / kScaleTileCols * ((H + 127) / 128);
+  w.total = w.sc + align256(tiles * kScaleTileWords * 4);
   (void)bits_g;
   (void)bits_u;
   return w;
@@ -224,6 +227,8 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   int* xexp = (int*)(wsb + L.xexp);
   _Float16* eg = (_Float16*)(wsb + L.eg);
   _Float16* eu = (_Float16*)(wsb + L.eu);
+  uint32_t* scl = (uint32_t*)(wsb + L.sc);
+  const int nss = (int)((H + 127) / 128);
 
   PrepParams pp;
   pp.x = (const uint16_t*)x;
@@ -234,6 +239,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.g0 = g0; pp.ldx = ldx; pp.kext = kext;
   pp.xa = xa; pp.xexp = xexp;
   pp.bext_g = eg; pp.bext_u = eu;
+  pp.scl = scl; pp.nss = nss;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;
@@ -241,6 +247,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.wu = Wu; p.su = (const uint16_t*)su;
   p.M = (int)M; p.H = (int)H; p.I = (int)I;
   p.n_begin = 0; p.n_end = (int)I;
+  p.scl = scl; p.nss = nss;
   p.gs_g = gs_g; p.gs_u = gs_u;
   p.ldx = ldx; p.kext = kext;
   p.bext_g = eg; p.bext_u = eu;

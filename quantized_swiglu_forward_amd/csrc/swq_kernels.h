@@ -23,6 +23,8 @@ struct PrepParams {
   int* xexp;           // out: [M] row exponents e (x' = x * 2^-e)
   _Float16* bext_g;    // out: [I, kext] extra-column B rows of the gate (c_hi, c_lo, c_hi per group)
   _Float16* bext_u;    // out: same for the up matrix
+  uint32_t* scl;       // out: scale tiles, see kScaleTileWords
+  int nss;             // super-steps of 128 inputs: ceil(H / 128)
 };
 
 struct MfmaParams {
@@ -34,6 +36,8 @@ struct MfmaParams {
   const uint16_t* su;
   int M, H, I;
   int n_begin, n_end;  // output columns [n_begin, n_end) of this launch
+  const uint32_t* scl; // scale tiles written by the prep kernel
+  int nss;
   int gs_g, gs_u;
   int ldx, kext;
   const _Float16* bext_g;
@@ -59,6 +63,13 @@ struct GemvParams {
   float* dbg_g;
   float* dbg_u;
 };
+
+// Scale tiles: for every 128 output columns and every 128 inputs (a
+// super-step of four K-steps of 32), the scale of each column's group in
+// each K-step and matrix as a binary16 pair (s, s), ordered
+// [K-step q][matrix][column]: 4 * 2 * 128 words, one contiguous 4 KB block.
+constexpr int kScaleTileCols = 128;
+constexpr int kScaleTileWords = 4 * 2 * kScaleTileCols;
 
 // Tile shapes of the MFMA kernel: rows, and columns per matrix.
 constexpr int kMfmaConfigs = 2;

@@ -133,12 +133,42 @@ __device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t
   if (k + 2 < kext) d[2] = chi;
 }
 
+// Scale tiles: thread (column n, super-step j) writes the 4 K-steps x 2
+// matrices words of n in tile (n / 128, j); columns past I get zeros.  A
+// bf16 scale with magnitude in [2^-17, 2^8) converts to binary16 exactly.
+__device__ __forceinline__ void prep_scale_tile(const PrepParams& p, int64_t n, int j) {
+  const int s_main = p.H / 32;
+  uint32_t* dst = p.scl + ((n / kScaleTileCols) * p.nss + j) * kScaleTileWords + (n % kScaleTileCols);
+  const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = 4 * j + q;
+    uint32_t vg = 0, vu = 0;
+    if (n < p.I && t < s_main) {
+      const _Float16 hg = (_Float16)bf16_to_f32(p.sg[n * ng_g + (32 * t) / p.gs_g]);
+      const _Float16 hu = (_Float16)bf16_to_f32(p.su[n * ng_u + (32 * t) / p.gs_u]);
+      vg = as_u32((f16x2){hg, hg});
+      vu = as_u32((f16x2){hu, hu});
+    }
+    dst[(2 * q) * kScaleTileCols] = vg;
+    dst[(2 * q + 1) * kScaleTileCols] = vu;
+  }
+}
+
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   if ((int)blockIdx.x < p.M) {
     prep_x_row(p, blockIdx.x);
     return;
   }
   const int per_row = (p.kext + 2) / 3;               // triplets per row, the last ones padding
+  const int64_t ext_blocks = (2 * (int64_t)p.I * per_row + 255) / 256;
+  if ((int64_t)blockIdx.x - p.M >= ext_blocks) {
+    // scale tiles: consecutive threads take consecutive columns of one super-step
+    const int64_t cols = (int64_t)(p.I + kScaleTileCols - 1) / kScaleTileCols * kScaleTileCols;
+    const int64_t i = ((int64_t)blockIdx.x - p.M - ext_blocks) * 256 + threadIdx.x;
+    if (i < cols * p.nss) prep_scale_tile(p, i % cols, (int)(i / cols));
+    return;
+  }
   const int64_t idx = (int64_t)(blockIdx.x - p.M) * 256 + threadIdx.x;
   const int64_t per_mat = (int64_t)p.I * per_row;
   const int ngroups = p.H / p.g0;
@@ -192,19 +222,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uint64_t)(lds_ptr_t)p;
 }
 
-// Buffer loads that write LDS: lane i's data lands at base + 16 i (16-byte
-// loads) or base + 4 i (2-byte loads, zero-extended).  They are issued from
-// inline assembly so that the compiler does not serialise every later LDS
-// read behind them (it cannot tell the stages apart); the kernel orders them
-// itself with explicit vmcnt waits and barriers.  m0 carries the LDS base.
+// Buffer loads that write LDS: lane i's 16 bytes land at base + 16 i.  They
+// are issued from inline assembly so that the compiler does not serialise
+// every later LDS read behind them (it cannot tell the stages apart); the
+// kernel orders them itself with explicit vmcnt waits and barriers.  m0
+// carries the LDS base.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds_base), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void dma2(i32x4 rs, uint32_t lds_base, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
                ::"s"(lds_base), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -265,14 +291,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   constexpr int A_INSTR = BM * 4 / NT;
   constexpr int B_EXT_INSTR = EXT_BYTES / 16 / NT;
   constexpr int SS_CODE_INSTR = SS_CODE_BYTES / 16 / NT;
-  constexpr int SS_SCALE_INSTR = 2 * BN * 4 / NT;
+  constexpr int SS_SCALE_INSTR = kScaleTileWords * 4 / 16 / NT;   // one 4 KB scale tile
   constexpr int N_SS = SS_CODE_INSTR + SS_SCALE_INSTR;  // buffer loads a thread issues per super-step
   constexpr int N_MAIN = A_INSTR;                       // ... per code K-step
   constexpr int N_EXT = A_INSTR + B_EXT_INSTR;          // ... per extra-column K-step
   constexpr int GM = 4;                                // row tiles per group of the tile order
   static_assert(SSG_BYTES % (16 * NT) == 0 && SSU_BYTES % (16 * NT) == 0 && (BN * 4) % NT == 0,
                 "each code or scale DMA instruction reads one matrix");
-  static_assert(BM <= NT && A_INSTR >= 1 && B_EXT_INSTR >= 1 && SS_SCALE_INSTR >= 1, "tile shape");
+  static_assert(BM <= NT && A_INSTR >= 1 && B_EXT_INSTR >= 1 && SS_SCALE_INSTR == 1, "tile shape");
+  static_assert(BN == kScaleTileCols && kScaleTileWords * 4 == 2 * BN * 16, "scale tile = ring slot scale area");
   static_assert(STAGES == SS, "a stage slot and the super-step phase are both t % 4");
   static_assert(STAGES * STAGE + 2 * SS_SLOT + BM * 4 <= 160 * 1024, "LDS");
 
@@ -305,15 +332,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int s_ext = p.kext / 32;
   const int s_total = s_main + 2 * s_ext;              // extra-column steps: gate then up, per 32 columns
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
-  const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
 
   // x' tile rows of K-step s: (s * M + m0 + row) * 64 bytes from the start of x'
   const i32x4 rs_a = make_srsrc(p.xa + (int64_t)m0 * 32, (uint32_t)(((int64_t)(p.ldx / 32) * p.M - m0) * 64));
   const uint32_t a_step = (uint32_t)p.M * 64;
   const i32x4 rs_wg = make_srsrc(p.wg + (int64_t)n0 * rw_g, (uint32_t)cols * rw_g * 4);
   const i32x4 rs_wu = make_srsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols * rw_u * 4);
-  const i32x4 rs_sg = make_srsrc(p.sg + (int64_t)n0 * ng_g, (uint32_t)cols * ng_g * 2);
-  const i32x4 rs_su = make_srsrc(p.su + (int64_t)n0 * ng_u, (uint32_t)cols * ng_u * 2);
+  const i32x4 rs_sc = make_srsrc(p.scl + (int64_t)(n0 / BN) * p.nss * kScaleTileWords,
+                                 (uint32_t)p.nss * kScaleTileWords * 4);
   const i32x4 rs_eg = make_srsrc(p.bext_g + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
   const i32x4 rs_eu = make_srsrc(p.bext_u + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
 
@@ -348,18 +374,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int L = j * NT + tid, row = L >> 2, c = (L & 3) ^ ((row >> 2) & 3);
     e_voff[j] = (uint32_t)(row * p.kext * 2 + c * 16);
   }
-  // super-step scales: 4 slots per row and matrix for the 128/gs groups the
-  // super-step touches (slots past the last one repeat it); piece L: matrix
-  // L / (4*BN), row (L % (4*BN)) / 4, slot L % 4
-  const int gps_g = 128 / p.gs_g, gps_u = 128 / p.gs_u;
-  uint32_t s_voff[SS_SCALE_INSTR];
-#pragma unroll
-  for (int j = 0; j < SS_SCALE_INSTR; ++j) {
-    const int L = j * NT + tid, rl = L % (4 * BN), r = rl / 4, k = rl % 4;
-    s_voff[j] = j * NT < 4 * BN ? (uint32_t)(r * ng_g * 2 + min(k, gps_g - 1) * 2)
-                                : (uint32_t)(r * ng_u * 2 + min(k, gps_u - 1) * 2);
-  }
-  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
+  // super-step scales: the tile's 4 KB block, 16 bytes per thread in order
+  const uint32_t s_voff[SS_SCALE_INSTR] = {(uint32_t)tid * 16};
 
   // row exponents of the tile: loaded first, published through LDS after the K loop
   const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;
@@ -390,10 +406,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       else dma16(rs_wu, sl + (q * NT + w * 64) * 16, c_voff[q], (uint32_t)(j * CPR_U * 16));
     }
 #pragma unroll
-    for (int q = 0; q < SS_SCALE_INSTR; ++q) {
-      if (q * NT < 4 * BN) dma2(rs_sg, sl + SS_CODE_BYTES + (q * NT + w * 64) * 4, s_voff[q], (uint32_t)((128 * j) >> lg_g) * 2);
-      else dma2(rs_su, sl + SS_CODE_BYTES + (q * NT + w * 64) * 4, s_voff[q], (uint32_t)((128 * j) >> lg_u) * 2);
-    }
+    for (int q = 0; q < SS_SCALE_INSTR; ++q)
+      dma16(rs_sc, sl + SS_CODE_BYTES + w * 64 * 16, s_voff[q], (uint32_t)j * kScaleTileWords * 4);
   };
 
   f32x16 acc_g[MF][NF], acc_u[MF][NF];
@@ -433,12 +447,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const unsigned char* ring = ssmem + ((t / SS) & 1) * SS_SLOT;
     const int q = t % SS;                              // K-step within the super-step
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(ring + SS_CODE_BYTES);
-    const int kg = (32 * q) >> lg_g, ku = (32 * q) >> lg_u;   // group slot of this K-step
+
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int n = w * WN + f * 32 + l32;
-      s_g[f] = bf16_to_h2((uint16_t)sc[4 * n + kg]);
-      s_u[f] = bf16_to_h2((uint16_t)sc[4 * BN + 4 * n + ku]);
+      s_g[f] = as_h2(sc[(2 * q) * BN + n]);
+      s_u[f] = as_h2(sc[(2 * q + 1) * BN + n]);
       // 4-bit: chunk q holds the K-step, this lane's two 8-code blocks at half * 8;
       // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half
       const unsigned char* qg = BITS_G == 4
@@ -533,12 +547,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
   };
 
-  // Loads of K-step s are issued STAGES - 1 = 3 steps ahead, at the start of
-  // step s - 3, and the codes and scales of super-step j at the start of step
-  // SS*(j-1).  At the barrier of step t everything issued up to step t-2 must
-  // have landed; only the loads of step t-1 may still be in flight: the x'
-  // (and extra-column) loads of K-step t+2, and those of super-step t/SS + 1 if
-  // step t-1 started a super-step.
+  // Loads of K-step s are issued STAGES - 1 = 3 steps ahead, after the
+  // barrier of step s - 3, and the codes and scales of super-step j at the
+  // start of step SS*(j-1) + 1 (before that step's x' loads).  At the barrier
+  // of step t everything issued before step t-1's x' loads must have landed:
+  // only those (K-step t+2) may still be in flight, and in a step that issued
+  // a super-step, the super-step too.  A super-step has therefore landed at the
+  // barrier of the step after the one that issued it, a step before its first
+  // codes are read (in the first half of step SS*j - 1).
 
   // one K-step t in stage ph = t % STAGES: sub-step (t, 0) while (t, 1) is
   // prepared from the same stage, then the barrier, then sub-step (t, 1)
@@ -553,6 +569,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     constexpr bool IS_EXT = D != 0;
     constexpr int NA = W2_EXT ? N_EXT : N_MAIN;
     const int nx = (ph + 1) % STAGES, is = (ph + STAGES - 1) % STAGES;
+    // codes and scales of the next super-step, apart from the x' loads that follow the barrier
+    if (ph == 1) issue_ss(t / SS + 1);
     read_a(ph, 1, a1);
     if constexpr (KIND == 0) dequant(1, cw_g[P], cw_u[P], s_g2[P], s_u2[P], g1a, g1b, u1a, u1b);
     else read_ext(ph, 1, g1a);
@@ -567,7 +585,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     else wait_vmcnt<NA>();
     block_barrier();
     issue(is, t + STAGES - 1, IS_EXT);
-    if (ph == 0) issue_ss(t / SS + 1);
     read_a(nx, 0, a0);
     if constexpr (!NXT_EXT) dequant(0, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1], g0a, g0b, u0a, u0b);
     else read_ext(nx, 0, g0a);
@@ -661,7 +678,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   const int64_t ext_threads = 2 * (int64_t)p.I * ((p.kext + 2) / 3);
-  const int64_t blocks = p.M + (ext_threads + 255) / 256;
+  const int64_t scl_threads = (int64_t)(p.I + kScaleTileCols - 1) / kScaleTileCols * kScaleTileCols * p.nss;
+  const int64_t blocks = p.M + (ext_threads + 255) / 256 + (scl_threads + 255) / 256;
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

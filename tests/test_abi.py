@@ -137,14 +137,16 @@ def test_strerror_and_version():
 
 def test_workspace_bytes():
     # x' rows of H + extra columns (3 per group of the finer group size,
-    # padded to 32) halves, row exponents, then one [I, kext] binary16 plane
-    # of extra-column B rows per matrix
+    # padded to 32) halves, row exponents, one [I, kext] binary16 plane of
+    # extra-column B rows per matrix, then 4 KB of scale tile per 128
+    # columns and 128 inputs
     def a256(v):
         return (v + 255) // 256 * 256
 
     def expect(M, H, I, bg, gg, bu, gu):
         ext = (3 * (H // min(gg, gu)) + 31) // 32 * 32
-        return a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2)
+        tiles = (I + 127) // 128 * ((H + 127) // 128)
+        return a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2) + a256(tiles * 4096)
 
     assert swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64) == expect(512, 2048, 8192, 4, 64, 4, 64)
     assert swq.swiglu_q_workspace_bytes(8192, 2560, 10240, 8, 32, 4, 64) == expect(8192, 2560, 10240, 8, 32, 4, 64)
