@@ -91,7 +91,9 @@ extern "C" {
  *   precision_mode  SWQ_MATCH, SWQ_F32 or SWQ_F32_BF16OUT
  *   out          [M, I] device pointer, bf16 or float32 by mode
  *   stream       hipStream_t (NULL = null stream)
- * M == 0 returns SWQ_OK with nothing launched.  All pointers 16-byte aligned.
+ * M == 0 returns SWQ_OK with nothing launched.  x, Wg and Wu must be 16-byte
+ * aligned, the scales, biases and out aligned to their element size
+ * (SWQ_ERR_ALIGN otherwise).
  */
 int swiglu_q_forward(const void *x,
                      const uint32_t *Wg, const void *sg, const void *bg,
