@@ -114,13 +114,14 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
 // Extra-column B rows: thread (n, G) writes columns 3G, 3G+1, 3G+2 of row n
 // of one matrix, (c_hi, c_lo, c_hi) for g0-group G with c = b + z*s exactly
 // in float32 (b and z*s are bf16 values times small powers of two and 17),
-// zeros past the last group (the padding up to kext).
-__device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t* B, int gs, int bits, int g0,
+// zeros past the last group (the padding up to kext).  Group sizes are
+// powers of two: lg_* are their logarithms.
+__device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t* B, int lg_gs, int bits, int lg_g0,
                                                int ngroups, int kext, _Float16* dst, int64_t n, int G) {
   _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
   if (G < ngroups) {
-    const int ng = ngroups * g0 / gs;               // groups of this matrix per row
-    const int64_t gi = n * ng + (G * g0) / gs;
+    const int ng = ngroups >> (lg_gs - lg_g0);       // groups of this matrix per row
+    const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
     const float z = bits == 8 ? 136.0f : 8.0f;
     const float c = fmaf(z, bf16_to_f32(S[gi]), bf16_to_f32(B[gi]));
     chi = (_Float16)c;
@@ -133,53 +134,97 @@ __device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t
   if (k + 2 < kext) d[2] = chi;
 }
 
-// Scale tiles: thread (column n, super-step j) writes the 4 K-steps x 2
-// matrices words of n in tile (n / 128, j); columns past I get zeros.  A
-// bf16 scale with magnitude in [2^-17, 2^8) converts to binary16 exactly.
-__device__ __forceinline__ void prep_scale_tile(const PrepParams& p, int64_t n, int j) {
-  const int s_main = p.H / 32;
-  uint32_t* dst = p.scl + ((n / kScaleTileCols) * p.nss + j) * kScaleTileWords + (n % kScaleTileCols);
-  const int ng_g = p.H / p.gs_g, ng_u = p.H / p.gs_u;
+// Scale tiles: one block per 128 columns and 2 super-steps (256 inputs).
+// The block reads the scales it needs row by row (a row's groups are
+// contiguous), transposes them through LDS and writes each (K-step, matrix)
+// row of 128 columns contiguously.  Columns past I and K-steps past H get
+// zeros.  A bf16 scale with magnitude in [2^-17, 2^8) converts to binary16
+// exactly.
+constexpr int kScaleBlockSteps = 2;                     // super-steps per block
+constexpr int kScaleBlockGroups = kScaleBlockSteps * 128 / 32;   // groups per block, at most (gs >= 32)
+__device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, int jb) {
+  __shared__ uint16_t src[2][kScaleTileCols][kScaleBlockGroups];   // [matrix][column][group of the block]
+  const int tid = threadIdx.x;
+  const int s_main = p.H >> 5;
+  const int64_t n0 = (int64_t)tile * kScaleTileCols;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int t = 4 * j + q;
-    uint32_t vg = 0, vu = 0;
-    if (n < p.I && t < s_main) {
-      const _Float16 hg = (_Float16)bf16_to_f32(p.sg[n * ng_g + (32 * t) / p.gs_g]);
-      const _Float16 hu = (_Float16)bf16_to_f32(p.su[n * ng_u + (32 * t) / p.gs_u]);
-      vg = as_u32((f16x2){hg, hg});
-      vu = as_u32((f16x2){hu, hu});
+  for (int mat = 0; mat < 2; ++mat) {
+    const int lg_gs = __builtin_ctz(mat ? p.gs_u : p.gs_g);
+    const uint16_t* S = mat ? p.su : p.sg;
+    const int ng = p.H >> lg_gs;
+    const int lg_gpb = __builtin_ctz(kScaleBlockSteps * 128) - lg_gs;   // groups per block: 256 / gs
+    const int g0 = jb << lg_gpb;
+#pragma unroll
+    for (int k = 0; k < kScaleTileCols * kScaleBlockGroups / 256; ++k) {
+      const int i = tid + 256 * k;
+      if (i < (kScaleTileCols << lg_gpb)) {
+        const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
+        const int64_t n = n0 + row;
+        src[mat][row][g] = (n < p.I && g0 + g < ng) ? S[n * ng + g0 + g] : (uint16_t)0;
+      }
     }
-    dst[(2 * q) * kScaleTileCols] = vg;
-    dst[(2 * q + 1) * kScaleTileCols] = vu;
+  }
+  __syncthreads();
+  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
+#pragma unroll
+  for (int k = 0; k < kScaleBlockSteps * kScaleTileWords / 256; ++k) {
+    const int idx = tid + 256 * k;
+    const int col = idx & (kScaleTileCols - 1);
+    const int rest = idx >> 7;                           // (super-step, K-step, matrix)
+    const int mat = rest & 1, q = (rest >> 1) & 3, jl = rest >> 3;
+    const int j = jb * kScaleBlockSteps + jl;
+    if (j >= p.nss) continue;
+    const int tl = 4 * jl + q;                           // K-step within the block
+    uint32_t v = 0;
+    if (4 * j + q < s_main && n0 + col < p.I) {
+      const _Float16 h = (_Float16)bf16_to_f32(src[mat][col][(32 * tl) >> (mat ? lg_u : lg_g)]);
+      v = as_u32((f16x2){h, h});
+    }
+    p.scl[((int64_t)tile * p.nss + j) * kScaleTileWords + (2 * q + mat) * kScaleTileCols + col] = v;
   }
 }
 
+// Index helpers of the prep grid (host and device agree on them).
+__host__ __device__ inline int prep_ext_lg(int kext) {          // log2 of triplet slots per row
+  const int per_row = (kext + 2) / 3;
+  int lg = 0;
+  while ((1 << lg) < per_row) ++lg;
+  return lg;
+}
+__host__ __device__ inline int64_t prep_scale_blocks(int I, int nss) {   // blocks of the scale tiles
+  return (int64_t)(I + kScaleTileCols - 1) / kScaleTileCols * ((nss + kScaleBlockSteps - 1) / kScaleBlockSteps);
+}
+
+// Blocks [0, M): x rows.  Then the extra-column rows, thread index
+// ((n * 2 + matrix) << lg) + G.  Then the scale tiles, one block per 128
+// columns and 8 super-steps.  Every division is by a power of two or
+// block-uniform.
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   if ((int)blockIdx.x < p.M) {
     prep_x_row(p, blockIdx.x);
     return;
   }
-  const int per_row = (p.kext + 2) / 3;               // triplets per row, the last ones padding
-  const int64_t ext_blocks = (2 * (int64_t)p.I * per_row + 255) / 256;
-  if ((int64_t)blockIdx.x - p.M >= ext_blocks) {
-    // scale tiles: consecutive threads take consecutive columns of one super-step
-    const int64_t cols = (int64_t)(p.I + kScaleTileCols - 1) / kScaleTileCols * kScaleTileCols;
-    const int64_t i = ((int64_t)blockIdx.x - p.M - ext_blocks) * 256 + threadIdx.x;
-    if (i < cols * p.nss) prep_scale_tile(p, i % cols, (int)(i / cols));
+  const int lg = prep_ext_lg(p.kext);
+  const int64_t ext_blocks = ((2 * (int64_t)p.I << lg) + 255) / 256;
+  const int64_t b = (int64_t)blockIdx.x - p.M;
+  if (b >= ext_blocks) {
+    const int nj = (p.nss + kScaleBlockSteps - 1) / kScaleBlockSteps;
+    const int b2 = (int)(b - ext_blocks);
+    const int tile = b2 / nj;                            // block-uniform
+    prep_scale_block(p, tile, b2 - tile * nj);
     return;
   }
-  const int64_t idx = (int64_t)(blockIdx.x - p.M) * 256 + threadIdx.x;
-  const int64_t per_mat = (int64_t)p.I * per_row;
-  const int ngroups = p.H / p.g0;
-  if (idx < per_mat) {
-    prep_ext_group(p.sg, p.bg, p.gs_g, p.bits_g, p.g0, ngroups, p.kext, p.bext_g, idx / per_row,
-                   (int)(idx % per_row));
-  } else if (idx < 2 * per_mat) {
-    const int64_t i2 = idx - per_mat;
-    prep_ext_group(p.su, p.bu, p.gs_u, p.bits_u, p.g0, ngroups, p.kext, p.bext_u, i2 / per_row,
-                   (int)(i2 % per_row));
-  }
+  const int64_t idx = b * 256 + threadIdx.x;
+  const int G = (int)(idx & ((1 << lg) - 1));
+  const int64_t rest = idx >> lg;
+  const int64_t n = rest >> 1;
+  if (n >= p.I) return;
+  const int lg_g0 = __builtin_ctz(p.g0);
+  const int ngroups = p.H >> lg_g0;
+  if ((rest & 1) == 0)
+    prep_ext_group(p.sg, p.bg, __builtin_ctz(p.gs_g), p.bits_g, lg_g0, ngroups, p.kext, p.bext_g, n, G);
+  else
+    prep_ext_group(p.su, p.bu, __builtin_ctz(p.gs_u), p.bits_u, lg_g0, ngroups, p.kext, p.bext_u, n, G);
 }
 
 // ----------------------------------------------------------- MFMA GEMM ----
@@ -677,9 +722,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const int64_t ext_threads = 2 * (int64_t)p.I * ((p.kext + 2) / 3);
-  const int64_t scl_threads = (int64_t)(p.I + kScaleTileCols - 1) / kScaleTileCols * kScaleTileCols * p.nss;
-  const int64_t blocks = p.M + (ext_threads + 255) / 256 + (scl_threads + 255) / 256;
+  const int64_t ext_threads = (2 * (int64_t)p.I) << prep_ext_lg(p.kext);
+  const int64_t scl_blocks = prep_scale_blocks(p.I, p.nss);
+  const int64_t blocks = p.M + (ext_threads + 255) / 256 + scl_blocks;
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
