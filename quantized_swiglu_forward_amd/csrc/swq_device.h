@@ -57,16 +57,34 @@ __device__ __forceinline__ f16x2 bf16_to_h2(uint16_t b) {
   return (f16x2){h, h};
 }
 
+// Nibble masks and f16 magic numbers of the unpack: a nibble in bits [0,4)
+// of a binary16 lane ORed with 0x6400 is 1024 + q; in bits [4,8) ORed with
+// 0x5400 it is 64 + q.  As literals (the default) or, from
+// nibble_consts_in_regs(), in registers: then each mask-and-OR is one
+// v_and_or_b32 (a VOP3 instruction cannot take two literals on this target).
+struct NibbleK {
+  uint32_t m_lo, m_hi, g_lo, g_hi;
+};
+constexpr NibbleK kNibbleLiterals = {0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+__device__ __forceinline__ NibbleK nibble_consts_in_regs() {
+  NibbleK k;
+  asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(k.m_lo));
+  asm volatile("s_mov_b32 %0, 0xf000f0" : "=s"(k.m_hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.g_lo));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(k.g_hi));
+  return k;
+}
+
 // Eight 4-bit codes of one word -> s*(q-8) as four f16 pairs in the order
 // (q0,q4) (q1,q5) (q2,q6) (q3,q7).
-__device__ __forceinline__ void dequant4(uint32_t w, f16x2 s2, uint32_t out[4]) {
+__device__ __forceinline__ void dequant4(uint32_t w, f16x2 s2, uint32_t out[4], const NibbleK& k = kNibbleLiterals) {
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
   const uint32_t w8 = w >> 8;
-  f16x2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - c1032;
-  f16x2 p1 = as_h2((w & 0x00F000F0u) | 0x54005400u) - c72;
-  f16x2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - c1032;
-  f16x2 p3 = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - c72;
+  f16x2 p0 = as_h2((w & k.m_lo) | k.g_lo) - c1032;
+  f16x2 p1 = as_h2((w & k.m_hi) | k.g_hi) - c72;
+  f16x2 p2 = as_h2((w8 & k.m_lo) | k.g_lo) - c1032;
+  f16x2 p3 = as_h2((w8 & k.m_hi) | k.g_hi) - c72;
   out[0] = as_u32(p0 * s2);
   out[1] = as_u32(p1 * s2);
   out[2] = as_u32(p2 * s2);
@@ -88,15 +106,16 @@ __device__ __forceinline__ void codes4(uint32_t w, uint32_t out[4]) {
 // and high nibble planes (lo-8) and (hi-8) as f16 pairs in the order
 // (c0,c4) (c1,c5) (c2,c6) (c3,c7).  v_perm_b32 gathers byte j of wa and byte j
 // of wb into bytes 0 and 2 of one register.
-__device__ __forceinline__ void codes8(uint32_t wa, uint32_t wb, uint32_t lo[4], uint32_t hi[4]) {
+__device__ __forceinline__ void codes8(uint32_t wa, uint32_t wb, uint32_t lo[4], uint32_t hi[4],
+                                       const NibbleK& k = kNibbleLiterals) {
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
     const uint32_t t = __builtin_amdgcn_perm(wb, wa, sel);
-    lo[j] = as_u32(as_h2((t & 0x000F000Fu) | 0x64006400u) - c1032);
-    hi[j] = as_u32(as_h2((t & 0x00F000F0u) | 0x54005400u) - c72);
+    lo[j] = as_u32(as_h2((t & k.m_lo) | k.g_lo) - c1032);
+    hi[j] = as_u32(as_h2((t & k.m_hi) | k.g_hi) - c72);
   }
 }
 

@@ -297,14 +297,14 @@ __device__ __forceinline__ void block_barrier() {
 
 // Dequantized B operands of one k16 sub-step (one 8-code block per lane) of one matrix.
 template <int BITS>
-__device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1) {
+__device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1, const NibbleK& k) {
   if (BITS == 4) {
     uint32_t o[4];
-    dequant4(w[0], s2, o);
+    dequant4(w[0], s2, o, k);
     b0 = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
   } else {
     uint32_t lo[4], hi[4];
-    codes8(w[0], w[1], lo, hi);
+    codes8(w[0], w[1], lo, hi, k);
     const f16x2 s16 = s2 * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
     u32x4 vl, vh;
 #pragma unroll
@@ -422,6 +422,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // super-step scales: the tile's 4 KB block, 16 bytes per thread in order
   const uint32_t s_voff[SS_SCALE_INSTR] = {(uint32_t)tid * 16};
 
+  const NibbleK nk = nibble_consts_in_regs();            // unpack constants in registers
+
   // row exponents of the tile: loaded first, published through LDS after the K loop
   const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;
 
@@ -528,8 +530,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
                      f16x8 (&ua)[NF], f16x8 (&ub)[NF]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      dequant_block<BITS_G>(&cg[f][ks * (BITS_G / 4)], s_g[f], ga[f], gb[f]);
-      dequant_block<BITS_U>(&cu[f][ks * (BITS_U / 4)], s_u[f], ua[f], ub[f]);
+      dequant_block<BITS_G>(&cg[f][ks * (BITS_G / 4)], s_g[f], ga[f], gb[f], nk);
+      dequant_block<BITS_U>(&cu[f][ks * (BITS_U / 4)], s_u[f], ua[f], ub[f], nk);
     }
   };
   // B operands of sub-step ks of an extra-column step from stage `slot` (one
