@@ -160,6 +160,42 @@ def test_gemv_and_mfma_agree(M):
     check(ym, o, 1, f"mfma M{M}")
 
 
+# ------------------------------------------------- tile shapes and splits --
+
+def test_tile_shapes_and_column_split_agree_bitwise():
+    """M=512, I=38400 gives 600 tiles of 256 x 128: two whole rounds on 256
+    CUs, so the columns past them run as 128 x 128 tiles in a second launch.
+    Every output accumulates the same products in the same order whatever
+    the tile shape, so the split launch, the single 256 x 128 launch and the
+    all-128 x 128 launch agree bit for bit; sampled outputs on both sides of
+    the split column are checked against the oracle."""
+    import os
+    p = make_custom(512, 256, 38400, 4, 64, 4, 64, seed=41)
+    dev = swq.to_device(p)
+    outs = {}
+    for name, env in (("split", {}), ("single", {"SWIGLU_Q_MFMA_SPLIT": "0"}), ("small", {"SWIGLU_Q_MFMA_CFG": "1"})):
+        say("tile shapes", name)
+        saved = {k: os.environ.get(k) for k in ("SWIGLU_Q_MFMA_SPLIT", "SWIGLU_Q_MFMA_CFG")}
+        try:
+            for k in saved:
+                os.environ.pop(k, None)
+            os.environ.update(env)
+            outs[name] = device_forward(p, 1, MFMA, dev=dev)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    assert np.array_equal(outs["split"], outs["single"])
+    assert np.array_equal(outs["split"], outs["small"])
+    rng = np.random.default_rng(3)
+    ns = np.concatenate([np.arange(32768 - 64, 32768 + 64), rng.integers(0, 38400, 200)])
+    ms = rng.integers(0, 512, ns.size)
+    o = oracle_pairs(p, 1, ms, ns)
+    check(outs["split"][ms, ns], o, 1, "split boundary sampled")
+
+
 # -------------------------------------------------------------- invariants --
 
 @pytest.mark.parametrize("path", [GEMV, MFMA])
