@@ -74,6 +74,28 @@ def test_shape_sweep(M, H, I, spec, mode, path):
     check(y, oracle_full(p, mode), mode, f"sweep M{M} H{H} I{I} {spec} mode{mode} path{path}")
 
 
+# ------------------------------------------------------- decode (M = 1) --
+
+# every branch of the M = 1 kernel: a whole wave per column with one or two
+# chunks per lane (H = 2048, 4096), two chunks with idle lanes (H = 3072),
+# fewer lanes per column (H = 1024, 512), both bit widths and all group
+# sizes on each side, ragged I
+DECODE_CASES = [
+    (2048, 5633, (4, 64, 4, 64)), (2048, 301, (8, 32, 4, 64)), (2048, 257, (4, 128, 8, 128)),
+    (2048, 130, (8, 64, 8, 32)), (4096, 515, (4, 64, 4, 64)), (4096, 129, (8, 128, 4, 32)),
+    (3072, 200, (4, 64, 8, 64)), (1024, 333, (4, 32, 4, 128)), (512, 97, (8, 64, 4, 64)),
+]
+
+
+@pytest.mark.parametrize("H,I,spec", DECODE_CASES, ids=[f"H{h}-I{i}-{s[0]}b{s[1]}-{s[2]}b{s[3]}" for h, i, s in DECODE_CASES])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_decode_branches(H, I, spec, mode):
+    p = make_custom(1, H, I, *spec, seed=H + I)
+    say("decode", H, I, spec, "mode", mode)
+    y = device_forward(p, mode, GEMV)
+    check(y, oracle_full(p, mode), mode, f"decode H{H} I{I} {spec} mode{mode}")
+
+
 # ------------------------------------------------------- full-size configs --
 
 @pytest.mark.parametrize("mode", [0, 1])
