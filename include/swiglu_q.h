@@ -33,10 +33,12 @@
  * Ownership and synchronisation: every pointer passed to the forward calls
  * is a DEVICE pointer owned by the caller; the library never frees or keeps
  * them.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- * and the call returns without synchronising.  The matrix-matrix path needs
- * a device workspace: the library keeps one per (device, stream), allocated
- * on first use and grown (never shrunk) when a call needs more; growth
- * synchronises that stream once.  swiglu_q_release_workspace() frees them.
+ * and the call returns without synchronising.  Every call with M > 1 (and
+ * M = 1 with H > 4096) needs a device workspace for the staged x, the
+ * matrix-matrix path more: the library keeps one per (device, stream),
+ * allocated on first use and grown (never shrunk) when a call needs more;
+ * growth synchronises that stream once.  swiglu_q_release_workspace() frees
+ * them.
  *
  * Exactness: the weights are dequantized exactly (no rounding of s·q + b);
  * gate and up are float32 dot products.  This holds when every scale and
@@ -76,7 +78,7 @@ extern "C" {
 #define SWQ_F32_BF16OUT  2  /* as SWQ_F32, rounded once to bf16 at the store       */
 
 /* Kernel paths chosen by the M-threshold dispatcher. */
-#define SWQ_PATH_GEMV    0  /* M < threshold: wavefront-reduction matrix-vector    */
+#define SWQ_PATH_GEMV    0  /* M < threshold (M <= 16): matrix-vector kernels      */
 #define SWQ_PATH_MFMA    1  /* M >= threshold: dequantizing bf16/f16 MFMA GEMM      */
 #define SWQ_PATH_AUTO   -1
 
@@ -108,8 +110,10 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
                        int precision_mode);
 
 /* M threshold T of the dispatcher: M < T takes SWQ_PATH_GEMV, M >= T takes
- * SWQ_PATH_MFMA.  The default comes from the environment variable
- * SWIGLU_Q_MMIN when set to a positive integer, else the built-in default.
+ * SWQ_PATH_MFMA; the matrix-vector path takes at most 16 rows, so M > 16
+ * always runs the MFMA path.  The default comes from the environment
+ * variable SWIGLU_Q_MMIN when set to a positive integer, else the built-in
+ * default 17 (measured: the matrix-vector path is faster for every M <= 16).
  * T <= 1 sends every M >= 1 to the MFMA path. */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);

@@ -1,14 +1,17 @@
 // C-ABI boundary of the fused quantized SwiGLU library (declared in
 // include/swiglu_q.h): argument validation, the M-threshold dispatcher,
-// per-path call counters, and the per-(device, stream) workspace of the
-// matrix-matrix path.
+// per-path call counters, and the per-(device, stream) workspace (x' and
+// the matrix-matrix path's staging).
 //
 // The dispatcher mirrors the pages' M threshold ("mlx-bun 0.0.7 -> 0.0.9"
 // diff, page 42, fused-swiglu-kernel.ts: below a small row count the
 // projections are matrix-vector products and a different path runs; the
-// threshold defaults to 2 there and can be set from the environment) and the
-// support predicate of the same file (bf16 activations, affine biases,
-// group size a multiple of 32, H a multiple of 32).
+// threshold defaults to 2 there, benchmarks are to set it, and it can be set
+// from the environment) and the support predicate of the same file (bf16
+// activations, affine biases, group size a multiple of 32, H a multiple of
+// 32).  Here the default is 17: measured on this GPU, the matrix-vector
+// kernels beat the matrix-matrix kernel for every M <= 16 (2-3x on the
+// decode and prefill weight shapes), and 16 rows is their limit.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -25,7 +28,7 @@ using namespace swq;
 
 namespace {
 
-constexpr int kDefaultThreshold = 2;
+constexpr int kDefaultThreshold = kGemvMaxM + 1;
 
 std::atomic<int> g_threshold{-1};
 std::atomic<uint64_t> g_calls[2];
@@ -85,8 +88,13 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
 }
 
 bool gemv_fits(int64_t M, int64_t H) {
-  return M >= 1 && M <= kGemvMaxM && gemv_lds_bytes(M, H) <= kGemvLdsBytes;
+  (void)H;
+  return M >= 1 && M <= kGemvMaxM;
 }
+
+// The M = 1 kernel reads x itself for H <= 4096; otherwise the matrix-vector
+// path stages x' with the prep kernel first.
+bool gemv_needs_rows(int64_t M, int64_t H) { return M > 1 || H > 4096; }
 
 // Tile shape of the MFMA kernel: 256 x 128 unless that leaves CUs idle
 // (fewer than two tiles per CU of the 256), then 128 x 128.  The environment
@@ -206,10 +214,30 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     p.M = (int)M; p.H = (int)H; p.I = (int)I;
     p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
     p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+    p.xa = nullptr; p.xexp = nullptr;
     if (logging())
       fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
               (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
     (void)hipGetLastError();
+    if (gemv_needs_rows(M, H)) {
+      // x' rows [H/32][M][32] (the extra columns of 32-input groups ride along
+      // unused), then the row exponents
+      const int kext = kext_columns(H, 32);
+      const int64_t xa_bytes = align256(M * (H + kext) * 2);
+      void* ws = nullptr;
+      int rc = get_workspace(stream, (size_t)(xa_bytes + align256(M * 4)), &ws);
+      if (rc != SWQ_OK) return rc;
+      PrepParams pp{};
+      pp.x = (const uint16_t*)x;
+      pp.M = (int)M; pp.H = (int)H; pp.I = 0;
+      pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
+      pp.g0 = 32; pp.ldx = (int)H + kext; pp.kext = kext;
+      pp.xa = (_Float16*)ws;
+      pp.xexp = (int*)((char*)ws + xa_bytes);
+      p.xa = pp.xa;
+      p.xexp = pp.xexp;
+      if (launch_prep_rows(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
+    }
     if (launch_gemv(p, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
     g_calls[SWQ_PATH_GEMV].fetch_add(1, std::memory_order_relaxed);
     return SWQ_OK;

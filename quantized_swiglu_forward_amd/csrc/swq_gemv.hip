@@ -3,30 +3,21 @@
 // At decode the two projections are memory-bound matrix-vector products and
 // reading Wg/Wu dominates ("mlx-bun 0.0.7 -> 0.0.9" diff, page 42,
 // fused-swiglu-kernel.ts, the comment on where the fusion pays off, and the
-// M-threshold function below which the caller keeps this path).  No MFMA
-// here: lanes stream packed rows with 16-byte loads, turn codes into exact
-// binary16 operands and accumulate x'q with v_dot2_f32_f16; per 32-input
-// chunk (always inside one quantization group) the partial sum P and the
-// chunk's sum of x' give the chunk's share of sum_k x'(s q + b) in float32.  A
-// cross-lane reduction per column then yields gate and up, and the same
-// epilogue as the matrix-matrix path writes hidden.
-//
-// Work split: a column group of `lpc` lanes (a power of two, at most 64)
-// owns one output column at a time; lane sl of the group handles the
-// 32-input chunks sl, sl + lpc, ...  Every lane issues its loads before
-// anything else, so the whole weight stream is in flight at once.
+// M-threshold function below which the caller keeps this path).  Lanes
+// stream packed rows with 16-byte loads, turn codes into exact binary16
+// operands, and per 32-input chunk (always inside one quantization group)
+// the chunk's share of sum_k x'(s q + b) is formed exactly up to float32
+// accumulation; the same epilogue as the matrix-matrix path writes hidden.
 //
 // Two kernels:
 //  * swq_gemv1_kernel: M = 1 with at most two chunks per lane (H <= 4096).
-//    Codes enter the dot products as exact binary16 subnormals with no
-//    offset, and each lane scales its own x chunk by a power of two; no LDS,
-//    no barrier (described above the kernel).
-//  * swq_gemvm_kernel: 1 <= M <= 16.  The block stages x' = x * 2^-e in
-//    binary16 (e = exponent of the row maximum; exact for every element at
-//    least 2^-17 of the maximum) in the [0,4,1,5,2,6,3,7] order of the code
-//    pairs, with per-chunk sums, in LDS; codes become exact binary16 (q - z)
-//    pairs; the loads of the next (column, chunk) item are in flight while
-//    the current one is computed.
+//    Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no offset,
+//    each chunk of x scaled by its own power of two; the block shares x
+//    through LDS (described above the kernel).
+//  * swq_skinny_kernel: 1 <= M <= 16 otherwise.  The prep kernel stages x'
+//    once per call; codes become exact binary16 s (q - z) and 16 x 16 x 32
+//    MFMAs multiply them with up to 16 rows at once (described above the
+//    kernel).
 #include "swq_device.h"
 #include "swq_kernels.h"
 
@@ -39,18 +30,7 @@ struct RawChunk {
   uint32_t sb;         // bf16 scale (low half) and bias (high half) of the chunk's group
 };
 
-template <int BITS>
-__device__ __forceinline__ void load_chunk(RawChunk<BITS>& r, const uint32_t* W, const uint16_t* S,
-                                           const uint16_t* B, int64_t row, int rw, int ng, int gs,
-                                           int kc) {
-  const uint32_t* base = W + row * rw + (int64_t)kc * (BITS);   // BITS words per 32-code chunk
-#pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) r.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 4 * i));
-  const int64_t gi = row * ng + (kc * 32) / gs;
-  r.sb = (uint32_t)S[gi] | ((uint32_t)B[gi] << 16);
-}
-
-// The same through buffer descriptors whose base is the wave's first column:
+// Chunk loads through buffer descriptors whose base is the wave's first column:
 // 32-bit offsets (one VALU op per address), and the descriptor's record count
 // returns zeros for columns past the end.
 struct MatBufs {
@@ -81,38 +61,6 @@ __device__ __forceinline__ void load_chunk_buf(RawChunk<BITS>& r, const MatBufs&
          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m.b, go, 0, 0) << 16);
 }
 
-// sum over the chunk of x'(q - z) as float32, split as  s*P + (b + z s)*Sx.
-template <int BITS>
-__device__ __forceinline__ float chunk_dot(const RawChunk<BITS>& r, const uint32_t xv[16], float sx) {
-  float p = 0.0f;
-  if (BITS == 4) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t q[4];
-      codes4(r.w[0][j], q);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) p = __builtin_amdgcn_fdot2(as_h2(xv[4 * j + t]), as_h2(q[t]), p, false);
-    }
-  } else {
-    float ph = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo[4], hi[4];
-      const u32x4& w = r.w[j / 2];
-      codes8(w[2 * (j & 1)], w[2 * (j & 1) + 1], lo, hi);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        p = __builtin_amdgcn_fdot2(as_h2(xv[4 * j + t]), as_h2(lo[t]), p, false);
-        ph = __builtin_amdgcn_fdot2(as_h2(xv[4 * j + t]), as_h2(hi[t]), ph, false);
-      }
-    }
-    p = fmaf(16.0f, ph, p);
-  }
-  const float s = bf16_to_f32((uint16_t)(r.sb & 0xFFFFu));
-  const float b = bf16_to_f32((uint16_t)(r.sb >> 16));
-  const float c = fmaf(CodeOffset<BITS>::z, s, b);   // b + z*s
-  return fmaf(s, p, c * sx);
-}
 
 __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, float g, float u) {
   const int64_t o = (int64_t)m * p.I + n;
@@ -443,138 +391,154 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
   }
 }
 
-// ---------------------------------------------------------- 1 <= M <= 16 --
+// --------------------------------------------------------- 2 <= M <= 16 --
+//
+// Matrix-vector products for a few rows.  The rows of x, staged once per call
+// by the prep kernel as x' = x 2^-e (binary16, per-row power of two, in the
+// code-pair order of the dequantized weights, 32 inputs per chunk), are the A
+// operand of v_mfma_f32_16x16x32_f16 (16 rows, M of them live); the
+// dequantized weights s (q - z) of 16 output columns are the B operand, so one
+// unpack serves every row.  A block of up to 16 waves owns 16 columns of both
+// matrices: wave w takes the chunk quads w, w + W, ... (W waves), and lane
+// group h = lane / 16 takes chunk 4 quad + h: the MFMA's K slots of group h
+// are that chunk's 8-code block, on the A side x' of the same inputs.  Every
+// lane issues the loads of two quads before computing either, so the weight
+// stream is in flight at once.  A fifth MFMA per chunk adds the bias term
+// sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c each split
+// into binary16 hi + lo, as on the matrix-matrix path.  The waves' partial
+// sums meet in LDS; wave 0 applies 2^e and the epilogue.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSkinnyMaxWaves = 16;
 
-template <int BITS_G, int BITS_U, int MAXM>
-__global__ __launch_bounds__(256) void swq_gemvm_kernel(GemvParams p, int lpc, int rounds) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int H = p.H, M = p.M;
-  const int nchunk = H / 32;
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);                   // [M][H]
-  float* sxs = reinterpret_cast<float*>(smem + (size_t)M * H * 2);     // [M][H/32]
-  __shared__ uint32_t rowmax[MAXM];
-  __shared__ int rowexp[MAXM];
+template <int BITS_G, int BITS_U>
+struct SkinnyChunk {
+  u32x4 cg[BITS_G / 4], cu[BITS_U / 4], x[4];
+  float sg, bg, su, bu;
+  bool live;
+};
 
+template <int BITS_G, int BITS_U>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void swq_skinny_kernel(GemvParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int sub = lane / lpc, sl = lane % lpc;
-  const int cpw = 64 / lpc;
-  const int cpl = (nchunk + lpc - 1) / lpc;
-  const int items = rounds * cpl;
-  const int ng_g = H / p.gs_g, ng_u = H / p.gs_u;
-  const int rw_g = H * BITS_G / 32, rw_u = H * BITS_U / 32;
-  const int col0 = blockIdx.x * rounds * 4 * cpw;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = blockDim.x >> 6;
+  const int r = lane & 15, h = lane >> 4;             // A row / B and D column; K-slot group
+  const int col = blockIdx.x * 16 + r;
+  const int colc = min(col, p.I - 1), rowc = min(r, p.M - 1);   // clamped for loads
+  const int nchunk = p.H >> 5;
+  const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
+  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
+  const uint32_t* wgr = p.wg + (int64_t)colc * rw_g;
+  const uint32_t* wur = p.wu + (int64_t)colc * rw_u;
+  const uint16_t* sgr = p.sg + (int64_t)colc * (p.H >> lg_g);
+  const uint16_t* bgr = p.bg + (int64_t)colc * (p.H >> lg_g);
+  const uint16_t* sur = p.su + (int64_t)colc * (p.H >> lg_u);
+  const uint16_t* bur = p.bu + (int64_t)colc * (p.H >> lg_u);
+  const NibbleK nk = nibble_consts_in_regs();
+  const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  const f16x8 zero8 = {};
 
-  auto item_col = [&](int j) { return col0 + (j / cpl) * 4 * cpw + wave * cpw + sub; };
-  auto item_chunk = [&](int j) { return sl + (j % cpl) * lpc; };
-
-  RawChunk<BITS_G> cg, ng;
-  RawChunk<BITS_U> cu, nu;
-  auto load_item = [&](int j, RawChunk<BITS_G>& a, RawChunk<BITS_U>& b) {
-    const int nn = min(item_col(j), p.I - 1);
-    const int kc = min(item_chunk(j), nchunk - 1);
-    load_chunk<BITS_G>(a, p.wg, p.sg, p.bg, nn, rw_g, ng_g, p.gs_g, kc);
-    load_chunk<BITS_U>(b, p.wu, p.su, p.bu, nn, rw_u, ng_u, p.gs_u, kc);
+  auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
+    const int c = 4 * quad + h;
+    d.live = c < nchunk;
+    const int cc = d.live ? c : 0;                     // an in-range chunk for the loads
+#pragma unroll
+    for (int i = 0; i < BITS_G / 4; ++i)
+      d.cg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wgr + cc * BITS_G + 4 * i));
+#pragma unroll
+    for (int i = 0; i < BITS_U / 4; ++i)
+      d.cu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wur + cc * BITS_U + 4 * i));
+    const int gg = (32 * cc) >> lg_g, gu = (32 * cc) >> lg_u;
+    d.sg = bf16_to_f32(sgr[gg]);
+    d.bg = bf16_to_f32(bgr[gg]);
+    d.su = bf16_to_f32(sur[gu]);
+    d.bu = bf16_to_f32(bur[gu]);
+    const _Float16* xr = p.xa + ((int64_t)cc * p.M + rowc) * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d.x[q] = *reinterpret_cast<const u32x4*>(xr + 8 * q);
   };
-  load_item(0, cg, cu);     // weights first: in flight while x is staged
 
-  // ---- stage x rows
-  if (tid < MAXM) rowmax[tid] = 0;
-  __syncthreads();
-  const int nchunk8 = M * (H / 8);
-  for (int c = tid; c < nchunk8; c += 256) {
-    const int m = c / (H / 8), k8 = c % (H / 8);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * H + 8 * k8);
-    uint32_t a = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a = max(a, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
-    atomicMax(&rowmax[m], a);
-  }
-  __syncthreads();
-  if (tid < M) rowexp[tid] = row_exponent(rowmax[tid]);
-  __syncthreads();
-  for (int base = 0; base < nchunk8; base += 256) {
-    const int c = base + tid;
-    float part = 0.0f;
-    if (c < nchunk8) {
-      const int m = c / (H / 8), k8 = c % (H / 8);
-      const int e = rowexp[m];
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * H + 8 * k8);
-      float f[8];
+  // one matrix's 8-code block kb of a chunk: one MFMA (4-bit) or two (8-bit planes)
+  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, bool live, int kb, const f16x8& a, f32x4& acc) {
+    const _Float16 hs = (_Float16)sf;
+    const f16x2 s2 = {hs, hs};
+    if constexpr (BITS == 4) {
+      uint32_t o[4];
+      dequant4(cw[0][kb], s2, o, nk);
+      const f16x8 b = live ? __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]}) : zero8;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    } else {
+      uint32_t lo[4], hi[4];
+      codes8(cw[kb >> 1][2 * (kb & 1)], cw[kb >> 1][2 * (kb & 1) + 1], lo, hi, nk);
+      const f16x2 s16 = s2 * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
+      u32x4 vl, vh;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -e);
-        f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -e);
+        vl[j] = as_u32(as_h2(lo[j]) * s2);
+        vh[j] = as_u32(as_h2(hi[j]) * s16);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) part += f[j];
-      f16x8 h;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[2 * j] = (_Float16)f[j];
-        h[2 * j + 1] = (_Float16)f[j + 4];
-      }
-      *reinterpret_cast<f16x8*>(xs + (size_t)m * H + 8 * k8) = h;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, live ? __builtin_bit_cast(f16x8, vl) : zero8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, live ? __builtin_bit_cast(f16x8, vh) : zero8, acc, 0, 0, 0);
     }
-    // four consecutive 8-value blocks (consecutive lanes) form one 32-input chunk
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    if (c < nchunk8 && (c & 3) == 0) {
-      const int m = c / (H / 8), k8 = c % (H / 8);
-      sxs[(size_t)m * nchunk + k8 / 4] = part;
-    }
-  }
-  __syncthreads();
+  };
 
-  float ag[MAXM], au[MAXM];
+  f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const SkinnyChunk<BITS_G, BITS_U>& d) {
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    ag[m] = 0.0f;
-    au[m] = 0.0f;
+    for (int kb = 0; kb < 4; ++kb) {
+      const f16x8 a = __builtin_bit_cast(f16x8, d.x[kb]);
+      block_mfma.template operator()<BITS_G>(d.cg, d.sg, d.live, kb, a, ag);
+      block_mfma.template operator()<BITS_U>(d.cu, d.su, d.live, kb, a, au);
+    }
+    // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
+    float sx = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d.x[q][j]), one2, sx, false);
+    const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
+    const _Float16 z0 = (_Float16)0.0f;
+    const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
+    const float cgf = fmaf(CodeOffset<BITS_G>::z, d.sg, d.bg), cuf = fmaf(CodeOffset<BITS_U>::z, d.su, d.bu);
+    const _Float16 cgh = (_Float16)cgf, cgl = (_Float16)(cgf - (float)cgh);
+    const _Float16 cuh = (_Float16)cuf, cul = (_Float16)(cuf - (float)cuh);
+    const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
+    const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
+    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, d.live ? beg : zero8, ag, 0, 0, 0);
+    au = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, d.live ? beu : zero8, au, 0, 0, 0);
+  };
+
+  // chunk quads w, w + nw, ...: two at a time, both loaded before either is used
+  const int nquad = (nchunk + 3) >> 2;
+  for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
+    SkinnyChunk<BITS_G, BITS_U> d0, d1;
+    const bool two = q0 + nw < nquad;                 // wave-uniform
+    load(q0, d0);
+    if (two) load(q0 + nw, d1);
+    compute(d0);
+    if (two) compute(d1);
   }
-  for (int j = 0; j < items; ++j) {
-    if (j + 1 < items) load_item(j + 1, ng, nu);
-    const int kc = item_chunk(j);
-    if (kc < nchunk) {
+
+  // the waves' partial sums; D element j of lane l is row 4 (l / 16) + j, column l % 16
+  __shared__ f32x4 red[kSkinnyMaxWaves][2][64];
+  red[w][0][lane] = ag;
+  red[w][1][lane] = au;
+  __syncthreads();
+  if (w == 0) {
+    f32x4 g = red[0][0][lane], u = red[0][1][lane];
+    for (int ww = 1; ww < nw; ++ww) {
+      g += red[ww][0][lane];
+      u += red[ww][1][lane];
+    }
 #pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        if (m < M) {
-          const uint32_t* xr = reinterpret_cast<const uint32_t*>(xs + (size_t)m * H + kc * 32);
-          uint32_t xv[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 t = *reinterpret_cast<const u32x4*>(xr + 4 * q);
-            xv[4 * q] = t[0];
-            xv[4 * q + 1] = t[1];
-            xv[4 * q + 2] = t[2];
-            xv[4 * q + 3] = t[3];
-          }
-          const float sx = sxs[(size_t)m * nchunk + kc];
-          ag[m] += chunk_dot<BITS_G>(cg, xv, sx);
-          au[m] += chunk_dot<BITS_U>(cu, xv, sx);
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * h + j;
+      if (m < p.M && col < p.I) {
+        const int e = p.xexp[m];
+        store_out(p, m, col, ldexpf(g[j], e), ldexpf(u[j], e));
       }
     }
-    if (j % cpl == cpl - 1) {
-      // end of a column: reduce over the group, write, reset
-      const int n = item_col(j);
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) {
-        if (m < M) {
-          float g = ag[m], u = au[m];
-          for (int off = lpc >> 1; off > 0; off >>= 1) {
-            g += __shfl_xor(g, off);
-            u += __shfl_xor(u, off);
-          }
-          if (sl == 0 && n < p.I) store_out(p, m, n, ldexpf(g, rowexp[m]), ldexpf(u, rowexp[m]));
-          ag[m] = 0.0f;
-          au[m] = 0.0f;
-        }
-      }
-    }
-    cg = ng;
-    cu = nu;
   }
 }
 
@@ -608,18 +572,6 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   return hipGetLastError();
 }
 
-template <int BG, int BU, int MAXM>
-static hipError_t launch_gemvm_t(const GemvParams& p, hipStream_t stream) {
-  const int lpc = gemv_lanes_per_column(p.H);
-  const int cpw = 64 / lpc;
-  const int rounds = 2;
-  const int cols_per_block = 4 * cpw * rounds;
-  const int blocks = (p.I + cols_per_block - 1) / cols_per_block;
-  const size_t lds = (size_t)gemv_lds_bytes(p.M, p.H);
-  hipLaunchKernelGGL((swq_gemvm_kernel<BG, BU, MAXM>), dim3(blocks), dim3(256), lds, stream, p, lpc, rounds);
-  return hipGetLastError();
-}
-
 static int gemv1_rounds() {
   static const int r = [] {
     const char* s = getenv("SWIGLU_Q_GEMV_ROUNDS");
@@ -633,7 +585,7 @@ template <int BG, int BU>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
   const int cpl = (p.H / 32 + lpc - 1) / lpc;
-  if (p.M == 1 && cpl <= 2 && !getenv("SWIGLU_Q_GEMV_GENERAL")) {
+  if (p.M == 1 && cpl <= 2) {
     const bool full = lpc == 64 && p.H == 2048 * cpl;
     if (cpl == 1) {
       return full ? launch_gemv1_t<BG, BU, 1, true>(p, gemv1_rounds(), stream)
@@ -642,12 +594,12 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     return full ? launch_gemv1_t<BG, BU, 2, true>(p, gemv1_rounds(), stream)
                 : launch_gemv1_t<BG, BU, 2, false>(p, gemv1_rounds(), stream);
   }
-  if (p.M <= 1) return launch_gemvm_t<BG, BU, 1>(p, stream);
-  if (p.M <= 2) return launch_gemvm_t<BG, BU, 2>(p, stream);
-  if (p.M <= 4) return launch_gemvm_t<BG, BU, 4>(p, stream);
-  if (p.M <= 8) return launch_gemvm_t<BG, BU, 8>(p, stream);
-  if (p.M <= kGemvMaxM) return launch_gemvm_t<BG, BU, kGemvMaxM>(p, stream);
-  return hipErrorInvalidValue;
+  if (p.M < 1 || p.M > kGemvMaxM || p.xa == nullptr) return hipErrorInvalidValue;
+  // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns
+  const int quads = (p.H / 32 + 3) / 4;
+  const int waves = quads < kSkinnyMaxWaves ? quads : kSkinnyMaxWaves;
+  hipLaunchKernelGGL((swq_skinny_kernel<BG, BU>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream) {

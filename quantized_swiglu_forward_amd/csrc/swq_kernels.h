@@ -62,6 +62,8 @@ struct GemvParams {
   void* out;
   float* dbg_g;
   float* dbg_u;
+  const _Float16* xa;  // M >= 2 (or H > 4096): x' staged by the prep kernel, [H/32][M][32]
+  const int* xexp;     // and its row exponents
 };
 
 // Scale tiles: for every 128 output columns and every 128 inputs (a
@@ -76,14 +78,8 @@ constexpr int kMfmaConfigs = 2;
 constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
 constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
-// Largest M the matrix-vector kernel takes, and its LDS budget for x.
+// Largest M the matrix-vector path takes (one 16-row MFMA tile).
 constexpr int kGemvMaxM = 16;
-constexpr int kGemvLdsBytes = 64 * 1024;
-
-inline int64_t gemv_lds_bytes(int64_t M, int64_t H) {
-  // binary16 x' plus one float32 partial sum per 32 inputs, per row
-  return M * (H * 2 + (H / 32) * 4);
-}
 
 inline int kext_columns(int64_t H, int g0) {
   const int64_t c = 3 * (H / g0);
@@ -91,6 +87,8 @@ inline int kext_columns(int64_t H, int g0) {
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
+// Only the x rows of the prep kernel (x' and row exponents), for the matrix-vector path.
+hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // cfg: tile shape (kMfmaBM/kMfmaBN); n_split > 0 with cfg 0: columns
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);

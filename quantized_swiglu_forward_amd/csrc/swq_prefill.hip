@@ -731,6 +731,11 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)p.M), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int BG, int BU, int BM, int WN, int OCC>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.n_end - p.n_begin + 4 * WN - 1) / (4 * WN));
