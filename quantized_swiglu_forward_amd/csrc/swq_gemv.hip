@@ -401,9 +401,9 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // unpack serves every row.  A block of up to 16 waves owns 16 columns of both
 // matrices: wave w takes the chunk quads w, w + W, ... (W waves), and lane
 // group h = lane / 16 takes chunk 4 quad + h: the MFMA's K slots of group h
-// are that chunk's 8-code block, on the A side x' of the same inputs.  Every
-// lane issues the loads of two quads before computing either, so the weight
-// stream is in flight at once.  A fifth MFMA per chunk adds the bias term
+// are that chunk's 8-code block, on the A side x' of the same inputs.  With
+// 4-bit codes at most 64 registers per lane let two such blocks share a CU,
+// so a whole decode-sized grid is resident at once.  A fifth MFMA per chunk adds the bias term
 // sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c each split
 // into binary16 hi + lo, as on the matrix-matrix path.  The waves' partial
 // sums meet in LDS; wave 0 applies 2^e and the epilogue.
@@ -418,56 +418,56 @@ struct SkinnyChunk {
 };
 
 template <int BITS_G, int BITS_U>
-__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void swq_skinny_kernel(GemvParams p) {
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves)
+__attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void swq_skinny_kernel(GemvParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = blockDim.x >> 6;
   const int r = lane & 15, h = lane >> 4;             // A row / B and D column; K-slot group
-  const int col = blockIdx.x * 16 + r;
-  const int colc = min(col, p.I - 1), rowc = min(r, p.M - 1);   // clamped for loads
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int col = (int)n0 + r;
+  const int rowc = min(r, p.M - 1);                   // clamped for loads (rows >= M are dropped)
   const int nchunk = p.H >> 5;
-  const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
-  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
-  const uint32_t* wgr = p.wg + (int64_t)colc * rw_g;
-  const uint32_t* wur = p.wu + (int64_t)colc * rw_u;
-  const uint16_t* sgr = p.sg + (int64_t)colc * (p.H >> lg_g);
-  const uint16_t* bgr = p.bg + (int64_t)colc * (p.H >> lg_g);
-  const uint16_t* sur = p.su + (int64_t)colc * (p.H >> lg_u);
-  const uint16_t* bur = p.bu + (int64_t)colc * (p.H >> lg_u);
+  // the block's 16 columns through buffer descriptors (columns past I read zeros)
+  const int ncols = (int)min((int64_t)16, (int64_t)p.I - n0);
+  const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
+  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols, p.H, BITS_U, p.gs_u);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xa, (short)0, nchunk * p.M * 64, 0x00020000);
   const NibbleK nk = nibble_consts_in_regs();
   const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-  const f16x8 zero8 = {};
 
   auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
     const int cc = d.live ? c : 0;                     // an in-range chunk for the loads
+    const int og = (r * mg.rw + cc * BITS_G) * 4, ou = (r * mu.rw + cc * BITS_U) * 4;
 #pragma unroll
-    for (int i = 0; i < BITS_G / 4; ++i)
-      d.cg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wgr + cc * BITS_G + 4 * i));
+    for (int i = 0; i < BITS_G / 4; ++i) d.cg[i] = __builtin_amdgcn_raw_buffer_load_b128(mg.w, og + 16 * i, 0, 2);
 #pragma unroll
-    for (int i = 0; i < BITS_U / 4; ++i)
-      d.cu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wur + cc * BITS_U + 4 * i));
-    const int gg = (32 * cc) >> lg_g, gu = (32 * cc) >> lg_u;
-    d.sg = bf16_to_f32(sgr[gg]);
-    d.bg = bf16_to_f32(bgr[gg]);
-    d.su = bf16_to_f32(sur[gu]);
-    d.bu = bf16_to_f32(bur[gu]);
-    const _Float16* xr = p.xa + ((int64_t)cc * p.M + rowc) * 32;
+    for (int i = 0; i < BITS_U / 4; ++i) d.cu[i] = __builtin_amdgcn_raw_buffer_load_b128(mu.w, ou + 16 * i, 0, 2);
+    // a chunk past the end gets zero scales and biases: its B operands vanish
+    const int gg = (r * mg.ng + ((32 * cc) >> mg.lg_gs)) * 2, gu = (r * mu.ng + ((32 * cc) >> mu.lg_gs)) * 2;
+    const float keep = d.live ? 1.0f : 0.0f;
+    d.sg = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mg.s, gg, 0, 0));
+    d.bg = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mg.b, gg, 0, 0));
+    d.su = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0));
+    d.bu = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0));
+    const int ox = (cc * p.M + rowc) * 64;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.x[q] = *reinterpret_cast<const u32x4*>(xr + 8 * q);
+    for (int q = 0; q < 4; ++q) d.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
   };
 
   // one matrix's 8-code block kb of a chunk: one MFMA (4-bit) or two (8-bit planes)
-  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, bool live, int kb, const f16x8& a, f32x4& acc) {
+  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, int kb, const f16x8& a, f32x4& acc) {
     const _Float16 hs = (_Float16)sf;
     const f16x2 s2 = {hs, hs};
     if constexpr (BITS == 4) {
       uint32_t o[4];
       dequant4(cw[0][kb], s2, o, nk);
-      const f16x8 b = live ? __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]}) : zero8;
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]}), acc,
+                                                  0, 0, 0);
     } else {
       uint32_t lo[4], hi[4];
       codes8(cw[kb >> 1][2 * (kb & 1)], cw[kb >> 1][2 * (kb & 1) + 1], lo, hi, nk);
@@ -478,8 +478,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void swq_skinny_kernel(GemvPa
         vl[j] = as_u32(as_h2(lo[j]) * s2);
         vh[j] = as_u32(as_h2(hi[j]) * s16);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, live ? __builtin_bit_cast(f16x8, vl) : zero8, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, live ? __builtin_bit_cast(f16x8, vh) : zero8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, vl), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, vh), acc, 0, 0, 0);
     }
   };
 
@@ -488,8 +488,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void swq_skinny_kernel(GemvPa
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f16x8 a = __builtin_bit_cast(f16x8, d.x[kb]);
-      block_mfma.template operator()<BITS_G>(d.cg, d.sg, d.live, kb, a, ag);
-      block_mfma.template operator()<BITS_U>(d.cu, d.su, d.live, kb, a, au);
+      block_mfma.template operator()<BITS_G>(d.cg, d.sg, kb, a, ag);
+      block_mfma.template operator()<BITS_U>(d.cu, d.su, kb, a, au);
     }
     // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
     float sx = 0.0f;
@@ -505,19 +505,16 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void swq_skinny_kernel(GemvPa
     const _Float16 cuh = (_Float16)cuf, cul = (_Float16)(cuf - (float)cuh);
     const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
     const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
-    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, d.live ? beg : zero8, ag, 0, 0, 0);
-    au = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, d.live ? beu : zero8, au, 0, 0, 0);
+    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag, 0, 0, 0);
+    au = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au, 0, 0, 0);
   };
 
-  // chunk quads w, w + nw, ...: two at a time, both loaded before either is used
+  // chunk quads w, w + nw, ... (one for H <= 2048)
   const int nquad = (nchunk + 3) >> 2;
-  for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
-    SkinnyChunk<BITS_G, BITS_U> d0, d1;
-    const bool two = q0 + nw < nquad;                 // wave-uniform
-    load(q0, d0);
-    if (two) load(q0 + nw, d1);
-    compute(d0);
-    if (two) compute(d1);
+  for (int q0 = w; q0 < nquad; q0 += nw) {
+    SkinnyChunk<BITS_G, BITS_U> d;
+    load(q0, d);
+    compute(d);
   }
 
   // the waves' partial sums; D element j of lane l is row 4 (l / 16) + j, column l % 16
