@@ -280,6 +280,10 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.ldx = ldx; p.kext = kext;
   p.bext_g = eg; p.bext_u = eu;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+  {
+    const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
+    p.vec = (I % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
+  }
   const int cfg = choose_mfma_config(M, I);
   const int n_split = choose_column_split(M, I, cfg, bits_g, bits_u);
   if (logging())

@@ -46,6 +46,7 @@ struct MfmaParams {
   void* out;
   float* dbg_g;        // non-null: write float32 gate/up instead of hidden
   float* dbg_u;
+  int vec;             // 1: the output rows allow 16-byte (f32) / 8-byte (bf16) stores of 4 features
 };
 
 struct GemvParams {

@@ -552,23 +552,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
-          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_g[i][f], 0, 0, 0);
-          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ua[f], acc_u[i][f], 0, 0, 0);
-          if (BITS_G == 8) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], gb[f], acc_g[i][f], 0, 0, 0);
-          if (BITS_U == 8) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ub[f], acc_u[i][f], 0, 0, 0);
+          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ga[f], a[i], acc_g[i][f], 0, 0, 0);
+          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ua[f], a[i], acc_u[i][f], 0, 0, 0);
+          if (BITS_G == 8) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gb[f], a[i], acc_g[i][f], 0, 0, 0);
+          if (BITS_U == 8) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ub[f], a[i], acc_u[i][f], 0, 0, 0);
         }
     } else if (kind == 1) {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int i = 0; i < MF; ++i)
-          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_g[i][f], 0, 0, 0);
+          acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ga[f], a[i], acc_g[i][f], 0, 0, 0);
     } else {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int i = 0; i < MF; ++i)
-          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], ga[f], acc_u[i][f], 0, 0, 0);
+          acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ga[f], a[i], acc_u[i][f], 0, 0, 0);
     }
   };
 
@@ -694,31 +694,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   if (tid < BM) rexp[tid] = my_exp;
   __syncthreads();
 
-  // ---- epilogue: lane holds rows 8*(r/4) + 4*half + r%4 of fragment i, column w*WN + 32f + l32
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int ocol = n0 + w * WN + f * 32 + l32;
+  // ---- epilogue.  The MFMAs compute W x'^T, so in fragment (i, f) lane l holds
+  // token row i*32 + l32 and, in accumulator entry 4j + c, feature
+  // w*WN + 32f + 8j + 4*half + c: four consecutive features per j, written
+  // with one vector store when the output allows it (p.vec).
+  auto epilogue = [&]<int MODE>() {                   // 0..2: precision mode, 3: debug gate/up
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
+      const int lr = i * 32 + l32;
+      const int e = rexp[lr];
+      const bool row_ok = lr < rows;
+      const int64_t orow = (int64_t)(m0 + lr) * p.I;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (lr >= rows || ocol >= p.n_end) continue;
-        const int e = rexp[lr];
-        const float g = ldexpf(acc_g[i][f][r], e);
-        const float u = ldexpf(acc_u[i][f][r], e);
-        const int64_t o = (int64_t)(m0 + lr) * p.I + ocol;
-        if (p.dbg_g) {
-          p.dbg_g[o] = g;
-          p.dbg_u[o] = u;
-        } else {
-          const float h = swiglu_epilogue(g, u, p.mode);
-          if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
-          else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
+      for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = n0 + w * WN + f * 32 + 8 * j + 4 * half;
+          float g[4], u[4], h[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            g[c] = ldexpf(acc_g[i][f][4 * j + c], e);
+            u[c] = ldexpf(acc_u[i][f][4 * j + c], e);
+            if constexpr (MODE != 3) h[c] = swiglu_epilogue(g[c], u[c], MODE);
+          }
+          if (!row_ok) continue;
+          const int64_t o = orow + c0;
+          if (p.vec && c0 + 4 <= p.n_end) {
+            if constexpr (MODE == 3) {
+              *reinterpret_cast<f32x4*>(p.dbg_g + o) = (f32x4){g[0], g[1], g[2], g[3]};
+              *reinterpret_cast<f32x4*>(p.dbg_u + o) = (f32x4){u[0], u[1], u[2], u[3]};
+            } else if constexpr (MODE == kF32) {
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o) = (f32x4){h[0], h[1], h[2], h[3]};
+            } else {
+              const uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
+              const uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + o) = (u32x2){lo, hi};
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if (c0 + c >= p.n_end) continue;
+              if constexpr (MODE == 3) {
+                p.dbg_g[o + c] = g[c];
+                p.dbg_u[o + c] = u[c];
+              } else if constexpr (MODE == kF32) {
+                reinterpret_cast<float*>(p.out)[o + c] = h[c];
+              } else {
+                reinterpret_cast<uint16_t*>(p.out)[o + c] = f32_to_bf16(h[c]);
+              }
+            }
+          }
         }
       }
     }
-  }
+  };
+  if (p.dbg_g) epilogue.template operator()<3>();
+  else if (p.mode == kMatch) epilogue.template operator()<kMatch>();
+  else if (p.mode == kF32) epilogue.template operator()<kF32>();
+  else epilogue.template operator()<kF32Bf16Out>();
 }
 
 // ------------------------------------------------------------ launchers ----

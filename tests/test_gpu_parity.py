@@ -218,6 +218,32 @@ def test_tile_shapes_and_column_split_agree_bitwise():
     check(outs["split"][ms, ns], o, 1, "split boundary sampled")
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_output_alignment_paths_agree_bitwise(mode):
+    """The matrix-matrix epilogue writes four consecutive features per store
+    when the output rows allow it (I a multiple of 4, output 16-byte
+    aligned) and one element per store otherwise.  An output view that
+    starts one element into a larger buffer takes the element path; both
+    paths must write the same bits, and match the oracle."""
+    M, H, I = 300, 256, 200
+    p = make_custom(M, H, I, 4, 64, 8, 32, seed=77)
+    dev = swq.to_device(p)
+    dt = torch.float32 if mode == 1 else torch.bfloat16
+    say("alignment", mode)
+    with forced_path(MFMA, M):
+        a = swq.forward(*dev, p.bits_g, p.gs_g, p.bits_u, p.gs_u, mode=mode)
+        big = torch.full((M * I + 8,), float("nan"), dtype=dt, device="cuda")
+        b = big[1:1 + M * I].view(M, I)
+        assert b.data_ptr() % 16 != 0
+        swq.forward(*dev, p.bits_g, p.gs_g, p.bits_u, p.gs_u, mode=mode, out=b)
+    torch.cuda.synchronize()
+    ya = a.float().cpu().numpy().astype(np.float64)
+    yb = b.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(ya, yb)
+    assert torch.isnan(big[0]).item() and torch.isnan(big[1 + M * I:]).all().item()
+    check(ya, oracle_full(p, mode), mode, f"alignment mode{mode}")
+
+
 # -------------------------------------------------------------- invariants --
 
 @pytest.mark.parametrize("path", [GEMV, MFMA])
