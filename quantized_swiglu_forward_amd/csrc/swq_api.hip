@@ -92,9 +92,15 @@ bool gemv_fits(int64_t M, int64_t H) {
   return M >= 1 && M <= kGemvMaxM;
 }
 
-// The M = 1 kernel reads x itself for H <= 4096; otherwise the matrix-vector
-// path stages x' with the prep kernel first.
-bool gemv_needs_rows(int64_t M, int64_t H) { return M > 1 || H > 4096; }
+// The M = 1 kernel reads x itself for H <= 4096, and the few-row kernel
+// builds x' itself for M*H <= kSkinnyStageMax; otherwise the prep kernel
+// stages x' first (in the workspace).  SWIGLU_Q_SKINNY_STAGE=0 always uses
+// the prep kernel.
+bool gemv_needs_rows(int64_t M, int64_t H) {
+  if (M == 1 && H <= 4096) return false;
+  const char* s = getenv("SWIGLU_Q_SKINNY_STAGE");
+  return M * H > kSkinnyStageMax || (s && s[0] == '0');
+}
 
 // Tile shape of the MFMA kernel: 256 x 128 unless that leaves CUs idle
 // (fewer than two tiles per CU of the 256), then 128 x 128.  The environment

@@ -406,7 +406,10 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // so a whole decode-sized grid is resident at once.  A fifth MFMA per chunk adds the bias term
 // sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c each split
 // into binary16 hi + lo, as on the matrix-matrix path.  The waves' partial
-// sums meet in LDS; wave 0 applies 2^e and the epilogue.
+// sums meet in LDS; wave 0 applies 2^e and the epilogue.  STAGE (M H at most
+// kSkinnyStageMax): every block builds x' itself in LDS (the same row
+// powers of two, conversion and layout as the prep kernel's x rows), so the
+// call is one launch.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSkinnyMaxWaves = 16;
 
@@ -417,7 +420,7 @@ struct SkinnyChunk {
   bool live;
 };
 
-template <int BITS_G, int BITS_U>
+template <int BITS_G, int BITS_U, bool STAGE>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
 __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void swq_skinny_kernel(GemvParams p) {
   const int tid = threadIdx.x;
@@ -438,6 +441,11 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
   const NibbleK nk = nibble_consts_in_regs();
   const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
+  // STAGE: x' in LDS as [H/32][M][32] binary16 (16-byte pieces), row exponents beside it
+  __shared__ u32x4 xs[STAGE ? kSkinnyStageMax / 8 : 1];
+  __shared__ int xe[kGemvMaxM];
+  __shared__ uint32_t xmax[kGemvMaxM];
+
   auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
@@ -454,9 +462,16 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
     d.bg = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mg.b, gg, 0, 0));
     d.su = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0));
     d.bu = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0));
-    const int ox = (cc * p.M + rowc) * 64;
+    if constexpr (!STAGE) {
+      const int ox = (cc * p.M + rowc) * 64;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
+      for (int q = 0; q < 4; ++q) d.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
+    }
+  };
+  auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
+    const int c = min(4 * quad + h, nchunk - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d.x[q] = xs[(c * p.M + rowc) * 4 + q];
   };
 
   // one matrix's 8-code block kb of a chunk: one MFMA (4-bit) or two (8-bit planes)
@@ -511,10 +526,50 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
 
   // chunk quads w, w + nw, ... (one for H <= 2048)
   const int nquad = (nchunk + 3) >> 2;
-  for (int q0 = w; q0 < nquad; q0 += nw) {
+  if constexpr (STAGE) {
+    // the first quad's weights are in flight while the block builds x'
     SkinnyChunk<BITS_G, BITS_U> d;
-    load(q0, d);
-    compute(d);
+    if (w < nquad) load(w, d);
+    const int nt = blockDim.x, nblk = p.M * (p.H >> 3);   // 8-value blocks of x
+    if (tid < p.M) xmax[tid] = 0;
+    __syncthreads();
+    for (int b = tid; b < nblk; b += nt) {              // row maxima of |x| (bf16 magnitude bits)
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + 8 * (int64_t)b);
+      uint32_t amax = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amax = max(amax, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+      atomicMax(&xmax[b / (p.H >> 3)], amax);
+    }
+    __syncthreads();
+    if (tid < p.M) xe[tid] = row_exponent(xmax[tid]);
+    __syncthreads();
+    for (int b = tid; b < nblk; b += nt) {              // x' = x 2^-e in the code-pair order
+      const int m = b / (p.H >> 3), k8 = b - m * (p.H >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + 8 * (int64_t)b);
+      const int e = xe[m];
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -e);
+        f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -e);
+      }
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = as_u32((f16x2){(_Float16)f[j], (_Float16)f[j + 4]});
+      xs[((k8 >> 2) * p.M + m) * 4 + (k8 & 3)] = o;
+    }
+    __syncthreads();
+    for (int q0 = w; q0 < nquad; q0 += nw) {
+      if (q0 != w) load(q0, d);
+      load_x_lds(q0, d);
+      compute(d);
+    }
+  } else {
+    for (int q0 = w; q0 < nquad; q0 += nw) {
+      SkinnyChunk<BITS_G, BITS_U> d;
+      load(q0, d);
+      compute(d);
+    }
   }
 
   // the waves' partial sums; D element j of lane l is row 4 (l / 16) + j, column l % 16
@@ -532,7 +587,7 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
     for (int j = 0; j < 4; ++j) {
       const int m = 4 * h + j;
       if (m < p.M && col < p.I) {
-        const int e = p.xexp[m];
+        const int e = STAGE ? xe[m] : p.xexp[m];
         store_out(p, m, col, ldexpf(g[j], e), ldexpf(u[j], e));
       }
     }
@@ -591,11 +646,16 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     return full ? launch_gemv1_t<BG, BU, 2, true>(p, gemv1_rounds(), stream)
                 : launch_gemv1_t<BG, BU, 2, false>(p, gemv1_rounds(), stream);
   }
-  if (p.M < 1 || p.M > kGemvMaxM || p.xa == nullptr) return hipErrorInvalidValue;
+  if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
   // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns
   const int quads = (p.H / 32 + 3) / 4;
   const int waves = quads < kSkinnyMaxWaves ? quads : kSkinnyMaxWaves;
-  hipLaunchKernelGGL((swq_skinny_kernel<BG, BU>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+  if (p.xa == nullptr) {
+    if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

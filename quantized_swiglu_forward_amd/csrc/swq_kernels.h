@@ -63,7 +63,7 @@ struct GemvParams {
   void* out;
   float* dbg_g;
   float* dbg_u;
-  const _Float16* xa;  // M >= 2 (or H > 4096): x' staged by the prep kernel, [H/32][M][32]
+  const _Float16* xa;  // x' staged by the prep kernel, [H/32][M][32] (M*H > kSkinnyStageMax), or null
   const int* xexp;     // and its row exponents
 };
 
@@ -81,6 +81,8 @@ constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
 // Largest M the matrix-vector path takes (one 16-row MFMA tile).
 constexpr int kGemvMaxM = 16;
+// M*H up to this: the few-row kernel builds x' itself (one launch, no workspace).
+constexpr int kSkinnyStageMax = 8192;
 
 inline int kext_columns(int64_t H, int g0) {
   const int64_t c = 3 * (H / g0);

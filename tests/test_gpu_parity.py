@@ -182,6 +182,24 @@ def test_gemv_and_mfma_agree(M):
     check(ym, o, 1, f"mfma M{M}")
 
 
+# the few-row kernel with x' built inside the kernel (M*H <= 8192: one
+# launch) and staged by the prep kernel (larger), on both sides of the
+# boundary, both bit widths, and M = 1 past the M = 1 kernel's H limit
+FEW_ROW = [(2, 4096, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (4, 2048, 257, (8, 64, 4, 128)),
+           (5, 2048, 96, (4, 32, 4, 64)), (9, 2048, 300, (4, 64, 4, 64)), (16, 2048, 129, (8, 32, 8, 64)),
+           (12, 4096, 64, (4, 128, 4, 64)), (16, 512, 100, (4, 64, 8, 64)), (1, 8192, 200, (4, 64, 4, 64)),
+           (1, 16384, 33, (8, 64, 4, 32)), (1, 32768, 40, (4, 64, 4, 64))]
+
+
+@pytest.mark.parametrize("M,H,I,spec", FEW_ROW, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in FEW_ROW])
+def test_few_row_kernel_x_staging(M, H, I, spec):
+    mode = (M + H // 1024) % 3
+    p = make_custom(M, H, I, *spec, seed=M * 31 + I)
+    say("few-row", M, H, I, spec, "mode", mode)
+    y = device_forward(p, mode, GEMV)
+    check(y, oracle_full(p, mode), mode, f"few-row M{M} H{H} I{I}")
+
+
 # ------------------------------------------------- tile shapes and splits --
 
 def test_tile_shapes_and_column_split_agree_bitwise():
