@@ -105,6 +105,33 @@ int swiglu_q_forward(const void *x,
                      int bits_g, int gs_g, int bits_u, int gs_u,
                      int precision_mode, void *out, void *stream);
 
+/* Output types of swiglu_q_linear. */
+#define SWQ_LINEAR_BF16  0  /* float32 sums rounded once to bf16 (RNE) at the store */
+#define SWQ_LINEAR_F32   1  /* float32 sums stored as float32                      */
+
+/*
+ * Quantized linear: out = x·Wᵀ, the plain projection the fused forward's
+ * output feeds (the down projection; "mlx-bun 0.0.7 -> 0.0.9" diff, page 43,
+ * steel-linear-kernel.ts: its header comment defines it as y = x·Wᵀ over an
+ * affine-quantized W, stored in the activation type).
+ *   x         bf16 [M, K] device pointer
+ *   W, s, b   codes [N, K·bits/32], scales and biases [N, K/gs] (same packing
+ *             and dequantization w = s·q + b as the forward)
+ *   M, K, N   rows of x, input size, output size
+ *   bits, gs  bits in {4, 8}, gs in {32, 64, 128}, K a multiple of gs and 32
+ *   out_mode  SWQ_LINEAR_BF16 or SWQ_LINEAR_F32
+ *   out       [M, N] device pointer, bf16 or float32 by out_mode
+ *   stream    hipStream_t (NULL = null stream)
+ * The sums are float32 dot products of the exactly dequantized weights (the
+ * forward's arithmetic).  It runs on the forward's kernels and dispatcher
+ * (threshold, workspace and counters included), W's first ceil(N/2) rows in
+ * the gate slot and the rest in the up slot.  Same status codes, limits and
+ * alignment rules as swiglu_q_forward with H = K and I = ceil(N/2).
+ */
+int swiglu_q_linear(const void *x, const uint32_t *W, const void *s, const void *b,
+                    int64_t M, int64_t K, int64_t N, int bits, int gs,
+                    int out_mode, void *out, void *stream);
+
 /* 1 if the combination is supported by swiglu_q_forward, else 0 (mirrors the
  * pages' support predicate, restricted to what this library implements). */
 int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,

@@ -7,7 +7,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 * ``swiglu_pairs`` / ``swiglu_full`` -- the float64 reference of
   ``hidden = silu(x Wg^T) * (x Wu^T)`` with affine group-quantized weights,
   in plain C (``swiglu_oracle.c``), one output element at a time.
-* ``qmm`` -- one plain quantized projection (the unfused building block).
+* ``qmm`` -- one plain quantized projection (the unfused building block), and
+  ``qmm_pairs`` -- the same sums element by element with their scales (the
+  reference of the quantized linear ``y = x W^T``).
 * ``exact`` -- an exact rational brute force for tiny shapes.
 * ``compare`` -- the per-element error metric used by the parity tests.
 """
@@ -116,6 +118,29 @@ def qmm(x_bits, W, S, B, M, H, N, bits, gs):
     if L.oracle_qmm(_p(x), _p(W), _p(S), _p(B), M, H, N, bits, gs, _p(y)) != 0:
         raise ValueError("oracle rejected its arguments")
     return y
+
+
+def qmm_pairs(x_bits, W, S, B, M, H, N, bits, gs, ms=None, ns=None, nthreads=0):
+    """``y = x W^T`` and its scale ``nu = sqrt(sum_k (x_k w_k)^2)`` in float64 at
+    the elements (ms[p], ns[p]) (every element, row-major, when None): the
+    oracle's gate dot product with W in both slots.  Returns (y, nu)."""
+    L = lib()
+    x, W, S, B = _c(x_bits, np.uint16), _c(W, np.uint32), _c(S, np.uint16), _c(B, np.uint16)
+    if ms is None:
+        n = M * N
+        msa = nsa = None
+    else:
+        msa, nsa = _c(ms, np.int64), _c(ns, np.int64)
+        if msa.shape != nsa.shape:
+            raise ValueError("ms and ns differ in length")
+        n = msa.size
+    y = np.empty(n, dtype=np.float64)
+    nu = np.empty(n, dtype=np.float64)
+    rc = L.oracle_swiglu_pairs(_p(x), _p(W), _p(S), _p(B), _p(W), _p(S), _p(B), M, H, N, bits, gs, bits, gs, 1,
+                               n, _p(msa), _p(nsa), _p(y), None, _p(nu), None, None, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return y, nu
 
 
 def unpack(W, rows, H, bits):

@@ -112,3 +112,36 @@ def evaluate(y, o, mode, eta=ETA):
     }
     stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= TOL[mode]))
     return stats
+
+
+LINEAR_TOL = {0: 8e-3, 1: 1e-4}   # bf16 output, float32 output
+
+
+def evaluate_linear(y, r, nu, out_mode, eta=ETA):
+    """Compare a device linear ``y = x W^T`` against the oracle's float64 sums
+    ``r`` and their scales ``nu``.  The same metric with the floor of a single
+    dot product, ``tau_i = 2^-4 * nu_i``; for bf16 output both roundings of a
+    sum within ``eta * nu`` of a bf16 midpoint are admissible."""
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    r0 = np.asarray(r, dtype=np.float64).reshape(-1)
+    nu = np.asarray(nu, dtype=np.float64).reshape(-1)
+    if out_mode == 0:
+        a, b = bf16_candidates(r0, nu, eta)
+        ref = np.where(np.abs(y - a) <= np.abs(y - b), a, b)
+    else:
+        ref = r0
+    rms = float(np.sqrt(np.mean(r0 * r0))) if r0.size else 0.0
+    denom = np.maximum(np.maximum(np.abs(ref), FLOOR * nu), TAU0 * rms)
+    diff = np.abs(y - ref)
+    finite = np.isfinite(y)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(denom > 0, diff / np.where(denom > 0, denom, 1.0),
+                       np.where(diff == 0, 0.0, np.inf))
+    err = np.where(finite, err, np.inf)
+    n = y.size
+    worst = int(np.argmax(err)) if n else -1
+    stats = {"n": n, "max_err": float(err[worst]) if n else 0.0, "worst_index": worst,
+             "nonfinite": int(np.sum(~finite)), "tol": LINEAR_TOL[out_mode],
+             "max_abs_over_rms": float(np.max(diff) / rms) if (n and rms > 0) else 0.0}
+    stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= LINEAR_TOL[out_mode]))
+    return stats

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG, "libswiglu_q.so")
 SWQ_OK, SWQ_ERR_NULL, SWQ_ERR_SHAPE, SWQ_ERR_UNSUPPORTED, SWQ_ERR_ALIGN, SWQ_ERR_HIP, SWQ_ERR_WORKSPACE = range(7)
 SWQ_MATCH, SWQ_F32, SWQ_F32_BF16OUT = 0, 1, 2
 SWQ_PATH_GEMV, SWQ_PATH_MFMA, SWQ_PATH_AUTO = 0, 1, -1
+SWQ_LINEAR_BF16, SWQ_LINEAR_F32 = 0, 1
 
 _lib = None
 
@@ -43,6 +44,8 @@ def lib():
     vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
     L.swiglu_q_forward.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
     L.swiglu_q_forward.restype = i32
+    L.swiglu_q_linear.argtypes = [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp, vp]
+    L.swiglu_q_linear.restype = i32
     L.swiglu_q_debug_gemm.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
     L.swiglu_q_debug_gemm.restype = i32
     L.swiglu_q_supported.argtypes = [i64, i32, i32, i32, i32, i32]
@@ -91,6 +94,11 @@ def swiglu_q_forward(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, g
     return lib().swiglu_q_forward(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
                                   M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
                                   _stream(stream))
+
+
+def swiglu_q_linear(x, W, s, b, M, K, N, bits, gs, out_mode, out, stream=None) -> int:
+    return lib().swiglu_q_linear(_ptr(x), _ptr(W), _ptr(s), _ptr(b), M, K, N, bits, gs, out_mode, _ptr(out),
+                                 _stream(stream))
 
 
 def swiglu_q_debug_gemm(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, path,
@@ -157,6 +165,21 @@ def forward(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_u=None,
     rc = swiglu_q_forward(x, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
     if rc != SWQ_OK:
         raise SwigluQError(rc, "swiglu_q_forward")
+    return out
+
+
+def linear(x, w, s, b, bits, gs, out_mode=SWQ_LINEAR_BF16, out=None, stream=None):
+    """``x W^T`` for device tensors: x [M, K] bf16, packed codes [N, K*bits/32],
+    scales/biases bf16 [N, K/gs].  Returns ``out`` ([M, N], bf16 or float32)."""
+    import torch
+    M, K = int(x.shape[0]), int(x.shape[1])
+    N = int(w.shape[0])
+    if out is None:
+        dt = torch.float32 if out_mode == SWQ_LINEAR_F32 else torch.bfloat16
+        out = torch.empty((M, N), dtype=dt, device=x.device)
+    rc = swiglu_q_linear(x, w, s, b, M, K, N, bits, gs, out_mode, out, stream)
+    if rc != SWQ_OK:
+        raise SwigluQError(rc, "swiglu_q_linear")
     return out
 
 

@@ -201,10 +201,12 @@ int get_workspace(hipStream_t stream, size_t need, void** out) {
   return SWQ_OK;
 }
 
+// I_u: rows of the up matrix (I, or fewer for the linear's split weight);
+// ldo: output row stride in elements (I, or N for the linear).
 int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
-        const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
-        int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u, int path,
-        void* stream_v) {
+        const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int64_t I_u, int64_t ldo,
+        int bits_g, int gs_g, int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u,
+        int path, void* stream_v) {
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
@@ -218,6 +220,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     p.wg = Wg; p.sg = (const uint16_t*)sg; p.bg = (const uint16_t*)bg;
     p.wu = Wu; p.su = (const uint16_t*)su; p.bu = (const uint16_t*)bu;
     p.M = (int)M; p.H = (int)H; p.I = (int)I;
+    p.I_u = (int)I_u; p.ldo = (int)ldo;
     p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
     p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
     p.xa = nullptr; p.xexp = nullptr;
@@ -235,7 +238,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       if (rc != SWQ_OK) return rc;
       PrepParams pp{};
       pp.x = (const uint16_t*)x;
-      pp.M = (int)M; pp.H = (int)H; pp.I = 0;
+      pp.M = (int)M; pp.H = (int)H; pp.I = 0; pp.I_u = 0;
       pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
       pp.g0 = 32; pp.ldx = (int)H + kext; pp.kext = kext;
       pp.xa = (_Float16*)ws;
@@ -268,7 +271,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.x = (const uint16_t*)x;
   pp.sg = (const uint16_t*)sg; pp.bg = (const uint16_t*)bg;
   pp.su = (const uint16_t*)su; pp.bu = (const uint16_t*)bu;
-  pp.M = (int)M; pp.H = (int)H; pp.I = (int)I;
+  pp.M = (int)M; pp.H = (int)H; pp.I = (int)I; pp.I_u = (int)I_u;
   pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
   pp.g0 = g0; pp.ldx = ldx; pp.kext = kext;
   pp.xa = xa; pp.xexp = xexp;
@@ -280,6 +283,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.wg = Wg; p.sg = (const uint16_t*)sg;
   p.wu = Wu; p.su = (const uint16_t*)su;
   p.M = (int)M; p.H = (int)H; p.I = (int)I;
+  p.I_u = (int)I_u; p.ldo = (int)ldo;
   p.n_begin = 0; p.n_end = (int)I;
   p.scl = scl; p.nss = nss;
   p.gs_g = gs_g; p.gs_u = gs_u;
@@ -288,7 +292,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
   {
     const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
-    p.vec = (I % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
+    p.vec = (I % 4 == 0) && (ldo % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
   }
   const int cfg = choose_mfma_config(M, I);
   const int n_split = choose_column_split(M, I, cfg, bits_g, bits_u);
@@ -316,8 +320,24 @@ int swiglu_q_forward(const void* x, const uint32_t* Wg, const void* sg, const vo
   if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return SWQ_ERR_UNSUPPORTED;
   if (!out) return SWQ_ERR_NULL;
   if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
-  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
              nullptr, nullptr, SWQ_PATH_AUTO, stream);
+}
+
+int swiglu_q_linear(const void* x, const uint32_t* W, const void* s, const void* b, int64_t M, int64_t K,
+                    int64_t N, int bits, int gs, int out_mode, void* out, void* stream) {
+  // W's rows [0, Ig) run in the gate slot of the fused kernels, [Ig, N) in the up slot
+  const int64_t Ig = N > 0 ? (N + 1) / 2 : 0, Iu = N - Ig;
+  int rc = validate(x, W, s, b, W, s, b, M, K, Ig, bits, gs, bits, gs);
+  if (rc != SWQ_OK) return rc;
+  if (out_mode != SWQ_LINEAR_BF16 && out_mode != SWQ_LINEAR_F32) return SWQ_ERR_UNSUPPORTED;
+  if (!out) return SWQ_ERR_NULL;
+  if (!aligned(out, out_mode == SWQ_LINEAR_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
+  const uint32_t* Wu = W + Ig * (K * bits / 32);
+  const uint16_t* su = (const uint16_t*)s + Ig * (K / gs);
+  const uint16_t* bu = (const uint16_t*)b + Ig * (K / gs);
+  return run(x, W, s, b, Wu, su, bu, M, K, Ig, Iu, N, bits, gs, bits, gs,
+             out_mode == SWQ_LINEAR_F32 ? swq::kLinF32 : swq::kLinBf16, out, nullptr, nullptr, SWQ_PATH_AUTO, stream);
 }
 
 int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
@@ -329,7 +349,7 @@ int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const
   if (path != SWQ_PATH_AUTO && path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return SWQ_ERR_UNSUPPORTED;
   if (!gate_out || !up_out) return SWQ_ERR_NULL;
   if (!aligned(gate_out, 4) || !aligned(up_out, 4)) return SWQ_ERR_ALIGN;
-  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, SWQ_F32, nullptr, gate_out,
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, SWQ_F32, nullptr, gate_out,
              up_out, path, stream);
 }
 

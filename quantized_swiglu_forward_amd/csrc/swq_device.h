@@ -137,6 +137,7 @@ __device__ __forceinline__ float sigmoid_fast(float t) {
 
 // Precision modes (values fixed by the public header).
 enum : int { kMatch = 0, kF32 = 1, kF32Bf16Out = 2 };
+// (the linear's epilogue kinds kLinBf16 / kLinF32 are in swq_kernels.h)
 
 // The epilogue on one element: gate g and up u in float32.
 __device__ __forceinline__ float swiglu_epilogue(float g, float u, int mode) {

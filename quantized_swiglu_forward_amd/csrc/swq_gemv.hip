@@ -63,10 +63,18 @@ __device__ __forceinline__ void load_chunk_buf(RawChunk<BITS>& r, const MatBufs&
 
 
 __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, float g, float u) {
-  const int64_t o = (int64_t)m * p.I + n;
+  const int64_t o = (int64_t)m * p.ldo + n;
   if (p.dbg_g) {
     p.dbg_g[o] = g;
     p.dbg_u[o] = u;
+  } else if (p.mode >= kLinBf16) {
+    if (p.mode == kLinF32) {
+      reinterpret_cast<float*>(p.out)[o] = g;
+      if (n < p.I_u) reinterpret_cast<float*>(p.out)[o + p.I] = u;
+    } else {
+      reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(g);
+      if (n < p.I_u) reinterpret_cast<uint16_t*>(p.out)[o + p.I] = f32_to_bf16(u);
+    }
   } else {
     const float h = swiglu_epilogue(g, u, p.mode);
     if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
@@ -317,7 +325,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
   const int64_t n0 = (int64_t)wave_global * R * cpw;           // the wave's first column
   const int ncols = (int)max((int64_t)0, min((int64_t)R * cpw, (int64_t)p.I - n0));
   const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
-  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols, p.H, BITS_U, p.gs_u);
+  const int ncols_u = (int)max((int64_t)0, min((int64_t)ncols, (int64_t)p.I_u - n0));
+  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols_u, p.H, BITS_U, p.gs_u);
   RawChunk<BITS_G> rg[R][CPL];
   RawChunk<BITS_U> ru[R][CPL];
 #pragma unroll
@@ -435,7 +444,8 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
   // the block's 16 columns through buffer descriptors (columns past I read zeros)
   const int ncols = (int)min((int64_t)16, (int64_t)p.I - n0);
   const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
-  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols, p.H, BITS_U, p.gs_u);
+  const int ncols_u = (int)max((int64_t)0, min((int64_t)ncols, (int64_t)p.I_u - n0));
+  const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols_u, p.H, BITS_U, p.gs_u);
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.xa, (short)0, nchunk * p.M * 64, 0x00020000);
   const NibbleK nk = nibble_consts_in_regs();

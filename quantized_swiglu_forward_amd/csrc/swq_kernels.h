@@ -6,6 +6,13 @@
 
 namespace swq {
 
+// Epilogue kinds of the quantized linear y = x W^T (after the precision modes
+// 0..2 of the fused forward).  It runs on the same kernels with W's rows split
+// in two, the first ceil(N/2) in the gate slot and the rest in the up slot; the
+// epilogue stores both projections as they are, gate column n at n and up
+// column n at I + n (I = ceil(N/2)), rounded to bf16 or as float32.
+constexpr int kLinBf16 = 4, kLinF32 = 5;
+
 // Row staging of x for the matrix-matrix path, and the extra-column rows
 // that carry the per-group bias term.
 struct PrepParams {
@@ -15,6 +22,7 @@ struct PrepParams {
   const uint16_t* su;
   const uint16_t* bu;
   int M, H, I;
+  int I_u;             // rows of the up matrix: I, or fewer (the second half of a split linear weight)
   int gs_g, gs_u, bits_g, bits_u;
   int g0;              // min(gs_g, gs_u): granularity of the group sums
   int ldx;             // columns of x': H + kext (a multiple of 32)
@@ -35,6 +43,8 @@ struct MfmaParams {
   const uint32_t* wu;
   const uint16_t* su;
   int M, H, I;
+  int I_u;             // rows of the up matrix (I, or fewer for a split linear weight)
+  int ldo;             // output row stride in elements (I, or N for the linear)
   int n_begin, n_end;  // output columns [n_begin, n_end) of this launch
   const uint32_t* scl; // scale tiles written by the prep kernel
   int nss;
@@ -58,6 +68,8 @@ struct GemvParams {
   const uint16_t* su;
   const uint16_t* bu;
   int M, H, I;
+  int I_u;             // rows of the up matrix (I, or fewer for a split linear weight)
+  int ldo;             // output row stride in elements (I, or N for the linear)
   int gs_g, gs_u;
   int mode;
   void* out;

@@ -29,9 +29,11 @@
 //     H columns (packed codes, dequantized in registers) and then the extra
 //     columns (precomputed binary16 rows); epilogue 2^e, then silu(g) * u per
 //     precision mode.
+#include <type_traits>
 #include <utility>
 
 #include "swq_device.h"
+
 #include "swq_kernels.h"
 
 namespace swq {
@@ -160,7 +162,7 @@ __device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, 
       if (i < (kScaleTileCols << lg_gpb)) {
         const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
         const int64_t n = n0 + row;
-        src[mat][row][g] = (n < p.I && g0 + g < ng) ? S[n * ng + g0 + g] : (uint16_t)0;
+        src[mat][row][g] = (n < (mat ? p.I_u : p.I) && g0 + g < ng) ? S[n * ng + g0 + g] : (uint16_t)0;
       }
     }
   }
@@ -176,7 +178,7 @@ __device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, 
     if (j >= p.nss) continue;
     const int tl = 4 * jl + q;                           // K-step within the block
     uint32_t v = 0;
-    if (4 * j + q < s_main && n0 + col < p.I) {
+    if (4 * j + q < s_main && n0 + col < (mat ? p.I_u : p.I)) {
       const _Float16 h = (_Float16)bf16_to_f32(src[mat][col][(32 * tl) >> (mat ? lg_u : lg_g)]);
       v = as_u32((f16x2){h, h});
     }
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   const int G = (int)(idx & ((1 << lg) - 1));
   const int64_t rest = idx >> lg;
   const int64_t n = rest >> 1;
-  if (n >= p.I) return;
+  if (n >= ((rest & 1) ? p.I_u : p.I)) return;       // up rows past I_u: read as zeros by the GEMM
   const int lg_g0 = __builtin_ctz(p.g0);
   const int ngroups = p.H >> lg_g0;
   if ((rest & 1) == 0)
@@ -372,6 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int n0 = p.n_begin + (in_grp / gsz) * BN;
   const int rows = min(BM, p.M - m0);
   const int cols = min(BN, p.n_end - n0);
+  const int cols_u = max(0, min(cols, p.I_u - n0));   // up rows of the tile (fewer for a split linear weight)
 
   const int s_main = p.H / 32;
   const int s_ext = p.kext / 32;
@@ -382,11 +385,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const i32x4 rs_a = make_srsrc(p.xa + (int64_t)m0 * 32, (uint32_t)(((int64_t)(p.ldx / 32) * p.M - m0) * 64));
   const uint32_t a_step = (uint32_t)p.M * 64;
   const i32x4 rs_wg = make_srsrc(p.wg + (int64_t)n0 * rw_g, (uint32_t)cols * rw_g * 4);
-  const i32x4 rs_wu = make_srsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols * rw_u * 4);
+  const i32x4 rs_wu = make_srsrc(p.wu + (int64_t)n0 * rw_u, (uint32_t)cols_u * rw_u * 4);
   const i32x4 rs_sc = make_srsrc(p.scl + (int64_t)(n0 / BN) * p.nss * kScaleTileWords,
                                  (uint32_t)p.nss * kScaleTileWords * 4);
   const i32x4 rs_eg = make_srsrc(p.bext_g + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
-  const i32x4 rs_eu = make_srsrc(p.bext_u + (int64_t)n0 * p.kext, (uint32_t)cols * p.kext * 2);
+  const i32x4 rs_eu = make_srsrc(p.bext_u + (int64_t)n0 * p.kext, (uint32_t)cols_u * p.kext * 2);
 
   // ---- per-thread DMA offsets (bytes)
   // A: LDS piece L = j*NT + tid holds row L/4, chunk (L%4) ^ ((row>>2)&3)
@@ -698,13 +701,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // token row i*32 + l32 and, in accumulator entry 4j + c, feature
   // w*WN + 32f + 8j + 4*half + c: four consecutive features per j, written
   // with one vector store when the output allows it (p.vec).
-  auto epilogue = [&]<int MODE>() {                   // 0..2: precision mode, 3: debug gate/up
+  // four consecutive outputs at element offset o of a float32 or bf16 array,
+  // columns c0 .. c0 + 3 stored while below lim
+  auto put4 = [&](auto* base, int64_t o, int c0, int lim, const float (&v)[4]) {
+    constexpr bool F32 = std::is_same_v<std::remove_pointer_t<decltype(base)>, float>;
+    if (p.vec && c0 + 4 <= lim) {
+      if constexpr (F32) {
+        *reinterpret_cast<f32x4*>(base + o) = (f32x4){v[0], v[1], v[2], v[3]};
+      } else {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(base + o) = (u32x2){lo, hi};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c0 + c >= lim) continue;
+        if constexpr (F32) base[o + c] = v[c];
+        else base[o + c] = f32_to_bf16(v[c]);
+      }
+    }
+  };
+  // MODE 0..2: precision mode; 3: debug gate/up; kLinBf16, kLinF32: the linear
+  auto epilogue = [&]<int MODE>() {
+    constexpr bool LIN = MODE == kLinBf16 || MODE == kLinF32;
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int lr = i * 32 + l32;
       const int e = rexp[lr];
       const bool row_ok = lr < rows;
-      const int64_t orow = (int64_t)(m0 + lr) * p.I;
+      const int64_t orow = (int64_t)(m0 + lr) * p.ldo;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
 #pragma unroll
@@ -715,34 +741,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
           for (int c = 0; c < 4; ++c) {
             g[c] = ldexpf(acc_g[i][f][4 * j + c], e);
             u[c] = ldexpf(acc_u[i][f][4 * j + c], e);
-            if constexpr (MODE != 3) h[c] = swiglu_epilogue(g[c], u[c], MODE);
+            if constexpr (MODE < 3) h[c] = swiglu_epilogue(g[c], u[c], MODE);
           }
           if (!row_ok) continue;
           const int64_t o = orow + c0;
-          if (p.vec && c0 + 4 <= p.n_end) {
-            if constexpr (MODE == 3) {
-              *reinterpret_cast<f32x4*>(p.dbg_g + o) = (f32x4){g[0], g[1], g[2], g[3]};
-              *reinterpret_cast<f32x4*>(p.dbg_u + o) = (f32x4){u[0], u[1], u[2], u[3]};
-            } else if constexpr (MODE == kF32) {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o) = (f32x4){h[0], h[1], h[2], h[3]};
-            } else {
-              const uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-              const uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
-              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + o) = (u32x2){lo, hi};
-            }
+          if constexpr (MODE == 3) {
+            put4(p.dbg_g, o, c0, p.n_end, g);
+            put4(p.dbg_u, o, c0, p.n_end, u);
+          } else if constexpr (LIN) {
+            auto* y = reinterpret_cast<std::conditional_t<MODE == kLinF32, float, uint16_t>*>(p.out);
+            put4(y, o, c0, p.n_end, g);
+            put4(y, o + p.I, c0, min(p.n_end, p.I_u), u);
+          } else if constexpr (MODE == kF32) {
+            put4(reinterpret_cast<float*>(p.out), o, c0, p.n_end, h);
           } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              if (c0 + c >= p.n_end) continue;
-              if constexpr (MODE == 3) {
-                p.dbg_g[o + c] = g[c];
-                p.dbg_u[o + c] = u[c];
-              } else if constexpr (MODE == kF32) {
-                reinterpret_cast<float*>(p.out)[o + c] = h[c];
-              } else {
-                reinterpret_cast<uint16_t*>(p.out)[o + c] = f32_to_bf16(h[c]);
-              }
-            }
+            put4(reinterpret_cast<uint16_t*>(p.out), o, c0, p.n_end, h);
           }
         }
       }
@@ -751,7 +764,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   if (p.dbg_g) epilogue.template operator()<3>();
   else if (p.mode == kMatch) epilogue.template operator()<kMatch>();
   else if (p.mode == kF32) epilogue.template operator()<kF32>();
-  else epilogue.template operator()<kF32Bf16Out>();
+  else if (p.mode == kF32Bf16Out) epilogue.template operator()<kF32Bf16Out>();
+  else if (p.mode == kLinBf16) epilogue.template operator()<kLinBf16>();
+  else epilogue.template operator()<kLinF32>();
 }
 
 // ------------------------------------------------------------ launchers ----

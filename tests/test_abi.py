@@ -95,6 +95,30 @@ def test_debug_gemm_validation():
     assert swq.swiglu_q_debug_gemm(**{**base, "M": 4096, "path": 0}) == swq.SWQ_ERR_UNSUPPORTED
 
 
+def test_linear_validation():
+    """swiglu_q_linear checks its arguments before any HIP call: M = 0 is a
+    no-op, bad shapes, specs, output types and alignments are rejected."""
+    base = dict(x=P, W=P, s=P, b=P, M=4, K=256, N=65, bits=4, gs=64, out_mode=0, out=P, stream=0)
+    before = (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1))
+    assert swq.swiglu_q_linear(**{**base, "M": 0}) == swq.SWQ_OK
+    assert swq.swiglu_q_linear(**{**base, "W": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_linear(**{**base, "out": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_linear(**{**base, "N": 0}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_linear(**{**base, "N": -3}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_linear(**{**base, "K": 96}) == swq.SWQ_ERR_SHAPE        # not a multiple of gs
+    assert swq.swiglu_q_linear(**{**base, "K": 80, "gs": 32}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_linear(**{**base, "M": -1}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_linear(**{**base, "bits": 3}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_linear(**{**base, "gs": 16}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_linear(**{**base, "out_mode": 2}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_linear(**{**base, "x": P + 8}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_linear(**{**base, "W": P + 4}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_linear(**{**base, "s": P + 1}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_linear(**{**base, "out": P + 1}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_linear(**{**base, "out": P + 2, "out_mode": 1}) == swq.SWQ_ERR_ALIGN
+    assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
+
+
 def test_supported_predicate():
     assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 0) == 1
     assert swq.swiglu_q_supported(2560, 8, 32, 4, 64, 1) == 1

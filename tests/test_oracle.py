@@ -113,6 +113,46 @@ def test_oracle_matches_exact_rationals(bits, gs, H):
     assert exact.qmm_grouped_exact(xg, p.wg, p.sg, p.bg, M, H, I, bits, gs) == ex_g
 
 
+@pytest.mark.parametrize("bits,gs", SPECS)
+def test_linear_reference_matches_exact_rationals(bits, gs):
+    """The quantized linear's reference (``qmm``, and ``qmm_pairs`` element by
+    element) against exact rational arithmetic, with an odd output size."""
+    M, H, N = 3, 128, 5
+    p = make_custom(M, H, N, bits, gs, bits, gs, seed=bits * 13 + gs)
+    xg = [list(r) for r in p.x]
+    ex = exact.qmm_exact(xg, p.wg, p.sg, p.bg, M, H, N, bits, gs)
+    y = oracle.qmm(p.x, p.wg, p.sg, p.bg, M, H, N, bits, gs)
+    yp, nu = oracle.qmm_pairs(p.x, p.wg, p.sg, p.bg, M, H, N, bits, gs, nthreads=2)
+    assert np.array_equal(y.reshape(-1), yp)            # the same sum in the same order
+    ms, ns = np.array([2, 0, 1]), np.array([4, 3, 0])
+    ys, nus = oracle.qmm_pairs(p.x, p.wg, p.sg, p.bg, M, H, N, bits, gs, ms, ns)
+    assert np.array_equal(ys, y[ms, ns]) and np.array_equal(nus, nu.reshape(M, N)[ms, ns])
+    for m in range(M):
+        for n in range(N):
+            assert _rel_to_scale(y[m, n], float(ex[m][n]), nu[m * N + n]) <= 1e-14
+
+
+def test_linear_metric_catches_planted_errors():
+    """The linear bar: the float64 sums pass, their bf16 and float32
+    roundings pass in their modes; a 2 % error (bf16 bar 8e-3), a 0.1 %
+    error (float32 bar 1e-4) or a wrong sign fails."""
+    M, H, N = 4, 256, 33
+    p = make_custom(M, H, N, 4, 64, 4, 64, seed=9)
+    r, nu = oracle.qmm_pairs(p.x, p.wg, p.sg, p.bg, M, H, N, 4, 64)
+    assert compare.evaluate_linear(r, r, nu, 0)["ok"] and compare.evaluate_linear(r, r, nu, 1)["ok"]
+    rb = oracle.bf16_value(oracle.bf16_rne(r))
+    assert compare.evaluate_linear(rb, r, nu, 0)["ok"]
+    assert not compare.evaluate_linear(rb, r, nu, 1)["ok"]
+    assert compare.evaluate_linear(r.astype(np.float32), r, nu, 1)["ok"]
+    big = np.argmax(np.abs(r))
+    bad = r.copy(); bad[big] *= 1.02
+    assert not compare.evaluate_linear(bad, r, nu, 0)["ok"]
+    bad = r.copy(); bad[big] *= 1.001
+    assert not compare.evaluate_linear(bad, r, nu, 1)["ok"]
+    bad = r.copy(); bad[big] = -bad[big]
+    assert not compare.evaluate_linear(bad, r, nu, 1)["ok"]
+
+
 def test_mixed_specs_against_exact():
     M, H, I = 2, 128, 3
     p = make_custom(M, H, I, 8, 32, 4, 64, seed=5, bias_mode="half")
