@@ -14,7 +14,11 @@ matrix-matrix path on the three prefill configurations (TFLOP/s and fraction
 of the bf16/f16 dense MFMA peak).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|c2|c3|c4|copy]
-                    [--no-prefill] [--no-cpu] [--eager]
+                    [--no-prefill] [--no-linear] [--no-cpu] [--eager]
+
+Unless ``--no-linear``: the quantized linear ``y = x W^T`` at the two down
+projections (decode model: M=1, K=5632, N=2048 with rotating weights as
+above; M=2048 prefill model: K=14336, N=4096), under ``linear``.
 
 ``--workload copy`` times a plain device-to-device copy of one decode call's
 algorithmic byte count, 1000 copies per step over 40 rotating sources: the
@@ -270,6 +274,87 @@ def bench_prefill_one(cfg, steps, warmup, mode=0):
             "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
 
 
+def bench_linear(M, K, N, bits, gs, steps, warmup, rotating):
+    """The quantized linear at one shape, bf16 output.  ``rotating``: 1000
+    calls per step on fresh x rows over 40 weight sets (drawn on the GPU from
+    the generator's distributions), recorded into a HIP graph; otherwise
+    ``steps`` calls on one problem."""
+    import numpy as np
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import make_custom
+
+    rows = CALLS if rotating else M
+    p = make_custom(rows, K, N, bits, gs, bits, gs, seed=K + N, bias_mode="factor")
+    dev = swq.to_device(p)
+    x, w, s, b = dev[:4]
+    wb = N * K * bits // 8 + 2 * 2 * N * (K // gs)
+    stream = torch.cuda.Stream()
+    if not rotating:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                swq.linear(x, w, s, b, bits, gs, out=out, stream=stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                swq.linear(x, w, s, b, bits, gs, out=out, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tflops = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+        return {"config": f"quantized linear M={M} K={K} N={N}, {bits}-bit gs{gs}, bf16 out",
+                "ms_per_call": round(ms, 4), "tflops": round(tflops, 2),
+                "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    sets = [(w, s, b)]
+    for _ in range(ROTATING_SETS - 1):
+        words = torch.randint(-2**31, 2**31 - 1, (N, K * bits // 32), generator=gen, device="cuda",
+                              dtype=torch.int64).to(torch.int32)
+        sc = (torch.rand((N, K // gs), generator=gen, device="cuda") * 0.015 + 0.005).to(torch.bfloat16)
+        bi = (-8.0 * sc.float() * (torch.rand((N, K // gs), generator=gen, device="cuda") * 0.2 + 0.9))
+        sets.append((words, sc, bi.to(torch.bfloat16)))
+    out = torch.empty((CALLS, N), dtype=torch.bfloat16, device="cuda")
+    L = swq.lib()
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+    x0, o0 = x.data_ptr(), out.data_ptr()
+
+    def step(sh):
+        for i in range(CALLS):
+            wp, sp, bp = ptrs[i % ROTATING_SETS]
+            rc = L.swiglu_q_linear(x0 + i * K * 2, wp, sp, bp, 1, K, N, bits, gs, swq.SWQ_LINEAR_BF16,
+                                   o0 + i * N * 2, sh)
+            if rc != 0:
+                raise RuntimeError(f"swiglu_q_linear failed: {swq.swiglu_q_strerror(rc)}")
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+    alg = wb + K * 2 + N * 2
+    return {"config": f"quantized linear M=1 K={K} N={N}, {bits}-bit gs{gs}, bf16 out, fresh x per call, "
+                      f"{ROTATING_SETS} rotating weight sets, hip graph",
+            "avg_launch_us": round(us, 3), "weight_GB_per_s": round(wb / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
+
+
 def bench_copy(args):
     """Plain copy kernel of a known size: 1000 copies of 12,991,488 bytes per
     step, sources rotating over 40 buffers, recorded into one HIP graph."""
@@ -342,6 +427,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
     args = ap.parse_args()
@@ -385,6 +471,11 @@ def main():
             pre[f"c{cfg}_{['match', 'f32'][mode]}"] = bench_prefill_one(cfg, steps=steps, warmup=3, mode=mode)
             torch.cuda.empty_cache()
         line["prefill"] = pre
+    if not args.no_linear:
+        log("linear: timing ...")
+        line["linear"] = {"decode_down_proj": bench_linear(1, 5632, 2048, 4, 64, max(1, args.steps // 4), 2, True),
+                          "prefill_down_proj": bench_linear(2048, 14336, 4096, 4, 64, 10, 3, False)}
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline_decode()

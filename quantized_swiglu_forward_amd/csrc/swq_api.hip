@@ -92,12 +92,12 @@ bool gemv_fits(int64_t M, int64_t H) {
   return M >= 1 && M <= kGemvMaxM;
 }
 
-// The M = 1 kernel reads x itself for H <= 4096, and the few-row kernel
+// The M = 1 kernel reads x itself for H <= 8192, and the few-row kernel
 // builds x' itself for M*H <= kSkinnyStageMax; otherwise the prep kernel
 // stages x' first (in the workspace).  SWIGLU_Q_SKINNY_STAGE=0 always uses
 // the prep kernel.
 bool gemv_needs_rows(int64_t M, int64_t H) {
-  if (M == 1 && H <= 4096) return false;
+  if (M == 1 && H <= 8192) return false;
   const char* s = getenv("SWIGLU_Q_SKINNY_STAGE");
   return M * H > kSkinnyStageMax || (s && s[0] == '0');
 }

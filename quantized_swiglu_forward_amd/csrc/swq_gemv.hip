@@ -10,7 +10,7 @@
 // accumulation; the same epilogue as the matrix-matrix path writes hidden.
 //
 // Two kernels:
-//  * swq_gemv1_kernel: M = 1 with at most two chunks per lane (H <= 4096).
+//  * swq_gemv1_kernel: M = 1 with at most four chunks per lane (H <= 8192).
 //    Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no offset,
 //    each chunk of x scaled by its own power of two; the block shares x
 //    through LDS (described above the kernel).
@@ -224,7 +224,7 @@ struct XChunk {
 };
 
 // Largest H of the M = 1 kernel: 64 lanes x 2 chunks of 32.
-constexpr int kGemv1MaxH = 4096;
+constexpr int kGemv1MaxH = 8192;
 
 // The block converts x once and shares it through LDS.  Thread t converts
 // the 8-value blocks t, t + 256, ...; the four blocks of a 32-value chunk
@@ -634,27 +634,31 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   return hipGetLastError();
 }
 
-static int gemv1_rounds() {
+// Columns per wave: two, or one when that leaves fewer than 2048 waves
+// (fewer columns than 4096), so that a small output still spreads over the
+// chip.  SWIGLU_Q_GEMV_ROUNDS (1, 2 or 4) overrides.
+static int gemv1_rounds(int I) {
   static const int r = [] {
     const char* s = getenv("SWIGLU_Q_GEMV_ROUNDS");
     const int v = s ? atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 2;
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
   }();
-  return r;
+  return r ? r : (I >= 4096 ? 2 : 1);
 }
 
 template <int BG, int BU>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
   const int cpl = (p.H / 32 + lpc - 1) / lpc;
-  if (p.M == 1 && cpl <= 2) {
+  if (p.M == 1 && cpl <= 4) {
     const bool full = lpc == 64 && p.H == 2048 * cpl;
-    if (cpl == 1) {
-      return full ? launch_gemv1_t<BG, BU, 1, true>(p, gemv1_rounds(), stream)
-                  : launch_gemv1_t<BG, BU, 1, false>(p, gemv1_rounds(), stream);
+    const int r = gemv1_rounds(p.I);
+    switch (cpl) {
+      case 1: return full ? launch_gemv1_t<BG, BU, 1, true>(p, r, stream) : launch_gemv1_t<BG, BU, 1, false>(p, r, stream);
+      case 2: return full ? launch_gemv1_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_t<BG, BU, 2, false>(p, r, stream);
+      case 3: return full ? launch_gemv1_t<BG, BU, 3, true>(p, r, stream) : launch_gemv1_t<BG, BU, 3, false>(p, r, stream);
+      default: return full ? launch_gemv1_t<BG, BU, 4, true>(p, r, stream) : launch_gemv1_t<BG, BU, 4, false>(p, r, stream);
     }
-    return full ? launch_gemv1_t<BG, BU, 2, true>(p, gemv1_rounds(), stream)
-                : launch_gemv1_t<BG, BU, 2, false>(p, gemv1_rounds(), stream);
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
   // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns

@@ -76,14 +76,17 @@ def test_shape_sweep(M, H, I, spec, mode, path):
 
 # ------------------------------------------------------- decode (M = 1) --
 
-# every branch of the M = 1 kernel: a whole wave per column with one or two
-# chunks per lane (H = 2048, 4096), two chunks with idle lanes (H = 3072),
-# fewer lanes per column (H = 1024, 512), both bit widths and all group
-# sizes on each side, ragged I
+# every branch of the M = 1 kernel: a whole wave per column with one to four
+# chunks per lane (H = 2048, 4096, 6144, 8192), with idle lanes (H = 3072,
+# 5632, 7168), fewer lanes per column (H = 1024, 512), one and two columns
+# per wave (I below and above 4096), both bit widths and all group sizes on
+# each side, ragged I
 DECODE_CASES = [
     (2048, 5633, (4, 64, 4, 64)), (2048, 301, (8, 32, 4, 64)), (2048, 257, (4, 128, 8, 128)),
     (2048, 130, (8, 64, 8, 32)), (4096, 515, (4, 64, 4, 64)), (4096, 129, (8, 128, 4, 32)),
     (3072, 200, (4, 64, 8, 64)), (1024, 333, (4, 32, 4, 128)), (512, 97, (8, 64, 4, 64)),
+    (6144, 300, (4, 64, 4, 64)), (5632, 257, (8, 32, 4, 64)), (8192, 130, (4, 128, 8, 64)),
+    (7168, 77, (8, 64, 8, 32)), (8192, 4100, (4, 64, 4, 64)),
 ]
 
 
