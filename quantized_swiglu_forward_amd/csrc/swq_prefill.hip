@@ -113,27 +113,38 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
 }
 
-// Extra-column B rows: thread (n, G) writes columns 3G, 3G+1, 3G+2 of row n
-// of one matrix, (c_hi, c_lo, c_hi) for g0-group G with c = b + z*s exactly
-// in float32 (b and z*s are bf16 values times small powers of two and 17),
-// zeros past the last group (the padding up to kext).  Group sizes are
-// powers of two: lg_* are their logarithms.
-__device__ __forceinline__ void prep_ext_group(const uint16_t* S, const uint16_t* B, int lg_gs, int bits, int lg_g0,
-                                               int ngroups, int kext, _Float16* dst, int64_t n, int G) {
-  _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
-  if (G < ngroups) {
-    const int ng = ngroups >> (lg_gs - lg_g0);       // groups of this matrix per row
-    const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
-    const float z = bits == 8 ? 136.0f : 8.0f;
-    const float c = fmaf(z, bf16_to_f32(S[gi]), bf16_to_f32(B[gi]));
-    chi = (_Float16)c;
-    clo = (_Float16)(c - (float)chi);
+// Extra-column B rows, eight g0-groups per thread: thread (n, matrix, c)
+// writes bytes [48c, 48c + 48) of row n of one matrix -- groups 8c .. 8c+7,
+// three binary16 each, (c_hi, c_lo, c_hi) with c = b + z*s exactly in
+// float32 (b and z*s are bf16 values times small powers of two and 17) --
+// zeros past the last group, as three 16-byte stores.  A row is kext*2 bytes,
+// a multiple of 64, so each store lies wholly inside or outside it.  Group
+// sizes are powers of two: lg_* are their logarithms.
+__device__ __forceinline__ void prep_ext_chunk(const uint16_t* S, const uint16_t* B, int lg_gs, int bits, int lg_g0,
+                                               int ngroups, int kext, _Float16* dst, int64_t n, int c) {
+  const int ng = ngroups >> (lg_gs - lg_g0);         // groups of this matrix per row
+  const float z = bits == 8 ? 136.0f : 8.0f;
+  f16x8 h[3];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int G = 8 * c + j;
+    _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
+    if (G < ngroups) {
+      const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
+      const float cv = fmaf(z, bf16_to_f32(S[gi]), bf16_to_f32(B[gi]));
+      chi = (_Float16)cv;
+      clo = (_Float16)(cv - (float)chi);
+    }
+    h[(3 * j) >> 3][(3 * j) & 7] = chi;
+    h[(3 * j + 1) >> 3][(3 * j + 1) & 7] = clo;
+    h[(3 * j + 2) >> 3][(3 * j + 2) & 7] = chi;
   }
-  _Float16* d = dst + n * kext + 3 * G;
-  const int k = 3 * G;
-  if (k < kext) d[0] = chi;
-  if (k + 1 < kext) d[1] = clo;
-  if (k + 2 < kext) d[2] = chi;
+  unsigned char* row = reinterpret_cast<unsigned char*>(dst + n * kext);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int off = 48 * c + 16 * q;
+    if (off < kext * 2) *reinterpret_cast<f16x8*>(row + off) = h[q];
+  }
 }
 
 // Scale tiles: one block per 128 columns and 2 super-steps (256 inputs).
@@ -187,8 +198,8 @@ __device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, 
 }
 
 // Index helpers of the prep grid (host and device agree on them).
-__host__ __device__ inline int prep_ext_lg(int kext) {          // log2 of triplet slots per row
-  const int per_row = (kext + 2) / 3;
+__host__ __device__ inline int prep_ext_lg(int kext) {          // log2 of 8-group chunk slots per row
+  const int per_row = (kext + 23) / 24;
   int lg = 0;
   while ((1 << lg) < per_row) ++lg;
   return lg;
@@ -198,9 +209,9 @@ __host__ __device__ inline int64_t prep_scale_blocks(int I, int nss) {   // bloc
 }
 
 // Blocks [0, M): x rows.  Then the extra-column rows, thread index
-// ((n * 2 + matrix) << lg) + G.  Then the scale tiles, one block per 128
-// columns and 8 super-steps.  Every division is by a power of two or
-// block-uniform.
+// ((n * 2 + matrix) << lg) + c for 8-group chunk c.  Then the scale tiles,
+// one block per 128 columns and kScaleBlockSteps super-steps.  Every
+// division is by a power of two or block-uniform.
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   if ((int)blockIdx.x < p.M) {
     prep_x_row(p, blockIdx.x);
@@ -217,16 +228,16 @@ __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
     return;
   }
   const int64_t idx = b * 256 + threadIdx.x;
-  const int G = (int)(idx & ((1 << lg) - 1));
+  const int c = (int)(idx & ((1 << lg) - 1));
   const int64_t rest = idx >> lg;
   const int64_t n = rest >> 1;
   if (n >= ((rest & 1) ? p.I_u : p.I)) return;       // up rows past I_u: read as zeros by the GEMM
   const int lg_g0 = __builtin_ctz(p.g0);
   const int ngroups = p.H >> lg_g0;
   if ((rest & 1) == 0)
-    prep_ext_group(p.sg, p.bg, __builtin_ctz(p.gs_g), p.bits_g, lg_g0, ngroups, p.kext, p.bext_g, n, G);
+    prep_ext_chunk(p.sg, p.bg, __builtin_ctz(p.gs_g), p.bits_g, lg_g0, ngroups, p.kext, p.bext_g, n, c);
   else
-    prep_ext_group(p.su, p.bu, __builtin_ctz(p.gs_u), p.bits_u, lg_g0, ngroups, p.kext, p.bext_u, n, G);
+    prep_ext_chunk(p.su, p.bu, __builtin_ctz(p.gs_u), p.bits_u, lg_g0, ngroups, p.kext, p.bext_u, n, c);
 }
 
 // ----------------------------------------------------------- MFMA GEMM ----
