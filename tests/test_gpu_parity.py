@@ -335,3 +335,40 @@ def test_m_zero_launches_nothing():
     rc = swq.swiglu_q_forward(dev[0], *dev[1:], 0, 256, 64, 4, 64, 4, 64, 0, out.data_ptr() or 256, None)
     assert rc == swq.SWQ_OK
     assert [swq.swiglu_q_call_count(k) for k in (0, 1)] == before
+
+
+# ---------------------------------------------------------------- HIP graphs --
+
+@pytest.mark.parametrize("M,H,I,spec", [(1, 2048, 600, (4, 64, 4, 64)), (6, 256, 300, (8, 32, 4, 64)),
+                                        (12, 2048, 200, (4, 64, 4, 64)), (300, 512, 384, (4, 64, 8, 32))],
+                         ids=["decode", "few-row-in-kernel", "few-row-prep", "mfma"])
+def test_graph_replays_match_eager(M, H, I, spec):
+    """The forward recorded into a HIP graph (after an eager call, so the
+    workspace exists) and replayed several times, with other eager work and
+    synchronisations between the replays, writes the eager result every
+    time: the kernels and the workspace they share need no per-call clearing."""
+    p = make_custom(M, H, I, *spec, seed=M + I)
+    dev = swq.to_device(p)
+    say("graph", M, H, I, spec)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):                   # the workspace belongs to (device, stream)
+        eager = swq.forward(*dev, p.bits_g, p.gs_g, p.bits_u, p.gs_u, mode=0, stream=stream)
+    torch.cuda.synchronize()
+    ref = eager.clone()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        swq.forward(*dev, p.bits_g, p.gs_g, p.bits_u, p.gs_u, mode=0, out=out,
+                    stream=torch.cuda.current_stream())
+    other = make_custom(M, H, I, *spec, seed=M + I + 1)
+    odev = swq.to_device(other)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        # another eager call on the same stream (and workspace) between replays
+        with torch.cuda.stream(stream):
+            swq.forward(*odev, other.bits_g, other.gs_g, other.bits_u, other.gs_u, mode=1, stream=stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+    check(out.float().cpu().numpy().astype(np.float64), oracle_full(p, 0), 0, "graph replay")
