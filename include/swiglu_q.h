@@ -66,7 +66,7 @@ extern "C" {
 #define SWQ_ERR_SHAPE        2  /* M < 0, H <= 0, I <= 0, H % gs != 0, H % 32 != 0,
                                    H > 2^20, M or I > 2^30, or a staged copy of x
                                    (2 bytes x M x about 1.05 H) of 4 GiB or more   */
-#define SWQ_ERR_UNSUPPORTED  3  /* bits not in {4, 8}, gs not in {32, 64, 128},
+#define SWQ_ERR_UNSUPPORTED  3  /* bits not in {2, 4, 8}, gs not in {32, 64, 128},
                                    unknown precision mode or path                   */
 #define SWQ_ERR_ALIGN        4  /* a pointer is not 16-byte aligned                 */
 #define SWQ_ERR_HIP          5  /* a HIP call or kernel launch failed               */
@@ -89,7 +89,7 @@ extern "C" {
  *   Wg, sg, bg   gate codes [I, H·bits_g/32], scales and biases [I, H/gs_g]
  *   Wu, su, bu   up codes [I, H·bits_u/32], scales and biases [I, H/gs_u]
  *   M, H, I      rows of x, hidden size, intermediate size
- *   bits_*, gs_* quantization spec of each matrix: bits in {4, 8},
+ *   bits_*, gs_* quantization spec of each matrix: bits in {2, 4, 8},
  *                gs in {32, 64, 128}, H a multiple of gs and of 32
  *   precision_mode  SWQ_MATCH, SWQ_F32 or SWQ_F32_BF16OUT
  *   out          [M, I] device pointer, bf16 or float32 by mode
@@ -118,7 +118,7 @@ int swiglu_q_forward(const void *x,
  *   W, s, b   codes [N, K·bits/32], scales and biases [N, K/gs] (same packing
  *             and dequantization w = s·q + b as the forward)
  *   M, K, N   rows of x, input size, output size
- *   bits, gs  bits in {4, 8}, gs in {32, 64, 128}, K a multiple of gs and 32
+ *   bits, gs  bits in {2, 4, 8}, gs in {32, 64, 128}, K a multiple of gs and 32
  *   out_mode  SWQ_LINEAR_BF16 or SWQ_LINEAR_F32
  *   out       [M, N] device pointer, bf16 or float32 by out_mode
  *   stream    hipStream_t (NULL = null stream)

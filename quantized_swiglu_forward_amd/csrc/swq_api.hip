@@ -65,7 +65,7 @@ bool logging() {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool spec_ok(int bits, int gs) {
-  return (bits == 4 || bits == 8) && (gs == 32 || gs == 64 || gs == 128);
+  return (bits == 2 || bits == 4 || bits == 8) && (gs == 32 || gs == 64 || gs == 128);
 }
 
 // Validation shared by every entry point; nothing touches HIP here.

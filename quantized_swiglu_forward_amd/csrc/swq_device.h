@@ -119,9 +119,27 @@ __device__ __forceinline__ void codes8(uint32_t wa, uint32_t wb, uint32_t lo[4],
   }
 }
 
+// 2-bit codes run through the 4-bit arithmetic: the eight 2-bit fields of
+// a 16-bit block (code j in bits [2j, 2j+2)) spread to eight nibbles of a
+// word (code j in bits [4j, 4j+4)), the 4-bit layout.  A code q <= 3 is a
+// 4-bit code too, and s*(q - 8) stays exact in binary16.
+__device__ __forceinline__ uint32_t spread2(uint32_t b16) {
+  uint32_t v = b16 & 0xFFFFu;
+  v = (v | (v << 8)) & 0x00FF00FFu;
+  v = (v | (v << 4)) & 0x0F0F0F0Fu;
+  v = (v | (v << 2)) & 0x33333333u;
+  return v;
+}
+
+// Width at which a code is computed: 2-bit codes as 4-bit ones.
+template <int BITS>
+inline constexpr int kCodeWidth = BITS == 2 ? 4 : BITS;
+
 // Offset z of the rewrite w = s*(q - z) + (b + z*s).
 template <int BITS>
 struct CodeOffset;
+template <>
+struct CodeOffset<2> { static constexpr float z = 8.0f; };
 template <>
 struct CodeOffset<4> { static constexpr float z = 8.0f; };
 template <>

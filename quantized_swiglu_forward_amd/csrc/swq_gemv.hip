@@ -18,6 +18,8 @@
 //    once per call; codes become exact binary16 s (q - z) and 16 x 16 x 32
 //    MFMAs multiply them with up to 16 rows at once (described above the
 //    kernel).
+#include <type_traits>
+
 #include "swq_device.h"
 #include "swq_kernels.h"
 
@@ -26,7 +28,7 @@ namespace swq {
 // Raw weight data of one (column, chunk) item for one matrix.
 template <int BITS>
 struct RawChunk {
-  u32x4 w[BITS / 4];   // 32 codes: 16 bytes (4-bit) or 32 bytes (8-bit)
+  u32x4 w[kCodeWidth<BITS> / 4];   // 32 codes: 16 bytes (4-bit, or 2-bit spread to nibbles) or 32 bytes (8-bit)
   uint32_t sb;         // bf16 scale (low half) and bias (high half) of the chunk's group
 };
 
@@ -54,8 +56,13 @@ __device__ __forceinline__ MatBufs mat_bufs(const uint32_t* W, const uint16_t* S
 template <int BITS>
 __device__ __forceinline__ void load_chunk_buf(RawChunk<BITS>& r, const MatBufs& m, int rel, int kc) {
   const int wo = (rel * m.rw + kc * BITS) * 4;
+  if constexpr (BITS == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(m.w, wo, 0, 2);
+    r.w[0] = (u32x4){spread2(v[0]), spread2(v[0] >> 16), spread2(v[1]), spread2(v[1] >> 16)};
+  } else {
 #pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(m.w, wo + 16 * i, 0, 2);
+    for (int i = 0; i < BITS / 4; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(m.w, wo + 16 * i, 0, 2);
+  }
   const int go = (rel * m.ng + ((kc * 32) >> m.lg_gs)) * 2;
   r.sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m.s, go, 0, 0) |
          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m.b, go, 0, 0) << 16);
@@ -117,7 +124,7 @@ __device__ __forceinline__ int row_exponent(uint32_t amax_bits) {
 template <int BITS>
 __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const uint32_t xa[8], const uint32_t xb[8]) {
   float p = 0.0f;
-  if (BITS == 4) {
+  if (kCodeWidth<BITS> == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = r.w[0][j];
@@ -424,14 +431,14 @@ constexpr int kSkinnyMaxWaves = 16;
 
 template <int BITS_G, int BITS_U>
 struct SkinnyChunk {
-  u32x4 cg[BITS_G / 4], cu[BITS_U / 4], x[4];
+  u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[4];
   float sg, bg, su, bu;
   bool live;
 };
 
 template <int BITS_G, int BITS_U, bool STAGE>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void swq_skinny_kernel(GemvParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,10 +468,18 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
     d.live = c < nchunk;
     const int cc = d.live ? c : 0;                     // an in-range chunk for the loads
     const int og = (r * mg.rw + cc * BITS_G) * 4, ou = (r * mu.rw + cc * BITS_U) * 4;
+    auto codes = [](const __amdgpu_buffer_rsrc_t& rs, int off, u32x4* dst, auto bits_tag) {
+      constexpr int BITS = decltype(bits_tag)::value;
+      if constexpr (BITS == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 2);
+        dst[0] = (u32x4){spread2(v[0]), spread2(v[0] >> 16), spread2(v[1]), spread2(v[1] >> 16)};
+      } else {
 #pragma unroll
-    for (int i = 0; i < BITS_G / 4; ++i) d.cg[i] = __builtin_amdgcn_raw_buffer_load_b128(mg.w, og + 16 * i, 0, 2);
-#pragma unroll
-    for (int i = 0; i < BITS_U / 4; ++i) d.cu[i] = __builtin_amdgcn_raw_buffer_load_b128(mu.w, ou + 16 * i, 0, 2);
+        for (int i = 0; i < BITS / 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 2);
+      }
+    };
+    codes(mg.w, og, d.cg, std::integral_constant<int, BITS_G>{});
+    codes(mu.w, ou, d.cu, std::integral_constant<int, BITS_U>{});
     // a chunk past the end gets zero scales and biases: its B operands vanish
     const int gg = (r * mg.ng + ((32 * cc) >> mg.lg_gs)) * 2, gu = (r * mu.ng + ((32 * cc) >> mu.lg_gs)) * 2;
     const float keep = d.live ? 1.0f : 0.0f;
@@ -488,7 +503,7 @@ __attribute__((amdgpu_waves_per_eu(BITS_G == 4 && BITS_U == 4 ? 8 : 4))) void sw
   auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, int kb, const f16x8& a, f32x4& acc) {
     const _Float16 hs = (_Float16)sf;
     const f16x2 s2 = {hs, hs};
-    if constexpr (BITS == 4) {
+    if constexpr (kCodeWidth<BITS> == 4) {
       uint32_t o[4];
       dequant4(cw[0][kb], s2, o, nk);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]}), acc,
@@ -673,11 +688,18 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BG>
+static hipError_t launch_gemv_g(const GemvParams& p, int bits_u, hipStream_t stream) {
+  if (bits_u == 2) return launch_gemv_bits<BG, 2>(p, stream);
+  if (bits_u == 4) return launch_gemv_bits<BG, 4>(p, stream);
+  if (bits_u == 8) return launch_gemv_bits<BG, 8>(p, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream) {
-  if (bits_g == 4 && bits_u == 4) return launch_gemv_bits<4, 4>(p, stream);
-  if (bits_g == 8 && bits_u == 4) return launch_gemv_bits<8, 4>(p, stream);
-  if (bits_g == 4 && bits_u == 8) return launch_gemv_bits<4, 8>(p, stream);
-  if (bits_g == 8 && bits_u == 8) return launch_gemv_bits<8, 8>(p, stream);
+  if (bits_g == 2) return launch_gemv_g<2>(p, bits_u, stream);
+  if (bits_g == 4) return launch_gemv_g<4>(p, bits_u, stream);
+  if (bits_g == 8) return launch_gemv_g<8>(p, bits_u, stream);
   return hipErrorInvalidValue;
 }
 

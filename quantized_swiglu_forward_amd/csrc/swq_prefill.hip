@@ -311,7 +311,7 @@ __device__ __forceinline__ void block_barrier() {
 // Dequantized B operands of one k16 sub-step (one 8-code block per lane) of one matrix.
 template <int BITS>
 __device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1, const NibbleK& k) {
-  if (BITS == 4) {
+  if (kCodeWidth<BITS> == 4) {
     uint32_t o[4];
     dequant4(w[0], s2, o, k);
     b0 = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
@@ -489,7 +489,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // this lane's codes and scales of two consecutive code K-steps: step t
   // uses set P and loads step t+1 into set P^1 (in the unrolled main loop P
   // alternates; elsewhere P = 0 and set 1 is copied back after the step)
-  uint32_t cw_g[2][NF][BITS_G / 2], cw_u[2][NF][BITS_U / 2];
+  constexpr int WG = kCodeWidth<BITS_G>, WU = kCodeWidth<BITS_U>;   // 2-bit codes held as nibbles
+  uint32_t cw_g[2][NF][WG / 2], cw_u[2][NF][WU / 2];
   f16x2 s_g2[2][NF], s_u2[2][NF];
 
   const uint32_t sw = (uint32_t)((l32 >> 2) & 3);
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     for (int i = 0; i < MF; ++i) a[i] = *reinterpret_cast<const f16x8*>(st + i * 32 * 64);
   };
   // this lane's codes and scales of code K-step t, from the code ring
-  auto load_codes = [&](int t, uint32_t (&cg)[NF][BITS_G / 2], uint32_t (&cu)[NF][BITS_U / 2], f16x2 (&s_g)[NF],
+  auto load_codes = [&](int t, uint32_t (&cg)[NF][WG / 2], uint32_t (&cu)[NF][WU / 2], f16x2 (&s_g)[NF],
                         f16x2 (&s_u)[NF]) {
     const unsigned char* ring = ssmem + ((t / SS) & 1) * SS_SLOT;
     const int q = t % SS;                              // K-step within the super-step
@@ -515,21 +516,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       s_g[f] = as_h2(sc[(2 * q) * BN + n]);
       s_u[f] = as_h2(sc[(2 * q + 1) * BN + n]);
       // 4-bit: chunk q holds the K-step, this lane's two 8-code blocks at half * 8;
-      // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half
-      const unsigned char* qg = BITS_G == 4
-          ? ring + n * (CPR_G * 16) + ((q ^ swz(n, CPR_G)) * 16) + half * 8
-          : ring + n * (CPR_G * 16) + (((2 * q + half) ^ swz(n, CPR_G)) * 16);
-      const unsigned char* qu = BITS_U == 4
-          ? ring + SSG_BYTES + n * (CPR_U * 16) + ((q ^ swz(n, CPR_U)) * 16) + half * 8
-          : ring + SSG_BYTES + n * (CPR_U * 16) + (((2 * q + half) ^ swz(n, CPR_U)) * 16);
-      if constexpr (BITS_G == 4) {
+      // 8-bit: chunks 2q, 2q+1 hold it, this lane's blocks are chunk 2q + half;
+      // 2-bit: chunk q/2 holds it at 8 (q % 2), this lane's blocks at half * 4
+      auto code_at = [&](int bits, int cpr, int base) {
+        return bits == 4 ? ring + base + n * (cpr * 16) + ((q ^ swz(n, cpr)) * 16) + half * 8
+             : bits == 8 ? ring + base + n * (cpr * 16) + (((2 * q + half) ^ swz(n, cpr)) * 16)
+                         : ring + base + n * (cpr * 16) + (((q >> 1) ^ swz(n, cpr)) * 16) + 8 * (q & 1) + half * 4;
+      };
+      const unsigned char* qg = code_at(BITS_G, CPR_G, 0);
+      const unsigned char* qu = code_at(BITS_U, CPR_U, SSG_BYTES);
+      if constexpr (BITS_G == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(qg);
+        cg[f][0] = spread2(v); cg[f][1] = spread2(v >> 16);
+      } else if constexpr (BITS_G == 4) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(qg);
         cg[f][0] = v[0]; cg[f][1] = v[1];
       } else {
         const u32x4 v = *reinterpret_cast<const u32x4*>(qg);
         cg[f][0] = v[0]; cg[f][1] = v[1]; cg[f][2] = v[2]; cg[f][3] = v[3];
       }
-      if constexpr (BITS_U == 4) {
+      if constexpr (BITS_U == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(qu);
+        cu[f][0] = spread2(v); cu[f][1] = spread2(v >> 16);
+      } else if constexpr (BITS_U == 4) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(qu);
         cu[f][0] = v[0]; cu[f][1] = v[1];
       } else {
@@ -539,13 +548,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
   };
   // B operands of sub-step ks from codes and scales in registers
-  auto dequant = [&](int ks, const uint32_t (&cg)[NF][BITS_G / 2], const uint32_t (&cu)[NF][BITS_U / 2],
+  auto dequant = [&](int ks, const uint32_t (&cg)[NF][WG / 2], const uint32_t (&cu)[NF][WU / 2],
                      const f16x2 (&s_g)[NF], const f16x2 (&s_u)[NF], f16x8 (&ga)[NF], f16x8 (&gb)[NF],
                      f16x8 (&ua)[NF], f16x8 (&ub)[NF]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      dequant_block<BITS_G>(&cg[f][ks * (BITS_G / 4)], s_g[f], ga[f], gb[f], nk);
-      dequant_block<BITS_U>(&cu[f][ks * (BITS_U / 4)], s_u[f], ua[f], ub[f], nk);
+      dequant_block<BITS_G>(&cg[f][ks * (WG / 4)], s_g[f], ga[f], gb[f], nk);
+      dequant_block<BITS_U>(&cu[f][ks * (WU / 4)], s_u[f], ua[f], ub[f], nk);
     }
   };
   // B operands of sub-step ks of an extra-column step from stage `slot` (one
@@ -590,7 +599,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // reads and the dequantization that prepare the next sub-step, so that the
   // matrix pipe stays fed while the vector ALU works (the reads go with the
   // first MFMAs, their results are needed by the dequantization).
-  constexpr int MF_MAIN = MF * NF * ((BITS_G / 4) + (BITS_U / 4));   // MFMAs of a code sub-step
+  constexpr int MF_MAIN = MF * NF * ((kCodeWidth<BITS_G> / 4) + (kCodeWidth<BITS_U> / 4));   // MFMAs of a code sub-step
   constexpr int DQ_VALU = NF * (BITS_G == 8 ? 40 : 20) + NF * (BITS_U == 8 ? 40 : 20);
   auto interleave = [&]<int NMFMA, int NDS, int NVALU>() {
     constexpr int LEAD = NMFMA < 8 ? NMFMA / 2 : 4;
@@ -657,9 +666,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
 #pragma unroll
-        for (int j = 0; j < BITS_G / 2; ++j) cw_g[0][f][j] = cw_g[1][f][j];
+        for (int j = 0; j < WG / 2; ++j) cw_g[0][f][j] = cw_g[1][f][j];
 #pragma unroll
-        for (int j = 0; j < BITS_U / 2; ++j) cw_u[0][f][j] = cw_u[1][f][j];
+        for (int j = 0; j < WU / 2; ++j) cw_u[0][f][j] = cw_u[1][f][j];
         s_g2[0][f] = s_g2[1][f];
         s_u2[0][f] = s_u2[1][f];
       }
@@ -820,11 +829,18 @@ static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hi
   return hipErrorInvalidValue;
 }
 
+template <int BG>
+static hipError_t launch_mfma_g(const MfmaParams& p, int cfg, int n_split, int bits_u, hipStream_t stream) {
+  if (bits_u == 2) return launch_mfma_bits<BG, 2>(p, cfg, n_split, stream);
+  if (bits_u == 4) return launch_mfma_bits<BG, 4>(p, cfg, n_split, stream);
+  if (bits_u == 8) return launch_mfma_bits<BG, 8>(p, cfg, n_split, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream) {
-  if (bits_g == 4 && bits_u == 4) return launch_mfma_bits<4, 4>(p, cfg, n_split, stream);
-  if (bits_g == 8 && bits_u == 4) return launch_mfma_bits<8, 4>(p, cfg, n_split, stream);
-  if (bits_g == 4 && bits_u == 8) return launch_mfma_bits<4, 8>(p, cfg, n_split, stream);
-  if (bits_g == 8 && bits_u == 8) return launch_mfma_bits<8, 8>(p, cfg, n_split, stream);
+  if (bits_g == 2) return launch_mfma_g<2>(p, cfg, n_split, bits_u, stream);
+  if (bits_g == 4) return launch_mfma_g<4>(p, cfg, n_split, bits_u, stream);
+  if (bits_g == 8) return launch_mfma_g<8>(p, cfg, n_split, bits_u, stream);
   return hipErrorInvalidValue;
 }
 

@@ -50,7 +50,8 @@ def _fwd(**kw):
     (dict(bu=None), swq.SWQ_ERR_NULL),
     (dict(out=None), swq.SWQ_ERR_NULL),
     (dict(bits_g=3), swq.SWQ_ERR_UNSUPPORTED),
-    (dict(bits_u=2), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(bits_u=6), swq.SWQ_ERR_UNSUPPORTED),
+    (dict(bits_g=16), swq.SWQ_ERR_UNSUPPORTED),
     (dict(gs_g=16), swq.SWQ_ERR_UNSUPPORTED),
     (dict(gs_u=96), swq.SWQ_ERR_UNSUPPORTED),
     (dict(precision_mode=3), swq.SWQ_ERR_UNSUPPORTED),
@@ -123,7 +124,9 @@ def test_supported_predicate():
     assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 0) == 1
     assert swq.swiglu_q_supported(2560, 8, 32, 4, 64, 1) == 1
     assert swq.swiglu_q_supported(4096, 4, 128, 8, 128, 2) == 1
-    assert swq.swiglu_q_supported(2048, 2, 64, 4, 64, 0) == 0
+    assert swq.swiglu_q_supported(2048, 2, 64, 4, 64, 0) == 1
+    assert swq.swiglu_q_supported(2048, 3, 64, 4, 64, 0) == 0
+    assert swq.swiglu_q_supported(2048, 4, 64, 6, 64, 0) == 0
     assert swq.swiglu_q_supported(2048, 4, 48, 4, 64, 0) == 0
     assert swq.swiglu_q_supported(96, 4, 64, 4, 32, 0) == 0
     assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 7) == 0

@@ -56,7 +56,8 @@ def check_linear(y, p, out_mode, what, ms=None, ns=None):
 CASES = [(300, 256, 200, 4, 64, MFMA), (129, 512, 77, 8, 32, MFMA), (64, 1024, 1, 4, 128, MFMA),
          (257, 256, 2, 4, 64, MFMA), (512, 1024, 1000, 4, 64, MFMA), (33, 384, 129, 8, 64, MFMA),
          (1, 2048, 300, 4, 64, GEMV), (1, 5632, 257, 4, 64, GEMV), (3, 1024, 77, 8, 32, GEMV),
-         (16, 2048, 130, 4, 64, GEMV), (1, 256, 1, 4, 32, GEMV), (7, 512, 2, 8, 128, GEMV)]
+         (16, 2048, 130, 4, 64, GEMV), (1, 256, 1, 4, 32, GEMV), (7, 512, 2, 8, 128, GEMV),
+         (129, 512, 77, 2, 64, MFMA), (1, 2048, 133, 2, 32, GEMV), (9, 1024, 65, 2, 128, GEMV)]
 
 
 @pytest.mark.parametrize("M,K,N,bits,gs,path", CASES,

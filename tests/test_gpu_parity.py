@@ -48,7 +48,7 @@ def test_config0_default_dispatch():
 # ------------------------------------------------------------ shape sweep --
 
 SPECS = [(4, 64, 4, 64), (4, 32, 4, 32), (4, 128, 4, 128), (8, 32, 4, 64), (8, 64, 8, 64),
-         (4, 64, 8, 128), (8, 128, 8, 32)]
+         (4, 64, 8, 128), (8, 128, 8, 32), (2, 32, 4, 64), (2, 64, 2, 64), (8, 64, 2, 128)]
 SHAPES = [(1, 256, 129), (2, 512, 200), (3, 256, 97), (4, 1024, 130), (5, 256, 64), (6, 384, 77),
           (7, 512, 129), (8, 256, 255), (16, 512, 100), (31, 256, 129), (32, 256, 96), (33, 512, 257),
           (63, 256, 65), (64, 128, 64), (65, 512, 300), (127, 256, 129), (128, 256, 128),
@@ -79,7 +79,7 @@ def test_shape_sweep(M, H, I, spec, mode, path):
 # every branch of the M = 1 kernel: a whole wave per column with one to four
 # chunks per lane (H = 2048, 4096, 6144, 8192), with idle lanes (H = 3072,
 # 5632, 7168), fewer lanes per column (H = 1024, 512), one and two columns
-# per wave (I below and above 4096), both bit widths and all group sizes on
+# per wave (I below and above 4096), all three code widths (2, 4, 8) and all group sizes on
 # each side, ragged I
 DECODE_CASES = [
     (2048, 5633, (4, 64, 4, 64)), (2048, 301, (8, 32, 4, 64)), (2048, 257, (4, 128, 8, 128)),
@@ -87,6 +87,7 @@ DECODE_CASES = [
     (3072, 200, (4, 64, 8, 64)), (1024, 333, (4, 32, 4, 128)), (512, 97, (8, 64, 4, 64)),
     (6144, 300, (4, 64, 4, 64)), (5632, 257, (8, 32, 4, 64)), (8192, 130, (4, 128, 8, 64)),
     (7168, 77, (8, 64, 8, 32)), (8192, 4100, (4, 64, 4, 64)),
+    (2048, 300, (2, 64, 2, 64)), (4096, 129, (2, 32, 8, 64)), (5632, 90, (4, 128, 2, 32)),
 ]
 
 
@@ -187,11 +188,12 @@ def test_gemv_and_mfma_agree(M):
 
 # the few-row kernel with x' built inside the kernel (M*H <= 8192: one
 # launch) and staged by the prep kernel (larger), on both sides of the
-# boundary, both bit widths, and M = 1 past the M = 1 kernel's H limit
+# boundary, all three code widths, and M = 1 past the M = 1 kernel's H limit
 FEW_ROW = [(2, 4096, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (4, 2048, 257, (8, 64, 4, 128)),
            (5, 2048, 96, (4, 32, 4, 64)), (9, 2048, 300, (4, 64, 4, 64)), (16, 2048, 129, (8, 32, 8, 64)),
            (12, 4096, 64, (4, 128, 4, 64)), (16, 512, 100, (4, 64, 8, 64)), (1, 8192, 200, (4, 64, 4, 64)),
-           (1, 16384, 33, (8, 64, 4, 32)), (1, 32768, 40, (4, 64, 4, 64))]
+           (1, 16384, 33, (8, 64, 4, 32)), (1, 32768, 40, (4, 64, 4, 64)), (5, 1024, 77, (2, 64, 4, 64)),
+           (12, 2048, 96, (2, 128, 2, 32)), (3, 2048, 50, (8, 32, 2, 64))]
 
 
 @pytest.mark.parametrize("M,H,I,spec", FEW_ROW, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in FEW_ROW])
