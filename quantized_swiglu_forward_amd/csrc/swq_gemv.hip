@@ -14,10 +14,12 @@
 //    Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no offset,
 //    each chunk of x scaled by its own power of two; the block shares x
 //    through LDS (described above the kernel).
-//  * swq_skinny_kernel: 1 <= M <= 16 otherwise.  The prep kernel stages x'
-//    once per call; codes become exact binary16 s (q - z) and 16 x 16 x 32
-//    MFMAs multiply them with up to 16 rows at once (described above the
-//    kernel).
+//  * swq_skinny_kernel: 1 <= M <= 16 otherwise.  x' comes from the prep
+//    kernel, or for M*H <= 8192 every block builds it in LDS itself; codes
+//    become exact binary16 s (q - z) and 16 x 16 x 32 MFMAs multiply them
+//    with up to 16 rows at once (described above the kernel).
+// 2-bit codes are spread to nibbles as they are loaded and take the 4-bit
+// arithmetic.
 #include <type_traits>
 
 #include "swq_device.h"
@@ -410,22 +412,22 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // --------------------------------------------------------- 2 <= M <= 16 --
 //
 // Matrix-vector products for a few rows.  The rows of x, staged once per call
-// by the prep kernel as x' = x 2^-e (binary16, per-row power of two, in the
-// code-pair order of the dequantized weights, 32 inputs per chunk), are the A
-// operand of v_mfma_f32_16x16x32_f16 (16 rows, M of them live); the
-// dequantized weights s (q - z) of 16 output columns are the B operand, so one
-// unpack serves every row.  A block of up to 16 waves owns 16 columns of both
-// matrices: wave w takes the chunk quads w, w + W, ... (W waves), and lane
-// group h = lane / 16 takes chunk 4 quad + h: the MFMA's K slots of group h
-// are that chunk's 8-code block, on the A side x' of the same inputs.  With
-// 4-bit codes at most 64 registers per lane let two such blocks share a CU,
-// so a whole decode-sized grid is resident at once.  A fifth MFMA per chunk adds the bias term
-// sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c each split
-// into binary16 hi + lo, as on the matrix-matrix path.  The waves' partial
-// sums meet in LDS; wave 0 applies 2^e and the epilogue.  STAGE (M H at most
-// kSkinnyStageMax): every block builds x' itself in LDS (the same row
-// powers of two, conversion and layout as the prep kernel's x rows), so the
-// call is one launch.
+// as x' = x 2^-e (binary16, per-row power of two, in the code-pair order of
+// the dequantized weights, 32 inputs per chunk), are the A operand of
+// v_mfma_f32_16x16x32_f16 (16 rows, M of them live); the dequantized weights
+// s (q - z) of 16 output columns are the B operand, so one unpack serves
+// every row.  A block of up to 16 waves owns 16 columns of both matrices:
+// wave w takes the chunk quads w, w + W, ... (W waves), and lane group
+// h = lane / 16 takes chunk 4 quad + h: the MFMA's K slots of group h are
+// that chunk's 8-code block, on the A side x' of the same inputs.  With 4-bit
+// codes at most 64 registers per lane let two such blocks share a CU, so a
+// whole decode-sized grid is resident at once.  A fifth MFMA per chunk adds
+// the bias term sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c
+// each split into binary16 hi + lo, as on the matrix-matrix path.  The waves'
+// partial sums meet in LDS; wave 0 applies 2^e and the epilogue.  x' comes
+// from the prep kernel, or (STAGE, M*H at most kSkinnyStageMax) every block
+// builds it itself in LDS with the prep kernel's row powers of two,
+// conversion and layout, so the call is one launch.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSkinnyMaxWaves = 16;
 

@@ -6,7 +6,8 @@
 // where x is read once for two GEMMs and down_proj stays separate).
 //
 // Exactness.  A weight w = s*q + b is split as  s*(q - z) + c  with
-// c = b + z*s per group (z = 8 for 4-bit codes; for 8-bit codes
+// c = b + z*s per group (z = 8 for 4-bit codes, and for 2-bit codes, which
+// are spread to nibbles and computed as 4-bit ones; for 8-bit codes
 // q = 16 hi + lo and s*q = 16s*(hi - 8) + s*(lo - 8) + 136 s).  Every
 // s*(code - 8) is exact in binary16 (a bf16 scale has 8 significant bits, the
 // offset code at most 4), so the K loop runs on f16 MFMA with exact products
@@ -23,12 +24,14 @@
 //     the dequantized weight pairs, and appends the extra columns
 //     (hi, hi, lo) of every group of g0 = min(gs_g, gs_u) inputs.  Every bf16
 //     x whose magnitude is at least 2^-17 of the row maximum converts
-//     exactly.  The remaining blocks write, for every output feature and
-//     matrix, the extra-column B rows (c_hi, c_lo, c_hi).
+//     exactly.  The next blocks write, for every output feature and matrix,
+//     the extra-column B rows (c_hi, c_lo, c_hi); the last ones the scale
+//     tiles (binary16 scale pairs per K-step, 128 columns at a time).
 //  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators over the
 //     H columns (packed codes, dequantized in registers) and then the extra
 //     columns (precomputed binary16 rows); epilogue 2^e, then silu(g) * u per
-//     precision mode.
+//     precision mode, or the two projections as they are for the quantized
+//     linear (W's rows split between the gate and up slots).
 #include <type_traits>
 #include <utility>
 
