@@ -60,11 +60,18 @@ GEMV_SOURCES = ["swq_gemv.hip", "swq_device.h", "swq_kernels.h"]
 
 
 def gemv_source_digest():
+    """First 16 hex digits of the SHA-256 of the decode kernel's sources with
+    comments and blank space removed (so an edit of comments alone keeps the
+    measured traffic valid)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMV_SOURCES:
-        with open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -153,6 +153,30 @@ def test_linear_metric_catches_planted_errors():
     assert not compare.evaluate_linear(bad, r, nu, 1)["ok"]
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_random_specs_and_magnitudes_against_exact(case):
+    """Seeded random tiny problems -- any gate/up code widths and group
+    sizes, output sizes 1-4, x scaled from 2^-10 to 2^10, scales anywhere in
+    the documented exact range [2^-17, 2^8) -- against exact rationals: the
+    oracle's float64 gate and up within 1e-14 of each dot product's scale."""
+    rng = np.random.default_rng(1000 + case)
+    bits_g, bits_u = (int(b) for b in rng.choice([2, 4, 8], 2))
+    gs_g, gs_u = (int(g) for g in rng.choice([32, 64, 128], 2))
+    H = int(max(gs_g, gs_u) * rng.integers(1, 3))
+    M, I = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    s_lo = float(2.0 ** rng.uniform(-17, 6))
+    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=case, x_sigma=float(2.0 ** rng.uniform(-10, 10)),
+                    s_lo=s_lo, s_hi=s_lo * 4, bias_mode="factor")
+    o = oracle.swiglu_full(p, mode=1, nthreads=1)
+    xg = [list(r) for r in p.x]
+    ex_g = exact.qmm_exact(xg, p.wg, p.sg, p.bg, M, H, I, bits_g, gs_g)
+    ex_u = exact.qmm_exact(xg, p.wu, p.su, p.bu, M, H, I, bits_u, gs_u)
+    for m in range(M):
+        for n in range(I):
+            assert _rel_to_scale(o["g"][m, n], float(ex_g[m][n]), o["nu_g"][m, n]) <= 1e-14
+            assert _rel_to_scale(o["u"][m, n], float(ex_u[m][n]), o["nu_u"][m, n]) <= 1e-14
+
+
 def test_mixed_specs_against_exact():
     M, H, I = 2, 128, 3
     p = make_custom(M, H, I, 8, 32, 4, 64, seed=5, bias_mode="half")
