@@ -74,6 +74,27 @@ def test_shape_sweep(M, H, I, spec, mode, path):
     check(y, oracle_full(p, mode), mode, f"sweep M{M} H{H} I{I} {spec} mode{mode} path{path}")
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_specs_and_magnitudes(case):
+    """Seeded random problems on both paths: any gate/up code widths and
+    group sizes, ragged I, x scaled from 2^-10 to 2^10 and scales anywhere in
+    the documented exact range [2^-17, 2^8), every precision mode."""
+    rng = np.random.default_rng(500 + case)
+    bits_g, bits_u = (int(b) for b in rng.choice([2, 4, 8], 2))
+    gs_g, gs_u = (int(g) for g in rng.choice([32, 64, 128], 2))
+    M = int(rng.choice([1, 3, 9, 40, 200]))
+    H = int(rng.choice([256, 512, 1024]))
+    I = int(rng.integers(33, 300))
+    s_lo = float(2.0 ** rng.uniform(-17, 6))
+    mode = case % 3
+    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=700 + case,
+                    x_sigma=float(2.0 ** rng.uniform(-10, 10)), s_lo=s_lo, s_hi=s_lo * 4)
+    path = GEMV if M <= 16 and case % 2 == 0 else MFMA
+    say("random", M, H, I, (bits_g, gs_g, bits_u, gs_u), "s_lo", s_lo, "mode", mode, "path", path)
+    y = device_forward(p, mode, path)
+    check(y, oracle_full(p, mode), mode, f"random case {case}")
+
+
 # ------------------------------------------------------- decode (M = 1) --
 
 # every branch of the M = 1 kernel: a whole wave per column with one to four
