@@ -120,6 +120,23 @@ def test_linear_validation():
     assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
 
 
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A plain C99 program includes include/swiglu_q.h, links the library and
+    gets the documented status codes from the host-side validation."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "c_abi_check")
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    libdir = os.path.dirname(swq.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                    "-L", libdir, "-lswiglu_q", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "c abi ok" in r.stdout
+
+
 def test_supported_predicate():
     assert swq.swiglu_q_supported(2048, 4, 64, 4, 64, 0) == 1
     assert swq.swiglu_q_supported(2560, 8, 32, 4, 64, 1) == 1
