@@ -281,6 +281,63 @@ def bench_prefill_one(cfg, steps, warmup, mode=0):
             "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
 
 
+def bench_decode_rows(M, steps, warmup):
+    """The decode shape (H=2048, I=5632, 4-bit gs64) at a few rows per call:
+    1000 calls per step on fresh x rows over the 40 rotating weight sets,
+    recorded into a HIP graph; per-call time and weight bytes per second."""
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import CONFIGS, make_problem
+
+    c = CONFIGS[1]
+    dev = swq.to_device(make_problem(1))
+    sets = rotating_weight_sets(c, dev, ROTATING_SETS, seed=101)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(M)
+    x = torch.randn((CALLS * M, c.H), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((CALLS * M, c.I), dtype=torch.bfloat16, device="cuda")
+    L = swq.lib()
+    ptrs = [tuple(t.data_ptr() for t in s) for s in sets]
+    x0, o0 = x.data_ptr(), out.data_ptr()
+    before = swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV)
+
+    def step(sh):
+        for i in range(CALLS):
+            wg, sg, bg, wu, su, bu = ptrs[i % ROTATING_SETS]
+            rc = L.swiglu_q_forward(x0 + i * M * c.H * 2, wg, sg, bg, wu, su, bu, M, c.H, c.I, c.bits_g, c.gs_g,
+                                    c.bits_u, c.gs_u, 0, o0 + i * M * c.I * 2, sh)
+            if rc != 0:
+                raise RuntimeError(f"swiglu_q_forward failed: {swq.swiglu_q_strerror(rc)}")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV) - before == CALLS, "not the matrix-vector path"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+    wb = weight_bytes(c)
+    alg = wb + M * (c.H + c.I) * 2
+    return {"config": f"decode shape M={M} H={c.H} I={c.I}, 4-bit gs64 gate and up, fresh x per call, "
+                      f"{ROTATING_SETS} rotating weight sets, hip graph",
+            "avg_launch_us": round(us, 3), "weight_GB_per_s": round(wb / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
+
+
 def bench_linear(M, K, N, bits, gs, steps, warmup, rotating):
     """The quantized linear at one shape, bf16 output.  ``rotating``: 1000
     calls per step on fresh x rows over 40 weight sets (drawn on the GPU from
@@ -470,6 +527,10 @@ def main():
                                 "precision_mode": "MATCH"},
                      "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None}})
+    if args.workload == "decode":
+        log("decode, a few rows per call: timing ...")
+        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4)}
+        torch.cuda.empty_cache()
     if not args.no_prefill:
         pre = {}
         for cfg, mode in ((0, 0), (2, 0), (2, 1), (3, 0), (4, 0)):

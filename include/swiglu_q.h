@@ -34,8 +34,9 @@
  * is a DEVICE pointer owned by the caller; the library never frees or keeps
  * them.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  * and the call returns without synchronising.  A matrix-vector call with
- * M*H > 8192 (other than M = 1 with H <= 8192) needs a device workspace for
- * the staged x, and every matrix-matrix call needs one for x and the
+ * M*H > 8192 (other than M = 1 with H <= 8192, and 2 <= M <= 4 with
+ * 2048 <= H <= 4096) needs a device workspace for the staged x, and every
+ * matrix-matrix call needs one for x and the
  * weights' extra rows and scale tiles: the library keeps one per (device, stream),
  * allocated on first use and grown (never shrunk) when a call needs more;
  * growth synchronises that stream once.  swiglu_q_release_workspace() frees

@@ -98,6 +98,7 @@ bool gemv_fits(int64_t M, int64_t H) {
 // the prep kernel.
 bool gemv_needs_rows(int64_t M, int64_t H) {
   if (M == 1 && H <= 8192) return false;
+  if (gemv1_rows_shape(M, H)) return false;
   const char* s = getenv("SWIGLU_Q_SKINNY_STAGE");
   return M * H > kSkinnyStageMax || (s && s[0] == '0');
 }

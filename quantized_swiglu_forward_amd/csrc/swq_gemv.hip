@@ -306,12 +306,16 @@ __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChun
 // a whole wave per column, the R columns' sums end wave-uniform and lane r
 // runs the epilogue of column r, so one pass serves all R columns.  FULL:
 // H = 2048 CPL exactly (64 lanes per column, every lane CPL chunks).
-template <int BITS_G, int BITS_U, int CPL, int R, bool FULL, int WPB>
+// MR > 1 serves MR = M rows (R <= 2): every row's x is staged and dotted
+// with the same weight chunks, which are loaded once; the reduction and
+// epilogue run per row.
+template <int BITS_G, int BITS_U, int CPL, int R, bool FULL, int WPB, int MR>
 __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int lg) {
+  static_assert(MR >= 1 && MR <= 4 && (MR == 1 || R <= 2), "several rows: at most two columns per wave");
   constexpr int NT = 64 * WPB;
-  constexpr int XI = (256 * CPL + NT - 1) / NT;   // 8-value blocks of x per thread
-  __shared__ u32x4 xs[kGemv1MaxH / 8];
-  __shared__ float2 xinfo[kGemv1MaxH / 32];
+  constexpr int XI = (256 * CPL + NT - 1) / NT;   // 8-value blocks of one row of x per thread
+  __shared__ u32x4 xs[MR][256 * CPL];
+  __shared__ float2 xinfo[MR][64 * CPL];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if constexpr (FULL) lg = 6;
@@ -323,12 +327,14 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 
   // 1. this thread's 8-value blocks of x (loads complete in issue order: x
   //    first, so it is not held up behind the weight stream)
-  u32x4 xraw[XI];
+  u32x4 xraw[MR][XI];
 #pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    const int blk = tid + NT * i;
-    xraw[i] = *reinterpret_cast<const u32x4*>(p.x + 8 * min(blk, nblk - 1));
-  }
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int blk = tid + NT * i;
+      xraw[m][i] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.H + 8 * min(blk, nblk - 1));
+    }
 
   // 2. all weight loads of this lane: R columns x CPL chunks x 2 matrices
   const int64_t n0 = (int64_t)wave_global * R * cpw;           // the wave's first column
@@ -354,58 +360,90 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 
   // 3. x' into LDS, shared by the block's four waves
 #pragma unroll
-  for (int i = 0; i < XI; ++i) stage_x_block(xraw[i], tid + NT * i, tid + NT * i < nblk, xs, xinfo);
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < XI; ++i) stage_x_block(xraw[m][i], tid + NT * i, tid + NT * i < nblk, xs[m], xinfo[m]);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  XChunk xc[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) read_x_chunk(xs, xinfo, min(sl + c * lpc, nchunk - 1), xc[c]);
 
   // 4. per column: chunk terms, reduction over the column group, epilogue
-  float ag[R], au[R];
+  // (row m of the output)
+  auto finish = [&](const float (&ag)[R], const float (&au)[R], int m) __attribute__((always_inline)) {
+    if (R <= 2 && (FULL || lpc == 64)) {
+      // Sums of the 2R values of the wave with two lane-swap folds and one row
+      // sum: row 0 ends with column 0's gate, row 2 with its up, rows 1 and 3
+      // with column 1's (R = 2); lane 16 r then runs column r's epilogue.
+      const float t0 = fold32(ag[0], au[0]);
+      const float t = R == 2 ? fold16(t0, fold32(ag[R - 1], au[R - 1])) : fold16(t0, t0);
+      const float g = row_sum(t);
+      const float u = upper_half(g);
+      const int col = lane >> 4;
+      const int64_t n = (int64_t)wave_global * R + col;
+      if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, m, (int)n, g, u);
+    } else if (FULL || lpc == 64) {
+      float g = 0.0f, u = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    ag[r] = 0.0f;
-    au[r] = 0.0f;
+      for (int r = 0; r < R; ++r) {
+        const float gr = wave_sum(ag[r]), ur = wave_sum(au[r]);
+        if (lane == r) {
+          g = gr;
+          u = ur;
+        }
+      }
+      const int n = wave_global * R + lane;
+      if (lane < R && n < p.I) store_out(p, m, n, g, u);
+    } else if constexpr (!FULL) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if (FULL || sl + c * lpc < nchunk) {
-        ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
-        au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
+      for (int r = 0; r < R; ++r) {
+        const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
+        const int n = (wave_global * R + r) * cpw + sub;
+        if (sl == 0 && n < p.I) store_out(p, m, n, g, u);
       }
     }
-  }
-  if (R <= 2 && (FULL || lpc == 64)) {
-    // Sums of the 2R values of the wave with two lane-swap folds and one row
-    // sum: row 0 ends with column 0's gate, row 2 with its up, rows 1 and 3
-    // with column 1's (R = 2); lane 16 r then runs column r's epilogue.
-    const float t0 = fold32(ag[0], au[0]);
-    const float t = R == 2 ? fold16(t0, fold32(ag[R - 1], au[R - 1])) : fold16(t0, t0);
-    const float g = row_sum(t);
-    const float u = upper_half(g);
-    const int col = lane >> 4;
-    const int64_t n = (int64_t)wave_global * R + col;
-    if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, 0, (int)n, g, u);
-  } else if (FULL || lpc == 64) {
-    float g = 0.0f, u = 0.0f;
+  };
+  if constexpr (MR > 1) {
+    // each row's x chunk is read from LDS once and serves the R columns
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float ag[R], au[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        ag[r] = 0.0f;
+        au[r] = 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (FULL || sl + c * lpc < nchunk) {
+          XChunk xc;   // per row and chunk: all of them at once would not fit in registers
+          read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc), xc.e + 20);
+            au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc), xc.e + 20);
+          }
+        }
+      }
+      finish(ag, au, m);
+    }
+  } else {
+    XChunk xc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) read_x_chunk(xs[0], xinfo[0], min(sl + c * lpc, nchunk - 1), xc[c]);
+    float ag[R], au[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float gr = wave_sum(ag[r]), ur = wave_sum(au[r]);
-      if (lane == r) {
-        g = gr;
-        u = ur;
+      ag[r] = 0.0f;
+      au[r] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (FULL || sl + c * lpc < nchunk) {
+          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
+          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
+        }
       }
     }
-    const int n = wave_global * R + lane;
-    if (lane < R && n < p.I) store_out(p, 0, n, g, u);
-  } else if constexpr (!FULL) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
-      const int n = (wave_global * R + r) * cpw + sub;
-      if (sl == 0 && n < p.I) store_out(p, 0, n, g, u);
-    }
+    finish(ag, au, 0);
   }
 }
 
@@ -633,6 +671,7 @@ static int gemv_lanes_per_column(int H) {
 
 template <int BG, int BU, int CPL, bool FULL>
 static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream) {
+  constexpr int WPB = 4;
   const int lpc = gemv_lanes_per_column(p.H);
   int lg = 0;
   while ((1 << lg) < lpc) ++lg;
@@ -640,12 +679,37 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   const int cols_per_wave = cpw * R;
   const int waves = (p.I + cols_per_wave - 1) / cols_per_wave;
   if (p.H > kGemv1MaxH || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
-  constexpr int WPB = 4;
   const int blocks = (waves + WPB - 1) / WPB;
   switch (R) {
-    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
-    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
-    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The several-row form (gemv1_rows_shape): a whole wave per column, R (one
+// or two) columns per wave.
+template <int BG, int BU, int CPL, bool FULL>
+static hipError_t launch_gemv1_rows_t(const GemvParams& p, int R, hipStream_t stream) {
+  constexpr int WPB = 4;
+  const int lpc = gemv_lanes_per_column(p.H);
+  int lg = 0;
+  while ((1 << lg) < lpc) ++lg;
+  const int cols_per_wave = 64 / lpc * R;
+  const int waves = (p.I + cols_per_wave - 1) / cols_per_wave;
+  if (!gemv1_rows_shape(p.M, p.H) || lpc != 64 || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
+  static_assert(kGemv1MaxRows == 4, "one instance per row count");
+  const int blocks = (waves + WPB - 1) / WPB;
+  const dim3 g(blocks), b(64 * WPB);
+  switch (R * 8 + p.M) {
+    case 8 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 2>), g, b, 0, stream, p, lg); break;
+    case 8 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 3>), g, b, 0, stream, p, lg); break;
+    case 8 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 4>), g, b, 0, stream, p, lg); break;
+    case 16 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 2>), g, b, 0, stream, p, lg); break;
+    case 16 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 3>), g, b, 0, stream, p, lg); break;
+    case 16 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 4>), g, b, 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -663,6 +727,16 @@ static int gemv1_rounds(int I) {
   return r ? r : (I >= 4096 ? 2 : 1);
 }
 
+// SWIGLU_Q_GEMV1_ROWS=0 sends 2 <= M <= kGemv1MaxRows to the few-row MFMA
+// kernel instead (for comparisons).
+bool gemv1_rows_enabled() {
+  static const bool on = [] {
+    const char* s = getenv("SWIGLU_Q_GEMV1_ROWS");
+    return !(s && s[0] == '0');
+  }();
+  return on;
+}
+
 template <int BG, int BU>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
@@ -676,6 +750,13 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
       case 3: return full ? launch_gemv1_t<BG, BU, 3, true>(p, r, stream) : launch_gemv1_t<BG, BU, 3, false>(p, r, stream);
       default: return full ? launch_gemv1_t<BG, BU, 4, true>(p, r, stream) : launch_gemv1_t<BG, BU, 4, false>(p, r, stream);
     }
+  }
+  if (gemv1_rows_shape(p.M, p.H)) {
+    static_assert(kGemv1RowsMaxH <= 2 * 2048, "at most two chunks per lane");
+    const bool full = lpc == 64 && p.H == 2048 * cpl;
+    const int r = gemv1_rounds(p.I) >= 2 ? 2 : 1;
+    if (cpl == 1) return full ? launch_gemv1_rows_t<BG, BU, 1, true>(p, r, stream) : hipErrorInvalidValue;   // H = 2048
+    return full ? launch_gemv1_rows_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false>(p, r, stream);
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
   // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns

@@ -95,6 +95,16 @@ constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 constexpr int kGemvMaxM = 16;
 // M*H up to this: the few-row kernel builds x' itself (one launch, no workspace).
 constexpr int kSkinnyStageMax = 8192;
+// the matrix-vector kernel's several-row form (no staging pass): 2 <= M <=
+// kGemv1MaxRows with a whole wave per column (H >= 2048) and at most two
+// chunks per lane (H <= 4096); below H = 2048 the few-row kernel is faster
+constexpr int kGemv1MaxRows = 4;
+constexpr int kGemv1RowsMinH = 2048;
+constexpr int kGemv1RowsMaxH = 4096;
+bool gemv1_rows_enabled();
+inline bool gemv1_rows_shape(int64_t M, int64_t H) {
+  return M >= 2 && M <= kGemv1MaxRows && H >= kGemv1RowsMinH && H <= kGemv1RowsMaxH && gemv1_rows_enabled();
+}
 
 inline int kext_columns(int64_t H, int g0) {
   const int64_t c = 3 * (H / g0);

@@ -57,7 +57,8 @@ CASES = [(300, 256, 200, 4, 64, MFMA), (129, 512, 77, 8, 32, MFMA), (64, 1024, 1
          (257, 256, 2, 4, 64, MFMA), (512, 1024, 1000, 4, 64, MFMA), (33, 384, 129, 8, 64, MFMA),
          (1, 2048, 300, 4, 64, GEMV), (1, 5632, 257, 4, 64, GEMV), (3, 1024, 77, 8, 32, GEMV),
          (16, 2048, 130, 4, 64, GEMV), (1, 256, 1, 4, 32, GEMV), (7, 512, 2, 8, 128, GEMV),
-         (129, 512, 77, 2, 64, MFMA), (1, 2048, 133, 2, 32, GEMV), (9, 1024, 65, 2, 128, GEMV)]
+         (129, 512, 77, 2, 64, MFMA), (1, 2048, 133, 2, 32, GEMV), (9, 1024, 65, 2, 128, GEMV),
+         (4, 2048, 131, 4, 64, GEMV), (2, 4096, 1, 2, 32, GEMV), (3, 3072, 2, 8, 64, GEMV)]
 
 
 @pytest.mark.parametrize("M,K,N,bits,gs,path", CASES,
@@ -71,7 +72,7 @@ def test_linear_against_oracle(M, K, N, bits, gs, path, out_mode):
 
 
 @pytest.mark.parametrize("M,K,N,path", [(200, 512, 301, MFMA), (1, 2048, 133, GEMV), (5, 1024, 64, GEMV),
-                                        (1, 8192, 40, GEMV)])
+                                        (1, 8192, 40, GEMV), (3, 2048, 65, GEMV)])
 def test_linear_equals_forward_gate_bitwise(M, K, N, path):
     """W's rows in the up slot take the same arithmetic as in the gate slot, so
     the linear's float32 output equals the forward's pre-epilogue gate with W

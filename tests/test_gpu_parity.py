@@ -121,6 +121,52 @@ def test_decode_branches(H, I, spec, mode):
     check(y, oracle_full(p, mode), mode, f"decode H{H} I{I} {spec} mode{mode}")
 
 
+# ------------------------------------------- decode, a few rows (M <= 4) --
+
+# the several-row form of the matrix-vector kernel (2 <= M <= 4,
+# 2048 <= H <= 4096): one and two chunks per lane (H = 2048, 4096), idle lanes
+# (H = 2560, 3072, 3584), one and two columns per wave (I below and above
+# 4096), every code width on each side, ragged I, every precision mode
+ROWS_CASES = [
+    (2, 2048, 5633, (4, 64, 4, 64)), (3, 2048, 301, (8, 32, 4, 64)), (4, 2048, 130, (2, 64, 8, 32)),
+    (2, 4096, 515, (4, 64, 4, 64)), (4, 4096, 129, (8, 128, 2, 32)), (3, 3072, 200, (4, 64, 8, 64)),
+    (4, 2560, 333, (4, 32, 4, 128)), (2, 3584, 97, (8, 64, 4, 64)), (4, 2048, 4100, (2, 32, 2, 64)),
+    (3, 4096, 4097, (4, 64, 4, 64)), (2, 3072, 4200, (8, 32, 4, 64)),
+]
+
+
+@pytest.mark.parametrize("M,H,I,spec", ROWS_CASES,
+                         ids=[f"M{m}-H{h}-I{i}-{s[0]}b{s[1]}-{s[2]}b{s[3]}" for m, h, i, s in ROWS_CASES])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_decode_rows(M, H, I, spec, mode):
+    p = make_custom(M, H, I, *spec, seed=M * 1000 + H + I)
+    say("decode rows", M, H, I, spec, "mode", mode)
+    y = device_forward(p, mode, GEMV)
+    check(y, oracle_full(p, mode), mode, f"decode rows M{M} H{H} I{I} {spec} mode{mode}")
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("M,H,I", [(4, 2048, 300), (3, 3072, 300), (2, 4096, 300), (4, 2048, 4100), (3, 3584, 4500)])
+def test_decode_rows_match_single_row_calls(M, H, I):
+    """Each row of a several-row call takes the single-row call's arithmetic
+    in the same order (the same columns per wave, chunks per lane and
+    reduction), so the results agree bit for bit."""
+    p = make_custom(M, H, I, 4, 64, 8, 32, seed=H + I)
+    dev = swq.to_device(p)
+    say("rows vs single-row calls", M, H, I)
+    with forced_path(GEMV, M):
+        for mode in (0, 1):
+            whole = swq.forward(*dev, p.bits_g, p.gs_g, p.bits_u, p.gs_u, mode=mode)
+            for m in range(M):
+                one = swq.forward(dev[0][m:m + 1].contiguous(), *dev[1:], p.bits_g, p.gs_g, p.bits_u, p.gs_u,
+                                  mode=mode)
+                torch.cuda.synchronize()
+                assert torch.equal(_bits(whole[m:m + 1]), _bits(one)), (M, H, I, mode, m)
+
+
 # ------------------------------------------------------- full-size configs --
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -209,12 +255,13 @@ def test_gemv_and_mfma_agree(M):
 
 # the few-row kernel with x' built inside the kernel (M*H <= 8192: one
 # launch) and staged by the prep kernel (larger), on both sides of the
-# boundary, all three code widths, and M = 1 past the M = 1 kernel's H limit
-FEW_ROW = [(2, 4096, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (4, 2048, 257, (8, 64, 4, 128)),
+# boundary, all three code widths, and M <= 4 and M = 1 past the
+# matrix-vector kernel's H limits
+FEW_ROW = [(6, 1024, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (8, 1024, 257, (8, 64, 4, 128)),
            (5, 2048, 96, (4, 32, 4, 64)), (9, 2048, 300, (4, 64, 4, 64)), (16, 2048, 129, (8, 32, 8, 64)),
            (12, 4096, 64, (4, 128, 4, 64)), (16, 512, 100, (4, 64, 8, 64)), (1, 8192, 200, (4, 64, 4, 64)),
            (1, 16384, 33, (8, 64, 4, 32)), (1, 32768, 40, (4, 64, 4, 64)), (5, 1024, 77, (2, 64, 4, 64)),
-           (12, 2048, 96, (2, 128, 2, 32)), (3, 2048, 50, (8, 32, 2, 64))]
+           (12, 2048, 96, (2, 128, 2, 32)), (3, 6144, 50, (8, 32, 2, 64)), (4, 5120, 70, (4, 64, 4, 64))]
 
 
 @pytest.mark.parametrize("M,H,I,spec", FEW_ROW, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in FEW_ROW])
@@ -362,9 +409,10 @@ def test_m_zero_launches_nothing():
 
 # ---------------------------------------------------------------- HIP graphs --
 
-@pytest.mark.parametrize("M,H,I,spec", [(1, 2048, 600, (4, 64, 4, 64)), (6, 256, 300, (8, 32, 4, 64)),
-                                        (12, 2048, 200, (4, 64, 4, 64)), (300, 512, 384, (4, 64, 8, 32))],
-                         ids=["decode", "few-row-in-kernel", "few-row-prep", "mfma"])
+@pytest.mark.parametrize("M,H,I,spec", [(1, 2048, 600, (4, 64, 4, 64)), (3, 2048, 600, (4, 64, 4, 64)),
+                                        (6, 256, 300, (8, 32, 4, 64)), (12, 2048, 200, (4, 64, 4, 64)),
+                                        (300, 512, 384, (4, 64, 8, 32))],
+                         ids=["decode", "decode-rows", "few-row-in-kernel", "few-row-prep", "mfma"])
 def test_graph_replays_match_eager(M, H, I, spec):
     """The forward recorded into a HIP graph (after an eager call, so the
     workspace exists) and replayed several times, with other eager work and
