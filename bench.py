@@ -477,7 +477,7 @@ def cpu_baseline_decode(max_seconds=20.0):
         oracle.swiglu_pairs(p, 0, nthreads=cores, want=("h",))
         calls += 1
         el = time.perf_counter() - t0
-        if el >= max_seconds or calls >= 200:
+        if el >= max_seconds or calls >= len(p.xs):
             break
     gbs = weight_bytes(c) * calls / el / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
@@ -492,6 +492,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-linear", action="store_true")
+    ap.add_argument("--no-small-batch", action="store_true", help="skip the decode shape at 2 and 4 rows")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
     args = ap.parse_args()
@@ -527,7 +528,7 @@ def main():
                                 "precision_mode": "MATCH"},
                      "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None}})
-    if args.workload == "decode":
+    if args.workload == "decode" and not args.no_small_batch:
         log("decode, a few rows per call: timing ...")
         line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4)}
         torch.cuda.empty_cache()
