@@ -338,6 +338,107 @@ def bench_decode_rows(M, steps, warmup):
             "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
 
 
+def bench_mlp_decode(steps, warmup):
+    """The whole MLP at the decode model's shape (M=1, H=2048, I=5632, Ho=2048,
+    4-bit gs64 gate, up and down, bf16 residual): 1000 calls per step on fresh
+    x rows, 40 rotating sets of all three matrices, recorded into a HIP graph."""
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import CONFIGS, make_problem
+
+    c = CONFIGS[1]
+    dev = swq.to_device(make_problem(1))
+    sets = rotating_weight_sets(c, dev, ROTATING_SETS, seed=101)
+    Ho, I, H = c.H, c.I, c.H
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    dsets = []
+    for _ in range(ROTATING_SETS):
+        words = torch.randint(-2**31, 2**31 - 1, (Ho, I * 4 // 32), generator=gen, device="cuda",
+                              dtype=torch.int64).to(torch.int32)
+        sc = (torch.rand((Ho, I // 64), generator=gen, device="cuda") * 0.015 + 0.005).to(torch.bfloat16)
+        bi = (-8.0 * sc.float() * (torch.rand((Ho, I // 64), generator=gen, device="cuda") * 0.2 + 0.9))
+        dsets.append((words, sc, bi.to(torch.bfloat16)))
+    x = torch.randn((CALLS, H), generator=gen, device="cuda").to(torch.bfloat16)
+    res = torch.randn((CALLS, Ho), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((CALLS, Ho), dtype=torch.bfloat16, device="cuda")
+    L = swq.lib()
+    ptrs = [tuple(t.data_ptr() for t in s) + tuple(t.data_ptr() for t in d) for s, d in zip(sets, dsets)]
+
+    def step(sh):
+        for i in range(CALLS):
+            wg, sg, bg, wu, su, bu, wd, sd, bd = ptrs[i % ROTATING_SETS]
+            rc = L.swiglu_q_mlp(x.data_ptr() + i * H * 2, wg, sg, bg, wu, su, bu, wd, sd, bd,
+                                res.data_ptr() + i * Ho * 2, 1, H, I, Ho, 4, 64, 4, 64, 4, 64,
+                                swq.SWQ_LINEAR_BF16, out.data_ptr() + i * Ho * 2, sh)
+            if rc != 0:
+                raise RuntimeError(f"swiglu_q_mlp failed: {swq.swiglu_q_strerror(rc)}")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+    wb = weight_bytes(c) + Ho * I * 4 // 8 + 2 * 2 * Ho * (I // 64)
+    return {"config": f"whole MLP M=1 H={H} I={I} Ho={Ho}, 4-bit gs64 gate, up and down, bf16 residual, "
+                      f"fresh x per call, {ROTATING_SETS} rotating weight sets, hip graph (two launches per call)",
+            "avg_call_us": round(us, 3), "weight_GB_per_s": round(wb / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(wb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "weight_bytes": wb}
+
+
+def bench_mlp_prefill(steps, warmup):
+    """The whole MLP of the M=2048 prefill model (H=4096, I=14336, Ho=4096,
+    4-bit gs64 everywhere, bf16 residual), one problem, ``steps`` calls."""
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+    from synth import make_custom, make_down, make_residual
+
+    M, H, I, Ho = 2048, 4096, 14336, 4096
+    p = make_custom(M, H, I, 4, 64, seed=3, x_sigma=0.5, s_lo=0.002, s_hi=0.01)
+    wd, sd, bd = make_down(Ho, I, 4, 64, seed=4)
+    dev = swq.to_device(p)
+
+    def t16(a):
+        return torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)
+
+    down = (torch.from_numpy(wd.view("int32")).cuda(), t16(sd), t16(bd))
+    res = t16(make_residual(M, Ho, seed=5))
+    out = torch.empty((M, Ho), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            swq.mlp(*dev, *down, (4, 64), (4, 64), (4, 64), residual=res, out=out, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            swq.mlp(*dev, *down, (4, 64), (4, 64), (4, 64), residual=res, out=out, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4.0 * M * H * I + 2.0 * M * I * Ho
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"config": f"whole MLP M={M} H={H} I={I} Ho={Ho}, 4-bit gs64 gate, up and down, bf16 residual",
+            "ms_per_call": round(ms, 4), "tflops": round(tflops, 2),
+            "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
 def bench_linear(M, K, N, bits, gs, steps, warmup, rotating):
     """The quantized linear at one shape, bf16 output.  ``rotating``: 1000
     calls per step on fresh x rows over 40 weight sets (drawn on the GPU from
@@ -493,6 +594,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-linear", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the decode shape at 2 and 4 rows")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the whole-MLP measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
     args = ap.parse_args()
@@ -544,6 +646,11 @@ def main():
         log("linear: timing ...")
         line["linear"] = {"decode_down_proj": bench_linear(1, 5632, 2048, 4, 64, max(1, args.steps // 4), 2, True),
                           "prefill_down_proj": bench_linear(2048, 14336, 4096, 4, 64, 10, 3, False)}
+        torch.cuda.empty_cache()
+    if not args.no_mlp:
+        log("whole MLP: timing ...")
+        line["mlp"] = {"decode": bench_mlp_decode(max(1, args.steps // 4), 2),
+                       "prefill": bench_mlp_prefill(10, 3)}
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample ...")

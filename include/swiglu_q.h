@@ -133,6 +133,39 @@ int swiglu_q_linear(const void *x, const uint32_t *W, const void *s, const void 
                     int64_t M, int64_t K, int64_t N, int bits, int gs,
                     int out_mode, void *out, void *stream);
 
+/*
+ * Whole MLP: out = residual + (silu(x·Wgᵀ) ⊙ (x·Wuᵀ))·Wdᵀ.  The pages' fused
+ * MLP ("mlx-bun 0.0.7 -> 0.0.9" diff, page 42, fused-mlp-kernel.ts, header
+ * comment and the fusedMlp host function) computes the SwiGLU hidden tensor
+ * of an (M, I) tile once, multiplies it into the down projection and returns
+ * the result in the activation type; the model's MLP ("mlx-bun 0.0.8 ->
+ * 0.0.10" diff, page 41, minicpm5.ts, LlamaMLP.forward) passes the layer
+ * input as a residual that the call adds to the MLP output.
+ *   x, Wg..bu, M, H, I, bits_g..gs_u   as swiglu_q_forward
+ *   Wd, sd, bd  down codes [Ho, I·bits_d/32], scales and biases [Ho, I/gs_d];
+ *               I a multiple of gs_d and of 32
+ *   residual    bf16 [M, Ho] device pointer, or NULL for none
+ *   Ho          output size (the model's hidden size)
+ *   out_mode    SWQ_LINEAR_BF16 or SWQ_LINEAR_F32
+ *   out         [M, Ho] device pointer, bf16 or float32 by out_mode
+ * Two launches on `stream`: the fused forward in SWQ_MATCH writes the hidden
+ * tensor (bf16 [M, I]) into a buffer the library keeps per (device, stream)
+ * beside its workspace (grown on demand, freed by swiglu_q_release_workspace),
+ * then the quantized linear of Wd reads it and adds the residual in float32
+ * before its one rounding.  Deterministic: no atomics.  Status codes and
+ * alignment rules as swiglu_q_forward and swiglu_q_linear; residual aligned
+ * to 2 bytes.  Calls that overlap on one stream's buffers are ordered by the
+ * stream.
+ */
+int swiglu_q_mlp(const void *x,
+                 const uint32_t *Wg, const void *sg, const void *bg,
+                 const uint32_t *Wu, const void *su, const void *bu,
+                 const uint32_t *Wd, const void *sd, const void *bd,
+                 const void *residual,
+                 int64_t M, int64_t H, int64_t I, int64_t Ho,
+                 int bits_g, int gs_g, int bits_u, int gs_u, int bits_d, int gs_d,
+                 int out_mode, void *out, void *stream);
+
 /* 1 if the combination is supported by swiglu_q_forward, else 0 (mirrors the
  * pages' support predicate, restricted to what this library implements). */
 int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,

@@ -10,6 +10,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 * ``qmm`` -- one plain quantized projection (the unfused building block), and
   ``qmm_pairs`` -- the same sums element by element with their scales (the
   reference of the quantized linear ``y = x W^T``).
+* ``mlp_pairs`` -- the whole MLP: the MATCH forward's hidden tensor in bf16,
+  its down projection and the residual.
 * ``exact`` -- an exact rational brute force for tiny shapes.
 * ``compare`` -- the per-element error metric used by the parity tests.
 """
@@ -141,6 +143,35 @@ def qmm_pairs(x_bits, W, S, B, M, H, N, bits, gs, ms=None, ns=None, nthreads=0):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return y, nu
+
+
+def mlp_pairs(prob, Wd, Sd, Bd, bits_d, gs_d, Ho, residual=None, ms=None, ns=None, nthreads=0):
+    """The whole MLP ``y = residual + hidden Wd^T`` at the elements (ms[p],
+    ns[p]) of ``[M, Ho]`` (every element, row-major, when None), as the pages'
+    fused MLP defines it ("mlx-bun 0.0.7 -> 0.0.9" diff, page 42,
+    fused-mlp-kernel.ts: SwiGLU of the tile, then its down projection; the
+    residual of minicpm5.ts's LlamaMLP.forward, page 41, added to the result).
+    ``hidden`` is the forward in MATCH rounded to bf16 (the activation type),
+    computed for every row that is asked for; the down projection is the
+    float64 sum over the exactly dequantized ``Wd`` [Ho, I].  Returns
+    (y, nu, rows, hidden_bits): nu = sqrt(sum_i (hidden_i wd_i)^2), rows the
+    distinct rows evaluated and hidden_bits their bf16 hidden rows."""
+    M, I = prob.M, prob.I
+    if ms is None:
+        ms = np.repeat(np.arange(M, dtype=np.int64), Ho)
+        ns = np.tile(np.arange(Ho, dtype=np.int64), M)
+    ms = np.asarray(ms, dtype=np.int64)
+    ns = np.asarray(ns, dtype=np.int64)
+    rows = np.unique(ms)
+    hm = np.repeat(rows, I)
+    hn = np.tile(np.arange(I, dtype=np.int64), rows.size)
+    h = swiglu_pairs(prob, MATCH, hm, hn, nthreads=nthreads, want=("h",))["h"]
+    hidden_bits = bf16_rne(h).reshape(rows.size, I)
+    local = np.searchsorted(rows, ms)
+    y, nu = qmm_pairs(hidden_bits, Wd, Sd, Bd, rows.size, I, Ho, bits_d, gs_d, local, ns, nthreads=nthreads)
+    if residual is not None:
+        y = y + bf16_value(np.asarray(residual, dtype=np.uint16)[ms, ns])
+    return y, nu, rows, hidden_bits
 
 
 def unpack(W, rows, H, bits):

@@ -145,3 +145,43 @@ def evaluate_linear(y, r, nu, out_mode, eta=ETA):
              "max_abs_over_rms": float(np.max(diff) / rms) if (n and rms > 0) else 0.0}
     stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= LINEAR_TOL[out_mode]))
     return stats
+
+
+# The whole MLP's hidden tensor is the forward's bf16 output, which may differ
+# from the oracle's rounding by an admissible bf16 neighbour (a gate or up sum
+# near a rounding midpoint, the final rounding of silu * up) at a small
+# fraction of elements.  Each such element moves the down projection by at
+# most 2^-6 |hidden_i wd_i|; with random signs the sum moves by well under
+# 2^-7 nu, which is the allowance added to the output's own bar.
+HIDDEN_SLACK = 2.0 ** -7
+
+
+def evaluate_mlp(y, r, nu, out_mode, eta=ETA):
+    """Compare a device whole-MLP output with the oracle's float64 result ``r``
+    and the down projection's scale ``nu``: pass iff every element satisfies
+    ``|y - ref| <= tol * max(|ref|, 2^-4 nu, tau_0) + 2^-7 nu`` (tol the
+    linear's bar by output type; for bf16 output both roundings of a value
+    within ``eta * nu`` of a midpoint are admissible).  ``max_ratio`` is the
+    largest ``|y - ref|`` over its allowance (pass iff <= 1)."""
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    r0 = np.asarray(r, dtype=np.float64).reshape(-1)
+    nu = np.asarray(nu, dtype=np.float64).reshape(-1)
+    if out_mode == 0:
+        a, b = bf16_candidates(r0, nu, eta)
+        ref = np.where(np.abs(y - a) <= np.abs(y - b), a, b)
+    else:
+        ref = r0
+    rms = float(np.sqrt(np.mean(r0 * r0))) if r0.size else 0.0
+    allow = LINEAR_TOL[out_mode] * np.maximum(np.maximum(np.abs(ref), FLOOR * nu), TAU0 * rms) + HIDDEN_SLACK * nu
+    diff = np.abs(y - ref)
+    finite = np.isfinite(y)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(allow > 0, diff / np.where(allow > 0, allow, 1.0), np.where(diff == 0, 0.0, np.inf))
+    ratio = np.where(finite, ratio, np.inf)
+    n = y.size
+    worst = int(np.argmax(ratio)) if n else -1
+    stats = {"n": n, "max_ratio": float(ratio[worst]) if n else 0.0, "worst_index": worst,
+             "nonfinite": int(np.sum(~finite)), "tol": LINEAR_TOL[out_mode], "slack": HIDDEN_SLACK,
+             "max_abs_over_nu": float(np.max(diff / np.maximum(nu, 1e-300))) if n else 0.0}
+    stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_ratio"] <= 1.0))
+    return stats

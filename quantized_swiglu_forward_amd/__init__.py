@@ -46,6 +46,8 @@ def lib():
     L.swiglu_q_forward.restype = i32
     L.swiglu_q_linear.argtypes = [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp, vp]
     L.swiglu_q_linear.restype = i32
+    L.swiglu_q_mlp.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    L.swiglu_q_mlp.restype = i32
     L.swiglu_q_debug_gemm.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp]
     L.swiglu_q_debug_gemm.restype = i32
     L.swiglu_q_supported.argtypes = [i64, i32, i32, i32, i32, i32]
@@ -99,6 +101,13 @@ def swiglu_q_forward(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, g
 def swiglu_q_linear(x, W, s, b, M, K, N, bits, gs, out_mode, out, stream=None) -> int:
     return lib().swiglu_q_linear(_ptr(x), _ptr(W), _ptr(s), _ptr(b), M, K, N, bits, gs, out_mode, _ptr(out),
                                  _stream(stream))
+
+
+def swiglu_q_mlp(x, Wg, sg, bg, Wu, su, bu, Wd, sd, bd, residual, M, H, I, Ho, bits_g, gs_g, bits_u, gs_u,
+                 bits_d, gs_d, out_mode, out, stream=None) -> int:
+    return lib().swiglu_q_mlp(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu), _ptr(Wd),
+                              _ptr(sd), _ptr(bd), _ptr(residual), M, H, I, Ho, bits_g, gs_g, bits_u, gs_u, bits_d,
+                              gs_d, out_mode, _ptr(out), _stream(stream))
 
 
 def swiglu_q_debug_gemm(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, path,
@@ -180,6 +189,24 @@ def linear(x, w, s, b, bits, gs, out_mode=SWQ_LINEAR_BF16, out=None, stream=None
     rc = swiglu_q_linear(x, w, s, b, M, K, N, bits, gs, out_mode, out, stream)
     if rc != SWQ_OK:
         raise SwigluQError(rc, "swiglu_q_linear")
+    return out
+
+
+def mlp(x, wg, sg, bg, wu, su, bu, wd, sd, bd, spec_g, spec_u, spec_d, residual=None,
+        out_mode=SWQ_LINEAR_BF16, out=None, stream=None):
+    """``residual + (silu(x Wg^T) * (x Wu^T)) Wd^T`` for device tensors; each
+    spec is (bits, group size); Wd is [Ho, I*bits_d/32].  Returns ``out``
+    ([M, Ho], bf16 or float32 by out_mode)."""
+    import torch
+    M, H = int(x.shape[0]), int(x.shape[1])
+    I, Ho = int(wg.shape[0]), int(wd.shape[0])
+    if out is None:
+        dt = torch.float32 if out_mode == SWQ_LINEAR_F32 else torch.bfloat16
+        out = torch.empty((M, Ho), dtype=dt, device=x.device)
+    rc = swiglu_q_mlp(x, wg, sg, bg, wu, su, bu, wd, sd, bd, residual, M, H, I, Ho, spec_g[0], spec_g[1],
+                      spec_u[0], spec_u[1], spec_d[0], spec_d[1], out_mode, out, stream)
+    if rc != SWQ_OK:
+        raise SwigluQError(rc, "swiglu_q_mlp")
     return out
 
 

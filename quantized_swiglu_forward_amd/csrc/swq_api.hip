@@ -19,6 +19,7 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "../../include/swiglu_q.h"
@@ -38,7 +39,8 @@ struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+// slot 0: the kernels' own staging; slot 1: the whole MLP's hidden tensor
+std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;
 
 int threshold_now() {
   int t = g_threshold.load(std::memory_order_relaxed);
@@ -68,11 +70,12 @@ bool spec_ok(int bits, int gs) {
   return (bits == 2 || bits == 4 || bits == 8) && (gs == 32 || gs == 64 || gs == 128);
 }
 
-// Validation shared by every entry point; nothing touches HIP here.
+// Validation shared by every entry point; nothing touches HIP here.  With
+// has_x false, x is library-owned (the whole MLP's hidden tensor) and not checked.
 int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
              const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
-             int bits_u, int gs_u) {
-  if (!x || !Wg || !sg || !bg || !Wu || !su || !bu) return SWQ_ERR_NULL;
+             int bits_u, int gs_u, bool has_x = true) {
+  if ((has_x && !x) || !Wg || !sg || !bg || !Wu || !su || !bu) return SWQ_ERR_NULL;
   if (!spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return SWQ_ERR_UNSUPPORTED;
   if (M < 0 || H <= 0 || I <= 0) return SWQ_ERR_SHAPE;
   if (H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0) return SWQ_ERR_SHAPE;
@@ -82,7 +85,7 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
   if (((M + 127) / 128) * ((I + 127) / 128) >= (1LL << 31)) return SWQ_ERR_SHAPE;
   // the staged x' ([H + extra columns] x M binary16) is addressed with 32-bit byte offsets
   if (M * (H + kext_columns(H, gs_g < gs_u ? gs_g : gs_u)) * 2 >= (1LL << 32)) return SWQ_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16)) return SWQ_ERR_ALIGN;
+  if ((has_x && !aligned(x, 16)) || !aligned(Wg, 16) || !aligned(Wu, 16)) return SWQ_ERR_ALIGN;
   if (!aligned(sg, 2) || !aligned(bg, 2) || !aligned(su, 2) || !aligned(bu, 2)) return SWQ_ERR_ALIGN;
   return SWQ_OK;
 }
@@ -176,11 +179,11 @@ WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bi
   return w;
 }
 
-int get_workspace(hipStream_t stream, size_t need, void** out) {
+int get_workspace(hipStream_t stream, size_t need, void** out, int slot = 0) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SWQ_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+  Workspace& w = g_ws[{dev, (uintptr_t)stream, slot}];
   if (w.bytes < need) {
     if (w.ptr) {
       // the old buffer may still be read by work queued on this stream
@@ -203,11 +206,12 @@ int get_workspace(hipStream_t stream, size_t need, void** out) {
 }
 
 // I_u: rows of the up matrix (I, or fewer for the linear's split weight);
-// ldo: output row stride in elements (I, or N for the linear).
+// ldo: output row stride in elements (I, or N for the linear); res: the
+// linear's residual (bf16 [M, ldo]) or null.
 int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
         const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int64_t I_u, int64_t ldo,
         int bits_g, int gs_g, int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u,
-        int path, void* stream_v) {
+        const void* res, int path, void* stream_v) {
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
@@ -223,7 +227,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     p.M = (int)M; p.H = (int)H; p.I = (int)I;
     p.I_u = (int)I_u; p.ldo = (int)ldo;
     p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
-    p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+    p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
     p.xa = nullptr; p.xexp = nullptr;
     if (logging())
       fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
@@ -290,7 +294,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.gs_g = gs_g; p.gs_u = gs_u;
   p.ldx = ldx; p.kext = kext;
   p.bext_g = eg; p.bext_u = eu;
-  p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u;
+  p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
   {
     const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
     p.vec = (I % 4 == 0) && (ldo % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
@@ -308,6 +312,30 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   return SWQ_OK;
 }
 
+int validate_linear(const void* x, const uint32_t* W, const void* s, const void* b, int64_t M, int64_t K,
+                    int64_t N, int bits, int gs, int out_mode, const void* out, bool has_x = true) {
+  const int64_t Ig = N > 0 ? (N + 1) / 2 : 0;
+  int rc = validate(x, W, s, b, W, s, b, M, K, Ig, bits, gs, bits, gs, has_x);
+  if (rc != SWQ_OK) return rc;
+  if (out_mode != SWQ_LINEAR_BF16 && out_mode != SWQ_LINEAR_F32) return SWQ_ERR_UNSUPPORTED;
+  if (!out) return SWQ_ERR_NULL;
+  if (!aligned(out, out_mode == SWQ_LINEAR_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
+  return SWQ_OK;
+}
+
+// y = x W^T (+ res): W's rows [0, Ig) run in the gate slot of the fused
+// kernels, [Ig, N) in the up slot
+int linear_run(const void* x, const uint32_t* W, const void* s, const void* b, const void* res, int64_t M,
+               int64_t K, int64_t N, int bits, int gs, int out_mode, void* out, void* stream) {
+  const int64_t Ig = N > 0 ? (N + 1) / 2 : 0, Iu = N - Ig;
+  const uint32_t* Wu = W + Ig * (K * bits / 32);
+  const uint16_t* su = (const uint16_t*)s + Ig * (K / gs);
+  const uint16_t* bu = (const uint16_t*)b + Ig * (K / gs);
+  return run(x, W, s, b, Wu, su, bu, M, K, Ig, Iu, N, bits, gs, bits, gs,
+             out_mode == SWQ_LINEAR_F32 ? swq::kLinF32 : swq::kLinBf16, out, nullptr, nullptr, res, SWQ_PATH_AUTO,
+             stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,23 +350,34 @@ int swiglu_q_forward(const void* x, const uint32_t* Wg, const void* sg, const vo
   if (!out) return SWQ_ERR_NULL;
   if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
   return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
-             nullptr, nullptr, SWQ_PATH_AUTO, stream);
+             nullptr, nullptr, nullptr, SWQ_PATH_AUTO, stream);
 }
 
 int swiglu_q_linear(const void* x, const uint32_t* W, const void* s, const void* b, int64_t M, int64_t K,
                     int64_t N, int bits, int gs, int out_mode, void* out, void* stream) {
-  // W's rows [0, Ig) run in the gate slot of the fused kernels, [Ig, N) in the up slot
-  const int64_t Ig = N > 0 ? (N + 1) / 2 : 0, Iu = N - Ig;
-  int rc = validate(x, W, s, b, W, s, b, M, K, Ig, bits, gs, bits, gs);
+  int rc = validate_linear(x, W, s, b, M, K, N, bits, gs, out_mode, out);
   if (rc != SWQ_OK) return rc;
-  if (out_mode != SWQ_LINEAR_BF16 && out_mode != SWQ_LINEAR_F32) return SWQ_ERR_UNSUPPORTED;
-  if (!out) return SWQ_ERR_NULL;
-  if (!aligned(out, out_mode == SWQ_LINEAR_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
-  const uint32_t* Wu = W + Ig * (K * bits / 32);
-  const uint16_t* su = (const uint16_t*)s + Ig * (K / gs);
-  const uint16_t* bu = (const uint16_t*)b + Ig * (K / gs);
-  return run(x, W, s, b, Wu, su, bu, M, K, Ig, Iu, N, bits, gs, bits, gs,
-             out_mode == SWQ_LINEAR_F32 ? swq::kLinF32 : swq::kLinBf16, out, nullptr, nullptr, SWQ_PATH_AUTO, stream);
+  return linear_run(x, W, s, b, nullptr, M, K, N, bits, gs, out_mode, out, stream);
+}
+
+int swiglu_q_mlp(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
+                 const void* su, const void* bu, const uint32_t* Wd, const void* sd, const void* bd,
+                 const void* residual, int64_t M, int64_t H, int64_t I, int64_t Ho, int bits_g, int gs_g,
+                 int bits_u, int gs_u, int bits_d, int gs_d, int out_mode, void* out, void* stream) {
+  int rc = validate(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u);
+  if (rc != SWQ_OK) return rc;
+  // the down projection (K = I, N = Ho) reads the library's hidden tensor
+  rc = validate_linear(nullptr, Wd, sd, bd, M, I, Ho, bits_d, gs_d, out_mode, out, false);
+  if (rc != SWQ_OK) return rc;
+  if (!aligned(residual, 2)) return SWQ_ERR_ALIGN;
+  if (M == 0) return SWQ_OK;
+  void* hidden = nullptr;
+  rc = get_workspace((hipStream_t)stream, (size_t)align256(M * I * 2), &hidden, 1);
+  if (rc != SWQ_OK) return rc;
+  rc = run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, SWQ_MATCH, hidden, nullptr,
+           nullptr, nullptr, SWQ_PATH_AUTO, stream);
+  if (rc != SWQ_OK) return rc;
+  return linear_run(hidden, Wd, sd, bd, residual, M, I, Ho, bits_d, gs_d, out_mode, out, stream);
 }
 
 int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
@@ -351,7 +390,7 @@ int swiglu_q_debug_gemm(const void* x, const uint32_t* Wg, const void* sg, const
   if (!gate_out || !up_out) return SWQ_ERR_NULL;
   if (!aligned(gate_out, 4) || !aligned(up_out, 4)) return SWQ_ERR_ALIGN;
   return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, SWQ_F32, nullptr, gate_out,
-             up_out, path, stream);
+             up_out, nullptr, path, stream);
 }
 
 int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode) {
@@ -402,7 +441,7 @@ int swiglu_q_release_workspace(void) {
   (void)hipGetDevice(&prev);
   for (auto& kv : g_ws) {
     if (!kv.second.ptr) continue;
-    if (hipSetDevice(kv.first.first) != hipSuccess) { rc = SWQ_ERR_HIP; continue; }
+    if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess) { rc = SWQ_ERR_HIP; continue; }
     if (hipDeviceSynchronize() != hipSuccess) rc = SWQ_ERR_HIP;
     if (hipFree(kv.second.ptr) != hipSuccess) rc = SWQ_ERR_HIP;
   }

@@ -77,6 +77,10 @@ __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, flo
     p.dbg_g[o] = g;
     p.dbg_u[o] = u;
   } else if (p.mode >= kLinBf16) {
+    if (p.res) {   // the residual of a whole MLP, added in float32 before the one rounding
+      g += bf16_to_f32(p.res[o]);
+      if (n < p.I_u) u += bf16_to_f32(p.res[o + p.I]);
+    }
     if (p.mode == kLinF32) {
       reinterpret_cast<float*>(p.out)[o] = g;
       if (n < p.I_u) reinterpret_cast<float*>(p.out)[o + p.I] = u;

@@ -56,6 +56,7 @@ struct MfmaParams {
   void* out;
   float* dbg_g;        // non-null: write float32 gate/up instead of hidden
   float* dbg_u;
+  const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
   int vec;             // 1: the output rows allow 16-byte (f32) / 8-byte (bf16) stores of 4 features
 };
 
@@ -75,6 +76,7 @@ struct GemvParams {
   void* out;
   float* dbg_g;
   float* dbg_u;
+  const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
   const _Float16* xa;  // x' staged by the prep kernel, [H/32][M][32] (M*H > kSkinnyStageMax), or null
   const int* xexp;     // and its row exponents
 };

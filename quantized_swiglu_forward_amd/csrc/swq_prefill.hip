@@ -772,6 +772,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
             put4(p.dbg_g, o, c0, p.n_end, g);
             put4(p.dbg_u, o, c0, p.n_end, u);
           } else if constexpr (LIN) {
+            if (p.res) {   // the residual of a whole MLP, added in float32 before the one rounding
+              const int lg_ = p.n_end - c0, lu_ = min(p.n_end, p.I_u) - c0;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                if (c < lg_) g[c] += bf16_to_f32(p.res[o + c]);
+                if (c < lu_) u[c] += bf16_to_f32(p.res[o + p.I + c]);
+              }
+            }
             auto* y = reinterpret_cast<std::conditional_t<MODE == kLinF32, float, uint16_t>*>(p.out);
             put4(y, o, c0, p.n_end, g);
             put4(y, o + p.I, c0, min(p.n_end, p.I_u), u);

@@ -157,6 +157,20 @@ def make_custom(M, H, I, bits_g=4, gs_g=64, bits_u=None, gs_u=None, seed=0,
                    codes_u=cu if keep_codes else None, xs=xs)
 
 
+def make_down(Ho, I, bits=4, gs=64, seed=0, s_lo=0.005, s_hi=0.02, bias_mode="factor"):
+    """The down projection of a whole MLP: packed codes [Ho, I*bits/32], bf16
+    scales and biases [Ho, I/gs] (bit patterns), drawn as the gate and up."""
+    rng = np.random.default_rng(seed)
+    _, w, s, b = _draw_matrix(rng, Ho, I, bits, gs, s_lo, s_hi, bias_mode)
+    return w, s, b
+
+
+def make_residual(M, Ho, seed=0, sigma=1.0) -> np.ndarray:
+    """A bf16 residual stream [M, Ho] (bit patterns), N(0, sigma^2)."""
+    rng = np.random.default_rng(seed)
+    return to_bf16_bits((rng.standard_normal((M, Ho), dtype=np.float32) * np.float32(sigma)).astype(np.float32))
+
+
 def make_problem(cfg: int | Config, keep_codes=False, with_calls=True) -> Problem:
     """The synthetic problem of a named configuration (seed = its index)."""
     c = CONFIGS[cfg] if isinstance(cfg, int) else cfg

@@ -58,6 +58,16 @@ int main(void) {
     expect(swiglu_q_linear(p, NULL, p, p, 4, 256, 65, 4, 64, SWQ_LINEAR_F32, p, NULL), SWQ_ERR_NULL,
            "linear W = NULL");
 
+    /* whole MLP */
+    expect(swiglu_q_mlp(p, w, p, p, w, p, p, w, p, p, NULL, 0, 256, 512, 256, 4, 64, 4, 64, 4, 64,
+                        SWQ_LINEAR_BF16, p, NULL), SWQ_OK, "mlp M = 0");
+    expect(swiglu_q_mlp(p, w, p, p, w, p, p, NULL, p, p, p, 4, 256, 512, 256, 4, 64, 4, 64, 4, 64,
+                        SWQ_LINEAR_BF16, p, NULL), SWQ_ERR_NULL, "mlp Wd = NULL");
+    expect(swiglu_q_mlp(p, w, p, p, w, p, p, w, p, p, p, 4, 256, 480, 256, 4, 64, 4, 64, 4, 64,
+                        SWQ_LINEAR_BF16, p, NULL), SWQ_ERR_SHAPE, "mlp I not a multiple of gs_d");
+    expect(swiglu_q_mlp(p, w, p, p, w, p, p, w, p, p, p + 1, 4, 256, 512, 256, 4, 64, 4, 64, 4, 64,
+                        SWQ_LINEAR_BF16, p, NULL), SWQ_ERR_ALIGN, "mlp residual misaligned");
+
     /* debug hook */
     expect(swiglu_q_debug_gemm(p, w, p, p, w, p, p, 4, 256, 64, 4, 64, 4, 64, 5, (float *)p, (float *)p, NULL),
            SWQ_ERR_UNSUPPORTED, "debug path");

@@ -120,6 +120,35 @@ def test_linear_validation():
     assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
 
 
+def test_mlp_validation():
+    """swiglu_q_mlp checks the forward's and the down projection's arguments
+    before any HIP call (the hidden buffer included): M = 0 is a no-op; bad
+    shapes, specs, output types and alignments are rejected."""
+    base = dict(x=P, Wg=P, sg=P, bg=P, Wu=P, su=P, bu=P, Wd=P, sd=P, bd=P, residual=P, M=4, H=256, I=512,
+                Ho=256, bits_g=4, gs_g=64, bits_u=4, gs_u=64, bits_d=4, gs_d=64, out_mode=0, out=P, stream=0)
+    before = (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1))
+    assert swq.swiglu_q_mlp(**{**base, "M": 0}) == swq.SWQ_OK
+    assert swq.swiglu_q_mlp(**{**base, "M": 0, "residual": None}) == swq.SWQ_OK
+    assert swq.swiglu_q_mlp(**{**base, "x": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_mlp(**{**base, "Wd": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_mlp(**{**base, "bd": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_mlp(**{**base, "out": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_mlp(**{**base, "bits_d": 3}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_mlp(**{**base, "gs_d": 16}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_mlp(**{**base, "bits_g": 5}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_mlp(**{**base, "out_mode": 2}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_mlp(**{**base, "I": 480}) == swq.SWQ_ERR_SHAPE          # down: I not a multiple of gs_d
+    assert swq.swiglu_q_mlp(**{**base, "Ho": 0}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_mlp(**{**base, "H": 96}) == swq.SWQ_ERR_SHAPE
+    assert swq.swiglu_q_mlp(**{**base, "I": 1 << 21}) == swq.SWQ_ERR_SHAPE      # the down projection's K limit
+    assert swq.swiglu_q_mlp(**{**base, "x": P + 8}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_mlp(**{**base, "Wd": P + 4}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_mlp(**{**base, "sd": P + 1}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_mlp(**{**base, "residual": P + 1}) == swq.SWQ_ERR_ALIGN
+    assert swq.swiglu_q_mlp(**{**base, "out": P + 2, "out_mode": 1}) == swq.SWQ_ERR_ALIGN
+    assert (swq.swiglu_q_call_count(0), swq.swiglu_q_call_count(1)) == before
+
+
 def test_header_compiles_as_c_and_links(tmp_path):
     """A plain C99 program includes include/swiglu_q.h, links the library and
     gets the documented status codes from the host-side validation."""

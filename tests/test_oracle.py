@@ -11,8 +11,8 @@ import torch
 
 import oracle
 from oracle import compare, exact
-from synth import (CONFIGS, bf16_bits_to_f32, make_custom, make_problem, pack_codes,
-                   to_bf16_bits)
+from synth import (CONFIGS, bf16_bits_to_f32, make_custom, make_down, make_problem, make_residual,
+                   pack_codes, to_bf16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SPECS = [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128), (2, 32), (2, 64)]
@@ -151,6 +151,98 @@ def test_linear_metric_catches_planted_errors():
     assert not compare.evaluate_linear(bad, r, nu, 1)["ok"]
     bad = r.copy(); bad[big] = -bad[big]
     assert not compare.evaluate_linear(bad, r, nu, 1)["ok"]
+
+
+# ------------------------------------------------------------- whole MLP --
+
+@pytest.mark.parametrize("bits_d,gs_d", [(4, 64), (8, 32), (2, 128)])
+def test_mlp_reference_matches_exact_rationals(bits_d, gs_d):
+    """The whole MLP's down projection and residual against exact rationals,
+    on the oracle's own bf16 hidden rows (the forward, pinned above, rounded):
+    every output within 1e-14 of the down projection's scale; asking for a
+    subset of elements gives the same values."""
+    M, H, I, Ho = 2, 128, 128, 5
+    p = make_custom(M, H, I, 4, 64, 8, 32, seed=gs_d + bits_d)
+    wd, sd, bd = make_down(Ho, I, bits_d, gs_d, seed=7)
+    res = make_residual(M, Ho, seed=8)
+    y, nu, rows, hb = oracle.mlp_pairs(p, wd, sd, bd, bits_d, gs_d, Ho, res)
+    assert list(rows) == list(range(M))
+    assert np.array_equal(hb, oracle.bf16_rne(oracle.swiglu_full(p, 0)["h"]))
+    ex = exact.qmm_exact([list(r) for r in hb], wd, sd, bd, M, I, Ho, bits_d, gs_d)
+    for m in range(M):
+        for n in range(Ho):
+            ref = ex[m][n] + exact.bf16_exact(res[m, n])
+            assert _rel_to_scale(y[m * Ho + n], float(ref), nu[m * Ho + n] + abs(float(ref))) <= 1e-14
+    ms, ns = np.array([1, 0, 1]), np.array([4, 2, 0])
+    ys, nus, rows2, _ = oracle.mlp_pairs(p, wd, sd, bd, bits_d, gs_d, Ho, res, ms, ns)
+    assert list(rows2) == [0, 1]
+    assert np.array_equal(ys, y.reshape(M, Ho)[ms, ns]) and np.array_equal(nus, nu.reshape(M, Ho)[ms, ns])
+
+
+def _zero_matrix(rows, K, bits, gs, seed):
+    """Constant codes q = 8 with biases -8 s: every dequantized weight is 0."""
+    rng = np.random.default_rng(seed)
+    codes = np.full((rows, K), 8, dtype=np.uint8)
+    s = to_bf16_bits(rng.uniform(0.005, 0.02, size=(rows, K // gs)).astype(np.float32))
+    b = to_bf16_bits((np.float32(-8.0) * bf16_bits_to_f32(s)).astype(np.float32))   # exact: a power of two
+    return pack_codes(codes, bits), s, b
+
+
+def test_mlp_closed_forms_give_the_residual():
+    """Zero down weights, or a zero gate (silu(0) = 0, so the hidden tensor
+    vanishes), leave exactly the residual; without a residual, exactly 0."""
+    M, H, I, Ho = 3, 128, 192, 64
+    p = make_custom(M, H, I, 4, 64, seed=3)
+    res = make_residual(M, Ho, seed=4)
+    wd, sd, bd = _zero_matrix(Ho, I, 4, 64, seed=5)
+    y, nu, _, _ = oracle.mlp_pairs(p, wd, sd, bd, 4, 64, Ho, res)
+    assert np.array_equal(y, bf16_bits_to_f32(res).astype(np.float64).reshape(-1)) and not nu.any()
+    y0, _, _, _ = oracle.mlp_pairs(p, wd, sd, bd, 4, 64, Ho)
+    assert not y0.any()
+    p.wg, p.sg, p.bg = _zero_matrix(I, H, 4, 64, seed=6)
+    wd, sd, bd = make_down(Ho, I, 4, 64, seed=7)
+    y, nu, _, hb = oracle.mlp_pairs(p, wd, sd, bd, 4, 64, Ho, res)
+    assert not (hb & 0x7FFF).any()
+    assert np.array_equal(y, bf16_bits_to_f32(res).astype(np.float64).reshape(-1))
+
+
+def test_mlp_metric_allows_hidden_roundings_and_catches_planted_errors():
+    """The whole-MLP bar: the oracle's result with 1 % of its hidden
+    elements moved to their other bf16 neighbour (ten times the rate of
+    admissible roundings measured on the device) passes, rounded to bf16 or
+    float32; a dropped group of the down projection, a missing residual, a
+    3 % error or a wrong sign fails."""
+    M, H, I, Ho = 2, 512, 2048, 256
+    p = make_custom(M, H, I, 4, 64, seed=11)
+    wd, sd, bd = make_down(Ho, I, 4, 64, seed=12)
+    res = make_residual(M, Ho, seed=13)
+    r, nu, _, hb = oracle.mlp_pairs(p, wd, sd, bd, 4, 64, Ho, res)
+    rng = np.random.default_rng(14)
+    moved = hb.copy()
+    pick = rng.random(hb.shape) < 0.01
+    nonzero = (hb & 0x7FFF) != 0
+    step = np.where(rng.random(hb.shape) < 0.5, 1, -1).astype(np.int32)
+    moved = np.where(pick & nonzero, (moved.astype(np.int32) + step).astype(np.uint16), moved)
+    assert (moved != hb).sum() > 0.005 * hb.size
+    rb = oracle.bf16_value(res).reshape(-1)
+    y_moved, _ = oracle.qmm_pairs(moved, wd, sd, bd, M, I, Ho, 4, 64)
+    y_moved = y_moved + rb
+    assert compare.evaluate_mlp(r, r, nu, 0)["ok"] and compare.evaluate_mlp(r, r, nu, 1)["ok"]
+    assert compare.evaluate_mlp(oracle.bf16_value(oracle.bf16_rne(y_moved)), r, nu, 0)["ok"]
+    assert compare.evaluate_mlp(y_moved.astype(np.float32), r, nu, 1)["ok"]
+    # planted errors
+    sd_drop = sd.copy(); bd_drop = bd.copy()
+    sd_drop[:, 5] = 0; bd_drop[:, 5] = 0                      # group 5 of every output contributes nothing
+    y_drop, _ = oracle.qmm_pairs(hb, wd, sd_drop, bd_drop, M, I, Ho, 4, 64)
+    y_drop = y_drop + rb
+    assert not compare.evaluate_mlp(y_drop.astype(np.float32), r, nu, 1)["ok"]
+    assert not compare.evaluate_mlp(oracle.bf16_value(oracle.bf16_rne(y_drop)), r, nu, 0)["ok"]
+    assert not compare.evaluate_mlp(r - rb, r, nu, 0)["ok"]
+    big = np.argmax(np.abs(r))
+    bad = r.copy(); bad[big] *= 1.03
+    assert not compare.evaluate_mlp(bad, r, nu, 0)["ok"]
+    bad = r.copy(); bad[big] = -bad[big]
+    assert not compare.evaluate_mlp(bad, r, nu, 1)["ok"]
 
 
 @pytest.mark.parametrize("case", range(24))
