@@ -407,28 +407,47 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
     }
   };
   if constexpr (MR > 1) {
-    // each row's x chunk is read from LDS once and serves the R columns
+    // A whole wave per column (the launcher's condition).  Every row's sums
+    // first (each row's x chunk read from LDS once for the R columns), then
+    // the rows' reductions side by side, then one store branch for all rows:
+    // the rows' dependency chains overlap instead of running one after the
+    // other.  Per row the arithmetic is the single-row case's, in its order.
+    float ag[MR][R], au[MR][R];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float ag[R], au[R];
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        ag[r] = 0.0f;
-        au[r] = 0.0f;
+        ag[m][r] = 0.0f;
+        au[m][r] = 0.0f;
       }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (FULL || sl + c * lpc < nchunk) {
+    for (int c = 0; c < CPL; ++c) {
+      if (FULL || sl + c * lpc < nchunk) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
           XChunk xc;   // per row and chunk: all of them at once would not fit in registers
           read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc), xc.e + 20);
-            au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc), xc.e + 20);
+            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc), xc.e + 20);
+            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc), xc.e + 20);
           }
         }
       }
-      finish(ag, au, m);
+    }
+    float gm[MR], um[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float t0 = fold32(ag[m][0], au[m][0]);
+      const float t = R == 2 ? fold16(t0, fold32(ag[m][R - 1], au[m][R - 1])) : fold16(t0, t0);
+      gm[m] = row_sum(t);
+      um[m] = upper_half(gm[m]);
+    }
+    const int col = lane >> 4;
+    const int64_t n = (int64_t)wave_global * R + col;
+    if ((lane & 15) == 0 && col < R && n < p.I) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) store_out(p, m, (int)n, gm[m], um[m]);
     }
   } else {
     XChunk xc[CPL];
