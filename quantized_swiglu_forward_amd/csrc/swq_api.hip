@@ -95,8 +95,9 @@ bool gemv_fits(int64_t M, int64_t H) {
   return M >= 1 && M <= kGemvMaxM;
 }
 
-// The M = 1 kernel reads x itself for H <= 8192, and the few-row kernel
-// builds x' itself for M*H <= kSkinnyStageMax; otherwise the prep kernel
+// The matrix-vector kernel reads x itself (M = 1 with H <= 8192, and its
+// several-row form), and the few-row kernel builds x' itself for
+// M*H <= kSkinnyStageMax; otherwise the prep kernel
 // stages x' first (in the workspace).  SWIGLU_Q_SKINNY_STAGE=0 always uses
 // the prep kernel.
 bool gemv_needs_rows(int64_t M, int64_t H) {

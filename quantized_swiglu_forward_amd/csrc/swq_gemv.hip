@@ -10,10 +10,12 @@
 // accumulation; the same epilogue as the matrix-matrix path writes hidden.
 //
 // Two kernels:
-//  * swq_gemv1_kernel: M = 1 with at most four chunks per lane (H <= 8192).
-//    Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no offset,
-//    each chunk of x scaled by its own power of two; the block shares x
-//    through LDS (described above the kernel).
+//  * swq_gemv1_kernel: M = 1 with at most four chunks per lane (H <= 8192),
+//    and 2 <= M <= 4 with a whole wave per column and at most two chunks
+//    per lane (2048 <= H <= 4096), each weight chunk loaded once for all
+//    rows.  Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no
+//    offset, each chunk of x scaled by its own power of two; the block
+//    shares x through LDS (described above the kernel).
 //  * swq_skinny_kernel: 1 <= M <= 16 otherwise.  x' comes from the prep
 //    kernel, or for M*H <= 8192 every block builds it in LDS itself; codes
 //    become exact binary16 s (q - z) and 16 x 16 x 32 MFMAs multiply them
