@@ -80,7 +80,7 @@ extern "C" {
 #define SWQ_F32_BF16OUT  2  /* as SWQ_F32, rounded once to bf16 at the store       */
 
 /* Kernel paths chosen by the M-threshold dispatcher. */
-#define SWQ_PATH_GEMV    0  /* M < threshold (M <= 16): matrix-vector kernels      */
+#define SWQ_PATH_GEMV    0  /* M < threshold (M <= 32): matrix-vector kernels      */
 #define SWQ_PATH_MFMA    1  /* M >= threshold: dequantizing bf16/f16 MFMA GEMM      */
 #define SWQ_PATH_AUTO   -1
 
@@ -172,10 +172,11 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
                        int precision_mode);
 
 /* M threshold T of the dispatcher: M < T takes SWQ_PATH_GEMV, M >= T takes
- * SWQ_PATH_MFMA; the matrix-vector path takes at most 16 rows, so M > 16
+ * SWQ_PATH_MFMA; the matrix-vector path takes at most 32 rows, so M > 32
  * always runs the MFMA path.  The default comes from the environment
  * variable SWIGLU_Q_MMIN when set to a positive integer, else the built-in
- * default 17 (measured: the matrix-vector path is faster for every M <= 16).
+ * default 33 (measured: the matrix-vector path is faster for every M <= 32
+ * but at the largest weight shape measured, where it is within 3 %).
  * T <= 1 sends every M >= 1 to the MFMA path. */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);

@@ -16,10 +16,10 @@
 //    rows.  Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no
 //    offset, each chunk of x scaled by its own power of two; the block
 //    shares x through LDS (described above the kernel).
-//  * swq_skinny_kernel: 1 <= M <= 16 otherwise.  x' comes from the prep
+//  * swq_skinny_kernel: 1 <= M <= 32 otherwise.  x' comes from the prep
 //    kernel, or for M*H <= 8192 every block builds it in LDS itself; codes
 //    become exact binary16 s (q - z) and 16 x 16 x 32 MFMAs multiply them
-//    with up to 16 rows at once (described above the kernel).
+//    with one or two tiles of 16 rows at once (described above the kernel).
 // 2-bit codes are spread to nibbles as they are loaded and take the 4-bit
 // arithmetic.
 #include <type_traits>
@@ -472,14 +472,14 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
   }
 }
 
-// --------------------------------------------------------- 2 <= M <= 16 --
+// --------------------------------------------------------- 2 <= M <= 32 --
 //
 // Matrix-vector products for a few rows.  The rows of x, staged once per call
 // as x' = x 2^-e (binary16, per-row power of two, in the code-pair order of
 // the dequantized weights, 32 inputs per chunk), are the A operand of
-// v_mfma_f32_16x16x32_f16 (16 rows, M of them live); the dequantized weights
-// s (q - z) of 16 output columns are the B operand, so one unpack serves
-// every row.  A block of up to 16 waves owns 16 columns of both matrices:
+// v_mfma_f32_16x16x32_f16 (RT tiles of 16 rows, M of them live); the
+// dequantized weights s (q - z) of 16 output columns are the B operand, so
+// one unpack serves every row of every tile.  A block of up to 16 waves owns 16 columns of both matrices:
 // wave w takes the chunk quads w, w + W, ... (W waves), and lane group
 // h = lane / 16 takes chunk 4 quad + h: the MFMA's K slots of group h are
 // that chunk's 8-code block, on the A side x' of the same inputs.  With 4-bit
@@ -494,16 +494,18 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSkinnyMaxWaves = 16;
 
-template <int BITS_G, int BITS_U>
+template <int BITS_G, int BITS_U, int RT>
 struct SkinnyChunk {
-  u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[4];
+  u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[RT][4];
   float sg, bg, su, bu;
   bool live;
 };
 
-template <int BITS_G, int BITS_U, bool STAGE>
+// RT: row tiles of 16 (M <= 16 RT = 1; M <= 32 RT = 2, whose second tile of x'
+// and accumulators need twice the registers: half the waves per SIMD)
+template <int BITS_G, int BITS_U, bool STAGE, int RT>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -511,7 +513,9 @@ __attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void sw
   const int r = lane & 15, h = lane >> 4;             // A row / B and D column; K-slot group
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int col = (int)n0 + r;
-  const int rowc = min(r, p.M - 1);                   // clamped for loads (rows >= M are dropped)
+  int rowc[RT];                                       // clamped for loads (rows >= M are dropped)
+#pragma unroll
+  for (int t = 0; t < RT; ++t) rowc[t] = min(16 * t + r, p.M - 1);
   const int nchunk = p.H >> 5;
   // the block's 16 columns through buffer descriptors (columns past I read zeros)
   const int ncols = (int)min((int64_t)16, (int64_t)p.I - n0);
@@ -528,7 +532,7 @@ __attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void sw
   __shared__ int xe[kGemvMaxM];
   __shared__ uint32_t xmax[kGemvMaxM];
 
-  auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
+  auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
     const int cc = d.live ? c : 0;                     // an in-range chunk for the loads
@@ -553,26 +557,33 @@ __attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void sw
     d.su = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0));
     d.bu = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0));
     if constexpr (!STAGE) {
-      const int ox = (cc * p.M + rowc) * 64;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) d.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
+      for (int t = 0; t < RT; ++t) {
+        const int ox = (cc * p.M + rowc[t]) * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d.x[t][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
+      }
     }
   };
-  auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U>& d) {
+  auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int c = min(4 * quad + h, nchunk - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.x[q] = xs[(c * p.M + rowc) * 4 + q];
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d.x[t][q] = xs[(c * p.M + rowc[t]) * 4 + q];
   };
 
-  // one matrix's 8-code block kb of a chunk: one MFMA (4-bit) or two (8-bit planes)
-  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, int kb, const f16x8& a, f32x4& acc) {
+  // one matrix's 8-code block kb of a chunk, multiplied into every row tile:
+  // one B operand (4-bit) or two (8-bit planes), built once
+  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, int kb, const f16x8 (&a)[RT], f32x4 (&acc)[RT]) {
     const _Float16 hs = (_Float16)sf;
     const f16x2 s2 = {hs, hs};
     if constexpr (kCodeWidth<BITS> == 4) {
       uint32_t o[4];
       dequant4(cw[0][kb], s2, o, nk);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]}), acc,
-                                                  0, 0, 0);
+      const f16x8 b = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc[t], 0, 0, 0);
     } else {
       uint32_t lo[4], hi[4];
       codes8(cw[kb >> 1][2 * (kb & 1)], cw[kb >> 1][2 * (kb & 1) + 1], lo, hi, nk);
@@ -583,42 +594,55 @@ __attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void sw
         vl[j] = as_u32(as_h2(lo[j]) * s2);
         vh[j] = as_u32(as_h2(hi[j]) * s16);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, vl), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, vh), acc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8, vl), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8, vh), acc[t], 0, 0, 0);
+      }
     }
   };
 
-  f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const SkinnyChunk<BITS_G, BITS_U>& d) {
+  f32x4 ag[RT], au[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    ag[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    au[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  auto compute = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const f16x8 a = __builtin_bit_cast(f16x8, d.x[kb]);
+      f16x8 a[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) a[t] = __builtin_bit_cast(f16x8, d.x[t][kb]);
       block_mfma.template operator()<BITS_G>(d.cg, d.sg, kb, a, ag);
       block_mfma.template operator()<BITS_U>(d.cu, d.su, kb, a, au);
     }
     // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
-    float sx = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d.x[q][j]), one2, sx, false);
-    const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
     const _Float16 z0 = (_Float16)0.0f;
-    const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
     const float cgf = fmaf(CodeOffset<BITS_G>::z, d.sg, d.bg), cuf = fmaf(CodeOffset<BITS_U>::z, d.su, d.bu);
     const _Float16 cgh = (_Float16)cgf, cgl = (_Float16)(cgf - (float)cgh);
     const _Float16 cuh = (_Float16)cuf, cul = (_Float16)(cuf - (float)cuh);
     const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
     const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
-    ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag, 0, 0, 0);
-    au = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      float sx = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d.x[t][q][j]), one2, sx, false);
+      const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
+      const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
+      ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[t], 0, 0, 0);
+      au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[t], 0, 0, 0);
+    }
   };
 
   // chunk quads w, w + nw, ... (one for H <= 2048)
   const int nquad = (nchunk + 3) >> 2;
   if constexpr (STAGE) {
     // the first quad's weights are in flight while the block builds x'
-    SkinnyChunk<BITS_G, BITS_U> d;
+    SkinnyChunk<BITS_G, BITS_U, RT> d;
     if (w < nquad) load(w, d);
     const int nt = blockDim.x, nblk = p.M * (p.H >> 3);   // 8-value blocks of x
     if (tid < p.M) xmax[tid] = 0;
@@ -656,29 +680,35 @@ __attribute__((amdgpu_waves_per_eu(BITS_G <= 4 && BITS_U <= 4 ? 8 : 4))) void sw
     }
   } else {
     for (int q0 = w; q0 < nquad; q0 += nw) {
-      SkinnyChunk<BITS_G, BITS_U> d;
+      SkinnyChunk<BITS_G, BITS_U, RT> d;
       load(q0, d);
       compute(d);
     }
   }
 
   // the waves' partial sums; D element j of lane l is row 4 (l / 16) + j, column l % 16
-  __shared__ f32x4 red[kSkinnyMaxWaves][2][64];
-  red[w][0][lane] = ag;
-  red[w][1][lane] = au;
+  __shared__ f32x4 red[kSkinnyMaxWaves][2 * RT][64];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    red[w][2 * t][lane] = ag[t];
+    red[w][2 * t + 1][lane] = au[t];
+  }
   __syncthreads();
   if (w == 0) {
-    f32x4 g = red[0][0][lane], u = red[0][1][lane];
-    for (int ww = 1; ww < nw; ++ww) {
-      g += red[ww][0][lane];
-      u += red[ww][1][lane];
-    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = 4 * h + j;
-      if (m < p.M && col < p.I) {
-        const int e = STAGE ? xe[m] : p.xexp[m];
-        store_out(p, m, col, ldexpf(g[j], e), ldexpf(u[j], e));
+    for (int t = 0; t < RT; ++t) {
+      f32x4 g = red[0][2 * t][lane], u = red[0][2 * t + 1][lane];
+      for (int ww = 1; ww < nw; ++ww) {
+        g += red[ww][2 * t][lane];
+        u += red[ww][2 * t + 1][lane];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 16 * t + 4 * h + j;
+        if (m < p.M && col < p.I) {
+          const int e = STAGE ? xe[m] : p.xexp[m];
+          store_out(p, m, col, ldexpf(g[j], e), ldexpf(u[j], e));
+        }
       }
     }
   }
@@ -787,11 +817,14 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns
   const int quads = (p.H / 32 + 3) / 4;
   const int waves = quads < kSkinnyMaxWaves ? quads : kSkinnyMaxWaves;
+  const dim3 g((p.I + 15) / 16), b(64 * waves);
   if (p.xa == nullptr) {
     if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 1>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 2>), g, b, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false>), dim3((p.I + 15) / 16), dim3(64 * waves), 0, stream, p);
+    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2>), g, b, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -93,8 +93,8 @@ constexpr int kMfmaConfigs = 2;
 constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
 constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
-// Largest M the matrix-vector path takes (one 16-row MFMA tile).
-constexpr int kGemvMaxM = 16;
+// Largest M the matrix-vector path takes (two 16-row MFMA tiles).
+constexpr int kGemvMaxM = 32;
 // M*H up to this: the few-row kernel builds x' itself (one launch, no workspace).
 constexpr int kSkinnyStageMax = 8192;
 // the matrix-vector kernel's several-row form (no staging pass): 2 <= M <=

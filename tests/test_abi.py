@@ -198,7 +198,7 @@ def test_threshold_default_from_environment():
     env = dict(os.environ, SWIGLU_Q_MMIN="junk")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
                          check=True).stdout.strip()
-    assert out == "17"
+    assert out == "33"
 
 
 def test_strerror_and_version():

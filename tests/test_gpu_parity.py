@@ -58,7 +58,7 @@ for i, (M, H, I) in enumerate(SHAPES):
     spec = SPECS[i % len(SPECS)]
     if H % spec[1] or H % spec[3]:
         spec = SPECS[0]
-    paths = [GEMV, MFMA] if M <= 16 else [MFMA]
+    paths = [GEMV, MFMA] if M <= 32 else [MFMA]
     for path in paths:
         SWEEP.append((M, H, I, spec, i % 3, path))
 
@@ -242,7 +242,7 @@ def test_integer_special_case_is_exact(path):
     assert np.array_equal(u, ref_u.astype(np.float64))
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 17, 24, 32])
 def test_gemv_and_mfma_agree(M):
     p = make_custom(M, 2048, 300, 4, 64, seed=M)
     say("gemv vs mfma", M)
@@ -253,15 +253,17 @@ def test_gemv_and_mfma_agree(M):
     check(ym, o, 1, f"mfma M{M}")
 
 
-# the few-row kernel with x' built inside the kernel (M*H <= 8192: one
-# launch) and staged by the prep kernel (larger), on both sides of the
-# boundary, all three code widths, and M <= 4 and M = 1 past the
-# matrix-vector kernel's H limits
+# the few-row kernel with one and two tiles of 16 rows (M up to 32), x' built
+# inside the kernel (M*H <= 8192: one launch) and staged by the prep kernel
+# (larger), on both sides of the boundary, all three code widths, and M <= 4
+# and M = 1 past the matrix-vector kernel's H limits
 FEW_ROW = [(6, 1024, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (8, 1024, 257, (8, 64, 4, 128)),
            (5, 2048, 96, (4, 32, 4, 64)), (9, 2048, 300, (4, 64, 4, 64)), (16, 2048, 129, (8, 32, 8, 64)),
            (12, 4096, 64, (4, 128, 4, 64)), (16, 512, 100, (4, 64, 8, 64)), (1, 8192, 200, (4, 64, 4, 64)),
            (1, 16384, 33, (8, 64, 4, 32)), (1, 32768, 40, (4, 64, 4, 64)), (5, 1024, 77, (2, 64, 4, 64)),
-           (12, 2048, 96, (2, 128, 2, 32)), (3, 6144, 50, (8, 32, 2, 64)), (4, 5120, 70, (4, 64, 4, 64))]
+           (12, 2048, 96, (2, 128, 2, 32)), (3, 6144, 50, (8, 32, 2, 64)), (4, 5120, 70, (4, 64, 4, 64)),
+           (17, 2048, 130, (4, 64, 8, 32)), (24, 256, 97, (4, 64, 4, 64)), (32, 256, 200, (8, 32, 2, 64)),
+           (32, 4096, 65, (4, 128, 4, 64)), (20, 1024, 77, (2, 64, 8, 128)), (29, 448, 33, (4, 64, 4, 64))]
 
 
 @pytest.mark.parametrize("M,H,I,spec", FEW_ROW, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in FEW_ROW])
@@ -411,8 +413,9 @@ def test_m_zero_launches_nothing():
 
 @pytest.mark.parametrize("M,H,I,spec", [(1, 2048, 600, (4, 64, 4, 64)), (3, 2048, 600, (4, 64, 4, 64)),
                                         (6, 256, 300, (8, 32, 4, 64)), (12, 2048, 200, (4, 64, 4, 64)),
-                                        (300, 512, 384, (4, 64, 8, 32))],
-                         ids=["decode", "decode-rows", "few-row-in-kernel", "few-row-prep", "mfma"])
+                                        (24, 1024, 300, (4, 64, 4, 64)), (300, 512, 384, (4, 64, 8, 32))],
+                         ids=["decode", "decode-rows", "few-row-in-kernel", "few-row-prep", "few-row-two-tiles",
+                              "mfma"])
 def test_graph_replays_match_eager(M, H, I, spec):
     """The forward recorded into a HIP graph (after an eager call, so the
     workspace exists) and replayed several times, with other eager work and
