@@ -40,7 +40,11 @@
  * weights' extra rows and scale tiles: the library keeps one per (device, stream),
  * allocated on first use and grown (never shrunk) when a call needs more;
  * growth synchronises that stream once.  swiglu_q_release_workspace() frees
- * them.
+ * them.  HIP graphs: a call recorded into a graph must not need to grow a
+ * buffer (allocation and synchronisation cannot be captured; such a call
+ * returns SWQ_ERR_HIP or SWQ_ERR_WORKSPACE), so make one call of the largest
+ * shape on the same stream before capturing; the kernels write every output
+ * element and need no clearing between replays.
  *
  * Exactness: the weights are dequantized exactly (no rounding of s·q + b);
  * gate and up are float32 dot products.  This holds when every scale and
