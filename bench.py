@@ -632,7 +632,7 @@ def main():
                                   "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None}})
     if args.workload == "decode" and not args.no_small_batch:
         log("decode, a few rows per call: timing ...")
-        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4)}
+        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32)}
         torch.cuda.empty_cache()
     if not args.no_prefill:
         pre = {}
