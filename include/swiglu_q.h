@@ -185,6 +185,12 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);
 
+/* The path (SWQ_PATH_GEMV or SWQ_PATH_MFMA) a call with M rows and hidden
+ * size H takes under the current threshold, by the same rule as the calls
+ * (M < T and M <= 32 take the matrix-vector path); -1 for M < 1 or H < 1.
+ * Host only: touches no device. */
+int swiglu_q_path_for(int64_t M, int64_t H);
+
 /* Number of forward (and debug) calls that launched each path since load
  * or the last reset.  path: SWQ_PATH_GEMV or SWQ_PATH_MFMA. */
 uint64_t swiglu_q_call_count(int path);

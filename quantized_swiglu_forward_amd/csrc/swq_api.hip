@@ -92,6 +92,13 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
   return SWQ_OK;
 }
 
+bool gemv_fits(int64_t M, int64_t H);
+
+// The dispatcher's rule.
+int auto_path(int64_t M, int64_t H) {
+  return (M < threshold_now() && gemv_fits(M, H)) ? SWQ_PATH_GEMV : SWQ_PATH_MFMA;
+}
+
 bool gemv_fits(int64_t M, int64_t H) {
   (void)H;
   return M >= 1 && M <= kGemvMaxM;
@@ -218,7 +225,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
-    path = (M < threshold_now() && gemv_fits(M, H)) ? SWQ_PATH_GEMV : SWQ_PATH_MFMA;
+    path = auto_path(M, H);
   }
   if (path == SWQ_PATH_GEMV && !gemv_fits(M, H)) return SWQ_ERR_UNSUPPORTED;
 
@@ -406,6 +413,11 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u, in
 void swiglu_q_set_m_threshold(int T) { g_threshold.store(T < 0 ? 0 : T); }
 
 int swiglu_q_get_m_threshold(void) { return threshold_now(); }
+
+int swiglu_q_path_for(int64_t M, int64_t H) {
+  if (M < 1 || H < 1) return -1;
+  return auto_path(M, H);
+}
 
 uint64_t swiglu_q_call_count(int path) {
   if (path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return 0;

@@ -189,6 +189,29 @@ def test_threshold_roundtrip():
         swq.swiglu_q_set_m_threshold(old)
 
 
+def test_dispatcher_choice_given_m_and_threshold():
+    """M < T takes the matrix-vector path while it fits (M <= 32), else the
+    MFMA path; T <= 1 sends everything to MFMA; invalid sizes give -1."""
+    old = swq.swiglu_q_get_m_threshold()
+    try:
+        swq.swiglu_q_set_m_threshold(33)
+        for M in (1, 2, 4, 5, 16, 17, 32):
+            assert swq.swiglu_q_path_for(M, 2048) == swq.SWQ_PATH_GEMV, M
+        for M in (33, 64, 2048):
+            assert swq.swiglu_q_path_for(M, 2048) == swq.SWQ_PATH_MFMA, M
+        swq.swiglu_q_set_m_threshold(9)
+        assert swq.swiglu_q_path_for(8, 4096) == swq.SWQ_PATH_GEMV
+        assert swq.swiglu_q_path_for(9, 4096) == swq.SWQ_PATH_MFMA
+        swq.swiglu_q_set_m_threshold(100)
+        assert swq.swiglu_q_path_for(32, 256) == swq.SWQ_PATH_GEMV
+        assert swq.swiglu_q_path_for(33, 256) == swq.SWQ_PATH_MFMA   # past the matrix-vector limit
+        swq.swiglu_q_set_m_threshold(1)
+        assert swq.swiglu_q_path_for(1, 2048) == swq.SWQ_PATH_MFMA
+        assert swq.swiglu_q_path_for(0, 2048) == -1 and swq.swiglu_q_path_for(4, 0) == -1
+    finally:
+        swq.swiglu_q_set_m_threshold(old)
+
+
 def test_threshold_default_from_environment():
     code = ("import quantized_swiglu_forward_amd as s; print(s.swiglu_q_get_m_threshold())")
     env = dict(os.environ, SWIGLU_Q_MMIN="13")
