@@ -202,6 +202,26 @@ def test_full_size_sampled(cfg, mode):
     assert np.all(np.isfinite(y))
 
 
+# large extents: H at 64 K inputs on every kernel (x' and the weight rows
+# addressed with 32-bit offsets far from 0), M beyond 65,536 rows, I beyond
+# 100 K columns, sampled outputs against the oracle
+LARGE = [(1, 65536, 100, (4, 64, 4, 64), GEMV), (4, 65536, 70, (8, 32, 4, 128), GEMV),
+         (64, 65536, 200, (4, 64, 8, 64), MFMA), (70000, 256, 96, (4, 64, 4, 64), MFMA),
+         (3, 1024, 120000, (4, 32, 4, 64), GEMV), (2, 4096, 40000, (4, 64, 4, 64), GEMV)]
+
+
+@pytest.mark.parametrize("M,H,I,spec,path", LARGE, ids=[f"M{c[0]}-H{c[1]}-I{c[2]}" for c in LARGE])
+def test_large_extents_sampled(M, H, I, spec, path):
+    p = make_custom(M, H, I, *spec, seed=M + I)
+    mode = (M + I) % 3
+    say("large extents", M, H, I, spec, "mode", mode, "path", path)
+    y = device_forward(p, mode, path)
+    ms, ns = sample_pairs(M, I, 600, seed=H)
+    o = oracle_pairs(p, mode, ms, ns)
+    check(y[ms, ns], o, mode, f"large M{M} H{H} I{I}")
+    assert np.all(np.isfinite(y))
+
+
 # -------------------------------------------------- pre-epilogue gate / up --
 
 @pytest.mark.parametrize("path", [GEMV, MFMA])
