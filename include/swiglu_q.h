@@ -180,7 +180,7 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
  * always runs the MFMA path.  The default comes from the environment
  * variable SWIGLU_Q_MMIN when set to a positive integer, else the built-in
  * default 33 (measured: the matrix-vector path is faster for every M <= 32
- * but at the largest weight shape measured, where it is within 3 %).
+ * on every weight shape measured).
  * T <= 1 sends every M >= 1 to the MFMA path. */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);

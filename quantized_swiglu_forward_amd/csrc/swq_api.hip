@@ -12,8 +12,7 @@
 // of 32, H a multiple of 32).  Here the default is 33: measured on this GPU,
 // the matrix-vector kernels beat the matrix-matrix kernel for every M <= 16
 // (2-3x on the decode and prefill weight shapes) and for M <= 32 on every
-// weight shape measured but the largest (within 3 % there), and 32 rows (two
-// 16-row MFMA tiles) is their limit.
+// weight shape measured, and 32 rows (two 16-row MFMA tiles) is their limit.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>

@@ -497,7 +497,7 @@ constexpr int kSkinnyMaxWaves = 16;
 template <int BITS_G, int BITS_U, int RT>
 struct SkinnyChunk {
   u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[RT][4];
-  float sg, bg, su, bu;
+  uint32_t sg, bg, su, bu;   // raw bf16 bits, converted where used (after every load is issued)
   bool live;
 };
 
@@ -549,13 +549,11 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
     };
     codes(mg.w, og, d.cg, std::integral_constant<int, BITS_G>{});
     codes(mu.w, ou, d.cu, std::integral_constant<int, BITS_U>{});
-    // a chunk past the end gets zero scales and biases: its B operands vanish
     const int gg = (r * mg.ng + ((32 * cc) >> mg.lg_gs)) * 2, gu = (r * mu.ng + ((32 * cc) >> mu.lg_gs)) * 2;
-    const float keep = d.live ? 1.0f : 0.0f;
-    d.sg = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mg.s, gg, 0, 0));
-    d.bg = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mg.b, gg, 0, 0));
-    d.su = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0));
-    d.bu = keep * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0));
+    d.sg = __builtin_amdgcn_raw_buffer_load_b16(mg.s, gg, 0, 0);
+    d.bg = __builtin_amdgcn_raw_buffer_load_b16(mg.b, gg, 0, 0);
+    d.su = __builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0);
+    d.bu = __builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0);
     if constexpr (!STAGE) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -564,6 +562,8 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
         for (int q = 0; q < 4; ++q) d.x[t][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
       }
     }
+    // every load of the chunk is in flight before the first use of any of them
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int c = min(4 * quad + h, nchunk - 1);
@@ -609,17 +609,21 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
     au[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   }
   auto compute = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    // a chunk past the end gets zero scales and biases: its B operands vanish
+    const float keep = d.live ? 1.0f : 0.0f;
+    const float sg = keep * bf16_to_f32((uint16_t)d.sg), bg = keep * bf16_to_f32((uint16_t)d.bg);
+    const float su = keep * bf16_to_f32((uint16_t)d.su), bu = keep * bf16_to_f32((uint16_t)d.bu);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f16x8 a[RT];
 #pragma unroll
       for (int t = 0; t < RT; ++t) a[t] = __builtin_bit_cast(f16x8, d.x[t][kb]);
-      block_mfma.template operator()<BITS_G>(d.cg, d.sg, kb, a, ag);
-      block_mfma.template operator()<BITS_U>(d.cu, d.su, kb, a, au);
+      block_mfma.template operator()<BITS_G>(d.cg, sg, kb, a, ag);
+      block_mfma.template operator()<BITS_U>(d.cu, su, kb, a, au);
     }
     // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
     const _Float16 z0 = (_Float16)0.0f;
-    const float cgf = fmaf(CodeOffset<BITS_G>::z, d.sg, d.bg), cuf = fmaf(CodeOffset<BITS_U>::z, d.su, d.bu);
+    const float cgf = fmaf(CodeOffset<BITS_G>::z, sg, bg), cuf = fmaf(CodeOffset<BITS_U>::z, su, bu);
     const _Float16 cgh = (_Float16)cgf, cgl = (_Float16)(cgf - (float)cgh);
     const _Float16 cuh = (_Float16)cuf, cul = (_Float16)(cuf - (float)cuh);
     const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
