@@ -127,14 +127,23 @@ __device__ __forceinline__ void prep_ext_chunk(const uint16_t* S, const uint16_t
                                                int ngroups, int kext, _Float16* dst, int64_t n, int c) {
   const int ng = ngroups >> (lg_gs - lg_g0);         // groups of this matrix per row
   const float z = bits == 8 ? 136.0f : 8.0f;
+  // all sixteen loads first (indices clamped into the row), then the
+  // arithmetic: one memory round trip instead of eight
+  uint16_t sv[8], bv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int G = min(8 * c + j, ngroups - 1);
+    const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
+    sv[j] = S[gi];
+    bv[j] = B[gi];
+  }
   f16x8 h[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int G = 8 * c + j;
     _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
     if (G < ngroups) {
-      const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
-      const float cv = fmaf(z, bf16_to_f32(S[gi]), bf16_to_f32(B[gi]));
+      const float cv = fmaf(z, bf16_to_f32(sv[j]), bf16_to_f32(bv[j]));
       chi = (_Float16)cv;
       clo = (_Float16)(cv - (float)chi);
     }
@@ -163,20 +172,40 @@ __device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, 
   const int tid = threadIdx.x;
   const int s_main = p.H >> 5;
   const int64_t n0 = (int64_t)tile * kScaleTileCols;
+  // all loads of both matrices first (indices clamped into the matrix; a
+  // matrix without rows, the linear's up slot at N = 1, loads nothing), then
+  // the LDS writes: one memory round trip
+  constexpr int KL = kScaleTileCols * kScaleBlockGroups / 256;
+  uint16_t v[2][KL];
 #pragma unroll
   for (int mat = 0; mat < 2; ++mat) {
     const int lg_gs = __builtin_ctz(mat ? p.gs_u : p.gs_g);
     const uint16_t* S = mat ? p.su : p.sg;
     const int ng = p.H >> lg_gs;
+    const int rows = mat ? p.I_u : p.I;
     const int lg_gpb = __builtin_ctz(kScaleBlockSteps * 128) - lg_gs;   // groups per block: 256 / gs
     const int g0 = jb << lg_gpb;
 #pragma unroll
-    for (int k = 0; k < kScaleTileCols * kScaleBlockGroups / 256; ++k) {
+    for (int k = 0; k < KL; ++k) {
+      const int i = tid + 256 * k;
+      const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
+      const int64_t n = min(n0 + row, (int64_t)rows - 1);
+      v[mat][k] = rows > 0 ? S[n * ng + min(g0 + g, ng - 1)] : (uint16_t)0;
+    }
+  }
+#pragma unroll
+  for (int mat = 0; mat < 2; ++mat) {
+    const int lg_gs = __builtin_ctz(mat ? p.gs_u : p.gs_g);
+    const int ng = p.H >> lg_gs;
+    const int rows = mat ? p.I_u : p.I;
+    const int lg_gpb = __builtin_ctz(kScaleBlockSteps * 128) - lg_gs;
+    const int g0 = jb << lg_gpb;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
       const int i = tid + 256 * k;
       if (i < (kScaleTileCols << lg_gpb)) {
         const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
-        const int64_t n = n0 + row;
-        src[mat][row][g] = (n < (mat ? p.I_u : p.I) && g0 + g < ng) ? S[n * ng + g0 + g] : (uint16_t)0;
+        src[mat][row][g] = (n0 + row < rows && g0 + g < ng) ? v[mat][k] : (uint16_t)0;
       }
     }
   }
