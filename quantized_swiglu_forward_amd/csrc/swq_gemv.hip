@@ -445,12 +445,18 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
       gm[m] = row_sum(t);
       um[m] = upper_half(gm[m]);
     }
-    const int col = lane >> 4;
+    // every lane of a 16-lane row holds its column's sums of every row:
+    // lane 16 col + m runs the epilogue of row m, all rows at once
+    const int col = lane >> 4, mrow = lane & 15;
     const int64_t n = (int64_t)wave_global * R + col;
-    if ((lane & 15) == 0 && col < R && n < p.I) {
+    float g = gm[0], u = um[0];
 #pragma unroll
-      for (int m = 0; m < MR; ++m) store_out(p, m, (int)n, gm[m], um[m]);
-    }
+    for (int m = 1; m < MR; ++m)
+      if (mrow == m) {
+        g = gm[m];
+        u = um[m];
+      }
+    if (mrow < MR && col < R && n < p.I) store_out(p, mrow, (int)n, g, u);
   } else {
     XChunk xc[CPL];
 #pragma unroll
