@@ -704,22 +704,20 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
     red[w][2 * t + 1][lane] = au[t];
   }
   __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      f32x4 g = red[0][2 * t][lane], u = red[0][2 * t + 1][lane];
-      for (int ww = 1; ww < nw; ++ww) {
-        g += red[ww][2 * t][lane];
-        u += red[ww][2 * t + 1][lane];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = 16 * t + 4 * h + j;
-        if (m < p.M && col < p.I) {
-          const int e = STAGE ? xe[m] : p.xexp[m];
-          store_out(p, m, col, ldexpf(g[j], e), ldexpf(u[j], e));
-        }
-      }
+  // element j of D (row 16 t + 4 h + j) of tile t: wave 4 t + j sums it over
+  // the waves (in wave order) and runs its epilogue, so the 4 RT epilogues
+  // of a lane run on different waves at once
+  for (int k = w; k < 4 * RT; k += nw) {
+    const int t = k >> 2, j = k & 3;
+    float g = 0.0f, u = 0.0f;
+    for (int ww = 0; ww < nw; ++ww) {
+      g += red[ww][2 * t][lane][j];
+      u += red[ww][2 * t + 1][lane][j];
+    }
+    const int m = 16 * t + 4 * h + j;
+    if (m < p.M && col < p.I) {
+      const int e = STAGE ? xe[m] : p.xexp[m];
+      store_out(p, m, col, ldexpf(g, e), ldexpf(u, e));
     }
   }
 }
