@@ -493,7 +493,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // whole decode-sized grid is resident at once.  A fifth MFMA per chunk adds
 // the bias term sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c
 // each split into binary16 hi + lo, as on the matrix-matrix path.  The waves'
-// partial sums meet in LDS; wave 0 applies 2^e and the epilogue.  x' comes
+// partial sums meet in LDS; wave 4 t + j sums element j of row tile t, applies
+// 2^e and runs that row's epilogue.  x' comes
 // from the prep kernel, or (STAGE, M*H at most kSkinnyStageMax) every block
 // builds it itself in LDS with the prep kernel's row powers of two,
 // conversion and layout, so the call is one launch.
