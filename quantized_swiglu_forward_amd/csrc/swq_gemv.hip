@@ -510,6 +510,8 @@ struct SkinnyChunk {
 
 // RT: row tiles of 16 (M <= 16 RT = 1; M <= 32 RT = 2, whose second tile of x'
 // and accumulators need twice the registers: half the waves per SIMD)
+template <int BITS_G, int BITS_U, int RT>
+inline constexpr bool kTwoQuads = RT == 2 && BITS_G <= 4 && BITS_U <= 4;
 template <int BITS_G, int BITS_U, bool STAGE, int RT>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
 __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
@@ -689,11 +691,22 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
       load_x_lds(q0, d);
       compute(d);
     }
-  } else {
+  } else if constexpr (!kTwoQuads<BITS_G, BITS_U, RT>) {
     for (int q0 = w; q0 < nquad; q0 += nw) {
       SkinnyChunk<BITS_G, BITS_U, RT> d;
       load(q0, d);
       compute(d);
+    }
+  } else {
+    // two row tiles (codes of at most 4 bits, so that two chunk records fit
+    // the registers): two chunk quads in flight per wave, half the waves (a
+    // quad past the end loads chunk 0 with zero scales and adds nothing)
+    for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
+      SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
+      load(q0, d0);
+      load(q0 + nw, d1);
+      compute(d0);
+      compute(d1);
     }
   }
 
@@ -823,9 +836,12 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     return full ? launch_gemv1_rows_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false>(p, r, stream);
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
-  // one wave per chunk quad, at most kSkinnyMaxWaves per block of 16 columns
+  // one wave per chunk quad (two quads with two row tiles, x' from the prep
+  // kernel), at most kSkinnyMaxWaves per block of 16 columns
   const int quads = (p.H / 32 + 3) / 4;
-  const int waves = quads < kSkinnyMaxWaves ? quads : kSkinnyMaxWaves;
+  const bool two = p.M > 16 && p.xa != nullptr && kTwoQuads<BG, BU, 2>;
+  const int per = two ? (quads + 1) / 2 : quads;
+  const int waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
   const dim3 g((p.I + 15) / 16), b(64 * waves);
   if (p.xa == nullptr) {
     if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
