@@ -509,12 +509,13 @@ struct SkinnyChunk {
 };
 
 // RT: row tiles of 16 (M <= 16 RT = 1; M <= 32 RT = 2, whose second tile of x'
-// and accumulators need twice the registers: half the waves per SIMD)
-template <int BITS_G, int BITS_U, int RT>
-inline constexpr bool kTwoQuads = RT == 2 && BITS_G <= 4 && BITS_U <= 4;
-template <int BITS_G, int BITS_U, bool STAGE, int RT>
+// and accumulators need twice the registers: half the waves per SIMD).  Q2:
+// two chunk quads in flight per wave (codes of at most 4 bits, x' from the
+// prep kernel), with half the waves per SIMD.
+template <int BITS_G, int BITS_U, bool STAGE, int RT, bool Q2>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+  static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_U <= 4), "two quads in flight: narrow codes, prep-fed x'");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -691,16 +692,15 @@ __attribute__((amdgpu_waves_per_eu((BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) 
       load_x_lds(q0, d);
       compute(d);
     }
-  } else if constexpr (!kTwoQuads<BITS_G, BITS_U, RT>) {
+  } else if constexpr (!Q2) {
     for (int q0 = w; q0 < nquad; q0 += nw) {
       SkinnyChunk<BITS_G, BITS_U, RT> d;
       load(q0, d);
       compute(d);
     }
   } else {
-    // two row tiles (codes of at most 4 bits, so that two chunk records fit
-    // the registers): two chunk quads in flight per wave, half the waves (a
-    // quad past the end loads chunk 0 with zero scales and adds nothing)
+    // two chunk quads in flight per wave, half the waves (a quad past the
+    // end loads chunk 0 with zero scales and adds nothing)
     for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
       SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
       load(q0, d0);
@@ -839,17 +839,23 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   // one wave per chunk quad (two quads with two row tiles, x' from the prep
   // kernel), at most kSkinnyMaxWaves per block of 16 columns
   const int quads = (p.H / 32 + 3) / 4;
-  const bool two = p.M > 16 && p.xa != nullptr && kTwoQuads<BG, BU, 2>;
+  // two quads in flight: measured faster with two row tiles everywhere, and
+  // with one up to H = 2048 (slower beyond, at half the waves per SIMD)
+  constexpr bool kNarrow = BG <= 4 && BU <= 4;
+  const bool two = kNarrow && p.xa != nullptr && (p.M > 16 || p.H <= 2048);
   const int per = two ? (quads + 1) / 2 : quads;
   const int waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
   const dim3 g((p.I + 15) / 16), b(64 * waves);
   if (p.xa == nullptr) {
     if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
-    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 1>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 2>), g, b, 0, stream, p);
-  } else {
-    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2>), g, b, 0, stream, p);
+    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 1, false>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 2, false>), g, b, 0, stream, p);
+  } else if (!two) {
+    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1, false>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2, false>), g, b, 0, stream, p);
+  } else if constexpr (kNarrow) {
+    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1, true>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2, true>), g, b, 0, stream, p);
   }
   return hipGetLastError();
 }
