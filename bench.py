@@ -602,7 +602,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
-              "the fused SwiGLU library runs on one GPU (a multi-GPU layout would shard I; see the design notes).", file=sys.stderr)
+              "the fused SwiGLU library runs on one GPU (a multi-GPU layout would shard the I dimension).", file=sys.stderr)
         sys.exit(2)
 
     import torch
