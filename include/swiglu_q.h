@@ -36,22 +36,30 @@
  * and the call returns without synchronising.  A matrix-vector call with
  * M*H > 8192 (other than M = 1 with H <= 8192, and 2 <= M <= 4 with
  * 2048 <= H <= 4096) needs a device workspace for the staged x, and every
- * matrix-matrix call needs one for x and the
- * weights' extra rows and scale tiles: the library keeps one per (device, stream),
- * allocated on first use and grown (never shrunk) when a call needs more;
- * growth synchronises that stream once.  swiglu_q_release_workspace() frees
- * them.  HIP graphs: a call recorded into a graph must not need to grow a
- * buffer (allocation and synchronisation cannot be captured; such a call
+ * matrix-matrix call needs one for x and the weights' extra rows, scale tiles
+ * and row exponents: the library keeps one per (device, stream), allocated on
+ * first use and replaced by a larger one (at least twice the size) when a call
+ * needs more.  Growth never synchronises: a replaced buffer is kept, not freed,
+ * until swiglu_q_release_workspace(), so work already queued on the stream and
+ * HIP graphs captured while it was current still have valid memory.  Calls and
+ * graph replays that use one stream's workspace must not run at the same time
+ * (on that stream they are ordered).  HIP graphs: a call recorded into a graph
+ * must not need to grow a buffer (allocation cannot be captured; such a call
  * returns SWQ_ERR_HIP or SWQ_ERR_WORKSPACE), so make one call of the largest
  * shape on the same stream before capturing; the kernels write every output
  * element and need no clearing between replays.
  *
- * Exactness: the weights are dequantized exactly (no rounding of s·q + b);
- * gate and up are float32 dot products.  This holds when every scale and
- * bias is zero or has magnitude in [2^-17, 2^8) (the range in which a bf16
- * value times a code offset of at most 2^(bits-1) stays exactly
- * representable in binary16); outside that range the dequantized weight is
- * rounded to binary16.
+ * Exactness: the weights are dequantized exactly (no rounding of s·q + b), and
+ * gate and up are float32 dot products, for any finite bf16 scales and biases.
+ * Before a kernel forms 16-bit operands it multiplies each weight row's scales
+ * and constants (c = b + z·s, z the code offset 8, or 136 for 8-bit codes) by a
+ * power of two of that row's own, chosen from the row's largest |s|·(largest
+ * code offset) and |c|, and multiplies the row's sums back at the end.  Every
+ * group whose largest such term is at least 2^-28 (8-bit codes: 2^-24) of the
+ * row's largest is then exact in binary16; a smaller group's weights are
+ * rounded to binary16's grid at the row's scale, an error below 2^-39 of the
+ * row's largest term per weight.  Results are finite whenever the float32
+ * sums are (the M = 1 kernel applies s and b in float32 throughout).
  *
  * Errors: every entry point validates its arguments on the host before any
  * HIP call and returns a status; nothing is launched on error.
@@ -192,7 +200,10 @@ int swiglu_q_get_m_threshold(void);
 int swiglu_q_path_for(int64_t M, int64_t H);
 
 /* Number of forward (and debug) calls that launched each path since load
- * or the last reset.  path: SWQ_PATH_GEMV or SWQ_PATH_MFMA. */
+ * or the last reset.  path: SWQ_PATH_GEMV or SWQ_PATH_MFMA.  Mirrors the
+ * pages' dispatch counter, which a gate test asserts on to prove that the
+ * kernel ran ("mlx-bun 0.0.7 -> 0.0.9" diff, page 42, fused-swiglu-kernel.ts,
+ * dispatch counter). */
 uint64_t swiglu_q_call_count(int path);
 void swiglu_q_reset_counts(void);
 
@@ -200,7 +211,10 @@ void swiglu_q_reset_counts(void);
 const char *swiglu_q_strerror(int status);
 
 /*
- * Test hook: the pre-epilogue gate and up projections in float32,
+ * Test hook (the pages' debug-gate switch, which writes the raw gate
+ * projection instead of hidden: "mlx-bun 0.0.7 -> 0.0.9" diff, page 42,
+ * fused-swiglu-kernel.ts, kernel source): the pre-epilogue gate and up
+ * projections in float32,
  * gate_out[M, I] and up_out[M, I] (device pointers, caller-owned), computed
  * by the kernel of `path` (SWQ_PATH_AUTO = what the dispatcher would pick).
  * Same validation and status codes as swiglu_q_forward.

@@ -163,36 +163,59 @@ strerror = swiglu_q_strerror
 
 
 # ---- tensor conveniences ----------------------------------------------------
+#
+# Like the pages' host entry, these take activations of any leading shape
+# [..., H]: the leading dimensions are collapsed into M rows (which must then be
+# one contiguous [M, H] block) and restored on the output ("mlx-bun 0.0.7 ->
+# 0.0.9" diff, page 42, fused-swiglu-kernel.ts, host entry).
+
+_BITS16 = ("torch.bfloat16", "torch.int16", "torch.uint16")
+
+
+def _rows(x, what):
+    """(x as [M, H], leading shape) for bf16 activations (or their int16/uint16
+    bit patterns); raises for any other dtype or a non-contiguous tensor."""
+    if str(x.dtype) not in _BITS16:
+        raise TypeError(f"{what}: x must be bfloat16 (or its 16-bit patterns), not {x.dtype}")
+    if x.dim() < 1:
+        raise ValueError(f"{what}: x needs at least one dimension")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: x must be contiguous (rows are read without strides)")
+    lead = tuple(x.shape[:-1])
+    return x.reshape(-1, x.shape[-1]), lead
+
 
 def forward(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_u=None,
             mode=SWQ_MATCH, out=None, stream=None):
-    """``hidden`` for device tensors: x [M, H] (bf16 or int16/uint16 bit
+    """``hidden`` for device tensors: x [..., H] (bf16 or int16/uint16 bit
     patterns), packed codes int32/uint32 [I, H*bits/32], scales/biases bf16
-    [I, H/gs].  Returns ``out`` ([M, I], bf16 or float32 by mode)."""
+    [I, H/gs].  Returns ``out`` ([..., I], bf16 or float32 by mode)."""
     import torch
     bits_u = bits_g if bits_u is None else bits_u
     gs_u = gs_g if gs_u is None else gs_u
-    M, H = int(x.shape[0]), int(x.shape[1])
+    x2, lead = _rows(x, "forward")
+    M, H = int(x2.shape[0]), int(x2.shape[1])
     I = int(wg.shape[0])
     if out is None:
         dt = torch.float32 if mode == SWQ_F32 else torch.bfloat16
-        out = torch.empty((M, I), dtype=dt, device=x.device)
-    rc = swiglu_q_forward(x, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
+        out = torch.empty(lead + (I,), dtype=dt, device=x.device)
+    rc = swiglu_q_forward(x2, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
     if rc != SWQ_OK:
         raise SwigluQError(rc, "swiglu_q_forward")
     return out
 
 
 def linear(x, w, s, b, bits, gs, out_mode=SWQ_LINEAR_BF16, out=None, stream=None):
-    """``x W^T`` for device tensors: x [M, K] bf16, packed codes [N, K*bits/32],
-    scales/biases bf16 [N, K/gs].  Returns ``out`` ([M, N], bf16 or float32)."""
+    """``x W^T`` for device tensors: x [..., K] bf16, packed codes [N, K*bits/32],
+    scales/biases bf16 [N, K/gs].  Returns ``out`` ([..., N], bf16 or float32)."""
     import torch
-    M, K = int(x.shape[0]), int(x.shape[1])
+    x2, lead = _rows(x, "linear")
+    M, K = int(x2.shape[0]), int(x2.shape[1])
     N = int(w.shape[0])
     if out is None:
         dt = torch.float32 if out_mode == SWQ_LINEAR_F32 else torch.bfloat16
-        out = torch.empty((M, N), dtype=dt, device=x.device)
-    rc = swiglu_q_linear(x, w, s, b, M, K, N, bits, gs, out_mode, out, stream)
+        out = torch.empty(lead + (N,), dtype=dt, device=x.device)
+    rc = swiglu_q_linear(x2, w, s, b, M, K, N, bits, gs, out_mode, out, stream)
     if rc != SWQ_OK:
         raise SwigluQError(rc, "swiglu_q_linear")
     return out
@@ -201,15 +224,21 @@ def linear(x, w, s, b, bits, gs, out_mode=SWQ_LINEAR_BF16, out=None, stream=None
 def mlp(x, wg, sg, bg, wu, su, bu, wd, sd, bd, spec_g, spec_u, spec_d, residual=None,
         out_mode=SWQ_LINEAR_BF16, out=None, stream=None):
     """``residual + (silu(x Wg^T) * (x Wu^T)) Wd^T`` for device tensors; each
-    spec is (bits, group size); Wd is [Ho, I*bits_d/32].  Returns ``out``
-    ([M, Ho], bf16 or float32 by out_mode)."""
+    spec is (bits, group size); Wd is [Ho, I*bits_d/32]; x is [..., H] and the
+    residual, when given, bf16 [..., Ho].  Returns ``out`` ([..., Ho], bf16 or
+    float32 by out_mode)."""
     import torch
-    M, H = int(x.shape[0]), int(x.shape[1])
+    x2, lead = _rows(x, "mlp")
+    M, H = int(x2.shape[0]), int(x2.shape[1])
     I, Ho = int(wg.shape[0]), int(wd.shape[0])
+    if residual is not None:
+        residual, rlead = _rows(residual, "mlp residual")
+        if rlead != lead or int(residual.shape[1]) != Ho:
+            raise ValueError(f"mlp: residual must be [..., {Ho}] with x's leading shape {lead}")
     if out is None:
         dt = torch.float32 if out_mode == SWQ_LINEAR_F32 else torch.bfloat16
-        out = torch.empty((M, Ho), dtype=dt, device=x.device)
-    rc = swiglu_q_mlp(x, wg, sg, bg, wu, su, bu, wd, sd, bd, residual, M, H, I, Ho, spec_g[0], spec_g[1],
+        out = torch.empty(lead + (Ho,), dtype=dt, device=x.device)
+    rc = swiglu_q_mlp(x2, wg, sg, bg, wu, su, bu, wd, sd, bd, residual, M, H, I, Ho, spec_g[0], spec_g[1],
                       spec_u[0], spec_u[1], spec_d[0], spec_d[1], out_mode, out, stream)
     if rc != SWQ_OK:
         raise SwigluQError(rc, "swiglu_q_mlp")
@@ -222,6 +251,7 @@ def debug_gemm_tensors(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_
     import torch
     bits_u = bits_g if bits_u is None else bits_u
     gs_u = gs_g if gs_u is None else gs_u
+    x, _ = _rows(x, "debug_gemm")
     M, H = int(x.shape[0]), int(x.shape[1])
     I = int(wg.shape[0])
     g = torch.empty((M, I), dtype=torch.float32, device=x.device)

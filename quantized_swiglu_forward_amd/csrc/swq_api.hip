@@ -22,6 +22,7 @@
 #include <mutex>
 #include <tuple>
 #include <utility>
+#include <vector>
 
 #include "../../include/swiglu_q.h"
 #include "swq_kernels.h"
@@ -42,6 +43,10 @@ struct Workspace {
 };
 // slot 0: the kernels' own staging; slot 1: the whole MLP's hidden tensor
 std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;
+// Buffers replaced by a larger one.  They stay allocated until
+// swiglu_q_release_workspace(): work already queued on the stream, and HIP
+// graphs captured while they were current, may still read and write them.
+std::vector<std::pair<int, void*>> g_retired;
 
 int threshold_now() {
   int t = g_threshold.load(std::memory_order_relaxed);
@@ -164,10 +169,10 @@ int choose_column_split(int64_t M, int64_t I, int cfg, int bits_g, int bits_u) {
 
 // Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
 // (binary16), row exponents [M] (int32), the extra-column B rows [I, kext]
-// (binary16) of the gate and of the up matrix, then the scale tiles
-// (4 KB per 128 columns and 128 inputs).
+// (binary16) of the gate and of the up matrix, the scale tiles (4 KB per
+// 128 columns and 128 inputs), then the weight rows' exponents k [2][I] (int32).
 struct WsLayout {
-  int64_t xa, xexp, eg, eu, sc, total;
+  int64_t xa, xexp, eg, eu, sc, kx, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -182,7 +187,8 @@ WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bi
   w.eu = w.eg + plane;
   w.sc = w.eu + plane;
   const int64_t tiles = (I + kScaleTileCols - 1) / kScaleTileCols * ((H + 127) / 128);
-  w.total = w.sc + align256(tiles * kScaleTileWords * 4);
+  w.kx = w.sc + align256(tiles * kScaleTileWords * 4);
+  w.total = w.kx + align256(2 * I * 4);
   (void)bits_g;
   (void)bits_u;
   return w;
@@ -194,20 +200,19 @@ int get_workspace(hipStream_t stream, size_t need, void** out, int slot = 0) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, (uintptr_t)stream, slot}];
   if (w.bytes < need) {
-    if (w.ptr) {
-      // the old buffer may still be read by work queued on this stream
-      if (hipStreamSynchronize(stream) != hipSuccess) return SWQ_ERR_HIP;
-      if (hipFree(w.ptr) != hipSuccess) return SWQ_ERR_HIP;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
+    // at least double, so that a sequence of growing calls retires a bounded
+    // total (under the size of the last buffer); no synchronisation: the old
+    // buffer is retired, not freed
     const size_t grain = 2u << 20;
-    const size_t bytes = (need + grain - 1) / grain * grain;
-    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+    const size_t want = need > 2 * w.bytes ? need : 2 * w.bytes;
+    const size_t bytes = (want + grain - 1) / grain * grain;
+    void* fresh = nullptr;
+    if (hipMalloc(&fresh, bytes) != hipSuccess) {
       (void)hipGetLastError();
-      w.ptr = nullptr;
       return SWQ_ERR_WORKSPACE;
     }
+    if (w.ptr) g_retired.emplace_back(dev, w.ptr);
+    w.ptr = fresh;
     w.bytes = bytes;
   }
   *out = w.ptr;
@@ -237,28 +242,36 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     p.I_u = (int)I_u; p.ldo = (int)ldo;
     p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
     p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
-    p.xa = nullptr; p.xexp = nullptr;
+    p.xa = nullptr; p.xexp = nullptr; p.kexp = nullptr;
     if (logging())
       fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
               (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
     (void)hipGetLastError();
     if (gemv_needs_rows(M, H)) {
       // x' rows [H/32][M][32] (the extra columns of 32-input groups ride along
-      // unused), then the row exponents
+      // unused), the row exponents, then the weight rows' exponents k [2][I]
+      // from the prep kernel's column blocks
       const int kext = kext_columns(H, 32);
       const int64_t xa_bytes = align256(M * (H + kext) * 2);
+      const int64_t xe_bytes = align256(M * 4);
       void* ws = nullptr;
-      int rc = get_workspace(stream, (size_t)(xa_bytes + align256(M * 4)), &ws);
+      int rc = get_workspace(stream, (size_t)(xa_bytes + xe_bytes + align256(2 * I * 4)), &ws);
       if (rc != SWQ_OK) return rc;
       PrepParams pp{};
       pp.x = (const uint16_t*)x;
-      pp.M = (int)M; pp.H = (int)H; pp.I = 0; pp.I_u = 0;
+      pp.sg = (const uint16_t*)sg; pp.bg = (const uint16_t*)bg;
+      pp.su = (const uint16_t*)su; pp.bu = (const uint16_t*)bu;
+      pp.M = (int)M; pp.H = (int)H; pp.I = (int)I; pp.I_u = (int)I_u;
       pp.gs_g = gs_g; pp.gs_u = gs_u; pp.bits_g = bits_g; pp.bits_u = bits_u;
       pp.g0 = 32; pp.ldx = (int)H + kext; pp.kext = kext;
       pp.xa = (_Float16*)ws;
       pp.xexp = (int*)((char*)ws + xa_bytes);
+      pp.kexp = (int*)((char*)ws + xa_bytes + xe_bytes);
+      pp.nss = (int)((H + 127) / 128);
+      pp.k_only = 1;
       p.xa = pp.xa;
       p.xexp = pp.xexp;
+      p.kexp = pp.kexp;
       if (launch_prep_rows(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
     }
     if (launch_gemv(p, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
@@ -291,6 +304,8 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.xa = xa; pp.xexp = xexp;
   pp.bext_g = eg; pp.bext_u = eu;
   pp.scl = scl; pp.nss = nss;
+  pp.kexp = (int*)(wsb + L.kx);
+  pp.k_only = 0;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;
@@ -303,6 +318,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.gs_g = gs_g; p.gs_u = gs_u;
   p.ldx = ldx; p.kext = kext;
   p.bext_g = eg; p.bext_u = eu;
+  p.kexp = pp.kexp;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
   {
     const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
@@ -453,14 +469,16 @@ int swiglu_q_release_workspace(void) {
   int rc = SWQ_OK;
   int prev = 0;
   (void)hipGetDevice(&prev);
-  for (auto& kv : g_ws) {
-    if (!kv.second.ptr) continue;
-    if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess) { rc = SWQ_ERR_HIP; continue; }
+  for (auto& kv : g_ws) g_retired.emplace_back(std::get<0>(kv.first), kv.second.ptr);
+  for (auto& r : g_retired) {
+    if (!r.second) continue;
+    if (hipSetDevice(r.first) != hipSuccess) { rc = SWQ_ERR_HIP; continue; }
     if (hipDeviceSynchronize() != hipSuccess) rc = SWQ_ERR_HIP;
-    if (hipFree(kv.second.ptr) != hipSuccess) rc = SWQ_ERR_HIP;
+    if (hipFree(r.second) != hipSuccess) rc = SWQ_ERR_HIP;
   }
   (void)hipSetDevice(prev);
   g_ws.clear();
+  g_retired.clear();
   return rc;
 }
 

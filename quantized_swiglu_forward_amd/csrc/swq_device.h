@@ -145,6 +145,29 @@ struct CodeOffset<4> { static constexpr float z = 8.0f; };
 template <>
 struct CodeOffset<8> { static constexpr float z = 136.0f; };
 
+// Weight-row exponent.  Every kernel that forms binary16 operands s (q - z)
+// and c = b + z s first multiplies a row's scales and constants by a power
+// of two 2^-k of its own: with m the largest over the row's groups of
+// |s| F and |c| (F the largest code offset times its plane weight: 8 for
+// codes of at most 4 bits, 128 for the 8-bit high plane 16 (hi - 8)) and m in
+// [2^E, 2^(E+1)), k = E - 14.  Every operand is then below 2^15 (finite in
+// binary16), the largest in [2^14, 2^15), and the row's sums are multiplied
+// by 2^k at the end.  A group whose own largest term is at least 2^-28 (8-bit:
+// 2^-24) of m keeps s 2^-k at or above 2^-17, where its 8 significant bits
+// times an offset of at most 3 significant bits are exact in binary16.
+template <int BITS>
+inline constexpr float kPlaneMax = kCodeWidth<BITS> == 8 ? 128.0f : 8.0f;
+
+__device__ __forceinline__ float group_term_max(float s, float b, float z, float F) {
+  return fmaxf(fabsf(s) * F, fabsf(fmaf(z, s, b)));
+}
+
+__device__ __forceinline__ int row_exponent_k(float m) {
+  if (!(m > 0.0f)) return 0;
+  const int E = __builtin_amdgcn_frexp_expf(m) - 1;     // m in [2^E, 2^(E+1))
+  return min(max(E - 14, -200), 200);
+}
+
 // sigma(t) = 1 / (1 + e^-t) with the hardware exp2 and reciprocal
 // (about 1 ulp each); e^-t overflows to +inf for t < about -88, giving
 // sigma = 0 and silu = -0.

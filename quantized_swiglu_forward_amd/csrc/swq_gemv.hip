@@ -542,6 +542,61 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   __shared__ int xe[kGemvMaxM];
   __shared__ uint32_t xmax[kGemvMaxM];
 
+  // Row exponents k of the block's 16 columns of both matrices
+  // (row_exponent_k): the scales and constants below are taken times 2^-k
+  // and the sums multiplied by 2^k in the epilogue.  With x' from the prep
+  // kernel, its column blocks computed them; with STAGE the block does:
+  // thread t scans column
+  // t % 16 of both matrices over groups t / 16, t / 16 + nt / 16, ...,
+  // loaded after the first weights (the block barrier below waits for the
+  // slowest wave's weights either way); the lanes of a column reduce with
+  // two swaps, and the waves meet in LDS.
+  __shared__ float kred[kSkinnyMaxWaves][32];
+  auto row_k_finish = [&]() {
+    const int kstride = blockDim.x >> 4;
+    float kmax_g = 0.0f, kmax_u = 0.0f;
+#pragma unroll 2
+    for (int g = tid >> 4; g < max(mg.ng, mu.ng); g += kstride) {
+      const int gg = min(g, mg.ng - 1), gu = min(g, mu.ng - 1);
+      const uint16_t s_g = __builtin_amdgcn_raw_buffer_load_b16(mg.s, (r * mg.ng + gg) * 2, 0, 0);
+      const uint16_t b_g = __builtin_amdgcn_raw_buffer_load_b16(mg.b, (r * mg.ng + gg) * 2, 0, 0);
+      const uint16_t s_u = __builtin_amdgcn_raw_buffer_load_b16(mu.s, (r * mu.ng + gu) * 2, 0, 0);
+      const uint16_t b_u = __builtin_amdgcn_raw_buffer_load_b16(mu.b, (r * mu.ng + gu) * 2, 0, 0);
+      if (g < mg.ng)
+        kmax_g = fmaxf(kmax_g, group_term_max(bf16_to_f32(s_g), bf16_to_f32(b_g), CodeOffset<BITS_G>::z,
+                                              kPlaneMax<BITS_G>));
+      if (g < mu.ng)
+        kmax_u = fmaxf(kmax_u, group_term_max(bf16_to_f32(s_u), bf16_to_f32(b_u), CodeOffset<BITS_U>::z,
+                                              kPlaneMax<BITS_U>));
+    }
+    kmax_g = fmaxf(kmax_g, __shfl_xor(kmax_g, 16));
+    kmax_g = fmaxf(kmax_g, __shfl_xor(kmax_g, 32));
+    kmax_u = fmaxf(kmax_u, __shfl_xor(kmax_u, 16));
+    kmax_u = fmaxf(kmax_u, __shfl_xor(kmax_u, 32));
+    if (lane < 16) {
+      kred[w][lane] = kmax_g;
+      kred[w][16 + lane] = kmax_u;
+    }
+  };
+  // this lane's column exponents: from the prep kernel (x' staged there),
+  // else from the block's own pass, after a barrier.  Both in one register
+  // (each in [-200, 200]): gate in the low half, up in the high half.
+  uint32_t kpack = 0;
+  auto set_k = [&](int kg_, int ku_) { kpack = ((uint32_t)kg_ & 0xFFFFu) | ((uint32_t)ku_ << 16); };
+  auto k_gate = [&]() { return (int)(int16_t)(kpack & 0xFFFFu); };
+  auto k_up = [&]() { return (int)kpack >> 16; };
+  if constexpr (!STAGE) {
+    if (col < p.I) set_k(p.kexp[col], p.kexp[p.I + col]);
+  }
+  auto row_k_read = [&]() {
+    float mg_ = 0.0f, mu_ = 0.0f;
+    for (int ww = 0; ww < nw; ++ww) {
+      mg_ = fmaxf(mg_, kred[ww][r]);
+      mu_ = fmaxf(mu_, kred[ww][16 + r]);
+    }
+    set_k(row_exponent_k(mg_), row_exponent_k(mu_));
+  };
+
   auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
@@ -620,9 +675,12 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   }
   auto compute = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     // a chunk past the end gets zero scales and biases: its B operands vanish
-    const float keep = d.live ? 1.0f : 0.0f;
-    const float sg = keep * bf16_to_f32((uint16_t)d.sg), bg = keep * bf16_to_f32((uint16_t)d.bg);
-    const float su = keep * bf16_to_f32((uint16_t)d.su), bu = keep * bf16_to_f32((uint16_t)d.bu);
+    // (scaled by the column's 2^-k)
+    const int kg_ = k_gate(), ku_ = k_up();
+    const float sg = d.live ? ldexpf(bf16_to_f32((uint16_t)d.sg), -kg_) : 0.0f;
+    const float bg = d.live ? ldexpf(bf16_to_f32((uint16_t)d.bg), -kg_) : 0.0f;
+    const float su = d.live ? ldexpf(bf16_to_f32((uint16_t)d.su), -ku_) : 0.0f;
+    const float bu = d.live ? ldexpf(bf16_to_f32((uint16_t)d.bu), -ku_) : 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f16x8 a[RT];
@@ -658,9 +716,11 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
     // the first quad's weights are in flight while the block builds x'
     SkinnyChunk<BITS_G, BITS_U, RT> d;
     if (w < nquad) load(w, d);
+    row_k_finish();
     const int nt = blockDim.x, nblk = p.M * (p.H >> 3);   // 8-value blocks of x
     if (tid < p.M) xmax[tid] = 0;
     __syncthreads();
+    row_k_read();
     for (int b = tid; b < nblk; b += nt) {              // row maxima of |x| (bf16 magnitude bits)
       const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + 8 * (int64_t)b);
       uint32_t amax = 0;
@@ -731,7 +791,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
     const int m = 16 * t + 4 * h + j;
     if (m < p.M && col < p.I) {
       const int e = STAGE ? xe[m] : p.xexp[m];
-      store_out(p, m, col, ldexpf(g, e), ldexpf(u, e));
+      store_out(p, m, col, ldexpf(g, e + k_gate()), ldexpf(u, e + k_up()));
     }
   }
 }

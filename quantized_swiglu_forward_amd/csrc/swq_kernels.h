@@ -33,6 +33,9 @@ struct PrepParams {
   _Float16* bext_u;    // out: same for the up matrix
   uint32_t* scl;       // out: scale tiles, see kScaleTileWords
   int nss;             // super-steps of 128 inputs: ceil(H / 128)
+  int* kexp;           // out: [2][I] row exponents k of the gate and up rows (scales and constants
+                       //      are stored times 2^-k; the sums are multiplied by 2^k)
+  int k_only;          // 1: the column blocks write kexp only (no extra-column rows, no scale tiles)
 };
 
 struct MfmaParams {
@@ -52,6 +55,7 @@ struct MfmaParams {
   int ldx, kext;
   const _Float16* bext_g;
   const _Float16* bext_u;
+  const int* kexp;     // [2][I] row exponents of the gate and up rows, from the prep kernel
   int mode;
   void* out;
   float* dbg_g;        // non-null: write float32 gate/up instead of hidden
@@ -79,6 +83,7 @@ struct GemvParams {
   const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
   const _Float16* xa;  // x' staged by the prep kernel, [H/32][M][32] (M*H > kSkinnyStageMax), or null
   const int* xexp;     // and its row exponents
+  const int* kexp;     // with xa: [2][I] weight-row exponents k from the prep kernel's column blocks
 };
 
 // Scale tiles: for every 128 output columns and every 128 inputs (a
@@ -114,7 +119,8 @@ inline int kext_columns(int64_t H, int g0) {
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
-// Only the x rows of the prep kernel (x' and row exponents), for the matrix-vector path.
+// The x rows of the prep kernel (x' and row exponents) and its column blocks
+// in k_only mode (weight-row exponents), for the matrix-vector path.
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // cfg: tile shape (kMfmaBM/kMfmaBN); n_split > 0 with cfg 0: columns
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.

@@ -8,14 +8,19 @@
 // Exactness.  A weight w = s*q + b is split as  s*(q - z) + c  with
 // c = b + z*s per group (z = 8 for 4-bit codes, and for 2-bit codes, which
 // are spread to nibbles and computed as 4-bit ones; for 8-bit codes
-// q = 16 hi + lo and s*q = 16s*(hi - 8) + s*(lo - 8) + 136 s).  Every
-// s*(code - 8) is exact in binary16 (a bf16 scale has 8 significant bits, the
-// offset code at most 4), so the K loop runs on f16 MFMA with exact products
-// and float32 accumulation.  The constant part sum_g Sx[m,g] * c[n,g] runs on
-// the same MFMAs as extra K columns: the group sum of x' (float32) split into
-// binary16 hi + lo, against c split into binary16 c_hi + c_lo, three columns
-// per group: (hi, hi, lo) x (c_hi, c_lo, c_hi); the dropped lo*c_lo term is
-// below 2^-22 of the group term.
+// q = 16 hi + lo and s*q = 16s*(hi - 8) + s*(lo - 8) + 136 s).  Each output
+// feature of each matrix first gets its own power of two 2^-k, chosen from
+// the row's largest |s| times code offset and largest |c| (see the column
+// blocks below), so that s 2^-k (code - 8) and c 2^-k are finite in binary16
+// and, with a bf16 scale's 8 significant bits and an offset of at most 4,
+// exact for every group within 2^28 (8-bit: 2^24) of the row's largest
+// term.  The K loop therefore runs on f16 MFMA with exact products and
+// float32 accumulation, and the epilogue multiplies by 2^k.  The constant
+// part sum_g Sx[m,g] * c[n,g] runs on the same MFMAs as extra K columns: the
+// group sum of x' (float32) split into binary16 hi + lo, against c 2^-k split
+// into binary16 c_hi + c_lo, three columns per group: (hi, hi, lo) x
+// (c_hi, c_lo, c_hi); the dropped lo*c_lo term is below 2^-22 of the group
+// term.
 //
 // Two kernels:
 //  1. swq_prep_kernel.  Blocks [0, M): one row of x each.  It picks a
@@ -24,14 +29,15 @@
 //     the dequantized weight pairs, and appends the extra columns
 //     (hi, hi, lo) of every group of g0 = min(gs_g, gs_u) inputs.  Every bf16
 //     x whose magnitude is at least 2^-17 of the row maximum converts
-//     exactly.  The next blocks write, for every output feature and matrix,
-//     the extra-column B rows (c_hi, c_lo, c_hi); the last ones the scale
-//     tiles (binary16 scale pairs per K-step, 128 columns at a time).
+//     exactly.  The column blocks then write, for 32 output features of both
+//     matrices each, the row exponents k, the extra-column B rows
+//     (c_hi, c_lo, c_hi) and the scale tiles (binary16 scale pairs per
+//     K-step, 128 columns at a time).
 //  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators over the
 //     H columns (packed codes, dequantized in registers) and then the extra
-//     columns (precomputed binary16 rows); epilogue 2^e, then silu(g) * u per
-//     precision mode, or the two projections as they are for the quantized
-//     linear (W's rows split between the gate and up slots).
+//     columns (precomputed binary16 rows); epilogue 2^(e + k), then
+//     silu(g) * u per precision mode, or the two projections as they are for
+//     the quantized linear (W's rows split between the gate and up slots).
 #include <type_traits>
 #include <utility>
 
@@ -116,34 +122,77 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
 }
 
-// Extra-column B rows, eight g0-groups per thread: thread (n, matrix, c)
-// writes bytes [48c, 48c + 48) of row n of one matrix -- groups 8c .. 8c+7,
-// three binary16 each, (c_hi, c_lo, c_hi) with c = b + z*s exactly in
-// float32 (b and z*s are bf16 values times small powers of two and 17) --
-// zeros past the last group, as three 16-byte stores.  A row is kext*2 bytes,
-// a multiple of 64, so each store lies wholly inside or outside it.  Group
-// sizes are powers of two: lg_* are their logarithms.
-__device__ __forceinline__ void prep_ext_chunk(const uint16_t* S, const uint16_t* B, int lg_gs, int bits, int lg_g0,
-                                               int ngroups, int kext, _Float16* dst, int64_t n, int c) {
-  const int ng = ngroups >> (lg_gs - lg_g0);         // groups of this matrix per row
-  const float z = bits == 8 ? 136.0f : 8.0f;
-  // all sixteen loads first (indices clamped into the row), then the
-  // arithmetic: one memory round trip instead of eight
-  uint16_t sv[8], bv[8];
+// Column blocks.  Block cb handles output features [32 cb, 32 cb + 32) of
+// both matrices: every thread-quad owns one (feature, matrix) row.
+//
+// 1. Row exponent k of each (feature, matrix) row (row_exponent_k): the
+//    row's scales and constants are stored times 2^-k, and the MFMA
+//    kernel's epilogue multiplies the sums by 2^k.
+// 2. Extra-column B rows: for eight g0-groups per slot, (c_hi, c_lo, c_hi)
+//    of c 2^-k split into two binary16 parts, zeros past the last group,
+//    three 16-byte stores per slot (a row is kext*2 bytes, a multiple of 64,
+//    so each store lies wholly inside or outside it).
+// 3. Scale tiles: for every super-step (128 inputs), the binary16 pair
+//    (s 2^-k, s 2^-k) of each column's group per K-step and matrix.  Columns
+//    past the matrix's rows and K-steps past H get zeros; the blocks cover
+//    whole 128-column tiles.
+constexpr int kColBlock = 32;                 // output features per column block
+constexpr int kSlotsReg = 4;                  // extra-column slots a thread keeps in registers
+constexpr int kPrepLdsGroups = 128;           // groups per row staged in LDS for the scale tiles
+
+struct RowSpec {
+  const uint16_t* S;
+  const uint16_t* B;
+  int lg_gs;      // log2 of the group size
+  int ng;         // groups per row
+  float z, F;     // code offset; largest |offset| times plane weight
+};
+
+__device__ __forceinline__ RowSpec row_spec(const PrepParams& p, int mat) {
+  RowSpec r;
+  const int gs = mat ? p.gs_u : p.gs_g, bits = mat ? p.bits_u : p.bits_g;
+  r.S = mat ? p.su : p.sg;
+  r.B = mat ? p.bu : p.bg;
+  r.lg_gs = __builtin_ctz(gs);
+  r.ng = p.H >> r.lg_gs;
+  r.z = bits == 8 ? 136.0f : 8.0f;
+  r.F = bits == 8 ? 128.0f : 8.0f;
+  return r;
+}
+
+// Raw scales and biases of the eight g0-groups of extra-column slot `slot`
+// of row n (indices clamped into the row).
+__device__ __forceinline__ void load_slot(const RowSpec& r, int64_t n, int lg_g0, int ngroups, int slot,
+                                          uint16_t (&sv)[8], uint16_t (&bv)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int G = min(8 * c + j, ngroups - 1);
-    const int64_t gi = n * ng + ((G << lg_g0) >> lg_gs);
-    sv[j] = S[gi];
-    bv[j] = B[gi];
+    const int G = min(8 * slot + j, ngroups - 1);
+    const int64_t gi = n * r.ng + ((G << lg_g0) >> r.lg_gs);
+    sv[j] = r.S[gi];
+    bv[j] = r.B[gi];
   }
+}
+
+__device__ __forceinline__ float slot_max(const RowSpec& r, int ngroups, int slot, const uint16_t (&sv)[8],
+                                          const uint16_t (&bv)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (8 * slot + j >= ngroups) continue;
+    m = fmaxf(m, group_term_max(bf16_to_f32(sv[j]), bf16_to_f32(bv[j]), r.z, r.F));
+  }
+  return m;
+}
+
+// (c_hi, c_lo, c_hi) of c 2^-k for the slot's eight g0-groups; c = b + z s in float32.
+__device__ __forceinline__ void store_slot(const RowSpec& r, int ngroups, int slot, int k, const uint16_t (&sv)[8],
+                                           const uint16_t (&bv)[8], int kext, unsigned char* row) {
   f16x8 h[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int G = 8 * c + j;
     _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
-    if (G < ngroups) {
-      const float cv = fmaf(z, bf16_to_f32(sv[j]), bf16_to_f32(bv[j]));
+    if (8 * slot + j < ngroups) {
+      const float cv = ldexpf(fmaf(r.z, bf16_to_f32(sv[j]), bf16_to_f32(bv[j])), -k);
       chi = (_Float16)cv;
       clo = (_Float16)(cv - (float)chi);
     }
@@ -151,125 +200,135 @@ __device__ __forceinline__ void prep_ext_chunk(const uint16_t* S, const uint16_t
     h[(3 * j + 1) >> 3][(3 * j + 1) & 7] = clo;
     h[(3 * j + 2) >> 3][(3 * j + 2) & 7] = chi;
   }
-  unsigned char* row = reinterpret_cast<unsigned char*>(dst + n * kext);
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
-    const int off = 48 * c + 16 * q;
+    const int off = 48 * slot + 16 * q;
     if (off < kext * 2) *reinterpret_cast<f16x8*>(row + off) = h[q];
   }
 }
 
-// Scale tiles: one block per 128 columns and 2 super-steps (256 inputs).
-// The block reads the scales it needs row by row (a row's groups are
-// contiguous), transposes them through LDS and writes each (K-step, matrix)
-// row of 128 columns contiguously.  Columns past I and K-steps past H get
-// zeros.  A bf16 scale with magnitude in [2^-17, 2^8) converts to binary16
-// exactly.
-constexpr int kScaleBlockSteps = 2;                     // super-steps per block
-constexpr int kScaleBlockGroups = kScaleBlockSteps * 128 / 32;   // groups per block, at most (gs >= 32)
-__device__ __forceinline__ void prep_scale_block(const PrepParams& p, int tile, int jb) {
-  __shared__ uint16_t src[2][kScaleTileCols][kScaleBlockGroups];   // [matrix][column][group of the block]
+// FAST: every row's slots fit kSlotsReg per thread and its groups the LDS row
+// (the scale tiles then read the scales from LDS); otherwise the slots are
+// loaded twice and the scale tiles read the scales from global memory.
+template <bool FAST>
+__device__ __forceinline__ void prep_columns(const PrepParams& p, int cb) {
+  __shared__ int kl[2][kColBlock];                              // row exponents k
+  __shared__ uint16_t srow[FAST ? 2 : 1][FAST ? kColBlock : 1][FAST ? kPrepLdsGroups : 1];
   const int tid = threadIdx.x;
-  const int s_main = p.H >> 5;
-  const int64_t n0 = (int64_t)tile * kScaleTileCols;
-  // all loads of both matrices first (indices clamped into the matrix; a
-  // matrix without rows, the linear's up slot at N = 1, loads nothing), then
-  // the LDS writes: one memory round trip
-  constexpr int KL = kScaleTileCols * kScaleBlockGroups / 256;
-  uint16_t v[2][KL];
+  const int pair = tid >> 2, sub = tid & 3;
+  const int mat = pair >> 5, col = pair & (kColBlock - 1);
+  const int64_t n = (int64_t)cb * kColBlock + col;
+  const int rows = mat ? p.I_u : p.I;
+  const bool live = n < rows;
+  const RowSpec r = row_spec(p, mat);
+  const int lg_g0 = __builtin_ctz(p.g0);
+  const int ngroups = p.H >> lg_g0;
+  const int per_row = (p.kext + 23) / 24;                       // slots, padding included
+  unsigned char* erow = reinterpret_cast<unsigned char*>((mat ? p.bext_u : p.bext_g) + n * p.kext);
+
+  // 1 + 2: row maximum over the quad, k, extra-column rows
+  float vmax = 0.0f;
+  if constexpr (FAST) {
+    uint16_t sv[kSlotsReg][8], bv[kSlotsReg][8];
 #pragma unroll
-  for (int mat = 0; mat < 2; ++mat) {
-    const int lg_gs = __builtin_ctz(mat ? p.gs_u : p.gs_g);
-    const uint16_t* S = mat ? p.su : p.sg;
-    const int ng = p.H >> lg_gs;
-    const int rows = mat ? p.I_u : p.I;
-    const int lg_gpb = __builtin_ctz(kScaleBlockSteps * 128) - lg_gs;   // groups per block: 256 / gs
-    const int g0 = jb << lg_gpb;
-#pragma unroll
-    for (int k = 0; k < KL; ++k) {
-      const int i = tid + 256 * k;
-      const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
-      const int64_t n = min(n0 + row, (int64_t)rows - 1);
-      v[mat][k] = rows > 0 ? S[n * ng + min(g0 + g, ng - 1)] : (uint16_t)0;
+    for (int i = 0; i < kSlotsReg; ++i) {
+      const int slot = sub + 4 * i;
+      if (live && slot < per_row) load_slot(r, n, lg_g0, ngroups, slot, sv[i], bv[i]);
     }
-  }
 #pragma unroll
-  for (int mat = 0; mat < 2; ++mat) {
-    const int lg_gs = __builtin_ctz(mat ? p.gs_u : p.gs_g);
-    const int ng = p.H >> lg_gs;
-    const int rows = mat ? p.I_u : p.I;
-    const int lg_gpb = __builtin_ctz(kScaleBlockSteps * 128) - lg_gs;
-    const int g0 = jb << lg_gpb;
+    for (int i = 0; i < kSlotsReg; ++i) {
+      const int slot = sub + 4 * i;
+      if (live && slot < per_row) {
+        vmax = fmaxf(vmax, slot_max(r, ngroups, slot, sv[i], bv[i]));
 #pragma unroll
-    for (int k = 0; k < KL; ++k) {
-      const int i = tid + 256 * k;
-      if (i < (kScaleTileCols << lg_gpb)) {
-        const int row = i >> lg_gpb, g = i & ((1 << lg_gpb) - 1);
-        src[mat][row][g] = (n0 + row < rows && g0 + g < ng) ? v[mat][k] : (uint16_t)0;
+        for (int j = 0; j < 8; ++j) {
+          const int G = 8 * slot + j;
+          if (G < ngroups) srow[mat][col][(G << lg_g0) >> r.lg_gs] = sv[i][j];   // g0 < gs: same value twice
+        }
       }
     }
-  }
-  __syncthreads();
-  const int lg_g = __builtin_ctz(p.gs_g), lg_u = __builtin_ctz(p.gs_u);
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
+    const int k = row_exponent_k(vmax);
 #pragma unroll
-  for (int k = 0; k < kScaleBlockSteps * kScaleTileWords / 256; ++k) {
-    const int idx = tid + 256 * k;
-    const int col = idx & (kScaleTileCols - 1);
-    const int rest = idx >> 7;                           // (super-step, K-step, matrix)
-    const int mat = rest & 1, q = (rest >> 1) & 3, jl = rest >> 3;
-    const int j = jb * kScaleBlockSteps + jl;
-    if (j >= p.nss) continue;
-    const int tl = 4 * jl + q;                           // K-step within the block
-    uint32_t v = 0;
-    if (4 * j + q < s_main && n0 + col < (mat ? p.I_u : p.I)) {
-      const _Float16 h = (_Float16)bf16_to_f32(src[mat][col][(32 * tl) >> (mat ? lg_u : lg_g)]);
-      v = as_u32((f16x2){h, h});
+    for (int i = 0; i < kSlotsReg; ++i) {
+      const int slot = sub + 4 * i;
+      if (live && slot < per_row && !p.k_only) store_slot(r, ngroups, slot, k, sv[i], bv[i], p.kext, erow);
     }
-    p.scl[((int64_t)tile * p.nss + j) * kScaleTileWords + (2 * q + mat) * kScaleTileCols + col] = v;
+    if (sub == 0) kl[mat][col] = k;
+    if (sub == 0 && live) p.kexp[(int64_t)mat * p.I + n] = k;
+  } else {
+    for (int slot = sub; live && slot < per_row; slot += 4) {
+      uint16_t sv[8], bv[8];
+      load_slot(r, n, lg_g0, ngroups, slot, sv, bv);
+      vmax = fmaxf(vmax, slot_max(r, ngroups, slot, sv, bv));
+    }
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
+    const int k = row_exponent_k(vmax);
+    for (int slot = sub; live && !p.k_only && slot < per_row; slot += 4) {
+      uint16_t sv[8], bv[8];
+      load_slot(r, n, lg_g0, ngroups, slot, sv, bv);
+      store_slot(r, ngroups, slot, k, sv, bv, p.kext, erow);
+    }
+    if (sub == 0) kl[mat][col] = k;
+    if (sub == 0 && live) p.kexp[(int64_t)mat * p.I + n] = k;
+  }
+  if (p.k_only) return;                                         // block-uniform
+  __syncthreads();
+
+  // 3: scale tiles.  Thread (matrix, K-step q, column) writes one word per
+  // super-step: 32 consecutive words of a (K-step, matrix) row per 32 threads.
+  {
+    const int c3 = tid & (kColBlock - 1), q = (tid >> 5) & 3, m3 = tid >> 7;
+    const int64_t n3 = (int64_t)cb * kColBlock + c3;
+    const bool live3 = n3 < (m3 ? p.I_u : p.I);
+    const RowSpec r3 = row_spec(p, m3);
+    const int k3 = kl[m3][c3];
+    const int s_main = p.H >> 5;
+    const int tile = cb / (kScaleTileCols / kColBlock);
+    const int word = (2 * q + m3) * kScaleTileCols + (cb % (kScaleTileCols / kColBlock)) * kColBlock + c3;
+    uint32_t* dst = p.scl + (int64_t)tile * p.nss * kScaleTileWords + word;
+    constexpr int U = 4;                                        // super-steps per batch of loads
+    for (int j0 = 0; j0 < p.nss; j0 += U) {
+      uint16_t sv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ks = 4 * (j0 + u) + q;
+        const bool ok = live3 && ks < s_main;
+        const int gi = ok ? ((32 * ks) >> r3.lg_gs) : 0;
+        if constexpr (FAST) sv[u] = ok ? srow[m3][c3][gi] : (uint16_t)0;
+        else sv[u] = ok ? r3.S[n3 * r3.ng + gi] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j0 + u >= p.nss) continue;
+        const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sv[u]), -k3);
+        dst[(int64_t)(j0 + u) * kScaleTileWords] = as_u32((f16x2){h, h});
+      }
+    }
   }
 }
 
 // Index helpers of the prep grid (host and device agree on them).
-__host__ __device__ inline int prep_ext_lg(int kext) {          // log2 of 8-group chunk slots per row
-  const int per_row = (kext + 23) / 24;
-  int lg = 0;
-  while ((1 << lg) < per_row) ++lg;
-  return lg;
+__host__ __device__ inline int64_t prep_col_blocks(int I) {        // whole 128-column tiles
+  return (int64_t)(I + kScaleTileCols - 1) / kScaleTileCols * (kScaleTileCols / kColBlock);
 }
-__host__ __device__ inline int64_t prep_scale_blocks(int I, int nss) {   // blocks of the scale tiles
-  return (int64_t)(I + kScaleTileCols - 1) / kScaleTileCols * ((nss + kScaleBlockSteps - 1) / kScaleBlockSteps);
+__host__ __device__ inline bool prep_fast(const PrepParams& p) {
+  const int per_row = (p.kext + 23) / 24;
+  return (per_row + 3) / 4 <= kSlotsReg && (p.H / p.gs_g) <= kPrepLdsGroups && (p.H / p.gs_u) <= kPrepLdsGroups;
 }
 
-// Blocks [0, M): x rows.  Then the extra-column rows, thread index
-// ((n * 2 + matrix) << lg) + c for 8-group chunk c.  Then the scale tiles,
-// one block per 128 columns and kScaleBlockSteps super-steps.  Every
-// division is by a power of two or block-uniform.
+// Blocks [0, M): x rows.  Then the column blocks, kColBlock output features
+// of both matrices each, over whole 128-column tiles.
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   if ((int)blockIdx.x < p.M) {
     prep_x_row(p, blockIdx.x);
     return;
   }
-  const int lg = prep_ext_lg(p.kext);
-  const int64_t ext_blocks = ((2 * (int64_t)p.I << lg) + 255) / 256;
-  const int64_t b = (int64_t)blockIdx.x - p.M;
-  if (b >= ext_blocks) {
-    const int nj = (p.nss + kScaleBlockSteps - 1) / kScaleBlockSteps;
-    const int b2 = (int)(b - ext_blocks);
-    const int tile = b2 / nj;                            // block-uniform
-    prep_scale_block(p, tile, b2 - tile * nj);
-    return;
-  }
-  const int64_t idx = b * 256 + threadIdx.x;
-  const int c = (int)(idx & ((1 << lg) - 1));
-  const int64_t rest = idx >> lg;
-  const int64_t n = rest >> 1;
-  if (n >= ((rest & 1) ? p.I_u : p.I)) return;       // up rows past I_u: read as zeros by the GEMM
-  const int lg_g0 = __builtin_ctz(p.g0);
-  const int ngroups = p.H >> lg_g0;
-  if ((rest & 1) == 0)
-    prep_ext_chunk(p.sg, p.bg, __builtin_ctz(p.gs_g), p.bits_g, lg_g0, ngroups, p.kext, p.bext_g, n, c);
-  else
-    prep_ext_chunk(p.su, p.bu, __builtin_ctz(p.gs_u), p.bits_u, lg_g0, ngroups, p.kext, p.bext_u, n, c);
+  const int cb = (int)blockIdx.x - p.M;
+  if (prep_fast(p)) prep_columns<true>(p, cb);
+  else prep_columns<false>(p, cb);
 }
 
 // ----------------------------------------------------------- MFMA GEMM ----
@@ -316,12 +375,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // are issued from inline assembly so that the compiler does not serialise
 // every later LDS read behind them (it cannot tell the stages apart); the
 // kernel orders them itself with explicit vmcnt waits and barriers.  m0
-// carries the LDS base.
+// carries the LDS base.  The whole byte offset rides in the VGPR offset (the
+// SGPR offset is 0): a raw buffer's range check covers the VGPR offset only,
+// so every load past the end of its buffer -- including the loads the
+// pipeline issues ahead past the last K-step -- returns zeros and touches no
+// memory.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds_base), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds_base), "v"(voff), "s"(rs) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -391,10 +454,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   static_assert(BM <= NT && A_INSTR >= 1 && B_EXT_INSTR >= 1 && SS_SCALE_INSTR == 1, "tile shape");
   static_assert(BN == kScaleTileCols && kScaleTileWords * 4 == 2 * BN * 16, "scale tile = ring slot scale area");
   static_assert(STAGES == SS, "a stage slot and the super-step phase are both t % 4");
-  static_assert(STAGES * STAGE + 2 * SS_SLOT + BM * 4 <= 160 * 1024, "LDS");
+  static_assert(STAGES * STAGE + 2 * SS_SLOT + BM * 4 + 2 * BN * 4 <= 160 * 1024, "LDS");
+  static_assert(2 * BN == NT, "one thread per (matrix, column) of the tile for the row exponents k");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE + 2 * SS_SLOT];
   __shared__ int rexp[BM];
+  __shared__ int rk[2][BN];
   unsigned char* const ssmem = smem + STAGES * STAGE;   // code ring: two super-step slots
 
   const int tid = threadIdx.x;
@@ -470,8 +535,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
   const NibbleK nk = nibble_consts_in_regs();            // unpack constants in registers
 
-  // row exponents of the tile: loaded first, published through LDS after the K loop
+  // row exponents of the tile (x rows e, weight rows k: thread = (matrix, column)):
+  // loaded first, published through LDS after the K loop
   const int my_exp = tid < rows ? p.xexp[m0 + tid] : 0;
+  const int kc = tid & (BN - 1), km = tid >> 7;
+  const int my_k = n0 + kc < (km ? min(p.n_end, p.I_u) : p.n_end) ? p.kexp[(int64_t)km * p.I + n0 + kc] : 0;
 
   // issue the x' (and for an extra-column step the B) loads of K-step s into stage `slot`
   const uint32_t smem0 = lds_addr(smem);
@@ -480,13 +548,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int es = s - s_main;                         // extra-column step: block es/2, matrix es%2
     const uint32_t soff_a = (uint32_t)(ext ? s_main + (es >> 1) : s) * a_step;
 #pragma unroll
-    for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j], soff_a);
+    for (int j = 0; j < A_INSTR; ++j) dma16(rs_a, st + (j * NT + w * 64) * 16, a_voff[j] + soff_a);
     if (ext) {
       const uint32_t sb = st + A_BYTES;
       const i32x4 rs_e = (es & 1) ? rs_eu : rs_eg;
       const uint32_t soff_e = (uint32_t)(es >> 1) * 64;
 #pragma unroll
-      for (int j = 0; j < B_EXT_INSTR; ++j) dma16(rs_e, sb + (j * NT + w * 64) * 16, e_voff[j], soff_e);
+      for (int j = 0; j < B_EXT_INSTR; ++j) dma16(rs_e, sb + (j * NT + w * 64) * 16, e_voff[j] + soff_e);
     }
   };
   // issue the codes and scales of super-step j (K-steps SS*j .. SS*j + SS-1) into its slot
@@ -495,12 +563,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const uint32_t sl = ssmem0 + (j & 1) * SS_SLOT;
 #pragma unroll
     for (int q = 0; q < SS_CODE_INSTR; ++q) {
-      if (q * NT < BN * CPR_G) dma16(rs_wg, sl + (q * NT + w * 64) * 16, c_voff[q], (uint32_t)(j * CPR_G * 16));
-      else dma16(rs_wu, sl + (q * NT + w * 64) * 16, c_voff[q], (uint32_t)(j * CPR_U * 16));
+      if (q * NT < BN * CPR_G) dma16(rs_wg, sl + (q * NT + w * 64) * 16, c_voff[q] + (uint32_t)(j * CPR_G * 16));
+      else dma16(rs_wu, sl + (q * NT + w * 64) * 16, c_voff[q] + (uint32_t)(j * CPR_U * 16));
     }
 #pragma unroll
     for (int q = 0; q < SS_SCALE_INSTR; ++q)
-      dma16(rs_sc, sl + SS_CODE_BYTES + w * 64 * 16, s_voff[q], (uint32_t)j * kScaleTileWords * 4);
+      dma16(rs_sc, sl + SS_CODE_BYTES + w * 64 * 16, s_voff[q] + (uint32_t)j * kScaleTileWords * 4);
   };
 
   f32x16 acc_g[MF][NF], acc_u[MF][NF];
@@ -747,6 +815,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   }
   wait_vmcnt<0>();                                   // nothing left in flight at exit
   if (tid < BM) rexp[tid] = my_exp;
+  rk[km][kc] = my_k;
   __syncthreads();
 
   // ---- epilogue.  The MFMAs compute W x'^T, so in fragment (i, f) lane l holds
@@ -787,12 +856,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       for (int f = 0; f < NF; ++f) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c0 = n0 + w * WN + f * 32 + 8 * j + 4 * half;
+          const int cl = w * WN + f * 32 + 8 * j + 4 * half;
+          const int c0 = n0 + cl;
           float g[4], u[4], h[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            g[c] = ldexpf(acc_g[i][f][4 * j + c], e);
-            u[c] = ldexpf(acc_u[i][f][4 * j + c], e);
+            g[c] = ldexpf(acc_g[i][f][4 * j + c], e + rk[0][cl + c]);
+            u[c] = ldexpf(acc_u[i][f][4 * j + c], e + rk[1][cl + c]);
             if constexpr (MODE < 3) h[c] = swiglu_epilogue(g[c], u[c], MODE);
           }
           if (!row_ok) continue;
@@ -832,15 +902,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const int64_t ext_threads = (2 * (int64_t)p.I) << prep_ext_lg(p.kext);
-  const int64_t scl_blocks = prep_scale_blocks(p.I, p.nss);
-  const int64_t blocks = p.M + (ext_threads + 255) / 256 + scl_blocks;
+  const int64_t blocks = p.M + prep_col_blocks(p.I);
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)p.M), dim3(256), 0, stream, p);
+  if (!p.k_only) return hipErrorInvalidValue;
+  const int64_t blocks = p.M + prep_col_blocks(p.I);
+  hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

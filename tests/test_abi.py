@@ -234,15 +234,16 @@ def test_strerror_and_version():
 def test_workspace_bytes():
     # x' rows of H + extra columns (3 per group of the finer group size,
     # padded to 32) halves, row exponents, one [I, kext] binary16 plane of
-    # extra-column B rows per matrix, then 4 KB of scale tile per 128
-    # columns and 128 inputs
+    # extra-column B rows per matrix, 4 KB of scale tile per 128 columns and
+    # 128 inputs, then the weight rows' exponents (int32, gate and up)
     def a256(v):
         return (v + 255) // 256 * 256
 
     def expect(M, H, I, bg, gg, bu, gu):
         ext = (3 * (H // min(gg, gu)) + 31) // 32 * 32
         tiles = (I + 127) // 128 * ((H + 127) // 128)
-        return a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2) + a256(tiles * 4096)
+        return (a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2) + a256(tiles * 4096)
+                + a256(2 * I * 4))
 
     assert swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64) == expect(512, 2048, 8192, 4, 64, 4, 64)
     assert swq.swiglu_q_workspace_bytes(8192, 2560, 10240, 8, 32, 4, 64) == expect(8192, 2560, 10240, 8, 32, 4, 64)
@@ -254,3 +255,35 @@ def test_binding_has_no_fallback():
     """The binding only marshals: it never imports the oracle."""
     src = open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "__init__.py")).read()
     assert "oracle" not in src
+
+
+def test_tensor_helpers_reject_other_activation_types():
+    """The tensor conveniences take bf16 activations (or their 16-bit bit
+    patterns) only: a float16 or float32 x is refused before any call into
+    the library, instead of being read as bf16 bits."""
+    import torch
+    w = torch.zeros((64, 32), dtype=torch.int32)
+    s = torch.zeros((64, 4), dtype=torch.bfloat16)
+    for dt in (torch.float16, torch.float32):
+        x = torch.zeros((2, 256), dtype=dt)
+        with pytest.raises(TypeError):
+            swq.forward(x, w, s, s, w, s, s, 4, 64)
+        with pytest.raises(TypeError):
+            swq.linear(x, w, s, s, 4, 64)
+        with pytest.raises(TypeError):
+            swq.debug_gemm_tensors(x, w, s, s, w, s, s, 4, 64)
+        with pytest.raises(TypeError):
+            swq.mlp(x, w, s, s, w, s, s, w, s, s, (4, 64), (4, 64), (4, 64))
+
+
+def test_tensor_helpers_collapse_leading_dimensions():
+    """x of shape [..., H] becomes M = prod(...) rows of one contiguous block
+    (the pages' host entry does the same), and a non-contiguous x is refused."""
+    import torch
+    x = torch.zeros((2, 3, 5, 256), dtype=torch.bfloat16)
+    x2, lead = swq._rows(x, "t")
+    assert tuple(x2.shape) == (30, 256) and lead == (2, 3, 5) and x2.data_ptr() == x.data_ptr()
+    x2, lead = swq._rows(torch.zeros((256,), dtype=torch.int16), "t")
+    assert tuple(x2.shape) == (1, 256) and lead == ()
+    with pytest.raises(ValueError):
+        swq._rows(torch.zeros((256, 4), dtype=torch.bfloat16).t(), "t")

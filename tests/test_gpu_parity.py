@@ -95,6 +95,73 @@ def test_random_specs_and_magnitudes(case):
     check(y, oracle_full(p, mode), mode, f"random case {case}")
 
 
+# ------------------------------------------- scale and bias magnitudes --
+
+# Scales and biases anywhere in bf16's range: each weight row's scales and
+# constants get their own power of two before they become binary16 operands,
+# so every kernel stays finite and exact (up to float32 accumulation) for
+# tiny and huge scales, scales that differ by many binades between the groups
+# of one row, and large biases.
+RANGE_LAWS = [
+    ("s2m24", (4, 64, 4, 64), ("pow", -24), "factor"),
+    ("s2m20", (4, 64, 4, 64), ("pow", -20), "factor"),
+    ("s2p10", (4, 64, 4, 64), ("pow", 10), "factor"),
+    ("s2p14", (4, 64, 4, 64), ("pow", 14), "factor"),
+    ("8bit-s2p10", (8, 32, 8, 64), ("pow", 10), "half"),
+    ("mixed-groups", (4, 64, 8, 32), ("mixed", -20, 14), "factor"),
+    ("bias1e5", (4, 64, 4, 64), ("pow", -7), ("uniform", 1e5)),
+    ("8bit-mixed-bias1e5", (8, 32, 2, 64), ("mixed", -20, 10), ("uniform", 1e5)),
+]
+# (M, H, I, path): the M = 1 kernel, its several-row form, the few-row kernel
+# with x' built in the block and from the prep kernel (one and two row tiles),
+# and the MFMA kernel
+RANGE_SHAPES = [(1, 1024, 130, GEMV), (3, 2048, 70, GEMV), (6, 512, 97, GEMV), (9, 2048, 66, GEMV),
+                (20, 1024, 50, GEMV), (70, 512, 130, MFMA)]
+RANGE_CASES = [(law, shape) for law in RANGE_LAWS for shape in RANGE_SHAPES]
+
+
+def _range_problem(M, H, I, spec, s_law, b_law, seed):
+    bits_g, gs_g, bits_u, gs_u = spec
+    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=seed)
+    rng = np.random.default_rng(seed)
+    for tag, bits, gs in (("g", bits_g, gs_g), ("u", bits_u, gs_u)):
+        shape = (I, H // gs)
+        if s_law[0] == "pow":
+            s = np.float32(2.0 ** s_law[1]) * rng.uniform(1.0, 2.0, shape).astype(np.float32)
+        else:
+            s = np.exp2(rng.uniform(s_law[1], s_law[2], shape)).astype(np.float32)
+        s_bits = to_bf16_bits(s)
+        sv = bf16_bits_to_f32(s_bits)
+        if b_law == "factor":
+            b = np.float32(-(1 << (bits - 1))) * sv * rng.uniform(0.9, 1.1, shape).astype(np.float32)
+        elif b_law == "half":
+            b = np.float32(-(1 << (bits - 1))) * sv
+        else:
+            b = rng.uniform(-b_law[1], b_law[1], shape).astype(np.float32)
+        setattr(p, "s" + tag, s_bits)
+        setattr(p, "b" + tag, to_bf16_bits(b.astype(np.float32)))
+    return p
+
+
+@pytest.mark.parametrize("law,shape", RANGE_CASES,
+                         ids=[f"{l[0]}-M{sh[0]}-H{sh[1]}-p{sh[3]}" for l, sh in RANGE_CASES])
+def test_scale_and_bias_range(law, shape):
+    name, spec, s_law, b_law = law
+    M, H, I, path = shape
+    mode = (len(name) + M) % 3
+    p = _range_problem(M, H, I, spec, s_law, b_law, seed=M * 131 + H + len(name))
+    say("range", name, M, H, I, spec, "mode", mode, "path", path)
+    o = oracle_full(p, mode)
+    g, u = device_gemm(p, path)
+    assert np.all(np.isfinite(g)) and np.all(np.isfinite(u)), name
+    eg = np.max(np.abs(g - o["g"]) / o["nu_g"])
+    eu = np.max(np.abs(u - o["u"]) / o["nu_u"])
+    print(f"  {name}: max |dg|/nu_g={eg:.3g} |du|/nu_u={eu:.3g}")
+    assert eg <= 1e-5 and eu <= 1e-5, (eg, eu)
+    y = device_forward(p, mode, path)
+    check(y, o, mode, f"range {name} M{M} H{H} path{path}")
+
+
 # ------------------------------------------------------- decode (M = 1) --
 
 # every branch of the M = 1 kernel: a whole wave per column with one to four
@@ -466,3 +533,51 @@ def test_graph_replays_match_eager(M, H, I, spec):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
     check(out.float().cpu().numpy().astype(np.float64), oracle_full(p, 0), 0, "graph replay")
+
+
+def test_graph_replay_after_workspace_growth():
+    """A graph captured while the stream's workspace was small keeps using
+    that buffer after a larger eager call replaced it: the old buffer is kept
+    (not freed), so replays still write the eager result, and memory allocated
+    after the growth is never written by them."""
+    small = make_custom(300, 512, 384, 4, 64, 8, 32, seed=91)
+    big = make_custom(3000, 2048, 1024, 4, 64, 4, 64, seed=92)
+    sdev, bdev = swq.to_device(small), swq.to_device(big)
+    say("graph replay after workspace growth")
+    stream = torch.cuda.Stream()
+    swq.swiglu_q_release_workspace()              # start from no workspace on this stream
+    with torch.cuda.stream(stream):
+        eager = swq.forward(*sdev, 4, 64, 8, 32, mode=1, stream=stream)
+    torch.cuda.synchronize()
+    ref = eager.clone()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        swq.forward(*sdev, 4, 64, 8, 32, mode=1, out=out, stream=torch.cuda.current_stream())
+    with torch.cuda.stream(stream):                # grows (replaces) the stream's workspace
+        yb = swq.forward(*bdev, 4, 64, 4, 64, mode=1, stream=stream)
+    torch.cuda.synchronize()
+    need = swq.swiglu_q_workspace_bytes(300, 512, 384, 4, 64, 8, 32)
+    guard = torch.full((need // 4 + 1024,), 7, dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+    assert bool((guard == 7).all().item())
+    ms, ns = sample_pairs(3000, 1024, 400, seed=5)
+    check(yb.cpu().numpy().astype(np.float64)[ms, ns], oracle_pairs(big, 1, ms, ns), 1, "grown call")
+    del g
+
+
+def test_leading_dimensions():
+    """x of shape [2, 3, H] gives the [2, 3, I] result of the same six rows as [6, H]."""
+    p = make_custom(6, 512, 200, 4, 64, 4, 64, seed=93)
+    dev = swq.to_device(p)
+    say("leading dimensions")
+    flat = swq.forward(*dev, 4, 64, mode=1)
+    shaped = swq.forward(dev[0].view(2, 3, 512), *dev[1:], 4, 64, mode=1)
+    torch.cuda.synchronize()
+    assert tuple(shaped.shape) == (2, 3, 200)
+    assert torch.equal(shaped.view(6, 200), flat)
