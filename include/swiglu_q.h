@@ -84,6 +84,8 @@ extern "C" {
 #define SWQ_ERR_ALIGN        4  /* a pointer is not 16-byte aligned                 */
 #define SWQ_ERR_HIP          5  /* a HIP call or kernel launch failed               */
 #define SWQ_ERR_WORKSPACE    6  /* the workspace could not be allocated             */
+#define SWQ_ERR_TOO_LARGE    7  /* swiglu_q_forward_noalloc: the call's staging would
+                                   exceed its fixed 64 MiB                          */
 
 /* Precision modes (the pages' two variants; the wide one with two output types). */
 #define SWQ_MATCH        0  /* gate and up rounded to bf16 (RNE) before silu·up;
@@ -117,6 +119,27 @@ int swiglu_q_forward(const void *x,
                      int64_t M, int64_t H, int64_t I,
                      int bits_g, int gs_g, int bits_u, int gs_u,
                      int precision_mode, void *out, void *stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, validation, kernels and results (bit for bit)
+ * as swiglu_q_forward, but the call allocates nothing: the staging that
+ * swiglu_q_forward keeps in its per-stream workspace lives in a fixed
+ * 64 MiB device array that each GPU the library runs on holds from the first
+ * such call until the process ends.  Returns SWQ_ERR_TOO_LARGE, before any
+ * HIP call, when the call would need more than that (the matrix-matrix path
+ * needs swiglu_q_workspace_bytes(...); M = 8192, H = 2560, I = 10240 with an
+ * 8-bit gs 32 gate fits).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU, on any streams, race and give wrong
+ * results; order them (one stream, or events).
+ */
+int swiglu_q_forward_noalloc(const void *x,
+                             const uint32_t *Wg, const void *sg, const void *bg,
+                             const uint32_t *Wu, const void *su, const void *bu,
+                             int64_t M, int64_t H, int64_t I,
+                             int bits_g, int gs_g, int bits_u, int gs_u,
+                             int precision_mode, void *out, void *stream);
 
 /* Output types of swiglu_q_linear. */
 #define SWQ_LINEAR_BF16  0  /* float32 sums rounded once to bf16 (RNE) at the store */

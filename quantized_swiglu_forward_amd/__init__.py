@@ -18,7 +18,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libswiglu_q.so")
 
-SWQ_OK, SWQ_ERR_NULL, SWQ_ERR_SHAPE, SWQ_ERR_UNSUPPORTED, SWQ_ERR_ALIGN, SWQ_ERR_HIP, SWQ_ERR_WORKSPACE = range(7)
+(SWQ_OK, SWQ_ERR_NULL, SWQ_ERR_SHAPE, SWQ_ERR_UNSUPPORTED, SWQ_ERR_ALIGN, SWQ_ERR_HIP, SWQ_ERR_WORKSPACE,
+ SWQ_ERR_TOO_LARGE) = range(8)
 SWQ_MATCH, SWQ_F32, SWQ_F32_BF16OUT = 0, 1, 2
 SWQ_PATH_GEMV, SWQ_PATH_MFMA, SWQ_PATH_AUTO = 0, 1, -1
 SWQ_LINEAR_BF16, SWQ_LINEAR_F32 = 0, 1
@@ -44,6 +45,8 @@ def lib():
     vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
     L.swiglu_q_forward.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
     L.swiglu_q_forward.restype = i32
+    L.swiglu_q_forward_noalloc.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
+    L.swiglu_q_forward_noalloc.restype = i32
     L.swiglu_q_linear.argtypes = [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp, vp]
     L.swiglu_q_linear.restype = i32
     L.swiglu_q_mlp.argtypes = [vp] * 11 + [i64, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp]
@@ -98,6 +101,13 @@ def swiglu_q_forward(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, g
     return lib().swiglu_q_forward(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
                                   M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
                                   _stream(stream))
+
+
+def swiglu_q_forward_noalloc(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u,
+                             precision_mode, out, stream=None) -> int:
+    return lib().swiglu_q_forward_noalloc(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
+                                          M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
+                                          _stream(stream))
 
 
 def swiglu_q_linear(x, W, s, b, M, K, N, bits, gs, out_mode, out, stream=None) -> int:

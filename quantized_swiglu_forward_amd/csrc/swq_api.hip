@@ -219,13 +219,40 @@ int get_workspace(hipStream_t stream, size_t need, void** out, int slot = 0) {
   return SWQ_OK;
 }
 
+// Staging of the matrix-vector path when the prep kernel stages x' (x' rows
+// [H/32][M][32] with the extra columns of 32-input groups riding along unused,
+// the row exponents, then the weight rows' exponents k [2][I]).
+int64_t gemv_stage_bytes(int64_t M, int64_t H, int64_t I) {
+  const int kext = kext_columns(H, 32);
+  return align256(M * (H + kext) * 2) + align256(M * 4) + align256(2 * I * 4);
+}
+
+// Device staging bytes of a call that takes `path` (0: none).
+int64_t staging_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bits_u, int gs_u, int path) {
+  if (M <= 0) return 0;
+  if (path == SWQ_PATH_GEMV) return gemv_needs_rows(M, H) ? gemv_stage_bytes(M, H, I) : 0;
+  return ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u).total;
+}
+
+// The staging buffer of a call: the caller's fixed one (fixed != null; it
+// must hold `need` bytes) or the library's per-(device, stream) workspace.
+int acquire(hipStream_t stream, size_t need, void** out, void* fixed, size_t fixed_bytes) {
+  if (fixed) {
+    if (need > fixed_bytes) return SWQ_ERR_TOO_LARGE;
+    *out = fixed;
+    return SWQ_OK;
+  }
+  return get_workspace(stream, need, out);
+}
+
 // I_u: rows of the up matrix (I, or fewer for the linear's split weight);
 // ldo: output row stride in elements (I, or N for the linear); res: the
-// linear's residual (bf16 [M, ldo]) or null.
+// linear's residual (bf16 [M, ldo]) or null; fixed: a caller-chosen staging
+// buffer of fixed_bytes (null: the library's workspace).
 int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
         const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int64_t I_u, int64_t ldo,
         int bits_g, int gs_g, int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u,
-        const void* res, int path, void* stream_v) {
+        const void* res, int path, void* stream_v, void* fixed = nullptr, size_t fixed_bytes = 0) {
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
@@ -248,14 +275,13 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
               (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
     (void)hipGetLastError();
     if (gemv_needs_rows(M, H)) {
-      // x' rows [H/32][M][32] (the extra columns of 32-input groups ride along
-      // unused), the row exponents, then the weight rows' exponents k [2][I]
-      // from the prep kernel's column blocks
+      // x' rows, their exponents and the weight rows' exponents k from the
+      // prep kernel's column blocks (gemv_stage_bytes)
       const int kext = kext_columns(H, 32);
       const int64_t xa_bytes = align256(M * (H + kext) * 2);
       const int64_t xe_bytes = align256(M * 4);
       void* ws = nullptr;
-      int rc = get_workspace(stream, (size_t)(xa_bytes + xe_bytes + align256(2 * I * 4)), &ws);
+      int rc = acquire(stream, (size_t)gemv_stage_bytes(M, H, I), &ws, fixed, fixed_bytes);
       if (rc != SWQ_OK) return rc;
       PrepParams pp{};
       pp.x = (const uint16_t*)x;
@@ -281,7 +307,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
 
   const WsLayout L = ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u);
   void* ws = nullptr;
-  int rc = get_workspace(stream, (size_t)L.total, &ws);
+  int rc = acquire(stream, (size_t)L.total, &ws, fixed, fixed_bytes);
   if (rc != SWQ_OK) return rc;
   char* wsb = (char*)ws;
   const int g0 = gs_g < gs_u ? gs_g : gs_u;
@@ -361,6 +387,40 @@ int linear_run(const void* x, const uint32_t* W, const void* s, const void* b, c
              stream);
 }
 
+// ---- allocation-free forward ------------------------------------------------
+//
+// swiglu_q_forward_noalloc stages into this file-scope device array instead of
+// the per-stream workspace.  Each GPU the library runs on holds its own copy
+// (kScratchBytes of device memory until the process ends).  In host code the
+// name `scratch` is only a stand-in: the device address of the copy on the
+// current GPU comes from hipGetSymbolAddress, taken once per device at the
+// entry point's first call there and kept in g_scratch.  Every call on one GPU
+// shares that GPU's copy, so calls that overlap in time on one GPU race.  No
+// byte of it needs to start at zero: the prep kernel writes everything the
+// GEMM kernels read before they read it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];   // device address of each GPU's copy, or null before its first call
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return SWQ_ERR_HIP;
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SWQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,6 +436,26 @@ int swiglu_q_forward(const void* x, const uint32_t* Wg, const void* sg, const vo
   if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
   return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
              nullptr, nullptr, nullptr, SWQ_PATH_AUTO, stream);
+}
+
+int swiglu_q_forward_noalloc(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
+                             const uint32_t* Wu, const void* su, const void* bu, int64_t M, int64_t H,
+                             int64_t I, int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode,
+                             void* out, void* stream) {
+  int rc = validate(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u);
+  if (rc != SWQ_OK) return rc;
+  if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return SWQ_ERR_UNSUPPORTED;
+  if (!out) return SWQ_ERR_NULL;
+  if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
+  if (M == 0) return SWQ_OK;
+  // the size check comes before any HIP call
+  const int path = auto_path(M, H);
+  if (staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path) > (int64_t)kScratchBytes) return SWQ_ERR_TOO_LARGE;
+  void* ptr = nullptr;
+  rc = scratch_address(&ptr);
+  if (rc != SWQ_OK) return rc;
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out, nullptr,
+             nullptr, nullptr, path, stream, ptr, kScratchBytes);
 }
 
 int swiglu_q_linear(const void* x, const uint32_t* W, const void* s, const void* b, int64_t M, int64_t K,
@@ -453,6 +533,7 @@ const char* swiglu_q_strerror(int status) {
     case SWQ_ERR_ALIGN: return "misaligned pointer (x, Wg, Wu need 16 bytes; others their element size)";
     case SWQ_ERR_HIP: return "HIP launch or runtime error";
     case SWQ_ERR_WORKSPACE: return "workspace allocation failed";
+    case SWQ_ERR_TOO_LARGE: return "the call needs more staging than the allocation-free entry point's fixed 64 MiB";
     default: return "unknown status";
   }
 }

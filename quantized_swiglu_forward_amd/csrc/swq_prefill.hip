@@ -256,7 +256,7 @@ __device__ __forceinline__ void prep_columns(const PrepParams& p, int cb) {
       if (live && slot < per_row && !p.k_only) store_slot(r, ngroups, slot, k, sv[i], bv[i], p.kext, erow);
     }
     if (sub == 0) kl[mat][col] = k;
-    if (sub == 0 && live) p.kexp[(int64_t)mat * p.I + n] = k;
+    if (sub == 0 && n < p.I) p.kexp[(int64_t)mat * p.I + n] = k;   // 0 for missing up rows
   } else {
     for (int slot = sub; live && slot < per_row; slot += 4) {
       uint16_t sv[8], bv[8];
@@ -272,7 +272,7 @@ __device__ __forceinline__ void prep_columns(const PrepParams& p, int cb) {
       store_slot(r, ngroups, slot, k, sv, bv, p.kext, erow);
     }
     if (sub == 0) kl[mat][col] = k;
-    if (sub == 0 && live) p.kexp[(int64_t)mat * p.I + n] = k;
+    if (sub == 0 && n < p.I) p.kexp[(int64_t)mat * p.I + n] = k;   // 0 for missing up rows
   }
   if (p.k_only) return;                                         // block-uniform
   __syncthreads();

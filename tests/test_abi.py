@@ -287,3 +287,19 @@ def test_tensor_helpers_collapse_leading_dimensions():
     assert tuple(x2.shape) == (1, 256) and lead == ()
     with pytest.raises(ValueError):
         swq._rows(torch.zeros((256, 4), dtype=torch.bfloat16).t(), "t")
+
+
+def test_noalloc_rejects_oversized_calls_before_any_hip_call():
+    """The allocation-free forward refuses a call whose staging would exceed
+    its fixed 64 MiB with SWQ_ERR_TOO_LARGE, and validates like the forward,
+    all on the host (no device is touched: these run without a GPU)."""
+    a = dict(x=P, Wg=P, sg=P, bg=P, Wu=P, su=P, bu=P, M=8192, H=4096, I=14336, bits_g=4, gs_g=64, bits_u=4,
+             gs_u=64, precision_mode=0, out=P, stream=0)
+    assert swq.swiglu_q_workspace_bytes(8192, 4096, 14336, 4, 64, 4, 64) > 64 << 20
+    assert swq.swiglu_q_forward_noalloc(**a) == swq.SWQ_ERR_TOO_LARGE
+    assert swq.swiglu_q_forward_noalloc(**{**a, "M": 0}) == swq.SWQ_OK
+    assert swq.swiglu_q_forward_noalloc(**{**a, "x": None}) == swq.SWQ_ERR_NULL
+    assert swq.swiglu_q_forward_noalloc(**{**a, "bits_g": 3}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_forward_noalloc(**{**a, "precision_mode": 3}) == swq.SWQ_ERR_UNSUPPORTED
+    assert swq.swiglu_q_forward_noalloc(**{**a, "out": P + 1}) == swq.SWQ_ERR_ALIGN
+    assert "64 MiB" in swq.swiglu_q_strerror(swq.SWQ_ERR_TOO_LARGE)
