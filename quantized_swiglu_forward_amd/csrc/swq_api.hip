@@ -294,10 +294,12 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       pp.xexp = (int*)((char*)ws + xa_bytes);
       pp.kexp = (int*)((char*)ws + xa_bytes + xe_bytes);
       pp.nss = (int)((H + 127) / 128);
-      pp.k_only = 1;
+      // the weight rows' exponents only when the few-row kernel cannot take
+      // them from the scales of its first pass
+      pp.k_only = skinny_needs_kexp((int)M, (int)H, bits_g, bits_u) ? 1 : 0;
       p.xa = pp.xa;
       p.xexp = pp.xexp;
-      p.kexp = pp.kexp;
+      p.kexp = pp.k_only ? pp.kexp : nullptr;
       if (launch_prep_rows(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
     }
     if (launch_gemv(p, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;

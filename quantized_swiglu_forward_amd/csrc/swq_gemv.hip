@@ -515,7 +515,7 @@ struct SkinnyChunk {
 template <int BITS_G, int BITS_U, bool STAGE, int RT, bool Q2>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
 __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
-  static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_U <= 4), "two quads in flight: narrow codes, prep-fed x'");
+  static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, prep-fed x'");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -586,7 +586,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   auto k_gate = [&]() { return (int)(int16_t)(kpack & 0xFFFFu); };
   auto k_up = [&]() { return (int)kpack >> 16; };
   if constexpr (!STAGE) {
-    if (col < p.I) set_k(p.kexp[col], p.kexp[p.I + col]);
+    const int nquad_ = (nchunk + 3) >> 2;
+    if (nquad_ > (Q2 ? 2 : 1) * nw && col < p.I) set_k(p.kexp[col], p.kexp[p.I + col]);
   }
   auto row_k_read = [&]() {
     float mg_ = 0.0f, mu_ = 0.0f;
@@ -710,17 +711,45 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
     }
   };
 
-  // chunk quads w, w + nw, ... (one for H <= 2048)
+  // chunk quads w, w + nw, ... (Q2: w, w + nw in one pass, then w + 2 nw, ...).
+  // When one pass loads every quad of the row, each wave takes its own
+  // column exponents from the scales and biases its loads brought (the
+  // largest term of its chunks of the column: two swaps, no barrier); its
+  // partial sums are multiplied by 2^k before the waves add them, so waves
+  // may differ.  A wave's maximum is at most the row's, so exactness holds
+  // as for the row's k.  Otherwise the exponents come from the prep kernel
+  // (x' staged there) or the block's own pass (STAGE).
   const int nquad = (nchunk + 3) >> 2;
+  const bool single = nquad <= (Q2 ? 2 : 1) * nw;
+  float cmax_g = 0.0f, cmax_u = 0.0f;
+  auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    if (!d.live) return;
+    cmax_g = fmaxf(cmax_g, group_term_max(bf16_to_f32((uint16_t)d.sg), bf16_to_f32((uint16_t)d.bg),
+                                          CodeOffset<BITS_G>::z, kPlaneMax<BITS_G>));
+    cmax_u = fmaxf(cmax_u, group_term_max(bf16_to_f32((uint16_t)d.su), bf16_to_f32((uint16_t)d.bu),
+                                          CodeOffset<BITS_U>::z, kPlaneMax<BITS_U>));
+  };
+  auto chunk_k_wave = [&]() {
+    cmax_g = fmaxf(cmax_g, __shfl_xor(cmax_g, 16));
+    cmax_g = fmaxf(cmax_g, __shfl_xor(cmax_g, 32));
+    cmax_u = fmaxf(cmax_u, __shfl_xor(cmax_u, 16));
+    cmax_u = fmaxf(cmax_u, __shfl_xor(cmax_u, 32));
+    set_k(row_exponent_k(cmax_g), row_exponent_k(cmax_u));
+  };
   if constexpr (STAGE) {
     // the first quad's weights are in flight while the block builds x'
     SkinnyChunk<BITS_G, BITS_U, RT> d;
     if (w < nquad) load(w, d);
-    row_k_finish();
+    if (single) {
+      if (w < nquad) chunk_k(d);
+      chunk_k_wave();
+    } else {
+      row_k_finish();
+    }
     const int nt = blockDim.x, nblk = p.M * (p.H >> 3);   // 8-value blocks of x
     if (tid < p.M) xmax[tid] = 0;
     __syncthreads();
-    row_k_read();
+    if (!single) row_k_read();
     for (int b = tid; b < nblk; b += nt) {              // row maxima of |x| (bf16 magnitude bits)
       const u32x4 v = *reinterpret_cast<const u32x4*>(p.x + 8 * (int64_t)b);
       uint32_t amax = 0;
@@ -753,29 +782,68 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
       compute(d);
     }
   } else if constexpr (!Q2) {
-    for (int q0 = w; q0 < nquad; q0 += nw) {
+    if (single) {
       SkinnyChunk<BITS_G, BITS_U, RT> d;
-      load(q0, d);
-      compute(d);
+      if (w < nquad) {
+        load(w, d);
+        chunk_k(d);
+      }
+      chunk_k_wave();
+      if (w < nquad) compute(d);
+    } else {
+      for (int q0 = w; q0 < nquad; q0 += nw) {
+        SkinnyChunk<BITS_G, BITS_U, RT> d;
+        load(q0, d);
+        compute(d);
+      }
     }
   } else {
     // two chunk quads in flight per wave, half the waves (a quad past the
     // end loads chunk 0 with zero scales and adds nothing)
-    for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
+    if (single) {
       SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
-      load(q0, d0);
-      load(q0 + nw, d1);
-      compute(d0);
-      compute(d1);
+      if (w < nquad) {
+        load(w, d0);
+        load(w + nw, d1);
+        chunk_k(d0);
+        chunk_k(d1);
+      }
+      chunk_k_wave();
+      if (w < nquad) {
+        compute(d0);
+        compute(d1);
+      }
+    } else {
+      for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
+        SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
+        load(q0, d0);
+        load(q0 + nw, d1);
+        compute(d0);
+        compute(d1);
+      }
     }
   }
 
-  // the waves' partial sums; D element j of lane l is row 4 (l / 16) + j, column l % 16
+  // the waves' partial sums in their true scale, times 2^(k + e) (weight
+  // column and x row; one scaling, so no intermediate leaves the range of
+  // the sums themselves); D element j of lane l is row 4 (l / 16) + j,
+  // column l % 16
   __shared__ f32x4 red[kSkinnyMaxWaves][2 * RT][64];
+  {
+    const int kg_ = k_gate(), ku_ = k_up();
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    red[w][2 * t][lane] = ag[t];
-    red[w][2 * t + 1][lane] = au[t];
+    for (int t = 0; t < RT; ++t) {
+      f32x4 a = ag[t], b = au[t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 16 * t + 4 * h + j;
+        const int e = m < p.M ? (STAGE ? xe[m] : p.xexp[m]) : 0;
+        a[j] = ldexpf(a[j], kg_ + e);
+        b[j] = ldexpf(b[j], ku_ + e);
+      }
+      red[w][2 * t][lane] = a;
+      red[w][2 * t + 1][lane] = b;
+    }
   }
   __syncthreads();
   // element j of D (row 16 t + 4 h + j) of tile t: wave 4 t + j sums it over
@@ -789,10 +857,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
       u += red[ww][2 * t + 1][lane][j];
     }
     const int m = 16 * t + 4 * h + j;
-    if (m < p.M && col < p.I) {
-      const int e = STAGE ? xe[m] : p.xexp[m];
-      store_out(p, m, col, ldexpf(g, e + k_gate()), ldexpf(u, e + k_up()));
-    }
+    if (m < p.M && col < p.I) store_out(p, m, col, g, u);
   }
 }
 
@@ -874,6 +939,25 @@ bool gemv1_rows_enabled() {
   return on;
 }
 
+// Waves per block of the few-row kernel and whether it takes two chunk quads
+// per pass (the launcher's choice below).
+static void skinny_shape(int M, int H, int bits_g, int bits_u, bool prep_fed, int* waves, bool* two) {
+  const int quads = (H / 32 + 3) / 4;
+  // (equal widths of at most 4 bits: mixed 2- and 4-bit codes would not fit
+  // two quads in the registers of four waves per SIMD)
+  const bool narrow = bits_g <= 4 && bits_u <= 4 && bits_g == bits_u;
+  *two = narrow && prep_fed && (M > 16 || H <= 2048);
+  const int per = *two ? (quads + 1) / 2 : quads;
+  *waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
+}
+
+bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
+  int waves;
+  bool two;
+  skinny_shape(M, H, bits_g, bits_u, true, &waves, &two);
+  return (H / 32 + 3) / 4 > (two ? 2 : 1) * waves;
+}
+
 template <int BG, int BU>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
@@ -897,14 +981,14 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
   // one wave per chunk quad (two quads with two row tiles, x' from the prep
-  // kernel), at most kSkinnyMaxWaves per block of 16 columns
-  const int quads = (p.H / 32 + 3) / 4;
-  // two quads in flight: measured faster with two row tiles everywhere, and
-  // with one up to H = 2048 (slower beyond, at half the waves per SIMD)
-  constexpr bool kNarrow = BG <= 4 && BU <= 4;
-  const bool two = kNarrow && p.xa != nullptr && (p.M > 16 || p.H <= 2048);
-  const int per = two ? (quads + 1) / 2 : quads;
-  const int waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
+  // kernel), at most kSkinnyMaxWaves per block of 16 columns; two quads in
+  // flight: measured faster with two row tiles everywhere, and with one up
+  // to H = 2048 (slower beyond, at half the waves per SIMD)
+  constexpr bool kNarrow = BG <= 4 && BU <= 4 && BG == BU;
+  int waves;
+  bool two;
+  skinny_shape(p.M, p.H, BG, BU, p.xa != nullptr, &waves, &two);
+  if (p.xa != nullptr && p.kexp == nullptr && skinny_needs_kexp(p.M, p.H, BG, BU)) return hipErrorInvalidValue;
   const dim3 g((p.I + 15) / 16), b(64 * waves);
   if (p.xa == nullptr) {
     if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;

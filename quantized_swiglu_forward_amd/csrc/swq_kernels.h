@@ -119,12 +119,16 @@ inline int kext_columns(int64_t H, int g0) {
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
-// The x rows of the prep kernel (x' and row exponents) and its column blocks
-// in k_only mode (weight-row exponents), for the matrix-vector path.
+// The x rows of the prep kernel (x' and row exponents), and with k_only its
+// weight rows' exponents, for the matrix-vector path.
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // cfg: tile shape (kMfmaBM/kMfmaBN); n_split > 0 with cfg 0: columns
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
+// Whether the few-row kernel, fed x' by the prep kernel, needs the weight-row
+// exponents from the prep kernel's k-only rows (a row longer than one pass of
+// its waves); otherwise it takes them from the scales its first pass loads.
+bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u);
 
 }  // namespace swq

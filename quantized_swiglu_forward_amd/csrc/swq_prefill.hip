@@ -122,24 +122,23 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
 }
 
-// Column blocks.  Block cb handles output features [32 cb, 32 cb + 32) of
-// both matrices: every thread-quad owns one (feature, matrix) row.
-//
-// 1. Row exponent k of each (feature, matrix) row (row_exponent_k): the
-//    row's scales and constants are stored times 2^-k, and the MFMA
-//    kernel's epilogue multiplies the sums by 2^k.
-// 2. Extra-column B rows: for eight g0-groups per slot, (c_hi, c_lo, c_hi)
-//    of c 2^-k split into two binary16 parts, zeros past the last group,
-//    three 16-byte stores per slot (a row is kext*2 bytes, a multiple of 64,
-//    so each store lies wholly inside or outside it).
-// 3. Scale tiles: for every super-step (128 inputs), the binary16 pair
-//    (s 2^-k, s 2^-k) of each column's group per K-step and matrix.  Columns
-//    past the matrix's rows and K-steps past H get zeros; the blocks cover
-//    whole 128-column tiles.
-constexpr int kColBlock = 32;                 // output features per column block
-constexpr int kSlotsReg = 4;                  // extra-column slots a thread keeps in registers
-constexpr int kPrepLdsGroups = 128;           // groups per row staged in LDS for the scale tiles
-
+// Weight rows.  Thread ((n * 2 + matrix) << lg) + c owns extra-column slot c
+// (eight g0-groups) of output feature n of one matrix and the scale-tile
+// words of the K-steps those groups cover.  The 2^lg threads of a row are
+// consecutive lanes of one wave (2^lg <= 64), so the row exponent k
+// (row_exponent_k) is a maximum over those lanes; a row with more than 64
+// slots gives each thread slots c, c + 64, ... (loaded once for the maximum
+// and again for the stores).  Each thread then writes
+//  - the slot's extra-column B row entries (c_hi, c_lo, c_hi) of c 2^-k, with
+//    c = b + z s in float32 and zeros past the last group, as three 16-byte
+//    stores (a row is kext*2 bytes, a multiple of 64, so each store lies
+//    wholly inside or outside it);
+//  - for every K-step (32 inputs) of its groups below H, the scale-tile word
+//    (s 2^-k, s 2^-k) in binary16 of that K-step's group;
+//  - (slot 0) k itself, for the MFMA kernel's epilogue.
+// With k_only (the matrix-vector path) only k is written.  The MFMA kernel
+// never reads scale-tile words of K-steps past H or of columns past the rows,
+// and they are left unwritten.
 struct RowSpec {
   const uint16_t* S;
   const uint16_t* B;
@@ -160,8 +159,8 @@ __device__ __forceinline__ RowSpec row_spec(const PrepParams& p, int mat) {
   return r;
 }
 
-// Raw scales and biases of the eight g0-groups of extra-column slot `slot`
-// of row n (indices clamped into the row).
+// Raw scales and biases of the eight g0-groups of slot `slot` of row n
+// (indices clamped into the row).
 __device__ __forceinline__ void load_slot(const RowSpec& r, int64_t n, int lg_g0, int ngroups, int slot,
                                           uint16_t (&sv)[8], uint16_t (&bv)[8]) {
 #pragma unroll
@@ -177,16 +176,15 @@ __device__ __forceinline__ float slot_max(const RowSpec& r, int ngroups, int slo
                                           const uint16_t (&bv)[8]) {
   float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (8 * slot + j >= ngroups) continue;
-    m = fmaxf(m, group_term_max(bf16_to_f32(sv[j]), bf16_to_f32(bv[j]), r.z, r.F));
-  }
+  for (int j = 0; j < 8; ++j)
+    if (8 * slot + j < ngroups) m = fmaxf(m, group_term_max(bf16_to_f32(sv[j]), bf16_to_f32(bv[j]), r.z, r.F));
   return m;
 }
 
-// (c_hi, c_lo, c_hi) of c 2^-k for the slot's eight g0-groups; c = b + z s in float32.
-__device__ __forceinline__ void store_slot(const RowSpec& r, int ngroups, int slot, int k, const uint16_t (&sv)[8],
-                                           const uint16_t (&bv)[8], int kext, unsigned char* row) {
+// The slot's extra-column entries and scale-tile words (see above).
+__device__ __forceinline__ void store_slot(const PrepParams& p, const RowSpec& r, int mat, int64_t n, int lg_g0,
+                                           int ngroups, int slot, int k, const uint16_t (&sv)[8],
+                                           const uint16_t (&bv)[8]) {
   f16x8 h[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -200,135 +198,90 @@ __device__ __forceinline__ void store_slot(const RowSpec& r, int ngroups, int sl
     h[(3 * j + 1) >> 3][(3 * j + 1) & 7] = clo;
     h[(3 * j + 2) >> 3][(3 * j + 2) & 7] = chi;
   }
+  unsigned char* row = reinterpret_cast<unsigned char*>((mat ? p.bext_u : p.bext_g) + n * p.kext);
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     const int off = 48 * slot + 16 * q;
-    if (off < kext * 2) *reinterpret_cast<f16x8*>(row + off) = h[q];
+    if (off < p.kext * 2) *reinterpret_cast<f16x8*>(row + off) = h[q];
+  }
+  // scale-tile words: K-steps (8 slot + j) g0/32 + u, u < g0/32, of group sv[j]
+  const int s_main = p.H >> 5, per = 1 << (lg_g0 - 5);
+  uint32_t* tile = p.scl + (n >> 7) * (int64_t)p.nss * kScaleTileWords + mat * kScaleTileCols + (n & 127);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const _Float16 hs = (_Float16)ldexpf(bf16_to_f32(sv[j]), -k);
+    const uint32_t word = as_u32((f16x2){hs, hs});
+    const int t0 = (8 * slot + j) * per;
+    for (int u = 0; u < per; ++u) {
+      const int t = t0 + u;
+      if (t < s_main) tile[(int64_t)(t >> 2) * kScaleTileWords + (t & 3) * 2 * kScaleTileCols] = word;
+    }
   }
 }
 
-// FAST: every row's slots fit kSlotsReg per thread and its groups the LDS row
-// (the scale tiles then read the scales from LDS); otherwise the slots are
-// loaded twice and the scale tiles read the scales from global memory.
-template <bool FAST>
-__device__ __forceinline__ void prep_columns(const PrepParams& p, int cb) {
-  __shared__ int kl[2][kColBlock];                              // row exponents k
-  __shared__ uint16_t srow[FAST ? 2 : 1][FAST ? kColBlock : 1][FAST ? kPrepLdsGroups : 1];
-  const int tid = threadIdx.x;
-  const int pair = tid >> 2, sub = tid & 3;
-  const int mat = pair >> 5, col = pair & (kColBlock - 1);
-  const int64_t n = (int64_t)cb * kColBlock + col;
-  const int rows = mat ? p.I_u : p.I;
-  const bool live = n < rows;
+// Threads per weight row: the slots (padding included) rounded up to a
+// power of two, at most a wavefront.  Host and device agree on it.
+__host__ __device__ inline int prep_row_lg(int kext) {
+  const int per_row = (kext + 23) / 24;
+  int lg = 0;
+  while ((1 << lg) < per_row && lg < 6) ++lg;
+  return lg;
+}
+
+__device__ __forceinline__ void prep_weight_rows(const PrepParams& p, int64_t idx) {
+  const int lg = prep_row_lg(p.kext);
+  const int c = (int)(idx & ((1 << lg) - 1));
+  const int64_t pair = idx >> lg;
+  const int64_t n = pair >> 1;
+  const int mat = (int)(pair & 1);
+  if (n >= p.I) return;                                 // whole rows: the lanes of a row leave together
+  const bool live = n < (mat ? p.I_u : p.I);            // up rows past I_u: none (k = 0)
   const RowSpec r = row_spec(p, mat);
   const int lg_g0 = __builtin_ctz(p.g0);
   const int ngroups = p.H >> lg_g0;
-  const int per_row = (p.kext + 23) / 24;                       // slots, padding included
-  unsigned char* erow = reinterpret_cast<unsigned char*>((mat ? p.bext_u : p.bext_g) + n * p.kext);
-
-  // 1 + 2: row maximum over the quad, k, extra-column rows
+  const int per_row = (p.kext + 23) / 24;
+  const int step = 1 << lg;
   float vmax = 0.0f;
-  if constexpr (FAST) {
-    uint16_t sv[kSlotsReg][8], bv[kSlotsReg][8];
-#pragma unroll
-    for (int i = 0; i < kSlotsReg; ++i) {
-      const int slot = sub + 4 * i;
-      if (live && slot < per_row) load_slot(r, n, lg_g0, ngroups, slot, sv[i], bv[i]);
+  int k;
+  if (per_row <= step) {                                // one slot per thread: keep it in registers
+    uint16_t sv[8], bv[8];
+    const bool mine = live && c < per_row;
+    if (mine) {
+      load_slot(r, n, lg_g0, ngroups, c, sv, bv);
+      vmax = slot_max(r, ngroups, c, sv, bv);
     }
-#pragma unroll
-    for (int i = 0; i < kSlotsReg; ++i) {
-      const int slot = sub + 4 * i;
-      if (live && slot < per_row) {
-        vmax = fmaxf(vmax, slot_max(r, ngroups, slot, sv[i], bv[i]));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int G = 8 * slot + j;
-          if (G < ngroups) srow[mat][col][(G << lg_g0) >> r.lg_gs] = sv[i][j];   // g0 < gs: same value twice
-        }
-      }
-    }
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
-    const int k = row_exponent_k(vmax);
-#pragma unroll
-    for (int i = 0; i < kSlotsReg; ++i) {
-      const int slot = sub + 4 * i;
-      if (live && slot < per_row && !p.k_only) store_slot(r, ngroups, slot, k, sv[i], bv[i], p.kext, erow);
-    }
-    if (sub == 0) kl[mat][col] = k;
-    if (sub == 0 && n < p.I) p.kexp[(int64_t)mat * p.I + n] = k;   // 0 for missing up rows
+    for (int off = 1; off < step; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    k = row_exponent_k(vmax);
+    if (mine && !p.k_only) store_slot(p, r, mat, n, lg_g0, ngroups, c, k, sv, bv);
   } else {
-    for (int slot = sub; live && slot < per_row; slot += 4) {
+    for (int slot = c; live && slot < per_row; slot += step) {
       uint16_t sv[8], bv[8];
       load_slot(r, n, lg_g0, ngroups, slot, sv, bv);
       vmax = fmaxf(vmax, slot_max(r, ngroups, slot, sv, bv));
     }
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 1));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 2));
-    const int k = row_exponent_k(vmax);
-    for (int slot = sub; live && !p.k_only && slot < per_row; slot += 4) {
+    for (int off = 1; off < step; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    k = row_exponent_k(vmax);
+    for (int slot = c; live && !p.k_only && slot < per_row; slot += step) {
       uint16_t sv[8], bv[8];
       load_slot(r, n, lg_g0, ngroups, slot, sv, bv);
-      store_slot(r, ngroups, slot, k, sv, bv, p.kext, erow);
-    }
-    if (sub == 0) kl[mat][col] = k;
-    if (sub == 0 && n < p.I) p.kexp[(int64_t)mat * p.I + n] = k;   // 0 for missing up rows
-  }
-  if (p.k_only) return;                                         // block-uniform
-  __syncthreads();
-
-  // 3: scale tiles.  Thread (matrix, K-step q, column) writes one word per
-  // super-step: 32 consecutive words of a (K-step, matrix) row per 32 threads.
-  {
-    const int c3 = tid & (kColBlock - 1), q = (tid >> 5) & 3, m3 = tid >> 7;
-    const int64_t n3 = (int64_t)cb * kColBlock + c3;
-    const bool live3 = n3 < (m3 ? p.I_u : p.I);
-    const RowSpec r3 = row_spec(p, m3);
-    const int k3 = kl[m3][c3];
-    const int s_main = p.H >> 5;
-    const int tile = cb / (kScaleTileCols / kColBlock);
-    const int word = (2 * q + m3) * kScaleTileCols + (cb % (kScaleTileCols / kColBlock)) * kColBlock + c3;
-    uint32_t* dst = p.scl + (int64_t)tile * p.nss * kScaleTileWords + word;
-    constexpr int U = 4;                                        // super-steps per batch of loads
-    for (int j0 = 0; j0 < p.nss; j0 += U) {
-      uint16_t sv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ks = 4 * (j0 + u) + q;
-        const bool ok = live3 && ks < s_main;
-        const int gi = ok ? ((32 * ks) >> r3.lg_gs) : 0;
-        if constexpr (FAST) sv[u] = ok ? srow[m3][c3][gi] : (uint16_t)0;
-        else sv[u] = ok ? r3.S[n3 * r3.ng + gi] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (j0 + u >= p.nss) continue;
-        const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sv[u]), -k3);
-        dst[(int64_t)(j0 + u) * kScaleTileWords] = as_u32((f16x2){h, h});
-      }
+      store_slot(p, r, mat, n, lg_g0, ngroups, slot, k, sv, bv);
     }
   }
+  if (c == 0) p.kexp[(int64_t)mat * p.I + n] = k;
 }
 
-// Index helpers of the prep grid (host and device agree on them).
-__host__ __device__ inline int64_t prep_col_blocks(int I) {        // whole 128-column tiles
-  return (int64_t)(I + kScaleTileCols - 1) / kScaleTileCols * (kScaleTileCols / kColBlock);
-}
-__host__ __device__ inline bool prep_fast(const PrepParams& p) {
-  const int per_row = (p.kext + 23) / 24;
-  return (per_row + 3) / 4 <= kSlotsReg && (p.H / p.gs_g) <= kPrepLdsGroups && (p.H / p.gs_u) <= kPrepLdsGroups;
-}
-
-// Blocks [0, M): x rows.  Then the column blocks, kColBlock output features
-// of both matrices each, over whole 128-column tiles.
+// Blocks [0, M): x rows.  Then the weight rows, 2^lg threads each (whole
+// rows per wave: 256 is a multiple of 2^lg).
 __global__ __launch_bounds__(256) void swq_prep_kernel(PrepParams p) {
   if ((int)blockIdx.x < p.M) {
     prep_x_row(p, blockIdx.x);
     return;
   }
-  const int cb = (int)blockIdx.x - p.M;
-  if (prep_fast(p)) prep_columns<true>(p, cb);
-  else prep_columns<false>(p, cb);
+  prep_weight_rows(p, ((int64_t)blockIdx.x - p.M) * 256 + threadIdx.x);
+}
+
+__host__ __device__ inline int64_t prep_row_blocks(int I, int kext) {
+  return ((2 * (int64_t)I << prep_row_lg(kext)) + 255) / 256;
 }
 
 // ----------------------------------------------------------- MFMA GEMM ----
@@ -902,14 +855,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const int64_t blocks = p.M + prep_col_blocks(p.I);
+  const int64_t blocks = p.M + prep_row_blocks(p.I, p.kext);
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream) {
-  if (!p.k_only) return hipErrorInvalidValue;
-  const int64_t blocks = p.M + prep_col_blocks(p.I);
+  const int64_t blocks = p.M + (p.k_only ? prep_row_blocks(p.I, p.kext) : 0);
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

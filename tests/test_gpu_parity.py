@@ -111,6 +111,8 @@ RANGE_LAWS = [
     ("mixed-groups", (4, 64, 8, 32), ("mixed", -20, 14), "factor"),
     ("bias1e5", (4, 64, 4, 64), ("pow", -7), ("uniform", 1e5)),
     ("8bit-mixed-bias1e5", (8, 32, 2, 64), ("mixed", -20, 10), ("uniform", 1e5)),
+    ("x2p60-s2m60", (4, 64, 8, 32), ("pow", -60), "factor", 60),
+    ("x2m50-s2p20", (4, 32, 4, 64), ("mixed", 10, 20), "factor", -50),
 ]
 # (M, H, I, path): the M = 1 kernel, its several-row form, the few-row kernel
 # with x' built in the block and from the prep kernel (one and two row tiles),
@@ -120,9 +122,9 @@ RANGE_SHAPES = [(1, 1024, 130, GEMV), (3, 2048, 70, GEMV), (6, 512, 97, GEMV), (
 RANGE_CASES = [(law, shape) for law in RANGE_LAWS for shape in RANGE_SHAPES]
 
 
-def _range_problem(M, H, I, spec, s_law, b_law, seed):
+def _range_problem(M, H, I, spec, s_law, b_law, seed, x_exp=0):
     bits_g, gs_g, bits_u, gs_u = spec
-    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=seed)
+    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=seed, x_sigma=float(2.0 ** x_exp))
     rng = np.random.default_rng(seed)
     for tag, bits, gs in (("g", bits_g, gs_g), ("u", bits_u, gs_u)):
         shape = (I, H // gs)
@@ -146,10 +148,11 @@ def _range_problem(M, H, I, spec, s_law, b_law, seed):
 @pytest.mark.parametrize("law,shape", RANGE_CASES,
                          ids=[f"{l[0]}-M{sh[0]}-H{sh[1]}-p{sh[3]}" for l, sh in RANGE_CASES])
 def test_scale_and_bias_range(law, shape):
-    name, spec, s_law, b_law = law
+    name, spec, s_law, b_law = law[:4]
+    x_exp = law[4] if len(law) > 4 else 0
     M, H, I, path = shape
     mode = (len(name) + M) % 3
-    p = _range_problem(M, H, I, spec, s_law, b_law, seed=M * 131 + H + len(name))
+    p = _range_problem(M, H, I, spec, s_law, b_law, seed=M * 131 + H + len(name), x_exp=x_exp)
     say("range", name, M, H, I, spec, "mode", mode, "path", path)
     o = oracle_full(p, mode)
     g, u = device_gemm(p, path)
