@@ -8,13 +8,21 @@ one of 40 distinct weight sets in rotation (about 520 MB, more than the
 ``value`` is weight GB/s over the timed steps.  The 1000 calls of a step are
 recorded once into a HIP graph and replayed.
 
-Also reported on the same JSON line: the roofline fraction of the decode
-kernel, the CPU oracle on a bounded sample (the baseline), and the
-matrix-matrix path on the three prefill configurations (TFLOP/s and fraction
-of the bf16/f16 dense MFMA peak).
+Also reported on the same JSON line:
+  * ``roofline`` of the decode kernel against 8 TB/s, with ``practical``: a
+    read-only stream of the same bytes in the same 1000-launch graph (what one
+    launch per call costs before any arithmetic);
+  * ``mfma_measured_peak``: the sustained dense f16 MFMA rate of this GPU on
+    random and on kernel-like operands (the MFMA pipes are power limited);
+  * ``prefill``: configurations 0 and 2-4, each with value, unit and a
+    ``roofline`` block (TFLOP/s against the 2.5 PFLOP/s spec and the measured
+    rate; HBM traffic from committed counter summaries);
+  * ``cpu_baseline``: the CPU oracle on bounded samples of every
+    configuration, with all cores (up to 16) and with one, and the CPU model.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|c2|c3|c4|copy]
-                    [--no-prefill] [--no-linear] [--no-cpu] [--eager]
+                    [--no-prefill] [--no-linear] [--no-mlp] [--no-small-batch] [--no-cpu]
+                    [--cpu-seconds S] [--eager]
 
 Unless ``--no-linear``: the quantized linear ``y = x W^T`` at the two down
 projections (decode model: M=1, K=5632, N=2048 with rotating weights as
@@ -55,18 +63,23 @@ def algorithmic_bytes(c, out_bytes=2):
     return weight_bytes(c) + c.M * c.H * 2 + c.M * c.I * out_bytes
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_gemv_M1_H2048_I5632_hbm_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_PROFILE = os.path.join(PROFILES, "decode_gemv_M1_H2048_I5632_hbm_traffic.md")
 GEMV_SOURCES = ["swq_gemv.hip", "swq_device.h", "swq_kernels.h"]
+PREFILL_SOURCES = ["swq_prefill.hip", "swq_device.h", "swq_kernels.h"]
+PREFILL_TRAFFIC = {2: "prefill_mfma_M512_H2048_I8192_hbm_traffic.md",
+                   3: "prefill_mfma_M2048_H4096_I14336_hbm_traffic.md",
+                   4: "prefill_mfma_M8192_H2560_I10240_hbm_traffic.md"}
 
 
-def gemv_source_digest():
-    """First 16 hex digits of the SHA-256 of the decode kernel's sources with
-    comments and blank space removed (so an edit of comments alone keeps the
-    measured traffic valid)."""
+def source_digest(files):
+    """First 16 hex digits of the SHA-256 of kernel sources with comments and
+    blank space removed (so an edit of comments alone keeps a measured
+    traffic figure valid)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in GEMV_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
@@ -75,20 +88,28 @@ def gemv_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter
+def gemv_source_digest():
+    return source_digest(GEMV_SOURCES)
+
+
+def profile_traffic(path, files, key):
+    """HBM bytes per launch (or per call) from a committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or
-    None when the decode kernel's sources changed since it was taken."""
+    None when the kernel's sources changed since the counters were taken."""
     try:
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(path) as fh:
             for line in fh:
                 if line.startswith("traffic-json:"):
                     rec = json.loads(line.split(":", 1)[1])
-                    if rec.get("source") == gemv_source_digest():
-                        return int(rec["bytes_per_launch"])
+                    if rec.get("source") == source_digest(files):
+                        return int(rec[key])
     except (OSError, ValueError, KeyError):
         pass
     return None
+
+
+def measured_traffic():
+    return profile_traffic(TRAFFIC_PROFILE, GEMV_SOURCES, "bytes_per_launch")
 
 
 def rotating_weight_sets(c, base_dev, n_sets, seed):
@@ -112,6 +133,83 @@ def rotating_weight_sets(c, base_dev, n_sets, seed):
             one += [words, s, b]
         sets.append(tuple(one))
     return sets
+
+
+def probe_lib():
+    """The benchmark's yardstick kernels (libswq_probe.so, built beside the library)."""
+    import ctypes
+    path = os.path.join(ROOT, "quantized_swiglu_forward_amd", "libswq_probe.so")
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.swq_probe_mfma_f16.argtypes = [i32, i32, i32, vp, vp]
+    L.swq_probe_mfma_f16.restype = i32
+    L.swq_probe_read.argtypes = [vp, i64, vp, vp]
+    L.swq_probe_read.restype = i32
+    L.swq_probe_read_blocks.argtypes = [i64]
+    L.swq_probe_read_blocks.restype = i64
+    return L
+
+
+def practical_read(nbytes, steps, warmup):
+    """The decode call's practical ceiling: a read-only stream of exactly
+    ``nbytes`` per launch (16-byte nontemporal loads, one store per block),
+    1000 launches per step over 40 rotating buffers in one HIP graph, as the
+    decode calls run.  Returns the average launch time in microseconds."""
+    import torch
+    L = probe_lib()
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(ROTATING_SETS)]
+    sink = torch.empty(int(L.swq_probe_read_blocks(nbytes)), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step(sh):
+        for i in range(CALLS):
+            if L.swq_probe_read(bufs[i % ROTATING_SETS].data_ptr(), nbytes, sink.data_ptr(), sh) != 0:
+                raise RuntimeError("read probe launch failed")
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+    del g, bufs
+    return us
+
+
+def mfma_peak(pattern, iters=3000, reps=5):
+    """Sustained dense f16 MFMA rate (TFLOP/s) of back-to-back 32x32x16
+    MFMAs, four waves per block and four blocks per compute unit, timed with
+    HIP events over ``reps`` launches after one warm-up launch."""
+    import torch
+    L = probe_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 4 * cus
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        if L.swq_probe_mfma_f16(blocks, iters, pattern, sink.data_ptr(), stream.cuda_stream) != 0:
+            raise RuntimeError("MFMA probe launch failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            L.swq_probe_mfma_f16(blocks, iters, pattern, sink.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    flops = reps * blocks * 4 * iters * 4 * 32768.0
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def bench_decode(args):
@@ -212,6 +310,7 @@ def bench_decode(args):
     value = wb * CALLS / (ms_step * 1e-3) / 1e9
     avg_launch_us = ms * 1e3 / launches
     achieved = algorithmic_bytes(c) / (avg_launch_us * 1e-6) / 1e9
+    prac_us = practical_read(algorithmic_bytes(c), args.steps, max(1, args.warmup)) if graph is not None else None
     res = {
         "value": round(value, 2), "unit": "GB/s", "ms_per_step": round(ms_step, 4),
         "dtype": "f16",
@@ -226,23 +325,50 @@ def bench_decode(args):
                      "bytes_per_launch": algorithmic_bytes(c)},
         "wall_s": round(wall, 3),
     }
+    if prac_us is not None:
+        # a read-only kernel that streams the same bytes in the same graph of
+        # 1000 launches over 40 rotating buffers: what one launch per call
+        # costs on this GPU before any arithmetic
+        res["roofline"]["practical"] = {
+            "kernel": "read-only 16-byte stream of the same bytes per launch, same 1000-launch graph, 40 buffers",
+            "avg_launch_us": round(prac_us, 3),
+            "GB_per_s": round(algorithmic_bytes(c) / (prac_us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(algorithmic_bytes(c) / (prac_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(prac_us / avg_launch_us, 4)}
     if hot is not None:
         res["decode_hot_cache"] = hot
     return res
 
 
-def bench_prefill_one(cfg, steps, warmup, mode=0):
+_PROBLEMS = {}
+
+
+def problem(cfg):
+    """The seeded host problem of a configuration, drawn once per run."""
+    from synth import make_problem
+    if cfg not in _PROBLEMS:
+        _PROBLEMS[cfg] = make_problem(cfg, with_calls=(cfg == 1))
+    return _PROBLEMS[cfg]
+
+
+def bench_prefill_one(cfg, steps, warmup, mode=0, measured_peak=None):
+    """One prefill configuration: ``steps`` calls on one stream after
+    ``warmup``, timed with HIP events on that stream.  A call is two launches
+    (the prep kernel, then the MFMA kernel; three when the columns are split
+    in two launches), so the rate is a lower bound on the MFMA kernel's own.
+    Config 0 (latency bound) is timed as 200 calls in one HIP graph."""
     import torch
 
     import quantized_swiglu_forward_amd as swq
-    from synth import CONFIGS, make_problem
+    from synth import CONFIGS
 
     c = CONFIGS[cfg]
-    p = make_problem(cfg)
-    dev = swq.to_device(p)
-    del p
+    dev = swq.to_device(problem(cfg))
     out = torch.empty((c.M, c.I), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
     stream = torch.cuda.Stream()
+    pm = ["MATCH", "F32", "F32_BF16OUT"][mode]
+    config = {"workload": c.describe, "M": c.M, "H": c.H, "I": c.I, "bits_g": c.bits_g, "gs_g": c.gs_g,
+              "bits_u": c.bits_u, "gs_u": c.gs_u, "precision_mode": pm}
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             swq.forward(*dev, c.bits_g, c.gs_g, c.bits_u, c.gs_u, mode=mode, out=out, stream=stream)
@@ -255,8 +381,6 @@ def bench_prefill_one(cfg, steps, warmup, mode=0):
         ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
-    flops = 4.0 * c.M * c.H * c.I
-    tflops = flops / (ms * 1e-3) / 1e12
     if cfg == 0:
         # latency-bound (no roofline target): the calls recorded into one HIP
         # graph, so the host's launch rate does not set the figure
@@ -274,11 +398,24 @@ def bench_prefill_one(cfg, steps, warmup, mode=0):
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        return {"config": c.describe, "us_per_call": round(e0.elapsed_time(e1) * 1e3 / steps, 2),
-                "launch": "hip graph", "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
-    return {"config": c.describe, "ms_per_call": round(ms, 4), "tflops": round(tflops, 2),
-            "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-            "precision_mode": ["MATCH", "F32", "F32_BF16OUT"][mode]}
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        return {"metric": "fused quant-SwiGLU call latency (tiny prefill)", "value": round(us, 2),
+                "unit": "us per call", "higher_is_better": False, "dtype": "f16", "config": config,
+                "launch": "hip graph of 200 calls",
+                "roofline": {"bound": "latency", "note": "233,472 bytes and 4.72 MFLOP per call: no roofline"}}
+    flops = 4.0 * c.M * c.H * c.I
+    tflops = flops / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": profile_traffic(os.path.join(PROFILES, PREFILL_TRAFFIC[cfg]), PREFILL_SOURCES,
+                                       "bytes_per_call") if mode == 0 else None,
+            "flops_per_call": flops, "algorithmic_bytes_per_call": algorithmic_bytes(c, 4 if mode == 1 else 2)}
+    if measured_peak:
+        roof["measured_peak"] = round(measured_peak, 1)
+        roof["frac_of_measured_peak"] = round(tflops / measured_peak, 4)
+    return {"metric": "fused quant-SwiGLU TFLOP/s (prefill)", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "ms_per_call": round(ms, 4), "higher_is_better": True, "dtype": "f16", "config": config,
+            "roofline": roof}
 
 
 def bench_decode_rows(M, steps, warmup):
@@ -558,31 +695,74 @@ def bench_copy(args):
                        "bytes_read": nbytes, "bytes_written": nbytes, "avg_launch_us": round(us, 3)}}
 
 
-def cpu_baseline_decode(max_seconds=20.0):
-    """The oracle as it stands, on a bounded sample of the decode workload:
-    whole calls (all 5632 columns) on fresh x rows, until about max_seconds."""
-    import oracle
-    from synth import CONFIGS, make_problem
-
-    c = CONFIGS[1]
-    p = make_problem(1)
+def cpu_model():
     try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
-    calls = 0
-    t0 = time.perf_counter()
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(threads, seconds):
+    """The oracle as it stands (plain C, float64, one output element at a
+    time, threaded over elements) on the host, ``threads`` threads, for about
+    ``seconds`` per configuration: the decode workload as whole calls on its
+    fresh x rows (weight GB/s), config 0 as whole calls (us per call), and
+    configs 2-4 on random output elements in batches (TFLOP/s counted as
+    4 H flops per element, the call's 4 M H I over its M I elements)."""
+    import numpy as np
+
+    import oracle
+    from synth import CONFIGS
+
+    res = {}
+    # decode: whole calls on the fresh x rows
+    c = CONFIGS[1]
+    p = problem(1)
+    calls, t0 = 0, time.perf_counter()
+    x0 = p.x
     while True:
         p.x = p.xs[calls:calls + 1]
-        oracle.swiglu_pairs(p, 0, nthreads=cores, want=("h",))
+        oracle.swiglu_pairs(p, 0, nthreads=threads, want=("h",))
         calls += 1
         el = time.perf_counter() - t0
-        if el >= max_seconds or calls >= len(p.xs):
+        if el >= seconds or calls >= len(p.xs):
             break
-    gbs = weight_bytes(c) * calls / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{calls} decode calls (M=1, H=2048, I=5632, all columns, MATCH) in {el:.1f} s"}
+    p.x = x0
+    res["c1"] = {"value": round(weight_bytes(c) * calls / el / 1e9, 4), "unit": "GB/s",
+                 "sample": f"{calls} whole decode calls (all {c.I} outputs, MATCH) in {el:.2f} s"}
+    # config 0: whole calls
+    p = problem(0)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.swiglu_pairs(p, 0, nthreads=threads, want=("h",))
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds / 4:
+            break
+    res["c0"] = {"value": round(el / calls * 1e6, 1), "unit": "us per call",
+                 "sample": f"{calls} whole calls ({p.M * p.I} outputs, MATCH) in {el:.2f} s"}
+    for cfg in (2, 3, 4):
+        c = CONFIGS[cfg]
+        p = problem(cfg)
+        rng = np.random.default_rng(cfg)
+        batch = 32 * threads
+        n, t0 = 0, time.perf_counter()
+        while True:
+            ms = rng.integers(0, c.M, batch)
+            ns = rng.integers(0, c.I, batch)
+            oracle.swiglu_pairs(p, 0, ms, ns, nthreads=threads, want=("h",))
+            n += batch
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        res[f"c{cfg}"] = {"value": round(4.0 * c.H * n / el / 1e12, 8), "unit": "TFLOP/s",
+                          "sample": f"{n} random outputs of the {c.M} x {c.I} call (MATCH) in {el:.2f} s"}
+    return res
 
 
 def main():
@@ -597,6 +777,8 @@ def main():
     ap.add_argument("--no-mlp", action="store_true", help="skip the whole-MLP measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=2.5,
+                    help="CPU-baseline time per configuration and thread count")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -622,24 +804,26 @@ def main():
         return
     else:
         cfg = int(args.workload[1])
-        from synth import CONFIGS
         r = bench_prefill_one(cfg, args.steps, args.warmup)
-        c = CONFIGS[cfg]
-        line.update({"value": r["tflops"], "unit": "TFLOP/s", "ms_per_step": r["ms_per_call"], "dtype": "f16",
-                     "config": {"workload": c.describe, "M": c.M, "H": c.H, "I": c.I,
-                                "precision_mode": "MATCH"},
-                     "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": r["frac_of_mfma_peak"], "traffic": None}})
+        line.update({"metric": r["metric"], "value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_call"],
+                     "dtype": r["dtype"], "config": r["config"], "roofline": r["roofline"]})
     if args.workload == "decode" and not args.no_small_batch:
         log("decode, a few rows per call: timing ...")
         line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32)}
         torch.cuda.empty_cache()
     if not args.no_prefill:
+        log("MFMA probe: sustained f16 rate ...")
+        peaks = {"random_operands": round(mfma_peak(0), 1), "kernel_like_operands": round(mfma_peak(1), 1)}
+        line["mfma_measured_peak"] = {
+            "unit": "TFLOP/s", **peaks, "spec": MFMA_F16_PEAK_TFLOPS,
+            "kernel": "back-to-back v_mfma_f32_32x32x16_f16, 4 waves per block, 4 blocks per CU",
+            "used_as_measured_peak": "kernel_like_operands"}
         pre = {}
         for cfg, mode in ((0, 0), (2, 0), (2, 1), (3, 0), (4, 0)):
             log(f"prefill c{cfg} mode {mode}: timing ...")
             steps = 200 if cfg == 0 else 10
-            pre[f"c{cfg}_{['match', 'f32'][mode]}"] = bench_prefill_one(cfg, steps=steps, warmup=3, mode=mode)
+            pre[f"c{cfg}_{['match', 'f32'][mode]}"] = bench_prefill_one(
+                cfg, steps=steps, warmup=3, mode=mode, measured_peak=peaks["kernel_like_operands"])
             torch.cuda.empty_cache()
         line["prefill"] = pre
     if not args.no_linear:
@@ -653,8 +837,19 @@ def main():
                        "prefill": bench_mlp_prefill(10, 3)}
         torch.cuda.empty_cache()
     if not args.no_cpu:
-        log("cpu baseline: oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline_decode()
+        log("cpu baseline: the oracle on bounded samples of every configuration ...")
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        cores = max(1, min(16, cores))
+        many = cpu_baseline(cores, args.cpu_seconds)
+        one = cpu_baseline(1, args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": many["c1"]["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": many["c1"]["sample"], "cpu_model": cpu_model(),
+            "configs": {k: {"all_cores": many[k], "one_core": one[k]} for k in sorted(many)},
+            "one_core_value": one["c1"]["value"]}
     print(json.dumps(line), flush=True)
 
 

@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu_q.so")
 SOURCES = ["swq_api.hip", "swq_prefill.hip", "swq_gemv.hip"]
+# measurement yardsticks for the benchmark only (a library of their own)
+PROBE_LIB = os.path.join(PKG, "libswq_probe.so")
+PROBE_SOURCES = ["swq_probe.hip"]
 ARCH = os.environ.get("SWIGLU_Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,19 +38,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source and link ``libswiglu_q.so``; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, lib):
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every HIP source and link ``libswiglu_q.so`` (and the benchmark's
+    ``libswq_probe.so``); returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 
