@@ -65,3 +65,12 @@ def qmm_grouped_exact(x, W, S, B, M: int, H: int, N: int, bits: int, gs: int):
             row.append(tot)
         out.append(row)
     return out
+
+
+def qmm_sq_exact(x, W, S, B, M: int, H: int, N: int, bits: int, gs: int):
+    """Exact ``sum_k (x[m,k] w[n,k])^2`` as a list of lists of Fractions: the
+    square of the oracle's cancellation-free scale nu of each dot product."""
+    xs = [[bf16_exact(x[m][k]) for k in range(H)] for m in range(M)]
+    ws = [dequant_row(W[n], S[n], B[n], H, bits, gs) for n in range(N)]
+    return [[sum(((xs[m][k] * ws[n][k]) ** 2 for k in range(H)), Fraction(0)) for n in range(N)]
+            for m in range(M)]

@@ -74,6 +74,31 @@ def test_shape_sweep(M, H, I, spec, mode, path):
     check(y, oracle_full(p, mode), mode, f"sweep M{M} H{H} I{I} {spec} mode{mode} path{path}")
 
 
+# H not a multiple of 128: the MFMA kernel's last code super-step is partial
+# (one to three K-steps of four), on both tile shapes
+PARTIAL = [(70, 96, 130, (4, 32, 4, 32)), (300, 160, 200, (8, 32, 4, 32)), (129, 2080, 257, (2, 32, 8, 32)),
+           (600, 2080, 384, (4, 32, 4, 32))]
+
+
+@pytest.mark.parametrize("tiles", ["0", "1"], ids=["256x128", "128x128"])
+@pytest.mark.parametrize("M,H,I,spec", PARTIAL, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in PARTIAL])
+def test_partial_super_step(M, H, I, spec, tiles):
+    import os
+    p = make_custom(M, H, I, *spec, seed=M + H + I)
+    mode = (M + H) % 3
+    say("partial super-step", M, H, I, spec, "tiles", tiles, "mode", mode)
+    old = os.environ.get("SWIGLU_Q_MFMA_CFG")
+    os.environ["SWIGLU_Q_MFMA_CFG"] = tiles
+    try:
+        y = device_forward(p, mode, MFMA)
+    finally:
+        if old is None:
+            os.environ.pop("SWIGLU_Q_MFMA_CFG", None)
+        else:
+            os.environ["SWIGLU_Q_MFMA_CFG"] = old
+    check(y, oracle_full(p, mode), mode, f"partial M{M} H{H} tiles{tiles}")
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_random_specs_and_magnitudes(case):
     """Seeded random problems on both paths: any gate/up code widths and
@@ -260,16 +285,56 @@ def test_config1_fresh_inputs():
         check(y, oracle_full(q, 0), 0, f"c1 call {call}")
 
 
+def tile_cover_pairs(M, I, seed, tile=128):
+    """For every tile x tile block of an [M, I] output, one sample in each of
+    its rows and each of its columns (a random permutation within the block).
+    Every output tile of either MFMA tile shape (256 x 128 or 128 x 128, and
+    the columns of a split launch, which start on a multiple of 128) then has
+    a sample in every row -- every fragment and lane of every wave -- and in
+    every column -- every wave, 32-column slice and accumulator entry."""
+    rng = np.random.default_rng(seed)
+    ms, ns = [], []
+    for m0 in range(0, M, tile):
+        rows = min(tile, M - m0)
+        for n0 in range(0, I, tile):
+            cols = min(tile, I - n0)
+            k = max(rows, cols)
+            ms.append(m0 + np.arange(k) % rows)
+            ns.append(n0 + rng.permutation(k) % cols)
+    return np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+
+
+_FULL_ORACLE = {}
+
+
+def _full_size_oracle(cfg):
+    """Configuration 2 in full; 3 and 4 on tile-covering samples.  The
+    oracle's gate, up and scales do not depend on the precision mode, so one
+    evaluation serves every mode."""
+    if cfg not in _FULL_ORACLE:
+        p = make_problem(cfg)
+        c = CONFIGS[cfg]
+        if cfg == 2:
+            ms = ns = None
+        else:
+            ms, ns = tile_cover_pairs(c.M, c.I, seed=cfg)
+        o = oracle.swiglu_pairs(p, 1, ms, ns, want=("g", "u", "nu_g", "nu_u"))
+        _FULL_ORACLE.clear()                            # one configuration held at a time
+        _FULL_ORACLE[cfg] = (p, ms, ns, o)
+    return _FULL_ORACLE[cfg]
+
+
 @pytest.mark.parametrize("cfg,mode", [(2, 0), (2, 1), (2, 2), (3, 0), (3, 1), (4, 0), (4, 1)])
-def test_full_size_sampled(cfg, mode):
-    p = make_problem(cfg)
-    c = CONFIGS[cfg]
-    say(f"config{cfg} full size", "mode", mode)
+def test_full_size(cfg, mode):
+    """The prefill configurations at full size in the launch configuration
+    the benchmark times: every output of configuration 2, and at least one
+    output per row and per column of every 128 x 128 block of 3 and 4."""
+    p, ms, ns, o = _full_size_oracle(cfg)
+    say(f"config{cfg} full size", "mode", mode, "samples", "all" if ms is None else ms.size)
     y = device_forward(p, mode, None, expect_path=MFMA)
-    ms, ns = sample_pairs(c.M, c.I, 3000, seed=cfg * 10 + mode)
-    o = oracle_pairs(p, mode, ms, ns)
-    check(y[ms, ns], o, mode, f"c{cfg} mode{mode} sampled")
     assert np.all(np.isfinite(y))
+    got = y.reshape(-1) if ms is None else y[ms, ns]
+    check(got, o, mode, f"c{cfg} mode{mode} " + ("all outputs" if ms is None else f"{ms.size} tile-covering samples"))
 
 
 # large extents: H at 64 K inputs on every kernel (x' and the weight rows

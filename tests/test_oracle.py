@@ -114,6 +114,39 @@ def test_oracle_matches_exact_rationals(bits, gs, H):
 
 
 @pytest.mark.parametrize("bits,gs", SPECS)
+def test_nu_matches_exact_rationals(bits, gs):
+    """The scale nu = sqrt(sum_k (x_k w_k)^2) that sets every floor of the
+    comparison metric, against its exact rational value: float64 within
+    1e-14 relative of the exact square root, for the gate and the up matrix."""
+    M, H, I = 2, 128, 3
+    p = make_custom(M, H, I, bits, gs, 8 if bits != 8 else 4, 32, seed=bits * 13 + gs)
+    o = oracle.swiglu_full(p, mode=1, nthreads=1)
+    xg = [list(r) for r in p.x]
+    sq_g = exact.qmm_sq_exact(xg, p.wg, p.sg, p.bg, M, H, I, bits, gs)
+    sq_u = exact.qmm_sq_exact(xg, p.wu, p.su, p.bu, M, H, I, p.bits_u, p.gs_u)
+    for m in range(M):
+        for n in range(I):
+            for got, sq in ((o["nu_g"][m, n], sq_g[m][n]), (o["nu_u"][m, n], sq_u[m][n])):
+                ref = math.sqrt(float(sq))
+                assert ref > 0 and abs(got - ref) <= 1e-14 * ref, (got, ref)
+
+
+def test_nu_single_term_closed_form():
+    """With one nonzero input x_j, nu is exactly |x_j w_j| and the dot
+    product is x_j w_j (no other term contributes)."""
+    M, H, I = 1, 64, 5
+    p = make_custom(M, H, I, 4, 32, 4, 32, seed=3)
+    x = np.zeros((M, H), np.float32)
+    x[0, 37] = -1.5
+    p.x = to_bf16_bits(x)
+    o = oracle.swiglu_full(p, mode=1, nthreads=1)
+    codes = oracle.unpack(p.wg, I, H, 4)[:, 37].astype(np.float64)
+    w = bf16_bits_to_f32(p.sg[:, 1]).astype(np.float64) * codes + bf16_bits_to_f32(p.bg[:, 1]).astype(np.float64)
+    assert np.array_equal(o["nu_g"][0], np.abs(-1.5 * w))
+    assert np.array_equal(o["g"][0], -1.5 * w)
+
+
+@pytest.mark.parametrize("bits,gs", SPECS)
 def test_linear_reference_matches_exact_rationals(bits, gs):
     """The quantized linear's reference (``qmm``, and ``qmm_pairs`` element by
     element) against exact rational arithmetic, with an odd output size."""
