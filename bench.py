@@ -73,8 +73,9 @@ PREFILL_TRAFFIC = {2: "prefill_mfma_M512_H2048_I8192_hbm_traffic.md",
 
 
 def source_digest(files):
-    """First 16 hex digits of the SHA-256 of kernel sources with comments and
-    blank space removed (so an edit of comments alone keeps a measured
+    """First 16 hex digits of the SHA-256 of kernel sources with comments,
+    blank space and the LDS-poison debug blocks removed (so an edit of
+    comments, or of code the product build does not compile, keeps a measured
     traffic figure valid)."""
     import hashlib
     import re
@@ -82,6 +83,7 @@ def source_digest(files):
     for f in files:
         with open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "csrc", f)) as fh:
             src = fh.read()
+        src = re.sub(r"#ifdef SWQ_LDS_POISON.*?#endif", " ", src, flags=re.S)
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
         h.update(" ".join(src.split()).encode())
@@ -120,10 +122,10 @@ def rotating_weight_sets(c, base_dev, n_sets, seed):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     sets = [base_dev[1:]]
-    ng = c.H // c.gs_g
     for _ in range(n_sets - 1):
         one = []
-        for bits in (c.bits_g, c.bits_u):
+        for bits, gs in ((c.bits_g, c.gs_g), (c.bits_u, c.gs_u)):
+            ng = c.H // gs
             words = torch.randint(-2**31, 2**31 - 1, (c.I, c.H * bits // 32), generator=gen, device="cuda",
                                   dtype=torch.int64).to(torch.int32)
             s = (torch.rand((c.I, ng), generator=gen, device="cuda") * (c.s_hi - c.s_lo) + c.s_lo)
@@ -344,8 +346,11 @@ _PROBLEMS = {}
 
 
 def problem(cfg):
-    """The seeded host problem of a configuration, drawn once per run."""
+    """The seeded host problem of a configuration (an index or a Config),
+    drawn once per run."""
     from synth import make_problem
+    if not isinstance(cfg, int):
+        return make_problem(cfg, with_calls=False)
     if cfg not in _PROBLEMS:
         _PROBLEMS[cfg] = make_problem(cfg, with_calls=(cfg == 1))
     return _PROBLEMS[cfg]
@@ -362,7 +367,7 @@ def bench_prefill_one(cfg, steps, warmup, mode=0, measured_peak=None):
     import quantized_swiglu_forward_amd as swq
     from synth import CONFIGS
 
-    c = CONFIGS[cfg]
+    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
     dev = swq.to_device(problem(cfg))
     out = torch.empty((c.M, c.I), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
     stream = torch.cuda.Stream()
@@ -408,7 +413,7 @@ def bench_prefill_one(cfg, steps, warmup, mode=0, measured_peak=None):
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
             "traffic": profile_traffic(os.path.join(PROFILES, PREFILL_TRAFFIC[cfg]), PREFILL_SOURCES,
-                                       "bytes_per_call") if mode == 0 else None,
+                                       "bytes_per_call") if mode == 0 and cfg in PREFILL_TRAFFIC else None,
             "flops_per_call": flops, "algorithmic_bytes_per_call": algorithmic_bytes(c, 4 if mode == 1 else 2)}
     if measured_peak:
         roof["measured_peak"] = round(measured_peak, 1)
@@ -416,6 +421,58 @@ def bench_prefill_one(cfg, steps, warmup, mode=0, measured_peak=None):
     return {"metric": "fused quant-SwiGLU TFLOP/s (prefill)", "value": round(tflops, 2), "unit": "TFLOP/s",
             "ms_per_call": round(ms, 4), "higher_is_better": True, "dtype": "f16", "config": config,
             "roofline": roof}
+
+
+def bench_decode_spec(c, steps, warmup):
+    """The decode call (1000 calls per step on fresh x rows over 40 rotating
+    weight sets, one HIP graph) for another quantization spec of the decode
+    shape: per-call time and weight bytes per second."""
+    import numpy as np
+    import torch
+
+    import quantized_swiglu_forward_amd as swq
+
+    p = problem(c)
+    dev = swq.to_device(p)
+    sets = rotating_weight_sets(c, dev, ROTATING_SETS, seed=103)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    x = torch.randn((CALLS, c.H), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((CALLS, c.I), dtype=torch.bfloat16, device="cuda")
+    L = swq.lib()
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+
+    def step(sh):
+        for i in range(CALLS):
+            wg, sg, bg, wu, su, bu = ptrs[i % ROTATING_SETS]
+            rc = L.swiglu_q_forward(x.data_ptr() + i * c.H * 2, wg, sg, bg, wu, su, bu, 1, c.H, c.I, c.bits_g,
+                                    c.gs_g, c.bits_u, c.gs_u, 0, out.data_ptr() + i * c.I * 2, sh)
+            if rc != 0:
+                raise RuntimeError(f"swiglu_q_forward failed: {swq.swiglu_q_strerror(rc)}")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+    alg = algorithmic_bytes(c)
+    return {"config": c.describe, "avg_launch_us": round(us, 3),
+            "weight_GB_per_s": round(weight_bytes(c) / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
 
 
 def bench_decode_rows(M, steps, warmup):
@@ -826,6 +883,22 @@ def main():
                 cfg, steps=steps, warmup=3, mode=mode, measured_peak=peaks["kernel_like_operands"])
             torch.cuda.empty_cache()
         line["prefill"] = pre
+        # the other group size and the third precision mode
+        from dataclasses import replace
+        from synth import CONFIGS
+        log("spec variants: timing ...")
+        c3g = replace(CONFIGS[3], name="large_prefill_gs128", gs_g=128, gs_u=128,
+                      describe="large prefill M=2048 H=4096 I=14336, 4-bit gs128 gate/up")
+        c1g = replace(CONFIGS[1], name="decode_gs128", gs_g=128, gs_u=128, calls=0,
+                      describe="decode GEMV M=1 H=2048 I=5632, 4-bit gs128 gate/up, fresh x per call, "
+                               "40 rotating weight sets, hip graph")
+        line["spec_variants"] = {
+            "c3_gs128_match": bench_prefill_one(c3g, steps=10, warmup=3, mode=0,
+                                                measured_peak=peaks["kernel_like_operands"]),
+            "c2_f32_bf16out": bench_prefill_one(2, steps=10, warmup=3, mode=2,
+                                                measured_peak=peaks["kernel_like_operands"]),
+            "c1_gs128": bench_decode_spec(c1g, max(1, args.steps // 4), 2)}
+        torch.cuda.empty_cache()
     if not args.no_linear:
         log("linear: timing ...")
         line["linear"] = {"decode_down_proj": bench_linear(1, 5632, 2048, 4, 64, max(1, args.steps // 4), 2, True),

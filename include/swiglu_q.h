@@ -230,6 +230,17 @@ int swiglu_q_path_for(int64_t M, int64_t H);
 uint64_t swiglu_q_call_count(int path);
 void swiglu_q_reset_counts(void);
 
+/* Call cap for bisecting, the pages' debug cap on how many fused calls run
+ * ("mlx-bun 0.0.7 -> 0.0.9" diff, page 42, fused-swiglu-kernel.ts, the cap
+ * function and its caller's predicate): a caller that keeps an unfused path
+ * asks swiglu_q_under_cap() before each call and takes its own path once it
+ * returns 0.  The cap counts launched calls of both paths (the sum of
+ * swiglu_q_call_count); n < 0 removes it.  The default comes from the
+ * environment variable SWIGLU_Q_MAXCALLS (a non-negative integer), else no
+ * cap.  Host only: the library itself never refuses a call. */
+void swiglu_q_set_max_calls(int64_t n);
+int swiglu_q_under_cap(void);
+
 /* Human-readable text of a status code (static storage). */
 const char *swiglu_q_strerror(int status);
 

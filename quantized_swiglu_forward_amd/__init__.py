@@ -41,7 +41,15 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_swiglu_forward_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path):
+    """A ctypes handle on a build of the library at ``path`` (the product, or
+    its LDS-poison debug twin ``libswiglu_q_ldspoison.so``) with every entry
+    point's signature declared."""
+    L = ctypes.CDLL(path)
     vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
     L.swiglu_q_forward.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
     L.swiglu_q_forward.restype = i32
@@ -65,6 +73,10 @@ def lib():
     L.swiglu_q_call_count.restype = u64
     L.swiglu_q_reset_counts.argtypes = []
     L.swiglu_q_reset_counts.restype = None
+    L.swiglu_q_set_max_calls.argtypes = [i64]
+    L.swiglu_q_set_max_calls.restype = None
+    L.swiglu_q_under_cap.argtypes = []
+    L.swiglu_q_under_cap.restype = i32
     L.swiglu_q_strerror.argtypes = [i32]
     L.swiglu_q_strerror.restype = ctypes.c_char_p
     L.swiglu_q_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
@@ -73,7 +85,6 @@ def lib():
     L.swiglu_q_release_workspace.restype = i32
     L.swiglu_q_version.argtypes = []
     L.swiglu_q_version.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 
@@ -151,6 +162,14 @@ def swiglu_q_call_count(path: int) -> int:
 
 def swiglu_q_reset_counts() -> None:
     lib().swiglu_q_reset_counts()
+
+
+def swiglu_q_set_max_calls(n: int) -> None:
+    lib().swiglu_q_set_max_calls(n)
+
+
+def swiglu_q_under_cap() -> int:
+    return lib().swiglu_q_under_cap()
 
 
 def swiglu_q_strerror(status: int) -> str:

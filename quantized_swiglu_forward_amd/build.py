@@ -18,6 +18,10 @@ SOURCES = ["swq_api.hip", "swq_prefill.hip", "swq_gemv.hip"]
 # measurement yardsticks for the benchmark only (a library of their own)
 PROBE_LIB = os.path.join(PKG, "libswq_probe.so")
 PROBE_SOURCES = ["swq_probe.hip"]
+# debug build of the same library whose kernels poison their LDS before use
+# (read by a GPU test only)
+POISON_LIB = os.path.join(PKG, "libswiglu_q_ldspoison.so")
+POISON_FLAGS = ["-DSWQ_LDS_POISON"]
 ARCH = os.environ.get("SWIGLU_Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,9 +33,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, extra = job if isinstance(job, tuple) else (job, [])
+    tag = "_poison" if extra else ""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -48,16 +54,21 @@ def _link(objs, lib):
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source and link ``libswiglu_q.so`` (and the benchmark's
-    ``libswq_probe.so``); returns the library's path."""
+    """Compile every HIP source and link ``libswiglu_q.so``, its LDS-poison
+    debug twin and the benchmark's ``libswq_probe.so`` (all objects in
+    parallel); returns the library's path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+    jobs = SOURCES + PROBE_SOURCES + [(src, POISON_FLAGS) for src in SOURCES]
+    workers = min(len(jobs), max(1, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n, m = len(SOURCES), len(PROBE_SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + m], PROBE_LIB)
+    _link(objs[n + m:], POISON_LIB)
     if verbose:
-        print(f"built {LIB}")
-        print(f"built {PROBE_LIB}")
+        for lib in (LIB, PROBE_LIB, POISON_LIB):
+            print(f"built {lib}")
     return LIB
 
 

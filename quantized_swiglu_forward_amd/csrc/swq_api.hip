@@ -35,6 +35,22 @@ constexpr int kDefaultThreshold = kGemvMaxM + 1;
 
 std::atomic<int> g_threshold{-1};
 std::atomic<uint64_t> g_calls[2];
+// Call cap (<0: none; -2: not yet read from the environment)
+std::atomic<int64_t> g_max_calls{-2};
+
+int64_t max_calls_now() {
+  int64_t v = g_max_calls.load();
+  if (v != -2) return v;
+  v = -1;
+  if (const char* s = getenv("SWIGLU_Q_MAXCALLS")) {
+    char* end = nullptr;
+    const long long t = strtoll(s, &end, 10);
+    if (end != s && t >= 0) v = t;
+  }
+  int64_t expected = -2;
+  g_max_calls.compare_exchange_strong(expected, v);
+  return g_max_calls.load();
+}
 std::mutex g_ws_mutex;
 
 struct Workspace {
@@ -519,6 +535,13 @@ int swiglu_q_path_for(int64_t M, int64_t H) {
 uint64_t swiglu_q_call_count(int path) {
   if (path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return 0;
   return g_calls[path].load();
+}
+
+void swiglu_q_set_max_calls(int64_t n) { g_max_calls.store(n < 0 ? -1 : n); }
+
+int swiglu_q_under_cap(void) {
+  const int64_t cap = max_calls_now();
+  return cap < 0 || (int64_t)(g_calls[0].load() + g_calls[1].load()) < cap;
 }
 
 void swiglu_q_reset_counts(void) {

@@ -176,6 +176,19 @@ __device__ __forceinline__ float sigmoid_fast(float t) {
   return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Debug build (-DSWQ_LDS_POISON): every kernel fills its LDS with a poison
+// pattern before using it -- NaN bits for floating-point data, 2^30 for
+// integer exponents -- so that a read of LDS the kernel did not write first
+// shows in its results (the pages' threadgroup-zeroing diagnostic, with a
+// pattern that cannot pass for data).  The product build has none of it.
+#ifdef SWQ_LDS_POISON
+constexpr uint32_t kPoisonFloat = 0xFFFFFFFFu;   // NaN as float32 and as binary16 pairs
+constexpr uint32_t kPoisonExp = 0x40000000u;     // an exponent of 2^30
+__device__ __forceinline__ void lds_poison(void* p, size_t bytes, uint32_t pattern) {
+  for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(p)[i] = pattern;
+}
+#endif
+
 // Precision modes (values fixed by the public header).
 enum : int { kMatch = 0, kF32 = 1, kF32Bf16Out = 2 };
 // (the linear's epilogue kinds kLinBf16 / kLinF32 are in swq_kernels.h)

@@ -322,6 +322,11 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
   constexpr int XI = (256 * CPL + NT - 1) / NT;   // 8-value blocks of one row of x per thread
   __shared__ u32x4 xs[MR][256 * CPL];
   __shared__ float2 xinfo[MR][64 * CPL];
+#ifdef SWQ_LDS_POISON
+  lds_poison(xs, sizeof(xs), kPoisonFloat);
+  lds_poison(xinfo, sizeof(xinfo), kPoisonFloat);
+  __syncthreads();
+#endif
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if constexpr (FULL) lg = 6;
@@ -552,6 +557,15 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   // slowest wave's weights either way); the lanes of a column reduce with
   // two swaps, and the waves meet in LDS.
   __shared__ float kred[kSkinnyMaxWaves][32];
+  __shared__ f32x4 red[kSkinnyMaxWaves][2 * RT][64];   // the waves' partial sums (after the K loop)
+#ifdef SWQ_LDS_POISON
+  lds_poison(xs, sizeof(xs), kPoisonFloat);
+  lds_poison(xe, sizeof(xe), kPoisonExp);
+  lds_poison(xmax, sizeof(xmax), kPoisonExp);
+  lds_poison(kred, sizeof(kred), kPoisonFloat);
+  lds_poison(red, sizeof(red), kPoisonFloat);
+  __syncthreads();
+#endif
   auto row_k_finish = [&]() {
     const int kstride = blockDim.x >> 4;
     float kmax_g = 0.0f, kmax_u = 0.0f;
@@ -828,7 +842,6 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   // column and x row; one scaling, so no intermediate leaves the range of
   // the sums themselves); D element j of lane l is row 4 (l / 16) + j,
   // column l % 16
-  __shared__ f32x4 red[kSkinnyMaxWaves][2 * RT][64];
   {
     const int kg_ = k_gate(), ku_ = k_up();
 #pragma unroll

@@ -72,6 +72,10 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
   __shared__ uint32_t red[4];
+#ifdef SWQ_LDS_POISON
+  lds_poison(red, sizeof(red), kPoisonFloat);
+  __syncthreads();
+#endif
   if (lane == 0) red[wave] = amax;
   __syncthreads();
   amax = max(max(red[0], red[1]), max(red[2], red[3]));
@@ -413,6 +417,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   __shared__ __attribute__((aligned(16))) unsigned char smem[STAGES * STAGE + 2 * SS_SLOT];
   __shared__ int rexp[BM];
   __shared__ int rk[2][BN];
+#ifdef SWQ_LDS_POISON
+  lds_poison(smem, sizeof(smem), kPoisonFloat);
+  lds_poison(rexp, sizeof(rexp), kPoisonExp);
+  lds_poison(rk, sizeof(rk), kPoisonExp);
+  __syncthreads();
+#endif
   unsigned char* const ssmem = smem + STAGES * STAGE;   // code ring: two super-step slots
 
   const int tid = threadIdx.x;

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int pattern,
   sink[t] = s;
 }
 
-constexpr int kReadPerThread = 4;   // 16-byte pieces per thread
+constexpr int kReadPerThread = 2;   // 16-byte pieces per thread (1 and 2 measured fastest, 4 slower)
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, int64_t pieces, float* sink) {
   const int64_t base = (int64_t)blockIdx.x * 256 * kReadPerThread + threadIdx.x;

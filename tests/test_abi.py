@@ -303,3 +303,34 @@ def test_noalloc_rejects_oversized_calls_before_any_hip_call():
     assert swq.swiglu_q_forward_noalloc(**{**a, "precision_mode": 3}) == swq.SWQ_ERR_UNSUPPORTED
     assert swq.swiglu_q_forward_noalloc(**{**a, "out": P + 1}) == swq.SWQ_ERR_ALIGN
     assert "64 MiB" in swq.swiglu_q_strerror(swq.SWQ_ERR_TOO_LARGE)
+
+
+def test_call_cap_predicate():
+    """The bisecting cap: under_cap is 1 while fewer calls than the cap have
+    launched, and always 1 without a cap (host only; the library never
+    refuses a call itself)."""
+    swq.swiglu_q_reset_counts()
+    swq.swiglu_q_set_max_calls(-1)
+    assert swq.swiglu_q_under_cap() == 1
+    swq.swiglu_q_set_max_calls(0)
+    assert swq.swiglu_q_under_cap() == 0
+    swq.swiglu_q_set_max_calls(3)
+    assert swq.swiglu_q_under_cap() == 1
+    swq.swiglu_q_set_max_calls(-5)
+    assert swq.swiglu_q_under_cap() == 1
+
+
+def test_hip_failure_maps_to_err_hip():
+    """Without a GPU every HIP call fails; a valid call that reaches HIP (a
+    matrix-matrix call needs its workspace, a decode call launches, the
+    allocation-free call needs the scratch array's address) returns
+    SWQ_ERR_HIP instead of crashing.  Skipped where a GPU is visible: there the
+    fake pointers would reach a kernel."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a machine without a GPU")
+    base = dict(x=P, Wg=P, sg=P, bg=P, Wu=P, su=P, bu=P, H=256, I=64, bits_g=4, gs_g=64, bits_u=4,
+                gs_u=64, precision_mode=0, out=P, stream=0)
+    assert swq.swiglu_q_forward(**{**base, "M": 300}) == swq.SWQ_ERR_HIP
+    assert swq.swiglu_q_forward(**{**base, "M": 1}) == swq.SWQ_ERR_HIP
+    assert swq.swiglu_q_forward_noalloc(**{**base, "M": 300}) == swq.SWQ_ERR_HIP

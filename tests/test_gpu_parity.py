@@ -649,3 +649,24 @@ def test_leading_dimensions():
     torch.cuda.synchronize()
     assert tuple(shaped.shape) == (2, 3, 200)
     assert torch.equal(shaped.view(6, 200), flat)
+
+
+def test_call_cap_counts_launched_calls():
+    """The bisecting cap turns the predicate off after that many launched
+    calls, of either path."""
+    p = make_custom(4, 256, 64, 4, 64, seed=6)
+    dev = swq.to_device(p)
+    say("call cap")
+    swq.swiglu_q_reset_counts()
+    swq.swiglu_q_set_max_calls(2)
+    try:
+        assert swq.swiglu_q_under_cap() == 1
+        swq.forward(*dev, 4, 64)
+        assert swq.swiglu_q_under_cap() == 1
+        with forced_path(MFMA, 4):
+            swq.forward(*dev, 4, 64)
+        torch.cuda.synchronize()
+        assert swq.swiglu_q_under_cap() == 0
+    finally:
+        swq.swiglu_q_set_max_calls(-1)
+    assert swq.swiglu_q_under_cap() == 1
