@@ -235,12 +235,14 @@ int get_workspace(hipStream_t stream, size_t need, void** out, int slot = 0) {
   return SWQ_OK;
 }
 
-// Staging of the matrix-vector path when the prep kernel stages x' (x' rows
-// [H/32][M][32] with the extra columns of 32-input groups riding along unused,
-// the row exponents, then the weight rows' exponents k [2][I]).
+// Staging of the matrix-vector path when the prep kernel stages x' (x' in the
+// few-row kernel's lane order: 4 KB per chunk quad and 16-row tile; the row
+// exponents; then the weight rows' exponents k [2][I]).
+int64_t gemv_x_bytes(int64_t M, int64_t H) {
+  return align256(((H + 127) / 128) * (M > 16 ? 2 : 1) * kSkinnyXUnitsPerQuadTile * 16);
+}
 int64_t gemv_stage_bytes(int64_t M, int64_t H, int64_t I) {
-  const int kext = kext_columns(H, 32);
-  return align256(M * (H + kext) * 2) + align256(M * 4) + align256(2 * I * 4);
+  return gemv_x_bytes(M, H) + align256(M * 4) + align256(2 * I * 4);
 }
 
 // Device staging bytes of a call that takes `path` (0: none).
@@ -294,7 +296,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       // x' rows, their exponents and the weight rows' exponents k from the
       // prep kernel's column blocks (gemv_stage_bytes)
       const int kext = kext_columns(H, 32);
-      const int64_t xa_bytes = align256(M * (H + kext) * 2);
+      const int64_t xa_bytes = gemv_x_bytes(M, H);
       const int64_t xe_bytes = align256(M * 4);
       void* ws = nullptr;
       int rc = acquire(stream, (size_t)gemv_stage_bytes(M, H, I), &ws, fixed, fixed_bytes);
@@ -313,6 +315,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       // the weight rows' exponents only when the few-row kernel cannot take
       // them from the scales of its first pass
       pp.k_only = skinny_needs_kexp((int)M, (int)H, bits_g, bits_u) ? 1 : 0;
+      pp.xlane = M > 16 ? 2 : 1;
       p.xa = pp.xa;
       p.xexp = pp.xexp;
       p.kexp = pp.k_only ? pp.kexp : nullptr;
@@ -350,6 +353,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.scl = scl; pp.nss = nss;
   pp.kexp = (int*)(wsb + L.kx);
   pp.k_only = 0;
+  pp.xlane = 0;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;

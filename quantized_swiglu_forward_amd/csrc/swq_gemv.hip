@@ -519,7 +519,7 @@ struct SkinnyChunk {
 // prep kernel), with half the waves per SIMD.
 template <int BITS_G, int BITS_U, bool STAGE, int RT, bool Q2>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
   static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, prep-fed x'");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -528,17 +528,43 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
   const int r = lane & 15, h = lane >> 4;             // A row / B and D column; K-slot group
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int col = (int)n0 + r;
-  int rowc[RT];                                       // clamped for loads (rows >= M are dropped)
+  // x' row of this lane per tile: from the prep kernel, a row past M reads
+  // zeros (see load); from LDS, clamped to the last row
+  bool rowok[RT];
+  int rowl[RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) rowc[t] = min(16 * t + r, p.M - 1);
+  for (int t = 0; t < RT; ++t) {
+    rowok[t] = 16 * t + r < p.M;
+    rowl[t] = min(16 * t + r, p.M - 1);
+  }
   const int nchunk = p.H >> 5;
   // the block's 16 columns through buffer descriptors (columns past I read zeros)
   const int ncols = (int)min((int64_t)16, (int64_t)p.I - n0);
   const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
   const int ncols_u = (int)max((int64_t)0, min((int64_t)ncols, (int64_t)p.I_u - n0));
   const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols_u, p.H, BITS_U, p.gs_u);
-  const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.xa, (short)0, nchunk * p.M * 64, 0x00020000);
+  // x' from the prep kernel in this kernel's lane order (kSkinnyXUnitsPerQuadTile)
+  const int nquad_all = (nchunk + 3) >> 2;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.xa, (short)0, nquad_all * RT * kSkinnyXUnitsPerQuadTile * 16, 0x00020000);
+  // exponents of this lane's accumulator rows 16 t + 4 h + j (prep-fed x'; the
+  // block's own in LDS otherwise), loaded with the first weights and packed
+  // as four biased bytes per tile (each lies in [-127, 127]); two row tiles
+  // with two quads in flight, and 2-bit codes (spread as they are loaded),
+  // have no registers to spare and load them at the end
+  constexpr bool kPreE = !STAGE && !(Q2 && RT == 2) && BITS_G != 2 && BITS_U != 2;
+  uint32_t xrow_e[RT];
+  if constexpr (kPreE) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      xrow_e[t] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 16 * t + 4 * h + j;
+        xrow_e[t] |= (uint32_t)((m < p.M ? p.xexp[m] : 0) + 128) << (8 * j);
+      }
+    }
+  }
   const NibbleK nk = nibble_consts_in_regs();
   const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
@@ -635,11 +661,16 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
     d.su = __builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0);
     d.bu = __builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0);
     if constexpr (!STAGE) {
+      // one contiguous kilobyte per instruction; a row past M or a chunk past
+      // H reads zeros (offset past the buffer's range)
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const int ox = (cc * p.M + rowc[t]) * 64;
+        const bool ok = d.live && rowok[t];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d.x[t][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox + 16 * q, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int ox = ok ? (((quad * RT + t) * 4 + q) * 64 + lane) * 16 : 0x7FFFFFF0;
+          d.x[t][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox, 0, 0);
+        }
       }
     }
     // every load of the chunk is in flight before the first use of any of them
@@ -650,7 +681,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) d.x[t][q] = xs[(c * p.M + rowc[t]) * 4 + q];
+      for (int q = 0; q < 4; ++q) d.x[t][q] = xs[(c * p.M + rowl[t]) * 4 + q];
   };
 
   // one matrix's 8-code block kb of a chunk, multiplied into every row tile:
@@ -725,7 +756,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
     }
   };
 
-  // chunk quads w, w + nw, ... (Q2: w, w + nw in one pass, then w + 2 nw, ...).
+  // chunk quads w, w + nw, ... (Q2: 2w and 2w + 1 in one pass, then 2(w + nw), ...).
   // When one pass loads every quad of the row, each wave takes its own
   // column exponents from the scales and biases its loads brought (the
   // largest term of its chunks of the column: two swaps, no barrier); its
@@ -812,26 +843,26 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
       }
     }
   } else {
-    // two chunk quads in flight per wave, half the waves (a quad past the
-    // end loads chunk 0 with zero scales and adds nothing)
+    // two adjacent chunk quads in flight per wave, half the waves (a quad
+    // past the end loads chunk 0 with zero scales and adds nothing)
     if (single) {
       SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
-      if (w < nquad) {
-        load(w, d0);
-        load(w + nw, d1);
+      if (2 * w < nquad) {
+        load(2 * w, d0);
+        load(2 * w + 1, d1);
         chunk_k(d0);
         chunk_k(d1);
       }
       chunk_k_wave();
-      if (w < nquad) {
+      if (2 * w < nquad) {
         compute(d0);
         compute(d1);
       }
     } else {
-      for (int q0 = w; q0 < nquad; q0 += 2 * nw) {
+      for (int pq = w; 2 * pq < nquad; pq += nw) {   // adjacent quads: their code rows share lines
         SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
-        load(q0, d0);
-        load(q0 + nw, d1);
+        load(2 * pq, d0);
+        load(2 * pq + 1, d1);
         compute(d0);
         compute(d1);
       }
@@ -850,7 +881,9 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G <= 4 && BITS_U <= 4 ? 8 : 4)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 16 * t + 4 * h + j;
-        const int e = m < p.M ? (STAGE ? xe[m] : p.xexp[m]) : 0;
+        int e;
+        if constexpr (kPreE) e = (int)((xrow_e[t] >> (8 * j)) & 0xFFu) - 128;
+        else e = m < p.M ? (STAGE ? xe[m] : p.xexp[m]) : 0;
         a[j] = ldexpf(a[j], kg_ + e);
         b[j] = ldexpf(b[j], ku_ + e);
       }

@@ -36,7 +36,18 @@ struct PrepParams {
   int* kexp;           // out: [2][I] row exponents k of the gate and up rows (scales and constants
                        //      are stored times 2^-k; the sums are multiplied by 2^k)
   int k_only;          // 1: the column blocks write kexp only (no extra-column rows, no scale tiles)
+  int xlane;           // 0: x' K-step major for the MFMA kernel (with the extra columns);
+                       // 1 or 2: in the few-row kernel's lane order with that many 16-row tiles
+                       // (see kSkinnyXUnit), no extra columns
 };
+
+// x' of the few-row kernel, in its MFMA lane order: for chunk quad Q (128
+// inputs), row tile t (16 rows), 8-input block kb and lane l = 16 h + r, the
+// 16 bytes x'[16 t + r][128 Q + 32 h + 8 kb .. + 8] at 16-byte unit
+// ((Q * RT + t) * 4 + kb) * 64 + l: every load instruction of a wave reads
+// one contiguous kilobyte.  Rows past M and inputs past H are never written
+// and never read (the kernel masks them).
+constexpr int kSkinnyXUnitsPerQuadTile = 4 * 64;
 
 struct MfmaParams {
   const _Float16* xa;

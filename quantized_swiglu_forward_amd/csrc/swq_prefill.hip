@@ -59,16 +59,27 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   auto xa_at = [&](int k) { return p.xa + ((int64_t)(k >> 5) * p.M + m) * 32 + (k & 31); };
   const int nchunk = p.H / 8;
 
-  // 1. row maximum of |x| (on the bf16 magnitude bits: monotone for finite values)
+  // 1. row maximum of |x| (on the bf16 magnitude bits: monotone for finite
+  //    values); the first kXRegs 8-value blocks of this thread stay in
+  //    registers for step 2 (all of them for H <= 8192), the rest are read again
+  constexpr int kXRegs = 4;
+  u32x4 keep[kXRegs];
   uint32_t amax = 0;
-  for (int c = tid; c < nchunk; c += 256) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xrow + 8 * c);
+  auto fold = [&](const u32x4& v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       amax = max(amax, v[j] & 0x7FFFu);
       amax = max(amax, (v[j] >> 16) & 0x7FFFu);
     }
+  };
+#pragma unroll
+  for (int i = 0; i < kXRegs; ++i) {
+    const int c = tid + 256 * i;
+    keep[i] = c < nchunk ? *reinterpret_cast<const u32x4*>(xrow + 8 * c) : (u32x4){0, 0, 0, 0};
   }
+#pragma unroll
+  for (int i = 0; i < kXRegs; ++i) fold(keep[i]);
+  for (int c = tid + 256 * kXRegs; c < nchunk; c += 256) fold(*reinterpret_cast<const u32x4*>(xrow + 8 * c));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
   __shared__ uint32_t red[4];
@@ -90,11 +101,18 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   // 2. scaled binary16 copy in pair order, and per-group sums
   const int gchunks = p.g0 / 8;
   const int ngroups = p.H / p.g0;
-  for (int base = 0; base < nchunk; base += 256) {
+  for (int base = 0, i = 0; base < nchunk; base += 256, ++i) {
     const int c = base + tid;
     float part = 0.0f;
     if (c < nchunk) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xrow + 8 * c);
+      u32x4 v;
+      if (i < kXRegs) {
+#pragma unroll
+        for (int q = 0; q < kXRegs; ++q)
+          if (q == i) v = keep[q];
+      } else {
+        v = *reinterpret_cast<const u32x4*>(xrow + 8 * c);
+      }
       float f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -109,11 +127,17 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
         h[2 * j] = (_Float16)f[j];
         h[2 * j + 1] = (_Float16)f[j + 4];
       }
-      *reinterpret_cast<f16x8*>(xa_at(8 * c)) = h;
+      if (p.xlane) {                                   // the few-row kernel's lane order
+        const int chunk = c >> 2, kb = c & 3;
+        const int64_t unit = ((int64_t)((chunk >> 2) * p.xlane + (m >> 4)) * 4 + kb) * 64 + (chunk & 3) * 16 + (m & 15);
+        *reinterpret_cast<f16x8*>(p.xa + unit * 8) = h;
+      } else {
+        *reinterpret_cast<f16x8*>(xa_at(8 * c)) = h;
+      }
     }
     // a group is g0/8 consecutive 8-value blocks = consecutive lanes
     for (int off = 1; off < gchunks; off <<= 1) part += __shfl_xor(part, off);
-    if (c < nchunk && (c % gchunks) == 0) {
+    if (!p.xlane && c < nchunk && (c % gchunks) == 0) {
       const int g = c / gchunks;
       const _Float16 hi = (_Float16)part;
       const _Float16 lo = (_Float16)(part - (float)hi);
@@ -123,7 +147,8 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
     }
   }
   // zero padding of the extra columns
-  for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
+  if (!p.xlane)
+    for (int k = 3 * ngroups + tid; k < p.kext; k += 256) *xa_at(p.H + k) = (_Float16)0.0f;
 }
 
 // Weight rows.  Thread ((n * 2 + matrix) << lg) + c owns extra-column slot c
