@@ -265,6 +265,15 @@ int swiglu_q_debug_gemm(const void *x,
 int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
                                  int bits_u, int gs_u);
 
+/* Bytes of device staging a call of this shape takes on `path`
+ * (SWQ_PATH_AUTO: the dispatcher's choice): what swiglu_q_forward takes from
+ * its workspace, and swiglu_q_forward_noalloc from its static array.  0 when
+ * the call stages nothing (the matrix-vector kernels read x themselves: M =
+ * 1, and the few-row kernel whenever a row fits one pass of its waves), when
+ * M == 0, or when the arguments are invalid. */
+int64_t swiglu_q_staging_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
+                               int bits_u, int gs_u, int path);
+
 /* Free every cached workspace (synchronises the device first). */
 int swiglu_q_release_workspace(void);
 

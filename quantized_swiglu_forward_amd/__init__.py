@@ -73,6 +73,8 @@ def load_library(path):
     L.swiglu_q_call_count.restype = u64
     L.swiglu_q_reset_counts.argtypes = []
     L.swiglu_q_reset_counts.restype = None
+    L.swiglu_q_staging_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
+    L.swiglu_q_staging_bytes.restype = i64
     L.swiglu_q_set_max_calls.argtypes = [i64]
     L.swiglu_q_set_max_calls.restype = None
     L.swiglu_q_under_cap.argtypes = []
@@ -178,6 +180,10 @@ def swiglu_q_strerror(status: int) -> str:
 
 def swiglu_q_workspace_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u) -> int:
     return lib().swiglu_q_workspace_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u)
+
+
+def swiglu_q_staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path=SWQ_PATH_AUTO) -> int:
+    return lib().swiglu_q_staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path)
 
 
 def swiglu_q_release_workspace() -> int:

@@ -125,15 +125,13 @@ bool gemv_fits(int64_t M, int64_t H) {
 }
 
 // The matrix-vector kernel reads x itself (M = 1 with H <= 8192, and its
-// several-row form), and the few-row kernel builds x' itself for
-// M*H <= kSkinnyStageMax; otherwise the prep kernel
-// stages x' first (in the workspace).  SWIGLU_Q_SKINNY_STAGE=0 always uses
-// the prep kernel.
-bool gemv_needs_rows(int64_t M, int64_t H) {
+// several-row form), and the few-row kernel converts x itself where
+// skinny_x_source says so; otherwise the prep kernel stages x' first (in the
+// workspace).
+bool gemv_needs_rows(int64_t M, int64_t H, int bits_g, int bits_u) {
   if (M == 1 && H <= 8192) return false;
   if (gemv1_rows_shape(M, H)) return false;
-  const char* s = getenv("SWIGLU_Q_SKINNY_STAGE");
-  return M * H > kSkinnyStageMax || (s && s[0] == '0');
+  return skinny_x_source(M, H, bits_g, bits_u) == kXPrep;
 }
 
 // Tile shape of the MFMA kernel: 256 x 128 unless that leaves CUs idle
@@ -248,7 +246,7 @@ int64_t gemv_stage_bytes(int64_t M, int64_t H, int64_t I) {
 // Device staging bytes of a call that takes `path` (0: none).
 int64_t staging_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bits_u, int gs_u, int path) {
   if (M <= 0) return 0;
-  if (path == SWQ_PATH_GEMV) return gemv_needs_rows(M, H) ? gemv_stage_bytes(M, H, I) : 0;
+  if (path == SWQ_PATH_GEMV) return gemv_needs_rows(M, H, bits_g, bits_u) ? gemv_stage_bytes(M, H, I) : 0;
   return ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u).total;
 }
 
@@ -292,7 +290,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
               (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
     (void)hipGetLastError();
-    if (gemv_needs_rows(M, H)) {
+    if (gemv_needs_rows(M, H, bits_g, bits_u)) {
       // x' rows, their exponents and the weight rows' exponents k from the
       // prep kernel's column blocks (gemv_stage_bytes)
       const int kext = kext_columns(H, 32);
@@ -572,6 +570,16 @@ int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int64_t I, int bits_g, in
   if (M <= 0 || H <= 0 || I <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
   if (H % gs_g != 0 || H % gs_u != 0) return 0;
   return ws_layout(M, H, I, bits_g, gs_g, bits_u, gs_u).total;
+}
+
+int64_t swiglu_q_staging_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bits_u, int gs_u,
+                               int path) {
+  if (M <= 0 || H <= 0 || I <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
+  if (H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0) return 0;
+  if (path == SWQ_PATH_AUTO) path = auto_path(M, H);
+  if (path == SWQ_PATH_GEMV && !gemv_fits(M, H)) return 0;
+  if (path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return 0;
+  return staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path);
 }
 
 int swiglu_q_release_workspace(void) {

@@ -202,4 +202,43 @@ __device__ __forceinline__ float swiglu_epilogue(float g, float u, int mode) {
   return g * sigmoid_fast(g) * u;
 }
 
+// ------------------------------------------------ LDS-writing loads ----
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer descriptor in scalar registers: base, no stride, `bytes` records
+// (hardware bounds check: reads past the end return zero).
+__device__ __forceinline__ i32x4 make_srsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uint64_t)(lds_ptr_t)p;
+}
+
+// Buffer loads that write LDS: lane i's 16 bytes land at base + 16 i.  They
+// are issued from inline assembly so that the compiler does not serialise
+// every later LDS read behind them (it cannot tell the stages apart); the
+// kernel orders them itself with explicit vmcnt waits and barriers.  m0
+// carries the LDS base.  The whole byte offset rides in the VGPR offset (the
+// SGPR offset is 0): a raw buffer's range check covers the VGPR offset only,
+// so every load past the end of its buffer -- including the loads the
+// pipeline issues ahead past the last K-step -- returns zeros and touches no
+// memory.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds_base), "v"(voff), "s"(rs) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace swq

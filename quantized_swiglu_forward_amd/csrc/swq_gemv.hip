@@ -22,6 +22,7 @@
 //    with one or two tiles of 16 rows at once (described above the kernel).
 // 2-bit codes are spread to nibbles as they are loaded and take the 4-bit
 // arithmetic.
+#include <cstring>
 #include <type_traits>
 
 #include "swq_device.h"
@@ -499,28 +500,50 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // the bias term sum_chunk x' * c (c = b + z s) with the chunk sum of x' and c
 // each split into binary16 hi + lo, as on the matrix-matrix path.  The waves'
 // partial sums meet in LDS; wave 4 t + j sums element j of row tile t, applies
-// 2^e and runs that row's epilogue.  x' comes
-// from the prep kernel, or (STAGE, M*H at most kSkinnyStageMax) every block
-// builds it itself in LDS with the prep kernel's row powers of two,
-// conversion and layout, so the call is one launch.
+// 2^e and runs that row's epilogue.  x' comes from one of three sources (XS):
+//  * kXSelf (M <= 16 and a row fits one pass of the block's waves): each
+//    wave copies the rows of x over its own chunks into its own LDS region
+//    (loads that write LDS, four lanes per 64-byte piece of a row), reads
+//    them back in the MFMA's lane order, takes the largest magnitude of each
+//    row over its chunks (two lane swaps) and converts in registers; its
+//    partial sums are multiplied by its own 2^e, so no other wave, block or
+//    kernel is involved;
+//  * kXStage (M*H at most kSkinnyStageMax): every block builds x' in LDS with
+//    the prep kernel's row powers of two, conversion and layout;
+//  * kXPrep: the prep kernel stages x' and the row exponents first.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kSkinnyMaxWaves = 16;
 
 template <int BITS_G, int BITS_U, int RT>
 struct SkinnyChunk {
+  // codes as loaded (the line-friendly lane order, 2-bit codes not yet
+  // spread), then in the MFMA's order
   u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[RT][4];
   uint32_t sg, bg, su, bu;   // raw bf16 bits, converted where used (after every load is issued)
   bool live;
+};
+
+// Scales and biases of a chunk quad (or of two adjacent quads): per array one
+// dword per lane, lane 4 rl + hl holding groups w + 2 hl and w + 2 hl + 1 of
+// column rl, where the window [w, w + 8) is the block of 8 groups, aligned to
+// 8, around the quad's first input; it holds every group of those 128 (or
+// 256) inputs.
+struct SbWindow {
+  uint32_t v[4];   // sg, bg, su, bu
+  int wg, wu;      // window starts (gate, up)
 };
 
 // RT: row tiles of 16 (M <= 16 RT = 1; M <= 32 RT = 2, whose second tile of x'
 // and accumulators need twice the registers: half the waves per SIMD).  Q2:
 // two chunk quads in flight per wave (codes of at most 4 bits, x' from the
 // prep kernel), with half the waves per SIMD.
-template <int BITS_G, int BITS_U, bool STAGE, int RT, bool Q2>
+template <int BITS_G, int BITS_U, int XS, int RT, bool Q2>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
-  static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, prep-fed x'");
+__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+  constexpr bool STAGE = XS == kXStage, SELF = XS == kXSelf;
+  static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, x' in registers");
+  static_assert(!SELF || RT == 1, "x converted by the waves: one row tile");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -552,7 +575,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   // as four biased bytes per tile (each lies in [-127, 127]); two row tiles
   // with two quads in flight, and 2-bit codes (spread as they are loaded),
   // have no registers to spare and load them at the end
-  constexpr bool kPreE = !STAGE && !(Q2 && RT == 2) && BITS_G != 2 && BITS_U != 2;
+  // (SELF: the wave's own exponents, packed the same way once its x is in)
+  constexpr bool kPreE = XS == kXPrep && !(Q2 && RT == 2) && BITS_G != 2 && BITS_U != 2;
   uint32_t xrow_e[RT];
   if constexpr (kPreE) {
 #pragma unroll
@@ -568,10 +592,29 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   const NibbleK nk = nibble_consts_in_regs();
   const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
+  // Codes, scales and biases are loaded in a line-friendly lane order and then
+  // moved to the MFMA's order with ds_bpermute.  In the MFMA's order adjacent
+  // lanes hold adjacent columns, each in its own cache line, and the vector
+  // L1 looks up one tag per cache line for every four lanes of a load; in the
+  // load order the four lanes 4 rl + hl (hl = 0..3) read one piece of column
+  // rl (its chunk 4 quad + hl, or one window of groups).  Lane 16 h + r of
+  // the MFMA's order takes its codes from lane 4 r + h.
+  const int rl = lane >> 2, hl = lane & 3;
+  const int perm = (4 * r + h) * 4;   // ds_bpermute byte address of that lane
+  // the windows of groups in dwords when every row of the four arrays starts
+  // on a dword boundary (else in two halves)
+  const bool sb_dword = (((mg.ng | mu.ng) & 1) == 0) &&
+                        ((((uintptr_t)p.sg | (uintptr_t)p.bg | (uintptr_t)p.su | (uintptr_t)p.bu) & 3) == 0);
+
   // STAGE: x' in LDS as [H/32][M][32] binary16 (16-byte pieces), row exponents beside it
   __shared__ u32x4 xs[STAGE ? kSkinnyStageMax / 8 : 1];
-  __shared__ int xe[kGemvMaxM];
-  __shared__ uint32_t xmax[kGemvMaxM];
+  __shared__ int xe[STAGE ? kGemvMaxM : 1];
+  __shared__ uint32_t xmax[STAGE ? kGemvMaxM : 1];
+  // SELF: the waves' regions (skinny_self_region bytes each), launched as dynamic LDS
+  extern __shared__ u32x4 swq_dyn[];
+  constexpr int kSelfChunks = Q2 ? 8 : 4;   // chunks per wave
+  const int rb = SELF ? skinny_self_region(p.M, kSelfChunks) : 0;
+  unsigned char* const xreg = reinterpret_cast<unsigned char*>(swq_dyn) + w * rb;
 
   // Row exponents k of the block's 16 columns of both matrices
   // (row_exponent_k): the scales and constants below are taken times 2^-k
@@ -582,14 +625,20 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   // loaded after the first weights (the block barrier below waits for the
   // slowest wave's weights either way); the lanes of a column reduce with
   // two swaps, and the waves meet in LDS.
-  __shared__ float kred[kSkinnyMaxWaves][32];
-  __shared__ f32x4 red[kSkinnyMaxWaves][2 * RT][64];   // the waves' partial sums (after the K loop)
+  __shared__ float kred[STAGE ? kSkinnyMaxWaves : 1][32];
+  // the waves' partial sums (after the K loop; SELF: in each wave's own region)
+  __shared__ f32x4 red[SELF ? 1 : kSkinnyMaxWaves][SELF ? 1 : 2 * RT][64];
+  auto red_at = [&](int ww, int i) -> f32x4* {
+    if constexpr (SELF) return reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(swq_dyn) + ww * rb) + 64 * i;
+    else return red[ww][i];
+  };
 #ifdef SWQ_LDS_POISON
   lds_poison(xs, sizeof(xs), kPoisonFloat);
   lds_poison(xe, sizeof(xe), kPoisonExp);
   lds_poison(xmax, sizeof(xmax), kPoisonExp);
   lds_poison(kred, sizeof(kred), kPoisonFloat);
   lds_poison(red, sizeof(red), kPoisonFloat);
+  if constexpr (SELF) lds_poison(swq_dyn, nw * rb, kPoisonFloat);
   __syncthreads();
 #endif
   auto row_k_finish = [&]() {
@@ -625,7 +674,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   auto set_k = [&](int kg_, int ku_) { kpack = ((uint32_t)kg_ & 0xFFFFu) | ((uint32_t)ku_ << 16); };
   auto k_gate = [&]() { return (int)(int16_t)(kpack & 0xFFFFu); };
   auto k_up = [&]() { return (int)kpack >> 16; };
-  if constexpr (!STAGE) {
+  if constexpr (XS == kXPrep) {
     const int nquad_ = (nchunk + 3) >> 2;
     if (nquad_ > (Q2 ? 2 : 1) * nw && col < p.I) set_k(p.kexp[col], p.kexp[p.I + col]);
   }
@@ -638,16 +687,53 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     set_k(row_exponent_k(mg_), row_exponent_k(mu_));
   };
 
+  // the window of groups around quad `quad` (issue before the quad's codes)
+  auto load_sb = [&](int quad, SbWindow& sw) {
+    sw.wg = ((128 * quad) >> mg.lg_gs) & ~7;
+    sw.wu = ((128 * quad) >> mu.lg_gs) & ~7;
+    const int og = (rl * mg.ng + sw.wg + 2 * hl) * 2, ou = (rl * mu.ng + sw.wu + 2 * hl) * 2;
+    if (sb_dword) {
+      sw.v[0] = __builtin_amdgcn_raw_buffer_load_b32(mg.s, og, 0, 0);
+      sw.v[1] = __builtin_amdgcn_raw_buffer_load_b32(mg.b, og, 0, 0);
+      sw.v[2] = __builtin_amdgcn_raw_buffer_load_b32(mu.s, ou, 0, 0);
+      sw.v[3] = __builtin_amdgcn_raw_buffer_load_b32(mu.b, ou, 0, 0);
+    } else {
+      auto two = [](const __amdgpu_buffer_rsrc_t& rs, int off) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0) |
+               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off + 2, 0, 0) << 16);
+      };
+      sw.v[0] = two(mg.s, og);
+      sw.v[1] = two(mg.b, og);
+      sw.v[2] = two(mu.s, ou);
+      sw.v[3] = two(mu.b, ou);
+    }
+  };
+  // this lane's scale and bias (chunk 4 quad + h of column r) from the window
+  auto pick_sb = [&](const SbWindow& sw, int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    const int c = 4 * quad + h;
+    const int ig = ((32 * c) >> mg.lg_gs) - sw.wg, iu = ((32 * c) >> mu.lg_gs) - sw.wu;   // in [0, 8)
+    const int ag = (4 * r + (ig >> 1)) * 4, au = (4 * r + (iu >> 1)) * 4;
+    const uint32_t s_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[0]);
+    const uint32_t b_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[1]);
+    const uint32_t s_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[2]);
+    const uint32_t b_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[3]);
+    d.sg = (ig & 1) ? s_g >> 16 : s_g & 0xFFFFu;
+    d.bg = (ig & 1) ? b_g >> 16 : b_g & 0xFFFFu;
+    d.su = (iu & 1) ? s_u >> 16 : s_u & 0xFFFFu;
+    d.bu = (iu & 1) ? b_u >> 16 : b_u & 0xFFFFu;
+  };
+
   auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
-    const int cc = d.live ? c : 0;                     // an in-range chunk for the loads
-    const int og = (r * mg.rw + cc * BITS_G) * 4, ou = (r * mu.rw + cc * BITS_U) * 4;
+    // codes in the load order: chunk 4 quad + hl of column rl (chunk 0 past the end)
+    const int cl = 4 * quad + hl < nchunk ? 4 * quad + hl : 0;
+    const int og = (rl * mg.rw + cl * BITS_G) * 4, ou = (rl * mu.rw + cl * BITS_U) * 4;
     auto codes = [](const __amdgpu_buffer_rsrc_t& rs, int off, u32x4* dst, auto bits_tag) {
       constexpr int BITS = decltype(bits_tag)::value;
       if constexpr (BITS == 2) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 2);
-        dst[0] = (u32x4){spread2(v[0]), spread2(v[0] >> 16), spread2(v[1]), spread2(v[1] >> 16)};
+        dst[0] = (u32x4){v[0], v[1], 0u, 0u};   // spread after the move
       } else {
 #pragma unroll
         for (int i = 0; i < BITS / 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 2);
@@ -655,12 +741,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     };
     codes(mg.w, og, d.cg, std::integral_constant<int, BITS_G>{});
     codes(mu.w, ou, d.cu, std::integral_constant<int, BITS_U>{});
-    const int gg = (r * mg.ng + ((32 * cc) >> mg.lg_gs)) * 2, gu = (r * mu.ng + ((32 * cc) >> mu.lg_gs)) * 2;
-    d.sg = __builtin_amdgcn_raw_buffer_load_b16(mg.s, gg, 0, 0);
-    d.bg = __builtin_amdgcn_raw_buffer_load_b16(mg.b, gg, 0, 0);
-    d.su = __builtin_amdgcn_raw_buffer_load_b16(mu.s, gu, 0, 0);
-    d.bu = __builtin_amdgcn_raw_buffer_load_b16(mu.b, gu, 0, 0);
-    if constexpr (!STAGE) {
+    if constexpr (XS == kXPrep) {
       // one contiguous kilobyte per instruction; a row past M or a chunk past
       // H reads zeros (offset past the buffer's range)
 #pragma unroll
@@ -719,7 +800,26 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     ag[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     au[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   }
-  auto compute = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  // the codes into the MFMA's order (lane 16 h + r from lane 4 r + h)
+  auto arrange = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    auto move = [&](u32x4* cw, auto bits_tag) {
+      constexpr int BITS = decltype(bits_tag)::value;
+      if constexpr (BITS == 2) {
+        const uint32_t v0 = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)cw[0][0]);
+        const uint32_t v1 = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)cw[0][1]);
+        cw[0] = (u32x4){spread2(v0), spread2(v0 >> 16), spread2(v1), spread2(v1 >> 16)};
+      } else {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cw[i][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)cw[i][j]);
+      }
+    };
+    move(d.cg, std::integral_constant<int, BITS_G>{});
+    move(d.cu, std::integral_constant<int, BITS_U>{});
+  };
+  auto compute = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    arrange(d);
     // a chunk past the end gets zero scales and biases: its B operands vanish
     // (scaled by the column's 2^-k)
     const int kg_ = k_gate(), ku_ = k_up();
@@ -766,6 +866,85 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   // (x' staged there) or the block's own pass (STAGE).
   const int nquad = (nchunk + 3) >> 2;
   const bool single = nquad <= (Q2 ? 2 : 1) * nw;
+
+  // SELF: the rows of x over the wave's chunks chunk0 .. chunk0 + kSelfChunks
+  // - 1 into its region, one (chunk slot s, row m) pair of 64 bytes per four
+  // lanes, at (s M + m) 64, its 16-byte pieces permuted by (m >> 2) & 3 so
+  // that the reads below (16 rows, one piece) spread over all banks.  A chunk
+  // past H, or a pair past the last, reads zeros.  Issued before every other
+  // load of the wave, so one vmcnt wait covers them.
+  const i32x4 rxs = make_srsrc(p.x, (uint32_t)(p.M * p.H * 2));
+  auto dma_x = [&](int chunk0) {
+    const int np = kSelfChunks * p.M;
+    for (int j = 0; 16 * j < np; ++j) {
+      const int pr = 16 * j + (lane >> 2);
+      const int sl = pr / p.M, m = pr - sl * p.M;
+      const int c = chunk0 + sl;
+      const int kb = (lane & 3) ^ ((m >> 2) & 3);
+      const uint32_t off = (pr < np && c < nchunk) ? (uint32_t)((m * p.H + 32 * c + 8 * kb) * 2) : 0x7FFFFFF0u;
+      dma16(rxs, lds_addr(xreg) + 1024 * j, off);
+    }
+  };
+  // ... chunk slot 4 qs + h of row r back, as the MFMA's A operand (bf16 bits)
+  auto read_x = [&](int qs, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+    const int sl = 4 * qs + h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      d.x[0][q] = rowok[0] ? *reinterpret_cast<const u32x4*>(xreg + (sl * p.M + r) * 64 + 16 * (q ^ ((r >> 2) & 3)))
+                           : (u32x4){0u, 0u, 0u, 0u};
+  };
+  // loads the wave issues after its x: the windows of groups (at least 4)
+  // and the codes of its quads
+  constexpr int kLoadsAfterX = 4 + (Q2 ? 2 : 1) * ((BITS_G == 8 ? 2 : 1) + (BITS_U == 8 ? 2 : 1));
+
+  // SELF: the largest bf16 magnitude of each of this lane's rows (packed
+  // halves, folded at the end), over the wave's chunks ...
+  uint32_t xam[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) xam[t] = 0;
+  auto x_amax = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xam[t] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, xam[t]),
+                                                                          __builtin_bit_cast(u16x2, d.x[t][q][j] & 0x7FFF7FFFu)));
+  };
+  // ... the row exponents e (the lanes of a row meet with two swaps; the
+  // accumulator rows' exponents packed as in the preload) ...
+  int xe_self[RT];
+  auto x_rows = [&]() {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      uint32_t a = max(xam[t] & 0xFFFFu, xam[t] >> 16);
+      a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+      a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+      xe_self[t] = row_exponent(a);
+      xrow_e[t] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xrow_e[t] |= (uint32_t)(__shfl(xe_self[t], 4 * h + j) + 128) << (8 * j);
+    }
+  };
+  // ... and x' = x 2^-e in binary16, in the code-pair order (word j of a
+  // block holds inputs j and j + 4), in place
+  auto x_convert = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = d.x[t][q];
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -xe_self[t]);
+          f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -xe_self[t]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d.x[t][q][j] = as_u32((f16x2){(_Float16)f[j], (_Float16)f[j + 4]});
+      }
+  };
   float cmax_g = 0.0f, cmax_u = 0.0f;
   auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     if (!d.live) return;
@@ -784,9 +963,16 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
   if constexpr (STAGE) {
     // the first quad's weights are in flight while the block builds x'
     SkinnyChunk<BITS_G, BITS_U, RT> d;
-    if (w < nquad) load(w, d);
+    SbWindow sw;
+    if (w < nquad) {
+      load_sb(w, sw);
+      load(w, d);
+    }
     if (single) {
-      if (w < nquad) chunk_k(d);
+      if (w < nquad) {
+        pick_sb(sw, w, d);
+        chunk_k(d);
+      }
       chunk_k_wave();
     } else {
       row_k_finish();
@@ -822,23 +1008,43 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     }
     __syncthreads();
     for (int q0 = w; q0 < nquad; q0 += nw) {
-      if (q0 != w) load(q0, d);
+      if (q0 != w) {
+        load_sb(q0, sw);
+        load(q0, d);
+      }
       load_x_lds(q0, d);
+      pick_sb(sw, q0, d);
       compute(d);
     }
   } else if constexpr (!Q2) {
     if (single) {
       SkinnyChunk<BITS_G, BITS_U, RT> d;
+      SbWindow sw;
       if (w < nquad) {
+        if constexpr (SELF) dma_x(4 * w);
+        load_sb(w, sw);
         load(w, d);
+        if constexpr (SELF) {
+          wait_vmcnt<kLoadsAfterX>();
+          read_x(0, d);
+        }
+        pick_sb(sw, w, d);
         chunk_k(d);
+        if constexpr (SELF) x_amax(d);
       }
       chunk_k_wave();
-      if (w < nquad) compute(d);
-    } else {
+      if constexpr (SELF) x_rows();
+      if (w < nquad) {
+        if constexpr (SELF) x_convert(d);
+        compute(d);
+      }
+    } else if constexpr (!SELF) {   // (SELF is launched for one pass only)
       for (int q0 = w; q0 < nquad; q0 += nw) {
         SkinnyChunk<BITS_G, BITS_U, RT> d;
+        SbWindow sw;
+        load_sb(q0, sw);
         load(q0, d);
+        pick_sb(sw, q0, d);
         compute(d);
       }
     }
@@ -847,22 +1053,45 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     // past the end loads chunk 0 with zero scales and adds nothing)
     if (single) {
       SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
+      SbWindow sw;   // one window holds both quads' groups
       if (2 * w < nquad) {
+        if constexpr (SELF) dma_x(8 * w);
+        load_sb(2 * w, sw);
         load(2 * w, d0);
         load(2 * w + 1, d1);
+        if constexpr (SELF) {
+          wait_vmcnt<kLoadsAfterX>();
+          read_x(0, d0);
+          read_x(1, d1);
+        }
+        pick_sb(sw, 2 * w, d0);
+        pick_sb(sw, 2 * w + 1, d1);
         chunk_k(d0);
         chunk_k(d1);
+        if constexpr (SELF) {
+          x_amax(d0);
+          x_amax(d1);
+        }
       }
       chunk_k_wave();
+      if constexpr (SELF) x_rows();
       if (2 * w < nquad) {
+        if constexpr (SELF) {
+          x_convert(d0);
+          x_convert(d1);
+        }
         compute(d0);
         compute(d1);
       }
-    } else {
+    } else if constexpr (!SELF) {
       for (int pq = w; 2 * pq < nquad; pq += nw) {   // adjacent quads: their code rows share lines
         SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
+        SbWindow sw;
+        load_sb(2 * pq, sw);
         load(2 * pq, d0);
         load(2 * pq + 1, d1);
+        pick_sb(sw, 2 * pq, d0);
+        pick_sb(sw, 2 * pq + 1, d1);
         compute(d0);
         compute(d1);
       }
@@ -882,13 +1111,14 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
       for (int j = 0; j < 4; ++j) {
         const int m = 16 * t + 4 * h + j;
         int e;
-        if constexpr (kPreE) e = (int)((xrow_e[t] >> (8 * j)) & 0xFFu) - 128;
-        else e = m < p.M ? (STAGE ? xe[m] : p.xexp[m]) : 0;
+        if constexpr (kPreE || SELF) e = (int)((xrow_e[t] >> (8 * j)) & 0xFFu) - 128;
+        else if constexpr (STAGE) e = m < p.M ? xe[m] : 0;
+        else e = m < p.M ? p.xexp[m] : 0;
         a[j] = ldexpf(a[j], kg_ + e);
         b[j] = ldexpf(b[j], ku_ + e);
       }
-      red[w][2 * t][lane] = a;
-      red[w][2 * t + 1][lane] = b;
+      red_at(w, 2 * t)[lane] = a;
+      red_at(w, 2 * t + 1)[lane] = b;
     }
   }
   __syncthreads();
@@ -899,8 +1129,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 8 : 4)
     const int t = k >> 2, j = k & 3;
     float g = 0.0f, u = 0.0f;
     for (int ww = 0; ww < nw; ++ww) {
-      g += red[ww][2 * t][lane][j];
-      u += red[ww][2 * t + 1][lane][j];
+      g += red_at(ww, 2 * t)[lane][j];
+      u += red_at(ww, 2 * t + 1)[lane][j];
     }
     const int m = 16 * t + 4 * h + j;
     if (m < p.M && col < p.I) store_out(p, m, col, g, u);
@@ -986,21 +1216,45 @@ bool gemv1_rows_enabled() {
 }
 
 // Waves per block of the few-row kernel and whether it takes two chunk quads
-// per pass (the launcher's choice below).
-static void skinny_shape(int M, int H, int bits_g, int bits_u, bool prep_fed, int* waves, bool* two) {
-  const int quads = (H / 32 + 3) / 4;
+// per pass (the launcher's choice below), for x source xs.
+static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, int* waves, bool* two) {
+  const int quads = (int)((H / 32 + 3) / 4);
   // (equal widths of at most 4 bits: mixed 2- and 4-bit codes would not fit
-  // two quads in the registers of four waves per SIMD)
+  // two quads in the registers of four waves per SIMD).  x' from the prep
+  // kernel: two quads measured faster with two row tiles everywhere, and with
+  // one up to H = 2048 (slower beyond, at half the waves per SIMD, where the
+  // rows take several passes); x converted by the waves themselves (M <= 16):
+  // two quads whenever the codes allow, which doubles the row one pass covers
   const bool narrow = bits_g <= 4 && bits_u <= 4 && bits_g == bits_u;
-  *two = narrow && prep_fed && (M > 16 || H <= 2048);
+  if (xs == kXSelf) *two = narrow;
+  else *two = narrow && xs == kXPrep && (M > 16 || H <= 2048);
   const int per = *two ? (quads + 1) / 2 : quads;
   *waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
+}
+
+// x' converted by each wave itself for M <= 16 whenever a row fits one pass
+// of the block's waves and their LDS regions fit kSkinnySelfMaxLds (no second
+// launch, no workspace); else built in LDS by each block for M*H <=
+// kSkinnyStageMax; else from the prep kernel.
+// SWIGLU_Q_SKINNY_X=prep or =stage (where M*H allows) overrides, for
+// comparisons and for tests of those sources.
+int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
+  const char* env = getenv("SWIGLU_Q_SKINNY_X");
+  if (env && strcmp(env, "prep") == 0) return kXPrep;
+  if (env && strcmp(env, "stage") == 0 && M * H <= kSkinnyStageMax) return kXStage;
+  int waves;
+  bool two;
+  skinny_shape(M, H, bits_g, bits_u, kXSelf, &waves, &two);
+  if (M <= 16 && (H / 32 + 3) / 4 <= (two ? 2 : 1) * waves &&
+      waves * skinny_self_region((int)M, two ? 8 : 4) <= kSkinnySelfMaxLds)
+    return kXSelf;
+  return M * H <= kSkinnyStageMax ? kXStage : kXPrep;
 }
 
 bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
   int waves;
   bool two;
-  skinny_shape(M, H, bits_g, bits_u, true, &waves, &two);
+  skinny_shape(M, H, bits_g, bits_u, kXPrep, &waves, &two);
   return (H / 32 + 3) / 4 > (two ? 2 : 1) * waves;
 }
 
@@ -1026,26 +1280,37 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     return full ? launch_gemv1_rows_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false>(p, r, stream);
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
-  // one wave per chunk quad (two quads with two row tiles, x' from the prep
-  // kernel), at most kSkinnyMaxWaves per block of 16 columns; two quads in
-  // flight: measured faster with two row tiles everywhere, and with one up
-  // to H = 2048 (slower beyond, at half the waves per SIMD)
+  // one wave per chunk quad (or pair of quads), at most kSkinnyMaxWaves per
+  // block of 16 columns
   constexpr bool kNarrow = BG <= 4 && BU <= 4 && BG == BU;
+  const int xs = p.xa != nullptr ? kXPrep : skinny_x_source(p.M, p.H, BG, BU);
   int waves;
   bool two;
-  skinny_shape(p.M, p.H, BG, BU, p.xa != nullptr, &waves, &two);
-  if (p.xa != nullptr && p.kexp == nullptr && skinny_needs_kexp(p.M, p.H, BG, BU)) return hipErrorInvalidValue;
+  skinny_shape(p.M, p.H, BG, BU, xs, &waves, &two);
+  const int quads = (p.H / 32 + 3) / 4;
+  if (xs == kXPrep && (p.xa == nullptr || (p.kexp == nullptr && skinny_needs_kexp(p.M, p.H, BG, BU))))
+    return hipErrorInvalidValue;
+  if (xs == kXStage && (int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
+  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4) : 0;
+  if (xs == kXSelf && (p.M > 16 || quads > (two ? 2 : 1) * waves || lds > kSkinnySelfMaxLds))
+    return hipErrorInvalidValue;   // one pass, one row tile, regions within bounds
   const dim3 g((p.I + 15) / 16), b(64 * waves);
-  if (p.xa == nullptr) {
-    if ((int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
-    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 1, false>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, true, 2, false>), g, b, 0, stream, p);
-  } else if (!two) {
-    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1, false>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2, false>), g, b, 0, stream, p);
+  auto go = [&](auto xs_tag, auto two_tag) {
+    constexpr int XS = decltype(xs_tag)::value;
+    constexpr bool TWO = decltype(two_tag)::value;
+    if constexpr (XS == kXSelf) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO>), g, b, lds, stream, p);
+    else if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO>), g, b, 0, stream, p);
+  };
+  using F = std::false_type;
+  using T = std::true_type;
+  if (xs == kXStage) go(std::integral_constant<int, kXStage>{}, F{});
+  else if (!two) {
+    if (xs == kXSelf) go(std::integral_constant<int, kXSelf>{}, F{});
+    else go(std::integral_constant<int, kXPrep>{}, F{});
   } else if constexpr (kNarrow) {
-    if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 1, true>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, false, 2, true>), g, b, 0, stream, p);
+    if (xs == kXSelf) go(std::integral_constant<int, kXSelf>{}, T{});
+    else go(std::integral_constant<int, kXPrep>{}, T{});
   }
   return hipGetLastError();
 }

@@ -92,7 +92,7 @@ struct GemvParams {
   float* dbg_g;
   float* dbg_u;
   const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
-  const _Float16* xa;  // x' staged by the prep kernel, [H/32][M][32] (M*H > kSkinnyStageMax), or null
+  const _Float16* xa;  // x' staged by the prep kernel in the few-row kernel's lane order, or null
   const int* xexp;     // and its row exponents
   const int* kexp;     // with xa: [2][I] weight-row exponents k from the prep kernel's column blocks
 };
@@ -111,8 +111,21 @@ constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
 // Largest M the matrix-vector path takes (two 16-row MFMA tiles).
 constexpr int kGemvMaxM = 32;
-// M*H up to this: the few-row kernel builds x' itself (one launch, no workspace).
+// Where the few-row kernel's x' comes from (skinny_x_source): the prep
+// kernel (staged in the workspace), the block's own LDS (M*H up to
+// kSkinnyStageMax), or each wave's own registers (a row fits one pass of the
+// block's waves).  The last two need no workspace and no second launch.
+constexpr int kXPrep = 0, kXStage = 1, kXSelf = 2;
 constexpr int kSkinnyStageMax = 8192;
+// kXSelf (M <= 16): each wave's LDS region in bytes -- its chunks' rows of x
+// as loaded (64 bytes per chunk and row, written 1 KB per load instruction),
+// later its partial sums (2 KB) -- for `nch` chunks per wave; the block's
+// regions together stay within kSkinnySelfMaxLds.
+__host__ __device__ inline int skinny_self_region(int M, int nch) {
+  const int x = (nch * M + 15) / 16 * 1024;
+  return x > 2048 ? x : 2048;
+}
+constexpr int kSkinnySelfMaxLds = 65536;
 // the matrix-vector kernel's several-row form (no staging pass): 2 <= M <=
 // kGemv1MaxRows with a whole wave per column (H >= 2048) and at most two
 // chunks per lane (H <= 4096); below H = 2048 the few-row kernel is faster
@@ -137,6 +150,8 @@ hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
+// The few-row kernel's x source for a call of M rows (kXPrep, kXStage or kXSelf).
+int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u);
 // Whether the few-row kernel, fed x' by the prep kernel, needs the weight-row
 // exponents from the prep kernel's k-only rows (a row longer than one pass of
 // its waves); otherwise it takes them from the scales its first pass loads.

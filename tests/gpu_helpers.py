@@ -33,6 +33,25 @@ def forced_path(path, M):
         swq.swiglu_q_set_m_threshold(old)
 
 
+@contextlib.contextmanager
+def skinny_x(source):
+    """Where the few-row kernel takes x' from: None (the library's choice),
+    "prep" or "stage" (SWIGLU_Q_SKINNY_X, read on every call)."""
+    import os
+    old = os.environ.get("SWIGLU_Q_SKINNY_X")
+    if source is None:
+        os.environ.pop("SWIGLU_Q_SKINNY_X", None)
+    else:
+        os.environ["SWIGLU_Q_SKINNY_X"] = source
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("SWIGLU_Q_SKINNY_X", None)
+        else:
+            os.environ["SWIGLU_Q_SKINNY_X"] = old
+
+
 def device_forward(prob, mode, path=None, dev=None, expect_path=None):
     """hidden on the GPU as a float64 numpy array [M, I]."""
     if dev is None:

@@ -251,6 +251,44 @@ def test_workspace_bytes():
     assert swq.swiglu_q_workspace_bytes(4, 2048, 64, 3, 64, 4, 64) == 0
 
 
+def test_few_row_x_source_and_workspace():
+    """The few-row kernel converts x itself (no prep launch, no workspace)
+    for M <= 16 when a row fits one pass of its waves and their LDS regions
+    (skinny_self_region each) fit 64 KB: up to H = 4096 with equal code
+    widths of at most 4 bits (two chunk quads per wave; M <= 8 there), up to
+    H = 2048 otherwise; other calls take x' from the prep kernel, and
+    SWIGLU_Q_SKINNY_X=prep forces that."""
+    def ws(M, H, bg=4, bu=4):
+        return swq.swiglu_q_staging_bytes(M, H, 5632, bg, 64, bu, 64)
+
+    def prep_bytes(M, H):   # x' in lane order, row exponents, weight-row exponents
+        a = lambda v: (v + 255) // 256 * 256
+        return a((H + 127) // 128 * (2 if M > 16 else 1) * 256 * 16) + a(M * 4) + a(2 * 5632 * 4)
+
+    for M, H in ((5, 2048), (8, 2048), (16, 2048), (8, 4096), (2, 1024), (16, 1056)):
+        assert ws(M, H) == 0, (M, H)
+    assert ws(16, 2048, 8, 8) == 0 and ws(8, 2048, 4, 8) == 0
+    assert ws(9, 4096) == prep_bytes(9, 4096)     # 16 waves x 8 KB of LDS
+    assert ws(8, 4096, 8, 8) == prep_bytes(8, 4096)
+    assert ws(17, 2048) == prep_bytes(17, 2048)
+    assert ws(32, 1024) == prep_bytes(32, 1024)
+    assert ws(8, 8192) == prep_bytes(8, 8192)
+    os.environ["SWIGLU_Q_SKINNY_X"] = "prep"
+    try:
+        assert ws(8, 2048) == prep_bytes(8, 2048)
+    finally:
+        os.environ.pop("SWIGLU_Q_SKINNY_X")
+    assert ws(8, 2048) == 0
+    # M = 1 reads x itself; the matrix-matrix path stages its workspace
+    assert ws(1, 2048) == 0
+    assert swq.swiglu_q_staging_bytes(512, 2048, 8192, 4, 64, 4, 64) == \
+        swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64)
+    assert swq.swiglu_q_staging_bytes(8, 2048, 5632, 4, 64, 4, 64, swq.SWQ_PATH_MFMA) == \
+        swq.swiglu_q_workspace_bytes(8, 2048, 5632, 4, 64, 4, 64)
+    assert swq.swiglu_q_staging_bytes(33, 2048, 5632, 4, 64, 4, 64, swq.SWQ_PATH_GEMV) == 0   # no such call
+    assert swq.swiglu_q_staging_bytes(8, 2048, 5632, 3, 64, 4, 64) == 0
+
+
 def test_binding_has_no_fallback():
     """The binding only marshals: it never imports the oracle."""
     src = open(os.path.join(ROOT, "quantized_swiglu_forward_amd", "__init__.py")).read()

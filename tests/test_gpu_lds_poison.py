@@ -2,8 +2,8 @@
 same kernels, each filling its LDS with NaN bits (and 2^30 exponents) before
 use, so a kernel that read LDS it had not written would fail here.  One case
 per kernel and branch: the M = 1 kernel and its several-row form, the
-few-row kernel (x' built in the block, from the prep kernel, two row tiles,
-rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
+few-row kernel (x' converted by each wave, built in the block, from the
+prep kernel, two row tiles, rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
 column split, a partial last super-step), the linear and the whole MLP."""
 import os
 
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import quantized_swiglu_forward_amd as swq
-from gpu_helpers import check, device_forward, oracle_full, oracle_pairs, say
+from gpu_helpers import check, skinny_x, device_forward, oracle_full, oracle_pairs, say
 from synth import make_custom, make_down, make_residual
 
 pytestmark = pytest.mark.gpu
@@ -48,9 +48,12 @@ CASES = [
 def test_forward_under_poison(M, H, I, spec, path):
     mode = (M + H) % 3
     p = make_custom(M, H, I, *spec, seed=M + H + I)
-    say("poison", M, H, I, spec, "mode", mode, "path", path)
-    y = device_forward(p, mode, path)
-    check(y, oracle_full(p, mode), mode, f"poison M{M} H{H} I{I}")
+    o = oracle_full(p, mode)
+    for source in [None] + (["prep"] if path == GEMV_PATH and M > 1 else []):
+        say("poison", M, H, I, spec, "mode", mode, "path", path, "x source", source or "default")
+        with skinny_x(source):
+            y = device_forward(p, mode, path)
+        check(y, o, mode, f"poison M{M} H{H} I{I} x source {source}")
 
 
 def test_split_launch_under_poison():

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import quantized_swiglu_forward_amd as swq
-from gpu_helpers import (check, device_forward, device_gemm, forced_path, oracle_full, oracle_pairs,
+from gpu_helpers import (skinny_x, check, device_forward, device_gemm, forced_path, oracle_full, oracle_pairs,
                          sample_pairs, say)
 from synth import CONFIGS, bf16_bits_to_f32, make_custom, make_problem, pack_codes, to_bf16_bits
 
@@ -408,10 +408,10 @@ def test_gemv_and_mfma_agree(M):
     check(ym, o, 1, f"mfma M{M}")
 
 
-# the few-row kernel with one and two tiles of 16 rows (M up to 32), x' built
-# inside the kernel (M*H <= 8192: one launch) and staged by the prep kernel
-# (larger), on both sides of the boundary, all three code widths, and M <= 4
-# and M = 1 past the matrix-vector kernel's H limits
+# the few-row kernel with one and two tiles of 16 rows (M up to 32), every x
+# source the shape allows (converted by each wave, built in the block's LDS
+# for M*H <= 8192, staged by the prep kernel), all three code widths, and
+# M <= 4 and M = 1 past the matrix-vector kernel's H limits
 FEW_ROW = [(6, 1024, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (8, 1024, 257, (8, 64, 4, 128)),
            (5, 2048, 96, (4, 32, 4, 64)), (9, 2048, 300, (4, 64, 4, 64)), (16, 2048, 129, (8, 32, 8, 64)),
            (12, 4096, 64, (4, 128, 4, 64)), (16, 512, 100, (4, 64, 8, 64)), (1, 8192, 200, (4, 64, 4, 64)),
@@ -425,9 +425,41 @@ FEW_ROW = [(6, 1024, 130, (4, 64, 8, 32)), (2, 8192, 97, (4, 64, 4, 64)), (8, 10
 def test_few_row_kernel_x_staging(M, H, I, spec):
     mode = (M + H // 1024) % 3
     p = make_custom(M, H, I, *spec, seed=M * 31 + I)
-    say("few-row", M, H, I, spec, "mode", mode)
-    y = device_forward(p, mode, GEMV)
-    check(y, oracle_full(p, mode), mode, f"few-row M{M} H{H} I{I}")
+    o = oracle_full(p, mode)
+    dev = swq.to_device(p)
+    for source in [None, "prep"] + (["stage"] if M * H <= 8192 else []):
+        say("few-row", M, H, I, spec, "mode", mode, "x source", source or "default")
+        with skinny_x(source):
+            y = device_forward(p, mode, GEMV, dev=dev)
+        check(y, o, mode, f"few-row M{M} H{H} I{I} x source {source}")
+
+
+# x converted by each wave of the few-row kernel with its own row exponents:
+# rows whose magnitudes differ by row and by 256-input slice (the waves of a
+# block see different slices), a row that is zero over half of H (whole waves
+# see only zeros), bf16 subnormals, ragged H, pairs past the last in the
+# waves' x loads (M * chunks not a multiple of 16); one and two chunk quads
+# per wave, narrow, mixed and 8-bit codes
+SELF_CASES = [(8, 2048, (4, 64, 4, 64)), (13, 2048, (8, 32, 8, 64)), (8, 4096, (4, 128, 4, 128)),
+              (16, 2048, (4, 64, 8, 32)), (5, 1056, (2, 32, 2, 32)), (16, 1024, (4, 32, 4, 64)),
+              (2, 1024, (4, 64, 4, 64)), (3, 1184, (8, 32, 4, 32))]
+
+
+@pytest.mark.parametrize("M,H,spec", SELF_CASES, ids=[f"M{m}-H{h}" for m, h, _ in SELF_CASES])
+def test_few_row_wave_exponents(M, H, spec):
+    from synth import bf16_bits_to_f32, to_bf16_bits
+    assert swq.swiglu_q_staging_bytes(M, H, 97, *spec) == 0, "x converted in the kernel"
+    p = make_custom(M, H, 97, *spec, seed=M * 7 + H)
+    rng = np.random.default_rng(M + H)
+    x = bf16_bits_to_f32(p.x).astype(np.float64)
+    x *= np.exp2(rng.integers(-20, 21, M))[:, None]
+    x *= np.repeat(np.exp2(rng.integers(-20, 21, (H + 255) // 256)), 256)[None, :H]
+    x[M // 2, : H // 2] = 0.0
+    x[-1, ::7] = rng.choice([1e-39, -3e-40, 5e-41, -7e-42], x[-1, ::7].size)
+    p.x = to_bf16_bits(x.astype(np.float32))
+    say("wave exponents", M, H, spec)
+    y = device_forward(p, 1, GEMV)
+    check(y, oracle_full(p, 1), 1, f"wave exponents M{M} H{H}")
 
 
 # ------------------------------------------------- tile shapes and splits --
