@@ -874,24 +874,28 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // past H, or a pair past the last, reads zeros.  Issued before every other
   // load of the wave, so one vmcnt wait covers them.
   const i32x4 rxs = make_srsrc(p.x, (uint32_t)(p.M * p.H * 2));
+  // pr / M as (pr * ceil(2^16 / M)) >> 16: exact for pr < 2^16 / M, and pr < 16 kSelfChunks here
+  const uint32_t inv_m = (65536u + (uint32_t)p.M - 1u) / (uint32_t)p.M;
   auto dma_x = [&](int chunk0) {
     const int np = kSelfChunks * p.M;
     for (int j = 0; 16 * j < np; ++j) {
       const int pr = 16 * j + (lane >> 2);
-      const int sl = pr / p.M, m = pr - sl * p.M;
+      const int sl = (int)(((uint32_t)pr * inv_m) >> 16), m = pr - sl * p.M;
       const int c = chunk0 + sl;
       const int kb = (lane & 3) ^ ((m >> 2) & 3);
       const uint32_t off = (pr < np && c < nchunk) ? (uint32_t)((m * p.H + 32 * c + 8 * kb) * 2) : 0x7FFFFFF0u;
       dma16(rxs, lds_addr(xreg) + 1024 * j, off);
     }
   };
-  // ... chunk slot 4 qs + h of row r back, as the MFMA's A operand (bf16 bits)
+  // ... chunk slot 4 qs + h of row r back, as the MFMA's A operand (bf16
+  // bits).  A lane of a row past M reads row M - 1 again: A's rows past M
+  // only reach D's rows past M, which are never stored.
   auto read_x = [&](int qs, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     const int sl = 4 * qs + h;
+    const int m = rowl[0];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      d.x[0][q] = rowok[0] ? *reinterpret_cast<const u32x4*>(xreg + (sl * p.M + r) * 64 + 16 * (q ^ ((r >> 2) & 3)))
-                           : (u32x4){0u, 0u, 0u, 0u};
+      d.x[0][q] = *reinterpret_cast<const u32x4*>(xreg + (sl * p.M + m) * 64 + 16 * (q ^ ((m >> 2) & 3)));
   };
   // loads the wave issues after its x: the windows of groups (at least 4)
   // and the codes of its quads
@@ -913,15 +917,27 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
                                                                           __builtin_bit_cast(u16x2, d.x[t][q][j] & 0x7FFF7FFFu)));
   };
   // ... the row exponents e (the lanes of a row meet with two swaps; the
-  // accumulator rows' exponents packed as in the preload) ...
+  // accumulator rows' exponents packed as in the preload) ...  When every
+  // row's largest magnitude lies in [1, 2^16) (0 <= e <= 15) the wave takes
+  // e = 0 instead, x' = x: every bf16 value below 2^16 is at most 65280, so
+  // x fits binary16, and an element is exact in binary16 down to 2^-17, not
+  // 2^(e - 17): at least as exact as with the row's own power of two.
   int xe_self[RT];
+  bool xe_zero = false;
   auto x_rows = [&]() {
+    bool in_range = true;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       uint32_t a = max(xam[t] & 0xFFFFu, xam[t] >> 16);
       a = max(a, (uint32_t)__shfl_xor((int)a, 16));
       a = max(a, (uint32_t)__shfl_xor((int)a, 32));
       xe_self[t] = row_exponent(a);
+      in_range = in_range && xe_self[t] >= 0 && xe_self[t] <= 15;
+    }
+    xe_zero = __all(in_range);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if (xe_zero) xe_self[t] = 0;
       xrow_e[t] = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) xrow_e[t] |= (uint32_t)(__shfl(xe_self[t], 4 * h + j) + 128) << (8 * j);
@@ -938,8 +954,12 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         float f[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -xe_self[t]);
-          f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -xe_self[t]);
+          f[2 * j] = bf16_to_f32((uint16_t)(v[j] & 0xFFFFu));
+          f[2 * j + 1] = bf16_to_f32((uint16_t)(v[j] >> 16));
+        }
+        if (!xe_zero) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = ldexpf(f[j], -xe_self[t]);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) d.x[t][q][j] = as_u32((f16x2){(_Float16)f[j], (_Float16)f[j + 4]});
@@ -1024,20 +1044,20 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         if constexpr (SELF) dma_x(4 * w);
         load_sb(w, sw);
         load(w, d);
-        if constexpr (SELF) {
+        if constexpr (SELF) {   // x arrives first (L2): convert it while the weights are in flight
           wait_vmcnt<kLoadsAfterX>();
           read_x(0, d);
+          x_amax(d);
         }
-        pick_sb(sw, w, d);
-        chunk_k(d);
-        if constexpr (SELF) x_amax(d);
       }
-      chunk_k_wave();
       if constexpr (SELF) x_rows();
       if (w < nquad) {
         if constexpr (SELF) x_convert(d);
-        compute(d);
+        pick_sb(sw, w, d);
+        chunk_k(d);
       }
+      chunk_k_wave();
+      if (w < nquad) compute(d);
     } else if constexpr (!SELF) {   // (SELF is launched for one pass only)
       for (int q0 = w; q0 < nquad; q0 += nw) {
         SkinnyChunk<BITS_G, BITS_U, RT> d;
@@ -1059,27 +1079,27 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         load_sb(2 * w, sw);
         load(2 * w, d0);
         load(2 * w + 1, d1);
-        if constexpr (SELF) {
+        if constexpr (SELF) {   // x arrives first (L2): convert it while the weights are in flight
           wait_vmcnt<kLoadsAfterX>();
           read_x(0, d0);
           read_x(1, d1);
-        }
-        pick_sb(sw, 2 * w, d0);
-        pick_sb(sw, 2 * w + 1, d1);
-        chunk_k(d0);
-        chunk_k(d1);
-        if constexpr (SELF) {
           x_amax(d0);
           x_amax(d1);
         }
       }
-      chunk_k_wave();
       if constexpr (SELF) x_rows();
       if (2 * w < nquad) {
         if constexpr (SELF) {
           x_convert(d0);
           x_convert(d1);
         }
+        pick_sb(sw, 2 * w, d0);
+        pick_sb(sw, 2 * w + 1, d1);
+        chunk_k(d0);
+        chunk_k(d1);
+      }
+      chunk_k_wave();
+      if (2 * w < nquad) {
         compute(d0);
         compute(d1);
       }
