@@ -149,7 +149,89 @@ def probe_lib():
     L.swq_probe_read.restype = i32
     L.swq_probe_read_blocks.argtypes = [i64]
     L.swq_probe_read_blocks.restype = i64
+    L.swq_probe_empty.argtypes = [i32, vp, vp]
+    L.swq_probe_empty.restype = i32
+    L.swq_probe_grid_barrier.argtypes = [i32, vp, i32, vp, vp]
+    L.swq_probe_grid_barrier.restype = i32
+    L.swq_probe_atomic_add.argtypes = [i32, i32, vp, vp]
+    L.swq_probe_atomic_add.restype = i32
+    L.swq_probe_read_slices.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    L.swq_probe_read_slices.restype = i32
     return L
+
+
+def graph_call_us(launch, steps, warmup):
+    """Microseconds per call of ``launch(i, stream_handle)`` (which enqueues
+    one call's kernels and returns 0), CALLS calls per step recorded into
+    one HIP graph, timed with HIP events over ``steps`` replays."""
+    import torch
+    stream = torch.cuda.Stream()
+
+    def step(sh):
+        for i in range(CALLS):
+            if launch(i, sh) != 0:
+                raise RuntimeError("probe launch failed")
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
+
+
+def bench_mlp_boundary(steps, warmup):
+    """What a whole MLP in one dispatch would pay at decode (M=1, H=Ho=2048,
+    I=5632, 4-bit down projection), measured with probe kernels in the decode
+    bench's graph setup: the second launch it would save (two dependent
+    trivial kernels against one), a grid-wide barrier between its phases
+    (352 blocks, as many as the gate/up phase's 16-column tiles), f32
+    atomic accumulation of every I-block's partial output (the pages'
+    design: 352 blocks, or 22 blocks of 256 inputs, times Ho atomics), and
+    the down projection's rows read in the 8-byte I-slices that 16-column
+    tiles own, against the same bytes read contiguously."""
+    import torch
+    L = probe_lib()
+    Ho, I = 2048, 5632
+    row_bytes = I * 4 // 8
+    b16, b256 = I // 16, I // 256
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.zeros(Ho, dtype=torch.float32, device="cuda")
+    sp, cp, yp = sink.data_ptr(), counter.data_ptr(), y.data_ptr()
+    one = graph_call_us(lambda i, sh: L.swq_probe_empty(1, sp, sh), steps, warmup)
+    two = graph_call_us(lambda i, sh: L.swq_probe_empty(1, sp, sh) or L.swq_probe_empty(1, sp, sh), steps, warmup)
+    empty16 = graph_call_us(lambda i, sh: L.swq_probe_empty(b16, sp, sh), steps, warmup)
+    barrier16 = graph_call_us(lambda i, sh: L.swq_probe_grid_barrier(b16, cp, 4096, sp, sh), steps, warmup)
+    torch.cuda.synchronize()
+    timed_out = int((sink[:b16] != 0).sum().item())
+    atomics16 = graph_call_us(lambda i, sh: L.swq_probe_atomic_add(b16, Ho, yp, sh), steps, warmup)
+    atomics256 = graph_call_us(lambda i, sh: L.swq_probe_atomic_add(b256, Ho, yp, sh), steps, warmup)
+    bufs = [torch.empty(Ho * row_bytes // 4, dtype=torch.int32, device="cuda").fill_(i + 1)
+            for i in range(ROTATING_SETS)]
+    ptrs = [t.data_ptr() for t in bufs]
+    slices8 = graph_call_us(lambda i, sh: L.swq_probe_read_slices(ptrs[i % ROTATING_SETS], Ho, row_bytes, 8, b16,
+                                                                  sp, sh), steps, warmup)
+    del bufs
+    whole = practical_read(Ho * row_bytes, steps, warmup)
+    return {"config": f"decode MLP parts: Ho={Ho}, I={I}, 4-bit down projection, {b16} blocks of 16 columns, "
+                      f"{CALLS} calls per graph",
+            "second_launch_us": round(two - one, 3),
+            "grid_barrier_us": round(barrier16 - empty16, 3), "grid_barrier_timeouts": timed_out,
+            "atomics_16col_blocks_us": round(atomics16, 3), "atomics_256input_blocks_us": round(atomics256, 3),
+            "down_read_8B_slices_us": round(slices8, 3), "down_read_contiguous_us": round(whole, 3)}
 
 
 def practical_read(nbytes, steps, warmup):
@@ -907,7 +989,8 @@ def main():
     if not args.no_mlp:
         log("whole MLP: timing ...")
         line["mlp"] = {"decode": bench_mlp_decode(max(1, args.steps // 4), 2),
-                       "prefill": bench_mlp_prefill(10, 3)}
+                       "prefill": bench_mlp_prefill(10, 3),
+                       "one_dispatch_parts": bench_mlp_boundary(max(1, args.steps // 4), 2)}
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: the oracle on bounded samples of every configuration ...")

@@ -13,7 +13,14 @@
 //    per block: the cost of reading a decode call's weight bytes once, which
 //    the matrix-vector kernel cannot beat.
 //
-// Both return 0, or -1 when the launch fails.
+//  * swq_probe_empty, swq_probe_grid_barrier, swq_probe_atomic_add,
+//    swq_probe_read_slices: the parts a whole MLP in one dispatch would pay
+//    at decode -- the launch it saves (a trivial kernel), a grid-wide barrier
+//    between its two phases, f32 atomic accumulation of every I-block's
+//    partial output, and reads of the down projection's rows in the I-slices
+//    the blocks of the first phase own.
+//
+// All return 0, or -1 when the launch fails (or the arguments are invalid).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,6 +100,58 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, int64
   if (threadIdx.x == 0) sink[blockIdx.x] = (float)(x & 0xFFFF);
 }
 
+__global__ __launch_bounds__(64) void probe_empty_kernel(float* sink) {
+  if (threadIdx.x == 0) sink[blockIdx.x] = (float)blockIdx.x;
+}
+
+// Every block arrives once (ticket = its position in the arrivals so far,
+// over every launch), then waits until the whole launch has arrived: the
+// counter never resets, so each launch waits for the next multiple of
+// `blocks`.  The wait gives up after max_spin polls and records that in the
+// block's sink slot (1), so the kernel ends whether or not every block of a
+// launch is resident.
+__global__ __launch_bounds__(256) void probe_grid_barrier_kernel(unsigned* counter, unsigned blocks, int max_spin,
+                                                                 float* sink) {
+  __shared__ int timed_out;
+  if (threadIdx.x == 0) {
+    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned target = (ticket / blocks + 1u) * blocks;
+    int spin = 0;
+    while ((int)(__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0 &&
+           spin < max_spin)
+      ++spin;
+    timed_out = spin >= max_spin;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = (float)timed_out;
+}
+
+// blocks x n f32 atomic adds: block b adds (b + 1) to each of y[0..n).
+__global__ __launch_bounds__(256) void probe_atomic_add_kernel(float* y, int n) {
+  const float v = (float)(blockIdx.x + 1);
+  for (int j = threadIdx.x; j < n; j += 256) __hip_atomic_fetch_add(y + j, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block b reads bytes [b piece, (b + 1) piece) of every one of `rows` rows
+// of row_bytes (piece: 8 or 16 bytes, one load per row), threads over rows.
+__global__ __launch_bounds__(256) void probe_read_slices_kernel(const unsigned char* src, int rows, int row_bytes,
+                                                                int piece, float* sink) {
+  uint32_t x = 0;
+  for (int r = threadIdx.x; r < rows; r += 256) {
+    const unsigned char* at = src + (int64_t)r * row_bytes + (int64_t)blockIdx.x * piece;
+    if (piece == 16) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(at));
+      x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    } else {
+      const uint64_t v = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(at));
+      x ^= (uint32_t)v ^ (uint32_t)(v >> 32);
+    }
+  }
+  x ^= __shfl_xor(x, 1);
+  x ^= __shfl_xor(x, 2);
+  if (threadIdx.x == 0) sink[blockIdx.x] = (float)(x & 0xFFFF);
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +173,42 @@ int swq_probe_read(const void* src, int64_t bytes, float* sink, void* stream) {
   const int64_t blocks = swq_probe_read_blocks(bytes);
   hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)src, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// One trivial block per `blocks`; sink: float32 [blocks].
+int swq_probe_empty(int blocks, float* sink, void* stream) {
+  if (blocks <= 0 || !sink) return -1;
+  hipLaunchKernelGGL(probe_empty_kernel, dim3(blocks), dim3(64), 0, (hipStream_t)stream, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// counter: one uint32 in device memory, zero before the first launch and
+// never written by the host afterwards; sink: float32 [blocks] (1 where a
+// block gave up waiting after max_spin polls).
+int swq_probe_grid_barrier(int blocks, unsigned* counter, int max_spin, float* sink, void* stream) {
+  if (blocks <= 0 || !counter || !sink || max_spin <= 0) return -1;
+  hipLaunchKernelGGL(probe_grid_barrier_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, counter,
+                     (unsigned)blocks, max_spin, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// y: float32 [n] device buffer.
+int swq_probe_atomic_add(int blocks, int n, float* y, void* stream) {
+  if (blocks <= 0 || n <= 0 || !y) return -1;
+  hipLaunchKernelGGL(probe_atomic_add_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, y, n);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// src: rows x row_bytes (16-byte aligned rows), blocks * piece <= row_bytes,
+// piece 8 or 16; sink: float32 [blocks].
+int swq_probe_read_slices(const void* src, int rows, int row_bytes, int piece, int blocks, float* sink,
+                          void* stream) {
+  if (!src || !sink || rows <= 0 || blocks <= 0 || (piece != 8 && piece != 16) || row_bytes % 16 ||
+      ((uintptr_t)src & 15) || (int64_t)blocks * piece > row_bytes)
+    return -1;
+  hipLaunchKernelGGL(probe_read_slices_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const unsigned char*)src, rows, row_bytes, piece, sink);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
