@@ -17,8 +17,10 @@
  *    specs independent), its shapes and "caller owns the result":
  *    same file, host entry and its docstring;
  *  - the two precision variants: same file, precision-variants comment;
- *  - the support predicate (bf16 activations, affine biases present, group
- *    size a multiple of 32, H a multiple of 32): same file, support predicate;
+ *  - the support predicate (bf16 or float16 activations, affine biases
+ *    present, group size a multiple of 32, H a multiple of 32): same file,
+ *    support predicate; the kernel's element type is x's (its template
+ *    dtype argument), so scales, biases and result share it;
  *  - the M threshold below which the caller keeps the matrix-vector path:
  *    same file, M-threshold function and the "where the win is" comment.
  *
@@ -33,11 +35,12 @@
  * Ownership and synchronisation: every pointer passed to the forward calls
  * is a DEVICE pointer owned by the caller; the library never frees or keeps
  * them.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- * and the call returns without synchronising.  A matrix-vector call with
- * M*H > 8192 (other than M = 1 with H <= 8192, and 2 <= M <= 4 with
- * 2048 <= H <= 4096) needs a device workspace for the staged x, and every
- * matrix-matrix call needs one for x and the weights' extra rows, scale tiles
- * and row exponents: the library keeps one per (device, stream), allocated on
+ * and the call returns without synchronising.  A matrix-vector call whose
+ * kernel cannot convert x itself needs a device workspace for the staged x
+ * (swiglu_q_staging_bytes says how much; most calls with M <= 32 need none),
+ * and every matrix-matrix call needs one for x and the weights' extra rows,
+ * scale tiles and row exponents: the library keeps one per (device, stream),
+ * allocated on
  * first use and replaced by a larger one (at least twice the size) when a call
  * needs more.  Growth never synchronises: a replaced buffer is kept, not freed,
  * until swiglu_q_release_workspace(), so work already queued on the stream and
@@ -60,6 +63,10 @@
  * rounded to binary16's grid at the row's scale, an error below 2^-39 of the
  * row's largest term per weight.  Results are finite whenever the float32
  * sums are (the M = 1 kernel applies s and b in float32 throughout).
+ * Binary16 scales (swiglu_q_forward_f16) have 11 significant bits; they are
+ * split into a part of 8 significant bits and a remainder of at most 3, each
+ * with its own MFMA operand, and the window becomes 2^-25 (8-bit codes:
+ * 2^-21) of the row's largest term, with the same bound outside it.
  *
  * Errors: every entry point validates its arguments on the host before any
  * HIP call and returns a status; nothing is launched on error.
@@ -134,6 +141,25 @@ int swiglu_q_forward(const void *x,
  * calls that overlap in time on one GPU, on any streams, race and give wrong
  * results; order them (one stream, or events).
  */
+/*
+ * Fused forward with binary16 activations: x, sg, bg, su and bu are float16
+ * (IEEE binary16) instead of bf16, and out is float16 for SWQ_MATCH (gate and
+ * up rounded to float16, RNE) and SWQ_F32_BF16OUT (float32 internal, rounded
+ * once to float16), float32 for SWQ_F32.  Everything else -- arguments,
+ * layout, validation, status codes, workspace, dispatch -- is as in
+ * swiglu_q_forward.  Source: the support predicate accepts float16
+ * activations and the kernel's element type follows x ("mlx-bun 0.0.7 ->
+ * 0.0.9", page 42, fused-swiglu-kernel.ts, support predicate and host
+ * entry).  The matrix-matrix path runs 128 x 128 tiles and one more MFMA per
+ * code block (the scales' two parts), the matrix-vector kernels as for bf16.
+ */
+int swiglu_q_forward_f16(const void *x,
+                         const uint32_t *Wg, const void *sg, const void *bg,
+                         const uint32_t *Wu, const void *su, const void *bu,
+                         int64_t M, int64_t H, int64_t I,
+                         int bits_g, int gs_g, int bits_u, int gs_u,
+                         int precision_mode, void *out, void *stream);
+
 int swiglu_q_forward_noalloc(const void *x,
                              const uint32_t *Wg, const void *sg, const void *bg,
                              const uint32_t *Wu, const void *su, const void *bu,

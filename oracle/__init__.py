@@ -53,6 +53,15 @@ def lib():
     L.oracle_swiglu_pairs.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32,
                                                  i64, vp, vp, vp, vp, vp, vp, vp, i32]
     L.oracle_swiglu_pairs.restype = i32
+    L.oracle_swiglu_pairs_act.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32,
+                                                     i64, vp, vp, vp, vp, vp, vp, vp, i32, i32]
+    L.oracle_swiglu_pairs_act.restype = i32
+    L.oracle_f16_rne_array.argtypes = [vp, i64, vp]
+    L.oracle_f16_rne_array.restype = None
+    L.oracle_f16_value_array.argtypes = [vp, i64, vp]
+    L.oracle_f16_value_array.restype = None
+    L.oracle_f16_rne.argtypes = [ctypes.c_double]
+    L.oracle_f16_rne.restype = ctypes.c_uint16
     L.oracle_qmm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.oracle_qmm.restype = i32
     L.oracle_unpack.argtypes = [vp, i64, i64, i32, vp]
@@ -81,8 +90,10 @@ def swiglu_pairs(prob, mode, ms=None, ns=None, nthreads=0, want=("g", "u", "nu_g
     """Evaluate selected output elements of a ``synth.Problem``.
 
     ``ms``/``ns`` are equal-length index arrays; ``None`` means every element
-    in row-major order.  Returns a dict of float64 arrays named
-    g, u, nu_g, nu_u, h (h is the unrounded float64 hidden value)."""
+    in row-major order.  A problem drawn with binary16 activations
+    (``prob.act == "f16"``) is read and, in MATCH, rounded as binary16.
+    Returns a dict of float64 arrays named g, u, nu_g, nu_u, h (h is the
+    unrounded float64 hidden value), and ``act``."""
     L = lib()
     x = _c(prob.x, np.uint16)
     wg, sg, bg = _c(prob.wg, np.uint32), _c(prob.sg, np.uint16), _c(prob.bg, np.uint16)
@@ -96,20 +107,30 @@ def swiglu_pairs(prob, mode, ms=None, ns=None, nthreads=0, want=("g", "u", "nu_g
             raise ValueError("ms and ns differ in length")
         n = msa.size
     out = {k: np.empty(n, dtype=np.float64) for k in want}
-    rc = L.oracle_swiglu_pairs(_p(x), _p(wg), _p(sg), _p(bg), _p(wu), _p(su), _p(bu),
-                               prob.M, prob.H, prob.I, prob.bits_g, prob.gs_g,
-                               prob.bits_u, prob.gs_u, int(mode), n, _p(msa), _p(nsa),
-                               _p(out.get("g")), _p(out.get("u")), _p(out.get("nu_g")),
-                               _p(out.get("nu_u")), _p(out.get("h")), int(nthreads))
+    act = act_code(prob)
+    rc = L.oracle_swiglu_pairs_act(_p(x), _p(wg), _p(sg), _p(bg), _p(wu), _p(su), _p(bu),
+                                   prob.M, prob.H, prob.I, prob.bits_g, prob.gs_g,
+                                   prob.bits_u, prob.gs_u, int(mode), n, _p(msa), _p(nsa),
+                                   _p(out.get("g")), _p(out.get("u")), _p(out.get("nu_g")),
+                                   _p(out.get("nu_u")), _p(out.get("h")), act, int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    out["act"] = act
     return out
+
+
+def act_code(prob):
+    """0 for bf16 activations (the default), 1 for binary16."""
+    a = getattr(prob, "act", "bf16")
+    if a not in ("bf16", "f16"):
+        raise ValueError(f"unknown activation type {a!r}")
+    return 1 if a == "f16" else 0
 
 
 def swiglu_full(prob, mode, nthreads=0):
     """Every output element, each array reshaped to ``[M, I]``."""
     r = swiglu_pairs(prob, mode, nthreads=nthreads)
-    return {k: v.reshape(prob.M, prob.I) for k, v in r.items()}
+    return {k: (v.reshape(prob.M, prob.I) if k != "act" else v) for k, v in r.items()}
 
 
 def qmm(x_bits, W, S, B, M, H, N, bits, gs):
@@ -197,6 +218,24 @@ def bf16_value(bits):
     """bf16 bit patterns -> float64."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f16_rne(v):
+    """float64 array -> IEEE binary16 bit patterns (uint16), rounded from the double."""
+    L = lib()
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    L.oracle_f16_rne_array(_p(v), v.size, _p(out))
+    return out
+
+
+def f16_value(bits):
+    """IEEE binary16 bit patterns -> float64 (the C oracle's decoder)."""
+    L = lib()
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    L.oracle_f16_value_array(_p(b), b.size, _p(out))
+    return out
 
 
 def silu(v):

@@ -19,14 +19,26 @@ In MATCH the gate and up are rounded to bf16 before the nonlinearity.  Where
 the exact value lies within ``eta * nu`` (eta = 2^-12) of a bf16 rounding
 midpoint, a correct float32 accumulation may round to either neighbour; both
 are admissible, and the candidate nearest the device value is used.
+
+Binary16 activations (the oracle dict's ``act`` = 1): the 16-bit output and
+MATCH's gate/up rounding are binary16, and the bar for a binary16 output is
+1e-3 -- two binary16 half-ulps (2^-11 each), as 8e-3 is two bf16 half-ulps
+(2^-8) rounded up: the one rounding at the store plus float32 error.  float32
+output keeps 1e-4.  An output below its type's normal range is rounded to
+that type's subnormal quantum (binary16: 2^-24, bf16: 2^-133, float32:
+2^-149), an absolute error up to half of it on top of the relative error
+of the steps before; so the denominator gains ``quantum / (2 tol)``, which
+admits exactly that rounding beside the relative bar (and is negligible for
+any output in the type's normal range).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import bf16_rne, bf16_value, silu
+from . import bf16_rne, bf16_value, f16_rne, f16_value, silu
 
 TOL = {0: 8e-3, 1: 1e-4, 2: 8e-3}
+TOL_F16 = {0: 1e-3, 1: 1e-4, 2: 1e-3}
 ETA = 2.0 ** -12
 FLOOR = 2.0 ** -4
 TAU0 = 2.0 ** -24
@@ -42,20 +54,34 @@ def silu_prime(t):
     return s * (1.0 + t * (1.0 - s))
 
 
-def bf16_candidates(v, nu, eta=ETA):
-    """(primary, alternative) bf16 roundings of float64 ``v`` as float64.
+def _rounding(act):
+    return (f16_rne, f16_value) if act else (bf16_rne, bf16_value)
 
-    primary = RNE(v).  alternative = the other bf16 neighbour of ``v`` when
-    ``v`` lies within ``eta * nu`` of the midpoint between the two; otherwise
-    it equals primary."""
+
+def output_quantum(mode, act):
+    """The smallest subnormal of the output type: float32 in mode 1, else the
+    16-bit activation type."""
+    if mode == 1:
+        return 2.0 ** -149
+    return 2.0 ** -24 if act else 2.0 ** -133
+
+
+def bf16_candidates(v, nu, eta=ETA, act=0):
+    """(primary, alternative) bf16 (act 1: binary16) roundings of float64 ``v``
+    as float64.
+
+    primary = RNE(v).  alternative = the other neighbour of ``v`` when ``v``
+    lies within ``eta * nu`` of the midpoint between the two; otherwise it
+    equals primary."""
+    rne, value = _rounding(act)
     v = np.asarray(v, dtype=np.float64)
     a = np.abs(v)
     sign = np.where(np.signbit(v), -1.0, 1.0)
-    pb = bf16_rne(a).astype(np.int64)
-    pv = bf16_value(pb.astype(np.uint16))
+    pb = rne(a).astype(np.int64)
+    pv = value(pb.astype(np.uint16))
     above = pv > a
     ob = np.where(above, np.maximum(pb - 1, 0), pb + 1)
-    ov = bf16_value(ob.astype(np.uint16))
+    ov = value(ob.astype(np.uint16))
     exact = pv == a
     mid = 0.5 * (pv + ov)
     admissible = (~exact) & (np.abs(a - mid) <= eta * np.asarray(nu, dtype=np.float64))
@@ -64,11 +90,12 @@ def bf16_candidates(v, nu, eta=ETA):
 
 
 def reference_values(o, mode):
-    """Primary reference r and its gate/up (rounded in MATCH)."""
+    """Primary reference r and its gate/up (rounded in MATCH to the activation type)."""
     g, u = o["g"], o["u"]
     if mode == 0:
-        g = bf16_value(bf16_rne(g))
-        u = bf16_value(bf16_rne(u))
+        rne, value = _rounding(o.get("act", 0))
+        g = value(rne(g))
+        u = value(rne(u))
     return silu(g) * u, g, u
 
 
@@ -77,12 +104,14 @@ def evaluate(y, o, mode, eta=ETA):
     oracle dict ``o``) against the oracle.  Returns a dict of statistics with
     ``ok`` set when the bar of ``mode`` holds."""
     y = np.asarray(y, dtype=np.float64).reshape(-1)
+    act = int(o.get("act", 0))
+    tol = (TOL_F16 if act else TOL)[mode]
     g, u = o["g"].reshape(-1), o["u"].reshape(-1)
     nug, nuu = o["nu_g"].reshape(-1), o["nu_u"].reshape(-1)
-    r0, gp, up = reference_values({"g": g, "u": u}, mode)
+    r0, gp, up = reference_values({"g": g, "u": u, "act": act}, mode)
     if mode == 0:
-        g_a, g_b = bf16_candidates(g, nug, eta)
-        u_a, u_b = bf16_candidates(u, nuu, eta)
+        g_a, g_b = bf16_candidates(g, nug, eta, act)
+        u_a, u_b = bf16_candidates(u, nuu, eta, act)
         cands = [silu(gc) * uc for gc in (g_a, g_b) for uc in (u_a, u_b)]
         dist = np.stack([np.abs(y - c) for c in cands])
         pick = np.argmin(dist, axis=0)
@@ -92,7 +121,7 @@ def evaluate(y, o, mode, eta=ETA):
     tau = FLOOR * (np.abs(silu(gp)) * nuu + np.abs(silu_prime(gp) * up) * nug)
     rms = float(np.sqrt(np.mean(r0 * r0))) if r0.size else 0.0
     tau0 = TAU0 * rms
-    denom = np.maximum(np.maximum(np.abs(r), tau), tau0)
+    denom = np.maximum(np.maximum(np.abs(r), tau), tau0) + output_quantum(mode, act) / 2.0 / tol
     diff = np.abs(y - r)
     finite = np.isfinite(y)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -108,9 +137,9 @@ def evaluate(y, o, mode, eta=ETA):
         "floor_fraction": float(np.mean(np.maximum(tau, tau0) > np.abs(r))) if n else 0.0,
         "max_abs_over_rms": float(np.max(diff) / rms) if (n and rms > 0) else 0.0,
         "nonfinite": int(np.sum(~finite)),
-        "tol": TOL[mode],
+        "tol": tol,
     }
-    stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= TOL[mode]))
+    stats["ok"] = bool(n == 0 or (stats["nonfinite"] == 0 and stats["max_err"] <= tol))
     return stats
 
 

@@ -28,22 +28,41 @@ def bf16_exact(bits: int) -> Fraction:
     return sign * Fraction(128 + man, 128) * (Fraction(2) ** (exp - 127))
 
 
+def f16_exact(bits: int) -> Fraction:
+    """Exact value of a finite IEEE binary16 bit pattern (1 sign, 5 exponent
+    bits with bias 15, 10 fraction bits)."""
+    bits = int(bits) & 0xFFFF
+    sign = -1 if bits & 0x8000 else 1
+    exp = (bits >> 10) & 0x1F
+    man = bits & 0x3FF
+    if exp == 0x1F:
+        raise ValueError("non-finite binary16")
+    if exp == 0:                       # subnormal: man * 2^(-14-10)
+        return sign * Fraction(man, 1 << 24)
+    return sign * Fraction(1024 + man, 1024) * (Fraction(2) ** (exp - 15))
+
+
+_DECODE = {"bf16": bf16_exact, "f16": f16_exact}
+
+
 def code_at(words_row, k: int, bits: int) -> int:
     per = 32 // bits
     w = int(words_row[k // per])
     return (w >> (bits * (k % per))) & ((1 << bits) - 1)
 
 
-def dequant_row(words_row, s_row, b_row, H: int, bits: int, gs: int):
-    """Exact weights of one output feature."""
-    return [bf16_exact(s_row[k // gs]) * code_at(words_row, k, bits) + bf16_exact(b_row[k // gs])
-            for k in range(H)]
+def dequant_row(words_row, s_row, b_row, H: int, bits: int, gs: int, act: str = "bf16"):
+    """Exact weights of one output feature (scales and biases of type ``act``)."""
+    dec = _DECODE[act]
+    return [dec(s_row[k // gs]) * code_at(words_row, k, bits) + dec(b_row[k // gs]) for k in range(H)]
 
 
-def qmm_exact(x, W, S, B, M: int, H: int, N: int, bits: int, gs: int):
-    """Exact ``y[m][n] = sum_k x[m,k] w[n,k]`` as a list of lists of Fractions."""
-    xs = [[bf16_exact(x[m][k]) for k in range(H)] for m in range(M)]
-    ws = [dequant_row(W[n], S[n], B[n], H, bits, gs) for n in range(N)]
+def qmm_exact(x, W, S, B, M: int, H: int, N: int, bits: int, gs: int, act: str = "bf16"):
+    """Exact ``y[m][n] = sum_k x[m,k] w[n,k]`` as a list of lists of Fractions
+    (x, scales and biases of type ``act``: "bf16" or "f16")."""
+    dec = _DECODE[act]
+    xs = [[dec(x[m][k]) for k in range(H)] for m in range(M)]
+    ws = [dequant_row(W[n], S[n], B[n], H, bits, gs, act) for n in range(N)]
     return [[sum((xs[m][k] * ws[n][k] for k in range(H)), Fraction(0)) for n in range(N)]
             for m in range(M)]
 

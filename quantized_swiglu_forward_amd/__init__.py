@@ -53,6 +53,8 @@ def load_library(path):
     vp, i64, i32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
     L.swiglu_q_forward.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
     L.swiglu_q_forward.restype = i32
+    L.swiglu_q_forward_f16.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
+    L.swiglu_q_forward_f16.restype = i32
     L.swiglu_q_forward_noalloc.argtypes = [vp] * 7 + [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp]
     L.swiglu_q_forward_noalloc.restype = i32
     L.swiglu_q_linear.argtypes = [vp] * 4 + [i64, i64, i64, i32, i32, i32, vp, vp]
@@ -114,6 +116,13 @@ def swiglu_q_forward(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, g
     return lib().swiglu_q_forward(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
                                   M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
                                   _stream(stream))
+
+
+def swiglu_q_forward_f16(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u,
+                         precision_mode, out, stream=None) -> int:
+    return lib().swiglu_q_forward_f16(_ptr(x), _ptr(Wg), _ptr(sg), _ptr(bg), _ptr(Wu), _ptr(su), _ptr(bu),
+                                      M, H, I, bits_g, gs_g, bits_u, gs_u, precision_mode, _ptr(out),
+                                      _stream(stream))
 
 
 def swiglu_q_forward_noalloc(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u,
@@ -207,11 +216,14 @@ strerror = swiglu_q_strerror
 _BITS16 = ("torch.bfloat16", "torch.int16", "torch.uint16")
 
 
-def _rows(x, what):
+def _rows(x, what, f16=False):
     """(x as [M, H], leading shape) for bf16 activations (or their int16/uint16
-    bit patterns); raises for any other dtype or a non-contiguous tensor."""
-    if str(x.dtype) not in _BITS16:
-        raise TypeError(f"{what}: x must be bfloat16 (or its 16-bit patterns), not {x.dtype}")
+    bit patterns; with f16, float16 activations); raises for any other dtype
+    or a non-contiguous tensor."""
+    ok = _BITS16 + (("torch.float16",) if f16 else ())
+    if str(x.dtype) not in ok:
+        raise TypeError(f"{what}: x must be bfloat16{' or float16' if f16 else ''} "
+                        f"(or its 16-bit patterns), not {x.dtype}")
     if x.dim() < 1:
         raise ValueError(f"{what}: x needs at least one dimension")
     if not x.is_contiguous():
@@ -224,19 +236,25 @@ def forward(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_u=None,
             mode=SWQ_MATCH, out=None, stream=None):
     """``hidden`` for device tensors: x [..., H] (bf16 or int16/uint16 bit
     patterns), packed codes int32/uint32 [I, H*bits/32], scales/biases bf16
-    [I, H/gs].  Returns ``out`` ([..., I], bf16 or float32 by mode)."""
+    [I, H/gs].  float16 x (with float16 scales and biases) runs
+    swiglu_q_forward_f16.  Returns ``out`` ([..., I]: float32 in SWQ_F32,
+    else x's 16-bit type)."""
     import torch
     bits_u = bits_g if bits_u is None else bits_u
     gs_u = gs_g if gs_u is None else gs_u
-    x2, lead = _rows(x, "forward")
+    x2, lead = _rows(x, "forward", f16=True)
+    f16 = x.dtype == torch.float16
+    if any((t.dtype == torch.float16) != f16 for t in (sg, bg, su, bu)):
+        raise TypeError("forward: scales and biases must have x's type (float16 with float16 x, bf16 otherwise)")
     M, H = int(x2.shape[0]), int(x2.shape[1])
     I = int(wg.shape[0])
     if out is None:
-        dt = torch.float32 if mode == SWQ_F32 else torch.bfloat16
+        dt = torch.float32 if mode == SWQ_F32 else (torch.float16 if f16 else torch.bfloat16)
         out = torch.empty(lead + (I,), dtype=dt, device=x.device)
-    rc = swiglu_q_forward(x2, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
+    entry = swiglu_q_forward_f16 if f16 else swiglu_q_forward
+    rc = entry(x2, wg, sg, bg, wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, mode, out, stream)
     if rc != SWQ_OK:
-        raise SwigluQError(rc, "swiglu_q_forward")
+        raise SwigluQError(rc, entry.__name__)
     return out
 
 
@@ -299,12 +317,14 @@ def debug_gemm_tensors(x, wg, sg, bg, wu, su, bu, bits_g, gs_g, bits_u=None, gs_
 
 def to_device(prob, device="cuda"):
     """Copy a host problem (numpy bit patterns) to device tensors; returns the
-    tuple (x, wg, sg, bg, wu, su, bu)."""
+    tuple (x, wg, sg, bg, wu, su, bu), x and the scales and biases as bf16, or
+    float16 for a problem drawn with binary16 activations."""
     import numpy as np
     import torch
+    dt16 = torch.float16 if getattr(prob, "act", "bf16") == "f16" else torch.bfloat16
 
     def t16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(dt16)
 
     def t32(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(device)

@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "../../include/swiglu_q.h"
+#include "swq_device.h"
 #include "swq_kernels.h"
 
 using namespace swq;
@@ -268,7 +269,8 @@ int acquire(hipStream_t stream, size_t need, void** out, void* fixed, size_t fix
 int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const uint32_t* Wu,
         const void* su, const void* bu, int64_t M, int64_t H, int64_t I, int64_t I_u, int64_t ldo,
         int bits_g, int gs_g, int bits_u, int gs_u, int mode, void* out, float* dbg_g, float* dbg_u,
-        const void* res, int path, void* stream_v, void* fixed = nullptr, size_t fixed_bytes = 0) {
+        const void* res, int path, void* stream_v, void* fixed = nullptr, size_t fixed_bytes = 0,
+        int act = kActBf16) {
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
@@ -286,6 +288,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     p.gs_g = gs_g; p.gs_u = gs_u; p.mode = mode;
     p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
     p.xa = nullptr; p.xexp = nullptr; p.kexp = nullptr;
+    p.act = act;
     if (logging())
       fprintf(stderr, "[swiglu_q] gemv M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
               (long long)M, (long long)H, (long long)I, bits_g, bits_u, gs_g, gs_u, mode);
@@ -314,6 +317,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       // them from the scales of its first pass
       pp.k_only = skinny_needs_kexp((int)M, (int)H, bits_g, bits_u) ? 1 : 0;
       pp.xlane = M > 16 ? 2 : 1;
+      pp.act = act;
       p.xa = pp.xa;
       p.xexp = pp.xexp;
       p.kexp = pp.k_only ? pp.kexp : nullptr;
@@ -352,6 +356,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   pp.kexp = (int*)(wsb + L.kx);
   pp.k_only = 0;
   pp.xlane = 0;
+  pp.act = act;
 
   MfmaParams p;
   p.xa = xa; p.xexp = xexp;
@@ -366,6 +371,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.bext_g = eg; p.bext_u = eu;
   p.kexp = pp.kexp;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
+  p.act = act;
   {
     const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
     p.vec = (I % 4 == 0) && (ldo % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
@@ -456,6 +462,19 @@ int swiglu_q_forward(const void* x, const uint32_t* Wg, const void* sg, const vo
   if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
   return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
              nullptr, nullptr, nullptr, SWQ_PATH_AUTO, stream);
+}
+
+int swiglu_q_forward_f16(const void* x, const uint32_t* Wg, const void* sg, const void* bg,
+                         const uint32_t* Wu, const void* su, const void* bu, int64_t M, int64_t H, int64_t I,
+                         int bits_g, int gs_g, int bits_u, int gs_u, int precision_mode, void* out,
+                         void* stream) {
+  int rc = validate(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u);
+  if (rc != SWQ_OK) return rc;
+  if (precision_mode < SWQ_MATCH || precision_mode > SWQ_F32_BF16OUT) return SWQ_ERR_UNSUPPORTED;
+  if (!out) return SWQ_ERR_NULL;
+  if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
+  return run(x, Wg, sg, bg, Wu, su, bu, M, H, I, I, I, bits_g, gs_g, bits_u, gs_u, precision_mode, out,
+             nullptr, nullptr, nullptr, SWQ_PATH_AUTO, stream, nullptr, 0, kActF16);
 }
 
 int swiglu_q_forward_noalloc(const void* x, const uint32_t* Wg, const void* sg, const void* bg,

@@ -48,6 +48,45 @@ __device__ __forceinline__ float round_to_bf16(float f) {
   return bf16_to_f32(f32_to_bf16(f));
 }
 
+// Activation types: bf16 (swiglu_q_forward) or binary16 (swiglu_q_forward_f16)
+// for x, the scales and biases, and the 16-bit output.
+enum : int { kActBf16 = 0, kActF16 = 1 };
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float act_to_f32(uint16_t b, int act) {
+  return act == kActF16 ? f16_to_f32(b) : bf16_to_f32(b);
+}
+__device__ __forceinline__ uint16_t f32_to_act(float f, int act) {
+  return act == kActF16 ? f32_to_f16(f) : f32_to_bf16(f);
+}
+__device__ __forceinline__ float round_to_act(float f, int act) {
+  return act == kActF16 ? (float)(_Float16)f : round_to_bf16(f);
+}
+
+// Exponent e of a row's (or chunk's) largest magnitude, from its bits without
+// the sign (bf16: 8-bit exponent field; binary16: 5-bit), so that x 2^-e lies
+// below 2 and its largest element in [1, 2) (a subnormal maximum: e one
+// below the smallest normal exponent, x 2^-e still below 2), an all-zero row 0.
+__device__ __forceinline__ int x_exponent(uint32_t amax_bits, int act) {
+  if (amax_bits == 0) return 0;
+  if (act == kActF16) {
+    const int field = (int)(amax_bits >> 10);
+    return field == 0 ? -15 : field - 15;
+  }
+  const int field = (int)(amax_bits >> 7);
+  return field == 0 ? -127 : field - 127;
+}
+
+// A binary16 scale (times its row's 2^-k) as two parts for two MFMA planes:
+// hi = s rounded to 8 significant bits, lo = s - hi (exact, at most 3
+// significant bits), so that hi (q - z) and lo (q - z) are each exact in
+// binary16 where a bf16 scale's product is (lo: 8-bit codes too).
+__device__ __forceinline__ f16x2 split_scale(float s) {
+  const float hi = round_to_bf16(s);
+  return (f16x2){(_Float16)hi, (_Float16)(s - hi)};
+}
+
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -105,17 +144,20 @@ __device__ __forceinline__ void codes4(uint32_t w, uint32_t out[4]) {
 // Eight 8-bit codes in two words (wa: codes 0..3, wb: codes 4..7) -> the low
 // and high nibble planes (lo-8) and (hi-8) as f16 pairs in the order
 // (c0,c4) (c1,c5) (c2,c6) (c3,c7).  v_perm_b32 gathers byte j of wa and byte j
-// of wb into bytes 0 and 2 of one register.
+// of wb into bytes 0 and 2 of one register.  With `full`, also the whole
+// codes q - 136 (a byte ORed with 0x6400 is 1024 + q; exact in binary16).
 __device__ __forceinline__ void codes8(uint32_t wa, uint32_t wb, uint32_t lo[4], uint32_t hi[4],
-                                       const NibbleK& k = kNibbleLiterals) {
+                                       const NibbleK& k = kNibbleLiterals, uint32_t* full = nullptr) {
   const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const f16x2 c1160 = {(_Float16)1160.0f, (_Float16)1160.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
     const uint32_t t = __builtin_amdgcn_perm(wb, wa, sel);
     lo[j] = as_u32(as_h2((t & k.m_lo) | k.g_lo) - c1032);
     hi[j] = as_u32(as_h2((t & k.m_hi) | k.g_hi) - c72);
+    if (full) full[j] = as_u32(as_h2((t & 0x00FF00FFu) | 0x64006400u) - c1160);
   }
 }
 
@@ -168,12 +210,20 @@ __device__ __forceinline__ int row_exponent_k(float m) {
   return min(max(E - 14, -200), 200);
 }
 
-// sigma(t) = 1 / (1 + e^-t) with the hardware exp2 and reciprocal
-// (about 1 ulp each); e^-t overflows to +inf for t < about -88, giving
-// sigma = 0 and silu = -0.
-__device__ __forceinline__ float sigmoid_fast(float t) {
-  const float e = __builtin_amdgcn_exp2f(-t * 1.4426950408889634f);
-  return __builtin_amdgcn_rcpf(1.0f + e);
+// silu(g) u = g sigma(g) u, sigma(g) = 1 / (1 + e^-g) for g >= 0 and
+// e^g / (1 + e^g) below, with e = e^-|g| from the hardware exp2 and the
+// reciprocal (about 1 ulp each).  Once |g| > 64 ln 2, e is taken times 2^64
+// (1 + e is then 1 in float32), so it stays a normal number down to
+// g = -190 ln 2 and a negative g's product leaves float32's normal range only
+// at the last step, one rounding; below that the true value is under half
+// float32's smallest subnormal whenever |g u| < 2^40.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  const float a = -fabsf(g) * 1.4426950408889634f;
+  const bool deep = a < -64.0f;
+  const float e = __builtin_amdgcn_exp2f(deep ? a + 64.0f : a);
+  const float r = __builtin_amdgcn_rcpf(1.0f + (deep ? 0.0f : e));
+  const float h = g * (g >= 0.0f ? r : e * r) * u;
+  return (deep && g < 0.0f) ? ldexpf(h, -64) : h;
 }
 
 // Debug build (-DSWQ_LDS_POISON): every kernel fills its LDS with a poison
@@ -193,13 +243,14 @@ __device__ __forceinline__ void lds_poison(void* p, size_t bytes, uint32_t patte
 enum : int { kMatch = 0, kF32 = 1, kF32Bf16Out = 2 };
 // (the linear's epilogue kinds kLinBf16 / kLinF32 are in swq_kernels.h)
 
-// The epilogue on one element: gate g and up u in float32.
-__device__ __forceinline__ float swiglu_epilogue(float g, float u, int mode) {
+// The epilogue on one element: gate g and up u in float32 (MATCH rounds them
+// to the activation type first).
+__device__ __forceinline__ float swiglu_epilogue(float g, float u, int mode, int act = kActBf16) {
   if (mode == kMatch) {
-    g = round_to_bf16(g);
-    u = round_to_bf16(u);
+    g = round_to_act(g, act);
+    u = round_to_act(u, act);
   }
-  return g * sigmoid_fast(g) * u;
+  return silu_times(g, u);
 }
 
 // ------------------------------------------------ LDS-writing loads ----

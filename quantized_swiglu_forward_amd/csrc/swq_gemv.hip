@@ -92,17 +92,13 @@ __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, flo
       if (n < p.I_u) reinterpret_cast<uint16_t*>(p.out)[o + p.I] = f32_to_bf16(u);
     }
   } else {
-    const float h = swiglu_epilogue(g, u, p.mode);
+    const float h = swiglu_epilogue(g, u, p.mode, p.act);
     if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
-    else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(h);
+    else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(h, p.act);
   }
 }
 
-__device__ __forceinline__ int row_exponent(uint32_t amax_bits) {
-  if (amax_bits == 0) return 0;
-  const int field = (int)(amax_bits >> 7);
-  return field == 0 ? -127 : field - 127;
-}
+
 
 // ------------------------------------------------------------- M == 1 ----
 //
@@ -128,6 +124,21 @@ __device__ __forceinline__ int row_exponent(uint32_t amax_bits) {
 // both meet 16 x', which is what q = 16 hi + lo needs.
 //
 
+// Two exact binary16 products x c, each added to p with one float32 rounding
+// (v_fma_mix_f32).  v_dot2_f32_f16 would take both in one instruction, but
+// its sum of two products and the accumulator is not rounded to nearest
+// when their exponents differ widely (measured: a downward bias of about
+// 2^-22 of the sum per step), which sums of many same-sign products turn
+// into errors well above float32 accumulation.
+// (Contraction is off here: the compiler would fold the two FMAs back into
+// v_dot2.)
+__device__ __forceinline__ float fma2(uint32_t xv, uint32_t cv, float p) {
+#pragma clang fp contract(off)
+  const f16x2 x = as_h2(xv), c = as_h2(cv);
+  p = __builtin_fmaf((float)x[0], (float)c[0], p);
+  return __builtin_fmaf((float)x[1], (float)c[1], p);
+}
+
 // Unscaled dot of one chunk in units of 2^-20: xa holds the 16x pairs
 // (codes at bits [0,4)), xb the 1x pairs (codes at bits [4,8)).
 template <int BITS>
@@ -138,10 +149,10 @@ __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const ui
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = r.w[0][j];
       const uint32_t w8 = w >> 8;
-      p = __builtin_amdgcn_fdot2(as_h2(xa[2 * j]), as_h2(w & 0x000F000Fu), p, false);
-      p = __builtin_amdgcn_fdot2(as_h2(xb[2 * j]), as_h2(w & 0x00F000F0u), p, false);
-      p = __builtin_amdgcn_fdot2(as_h2(xa[2 * j + 1]), as_h2(w8 & 0x000F000Fu), p, false);
-      p = __builtin_amdgcn_fdot2(as_h2(xb[2 * j + 1]), as_h2(w8 & 0x00F000F0u), p, false);
+      p = fma2(xa[2 * j], w & 0x000F000Fu, p);
+      p = fma2(xb[2 * j], w & 0x00F000F0u, p);
+      p = fma2(xa[2 * j + 1], w8 & 0x000F000Fu, p);
+      p = fma2(xb[2 * j + 1], w8 & 0x00F000F0u, p);
     }
   } else {
     // xa / xb interleave as (pair 0, pair 2) / (pair 1, pair 3) of each 8-block;
@@ -157,21 +168,12 @@ __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const ui
       for (int t = 0; t < 4; ++t) {
         const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + t) << 16) | (uint32_t)t;
         const uint32_t v = __builtin_amdgcn_perm(wb, wa, sel);
-        p = __builtin_amdgcn_fdot2(as_h2(xq[t]), as_h2(v & 0x000F000Fu), p, false);
-        p = __builtin_amdgcn_fdot2(as_h2(xq[t]), as_h2(v & 0x00F000F0u), p, false);
+        p = fma2(xq[t], v & 0x000F000Fu, p);
+        p = fma2(xq[t], v & 0x00F000F0u, p);
       }
     }
   }
   return p;
-}
-
-template <int BITS>
-__device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const uint32_t xa[8], const uint32_t xb[8],
-                                            float sx) {
-  const float P = chunk_dot_sub<BITS>(r, xa, xb);
-  const float s = __uint_as_float(r.sb << 16);
-  const float b = __uint_as_float(r.sb & 0xFFFF0000u);
-  return fmaf(s, P, b * sx);
 }
 
 // Sum over aligned groups of `width` lanes (a power of two); every lane of a
@@ -249,31 +251,29 @@ constexpr int kGemv1MaxH = 8192;
 // (16x'0, 16x'4), (x'1, x'5), (16x'2, 16x'6), (x'3, x'7): the operands of
 // code word j in the order the dot products take them.  Lanes past the end
 // of x carry zeros (a quad is all in or all out: H is a multiple of 32).
-__device__ __forceinline__ void stage_x_block(const u32x4& raw, int blk, bool valid, u32x4* xs, float2* xinfo) {
+__device__ __forceinline__ void stage_x_block(const u32x4& raw, int blk, bool valid, u32x4* xs, float2* xinfo,
+                                              int act) {
   uint32_t amax = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) amax = max(amax, max(raw[j] & 0x7FFFu, (raw[j] >> 16) & 0x7FFFu));
   amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
   amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
-  const int e = row_exponent(amax);
+  const int e = x_exponent(amax, act);
   float f[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f[2 * j] = bf16_to_f32((uint16_t)(raw[j] & 0xFFFFu));
-    f[2 * j + 1] = bf16_to_f32((uint16_t)(raw[j] >> 16));
+    f[2 * j] = act_to_f32((uint16_t)(raw[j] & 0xFFFFu), act);
+    f[2 * j + 1] = act_to_f32((uint16_t)(raw[j] >> 16), act);
   }
   u32x4 v;
   v[0] = as_u32((f16x2){(_Float16)ldexpf(f[0], 4 - e), (_Float16)ldexpf(f[4], 4 - e)});
   v[1] = as_u32((f16x2){(_Float16)ldexpf(f[1], -e), (_Float16)ldexpf(f[5], -e)});
   v[2] = as_u32((f16x2){(_Float16)ldexpf(f[2], 4 - e), (_Float16)ldexpf(f[6], 4 - e)});
   v[3] = as_u32((f16x2){(_Float16)ldexpf(f[3], -e), (_Float16)ldexpf(f[7], -e)});
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  // the chunk's sum of x' (exact values, float32 adds)
   float sx = 0.0f;
-  sx = __builtin_amdgcn_fdot2(as_h2(v[0]), sixteenth, sx, false);
-  sx = __builtin_amdgcn_fdot2(as_h2(v[1]), one, sx, false);
-  sx = __builtin_amdgcn_fdot2(as_h2(v[2]), sixteenth, sx, false);
-  sx = __builtin_amdgcn_fdot2(as_h2(v[3]), one, sx, false);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sx += ldexpf(f[j], -e);
   sx += __builtin_amdgcn_update_dpp(0.0f, sx, 0xB1, 0xF, 0xF, false);
   sx += __builtin_amdgcn_update_dpp(0.0f, sx, 0x4E, 0xF, 0xF, false);
   if (valid) {
@@ -298,10 +298,10 @@ __device__ __forceinline__ void read_x_chunk(const u32x4* xs, const float2* xinf
 
 // The chunk's share of sum_k x_k (s q_k + b), in the chunk's own scale 2^(e+20).
 template <int BITS>
-__device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChunk& x) {
+__device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChunk& x, int act) {
   const float P = chunk_dot_sub<BITS>(r, x.xa, x.xb);
-  const float s = __uint_as_float(r.sb << 16);
-  const float b = __uint_as_float(r.sb & 0xFFFF0000u);
+  const float s = act_to_f32((uint16_t)(r.sb & 0xFFFFu), act);
+  const float b = act_to_f32((uint16_t)(r.sb >> 16), act);
   return fmaf(s, P, b * x.sx);
 }
 
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int i = 0; i < XI; ++i) stage_x_block(xraw[m][i], tid + NT * i, tid + NT * i < nblk, xs[m], xinfo[m]);
+    for (int i = 0; i < XI; ++i) stage_x_block(xraw[m][i], tid + NT * i, tid + NT * i < nblk, xs[m], xinfo[m], p.act);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -437,8 +437,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
           read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc), xc.e + 20);
-            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc), xc.e + 20);
+            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc, p.act), xc.e + 20);
+            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc, p.act), xc.e + 20);
           }
         }
       }
@@ -475,8 +475,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         if (FULL || sl + c * lpc < nchunk) {
-          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c]), xc[c].e + 20);
-          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c]), xc[c].e + 20);
+          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c], p.act), xc[c].e + 20);
+          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c], p.act), xc[c].e + 20);
         }
       }
     }
@@ -590,7 +590,6 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     }
   }
   const NibbleK nk = nibble_consts_in_regs();
-  const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
   // Codes, scales and biases are loaded in a line-friendly lane order and then
   // moved to the MFMA's order with ds_bpermute.  In the MFMA's order adjacent
@@ -652,10 +651,10 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       const uint16_t s_u = __builtin_amdgcn_raw_buffer_load_b16(mu.s, (r * mu.ng + gu) * 2, 0, 0);
       const uint16_t b_u = __builtin_amdgcn_raw_buffer_load_b16(mu.b, (r * mu.ng + gu) * 2, 0, 0);
       if (g < mg.ng)
-        kmax_g = fmaxf(kmax_g, group_term_max(bf16_to_f32(s_g), bf16_to_f32(b_g), CodeOffset<BITS_G>::z,
+        kmax_g = fmaxf(kmax_g, group_term_max(act_to_f32(s_g, p.act), act_to_f32(b_g, p.act), CodeOffset<BITS_G>::z,
                                               kPlaneMax<BITS_G>));
       if (g < mu.ng)
-        kmax_u = fmaxf(kmax_u, group_term_max(bf16_to_f32(s_u), bf16_to_f32(b_u), CodeOffset<BITS_U>::z,
+        kmax_u = fmaxf(kmax_u, group_term_max(act_to_f32(s_u, p.act), act_to_f32(b_u, p.act), CodeOffset<BITS_U>::z,
                                               kPlaneMax<BITS_U>));
     }
     kmax_g = fmaxf(kmax_g, __shfl_xor(kmax_g, 16));
@@ -767,29 +766,52 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
 
   // one matrix's 8-code block kb of a chunk, multiplied into every row tile:
   // one B operand (4-bit) or two (8-bit planes), built once
-  auto block_mfma = [&]<int BITS>(const u32x4* cw, float sf, int kb, const f16x8 (&a)[RT], f32x4 (&acc)[RT]) {
-    const _Float16 hs = (_Float16)sf;
-    const f16x2 s2 = {hs, hs};
-    if constexpr (kCodeWidth<BITS> == 4) {
-      uint32_t o[4];
-      dequant4(cw[0][kb], s2, o, nk);
-      const f16x8 b = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
+  // s2 = (s, s), or with binary16 scales (split) its two parts (hi, lo):
+  // then each part takes its own plane (split_scale)
+  auto block_mfma = [&]<int BITS>(const u32x4* cw, f16x2 s2, bool split, int kb, const f16x8 (&a)[RT],
+                                  f32x4 (&acc)[RT]) {
+    auto mfma_b = [&](const u32x4& v) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b, acc[t], 0, 0, 0);
+      for (int t = 0; t < RT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8, v), acc[t], 0, 0, 0);
+    };
+    if constexpr (kCodeWidth<BITS> == 4) {
+      if (split) {
+        const f16x2 shi = {s2[0], s2[0]}, slo = {s2[1], s2[1]};
+        uint32_t q[4];
+        codes4(cw[0][kb], q);
+        u32x4 vh, vl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vh[j] = as_u32(as_h2(q[j]) * shi);
+          vl[j] = as_u32(as_h2(q[j]) * slo);
+        }
+        mfma_b(vh);
+        mfma_b(vl);
+      } else {
+        uint32_t o[4];
+        dequant4(cw[0][kb], s2, o, nk);
+        mfma_b((u32x4){o[0], o[1], o[2], o[3]});
+      }
     } else {
-      uint32_t lo[4], hi[4];
-      codes8(cw[kb >> 1][2 * (kb & 1)], cw[kb >> 1][2 * (kb & 1) + 1], lo, hi, nk);
-      const f16x2 s16 = s2 * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
+      uint32_t lo[4], hi[4], full[4];
+      codes8(cw[kb >> 1][2 * (kb & 1)], cw[kb >> 1][2 * (kb & 1) + 1], lo, hi, nk, split ? full : nullptr);
+      const f16x2 sh = split ? (f16x2){s2[0], s2[0]} : s2;
+      const f16x2 s16 = sh * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
       u32x4 vl, vh;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        vl[j] = as_u32(as_h2(lo[j]) * s2);
+        vl[j] = as_u32(as_h2(lo[j]) * sh);
         vh[j] = as_u32(as_h2(hi[j]) * s16);
       }
+      mfma_b(vl);
+      mfma_b(vh);
+      if (split) {
+        const f16x2 slo = {s2[1], s2[1]};
+        u32x4 vf;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8, vl), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8, vh), acc[t], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) vf[j] = as_u32(as_h2(full[j]) * slo);
+        mfma_b(vf);
       }
     }
   };
@@ -823,17 +845,20 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     // a chunk past the end gets zero scales and biases: its B operands vanish
     // (scaled by the column's 2^-k)
     const int kg_ = k_gate(), ku_ = k_up();
-    const float sg = d.live ? ldexpf(bf16_to_f32((uint16_t)d.sg), -kg_) : 0.0f;
-    const float bg = d.live ? ldexpf(bf16_to_f32((uint16_t)d.bg), -kg_) : 0.0f;
-    const float su = d.live ? ldexpf(bf16_to_f32((uint16_t)d.su), -ku_) : 0.0f;
-    const float bu = d.live ? ldexpf(bf16_to_f32((uint16_t)d.bu), -ku_) : 0.0f;
+    const float sg = d.live ? ldexpf(act_to_f32((uint16_t)d.sg, p.act), -kg_) : 0.0f;
+    const float bg = d.live ? ldexpf(act_to_f32((uint16_t)d.bg, p.act), -kg_) : 0.0f;
+    const float su = d.live ? ldexpf(act_to_f32((uint16_t)d.su, p.act), -ku_) : 0.0f;
+    const float bu = d.live ? ldexpf(act_to_f32((uint16_t)d.bu, p.act), -ku_) : 0.0f;
+    const bool split = p.act == kActF16;
+    const f16x2 sg2 = split ? split_scale(sg) : (f16x2){(_Float16)sg, (_Float16)sg};
+    const f16x2 su2 = split ? split_scale(su) : (f16x2){(_Float16)su, (_Float16)su};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f16x8 a[RT];
 #pragma unroll
       for (int t = 0; t < RT; ++t) a[t] = __builtin_bit_cast(f16x8, d.x[t][kb]);
-      block_mfma.template operator()<BITS_G>(d.cg, sg, kb, a, ag);
-      block_mfma.template operator()<BITS_U>(d.cu, su, kb, a, au);
+      block_mfma.template operator()<BITS_G>(d.cg, sg2, split, kb, a, ag);
+      block_mfma.template operator()<BITS_U>(d.cu, su2, split, kb, a, au);
     }
     // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
     const _Float16 z0 = (_Float16)0.0f;
@@ -848,7 +873,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d.x[t][q][j]), one2, sx, false);
+        for (int j = 0; j < 4; ++j) sx = fma2(d.x[t][q][j], 0x3C003C00u, sx);   // x' times 1 (see fma2)
       const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
       const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
       ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[t], 0, 0, 0);
@@ -918,10 +943,11 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   };
   // ... the row exponents e (the lanes of a row meet with two swaps; the
   // accumulator rows' exponents packed as in the preload) ...  When every
-  // row's largest magnitude lies in [1, 2^16) (0 <= e <= 15) the wave takes
-  // e = 0 instead, x' = x: every bf16 value below 2^16 is at most 65280, so
-  // x fits binary16, and an element is exact in binary16 down to 2^-17, not
-  // 2^(e - 17): at least as exact as with the row's own power of two.
+  // row's largest magnitude lies in [1, 2^10) (0 <= e <= 9) the wave takes
+  // e = 0 instead, x' = x: x fits binary16, a chunk's sum of x' (carried as
+  // binary16 hi + lo) stays below 2^15, and an element is exact in binary16
+  // down to 2^-17 (binary16 x: 2^-14), not 2^(e - 17): at least as exact as
+  // with the row's own power of two.
   int xe_self[RT];
   bool xe_zero = false;
   auto x_rows = [&]() {
@@ -931,8 +957,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       uint32_t a = max(xam[t] & 0xFFFFu, xam[t] >> 16);
       a = max(a, (uint32_t)__shfl_xor((int)a, 16));
       a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-      xe_self[t] = row_exponent(a);
-      in_range = in_range && xe_self[t] >= 0 && xe_self[t] <= 15;
+      xe_self[t] = x_exponent(a, p.act);
+      in_range = in_range && xe_self[t] >= 0 && xe_self[t] <= 9;
     }
     xe_zero = __all(in_range);
 #pragma unroll
@@ -954,8 +980,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         float f[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          f[2 * j] = bf16_to_f32((uint16_t)(v[j] & 0xFFFFu));
-          f[2 * j + 1] = bf16_to_f32((uint16_t)(v[j] >> 16));
+          f[2 * j] = act_to_f32((uint16_t)(v[j] & 0xFFFFu), p.act);
+          f[2 * j + 1] = act_to_f32((uint16_t)(v[j] >> 16), p.act);
         }
         if (!xe_zero) {
 #pragma unroll
@@ -968,9 +994,9 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   float cmax_g = 0.0f, cmax_u = 0.0f;
   auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     if (!d.live) return;
-    cmax_g = fmaxf(cmax_g, group_term_max(bf16_to_f32((uint16_t)d.sg), bf16_to_f32((uint16_t)d.bg),
+    cmax_g = fmaxf(cmax_g, group_term_max(act_to_f32((uint16_t)d.sg, p.act), act_to_f32((uint16_t)d.bg, p.act),
                                           CodeOffset<BITS_G>::z, kPlaneMax<BITS_G>));
-    cmax_u = fmaxf(cmax_u, group_term_max(bf16_to_f32((uint16_t)d.su), bf16_to_f32((uint16_t)d.bu),
+    cmax_u = fmaxf(cmax_u, group_term_max(act_to_f32((uint16_t)d.su, p.act), act_to_f32((uint16_t)d.bu, p.act),
                                           CodeOffset<BITS_U>::z, kPlaneMax<BITS_U>));
   };
   auto chunk_k_wave = [&]() {
@@ -1009,7 +1035,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       atomicMax(&xmax[b / (p.H >> 3)], amax);
     }
     __syncthreads();
-    if (tid < p.M) xe[tid] = row_exponent(xmax[tid]);
+    if (tid < p.M) xe[tid] = x_exponent(xmax[tid], p.act);
     __syncthreads();
     for (int b = tid; b < nblk; b += nt) {              // x' = x 2^-e in the code-pair order
       const int m = b / (p.H >> 3), k8 = b - m * (p.H >> 3);
@@ -1018,8 +1044,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       float f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -e);
-        f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -e);
+        f[2 * j] = ldexpf(act_to_f32((uint16_t)(v[j] & 0xFFFFu), p.act), -e);
+        f[2 * j + 1] = ldexpf(act_to_f32((uint16_t)(v[j] >> 16), p.act), -e);
       }
       u32x4 o;
 #pragma unroll

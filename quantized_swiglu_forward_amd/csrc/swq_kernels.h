@@ -39,6 +39,8 @@ struct PrepParams {
   int xlane;           // 0: x' K-step major for the MFMA kernel (with the extra columns);
                        // 1 or 2: in the few-row kernel's lane order with that many 16-row tiles
                        // (see kSkinnyXUnit), no extra columns
+  int act;             // kActBf16 or kActF16: the type of x, the scales and the biases (binary16:
+                       // x' = x, e = 0; scale tiles hold (hi, lo) parts, split_scale)
 };
 
 // x' of the few-row kernel, in its MFMA lane order: for chunk quad Q (128
@@ -73,10 +75,11 @@ struct MfmaParams {
   float* dbg_u;
   const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
   int vec;             // 1: the output rows allow 16-byte (f32) / 8-byte (bf16) stores of 4 features
+  int act;             // kActBf16 or kActF16 (output type of modes 0 and 2, MATCH rounding)
 };
 
 struct GemvParams {
-  const uint16_t* x;   // bf16 [M, H]
+  const uint16_t* x;   // bf16 (or binary16, act) [M, H]
   const uint32_t* wg;
   const uint16_t* sg;
   const uint16_t* bg;
@@ -95,11 +98,13 @@ struct GemvParams {
   const _Float16* xa;  // x' staged by the prep kernel in the few-row kernel's lane order, or null
   const int* xexp;     // and its row exponents
   const int* kexp;     // with xa: [2][I] weight-row exponents k from the prep kernel's column blocks
+  int act;             // kActBf16 or kActF16: the type of x, the scales and biases, and the output
 };
 
 // Scale tiles: for every 128 output columns and every 128 inputs (a
 // super-step of four K-steps of 32), the scale of each column's group in
-// each K-step and matrix as a binary16 pair (s, s), ordered
+// each K-step and matrix as a binary16 pair (s, s) -- binary16 scales: its
+// two parts (hi, lo), see split_scale -- ordered
 // [K-step q][matrix][column]: 4 * 2 * 128 words, one contiguous 4 KB block.
 constexpr int kScaleTileCols = 128;
 constexpr int kScaleTileWords = 4 * 2 * kScaleTileCols;

@@ -91,11 +91,7 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
   __syncthreads();
   amax = max(max(red[0], red[1]), max(red[2], red[3]));
   // exponent of the row maximum: max|x| in [2^e, 2^(e+1))
-  int e = 0;
-  if (amax != 0) {
-    const int field = (int)(amax >> 7);
-    e = (field == 0) ? -127 : field - 127;
-  }
+  const int e = x_exponent(amax, p.act);
   if (tid == 0) p.xexp[m] = e;
 
   // 2. scaled binary16 copy in pair order, and per-group sums
@@ -116,8 +112,8 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
       float f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[2 * j] = ldexpf(bf16_to_f32((uint16_t)(v[j] & 0xFFFFu)), -e);
-        f[2 * j + 1] = ldexpf(bf16_to_f32((uint16_t)(v[j] >> 16)), -e);
+        f[2 * j] = ldexpf(act_to_f32((uint16_t)(v[j] & 0xFFFFu), p.act), -e);
+        f[2 * j + 1] = ldexpf(act_to_f32((uint16_t)(v[j] >> 16), p.act), -e);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) part += f[j];
@@ -163,7 +159,8 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
 //    stores (a row is kext*2 bytes, a multiple of 64, so each store lies
 //    wholly inside or outside it);
 //  - for every K-step (32 inputs) of its groups below H, the scale-tile word
-//    (s 2^-k, s 2^-k) in binary16 of that K-step's group;
+//    (s 2^-k, s 2^-k) in binary16 of that K-step's group (binary16 scales:
+//    split_scale(s 2^-k), the two parts of two MFMA planes);
 //  - (slot 0) k itself, for the MFMA kernel's epilogue.
 // With k_only (the matrix-vector path) only k is written.  The MFMA kernel
 // never reads scale-tile words of K-steps past H or of columns past the rows,
@@ -174,6 +171,7 @@ struct RowSpec {
   int lg_gs;      // log2 of the group size
   int ng;         // groups per row
   float z, F;     // code offset; largest |offset| times plane weight
+  int act;        // type of the scales and biases (kActBf16, kActF16)
 };
 
 __device__ __forceinline__ RowSpec row_spec(const PrepParams& p, int mat) {
@@ -185,6 +183,7 @@ __device__ __forceinline__ RowSpec row_spec(const PrepParams& p, int mat) {
   r.ng = p.H >> r.lg_gs;
   r.z = bits == 8 ? 136.0f : 8.0f;
   r.F = bits == 8 ? 128.0f : 8.0f;
+  r.act = p.act;
   return r;
 }
 
@@ -206,7 +205,8 @@ __device__ __forceinline__ float slot_max(const RowSpec& r, int ngroups, int slo
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (8 * slot + j < ngroups) m = fmaxf(m, group_term_max(bf16_to_f32(sv[j]), bf16_to_f32(bv[j]), r.z, r.F));
+    if (8 * slot + j < ngroups)
+      m = fmaxf(m, group_term_max(act_to_f32(sv[j], r.act), act_to_f32(bv[j], r.act), r.z, r.F));
   return m;
 }
 
@@ -219,7 +219,7 @@ __device__ __forceinline__ void store_slot(const PrepParams& p, const RowSpec& r
   for (int j = 0; j < 8; ++j) {
     _Float16 chi = (_Float16)0.0f, clo = (_Float16)0.0f;
     if (8 * slot + j < ngroups) {
-      const float cv = ldexpf(fmaf(r.z, bf16_to_f32(sv[j]), bf16_to_f32(bv[j])), -k);
+      const float cv = ldexpf(fmaf(r.z, act_to_f32(sv[j], r.act), act_to_f32(bv[j], r.act)), -k);
       chi = (_Float16)cv;
       clo = (_Float16)(cv - (float)chi);
     }
@@ -238,8 +238,9 @@ __device__ __forceinline__ void store_slot(const PrepParams& p, const RowSpec& r
   uint32_t* tile = p.scl + (n >> 7) * (int64_t)p.nss * kScaleTileWords + mat * kScaleTileCols + (n & 127);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const _Float16 hs = (_Float16)ldexpf(bf16_to_f32(sv[j]), -k);
-    const uint32_t word = as_u32((f16x2){hs, hs});
+    const float sk = ldexpf(act_to_f32(sv[j], r.act), -k);
+    const _Float16 hs = (_Float16)sk;
+    const uint32_t word = r.act == kActF16 ? as_u32(split_scale(sk)) : as_u32((f16x2){hs, hs});
     const int t0 = (8 * slot + j) * per;
     for (int u = 0; u < per; ++u) {
       const int t = t0 + u;
@@ -349,28 +350,60 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // Dequantized B operands of one k16 sub-step (one 8-code block per lane) of one matrix.
-template <int BITS>
-__device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1, const NibbleK& k) {
+template <int BITS, bool A16>
+__device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8& b0, f16x8& b1, f16x8& b2,
+                                              const NibbleK& k) {
   if (kCodeWidth<BITS> == 4) {
-    uint32_t o[4];
-    dequant4(w[0], s2, o, k);
-    b0 = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
+    if constexpr (A16) {   // s2 = (hi, lo): planes hi (q - 8) and lo (q - 8)
+      const f16x2 shi = {s2[0], s2[0]}, slo = {s2[1], s2[1]};
+      const f16x2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+      const f16x2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+      const uint32_t w8 = w[0] >> 8;
+      const f16x2 q[4] = {as_h2((w[0] & k.m_lo) | k.g_lo) - c1032, as_h2((w[0] & k.m_hi) | k.g_hi) - c72,
+                          as_h2((w8 & k.m_lo) | k.g_lo) - c1032, as_h2((w8 & k.m_hi) | k.g_hi) - c72};
+      u32x4 vh, vl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vh[j] = as_u32(q[j] * shi);
+        vl[j] = as_u32(q[j] * slo);
+      }
+      b0 = __builtin_bit_cast(f16x8, vh);
+      b1 = __builtin_bit_cast(f16x8, vl);
+    } else {
+      uint32_t o[4];
+      dequant4(w[0], s2, o, k);
+      b0 = __builtin_bit_cast(f16x8, (u32x4){o[0], o[1], o[2], o[3]});
+    }
   } else {
-    uint32_t lo[4], hi[4];
-    codes8(w[0], w[1], lo, hi, k);
-    const f16x2 s16 = s2 * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
+    // planes s (lo - 8) and 16 s (hi - 8); A16: with s = hi part, and a third
+    // plane lo part times the whole code q - 136
+    uint32_t lo[4], hi[4], full[4];
+    codes8(w[0], w[1], lo, hi, k, A16 ? full : nullptr);
+    const f16x2 sh = A16 ? (f16x2){s2[0], s2[0]} : s2;
+    const f16x2 s16 = sh * (f16x2){(_Float16)16.0f, (_Float16)16.0f};
     u32x4 vl, vh;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vl[j] = as_u32(as_h2(lo[j]) * s2);
+      vl[j] = as_u32(as_h2(lo[j]) * sh);
       vh[j] = as_u32(as_h2(hi[j]) * s16);
     }
     b0 = __builtin_bit_cast(f16x8, vl);
     b1 = __builtin_bit_cast(f16x8, vh);
+    if constexpr (A16) {
+      const f16x2 slo = {s2[1], s2[1]};
+      u32x4 vf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vf[j] = as_u32(as_h2(full[j]) * slo);
+      b2 = __builtin_bit_cast(f16x8, vf);
+    }
   }
 }
 
-template <int BITS_G, int BITS_U, int BM, int WN, int OCC>
+// MFMA planes per matrix: 8-bit codes two (nibbles), binary16 scales one more.
+template <int BITS, bool A16>
+inline constexpr int kPlanes = (kCodeWidth<BITS> == 8 ? 2 : 1) + (A16 ? 1 : 0);
+
+template <int BITS_G, int BITS_U, int BM, int WN, int OCC, bool A16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void swq_mfma_kernel(MfmaParams p) {
   constexpr int NT = 256;
   constexpr int STAGES = 4;                            // x' / extra-column ring: K-steps in flight
@@ -535,8 +568,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
   // operand registers of the two sub-steps of a K-step
   f16x8 a0[MF], a1[MF];
-  f16x8 g0a[NF], g0b[NF], u0a[NF], u0b[NF];     // sub-step 0: gate planes, up planes
-  f16x8 g1a[NF], g1b[NF], u1a[NF], u1b[NF];     // sub-step 1
+  f16x8 g0a[NF], g0b[NF], g0c[NF], u0a[NF], u0b[NF], u0c[NF];   // sub-step 0: gate planes, up planes
+  f16x8 g1a[NF], g1b[NF], g1c[NF], u1a[NF], u1b[NF], u1c[NF];   // sub-step 1
+  constexpr int PL_G = kPlanes<BITS_G, A16>, PL_U = kPlanes<BITS_U, A16>;
   // this lane's codes and scales of two consecutive code K-steps: step t
   // uses set P and loads step t+1 into set P^1 (in the unrolled main loop P
   // alternates; elsewhere P = 0 and set 1 is copied back after the step)
@@ -601,11 +635,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // B operands of sub-step ks from codes and scales in registers
   auto dequant = [&](int ks, const uint32_t (&cg)[NF][WG / 2], const uint32_t (&cu)[NF][WU / 2],
                      const f16x2 (&s_g)[NF], const f16x2 (&s_u)[NF], f16x8 (&ga)[NF], f16x8 (&gb)[NF],
-                     f16x8 (&ua)[NF], f16x8 (&ub)[NF]) {
+                     f16x8 (&gc)[NF], f16x8 (&ua)[NF], f16x8 (&ub)[NF], f16x8 (&uc)[NF]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      dequant_block<BITS_G>(&cg[f][ks * (WG / 4)], s_g[f], ga[f], gb[f], nk);
-      dequant_block<BITS_U>(&cu[f][ks * (WU / 4)], s_u[f], ua[f], ub[f], nk);
+      dequant_block<BITS_G, A16>(&cg[f][ks * (WG / 4)], s_g[f], ga[f], gb[f], gc[f], nk);
+      dequant_block<BITS_U, A16>(&cu[f][ks * (WU / 4)], s_u[f], ua[f], ub[f], uc[f], nk);
     }
   };
   // B operands of sub-step ks of an extra-column step from stage `slot` (one
@@ -620,7 +654,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   };
   // kind 0: code step (both matrices); 1: extra columns of the gate; 2: of the up matrix
   auto mfma = [&](int kind, const f16x8 (&a)[MF], const f16x8 (&ga)[NF], const f16x8 (&gb)[NF],
-                  const f16x8 (&ua)[NF], const f16x8 (&ub)[NF]) {
+                  const f16x8 (&gc)[NF], const f16x8 (&ua)[NF], const f16x8 (&ub)[NF], const f16x8 (&uc)[NF]) {
     if (kind == 0) {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
@@ -628,8 +662,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         for (int i = 0; i < MF; ++i) {
           acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ga[f], a[i], acc_g[i][f], 0, 0, 0);
           acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ua[f], a[i], acc_u[i][f], 0, 0, 0);
-          if (BITS_G == 8) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gb[f], a[i], acc_g[i][f], 0, 0, 0);
-          if (BITS_U == 8) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ub[f], a[i], acc_u[i][f], 0, 0, 0);
+          if (PL_G >= 2) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gb[f], a[i], acc_g[i][f], 0, 0, 0);
+          if (PL_U >= 2) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ub[f], a[i], acc_u[i][f], 0, 0, 0);
+          if (PL_G >= 3) acc_g[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gc[f], a[i], acc_g[i][f], 0, 0, 0);
+          if (PL_U >= 3) acc_u[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(uc[f], a[i], acc_u[i][f], 0, 0, 0);
         }
     } else if (kind == 1) {
 #pragma unroll
@@ -650,8 +686,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // reads and the dequantization that prepare the next sub-step, so that the
   // matrix pipe stays fed while the vector ALU works (the reads go with the
   // first MFMAs, their results are needed by the dequantization).
-  constexpr int MF_MAIN = MF * NF * ((kCodeWidth<BITS_G> / 4) + (kCodeWidth<BITS_U> / 4));   // MFMAs of a code sub-step
-  constexpr int DQ_VALU = NF * (BITS_G == 8 ? 40 : 20) + NF * (BITS_U == 8 ? 40 : 20);
+  constexpr int MF_MAIN = MF * NF * (PL_G + PL_U);   // MFMAs of a code sub-step
+  constexpr int DQ_VALU = NF * (BITS_G == 8 ? 40 : 20) * (A16 ? 3 : 2) / 2 + NF * (BITS_U == 8 ? 40 : 20) * (A16 ? 3 : 2) / 2;
   auto interleave = [&]<int NMFMA, int NDS, int NVALU>() {
     constexpr int LEAD = NMFMA < 8 ? NMFMA / 2 : 4;
     constexpr int DS_PER = (NDS + LEAD - 1) / LEAD;
@@ -693,11 +729,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     // codes and scales of the next super-step, apart from the x' loads that follow the barrier
     if (ph == 1) issue_ss(t / SS + 1);
     read_a(ph, 1, a1);
-    if constexpr (KIND == 0) dequant(1, cw_g[P], cw_u[P], s_g2[P], s_u2[P], g1a, g1b, u1a, u1b);
+    if constexpr (KIND == 0) dequant(1, cw_g[P], cw_u[P], s_g2[P], s_u2[P], g1a, g1b, g1c, u1a, u1b, u1c);
     else read_ext(ph, 1, g1a);
     // the next code step's codes: its super-step landed before the previous barrier
     if constexpr (!NXT_EXT) load_codes(t + 1, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1]);
-    mfma(KIND, a0, g0a, g0b, u0a, u0b);
+    mfma(KIND, a0, g0a, g0b, g0c, u0a, u0b, u0c);
     if (D == 0) interleave.template operator()<MF_MAIN, MF + 4 * NF, DQ_VALU + 4 * NF>();
     // stage t+1 and its super-step complete for every wave, and every wave is done with stage t-1
     // (scheduling fences keep the first half's MFMAs ahead of the wait)
@@ -707,9 +743,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     block_barrier();
     issue(is, t + STAGES - 1, IS_EXT);
     read_a(nx, 0, a0);
-    if constexpr (!NXT_EXT) dequant(0, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1], g0a, g0b, u0a, u0b);
+    if constexpr (!NXT_EXT) dequant(0, cw_g[P ^ 1], cw_u[P ^ 1], s_g2[P ^ 1], s_u2[P ^ 1], g0a, g0b, g0c, u0a, u0b, u0c);
     else read_ext(nx, 0, g0a);
-    mfma(KIND, a1, g1a, g1b, u1a, u1b);
+    mfma(KIND, a1, g1a, g1b, g1c, u1a, u1b, u1c);
     if (D == 0) interleave.template operator()<MF_MAIN, MF, DQ_VALU>();
     __builtin_amdgcn_sched_barrier(0);   // each step is its own scheduling region
     if constexpr (COPY && !NXT_EXT) {
@@ -742,7 +778,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   read_a(0, 0, a0);
   if (0 < s_main) {
     load_codes(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0]);
-    dequant(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0], g0a, g0b, u0a, u0b);
+    dequant(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0], g0a, g0b, g0c, u0a, u0b, u0c);
   } else {
     read_ext(0, 0, g0a);
   }
@@ -775,14 +811,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   // with one vector store when the output allows it (p.vec).
   // four consecutive outputs at element offset o of a float32 or bf16 array,
   // columns c0 .. c0 + 3 stored while below lim
+  constexpr int ACT = A16 ? kActF16 : kActBf16;   // 16-bit output type
   auto put4 = [&](auto* base, int64_t o, int c0, int lim, const float (&v)[4]) {
     constexpr bool F32 = std::is_same_v<std::remove_pointer_t<decltype(base)>, float>;
     if (p.vec && c0 + 4 <= lim) {
       if constexpr (F32) {
         *reinterpret_cast<f32x4*>(base + o) = (f32x4){v[0], v[1], v[2], v[3]};
       } else {
-        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        const uint32_t lo = (uint32_t)f32_to_act(v[0], ACT) | ((uint32_t)f32_to_act(v[1], ACT) << 16);
+        const uint32_t hi = (uint32_t)f32_to_act(v[2], ACT) | ((uint32_t)f32_to_act(v[3], ACT) << 16);
         *reinterpret_cast<u32x2*>(base + o) = (u32x2){lo, hi};
       }
     } else {
@@ -790,7 +827,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       for (int c = 0; c < 4; ++c) {
         if (c0 + c >= lim) continue;
         if constexpr (F32) base[o + c] = v[c];
-        else base[o + c] = f32_to_bf16(v[c]);
+        else base[o + c] = f32_to_act(v[c], ACT);
       }
     }
   };
@@ -814,7 +851,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
           for (int c = 0; c < 4; ++c) {
             g[c] = ldexpf(acc_g[i][f][4 * j + c], e + rk[0][cl + c]);
             u[c] = ldexpf(acc_u[i][f][4 * j + c], e + rk[1][cl + c]);
-            if constexpr (MODE < 3) h[c] = swiglu_epilogue(g[c], u[c], MODE);
+            if constexpr (MODE < 3) h[c] = swiglu_epilogue(g[c], u[c], MODE, ACT);
           }
           if (!row_ok) continue;
           const int64_t o = orow + c0;
@@ -864,16 +901,18 @@ hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BG, int BU, int BM, int WN, int OCC>
+template <int BG, int BU, int BM, int WN, int OCC, bool A16 = false>
 static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.n_end - p.n_begin + 4 * WN - 1) / (4 * WN));
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC>), dim3(tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC, A16>), dim3(tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU>
 static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
+  // binary16 activations: 128 x 128 tiles (their extra MFMA planes take the registers)
+  if (p.act == kActF16) return launch_mfma_t<BG, BU, 128, 32, 1, true>(p, stream);
   // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
   if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
   if constexpr (!(BG == 8 && BU == 8)) {

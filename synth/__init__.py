@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "Config", "CONFIGS", "Problem", "make_problem", "make_custom",
-    "to_bf16_bits", "bf16_bits_to_f32", "pack_codes", "decode_xs",
+    "to_bf16_bits", "bf16_bits_to_f32", "to_f16_bits", "f16_bits_to_f32", "pack_codes", "decode_xs",
 ]
 
 
@@ -35,6 +35,16 @@ def to_bf16_bits(a) -> np.ndarray:
     """float32 array -> bf16 bit patterns (uint16), torch's RNE CPU cast."""
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_f16_bits(a) -> np.ndarray:
+    """float32 array -> IEEE binary16 bit patterns (uint16), numpy's RNE cast."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
+
+
+def f16_bits_to_f32(b) -> np.ndarray:
+    """binary16 bit patterns -> float32 (exact widening)."""
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:
@@ -115,21 +125,26 @@ class Problem:
     codes_u: np.ndarray | None = None
     xs: np.ndarray | None = None         # uint16 [calls, H] fresh decode inputs
     extra: dict = field(default_factory=dict)
+    act: str = "bf16"                    # type of x, scales and biases: "bf16" or "f16" (binary16)
 
     def args(self):
         """Positional tuple in the order of the forward entry point."""
         return (self.x, self.wg, self.sg, self.bg, self.wu, self.su, self.bu)
 
 
-def _draw_matrix(rng, I, H, bits, gs, s_lo, s_hi, bias_mode):
+_TO16 = {"bf16": (to_bf16_bits, bf16_bits_to_f32), "f16": (to_f16_bits, f16_bits_to_f32)}
+
+
+def _draw_matrix(rng, I, H, bits, gs, s_lo, s_hi, bias_mode, act="bf16"):
+    to16, from16 = _TO16[act]
     codes = rng.integers(0, 1 << bits, size=(I, H), dtype=np.uint8)
-    s_bits = to_bf16_bits(rng.uniform(s_lo, s_hi, size=(I, H // gs)).astype(np.float32))
-    s = bf16_bits_to_f32(s_bits)
+    s_bits = to16(rng.uniform(s_lo, s_hi, size=(I, H // gs)).astype(np.float32))
+    s = from16(s_bits)
     if bias_mode == "factor":
         f = rng.uniform(0.9, 1.1, size=(I, H // gs)).astype(np.float32)
-        b_bits = to_bf16_bits((np.float32(-8.0) * s * f).astype(np.float32))
+        b_bits = to16((np.float32(-8.0) * s * f).astype(np.float32))
     elif bias_mode == "half":
-        b_bits = to_bf16_bits((np.float32(-(1 << (bits - 1))) * s).astype(np.float32))
+        b_bits = to16((np.float32(-(1 << (bits - 1))) * s).astype(np.float32))
     else:
         raise ValueError(bias_mode)
     return codes, pack_codes(codes, bits), s_bits, b_bits
@@ -137,24 +152,24 @@ def _draw_matrix(rng, I, H, bits, gs, s_lo, s_hi, bias_mode):
 
 def make_custom(M, H, I, bits_g=4, gs_g=64, bits_u=None, gs_u=None, seed=0,
                 x_sigma=1.0, s_lo=0.005, s_hi=0.02, bias_mode="factor",
-                calls=0, keep_codes=False) -> Problem:
+                calls=0, keep_codes=False, act="bf16") -> Problem:
     """Draw one problem. Order of draws: x, gate codes, gate scales, gate bias
     factors, up codes, up scales, up bias factors, then (if ``calls``) the
-    ``[calls, H]`` fresh decode inputs."""
+    ``[calls, H]`` fresh decode inputs.  ``act`` = "f16" rounds x, the scales
+    and the biases to binary16 instead of bf16 (the same draws)."""
     bits_u = bits_g if bits_u is None else bits_u
     gs_u = gs_g if gs_u is None else gs_u
+    to16 = _TO16[act][0]
     rng = np.random.default_rng(seed)
-    x = to_bf16_bits((rng.standard_normal((M, H), dtype=np.float32)
-                      * np.float32(x_sigma)).astype(np.float32))
-    cg, wg, sg, bg = _draw_matrix(rng, I, H, bits_g, gs_g, s_lo, s_hi, bias_mode)
-    cu, wu, su, bu = _draw_matrix(rng, I, H, bits_u, gs_u, s_lo, s_hi, bias_mode)
+    x = to16((rng.standard_normal((M, H), dtype=np.float32) * np.float32(x_sigma)).astype(np.float32))
+    cg, wg, sg, bg = _draw_matrix(rng, I, H, bits_g, gs_g, s_lo, s_hi, bias_mode, act)
+    cu, wu, su, bu = _draw_matrix(rng, I, H, bits_u, gs_u, s_lo, s_hi, bias_mode, act)
     xs = None
     if calls:
-        xs = to_bf16_bits((rng.standard_normal((calls, H), dtype=np.float32)
-                           * np.float32(x_sigma)).astype(np.float32))
+        xs = to16((rng.standard_normal((calls, H), dtype=np.float32) * np.float32(x_sigma)).astype(np.float32))
     return Problem(M, H, I, bits_g, gs_g, bits_u, gs_u, x, wg, sg, bg, wu, su, bu,
                    codes_g=cg if keep_codes else None,
-                   codes_u=cu if keep_codes else None, xs=xs)
+                   codes_u=cu if keep_codes else None, xs=xs, act=act)
 
 
 def make_down(Ho, I, bits=4, gs=64, seed=0, s_lo=0.005, s_hi=0.02, bias_mode="factor"):

@@ -702,3 +702,43 @@ def test_call_cap_counts_launched_calls():
     finally:
         swq.swiglu_q_set_max_calls(-1)
     assert swq.swiglu_q_under_cap() == 1
+
+
+# Sums of many same-sign products: activations all positive (as after a SiLU
+# or ReLU) or all negative, bf16 and binary16, on every path, in the wide
+# mode whose bar is the tightest.  (A dot-product instruction whose sums are
+# not rounded to nearest shows here as a one-sided error.)
+SIGN_SHAPES = [(1, 2048, 300, (4, 64, 4, 64)), (1, 1024, 130, (8, 32, 4, 64)), (3, 2048, 129, (4, 64, 8, 32)),
+               (8, 2048, 200, (4, 64, 4, 64)), (20, 1024, 77, (4, 64, 4, 64)), (70, 512, 130, (8, 32, 4, 64))]
+
+
+@pytest.mark.parametrize("sign", ["positive", "negative"])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("M,H,I,spec", SIGN_SHAPES, ids=[f"M{m}-H{h}-I{i}" for m, h, i, _ in SIGN_SHAPES])
+def test_same_sign_activations(M, H, I, spec, act, sign):
+    p = make_custom(M, H, I, *spec, seed=M + H + I, act=act)
+    mag = p.x & np.uint16(0x7FFF)
+    p.x = mag | np.uint16(0x8000) if sign == "negative" else mag
+    say("same-sign x", sign, act, M, H, I, spec)
+    y = device_forward(p, 1)
+    check(y, oracle_full(p, 1), 1, f"same-sign {sign} {act} M{M} H{H}")
+
+
+# The few-row kernel takes x' = x when every row's largest magnitude lies in
+# [1, 2^10), else scales by each row's power of two: all-positive rows just
+# inside (2^9, 2^10) and well outside (2^14) that range, where a chunk's sum
+# of 32 such values would not fit binary16 unscaled.
+@pytest.mark.parametrize("top", [2.0 ** 9, 2.0 ** 10, 2.0 ** 14])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_few_row_unscaled_range_edges(top, act):
+    from synth import f16_bits_to_f32, to_f16_bits
+    M, H, I = 8, 2048, 96
+    p = make_custom(M, H, I, 4, 64, 4, 64, seed=int(np.log2(top)), act=act)
+    rng = np.random.default_rng(int(top))
+    x = (rng.uniform(0.5, 1.0, (M, H)) * top * (1 - 2.0 ** -9)).astype(np.float32)
+    p.x = to_f16_bits(x) if act == "f16" else to_bf16_bits(x)
+    assert swq.swiglu_q_staging_bytes(M, H, I, 4, 64, 4, 64) == 0
+    for mode in ((0, 1) if act == "bf16" else (1,)):   # (gate sums of 10^5 overflow a binary16 output)
+        say("unscaled range edge", top, act, "mode", mode)
+        y = device_forward(p, mode, GEMV)
+        check(y, oracle_full(p, mode), mode, f"range edge {top} {act} mode {mode}")

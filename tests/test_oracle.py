@@ -541,3 +541,31 @@ def test_configs_shapes():
     assert s.min() >= 0.0049 and s.max() <= 0.0201
     ratio = bf16_bits_to_f32(p.bg) / s
     assert ratio.min() >= -8.8 - 0.1 and ratio.max() <= -7.2 + 0.1
+
+
+@pytest.mark.parametrize("act,mode", [("bf16", 0), ("bf16", 1), ("bf16", 2), ("f16", 0), ("f16", 1), ("f16", 2)])
+def test_metric_allows_the_output_subnormal_rounding_only(act, mode):
+    """An output below its type's normal range (silu of a far negative gate)
+    is stored as its nearest value of that type; the bar allows that one
+    rounding and rejects a quantum more."""
+    p = make_custom(1, 256, 64, 4, 64, seed=8, act=act)
+    o = oracle.swiglu_full(p, mode)
+    o = {k: (v.reshape(-1).copy() if k != "act" else v) for k, v in o.items()}
+    q = compare.output_quantum(mode, 1 if act == "f16" else 0)
+    # gate far negative: silu(g) u lies between 1 and 2 quanta of the output type
+    # (steps of g and u exact in either 16-bit type, so MATCH's rounding keeps them)
+    u = -2.125
+    g = -16.0
+    while abs(g / (1 + np.exp(-g)) * u) > 1.5 * q:
+        g -= 1.0 / 64 if act == "f16" else 0.5
+    # every element so (a row of one-signed x can do this), else the
+    # output's rms would set the floor
+    o["g"][:], o["u"][:], o["nu_g"][:], o["nu_u"][:] = g, u, 1e-3, 1e-3
+    o["g"][1::2] -= 1.0 / 64 if act == "f16" else 0.5
+    r = compare.reference_values(o, mode)[0]
+    y = r.copy()
+    y[0] = np.round(r[0] / q) * q                   # nearest value of the output type
+    assert abs(y[0] - r[0]) > compare.evaluate(r, o, mode)["tol"] * abs(r[0])
+    assert compare.evaluate(y, o, mode)["ok"]
+    y[0] += q if y[0] >= r[0] else -q               # one quantum further: rejected
+    assert not compare.evaluate(y, o, mode)["ok"]
