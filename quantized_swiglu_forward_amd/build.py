@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu_q.so")
-SOURCES = ["swq_api.hip", "swq_prefill.hip", "swq_gemv.hip"]
+SOURCES = ["swq_api.hip", "swq_prefill.hip", "swq_gemv.hip", "swq_gemv_f16.hip"]
 # measurement yardsticks for the benchmark only (a library of their own)
 PROBE_LIB = os.path.join(PKG, "libswq_probe.so")
 PROBE_SOURCES = ["swq_probe.hip"]

@@ -13,20 +13,31 @@
 //  * swq_gemv1_kernel: M = 1 with at most four chunks per lane (H <= 8192),
 //    and 2 <= M <= 4 with a whole wave per column and at most two chunks
 //    per lane (2048 <= H <= 4096), each weight chunk loaded once for all
-//    rows.  Codes enter v_dot2_f32_f16 as exact binary16 subnormals with no
-//    offset, each chunk of x scaled by its own power of two; the block
-//    shares x through LDS (described above the kernel).
-//  * swq_skinny_kernel: 1 <= M <= 32 otherwise.  x' comes from the prep
-//    kernel, or for M*H <= 8192 every block builds it in LDS itself; codes
-//    become exact binary16 s (q - z) and 16 x 16 x 32 MFMAs multiply them
-//    with one or two tiles of 16 rows at once (described above the kernel).
+//    rows.  Codes enter mixed-precision FMAs as exact binary16 subnormals
+//    with no offset, each chunk of x scaled by its own power of two; the
+//    block shares x through LDS (described above the kernel).
+//  * swq_skinny_kernel: 1 <= M <= 32 otherwise.  x' is converted by the
+//    waves themselves (M <= 16), built in LDS by every block, or staged by
+//    the prep kernel; codes become exact binary16 s (q - z) and
+//    16 x 16 x 32 MFMAs multiply them with one or two tiles of 16 rows at
+//    once (described above the kernel).
 // 2-bit codes are spread to nibbles as they are loaded and take the 4-bit
-// arithmetic.
+// arithmetic.  The activation type (bf16 or binary16) is a template
+// parameter of both kernels.
+//
+// This file is compiled twice: on its own (SWQ_GEMV_ACT unset) for the bf16
+// instances, the shared host functions and the dispatcher, and through
+// swq_gemv_f16.hip for the binary16 instances only, so that the two halves
+// build in parallel.
 #include <cstring>
 #include <type_traits>
 
 #include "swq_device.h"
 #include "swq_kernels.h"
+
+#ifndef SWQ_GEMV_ACT
+#define SWQ_GEMV_ACT 0
+#endif
 
 namespace swq {
 
@@ -74,7 +85,8 @@ __device__ __forceinline__ void load_chunk_buf(RawChunk<BITS>& r, const MatBufs&
 }
 
 
-__device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, float g, float u) {
+// (act: the activation type, a constant in every caller)
+__device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, float g, float u, int act) {
   const int64_t o = (int64_t)m * p.ldo + n;
   if (p.dbg_g) {
     p.dbg_g[o] = g;
@@ -92,9 +104,9 @@ __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, flo
       if (n < p.I_u) reinterpret_cast<uint16_t*>(p.out)[o + p.I] = f32_to_bf16(u);
     }
   } else {
-    const float h = swiglu_epilogue(g, u, p.mode, p.act);
+    const float h = swiglu_epilogue(g, u, p.mode, act);
     if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
-    else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(h, p.act);
+    else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(h, act);
   }
 }
 
@@ -316,7 +328,7 @@ __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChun
 // MR > 1 serves MR = M rows (R <= 2): every row's x is staged and dotted
 // with the same weight chunks, which are loaded once; the reduction and
 // epilogue run per row.
-template <int BITS_G, int BITS_U, int CPL, int R, bool FULL, int WPB, int MR>
+template <int BITS_G, int BITS_U, int CPL, int R, bool FULL, int WPB, int MR, int ACT>
 __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int lg) {
   static_assert(MR >= 1 && MR <= 4 && (MR == 1 || R <= 2), "several rows: at most two columns per wave");
   constexpr int NT = 64 * WPB;
@@ -374,7 +386,7 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int i = 0; i < XI; ++i) stage_x_block(xraw[m][i], tid + NT * i, tid + NT * i < nblk, xs[m], xinfo[m], p.act);
+    for (int i = 0; i < XI; ++i) stage_x_block(xraw[m][i], tid + NT * i, tid + NT * i < nblk, xs[m], xinfo[m], ACT);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
       const float u = upper_half(g);
       const int col = lane >> 4;
       const int64_t n = (int64_t)wave_global * R + col;
-      if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, m, (int)n, g, u);
+      if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, m, (int)n, g, u, ACT);
     } else if (FULL || lpc == 64) {
       float g = 0.0f, u = 0.0f;
 #pragma unroll
@@ -404,13 +416,13 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
         }
       }
       const int n = wave_global * R + lane;
-      if (lane < R && n < p.I) store_out(p, m, n, g, u);
+      if (lane < R && n < p.I) store_out(p, m, n, g, u, ACT);
     } else if constexpr (!FULL) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
         const int n = (wave_global * R + r) * cpw + sub;
-        if (sl == 0 && n < p.I) store_out(p, m, n, g, u);
+        if (sl == 0 && n < p.I) store_out(p, m, n, g, u, ACT);
       }
     }
   };
@@ -437,8 +449,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
           read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc, p.act), xc.e + 20);
-            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc, p.act), xc.e + 20);
+            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc, ACT), xc.e + 20);
+            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc, ACT), xc.e + 20);
           }
         }
       }
@@ -462,7 +474,7 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
         g = gm[m];
         u = um[m];
       }
-    if (mrow < MR && col < R && n < p.I) store_out(p, mrow, (int)n, g, u);
+    if (mrow < MR && col < R && n < p.I) store_out(p, mrow, (int)n, g, u, ACT);
   } else {
     XChunk xc[CPL];
 #pragma unroll
@@ -475,8 +487,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         if (FULL || sl + c * lpc < nchunk) {
-          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c], p.act), xc[c].e + 20);
-          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c], p.act), xc[c].e + 20);
+          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c], ACT), xc[c].e + 20);
+          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c], ACT), xc[c].e + 20);
         }
       }
     }
@@ -538,7 +550,7 @@ struct SbWindow {
 // and accumulators need twice the registers: half the waves per SIMD).  Q2:
 // two chunk quads in flight per wave (codes of at most 4 bits, x' from the
 // prep kernel), with half the waves per SIMD.
-template <int BITS_G, int BITS_U, int XS, int RT, bool Q2>
+template <int BITS_G, int BITS_U, int XS, int RT, bool Q2, int ACT>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
 __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
   constexpr bool STAGE = XS == kXStage, SELF = XS == kXSelf;
@@ -651,10 +663,10 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       const uint16_t s_u = __builtin_amdgcn_raw_buffer_load_b16(mu.s, (r * mu.ng + gu) * 2, 0, 0);
       const uint16_t b_u = __builtin_amdgcn_raw_buffer_load_b16(mu.b, (r * mu.ng + gu) * 2, 0, 0);
       if (g < mg.ng)
-        kmax_g = fmaxf(kmax_g, group_term_max(act_to_f32(s_g, p.act), act_to_f32(b_g, p.act), CodeOffset<BITS_G>::z,
+        kmax_g = fmaxf(kmax_g, group_term_max(act_to_f32(s_g, ACT), act_to_f32(b_g, ACT), CodeOffset<BITS_G>::z,
                                               kPlaneMax<BITS_G>));
       if (g < mu.ng)
-        kmax_u = fmaxf(kmax_u, group_term_max(act_to_f32(s_u, p.act), act_to_f32(b_u, p.act), CodeOffset<BITS_U>::z,
+        kmax_u = fmaxf(kmax_u, group_term_max(act_to_f32(s_u, ACT), act_to_f32(b_u, ACT), CodeOffset<BITS_U>::z,
                                               kPlaneMax<BITS_U>));
     }
     kmax_g = fmaxf(kmax_g, __shfl_xor(kmax_g, 16));
@@ -845,11 +857,11 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     // a chunk past the end gets zero scales and biases: its B operands vanish
     // (scaled by the column's 2^-k)
     const int kg_ = k_gate(), ku_ = k_up();
-    const float sg = d.live ? ldexpf(act_to_f32((uint16_t)d.sg, p.act), -kg_) : 0.0f;
-    const float bg = d.live ? ldexpf(act_to_f32((uint16_t)d.bg, p.act), -kg_) : 0.0f;
-    const float su = d.live ? ldexpf(act_to_f32((uint16_t)d.su, p.act), -ku_) : 0.0f;
-    const float bu = d.live ? ldexpf(act_to_f32((uint16_t)d.bu, p.act), -ku_) : 0.0f;
-    const bool split = p.act == kActF16;
+    const float sg = d.live ? ldexpf(act_to_f32((uint16_t)d.sg, ACT), -kg_) : 0.0f;
+    const float bg = d.live ? ldexpf(act_to_f32((uint16_t)d.bg, ACT), -kg_) : 0.0f;
+    const float su = d.live ? ldexpf(act_to_f32((uint16_t)d.su, ACT), -ku_) : 0.0f;
+    const float bu = d.live ? ldexpf(act_to_f32((uint16_t)d.bu, ACT), -ku_) : 0.0f;
+    constexpr bool split = ACT == kActF16;
     const f16x2 sg2 = split ? split_scale(sg) : (f16x2){(_Float16)sg, (_Float16)sg};
     const f16x2 su2 = split ? split_scale(su) : (f16x2){(_Float16)su, (_Float16)su};
 #pragma unroll
@@ -957,7 +969,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       uint32_t a = max(xam[t] & 0xFFFFu, xam[t] >> 16);
       a = max(a, (uint32_t)__shfl_xor((int)a, 16));
       a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-      xe_self[t] = x_exponent(a, p.act);
+      xe_self[t] = x_exponent(a, ACT);
       in_range = in_range && xe_self[t] >= 0 && xe_self[t] <= 9;
     }
     xe_zero = __all(in_range);
@@ -980,8 +992,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         float f[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          f[2 * j] = act_to_f32((uint16_t)(v[j] & 0xFFFFu), p.act);
-          f[2 * j + 1] = act_to_f32((uint16_t)(v[j] >> 16), p.act);
+          f[2 * j] = act_to_f32((uint16_t)(v[j] & 0xFFFFu), ACT);
+          f[2 * j + 1] = act_to_f32((uint16_t)(v[j] >> 16), ACT);
         }
         if (!xe_zero) {
 #pragma unroll
@@ -994,9 +1006,9 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   float cmax_g = 0.0f, cmax_u = 0.0f;
   auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
     if (!d.live) return;
-    cmax_g = fmaxf(cmax_g, group_term_max(act_to_f32((uint16_t)d.sg, p.act), act_to_f32((uint16_t)d.bg, p.act),
+    cmax_g = fmaxf(cmax_g, group_term_max(act_to_f32((uint16_t)d.sg, ACT), act_to_f32((uint16_t)d.bg, ACT),
                                           CodeOffset<BITS_G>::z, kPlaneMax<BITS_G>));
-    cmax_u = fmaxf(cmax_u, group_term_max(act_to_f32((uint16_t)d.su, p.act), act_to_f32((uint16_t)d.bu, p.act),
+    cmax_u = fmaxf(cmax_u, group_term_max(act_to_f32((uint16_t)d.su, ACT), act_to_f32((uint16_t)d.bu, ACT),
                                           CodeOffset<BITS_U>::z, kPlaneMax<BITS_U>));
   };
   auto chunk_k_wave = [&]() {
@@ -1035,7 +1047,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       atomicMax(&xmax[b / (p.H >> 3)], amax);
     }
     __syncthreads();
-    if (tid < p.M) xe[tid] = x_exponent(xmax[tid], p.act);
+    if (tid < p.M) xe[tid] = x_exponent(xmax[tid], ACT);
     __syncthreads();
     for (int b = tid; b < nblk; b += nt) {              // x' = x 2^-e in the code-pair order
       const int m = b / (p.H >> 3), k8 = b - m * (p.H >> 3);
@@ -1044,8 +1056,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       float f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f[2 * j] = ldexpf(act_to_f32((uint16_t)(v[j] & 0xFFFFu), p.act), -e);
-        f[2 * j + 1] = ldexpf(act_to_f32((uint16_t)(v[j] >> 16), p.act), -e);
+        f[2 * j] = ldexpf(act_to_f32((uint16_t)(v[j] & 0xFFFFu), ACT), -e);
+        f[2 * j + 1] = ldexpf(act_to_f32((uint16_t)(v[j] >> 16), ACT), -e);
       }
       u32x4 o;
 #pragma unroll
@@ -1179,7 +1191,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       u += red_at(ww, 2 * t + 1)[lane][j];
     }
     const int m = 16 * t + 4 * h + j;
-    if (m < p.M && col < p.I) store_out(p, m, col, g, u);
+    if (m < p.M && col < p.I) store_out(p, m, col, g, u, ACT);
   }
 }
 
@@ -1193,7 +1205,7 @@ static int gemv_lanes_per_column(int H) {
   return l;
 }
 
-template <int BG, int BU, int CPL, bool FULL>
+template <int BG, int BU, int CPL, bool FULL, int ACT>
 static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream) {
   constexpr int WPB = 4;
   const int lpc = gemv_lanes_per_column(p.H);
@@ -1205,9 +1217,9 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
   if (p.H > kGemv1MaxH || p.H / 8 > 256 * CPL) return hipErrorInvalidValue;
   const int blocks = (waves + WPB - 1) / WPB;
   switch (R) {
-    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
-    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
-    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL, WPB, 1>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 1: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 1, ACT>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 1, ACT>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
+    case 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 4, FULL, WPB, 1, ACT>), dim3(blocks), dim3(64 * WPB), 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1215,7 +1227,7 @@ static hipError_t launch_gemv1_t(const GemvParams& p, int R, hipStream_t stream)
 
 // The several-row form (gemv1_rows_shape): a whole wave per column, R (one
 // or two) columns per wave.
-template <int BG, int BU, int CPL, bool FULL>
+template <int BG, int BU, int CPL, bool FULL, int ACT>
 static hipError_t launch_gemv1_rows_t(const GemvParams& p, int R, hipStream_t stream) {
   constexpr int WPB = 4;
   const int lpc = gemv_lanes_per_column(p.H);
@@ -1228,12 +1240,12 @@ static hipError_t launch_gemv1_rows_t(const GemvParams& p, int R, hipStream_t st
   const int blocks = (waves + WPB - 1) / WPB;
   const dim3 g(blocks), b(64 * WPB);
   switch (R * 8 + p.M) {
-    case 8 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 2>), g, b, 0, stream, p, lg); break;
-    case 8 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 3>), g, b, 0, stream, p, lg); break;
-    case 8 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 4>), g, b, 0, stream, p, lg); break;
-    case 16 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 2>), g, b, 0, stream, p, lg); break;
-    case 16 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 3>), g, b, 0, stream, p, lg); break;
-    case 16 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 4>), g, b, 0, stream, p, lg); break;
+    case 8 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 2, ACT>), g, b, 0, stream, p, lg); break;
+    case 8 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 3, ACT>), g, b, 0, stream, p, lg); break;
+    case 8 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 1, FULL, WPB, 4, ACT>), g, b, 0, stream, p, lg); break;
+    case 16 + 2: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 2, ACT>), g, b, 0, stream, p, lg); break;
+    case 16 + 3: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 3, ACT>), g, b, 0, stream, p, lg); break;
+    case 16 + 4: hipLaunchKernelGGL((swq_gemv1_kernel<BG, BU, CPL, 2, FULL, WPB, 4, ACT>), g, b, 0, stream, p, lg); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1251,6 +1263,7 @@ static int gemv1_rounds(int I) {
   return r ? r : (I >= 4096 ? 2 : 1);
 }
 
+#if SWQ_GEMV_ACT == 0
 // SWIGLU_Q_GEMV1_ROWS=0 sends 2 <= M <= kGemv1MaxRows to the few-row MFMA
 // kernel instead (for comparisons).
 bool gemv1_rows_enabled() {
@@ -1260,6 +1273,7 @@ bool gemv1_rows_enabled() {
   }();
   return on;
 }
+#endif
 
 // Waves per block of the few-row kernel and whether it takes two chunk quads
 // per pass (the launcher's choice below), for x source xs.
@@ -1284,6 +1298,7 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
 // kSkinnyStageMax; else from the prep kernel.
 // SWIGLU_Q_SKINNY_X=prep or =stage (where M*H allows) overrides, for
 // comparisons and for tests of those sources.
+#if SWQ_GEMV_ACT == 0
 int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
   const char* env = getenv("SWIGLU_Q_SKINNY_X");
   if (env && strcmp(env, "prep") == 0) return kXPrep;
@@ -1303,8 +1318,9 @@ bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
   skinny_shape(M, H, bits_g, bits_u, kXPrep, &waves, &two);
   return (H / 32 + 3) / 4 > (two ? 2 : 1) * waves;
 }
+#endif
 
-template <int BG, int BU>
+template <int BG, int BU, int ACT>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
   const int cpl = (p.H / 32 + lpc - 1) / lpc;
@@ -1312,18 +1328,18 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     const bool full = lpc == 64 && p.H == 2048 * cpl;
     const int r = gemv1_rounds(p.I);
     switch (cpl) {
-      case 1: return full ? launch_gemv1_t<BG, BU, 1, true>(p, r, stream) : launch_gemv1_t<BG, BU, 1, false>(p, r, stream);
-      case 2: return full ? launch_gemv1_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_t<BG, BU, 2, false>(p, r, stream);
-      case 3: return full ? launch_gemv1_t<BG, BU, 3, true>(p, r, stream) : launch_gemv1_t<BG, BU, 3, false>(p, r, stream);
-      default: return full ? launch_gemv1_t<BG, BU, 4, true>(p, r, stream) : launch_gemv1_t<BG, BU, 4, false>(p, r, stream);
+      case 1: return full ? launch_gemv1_t<BG, BU, 1, true, ACT>(p, r, stream) : launch_gemv1_t<BG, BU, 1, false, ACT>(p, r, stream);
+      case 2: return full ? launch_gemv1_t<BG, BU, 2, true, ACT>(p, r, stream) : launch_gemv1_t<BG, BU, 2, false, ACT>(p, r, stream);
+      case 3: return full ? launch_gemv1_t<BG, BU, 3, true, ACT>(p, r, stream) : launch_gemv1_t<BG, BU, 3, false, ACT>(p, r, stream);
+      default: return full ? launch_gemv1_t<BG, BU, 4, true, ACT>(p, r, stream) : launch_gemv1_t<BG, BU, 4, false, ACT>(p, r, stream);
     }
   }
   if (gemv1_rows_shape(p.M, p.H)) {
     static_assert(kGemv1RowsMaxH <= 2 * 2048, "at most two chunks per lane");
     const bool full = lpc == 64 && p.H == 2048 * cpl;
     const int r = gemv1_rounds(p.I) >= 2 ? 2 : 1;
-    if (cpl == 1) return full ? launch_gemv1_rows_t<BG, BU, 1, true>(p, r, stream) : hipErrorInvalidValue;   // H = 2048
-    return full ? launch_gemv1_rows_t<BG, BU, 2, true>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false>(p, r, stream);
+    if (cpl == 1) return full ? launch_gemv1_rows_t<BG, BU, 1, true, ACT>(p, r, stream) : hipErrorInvalidValue;   // H = 2048
+    return full ? launch_gemv1_rows_t<BG, BU, 2, true, ACT>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false, ACT>(p, r, stream);
   }
   if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
   // one wave per chunk quad (or pair of quads), at most kSkinnyMaxWaves per
@@ -1344,9 +1360,9 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   auto go = [&](auto xs_tag, auto two_tag) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr bool TWO = decltype(two_tag)::value;
-    if constexpr (XS == kXSelf) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO>), g, b, lds, stream, p);
-    else if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO>), g, b, 0, stream, p);
+    if constexpr (XS == kXSelf) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT>), g, b, lds, stream, p);
+    else if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO, ACT>), g, b, 0, stream, p);
   };
   using F = std::false_type;
   using T = std::true_type;
@@ -1361,19 +1377,32 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BG>
+template <int BG, int ACT>
 static hipError_t launch_gemv_g(const GemvParams& p, int bits_u, hipStream_t stream) {
-  if (bits_u == 2) return launch_gemv_bits<BG, 2>(p, stream);
-  if (bits_u == 4) return launch_gemv_bits<BG, 4>(p, stream);
-  if (bits_u == 8) return launch_gemv_bits<BG, 8>(p, stream);
+  if (bits_u == 2) return launch_gemv_bits<BG, 2, ACT>(p, stream);
+  if (bits_u == 4) return launch_gemv_bits<BG, 4, ACT>(p, stream);
+  if (bits_u == 8) return launch_gemv_bits<BG, 8, ACT>(p, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream) {
-  if (bits_g == 2) return launch_gemv_g<2>(p, bits_u, stream);
-  if (bits_g == 4) return launch_gemv_g<4>(p, bits_u, stream);
-  if (bits_g == 8) return launch_gemv_g<8>(p, bits_u, stream);
+template <int ACT>
+hipError_t launch_gemv_act(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream) {
+  if (bits_g == 2) return launch_gemv_g<2, ACT>(p, bits_u, stream);
+  if (bits_g == 4) return launch_gemv_g<4, ACT>(p, bits_u, stream);
+  if (bits_g == 8) return launch_gemv_g<8, ACT>(p, bits_u, stream);
   return hipErrorInvalidValue;
 }
+
+template hipError_t launch_gemv_act<SWQ_GEMV_ACT>(const GemvParams&, int, int, hipStream_t);
+
+#if SWQ_GEMV_ACT == 0
+extern template hipError_t launch_gemv_act<kActF16>(const GemvParams&, int, int, hipStream_t);
+
+hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream) {
+  if (p.act == kActF16) return launch_gemv_act<kActF16>(p, bits_g, bits_u, stream);
+  if (p.act == kActBf16) return launch_gemv_act<kActBf16>(p, bits_g, bits_u, stream);
+  return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace swq

@@ -155,6 +155,10 @@ hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
+// the instances of one activation type (kActBf16 / kActF16), each compiled in
+// its own translation unit
+template <int ACT>
+hipError_t launch_gemv_act(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
 // The few-row kernel's x source for a call of M rows (kXPrep, kXStage or kXSelf).
 int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u);
 // Whether the few-row kernel, fed x' by the prep kernel, needs the weight-row
