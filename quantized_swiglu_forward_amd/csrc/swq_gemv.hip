@@ -532,7 +532,8 @@ struct SkinnyChunk {
   // codes as loaded (the line-friendly lane order, 2-bit codes not yet
   // spread), then in the MFMA's order
   u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[RT][4];
-  uint32_t sg, bg, su, bu;   // raw bf16 bits, converted where used (after every load is issued)
+  uint32_t sg, bg, su, bu;   // raw 16-bit bits, converted where used (after every load is issued)
+  float sx[RT];              // x converted by the wave: the lane's sum of x' (float32 adds)
   bool live;
 };
 
@@ -882,10 +883,14 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       float sx = 0.0f;
+      if constexpr (SELF) {
+        sx = d.sx[t];   // summed as x was converted
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sx = fma2(d.x[t][q][j], 0x3C003C00u, sx);   // x' times 1 (see fma2)
+          for (int j = 0; j < 4; ++j) sx = fma2(d.x[t][q][j], 0x3C003C00u, sx);   // x' times 1 (see fma2)
+      }
       const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
       const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
       ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[t], 0, 0, 0);
@@ -982,10 +987,13 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     }
   };
   // ... and x' = x 2^-e in binary16, in the code-pair order (word j of a
-  // block holds inputs j and j + 4), in place
+  // block holds inputs j and j + 4), in place, with the lane's sum of x'
+  // for the bias term (float32 adds of x 2^-e, which is x' wherever binary16
+  // holds it exactly; done here, while the weights are still in flight)
   auto x_convert = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < RT; ++t) {
+      d.sx[t] = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x4 v = d.x[t][q];
@@ -1001,7 +1009,10 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) d.x[t][q][j] = as_u32((f16x2){(_Float16)f[j], (_Float16)f[j + 4]});
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d.sx[t] += f[j];
       }
+    }
   };
   float cmax_g = 0.0f, cmax_u = 0.0f;
   auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
