@@ -724,6 +724,31 @@ def test_same_sign_activations(M, H, I, spec, act, sign):
     check(y, oracle_full(p, 1), 1, f"same-sign {sign} {act} M{M} H{H}")
 
 
+# x of a wide dynamic range: every element 2^-j (1 + f) with j uniform in
+# 0..17, so one 32-input chunk spans the whole window in which x' is exact
+# binary16 (2^-17 of its largest element), products meet the dot products
+# and MFMAs at very different exponents, and small terms must not be lost
+# beside large ones; mixed and one sign, on every path.
+WIDE_SHAPES = [(1, 2048, 256, "gemv"), (3, 2048, 128, "gemv"), (8, 2048, 128, "gemv"), (24, 2048, 96, "gemv"),
+               (70, 1024, 256, "mfma"), (300, 2048, 160, "mfma")]
+
+
+@pytest.mark.parametrize("sign", ["mixed", "positive"])
+@pytest.mark.parametrize("M,H,I,path", WIDE_SHAPES, ids=[f"M{m}-H{h}-{p}" for m, h, _, p in WIDE_SHAPES])
+def test_wide_range_x(M, H, I, path, sign):
+    p = make_custom(M, H, I, 4, 64, 4, 64, seed=M + H)
+    rng = np.random.default_rng(M * 7 + 17)
+    x = np.ldexp(rng.uniform(1, 2, (M, H)), -rng.integers(0, 18, (M, H)))
+    if sign == "mixed":
+        x *= rng.choice([-1.0, 1.0], (M, H))
+    p.x = to_bf16_bits(x.astype(np.float32))
+    path = swq.SWQ_PATH_GEMV if path == "gemv" else swq.SWQ_PATH_MFMA
+    for mode in (1, 0):
+        say("wide-range x", sign, M, H, I, "path", path, "mode", mode)
+        y = device_forward(p, mode, path)
+        check(y, oracle_full(p, mode), mode, f"wide x {sign} M{M} mode {mode}")
+
+
 # The few-row kernel takes x' = x when every row's largest magnitude lies in
 # [1, 2^10), else scales by each row's power of two: all-positive rows just
 # inside (2^9, 2^10) and well outside (2^14) that range, where a chunk's sum
