@@ -210,20 +210,21 @@ __device__ __forceinline__ int row_exponent_k(float m) {
   return min(max(E - 14, -200), 200);
 }
 
-// silu(g) u = g sigma(g) u, sigma(g) = 1 / (1 + e^-g) for g >= 0 and
-// e^g / (1 + e^g) below, with e = e^-|g| from the hardware exp2 and the
-// reciprocal (about 1 ulp each).  Once |g| > 64 ln 2, e is taken times 2^64
-// (1 + e is then 1 in float32), so it stays a normal number down to
-// g = -190 ln 2 and a negative g's product leaves float32's normal range only
-// at the last step, one rounding; below that the true value is under half
-// float32's smallest subnormal whenever |g u| < 2^40.
+// silu(g) u = g sigma(g) u with sigma(g) = 1 / (1 + 2^b), b = -g log2(e),
+// from the hardware exp2 and reciprocal (about 1 ulp each).  Past b = 64
+// (g < -44.4) the 1 in the denominator is below float32's resolution, so
+// sigma(g) = 2^-b to within 2^-64, taken as 2^64 rcp(2^(b - 64)): the
+// reciprocal stays a normal number down to b = 190 (g = -131.7), where
+// sigma(g) itself has long left float32's normal range, and the product
+// leaves that range only at its last step, one rounding (float32's own
+// subnormals).  Below b = 190 the true value is under half float32's
+// smallest subnormal whenever |g u| < 2^40.
 __device__ __forceinline__ float silu_times(float g, float u) {
-  const float a = -fabsf(g) * 1.4426950408889634f;
-  const bool deep = a < -64.0f;
-  const float e = __builtin_amdgcn_exp2f(deep ? a + 64.0f : a);
-  const float r = __builtin_amdgcn_rcpf(1.0f + (deep ? 0.0f : e));
-  const float h = g * (g >= 0.0f ? r : e * r) * u;
-  return (deep && g < 0.0f) ? ldexpf(h, -64) : h;
+  const float b = g * -1.4426950408889634f;
+  const bool deep = b > 64.0f;
+  const float e = __builtin_amdgcn_exp2f(b - (deep ? 64.0f : 0.0f));
+  const float r = __builtin_amdgcn_rcpf(e + (deep ? 0.0f : 1.0f));
+  return ldexpf(g * r * u, deep ? -64 : 0);
 }
 
 // Debug build (-DSWQ_LDS_POISON): every kernel fills its LDS with a poison
