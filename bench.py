@@ -116,9 +116,10 @@ def measured_traffic():
 
 def rotating_weight_sets(c, base_dev, n_sets, seed):
     """Set 0 is the seeded problem; the others are drawn on the GPU from the
-    same distributions (uniform codes, scales U[0.005,0.02] in bf16, biases
-    -8*s*U[0.9,1.1] in bf16), seeded."""
+    same distributions (uniform codes, scales U[0.005,0.02] and biases
+    -8*s*U[0.9,1.1] in the activation type), seeded."""
     import torch
+    dt16 = torch.float16 if c.act == "f16" else torch.bfloat16
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     sets = [base_dev[1:]]
@@ -129,9 +130,9 @@ def rotating_weight_sets(c, base_dev, n_sets, seed):
             words = torch.randint(-2**31, 2**31 - 1, (c.I, c.H * bits // 32), generator=gen, device="cuda",
                                   dtype=torch.int64).to(torch.int32)
             s = (torch.rand((c.I, ng), generator=gen, device="cuda") * (c.s_hi - c.s_lo) + c.s_lo)
-            s = s.to(torch.bfloat16)
+            s = s.to(dt16)
             f = torch.rand((c.I, ng), generator=gen, device="cuda") * 0.2 + 0.9
-            b = (-8.0 * s.float() * f).to(torch.bfloat16)
+            b = (-8.0 * s.float() * f).to(dt16)
             one += [words, s, b]
         sets.append(tuple(one))
     return sets
@@ -451,11 +452,12 @@ def bench_prefill_one(cfg, steps, warmup, mode=0, measured_peak=None):
 
     c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
     dev = swq.to_device(problem(cfg))
-    out = torch.empty((c.M, c.I), dtype=torch.float32 if mode == 1 else torch.bfloat16, device="cuda")
+    out16 = torch.float16 if c.act == "f16" else torch.bfloat16
+    out = torch.empty((c.M, c.I), dtype=torch.float32 if mode == 1 else out16, device="cuda")
     stream = torch.cuda.Stream()
     pm = ["MATCH", "F32", "F32_BF16OUT"][mode]
     config = {"workload": c.describe, "M": c.M, "H": c.H, "I": c.I, "bits_g": c.bits_g, "gs_g": c.gs_g,
-              "bits_u": c.bits_u, "gs_u": c.gs_u, "precision_mode": pm}
+              "bits_u": c.bits_u, "gs_u": c.gs_u, "precision_mode": pm, "activations": c.act}
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             swq.forward(*dev, c.bits_g, c.gs_g, c.bits_u, c.gs_u, mode=mode, out=out, stream=stream)
@@ -519,16 +521,18 @@ def bench_decode_spec(c, steps, warmup):
     sets = rotating_weight_sets(c, dev, ROTATING_SETS, seed=103)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
-    x = torch.randn((CALLS, c.H), generator=gen, device="cuda").to(torch.bfloat16)
-    out = torch.empty((CALLS, c.I), dtype=torch.bfloat16, device="cuda")
+    dt16 = torch.float16 if c.act == "f16" else torch.bfloat16
+    x = torch.randn((CALLS, c.H), generator=gen, device="cuda").to(dt16)
+    out = torch.empty((CALLS, c.I), dtype=dt16, device="cuda")
     L = swq.lib()
+    entry = L.swiglu_q_forward_f16 if c.act == "f16" else L.swiglu_q_forward
     ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
 
     def step(sh):
         for i in range(CALLS):
             wg, sg, bg, wu, su, bu = ptrs[i % ROTATING_SETS]
-            rc = L.swiglu_q_forward(x.data_ptr() + i * c.H * 2, wg, sg, bg, wu, su, bu, 1, c.H, c.I, c.bits_g,
-                                    c.gs_g, c.bits_u, c.gs_u, 0, out.data_ptr() + i * c.I * 2, sh)
+            rc = entry(x.data_ptr() + i * c.H * 2, wg, sg, bg, wu, su, bu, 1, c.H, c.I, c.bits_g,
+                       c.gs_g, c.bits_u, c.gs_u, 0, out.data_ptr() + i * c.I * 2, sh)
             if rc != 0:
                 raise RuntimeError(f"swiglu_q_forward failed: {swq.swiglu_q_strerror(rc)}")
 
@@ -552,7 +556,7 @@ def bench_decode_spec(c, steps, warmup):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (steps * CALLS)
     alg = algorithmic_bytes(c)
-    return {"config": c.describe, "avg_launch_us": round(us, 3),
+    return {"config": c.describe, "activations": c.act, "avg_launch_us": round(us, 3),
             "weight_GB_per_s": round(weight_bytes(c) / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
 
@@ -974,12 +978,21 @@ def main():
         c1g = replace(CONFIGS[1], name="decode_gs128", gs_g=128, gs_u=128, calls=0,
                       describe="decode GEMV M=1 H=2048 I=5632, 4-bit gs128 gate/up, fresh x per call, "
                                "40 rotating weight sets, hip graph")
+        # binary16 activations (x, scales and biases float16)
+        c3h = replace(CONFIGS[3], name="large_prefill_f16", act="f16",
+                      describe="large prefill M=2048 H=4096 I=14336, 4-bit gs64 gate/up, float16 activations")
+        c1h = replace(CONFIGS[1], name="decode_f16", act="f16", calls=0,
+                      describe="decode GEMV M=1 H=2048 I=5632, 4-bit gs64 gate/up, float16 activations, fresh x "
+                               "per call, 40 rotating weight sets, hip graph")
         line["spec_variants"] = {
             "c3_gs128_match": bench_prefill_one(c3g, steps=10, warmup=3, mode=0,
                                                 measured_peak=peaks["kernel_like_operands"]),
             "c2_f32_bf16out": bench_prefill_one(2, steps=10, warmup=3, mode=2,
                                                 measured_peak=peaks["kernel_like_operands"]),
-            "c1_gs128": bench_decode_spec(c1g, max(1, args.steps // 4), 2)}
+            "c1_gs128": bench_decode_spec(c1g, max(1, args.steps // 4), 2),
+            "c3_f16_match": bench_prefill_one(c3h, steps=10, warmup=3, mode=0,
+                                              measured_peak=peaks["kernel_like_operands"]),
+            "c1_f16": bench_decode_spec(c1h, max(1, args.steps // 4), 2)}
         torch.cuda.empty_cache()
     if not args.no_linear:
         log("linear: timing ...")

@@ -85,6 +85,7 @@ class Config:
     bias_mode: str = "factor"
     calls: int = 1            # decode workload: number of fresh-x calls
     describe: str = ""
+    act: str = "bf16"         # activation type: "bf16" or "f16" (binary16 x, scales and biases)
 
 
 CONFIGS = {
@@ -193,7 +194,7 @@ def make_problem(cfg: int | Config, keep_codes=False, with_calls=True) -> Proble
                        seed=c.seed, x_sigma=c.x_sigma, s_lo=c.s_lo, s_hi=c.s_hi,
                        bias_mode=c.bias_mode,
                        calls=(c.calls if (with_calls and c.calls > 1) else 0),
-                       keep_codes=keep_codes)
+                       keep_codes=keep_codes, act=c.act)
 
 
 def decode_xs(cfg: int | Config) -> np.ndarray:
