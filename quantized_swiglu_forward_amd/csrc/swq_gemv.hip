@@ -13,9 +13,10 @@
 //  * swq_gemv1_kernel: M = 1 with at most four chunks per lane (H <= 8192),
 //    and 2 <= M <= 4 with a whole wave per column and at most two chunks
 //    per lane (2048 <= H <= 4096), each weight chunk loaded once for all
-//    rows.  Codes enter mixed-precision FMAs as exact binary16 subnormals
-//    with no offset, each chunk of x scaled by its own power of two; the
-//    block shares x through LDS (described above the kernel).
+//    rows.  Codes enter mixed-precision FMAs (MATCH: v_dot2_f32_f16) as
+//    exact binary16 subnormals with no offset, each chunk of x scaled by its
+//    own power of two; the block shares x through LDS (described above the
+//    kernel).
 //  * swq_skinny_kernel: 1 <= M <= 32 otherwise.  x' is converted by the
 //    waves themselves (M <= 16), built in LDS by every block, or staged by
 //    the prep kernel; codes become exact binary16 s (q - z) and
@@ -117,8 +118,8 @@ __device__ __forceinline__ void store_out(const GemvParams& p, int m, int n, flo
 // Codes as binary16 subnormals.  A 4-bit code q in bits [0,4) of a binary16
 // lane, with the exponent field zero, is the subnormal q * 2^-24; in bits
 // [4,8) it is 16q * 2^-24.  So one AND per code pair of a word yields exact
-// binary16 operands (no magic constant, no offset), and v_dot2_f32_f16
-// forms exact products x' * q in float32.  The x' pairs that meet a code in
+// binary16 operands (no magic constant, no offset), and mixed-precision FMAs
+// (or v_dot2_f32_f16) form exact products x' * q in float32.  The x' pairs that meet a code in
 // bits [0,4) are stored pre-multiplied by 16 (exact: a power of two, and
 // 16 max|x'| < 32), so every product lands in the same unit 2^-20:
 //
@@ -151,9 +152,21 @@ __device__ __forceinline__ float fma2(uint32_t xv, uint32_t cv, float p) {
   return __builtin_fmaf((float)x[1], (float)c[1], p);
 }
 
+// The same two products, summed by v_dot2_f32_f16 (DOT) or by fma2.  The M = 1
+// kernel takes v_dot2 in MATCH, where gate and up are rounded to the 16-bit
+// activation type: its summation error (measured: at most about 5e-5 of the
+// column's cancellation-free scale on rows of one-signed x) lies far inside
+// that rounding's tie allowance, and one instruction per pair halves the
+// arithmetic that follows the loads.  The float32 modes take fma2.
+template <bool DOT>
+__device__ __forceinline__ float pair2(uint32_t xv, uint32_t cv, float p) {
+  if constexpr (DOT) return __builtin_amdgcn_fdot2(as_h2(xv), as_h2(cv), p, false);
+  else return fma2(xv, cv, p);
+}
+
 // Unscaled dot of one chunk in units of 2^-20: xa holds the 16x pairs
 // (codes at bits [0,4)), xb the 1x pairs (codes at bits [4,8)).
-template <int BITS>
+template <int BITS, bool DOT>
 __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const uint32_t xa[8], const uint32_t xb[8]) {
   float p = 0.0f;
   if (kCodeWidth<BITS> == 4) {
@@ -161,10 +174,10 @@ __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const ui
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = r.w[0][j];
       const uint32_t w8 = w >> 8;
-      p = fma2(xa[2 * j], w & 0x000F000Fu, p);
-      p = fma2(xb[2 * j], w & 0x00F000F0u, p);
-      p = fma2(xa[2 * j + 1], w8 & 0x000F000Fu, p);
-      p = fma2(xb[2 * j + 1], w8 & 0x00F000F0u, p);
+      p = pair2<DOT>(xa[2 * j], w & 0x000F000Fu, p);
+      p = pair2<DOT>(xb[2 * j], w & 0x00F000F0u, p);
+      p = pair2<DOT>(xa[2 * j + 1], w8 & 0x000F000Fu, p);
+      p = pair2<DOT>(xb[2 * j + 1], w8 & 0x00F000F0u, p);
     }
   } else {
     // xa / xb interleave as (pair 0, pair 2) / (pair 1, pair 3) of each 8-block;
@@ -180,8 +193,8 @@ __device__ __forceinline__ float chunk_dot_sub(const RawChunk<BITS>& r, const ui
       for (int t = 0; t < 4; ++t) {
         const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + t) << 16) | (uint32_t)t;
         const uint32_t v = __builtin_amdgcn_perm(wb, wa, sel);
-        p = fma2(xq[t], v & 0x000F000Fu, p);
-        p = fma2(xq[t], v & 0x00F000F0u, p);
+        p = pair2<DOT>(xq[t], v & 0x000F000Fu, p);
+        p = pair2<DOT>(xq[t], v & 0x00F000F0u, p);
       }
     }
   }
@@ -309,9 +322,9 @@ __device__ __forceinline__ void read_x_chunk(const u32x4* xs, const float2* xinf
 }
 
 // The chunk's share of sum_k x_k (s q_k + b), in the chunk's own scale 2^(e+20).
-template <int BITS>
+template <int BITS, bool DOT>
 __device__ __forceinline__ float chunk_term(const RawChunk<BITS>& r, const XChunk& x, int act) {
-  const float P = chunk_dot_sub<BITS>(r, x.xa, x.xb);
+  const float P = chunk_dot_sub<BITS, DOT>(r, x.xa, x.xb);
   const float s = act_to_f32((uint16_t)(r.sb & 0xFFFFu), act);
   const float b = act_to_f32((uint16_t)(r.sb >> 16), act);
   return fmaf(s, P, b * x.sx);
@@ -392,108 +405,114 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
   asm volatile("" ::: "memory");
 
   // 4. per column: chunk terms, reduction over the column group, epilogue
-  // (row m of the output)
-  auto finish = [&](const float (&ag)[R], const float (&au)[R], int m) __attribute__((always_inline)) {
-    if (R <= 2 && (FULL || lpc == 64)) {
-      // Sums of the 2R values of the wave with two lane-swap folds and one row
-      // sum: row 0 ends with column 0's gate, row 2 with its up, rows 1 and 3
-      // with column 1's (R = 2); lane 16 r then runs column r's epilogue.
-      const float t0 = fold32(ag[0], au[0]);
-      const float t = R == 2 ? fold16(t0, fold32(ag[R - 1], au[R - 1])) : fold16(t0, t0);
-      const float g = row_sum(t);
-      const float u = upper_half(g);
-      const int col = lane >> 4;
-      const int64_t n = (int64_t)wave_global * R + col;
-      if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, m, (int)n, g, u, ACT);
-    } else if (FULL || lpc == 64) {
-      float g = 0.0f, u = 0.0f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float gr = wave_sum(ag[r]), ur = wave_sum(au[r]);
-        if (lane == r) {
-          g = gr;
-          u = ur;
+  // (row m of the output); the products summed by v_dot2 in MATCH, by FMAs
+  // otherwise (pair2)
+  auto columns = [&](auto dot_tag) {
+    constexpr bool DOT = decltype(dot_tag)::value;
+    auto finish = [&](const float (&ag)[R], const float (&au)[R], int m) __attribute__((always_inline)) {
+      if (R <= 2 && (FULL || lpc == 64)) {
+        // Sums of the 2R values of the wave with two lane-swap folds and one row
+        // sum: row 0 ends with column 0's gate, row 2 with its up, rows 1 and 3
+        // with column 1's (R = 2); lane 16 r then runs column r's epilogue.
+        const float t0 = fold32(ag[0], au[0]);
+        const float t = R == 2 ? fold16(t0, fold32(ag[R - 1], au[R - 1])) : fold16(t0, t0);
+        const float g = row_sum(t);
+        const float u = upper_half(g);
+        const int col = lane >> 4;
+        const int64_t n = (int64_t)wave_global * R + col;
+        if ((lane & 15) == 0 && col < R && n < p.I) store_out(p, m, (int)n, g, u, ACT);
+      } else if (FULL || lpc == 64) {
+        float g = 0.0f, u = 0.0f;
+  #pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float gr = wave_sum(ag[r]), ur = wave_sum(au[r]);
+          if (lane == r) {
+            g = gr;
+            u = ur;
+          }
+        }
+        const int n = wave_global * R + lane;
+        if (lane < R && n < p.I) store_out(p, m, n, g, u, ACT);
+      } else if constexpr (!FULL) {
+  #pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
+          const int n = (wave_global * R + r) * cpw + sub;
+          if (sl == 0 && n < p.I) store_out(p, m, n, g, u, ACT);
         }
       }
-      const int n = wave_global * R + lane;
-      if (lane < R && n < p.I) store_out(p, m, n, g, u, ACT);
-    } else if constexpr (!FULL) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float g = group_sum(ag[r], lpc), u = group_sum(au[r], lpc);
-        const int n = (wave_global * R + r) * cpw + sub;
-        if (sl == 0 && n < p.I) store_out(p, m, n, g, u, ACT);
-      }
-    }
-  };
-  if constexpr (MR > 1) {
-    // A whole wave per column (the launcher's condition).  Every row's sums
-    // first (each row's x chunk read from LDS once for the R columns), then
-    // the rows' reductions side by side, then one store branch for all rows:
-    // the rows' dependency chains overlap instead of running one after the
-    // other.  Per row the arithmetic is the single-row case's, in its order.
-    float ag[MR][R], au[MR][R];
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        ag[m][r] = 0.0f;
-        au[m][r] = 0.0f;
-      }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if (FULL || sl + c * lpc < nchunk) {
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-          XChunk xc;   // per row and chunk: all of them at once would not fit in registers
-          read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            ag[m][r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc, ACT), xc.e + 20);
-            au[m][r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc, ACT), xc.e + 20);
+    };
+    if constexpr (MR > 1) {
+      // A whole wave per column (the launcher's condition).  Every row's sums
+      // first (each row's x chunk read from LDS once for the R columns), then
+      // the rows' reductions side by side, then one store branch for all rows:
+      // the rows' dependency chains overlap instead of running one after the
+      // other.  Per row the arithmetic is the single-row case's, in its order.
+      float ag[MR][R], au[MR][R];
+  #pragma unroll
+      for (int m = 0; m < MR; ++m)
+  #pragma unroll
+        for (int r = 0; r < R; ++r) {
+          ag[m][r] = 0.0f;
+          au[m][r] = 0.0f;
+        }
+  #pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        if (FULL || sl + c * lpc < nchunk) {
+  #pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            XChunk xc;   // per row and chunk: all of them at once would not fit in registers
+            read_x_chunk(xs[m], xinfo[m], sl + c * lpc, xc);
+  #pragma unroll
+            for (int r = 0; r < R; ++r) {
+              ag[m][r] += ldexpf(chunk_term<BITS_G, DOT>(rg[r][c], xc, ACT), xc.e + 20);
+              au[m][r] += ldexpf(chunk_term<BITS_U, DOT>(ru[r][c], xc, ACT), xc.e + 20);
+            }
           }
         }
       }
-    }
-    float gm[MR], um[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const float t0 = fold32(ag[m][0], au[m][0]);
-      const float t = R == 2 ? fold16(t0, fold32(ag[m][R - 1], au[m][R - 1])) : fold16(t0, t0);
-      gm[m] = row_sum(t);
-      um[m] = upper_half(gm[m]);
-    }
-    // every lane of a 16-lane row holds its column's sums of every row:
-    // lane 16 col + m runs the epilogue of row m, all rows at once
-    const int col = lane >> 4, mrow = lane & 15;
-    const int64_t n = (int64_t)wave_global * R + col;
-    float g = gm[0], u = um[0];
-#pragma unroll
-    for (int m = 1; m < MR; ++m)
-      if (mrow == m) {
-        g = gm[m];
-        u = um[m];
+      float gm[MR], um[MR];
+  #pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float t0 = fold32(ag[m][0], au[m][0]);
+        const float t = R == 2 ? fold16(t0, fold32(ag[m][R - 1], au[m][R - 1])) : fold16(t0, t0);
+        gm[m] = row_sum(t);
+        um[m] = upper_half(gm[m]);
       }
-    if (mrow < MR && col < R && n < p.I) store_out(p, mrow, (int)n, g, u, ACT);
-  } else {
-    XChunk xc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) read_x_chunk(xs[0], xinfo[0], min(sl + c * lpc, nchunk - 1), xc[c]);
-    float ag[R], au[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      ag[r] = 0.0f;
-      au[r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (FULL || sl + c * lpc < nchunk) {
-          ag[r] += ldexpf(chunk_term<BITS_G>(rg[r][c], xc[c], ACT), xc[c].e + 20);
-          au[r] += ldexpf(chunk_term<BITS_U>(ru[r][c], xc[c], ACT), xc[c].e + 20);
+      // every lane of a 16-lane row holds its column's sums of every row:
+      // lane 16 col + m runs the epilogue of row m, all rows at once
+      const int col = lane >> 4, mrow = lane & 15;
+      const int64_t n = (int64_t)wave_global * R + col;
+      float g = gm[0], u = um[0];
+  #pragma unroll
+      for (int m = 1; m < MR; ++m)
+        if (mrow == m) {
+          g = gm[m];
+          u = um[m];
+        }
+      if (mrow < MR && col < R && n < p.I) store_out(p, mrow, (int)n, g, u, ACT);
+    } else {
+      XChunk xc[CPL];
+  #pragma unroll
+      for (int c = 0; c < CPL; ++c) read_x_chunk(xs[0], xinfo[0], min(sl + c * lpc, nchunk - 1), xc[c]);
+      float ag[R], au[R];
+  #pragma unroll
+      for (int r = 0; r < R; ++r) {
+        ag[r] = 0.0f;
+        au[r] = 0.0f;
+  #pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          if (FULL || sl + c * lpc < nchunk) {
+            ag[r] += ldexpf(chunk_term<BITS_G, DOT>(rg[r][c], xc[c], ACT), xc[c].e + 20);
+            au[r] += ldexpf(chunk_term<BITS_U, DOT>(ru[r][c], xc[c], ACT), xc[c].e + 20);
+          }
         }
       }
+      finish(ag, au, 0);
     }
-    finish(ag, au, 0);
-  }
+  };
+  if (p.mode == kMatch) columns(std::true_type{});
+  else columns(std::false_type{});
 }
 
 // --------------------------------------------------------- 2 <= M <= 32 --
