@@ -150,8 +150,9 @@ int swiglu_q_forward(const void *x,
  * swiglu_q_forward.  Source: the support predicate accepts float16
  * activations and the kernel's element type follows x ("mlx-bun 0.0.7 ->
  * 0.0.9", page 42, fused-swiglu-kernel.ts, support predicate and host
- * entry).  The matrix-matrix path runs 128 x 128 tiles and one more MFMA per
- * code block (the scales' two parts), the matrix-vector kernels as for bf16.
+ * entry).  The matrix-matrix path runs the bf16 tile shapes with one more
+ * MFMA per code block (the scales' two parts), the matrix-vector kernels as
+ * for bf16.
  */
 int swiglu_q_forward_f16(const void *x,
                          const uint32_t *Wg, const void *sg, const void *bg,

@@ -909,23 +909,28 @@ static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BG, int BU>
-static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
-  // binary16 activations: 128 x 128 tiles (their extra MFMA planes take the registers)
-  if (p.act == kActF16) return launch_mfma_t<BG, BU, 128, 32, 1, true>(p, stream);
+template <int BG, int BU, bool A16>
+static hipError_t launch_mfma_cfg(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
   // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
-  if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1>(p, stream);
+  if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1, A16>(p, stream);
   if constexpr (!(BG == 8 && BU == 8)) {
-    if (n_split <= 0 || n_split >= p.I) return launch_mfma_t<BG, BU, 256, 32, 1>(p, stream);
+    if (n_split <= 0 || n_split >= p.I) return launch_mfma_t<BG, BU, 256, 32, 1, A16>(p, stream);
     // columns [0, n_split) in whole rounds of 256 x 128 tiles, the rest in 128 x 128 tiles
     MfmaParams a = p, b = p;
     a.n_end = n_split;
     b.n_begin = n_split;
-    const hipError_t e = launch_mfma_t<BG, BU, 256, 32, 1>(a, stream);
+    const hipError_t e = launch_mfma_t<BG, BU, 256, 32, 1, A16>(a, stream);
     if (e != hipSuccess) return e;
-    return launch_mfma_t<BG, BU, 128, 32, 1>(b, stream);
+    return launch_mfma_t<BG, BU, 128, 32, 1, A16>(b, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// binary16 activations take the instances with the split-scale planes
+template <int BG, int BU>
+static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
+  if (p.act == kActF16) return launch_mfma_cfg<BG, BU, true>(p, cfg, n_split, stream);
+  return launch_mfma_cfg<BG, BU, false>(p, cfg, n_split, stream);
 }
 
 template <int BG>

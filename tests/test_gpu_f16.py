@@ -79,3 +79,31 @@ def test_f16_range(law, M, H, I, path):
     say("f16 range", name, M, H, I, "path", path)
     y = device_forward(p, 1, path)
     check(y, oracle_full(p, 1), 1, f"f16 range {name} M{M}")
+
+
+def test_f16_mfma_tile_shapes_agree_bitwise():
+    """The binary16 MFMA path in 256 x 128 tiles (forced), in 128 x 128 tiles
+    and with the library's choice: every output accumulates the same products
+    in the same order whatever the tile shape, so all three agree bit for bit,
+    and the oracle accepts them (one row tile past 256 and ragged I)."""
+    import os
+    p = make_custom(300, 1024, 400, 4, 64, 8, 32, seed=77, act="f16")
+    dev = swq.to_device(p)
+    outs = {}
+    for name, env in (("256", "0"), ("128", "1"), ("auto", None)):
+        old = os.environ.get("SWIGLU_Q_MFMA_CFG")
+        if env is None:
+            os.environ.pop("SWIGLU_Q_MFMA_CFG", None)
+        else:
+            os.environ["SWIGLU_Q_MFMA_CFG"] = env
+        try:
+            say("f16 tile shape", name)
+            outs[name] = device_forward(p, 1, MFMA, dev=dev)
+        finally:
+            if old is None:
+                os.environ.pop("SWIGLU_Q_MFMA_CFG", None)
+            else:
+                os.environ["SWIGLU_Q_MFMA_CFG"] = old
+    assert np.array_equal(outs["256"].view(np.int64), outs["128"].view(np.int64))
+    assert np.array_equal(outs["256"].view(np.int64), outs["auto"].view(np.int64))
+    check(outs["256"], oracle_full(p, 1), 1, "f16 256-row tiles")
