@@ -892,28 +892,38 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       block_mfma.template operator()<BITS_G>(d.cg, sg2, split, kb, a, ag);
       block_mfma.template operator()<BITS_U>(d.cu, su2, split, kb, a, au);
     }
-    // bias term: K slots (hi, hi, lo) x (c_hi, c_lo, c_hi) of this chunk
-    const _Float16 z0 = (_Float16)0.0f;
+    // bias term sum_k x'_k c of this chunk (c = b + z s split into two
+    // binary16 parts, c_hi + c_lo; every product exact):
     const float cgf = fmaf(CodeOffset<BITS_G>::z, sg, bg), cuf = fmaf(CodeOffset<BITS_U>::z, su, bu);
     const _Float16 cgh = (_Float16)cgf, cgl = (_Float16)(cgf - (float)cgh);
     const _Float16 cuh = (_Float16)cuf, cul = (_Float16)(cuf - (float)cuh);
-    const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
-    const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      float sx = 0.0f;
-      if constexpr (SELF) {
-        sx = d.sx[t];   // summed as x was converted
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sx = fma2(d.x[t][q][j], 0x3C003C00u, sx);   // x' times 1 (see fma2)
-      }
+    if constexpr (SELF) {
+      // x converted by the wave, which summed x' as it went: K slots
+      // (hi, hi, lo) of that sum against (c_hi, c_lo, c_hi)
+      const _Float16 z0 = (_Float16)0.0f;
+      const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
+      const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
+      const float sx = d.sx[0];
       const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
       const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
-      ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[t], 0, 0, 0);
-      au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[t], 0, 0, 0);
+      ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[0], 0, 0, 0);
+      au[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[0], 0, 0, 0);
+    } else {
+      // x' staged elsewhere: the block's A operands once more against
+      // B = c_hi and B = c_lo in every K slot of the lane's chunk (MFMAs
+      // instead of a VALU sum of x')
+      const f16x8 bgh = {cgh, cgh, cgh, cgh, cgh, cgh, cgh, cgh}, bgl = {cgl, cgl, cgl, cgl, cgl, cgl, cgl, cgl};
+      const f16x8 buh = {cuh, cuh, cuh, cuh, cuh, cuh, cuh, cuh}, bul = {cul, cul, cul, cul, cul, cul, cul, cul};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const f16x8 a = __builtin_bit_cast(f16x8, d.x[t][kb]);
+          ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgh, ag[t], 0, 0, 0);
+          au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, buh, au[t], 0, 0, 0);
+          ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgl, ag[t], 0, 0, 0);
+          au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bul, au[t], 0, 0, 0);
+        }
     }
   };
 
