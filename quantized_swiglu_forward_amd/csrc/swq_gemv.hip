@@ -1333,9 +1333,9 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
 }
 
 // x' converted by each wave itself for M <= 16 whenever a row fits one pass
-// of the block's waves and their LDS regions fit kSkinnySelfMaxLds (no second
-// launch, no workspace); else built in LDS by each block for M*H <=
-// kSkinnyStageMax; else from the prep kernel.
+// of the block's waves, their LDS regions fit kSkinnySelfMaxLds and the block
+// has more than one wave (no second launch, no workspace); else built in LDS
+// by each block for M*H <= kSkinnyStageMax; else from the prep kernel.
 // SWIGLU_Q_SKINNY_X=prep or =stage (where M*H allows) overrides, for
 // comparisons and for tests of those sources.
 #if SWQ_GEMV_ACT == 0
@@ -1346,10 +1346,13 @@ int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
   int waves;
   bool two;
   skinny_shape(M, H, bits_g, bits_u, kXSelf, &waves, &two);
+  const bool stage = M * H <= kSkinnyStageMax;
+  // (a one-wave block, H <= 256 with two quads per wave, converts faster in
+  // the block: measured 4.4 against 4.9 us at M = 6, H = 256, I = 768)
   if (M <= 16 && (H / 32 + 3) / 4 <= (two ? 2 : 1) * waves &&
-      waves * skinny_self_region((int)M, two ? 8 : 4) <= kSkinnySelfMaxLds)
+      waves * skinny_self_region((int)M, two ? 8 : 4) <= kSkinnySelfMaxLds && !(waves == 1 && stage))
     return kXSelf;
-  return M * H <= kSkinnyStageMax ? kXStage : kXPrep;
+  return stage ? kXStage : kXPrep;
 }
 
 bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
