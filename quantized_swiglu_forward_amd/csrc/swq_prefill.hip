@@ -29,10 +29,10 @@
 //     the dequantized weight pairs, and appends the extra columns
 //     (hi, hi, lo) of every group of g0 = min(gs_g, gs_u) inputs.  Every bf16
 //     x whose magnitude is at least 2^-17 of the row maximum converts
-//     exactly.  The column blocks then write, for 32 output features of both
-//     matrices each, the row exponents k, the extra-column B rows
-//     (c_hi, c_lo, c_hi) and the scale tiles (binary16 scale pairs per
-//     K-step, 128 columns at a time).
+//     exactly.  The column blocks then write, for a run of consecutive
+//     output features of both matrices each, the row exponents k, the
+//     extra-column B rows (c_hi, c_lo, c_hi) and the scale tiles (binary16
+//     scale pairs per K-step, 128 columns at a time).
 //  2. swq_mfma_kernel: f16 MFMA 32x32x16 with float32 accumulators over the
 //     H columns (packed codes, dequantized in registers) and then the extra
 //     columns (precomputed binary16 rows); epilogue 2^(e + k), then
@@ -160,7 +160,9 @@ __device__ __forceinline__ void prep_x_row(const PrepParams& p, int m) {
 //    wholly inside or outside it);
 //  - for every K-step (32 inputs) of its groups below H, the scale-tile word
 //    (s 2^-k, s 2^-k) in binary16 of that K-step's group (binary16 scales:
-//    split_scale(s 2^-k), the two parts of two MFMA planes);
+//    split_scale(s 2^-k), the two parts of two MFMA planes): through LDS,
+//    where the block stores its features' words as whole 16-byte pieces
+//    (see kPrepWordsLds), else one store per word;
 //  - (slot 0) k itself, for the MFMA kernel's epilogue.
 // With k_only (the matrix-vector path) only k is written.  The MFMA kernel
 // never reads scale-tile words of K-steps past H or of columns past the rows,
@@ -191,6 +193,21 @@ __device__ __forceinline__ RowSpec row_spec(const PrepParams& p, int mat) {
 // (indices clamped into the row).
 __device__ __forceinline__ void load_slot(const RowSpec& r, int64_t n, int lg_g0, int ngroups, int slot,
                                           uint16_t (&sv)[8], uint16_t (&bv)[8]) {
+  if (lg_g0 == r.lg_gs && 8 * slot + 8 <= ngroups) {   // eight whole groups of the row, one load each
+    const uint16_t* ps = r.S + n * r.ng + 8 * slot;
+    const uint16_t* pb = r.B + n * r.ng + 8 * slot;
+    if ((((uintptr_t)ps | (uintptr_t)pb) & 15) == 0) {
+      const u32x4 vs = *reinterpret_cast<const u32x4*>(ps), vb = *reinterpret_cast<const u32x4*>(pb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[2 * j] = (uint16_t)(vs[j] & 0xFFFFu);
+        sv[2 * j + 1] = (uint16_t)(vs[j] >> 16);
+        bv[2 * j] = (uint16_t)(vb[j] & 0xFFFFu);
+        bv[2 * j + 1] = (uint16_t)(vb[j] >> 16);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int G = min(8 * slot + j, ngroups - 1);
@@ -210,10 +227,17 @@ __device__ __forceinline__ float slot_max(const RowSpec& r, int ngroups, int slo
   return m;
 }
 
-// The slot's extra-column entries and scale-tile words (see above).
-__device__ __forceinline__ void store_slot(const PrepParams& p, const RowSpec& r, int mat, int64_t n, int lg_g0,
-                                           int ngroups, int slot, int k, const uint16_t (&sv)[8],
-                                           const uint16_t (&bv)[8]) {
+// The scale-tile word of g0-group j of a slot: (s 2^-k, s 2^-k) in binary16,
+// or with binary16 scales split_scale(s 2^-k).
+__device__ __forceinline__ uint32_t scale_word(const RowSpec& r, int k, uint16_t sv) {
+  const float sk = ldexpf(act_to_f32(sv, r.act), -k);
+  const _Float16 hs = (_Float16)sk;
+  return r.act == kActF16 ? as_u32(split_scale(sk)) : as_u32((f16x2){hs, hs});
+}
+
+// The slot's extra-column entries (see above).
+__device__ __forceinline__ void store_ext(const PrepParams& p, const RowSpec& r, int mat, int64_t n, int ngroups,
+                                          int slot, int k, const uint16_t (&sv)[8], const uint16_t (&bv)[8]) {
   f16x8 h[3];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -233,14 +257,18 @@ __device__ __forceinline__ void store_slot(const PrepParams& p, const RowSpec& r
     const int off = 48 * slot + 16 * q;
     if (off < p.kext * 2) *reinterpret_cast<f16x8*>(row + off) = h[q];
   }
-  // scale-tile words: K-steps (8 slot + j) g0/32 + u, u < g0/32, of group sv[j]
+}
+
+// The slot's scale-tile words, one store per K-step (K-steps (8 slot + j)
+// g0/32 + u, u < g0/32, take group sv[j]); rows whose block cannot gather
+// its words in LDS (see prep_weight_rows).
+__device__ __forceinline__ void store_slot_words(const PrepParams& p, const RowSpec& r, int mat, int64_t n,
+                                                 int lg_g0, int slot, int k, const uint16_t (&sv)[8]) {
   const int s_main = p.H >> 5, per = 1 << (lg_g0 - 5);
   uint32_t* tile = p.scl + (n >> 7) * (int64_t)p.nss * kScaleTileWords + mat * kScaleTileCols + (n & 127);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float sk = ldexpf(act_to_f32(sv[j], r.act), -k);
-    const _Float16 hs = (_Float16)sk;
-    const uint32_t word = r.act == kActF16 ? as_u32(split_scale(sk)) : as_u32((f16x2){hs, hs});
+    const uint32_t word = scale_word(r, k, sv[j]);
     const int t0 = (8 * slot + j) * per;
     for (int u = 0; u < per; ++u) {
       const int t = t0 + u;
@@ -258,19 +286,29 @@ __host__ __device__ inline int prep_row_lg(int kext) {
   return lg;
 }
 
+// Scale-tile words gathered per block: with one slot per thread (2^lg >=
+// the slots of a row) and 2^lg <= 32, the block's 256 >> lg rows are
+// C = 128 >> lg consecutive output features of both matrices, and its words
+// (2 H/g0 C, at most kPrepWordsLds) meet in LDS as [matrix][g0-group][C];
+// after a barrier the block stores them per K-step as 16-byte pieces of four
+// features, C * 4 contiguous bytes per (K-step, matrix).
+constexpr int kPrepWordsLds = 2048;
+
 __device__ __forceinline__ void prep_weight_rows(const PrepParams& p, int64_t idx) {
   const int lg = prep_row_lg(p.kext);
   const int c = (int)(idx & ((1 << lg) - 1));
   const int64_t pair = idx >> lg;
   const int64_t n = pair >> 1;
   const int mat = (int)(pair & 1);
-  if (n >= p.I) return;                                 // whole rows: the lanes of a row leave together
-  const bool live = n < (mat ? p.I_u : p.I);            // up rows past I_u: none (k = 0)
   const RowSpec r = row_spec(p, mat);
   const int lg_g0 = __builtin_ctz(p.g0);
   const int ngroups = p.H >> lg_g0;
   const int per_row = (p.kext + 23) / 24;
   const int step = 1 << lg;
+  const int C = 128 >> lg;
+  const bool gather = !p.k_only && per_row <= step && lg <= 5 && 2 * ngroups * C <= kPrepWordsLds;
+  if (!gather && n >= p.I) return;                      // whole rows: the lanes of a row leave together
+  const bool live = n < p.I && n < (mat ? p.I_u : p.I); // up rows past I_u: none (k = 0)
   float vmax = 0.0f;
   int k;
   if (per_row <= step) {                                // one slot per thread: keep it in registers
@@ -282,7 +320,39 @@ __device__ __forceinline__ void prep_weight_rows(const PrepParams& p, int64_t id
     }
     for (int off = 1; off < step; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
     k = row_exponent_k(vmax);
-    if (mine && !p.k_only) store_slot(p, r, mat, n, lg_g0, ngroups, c, k, sv, bv);
+    if (mine && !p.k_only) {
+      store_ext(p, r, mat, n, ngroups, c, k, sv, bv);
+      if (!gather) store_slot_words(p, r, mat, n, lg_g0, c, k, sv);
+    }
+    if (gather) {
+      __shared__ __align__(16) uint32_t words[kPrepWordsLds];
+      const int64_t nb0 = (idx - threadIdx.x) >> (lg + 1);   // the block's first feature (a multiple of C)
+      const int cl = (int)(n - nb0);
+#ifdef SWQ_LDS_POISON
+      lds_poison(words, sizeof(words), kPoisonFloat);
+      __syncthreads();
+#endif
+      if (c < per_row) {                                 // zeros for rows past I (or I_u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (8 * c + j < ngroups) words[(mat * ngroups + 8 * c + j) * C + cl] = mine ? scale_word(r, k, sv[j]) : 0u;
+      }
+      __syncthreads();
+      const int s_main = p.H >> 5, per = 1 << (lg_g0 - 5);
+      const int lq = 5 - lg;                             // log2 of the 16-byte pieces per row of C words
+      for (int i = threadIdx.x; i < (2 * ngroups) << lq; i += blockDim.x) {
+        const int q = i & ((1 << lq) - 1), mg = i >> lq;  // piece, (matrix, g0-group)
+        const int m = mg >= ngroups ? 1 : 0, G = mg - m * ngroups;
+        const int64_t n4 = nb0 + 4 * q;
+        if (n4 >= p.I) continue;                         // (pieces past I lie in the last tile of 128)
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&words[mg * C + 4 * q]);
+        uint32_t* tile = p.scl + (n4 >> 7) * (int64_t)p.nss * kScaleTileWords + m * kScaleTileCols + (n4 & 127);
+        for (int u = 0; u < per; ++u) {
+          const int t = G * per + u;
+          if (t < s_main) *reinterpret_cast<u32x4*>(tile + (int64_t)(t >> 2) * kScaleTileWords + (t & 3) * 2 * kScaleTileCols) = v;
+        }
+      }
+    }
   } else {
     for (int slot = c; live && slot < per_row; slot += step) {
       uint16_t sv[8], bv[8];
@@ -294,10 +364,11 @@ __device__ __forceinline__ void prep_weight_rows(const PrepParams& p, int64_t id
     for (int slot = c; live && !p.k_only && slot < per_row; slot += step) {
       uint16_t sv[8], bv[8];
       load_slot(r, n, lg_g0, ngroups, slot, sv, bv);
-      store_slot(p, r, mat, n, lg_g0, ngroups, slot, k, sv, bv);
+      store_ext(p, r, mat, n, ngroups, slot, k, sv, bv);
+      store_slot_words(p, r, mat, n, lg_g0, slot, k, sv);
     }
   }
-  if (c == 0) p.kexp[(int64_t)mat * p.I + n] = k;
+  if (c == 0 && n < p.I) p.kexp[(int64_t)mat * p.I + n] = k;
 }
 
 // Blocks [0, M): x rows.  Then the weight rows, 2^lg threads each (whole
