@@ -30,6 +30,21 @@
 
 using namespace swq;
 
+// Compute units of the current device (cached per device).
+int swq::device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
 namespace {
 
 constexpr int kDefaultThreshold = kGemvMaxM + 1;
@@ -146,21 +161,6 @@ int choose_mfma_config(int64_t M, int64_t I) {
   }
   const int64_t tiles256 = ((M + 255) / 256) * ((I + 127) / 128);
   return tiles256 >= 512 ? 0 : 1;
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  cache[dev] = cus;
-  return cus;
 }
 
 // With 256 x 128 tiles (one per CU at a time), a partly filled last round

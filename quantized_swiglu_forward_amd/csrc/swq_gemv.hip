@@ -546,12 +546,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kSkinnyMaxWaves = 16;
 
-template <int BITS_G, int BITS_U, int RT>
+template <int BITS_G, int BITS_U, int RT, int CT>
 struct SkinnyChunk {
-  // codes as loaded (the line-friendly lane order, 2-bit codes not yet
-  // spread), then in the MFMA's order
-  u32x4 cg[kCodeWidth<BITS_G> / 4], cu[kCodeWidth<BITS_U> / 4], x[RT][4];
-  uint32_t sg, bg, su, bu;   // raw 16-bit bits, converted where used (after every load is issued)
+  // codes of each column tile as loaded (the line-friendly lane order, 2-bit
+  // codes not yet spread), then in the MFMA's order
+  u32x4 cg[CT][kCodeWidth<BITS_G> / 4], cu[CT][kCodeWidth<BITS_U> / 4], x[RT][4];
+  uint32_t sg[CT], bg[CT], su[CT], bu[CT];   // raw 16-bit bits, converted where used (after every load is issued)
   float sx[RT];              // x converted by the wave: the lane's sum of x' (float32 adds)
   bool live;
 };
@@ -561,28 +561,34 @@ struct SkinnyChunk {
 // column rl, where the window [w, w + 8) is the block of 8 groups, aligned to
 // 8, around the quad's first input; it holds every group of those 128 (or
 // 256) inputs.
+template <int CT>
 struct SbWindow {
-  uint32_t v[4];   // sg, bg, su, bu
-  int wg, wu;      // window starts (gate, up)
+  uint32_t v[CT][4];   // per column tile: sg, bg, su, bu
+  int wg, wu;          // window starts (gate, up)
 };
 
 // RT: row tiles of 16 (M <= 16 RT = 1; M <= 32 RT = 2, whose second tile of x'
 // and accumulators need twice the registers: half the waves per SIMD).  Q2:
 // two chunk quads in flight per wave (codes of at most 4 bits, x' from the
-// prep kernel), with half the waves per SIMD.
-template <int BITS_G, int BITS_U, int XS, int RT, bool Q2, int ACT>
+// prep kernel), with half the waves per SIMD.  CT: column tiles of 16 per
+// block (CT = 2 with x converted by the waves, one chunk quad per wave and
+// narrow codes: one conversion of x serves 32 columns, for grids of more
+// tiles than CUs).
+template <int BITS_G, int BITS_U, int XS, int RT, bool Q2, int ACT, int CT>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
   constexpr bool STAGE = XS == kXStage, SELF = XS == kXSelf;
   static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, x' in registers");
   static_assert(!SELF || RT == 1, "x converted by the waves: one row tile");
+  static_assert(CT == 1 || (CT == 2 && SELF && !Q2 && BITS_G <= 4 && BITS_G == BITS_U),
+                "two column tiles: x converted by the waves, one quad per wave, narrow codes");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = blockDim.x >> 6;
   const int r = lane & 15, h = lane >> 4;             // A row / B and D column; K-slot group
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int col = (int)n0 + r;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * CT;
+  const int col = (int)n0 + r;                        // (column tile 0; tile c: col + 16 c)
   // x' row of this lane per tile: from the prep kernel, a row past M reads
   // zeros (see load); from LDS, clamped to the last row
   bool rowok[RT];
@@ -593,8 +599,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     rowl[t] = min(16 * t + r, p.M - 1);
   }
   const int nchunk = p.H >> 5;
-  // the block's 16 columns through buffer descriptors (columns past I read zeros)
-  const int ncols = (int)min((int64_t)16, (int64_t)p.I - n0);
+  // the block's 16 CT columns through buffer descriptors (columns past I read zeros)
+  const int ncols = (int)min((int64_t)16 * CT, (int64_t)p.I - n0);
   const MatBufs mg = mat_bufs(p.wg, p.sg, p.bg, n0, ncols, p.H, BITS_G, p.gs_g);
   const int ncols_u = (int)max((int64_t)0, min((int64_t)ncols, (int64_t)p.I_u - n0));
   const MatBufs mu = mat_bufs(p.wu, p.su, p.bu, n0, ncols_u, p.H, BITS_U, p.gs_u);
@@ -644,7 +650,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // SELF: the waves' regions (skinny_self_region bytes each), launched as dynamic LDS
   extern __shared__ u32x4 swq_dyn[];
   constexpr int kSelfChunks = Q2 ? 8 : 4;   // chunks per wave
-  const int rb = SELF ? skinny_self_region(p.M, kSelfChunks) : 0;
+  const int rb = SELF ? skinny_self_region(p.M, kSelfChunks, CT) : 0;
   unsigned char* const xreg = reinterpret_cast<unsigned char*>(swq_dyn) + w * rb;
 
   // Row exponents k of the block's 16 columns of both matrices
@@ -701,13 +707,15 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // this lane's column exponents: from the prep kernel (x' staged there),
   // else from the block's own pass, after a barrier.  Both in one register
   // (each in [-200, 200]): gate in the low half, up in the high half.
-  uint32_t kpack = 0;
-  auto set_k = [&](int kg_, int ku_) { kpack = ((uint32_t)kg_ & 0xFFFFu) | ((uint32_t)ku_ << 16); };
-  auto k_gate = [&]() { return (int)(int16_t)(kpack & 0xFFFFu); };
-  auto k_up = [&]() { return (int)kpack >> 16; };
+  uint32_t kpack[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) kpack[ct] = 0;
+  auto set_k = [&](int ct, int kg_, int ku_) { kpack[ct] = ((uint32_t)kg_ & 0xFFFFu) | ((uint32_t)ku_ << 16); };
+  auto k_gate = [&](int ct) { return (int)(int16_t)(kpack[ct] & 0xFFFFu); };
+  auto k_up = [&](int ct) { return (int)kpack[ct] >> 16; };
   if constexpr (XS == kXPrep) {
     const int nquad_ = (nchunk + 3) >> 2;
-    if (nquad_ > (Q2 ? 2 : 1) * nw && col < p.I) set_k(p.kexp[col], p.kexp[p.I + col]);
+    if (nquad_ > (Q2 ? 2 : 1) * nw && col < p.I) set_k(0, p.kexp[col], p.kexp[p.I + col]);
   }
   auto row_k_read = [&]() {
     float mg_ = 0.0f, mu_ = 0.0f;
@@ -715,51 +723,57 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       mg_ = fmaxf(mg_, kred[ww][r]);
       mu_ = fmaxf(mu_, kred[ww][16 + r]);
     }
-    set_k(row_exponent_k(mg_), row_exponent_k(mu_));
+    set_k(0, row_exponent_k(mg_), row_exponent_k(mu_));
   };
 
   // the window of groups around quad `quad` (issue before the quad's codes)
-  auto load_sb = [&](int quad, SbWindow& sw) {
+  auto load_sb = [&](int quad, SbWindow<CT>& sw) {
     sw.wg = ((128 * quad) >> mg.lg_gs) & ~7;
     sw.wu = ((128 * quad) >> mu.lg_gs) & ~7;
-    const int og = (rl * mg.ng + sw.wg + 2 * hl) * 2, ou = (rl * mu.ng + sw.wu + 2 * hl) * 2;
-    if (sb_dword) {
-      sw.v[0] = __builtin_amdgcn_raw_buffer_load_b32(mg.s, og, 0, 0);
-      sw.v[1] = __builtin_amdgcn_raw_buffer_load_b32(mg.b, og, 0, 0);
-      sw.v[2] = __builtin_amdgcn_raw_buffer_load_b32(mu.s, ou, 0, 0);
-      sw.v[3] = __builtin_amdgcn_raw_buffer_load_b32(mu.b, ou, 0, 0);
-    } else {
-      auto two = [](const __amdgpu_buffer_rsrc_t& rs, int off) {
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0) |
-               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off + 2, 0, 0) << 16);
-      };
-      sw.v[0] = two(mg.s, og);
-      sw.v[1] = two(mg.b, og);
-      sw.v[2] = two(mu.s, ou);
-      sw.v[3] = two(mu.b, ou);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int og = ((16 * ct + rl) * mg.ng + sw.wg + 2 * hl) * 2, ou = ((16 * ct + rl) * mu.ng + sw.wu + 2 * hl) * 2;
+      if (sb_dword) {
+        sw.v[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(mg.s, og, 0, 0);
+        sw.v[ct][1] = __builtin_amdgcn_raw_buffer_load_b32(mg.b, og, 0, 0);
+        sw.v[ct][2] = __builtin_amdgcn_raw_buffer_load_b32(mu.s, ou, 0, 0);
+        sw.v[ct][3] = __builtin_amdgcn_raw_buffer_load_b32(mu.b, ou, 0, 0);
+      } else {
+        auto two = [](const __amdgpu_buffer_rsrc_t& rs, int off) {
+          return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0) |
+                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off + 2, 0, 0) << 16);
+        };
+        sw.v[ct][0] = two(mg.s, og);
+        sw.v[ct][1] = two(mg.b, og);
+        sw.v[ct][2] = two(mu.s, ou);
+        sw.v[ct][3] = two(mu.b, ou);
+      }
     }
   };
   // this lane's scale and bias (chunk 4 quad + h of column r) from the window
-  auto pick_sb = [&](const SbWindow& sw, int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto pick_sb = [&](const SbWindow<CT>& sw, int quad, SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     const int c = 4 * quad + h;
     const int ig = ((32 * c) >> mg.lg_gs) - sw.wg, iu = ((32 * c) >> mu.lg_gs) - sw.wu;   // in [0, 8)
     const int ag = (4 * r + (ig >> 1)) * 4, au = (4 * r + (iu >> 1)) * 4;
-    const uint32_t s_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[0]);
-    const uint32_t b_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[1]);
-    const uint32_t s_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[2]);
-    const uint32_t b_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[3]);
-    d.sg = (ig & 1) ? s_g >> 16 : s_g & 0xFFFFu;
-    d.bg = (ig & 1) ? b_g >> 16 : b_g & 0xFFFFu;
-    d.su = (iu & 1) ? s_u >> 16 : s_u & 0xFFFFu;
-    d.bu = (iu & 1) ? b_u >> 16 : b_u & 0xFFFFu;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const uint32_t s_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[ct][0]);
+      const uint32_t b_g = (uint32_t)__builtin_amdgcn_ds_bpermute(ag, (int)sw.v[ct][1]);
+      const uint32_t s_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[ct][2]);
+      const uint32_t b_u = (uint32_t)__builtin_amdgcn_ds_bpermute(au, (int)sw.v[ct][3]);
+      d.sg[ct] = (ig & 1) ? s_g >> 16 : s_g & 0xFFFFu;
+      d.bg[ct] = (ig & 1) ? b_g >> 16 : b_g & 0xFFFFu;
+      d.su[ct] = (iu & 1) ? s_u >> 16 : s_u & 0xFFFFu;
+      d.bu[ct] = (iu & 1) ? b_u >> 16 : b_u & 0xFFFFu;
+    }
   };
 
-  auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto load = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     const int c = 4 * quad + h;
     d.live = c < nchunk;
-    // codes in the load order: chunk 4 quad + hl of column rl (chunk 0 past the end)
+    // codes in the load order: chunk 4 quad + hl of column rl of each column
+    // tile (chunk 0 past the end)
     const int cl = 4 * quad + hl < nchunk ? 4 * quad + hl : 0;
-    const int og = (rl * mg.rw + cl * BITS_G) * 4, ou = (rl * mu.rw + cl * BITS_U) * 4;
     auto codes = [](const __amdgpu_buffer_rsrc_t& rs, int off, u32x4* dst, auto bits_tag) {
       constexpr int BITS = decltype(bits_tag)::value;
       if constexpr (BITS == 2) {
@@ -770,8 +784,12 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         for (int i = 0; i < BITS / 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 2);
       }
     };
-    codes(mg.w, og, d.cg, std::integral_constant<int, BITS_G>{});
-    codes(mu.w, ou, d.cu, std::integral_constant<int, BITS_U>{});
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int og = ((16 * ct + rl) * mg.rw + cl * BITS_G) * 4, ou = ((16 * ct + rl) * mu.rw + cl * BITS_U) * 4;
+      codes(mg.w, og, d.cg[ct], std::integral_constant<int, BITS_G>{});
+      codes(mu.w, ou, d.cu[ct], std::integral_constant<int, BITS_U>{});
+    }
     if constexpr (XS == kXPrep) {
       // one contiguous kilobyte per instruction; a row past M or a chunk past
       // H reads zeros (offset past the buffer's range)
@@ -788,7 +806,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     // every load of the chunk is in flight before the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto load_x_lds = [&](int quad, SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     const int c = min(4 * quad + h, nchunk - 1);
 #pragma unroll
     for (int t = 0; t < RT; ++t)
@@ -848,14 +866,16 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     }
   };
 
-  f32x4 ag[RT], au[RT];
+  f32x4 ag[CT][RT], au[CT][RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    ag[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    au[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      ag[ct][t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      au[ct][t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
   // the codes into the MFMA's order (lane 16 h + r from lane 4 r + h)
-  auto arrange = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto arrange = [&](SkinnyChunk<BITS_G, BITS_U, RT, CT>& d, int ct) {
     auto move = [&](u32x4* cw, auto bits_tag) {
       constexpr int BITS = decltype(bits_tag)::value;
       if constexpr (BITS == 2) {
@@ -869,18 +889,20 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
           for (int j = 0; j < 4; ++j) cw[i][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm, (int)cw[i][j]);
       }
     };
-    move(d.cg, std::integral_constant<int, BITS_G>{});
-    move(d.cu, std::integral_constant<int, BITS_U>{});
+    move(d.cg[ct], std::integral_constant<int, BITS_G>{});
+    move(d.cu[ct], std::integral_constant<int, BITS_U>{});
   };
-  auto compute = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
-    arrange(d);
+  auto compute = [&](SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
+#pragma unroll
+   for (int ct = 0; ct < CT; ++ct) {
+    arrange(d, ct);
     // a chunk past the end gets zero scales and biases: its B operands vanish
     // (scaled by the column's 2^-k)
-    const int kg_ = k_gate(), ku_ = k_up();
-    const float sg = d.live ? ldexpf(act_to_f32((uint16_t)d.sg, ACT), -kg_) : 0.0f;
-    const float bg = d.live ? ldexpf(act_to_f32((uint16_t)d.bg, ACT), -kg_) : 0.0f;
-    const float su = d.live ? ldexpf(act_to_f32((uint16_t)d.su, ACT), -ku_) : 0.0f;
-    const float bu = d.live ? ldexpf(act_to_f32((uint16_t)d.bu, ACT), -ku_) : 0.0f;
+    const int kg_ = k_gate(ct), ku_ = k_up(ct);
+    const float sg = d.live ? ldexpf(act_to_f32((uint16_t)d.sg[ct], ACT), -kg_) : 0.0f;
+    const float bg = d.live ? ldexpf(act_to_f32((uint16_t)d.bg[ct], ACT), -kg_) : 0.0f;
+    const float su = d.live ? ldexpf(act_to_f32((uint16_t)d.su[ct], ACT), -ku_) : 0.0f;
+    const float bu = d.live ? ldexpf(act_to_f32((uint16_t)d.bu[ct], ACT), -ku_) : 0.0f;
     constexpr bool split = ACT == kActF16;
     const f16x2 sg2 = split ? split_scale(sg) : (f16x2){(_Float16)sg, (_Float16)sg};
     const f16x2 su2 = split ? split_scale(su) : (f16x2){(_Float16)su, (_Float16)su};
@@ -889,8 +911,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       f16x8 a[RT];
 #pragma unroll
       for (int t = 0; t < RT; ++t) a[t] = __builtin_bit_cast(f16x8, d.x[t][kb]);
-      block_mfma.template operator()<BITS_G>(d.cg, sg2, split, kb, a, ag);
-      block_mfma.template operator()<BITS_U>(d.cu, su2, split, kb, a, au);
+      block_mfma.template operator()<BITS_G>(d.cg[ct], sg2, split, kb, a, ag[ct]);
+      block_mfma.template operator()<BITS_U>(d.cu[ct], su2, split, kb, a, au[ct]);
     }
     // bias term sum_k x'_k c of this chunk (c = b + z s split into two
     // binary16 parts, c_hi + c_lo; every product exact):
@@ -906,8 +928,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       const float sx = d.sx[0];
       const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
       const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
-      ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[0], 0, 0, 0);
-      au[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[0], 0, 0, 0);
+      ag[ct][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[ct][0], 0, 0, 0);
+      au[ct][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[ct][0], 0, 0, 0);
     } else {
       // x' staged elsewhere: the block's A operands once more against
       // B = c_hi and B = c_lo in every K slot of the lane's chunk (MFMAs
@@ -919,12 +941,13 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const f16x8 a = __builtin_bit_cast(f16x8, d.x[t][kb]);
-          ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgh, ag[t], 0, 0, 0);
-          au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, buh, au[t], 0, 0, 0);
-          ag[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgl, ag[t], 0, 0, 0);
-          au[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bul, au[t], 0, 0, 0);
+          ag[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgh, ag[ct][t], 0, 0, 0);
+          au[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, buh, au[ct][t], 0, 0, 0);
+          ag[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bgl, ag[ct][t], 0, 0, 0);
+          au[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bul, au[ct][t], 0, 0, 0);
         }
     }
+   }
   };
 
   // chunk quads w, w + nw, ... (Q2: 2w and 2w + 1 in one pass, then 2(w + nw), ...).
@@ -961,7 +984,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // ... chunk slot 4 qs + h of row r back, as the MFMA's A operand (bf16
   // bits).  A lane of a row past M reads row M - 1 again: A's rows past M
   // only reach D's rows past M, which are never stored.
-  auto read_x = [&](int qs, SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto read_x = [&](int qs, SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     const int sl = 4 * qs + h;
     const int m = rowl[0];
 #pragma unroll
@@ -970,14 +993,14 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   };
   // loads the wave issues after its x: the windows of groups (at least 4)
   // and the codes of its quads
-  constexpr int kLoadsAfterX = 4 + (Q2 ? 2 : 1) * ((BITS_G == 8 ? 2 : 1) + (BITS_U == 8 ? 2 : 1));
+  constexpr int kLoadsAfterX = CT * (4 + (Q2 ? 2 : 1) * ((BITS_G == 8 ? 2 : 1) + (BITS_U == 8 ? 2 : 1)));
 
   // SELF: the largest bf16 magnitude of each of this lane's rows (packed
   // halves, folded at the end), over the wave's chunks ...
   uint32_t xam[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) xam[t] = 0;
-  auto x_amax = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto x_amax = [&](const SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1019,7 +1042,7 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // block holds inputs j and j + 4), in place, with the lane's sum of x'
   // for the bias term (float32 adds of x 2^-e, which is x' wherever binary16
   // holds it exactly; done here, while the weights are still in flight)
-  auto x_convert = [&](SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  auto x_convert = [&](SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       d.sx[t] = 0.0f;
@@ -1043,25 +1066,34 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       }
     }
   };
-  float cmax_g = 0.0f, cmax_u = 0.0f;
-  auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT>& d) {
+  float cmax_g[CT], cmax_u[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) cmax_g[ct] = cmax_u[ct] = 0.0f;
+  auto chunk_k = [&](const SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     if (!d.live) return;
-    cmax_g = fmaxf(cmax_g, group_term_max(act_to_f32((uint16_t)d.sg, ACT), act_to_f32((uint16_t)d.bg, ACT),
-                                          CodeOffset<BITS_G>::z, kPlaneMax<BITS_G>));
-    cmax_u = fmaxf(cmax_u, group_term_max(act_to_f32((uint16_t)d.su, ACT), act_to_f32((uint16_t)d.bu, ACT),
-                                          CodeOffset<BITS_U>::z, kPlaneMax<BITS_U>));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      cmax_g[ct] = fmaxf(cmax_g[ct], group_term_max(act_to_f32((uint16_t)d.sg[ct], ACT), act_to_f32((uint16_t)d.bg[ct], ACT),
+                                                    CodeOffset<BITS_G>::z, kPlaneMax<BITS_G>));
+      cmax_u[ct] = fmaxf(cmax_u[ct], group_term_max(act_to_f32((uint16_t)d.su[ct], ACT), act_to_f32((uint16_t)d.bu[ct], ACT),
+                                                    CodeOffset<BITS_U>::z, kPlaneMax<BITS_U>));
+    }
   };
   auto chunk_k_wave = [&]() {
-    cmax_g = fmaxf(cmax_g, __shfl_xor(cmax_g, 16));
-    cmax_g = fmaxf(cmax_g, __shfl_xor(cmax_g, 32));
-    cmax_u = fmaxf(cmax_u, __shfl_xor(cmax_u, 16));
-    cmax_u = fmaxf(cmax_u, __shfl_xor(cmax_u, 32));
-    set_k(row_exponent_k(cmax_g), row_exponent_k(cmax_u));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float g = cmax_g[ct], u = cmax_u[ct];
+      g = fmaxf(g, __shfl_xor(g, 16));
+      g = fmaxf(g, __shfl_xor(g, 32));
+      u = fmaxf(u, __shfl_xor(u, 16));
+      u = fmaxf(u, __shfl_xor(u, 32));
+      set_k(ct, row_exponent_k(g), row_exponent_k(u));
+    }
   };
   if constexpr (STAGE) {
     // the first quad's weights are in flight while the block builds x'
-    SkinnyChunk<BITS_G, BITS_U, RT> d;
-    SbWindow sw;
+    SkinnyChunk<BITS_G, BITS_U, RT, CT> d;
+    SbWindow<CT> sw;
     if (w < nquad) {
       load_sb(w, sw);
       load(w, d);
@@ -1116,8 +1148,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     }
   } else if constexpr (!Q2) {
     if (single) {
-      SkinnyChunk<BITS_G, BITS_U, RT> d;
-      SbWindow sw;
+      SkinnyChunk<BITS_G, BITS_U, RT, CT> d;
+      SbWindow<CT> sw;
       if (w < nquad) {
         if constexpr (SELF) dma_x(4 * w);
         load_sb(w, sw);
@@ -1138,8 +1170,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       if (w < nquad) compute(d);
     } else if constexpr (!SELF) {   // (SELF is launched for one pass only)
       for (int q0 = w; q0 < nquad; q0 += nw) {
-        SkinnyChunk<BITS_G, BITS_U, RT> d;
-        SbWindow sw;
+        SkinnyChunk<BITS_G, BITS_U, RT, CT> d;
+        SbWindow<CT> sw;
         load_sb(q0, sw);
         load(q0, d);
         pick_sb(sw, q0, d);
@@ -1150,8 +1182,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
     // two adjacent chunk quads in flight per wave, half the waves (a quad
     // past the end loads chunk 0 with zero scales and adds nothing)
     if (single) {
-      SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
-      SbWindow sw;   // one window holds both quads' groups
+      SkinnyChunk<BITS_G, BITS_U, RT, CT> d0, d1;
+      SbWindow<CT> sw;   // one window holds both quads' groups
       if (2 * w < nquad) {
         if constexpr (SELF) dma_x(8 * w);
         load_sb(2 * w, sw);
@@ -1183,8 +1215,8 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
       }
     } else if constexpr (!SELF) {
       for (int pq = w; 2 * pq < nquad; pq += nw) {   // adjacent quads: their code rows share lines
-        SkinnyChunk<BITS_G, BITS_U, RT> d0, d1;
-        SbWindow sw;
+        SkinnyChunk<BITS_G, BITS_U, RT, CT> d0, d1;
+        SbWindow<CT> sw;
         load_sb(2 * pq, sw);
         load(2 * pq, d0);
         load(2 * pq + 1, d1);
@@ -1200,11 +1232,12 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
   // column and x row; one scaling, so no intermediate leaves the range of
   // the sums themselves); D element j of lane l is row 4 (l / 16) + j,
   // column l % 16
-  {
-    const int kg_ = k_gate(), ku_ = k_up();
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int kg_ = k_gate(ct), ku_ = k_up(ct);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      f32x4 a = ag[t], b = au[t];
+      f32x4 a = ag[ct][t], b = au[ct][t];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 16 * t + 4 * h + j;
@@ -1215,23 +1248,25 @@ __attribute__((amdgpu_waves_per_eu(Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4)
         a[j] = ldexpf(a[j], kg_ + e);
         b[j] = ldexpf(b[j], ku_ + e);
       }
-      red_at(w, 2 * t)[lane] = a;
-      red_at(w, 2 * t + 1)[lane] = b;
+      red_at(w, 2 * (ct * RT + t))[lane] = a;
+      red_at(w, 2 * (ct * RT + t) + 1)[lane] = b;
     }
   }
   __syncthreads();
-  // element j of D (row 16 t + 4 h + j) of tile t: wave 4 t + j sums it over
-  // the waves (in wave order) and runs its epilogue, so the 4 RT epilogues
-  // of a lane run on different waves at once
-  for (int k = w; k < 4 * RT; k += nw) {
-    const int t = k >> 2, j = k & 3;
+  // element j of D (row 16 t + 4 h + j) of row tile t and column tile ct:
+  // wave 4 (ct RT + t) + j sums it over the waves (in wave order) and runs
+  // its epilogue, so the 4 RT CT epilogues of a lane run on different waves
+  // at once
+  for (int k = w; k < 4 * RT * CT; k += nw) {
+    const int tt = k >> 2, j = k & 3;                 // tt = ct RT + t
+    const int t = tt % RT, c16 = col + 16 * (tt / RT);
     float g = 0.0f, u = 0.0f;
     for (int ww = 0; ww < nw; ++ww) {
-      g += red_at(ww, 2 * t)[lane][j];
-      u += red_at(ww, 2 * t + 1)[lane][j];
+      g += red_at(ww, 2 * tt)[lane][j];
+      u += red_at(ww, 2 * tt + 1)[lane][j];
     }
     const int m = 16 * t + 4 * h + j;
-    if (m < p.M && col < p.I) store_out(p, m, col, g, u, ACT);
+    if (m < p.M && c16 < p.I) store_out(p, m, c16, g, u, ACT);
   }
 }
 
@@ -1326,7 +1361,10 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
   // rows take several passes); x converted by the waves themselves (M <= 16):
   // two quads whenever the codes allow, which doubles the row one pass covers
   const bool narrow = bits_g <= 4 && bits_u <= 4 && bits_g == bits_u;
-  if (xs == kXSelf) *two = narrow;
+  // (SWIGLU_Q_SKINNY_QUADS=1, read on every call: one quad per wave, for
+  // comparisons and tests)
+  const char* q = getenv("SWIGLU_Q_SKINNY_QUADS");
+  if (xs == kXSelf) *two = narrow && !(q && q[0] == '1' && q[1] == 0);
   else *two = narrow && xs == kXPrep && (M > 16 || H <= 2048);
   const int per = *two ? (quads + 1) / 2 : quads;
   *waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
@@ -1363,6 +1401,22 @@ bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
 }
 #endif
 
+// Column tiles per block of the few-row kernel: two (with one chunk quad per
+// wave, the row in one pass of at most kSkinnyMaxWaves waves) when each wave
+// converts x itself, the codes are narrow, and the 16-column tiles are more
+// than the device's CUs but at most twice as many: one round of blocks of 32
+// columns, each conversion of x serving both tiles, instead of some CUs
+// taking a second block of 16 (measured at H = 2048: I = 5632, M = 8 / 16:
+// 9.04 / 10.12 -> 8.59 / 9.21 us; one tile stays ahead at most one round of
+// tiles and at 3.5 rounds).  SWIGLU_Q_SKINNY_CT=1 or 2 (read on every call)
+// overrides where two are possible, for comparisons and tests.
+static int skinny_ct(int64_t I, int xs, bool narrow, int quads) {
+  if (xs != kXSelf || !narrow || quads > kSkinnyMaxWaves) return 1;
+  if (const char* s = getenv("SWIGLU_Q_SKINNY_CT"); s && (s[0] == '1' || s[0] == '2') && s[1] == 0) return s[0] - '0';
+  const int64_t tiles = (I + 15) / 16, cus = device_cus();
+  return tiles > cus && tiles <= 2 * cus ? 2 : 1;
+}
+
 template <int BG, int BU, int ACT>
 static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   const int lpc = gemv_lanes_per_column(p.H);
@@ -1396,16 +1450,28 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
   if (xs == kXPrep && (p.xa == nullptr || (p.kexp == nullptr && skinny_needs_kexp(p.M, p.H, BG, BU))))
     return hipErrorInvalidValue;
   if (xs == kXStage && (int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
-  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4) : 0;
+  const int ct = skinny_ct(p.I, xs, kNarrow, quads);
+  if (ct == 2) {   // one quad per wave
+    two = false;
+    waves = quads;
+  }
+  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4, ct) : 0;
   if (xs == kXSelf && (p.M > 16 || quads > (two ? 2 : 1) * waves || lds > kSkinnySelfMaxLds))
     return hipErrorInvalidValue;   // one pass, one row tile, regions within bounds
-  const dim3 g((p.I + 15) / 16), b(64 * waves);
+  const dim3 g((p.I + 16 * ct - 1) / (16 * ct)), b(64 * waves);
   auto go = [&](auto xs_tag, auto two_tag) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr bool TWO = decltype(two_tag)::value;
-    if constexpr (XS == kXSelf) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT>), g, b, lds, stream, p);
-    else if (p.M <= 16) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO, ACT>), g, b, 0, stream, p);
+    if constexpr (XS == kXSelf && kNarrow && !TWO) {
+      if (ct == 2) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 2>), g, b, lds, stream, p);
+      else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
+    } else if constexpr (XS == kXSelf) {
+      hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
+    } else if (p.M <= 16) {
+      hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO, ACT, 1>), g, b, 0, stream, p);
+    }
   };
   using F = std::false_type;
   using T = std::true_type;

@@ -124,11 +124,12 @@ constexpr int kXPrep = 0, kXStage = 1, kXSelf = 2;
 constexpr int kSkinnyStageMax = 8192;
 // kXSelf (M <= 16): each wave's LDS region in bytes -- its chunks' rows of x
 // as loaded (64 bytes per chunk and row, written 1 KB per load instruction),
-// later its partial sums (2 KB) -- for `nch` chunks per wave; the block's
-// regions together stay within kSkinnySelfMaxLds.
-__host__ __device__ inline int skinny_self_region(int M, int nch) {
+// later its partial sums (2 KB per column tile) -- for `nch` chunks per wave
+// and `ct` column tiles per block; the block's regions together stay within
+// kSkinnySelfMaxLds.
+__host__ __device__ inline int skinny_self_region(int M, int nch, int ct = 1) {
   const int x = (nch * M + 15) / 16 * 1024;
-  return x > 2048 ? x : 2048;
+  return x > 2048 * ct ? x : 2048 * ct;
 }
 constexpr int kSkinnySelfMaxLds = 65536;
 // the matrix-vector kernel's several-row form (no staging pass): 2 <= M <=
@@ -161,6 +162,8 @@ template <int ACT>
 hipError_t launch_gemv_act(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
 // The few-row kernel's x source for a call of M rows (kXPrep, kXStage or kXSelf).
 int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u);
+// compute units of the current device (cached per device)
+int device_cus();
 // Whether the few-row kernel, fed x' by the prep kernel, needs the weight-row
 // exponents from the prep kernel's k-only rows (a row longer than one pass of
 // its waves); otherwise it takes them from the scales its first pass loads.

@@ -52,6 +52,32 @@ def skinny_x(source):
             os.environ["SWIGLU_Q_SKINNY_X"] = old
 
 
+@contextlib.contextmanager
+def skinny_ct(ct, quads=None):
+    """Column tiles per block of the few-row kernel: None (the library's
+    choice), 1 or 2 (SWIGLU_Q_SKINNY_CT; 2 applies where the waves convert x
+    and a row fits one pass of one chunk quad per wave, and implies one quad
+    per wave); ``quads=1`` also gives one tile one quad per wave
+    (SWIGLU_Q_SKINNY_QUADS).  Both are read on every call."""
+    import os
+    want = {"SWIGLU_Q_SKINNY_CT": None if ct is None else str(ct),
+            "SWIGLU_Q_SKINNY_QUADS": None if quads is None else str(quads)}
+    old = {k: os.environ.get(k) for k in want}
+    for k, v in want.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 def device_forward(prob, mode, path=None, dev=None, expect_path=None):
     """hidden on the GPU as a float64 numpy array [M, I]."""
     if dev is None:

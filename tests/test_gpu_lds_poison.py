@@ -3,7 +3,7 @@ same kernels, each filling its LDS with NaN bits (and 2^30 exponents) before
 use, so a kernel that read LDS it had not written would fail here.  One case
 per kernel and branch: the M = 1 kernel and its several-row form, the
 few-row kernel (x' converted by each wave, built in the block, from the
-prep kernel, two row tiles, rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
+prep kernel, two row tiles, two column tiles, rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
 column split, a partial last super-step), the linear and the whole MLP."""
 import os
 
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import quantized_swiglu_forward_amd as swq
-from gpu_helpers import check, skinny_x, device_forward, oracle_full, oracle_pairs, say
+from gpu_helpers import check, skinny_ct, skinny_x, device_forward, oracle_full, oracle_pairs, say
 from synth import make_custom, make_down, make_residual
 
 pytestmark = pytest.mark.gpu
@@ -54,6 +54,18 @@ def test_forward_under_poison(M, H, I, spec, path):
         with skinny_x(source):
             y = device_forward(p, mode, path)
         check(y, o, mode, f"poison M{M} H{H} I{I} x source {source}")
+
+
+@pytest.mark.parametrize("M,H,I", [(8, 2048, 1000), (5, 1024, 72)])
+def test_few_row_two_column_tiles_under_poison(M, H, I):
+    """Two column tiles per block of the few-row kernel (their partial sums
+    in each wave's region, twice the one-tile size)."""
+    p = make_custom(M, H, I, 4, 64, 4, 64, seed=M + I)
+    o = oracle_full(p, 1)
+    say("poison two column tiles", M, H, I)
+    with skinny_ct(2):
+        y = device_forward(p, 1, GEMV_PATH)
+    check(y, o, 1, f"poison two column tiles M{M} H{H} I{I}")
 
 
 def test_split_launch_under_poison():

@@ -87,6 +87,24 @@ def test_linear_equals_forward_gate_bitwise(M, K, N, path):
     assert np.array_equal(y, g.cpu().numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("M,K,N", [(8, 2048, 1201), (13, 1024, 8193)])
+def test_linear_few_row_two_column_tiles(M, K, N):
+    """The few-row kernel with two column tiles per block, W's rows split
+    between the gate and up slots (an odd N leaves the up slot one row
+    short): bit for bit the one-tile result with one quad per wave, and
+    against the oracle."""
+    from gpu_helpers import skinny_ct
+    p = make_custom(M, K, N, 4, 64, 4, 64, seed=M + N)
+    dev = swq.to_device(p)
+    ys = {}
+    for ct in (1, 2):
+        say("linear column tiles", M, K, N, "ct", ct)
+        with skinny_ct(ct, quads=1):
+            ys[ct] = device_linear(p, swq.SWQ_LINEAR_F32, GEMV, dev=dev)
+    assert np.array_equal(ys[1], ys[2])
+    check_linear(ys[2], p, swq.SWQ_LINEAR_F32, f"linear two column tiles M{M} K{K} N{N}")
+
+
 @pytest.mark.parametrize("M,K,N,path", [(1, 5632, 2048, GEMV), (2048, 14336, 4096, MFMA)],
                          ids=["decode-down-proj", "prefill-down-proj"])
 def test_linear_full_size_sampled(M, K, N, path):

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import quantized_swiglu_forward_amd as swq
-from gpu_helpers import (skinny_x, check, device_forward, device_gemm, forced_path, oracle_full, oracle_pairs,
+from gpu_helpers import (skinny_ct, skinny_x, check, device_forward, device_gemm, forced_path, oracle_full, oracle_pairs,
                          sample_pairs, say)
 from synth import CONFIGS, bf16_bits_to_f32, make_custom, make_problem, pack_codes, to_bf16_bits
 
@@ -460,6 +460,39 @@ def test_few_row_wave_exponents(M, H, spec):
     say("wave exponents", M, H, spec)
     y = device_forward(p, 1, GEMV)
     check(y, oracle_full(p, 1), 1, f"wave exponents M{M} H{H}")
+
+
+# two column tiles per block of the few-row kernel (x converted by the waves,
+# one chunk quad per wave): the decode width (the default picks two tiles
+# there), ragged widths whose last block has a partial or an empty second
+# tile, 2- and 4-bit codes, gs 32 to 128, both activation types.  Each
+# column's arithmetic is that of one tile per block with one quad per wave,
+# so the two agree bit for bit; every form passes against the oracle on
+# every output.
+CT2_CASES = [(8, 2048, 5632, (4, 64, 4, 64), "bf16"), (5, 1024, 1000, (4, 64, 4, 64), "bf16"),
+             (16, 2048, 56, (2, 32, 2, 32), "bf16"), (13, 512, 40, (4, 128, 4, 128), "bf16"),
+             (9, 1536, 300, (4, 32, 4, 32), "bf16"), (8, 2048, 33, (4, 64, 4, 64), "f16"),
+             (16, 2048, 600, (2, 64, 2, 64), "f16"), (6, 2048, 5632, (4, 64, 4, 64), "f16")]
+
+
+@pytest.mark.parametrize("M,H,I,spec,act", CT2_CASES, ids=[f"M{m}-H{h}-I{i}-{a}" for m, h, i, _, a in CT2_CASES])
+def test_few_row_two_column_tiles(M, H, I, spec, act):
+    mode = (M + I) % 3
+    p = make_custom(M, H, I, *spec, seed=M * 5 + I, act=act)
+    assert swq.swiglu_q_staging_bytes(M, H, I, *spec) == 0, "x converted by the waves"
+    o = oracle_full(p, mode)
+    dev = swq.to_device(p)
+    ys = {}
+    for key, ct, quads in (("one tile", 1, None), ("one tile, one quad", 1, 1), ("two tiles", 2, None),
+                           ("default", None, None)):
+        say("few-row column tiles", M, H, I, spec, act, "mode", mode, key)
+        with skinny_ct(ct, quads):
+            ys[key] = device_forward(p, mode, GEMV, dev=dev)
+        check(ys[key], o, mode, f"few-row M{M} H{H} I{I} {act} {key}")
+    assert np.array_equal(ys["one tile, one quad"], ys["two tiles"]), "one and two column tiles differ"
+    tiles = (I + 15) // 16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert np.array_equal(ys["default"], ys["two tiles" if cus < tiles <= 2 * cus else "one tile"])
 
 
 # ------------------------------------------------- tile shapes and splits --
