@@ -31,6 +31,7 @@
 // swq_gemv_f16.hip for the binary16 instances only, so that the two halves
 // build in parallel.
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "swq_device.h"
@@ -532,7 +533,8 @@ __global__ __launch_bounds__(64 * WPB) void swq_gemv1_kernel(GemvParams p, int l
 // each split into binary16 hi + lo, as on the matrix-matrix path.  The waves'
 // partial sums meet in LDS; wave 4 t + j sums element j of row tile t, applies
 // 2^e and runs that row's epilogue.  x' comes from one of three sources (XS):
-//  * kXSelf (M <= 16 and a row fits one pass of the block's waves): each
+//  * kXSelf (a row fits one pass of the block's waves; M <= 16, or up to 32
+//    rows in two tiles with narrow codes and one chunk quad per wave): each
 //    wave copies the rows of x over its own chunks into its own LDS region
 //    (loads that write LDS, four lanes per 64-byte piece of a row), reads
 //    them back in the MFMA's lane order, takes the largest magnitude of each
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
 __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
   constexpr bool STAGE = XS == kXStage, SELF = XS == kXSelf;
   static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, x' in registers");
-  static_assert(!SELF || RT == 1, "x converted by the waves: one row tile");
+  static_assert(!SELF || RT == 1 || !Q2, "x converted by the waves: two row tiles with one quad per wave");
   static_assert(CT == 1 || (CT == 2 && SELF && !Q2 && BITS_G <= 4 && BITS_G == BITS_U),
                 "two column tiles: x converted by the waves, one quad per wave, narrow codes");
   const int tid = threadIdx.x;
@@ -650,7 +652,7 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
   // SELF: the waves' regions (skinny_self_region bytes each), launched as dynamic LDS
   extern __shared__ u32x4 swq_dyn[];
   constexpr int kSelfChunks = Q2 ? 8 : 4;   // chunks per wave
-  const int rb = SELF ? skinny_self_region(p.M, kSelfChunks, CT) : 0;
+  const int rb = SELF ? skinny_self_region(p.M, kSelfChunks, CT * RT) : 0;
   unsigned char* const xreg = reinterpret_cast<unsigned char*>(swq_dyn) + w * rb;
 
   // Row exponents k of the block's 16 columns of both matrices
@@ -925,11 +927,14 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
       const _Float16 z0 = (_Float16)0.0f;
       const f16x8 beg = {cgh, cgl, cgh, z0, z0, z0, z0, z0};
       const f16x8 beu = {cuh, cul, cuh, z0, z0, z0, z0, z0};
-      const float sx = d.sx[0];
-      const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
-      const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
-      ag[ct][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[ct][0], 0, 0, 0);
-      au[ct][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[ct][0], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const float sx = d.sx[t];
+        const _Float16 xhi = (_Float16)sx, xlo = (_Float16)(sx - (float)xhi);
+        const f16x8 ae = {xhi, xhi, xlo, z0, z0, z0, z0, z0};
+        ag[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beg, ag[ct][t], 0, 0, 0);
+        au[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, beu, au[ct][t], 0, 0, 0);
+      }
     } else {
       // x' staged elsewhere: the block's A operands once more against
       // B = c_hi and B = c_lo in every K slot of the lane's chunk (MFMAs
@@ -986,10 +991,13 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
   // only reach D's rows past M, which are never stored.
   auto read_x = [&](int qs, SkinnyChunk<BITS_G, BITS_U, RT, CT>& d) {
     const int sl = 4 * qs + h;
-    const int m = rowl[0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      d.x[0][q] = *reinterpret_cast<const u32x4*>(xreg + (sl * p.M + m) * 64 + 16 * (q ^ ((m >> 2) & 3)));
+    for (int t = 0; t < RT; ++t) {
+      const int m = rowl[t];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        d.x[t][q] = *reinterpret_cast<const u32x4*>(xreg + (sl * p.M + m) * 64 + 16 * (q ^ ((m >> 2) & 3)));
+    }
   };
   // loads the wave issues after its x: the windows of groups (at least 4)
   // and the codes of its quads
@@ -1364,7 +1372,7 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
   // (SWIGLU_Q_SKINNY_QUADS=1, read on every call: one quad per wave, for
   // comparisons and tests)
   const char* q = getenv("SWIGLU_Q_SKINNY_QUADS");
-  if (xs == kXSelf) *two = narrow && !(q && q[0] == '1' && q[1] == 0);
+  if (xs == kXSelf) *two = narrow && M <= 16 && !(q && q[0] == '1' && q[1] == 0);
   else *two = narrow && xs == kXPrep && (M > 16 || H <= 2048);
   const int per = *two ? (quads + 1) / 2 : quads;
   *waves = per < kSkinnyMaxWaves ? per : kSkinnyMaxWaves;
@@ -1372,8 +1380,10 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
 
 // x' converted by each wave itself for M <= 16 whenever a row fits one pass
 // of the block's waves, their LDS regions fit kSkinnySelfMaxLds and the block
-// has more than one wave (no second launch, no workspace); else built in LDS
-// by each block for M*H <= kSkinnyStageMax; else from the prep kernel.
+// has more than one wave (no second launch, no workspace); for 16 < M <= 32
+// (two row tiles) likewise with narrow codes and one chunk quad per wave,
+// within kSkinnySelfRt2MaxLds; else built in LDS by each block for
+// M*H <= kSkinnyStageMax; else from the prep kernel.
 // SWIGLU_Q_SKINNY_X=prep or =stage (where M*H allows) overrides, for
 // comparisons and for tests of those sources.
 #if SWQ_GEMV_ACT == 0
@@ -1389,6 +1399,10 @@ int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
   // the block: measured 4.4 against 4.9 us at M = 6, H = 256, I = 768)
   if (M <= 16 && (H / 32 + 3) / 4 <= (two ? 2 : 1) * waves &&
       waves * skinny_self_region((int)M, two ? 8 : 4) <= kSkinnySelfMaxLds && !(waves == 1 && stage))
+    return kXSelf;
+  const bool narrow = bits_g <= 4 && bits_u <= 4 && bits_g == bits_u;
+  if (M > 16 && M <= 32 && narrow && (H / 32 + 3) / 4 <= waves && waves > 1 &&
+      waves * skinny_self_region((int)M, 4, 4) <= kSkinnySelfRt2MaxLds)
     return kXSelf;
   return stage ? kXStage : kXPrep;
 }
@@ -1415,6 +1429,21 @@ static int skinny_ct(int64_t I, int xs, bool narrow, int quads) {
   if (const char* s = getenv("SWIGLU_Q_SKINNY_CT"); s && (s[0] == '1' || s[0] == '2') && s[1] == 0) return s[0] - '0';
   const int64_t tiles = (I + 15) / 16, cus = device_cus();
   return tiles > cus && tiles <= 2 * cus ? 2 : 1;
+}
+
+// Two row tiles with x converted by the waves: regions past 64 KB of
+// dynamic LDS, allowed once per instance (and device) before the launch.
+template <int BG, int BU, int ACT, int CT>
+static void launch_self_rt2(dim3 g, dim3 b, int lds, hipStream_t stream, const GemvParams& p) {
+  auto kern = swq_skinny_kernel<BG, BU, kXSelf, 2, false, ACT, CT>;
+  constexpr int kDevices = 64;
+  static std::once_flag once[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kDevices)
+    std::call_once(once[dev], [&] {
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnySelfRt2MaxLds);
+    });
+  hipLaunchKernelGGL(kern, g, b, lds, stream, p);
 }
 
 template <int BG, int BU, int ACT>
@@ -1455,16 +1484,24 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     two = false;
     waves = quads;
   }
-  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4, ct) : 0;
-  if (xs == kXSelf && (p.M > 16 || quads > (two ? 2 : 1) * waves || lds > kSkinnySelfMaxLds))
-    return hipErrorInvalidValue;   // one pass, one row tile, regions within bounds
+  const int rt = p.M > 16 ? 2 : 1;
+  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4, ct * rt) : 0;
+  if (xs == kXSelf && (p.M > 32 || quads > (two ? 2 : 1) * waves || (rt == 2 && (two || !kNarrow)) ||
+                       lds > (rt == 2 ? kSkinnySelfRt2MaxLds : kSkinnySelfMaxLds)))
+    return hipErrorInvalidValue;   // one pass, regions within bounds; two row tiles: one quad per wave
   const dim3 g((p.I + 16 * ct - 1) / (16 * ct)), b(64 * waves);
   auto go = [&](auto xs_tag, auto two_tag) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr bool TWO = decltype(two_tag)::value;
     if constexpr (XS == kXSelf && kNarrow && !TWO) {
-      if (ct == 2) hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 2>), g, b, lds, stream, p);
-      else hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
+      if (rt == 2) {
+        if (ct == 2) launch_self_rt2<BG, BU, ACT, 2>(g, b, lds, stream, p);
+        else launch_self_rt2<BG, BU, ACT, 1>(g, b, lds, stream, p);
+      } else if (ct == 2) {
+        hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 2>), g, b, lds, stream, p);
+      } else {
+        hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
+      }
     } else if constexpr (XS == kXSelf) {
       hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
     } else if (p.M <= 16) {

@@ -132,6 +132,9 @@ __host__ __device__ inline int skinny_self_region(int M, int nch, int ct = 1) {
   return x > 2048 * ct ? x : 2048 * ct;
 }
 constexpr int kSkinnySelfMaxLds = 65536;
+// ... and with two row tiles (16 < M <= 32, one chunk quad per wave): 8 KB
+// regions for up to 16 waves (the device allows 160 KB per block)
+constexpr int kSkinnySelfRt2MaxLds = 131072;
 // the matrix-vector kernel's several-row form (no staging pass): 2 <= M <=
 // kGemv1MaxRows with a whole wave per column (H >= 2048) and at most two
 // chunks per lane (H <= 4096); below H = 2048 the few-row kernel is faster

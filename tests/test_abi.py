@@ -256,8 +256,10 @@ def test_few_row_x_source_and_workspace():
     for M <= 16 when a row fits one pass of its waves and their LDS regions
     (skinny_self_region each) fit 64 KB: up to H = 4096 with equal code
     widths of at most 4 bits (two chunk quads per wave; M <= 8 there), up to
-    H = 2048 otherwise; other calls take x' from the prep kernel, and
-    SWIGLU_Q_SKINNY_X=prep forces that."""
+    H = 2048 otherwise; for 16 < M <= 32 (two row tiles) with equal code
+    widths of at most 4 bits and one chunk quad per wave, up to H = 2048
+    (8 KB regions within 128 KB); other calls take x' from the prep kernel,
+    and SWIGLU_Q_SKINNY_X=prep forces that."""
     def ws(M, H, bg=4, bu=4):
         return swq.swiglu_q_staging_bytes(M, H, 5632, bg, 64, bu, 64)
 
@@ -270,8 +272,9 @@ def test_few_row_x_source_and_workspace():
     assert ws(16, 2048, 8, 8) == 0 and ws(8, 2048, 4, 8) == 0
     assert ws(9, 4096) == prep_bytes(9, 4096)     # 16 waves x 8 KB of LDS
     assert ws(8, 4096, 8, 8) == prep_bytes(8, 4096)
-    assert ws(17, 2048) == prep_bytes(17, 2048)
-    assert ws(32, 1024) == prep_bytes(32, 1024)
+    assert ws(17, 2048) == 0 and ws(32, 1024) == 0 and ws(32, 2048, 2, 2) == 0 and ws(24, 512) == 0
+    assert ws(17, 2048, 8, 4) == prep_bytes(17, 2048)   # codes not narrow
+    assert ws(24, 4096) == prep_bytes(24, 4096)         # 32 quads: no one pass of one quad per wave
     assert ws(8, 8192) == prep_bytes(8, 8192)
     os.environ["SWIGLU_Q_SKINNY_X"] = "prep"
     try:

@@ -56,10 +56,11 @@ def test_forward_under_poison(M, H, I, spec, path):
         check(y, o, mode, f"poison M{M} H{H} I{I} x source {source}")
 
 
-@pytest.mark.parametrize("M,H,I", [(8, 2048, 1000), (5, 1024, 72)])
+@pytest.mark.parametrize("M,H,I", [(8, 2048, 1000), (5, 1024, 72), (24, 2048, 1000), (32, 1024, 40)])
 def test_few_row_two_column_tiles_under_poison(M, H, I):
     """Two column tiles per block of the few-row kernel (their partial sums
-    in each wave's region, twice the one-tile size)."""
+    in each wave's region, twice the one-tile size), with one and two row
+    tiles (M > 16: regions past 64 KB of LDS per block)."""
     p = make_custom(M, H, I, 4, 64, 4, 64, seed=M + I)
     o = oracle_full(p, 1)
     say("poison two column tiles", M, H, I)

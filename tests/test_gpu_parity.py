@@ -439,10 +439,11 @@ def test_few_row_kernel_x_staging(M, H, I, spec):
 # block see different slices), a row that is zero over half of H (whole waves
 # see only zeros), bf16 subnormals, ragged H, pairs past the last in the
 # waves' x loads (M * chunks not a multiple of 16); one and two chunk quads
-# per wave, narrow, mixed and 8-bit codes
+# per wave, one and two row tiles, narrow, mixed and 8-bit codes
 SELF_CASES = [(8, 2048, (4, 64, 4, 64)), (13, 2048, (8, 32, 8, 64)), (8, 4096, (4, 128, 4, 128)),
               (16, 2048, (4, 64, 8, 32)), (5, 1056, (2, 32, 2, 32)), (16, 1024, (4, 32, 4, 64)),
-              (2, 1024, (4, 64, 4, 64)), (3, 1184, (8, 32, 4, 32))]
+              (2, 1024, (4, 64, 4, 64)), (3, 1184, (8, 32, 4, 32)), (24, 2048, (4, 64, 4, 64)),
+              (32, 1056, (2, 32, 2, 32)), (17, 2048, (4, 128, 4, 128))]
 
 
 @pytest.mark.parametrize("M,H,spec", SELF_CASES, ids=[f"M{m}-H{h}" for m, h, _ in SELF_CASES])
@@ -465,14 +466,19 @@ def test_few_row_wave_exponents(M, H, spec):
 # two column tiles per block of the few-row kernel (x converted by the waves,
 # one chunk quad per wave): the decode width (the default picks two tiles
 # there), ragged widths whose last block has a partial or an empty second
-# tile, 2- and 4-bit codes, gs 32 to 128, both activation types.  Each
+# tile, 2- and 4-bit codes, gs 32 to 128, both activation types, one and
+# two row tiles (ragged H too).  Each
 # column's arithmetic is that of one tile per block with one quad per wave,
 # so the two agree bit for bit; every form passes against the oracle on
 # every output.
 CT2_CASES = [(8, 2048, 5632, (4, 64, 4, 64), "bf16"), (5, 1024, 1000, (4, 64, 4, 64), "bf16"),
              (16, 2048, 56, (2, 32, 2, 32), "bf16"), (13, 512, 40, (4, 128, 4, 128), "bf16"),
              (9, 1536, 300, (4, 32, 4, 32), "bf16"), (8, 2048, 33, (4, 64, 4, 64), "f16"),
-             (16, 2048, 600, (2, 64, 2, 64), "f16"), (6, 2048, 5632, (4, 64, 4, 64), "f16")]
+             (16, 2048, 600, (2, 64, 2, 64), "f16"), (6, 2048, 5632, (4, 64, 4, 64), "f16"),
+             # two row tiles (16 < M <= 32)
+             (24, 2048, 5632, (4, 64, 4, 64), "bf16"), (17, 1024, 1000, (4, 64, 4, 64), "bf16"),
+             (32, 2048, 56, (2, 32, 2, 32), "f16"), (20, 512, 600, (4, 128, 4, 128), "bf16"),
+             (29, 1504, 130, (4, 32, 4, 32), "f16")]
 
 
 @pytest.mark.parametrize("M,H,I,spec,act", CT2_CASES, ids=[f"M{m}-H{h}-I{i}-{a}" for m, h, i, _, a in CT2_CASES])
