@@ -234,18 +234,21 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
                        int precision_mode);
 
 /* M threshold T of the dispatcher: M < T takes SWQ_PATH_GEMV, M >= T takes
- * SWQ_PATH_MFMA; the matrix-vector path takes at most 32 rows, so M > 32
- * always runs the MFMA path.  The default comes from the environment
- * variable SWIGLU_Q_MMIN when set to a positive integer, else the built-in
- * default 33 (measured: the matrix-vector path is faster for every M <= 32
- * on every weight shape measured).
+ * SWQ_PATH_MFMA; the matrix-vector path takes at most 128 rows (past 32, as
+ * row groups of 32 that each read the weights once), so M > 128 always runs
+ * the MFMA path.  The default comes from the environment variable
+ * SWIGLU_Q_MMIN when set to a positive integer, else the built-in default 65
+ * (measured: the matrix-vector path is faster for every M <= 32 on every
+ * weight shape measured; for 33 <= M <= 64 it is 20-45 % faster with
+ * intermediate sizes up to 8192, level at H = 2048, I = 14336, and up to
+ * 19 % slower at H = 4096, I = 14336, where T = 33 suits better).
  * T <= 1 sends every M >= 1 to the MFMA path. */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);
 
 /* The path (SWQ_PATH_GEMV or SWQ_PATH_MFMA) a call with M rows and hidden
  * size H takes under the current threshold, by the same rule as the calls
- * (M < T and M <= 32 take the matrix-vector path); -1 for M < 1 or H < 1.
+ * (M < T and M <= 128 take the matrix-vector path); -1 for M < 1 or H < 1.
  * Host only: touches no device. */
 int swiglu_q_path_for(int64_t M, int64_t H);
 

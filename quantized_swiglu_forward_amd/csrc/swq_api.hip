@@ -9,10 +9,13 @@
 // threshold defaults to 2 there, benchmarks are to set it, and it can be set
 // from the environment) and the support predicate of the same file (bf16
 // activations, affine biases, 2-, 4- or 8-bit codes, group size a multiple
-// of 32, H a multiple of 32).  Here the default is 33: measured on this GPU,
-// the matrix-vector kernels beat the matrix-matrix kernel for every M <= 16
-// (2-3x on the decode and prefill weight shapes) and for M <= 32 on every
-// weight shape measured, and 32 rows (two 16-row MFMA tiles) is their limit.
+// of 32, H a multiple of 32).  Here the default is 65: measured on this GPU,
+// the matrix-vector kernels beat the matrix-matrix kernel for every M <= 32
+// on every weight shape measured (2-3x on the decode and prefill weight
+// shapes for M <= 16), and with two row groups of 32 (33 <= M <= 64) by
+// 20-45 % on decode-width weights (I up to 8192), level at H = 2048,
+// I = 14336 and up to 19 % behind at H = 4096, I = 14336; the few-row
+// kernel takes at most 128 rows (four groups).
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,7 +50,8 @@ int swq::device_cus() {
 
 namespace {
 
-constexpr int kDefaultThreshold = kGemvMaxM + 1;
+// Default M threshold: the matrix-vector path up to two row groups (M <= 64).
+constexpr int kDefaultThreshold = 2 * kGemvMaxM + 1;
 
 std::atomic<int> g_threshold{-1};
 std::atomic<uint64_t> g_calls[2];
@@ -137,7 +141,7 @@ int auto_path(int64_t M, int64_t H) {
 
 bool gemv_fits(int64_t M, int64_t H) {
   (void)H;
-  return M >= 1 && M <= kGemvMaxM;
+  return M >= 1 && M <= kGemvGroupsMaxM;
 }
 
 // The matrix-vector kernel reads x itself (M = 1 with H <= 8192, and its
@@ -235,10 +239,11 @@ int get_workspace(hipStream_t stream, size_t need, void** out, int slot = 0) {
 }
 
 // Staging of the matrix-vector path when the prep kernel stages x' (x' in the
-// few-row kernel's lane order: 4 KB per chunk quad and 16-row tile; the row
-// exponents; then the weight rows' exponents k [2][I]).
+// few-row kernel's lane order: 4 KB per chunk quad and 16-row tile, two
+// tiles per row group past 16 rows; the row exponents; then the weight
+// rows' exponents k [2][I]).
 int64_t gemv_x_bytes(int64_t M, int64_t H) {
-  return align256(((H + 127) / 128) * (M > 16 ? 2 : 1) * kSkinnyXUnitsPerQuadTile * 16);
+  return align256(((H + 127) / 128) * gemv_x_tiles(M) * kSkinnyXUnitsPerQuadTile * 16);
 }
 int64_t gemv_stage_bytes(int64_t M, int64_t H, int64_t I) {
   return gemv_x_bytes(M, H) + align256(M * 4) + align256(2 * I * 4);
@@ -316,7 +321,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
       // the weight rows' exponents only when the few-row kernel cannot take
       // them from the scales of its first pass
       pp.k_only = skinny_needs_kexp((int)M, (int)H, bits_g, bits_u) ? 1 : 0;
-      pp.xlane = M > 16 ? 2 : 1;
+      pp.xlane = (int)gemv_x_tiles(M);
       pp.act = act;
       p.xa = pp.xa;
       p.xexp = pp.xexp;

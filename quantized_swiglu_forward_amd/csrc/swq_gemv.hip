@@ -578,12 +578,22 @@ struct SbWindow {
 // tiles than CUs).
 template <int BITS_G, int BITS_U, int XS, int RT, bool Q2, int ACT, int CT>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves)
-__attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams p) {
+__attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U == 4 ? 6 : 4) / RT))) void swq_skinny_kernel(GemvParams pin) {
   constexpr bool STAGE = XS == kXStage, SELF = XS == kXSelf;
+  // rows of this block: row group blockIdx.y of kGemvMaxM rows (x, its
+  // staged exponents and the stores offset by m0; p.M the group's rows)
+  const int m0 = (int)blockIdx.y * kGemvMaxM;
+  GemvParams p = pin;
+  p.x = pin.x + (int64_t)m0 * pin.H;
+  p.M = min(kGemvMaxM, pin.M - m0);
+  if constexpr (XS == kXPrep) p.xexp = pin.xexp + m0;
+  // 16-row tiles of x' staged by the prep kernel (every group's), and this group's first
+  const int xtiles = RT * (int)gridDim.y, xtile0 = RT * (int)blockIdx.y;
   static_assert(!Q2 || (!STAGE && BITS_G <= 4 && BITS_G == BITS_U), "two quads in flight: narrow codes, x' in registers");
   static_assert(!SELF || RT == 1 || !Q2, "x converted by the waves: two row tiles with one quad per wave");
   static_assert(CT == 1 || (CT == 2 && SELF && !Q2 && BITS_G <= 4 && BITS_G == BITS_U),
                 "two column tiles: x converted by the waves, one quad per wave, narrow codes");
+  (void)xtile0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -609,7 +619,7 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
   // x' from the prep kernel in this kernel's lane order (kSkinnyXUnitsPerQuadTile)
   const int nquad_all = (nchunk + 3) >> 2;
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.xa, (short)0, nquad_all * RT * kSkinnyXUnitsPerQuadTile * 16, 0x00020000);
+      (void*)p.xa, (short)0, nquad_all * xtiles * kSkinnyXUnitsPerQuadTile * 16, 0x00020000);
   // exponents of this lane's accumulator rows 16 t + 4 h + j (prep-fed x'; the
   // block's own in LDS otherwise), loaded with the first weights and packed
   // as four biased bytes per tile (each lies in [-127, 127]); two row tiles
@@ -800,7 +810,7 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
         const bool ok = d.live && rowok[t];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ox = ok ? (((quad * RT + t) * 4 + q) * 64 + lane) * 16 : 0x7FFFFFF0;
+          const int ox = ok ? (((quad * xtiles + xtile0 + t) * 4 + q) * 64 + lane) * 16 : 0x7FFFFFF0;
           d.x[t][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ox, 0, 0);
         }
       }
@@ -1274,7 +1284,7 @@ __attribute__((amdgpu_waves_per_eu(CT == 2 || Q2 ? 4 : (BITS_G == 4 && BITS_U ==
       u += red_at(ww, 2 * tt + 1)[lane][j];
     }
     const int m = 16 * t + 4 * h + j;
-    if (m < p.M && c16 < p.I) store_out(p, m, c16, g, u, ACT);
+    if (m < p.M && c16 < p.I) store_out(p, m0 + m, c16, g, u, ACT);
   }
 }
 
@@ -1391,18 +1401,20 @@ int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
   const char* env = getenv("SWIGLU_Q_SKINNY_X");
   if (env && strcmp(env, "prep") == 0) return kXPrep;
   if (env && strcmp(env, "stage") == 0 && M * H <= kSkinnyStageMax) return kXStage;
+  // (more than kGemvMaxM rows: row groups of kGemvMaxM, never built in the block)
+  const int64_t Mg = M > kGemvMaxM ? kGemvMaxM : M;
   int waves;
   bool two;
-  skinny_shape(M, H, bits_g, bits_u, kXSelf, &waves, &two);
-  const bool stage = M * H <= kSkinnyStageMax;
+  skinny_shape(Mg, H, bits_g, bits_u, kXSelf, &waves, &two);
+  const bool stage = M <= kGemvMaxM && M * H <= kSkinnyStageMax;
   // (a one-wave block, H <= 256 with two quads per wave, converts faster in
   // the block: measured 4.4 against 4.9 us at M = 6, H = 256, I = 768)
-  if (M <= 16 && (H / 32 + 3) / 4 <= (two ? 2 : 1) * waves &&
-      waves * skinny_self_region((int)M, two ? 8 : 4) <= kSkinnySelfMaxLds && !(waves == 1 && stage))
+  if (Mg <= 16 && (H / 32 + 3) / 4 <= (two ? 2 : 1) * waves &&
+      waves * skinny_self_region((int)Mg, two ? 8 : 4) <= kSkinnySelfMaxLds && !(waves == 1 && stage))
     return kXSelf;
   const bool narrow = bits_g <= 4 && bits_u <= 4 && bits_g == bits_u;
-  if (M > 16 && M <= 32 && narrow && (H / 32 + 3) / 4 <= waves && waves > 1 &&
-      waves * skinny_self_region((int)M, 4, 4) <= kSkinnySelfRt2MaxLds)
+  if (Mg > 16 && narrow && (H / 32 + 3) / 4 <= waves && waves > 1 &&
+      waves * skinny_self_region((int)Mg, 4, 4) <= kSkinnySelfRt2MaxLds)
     return kXSelf;
   return stage ? kXStage : kXPrep;
 }
@@ -1410,7 +1422,7 @@ int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
 bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
   int waves;
   bool two;
-  skinny_shape(M, H, bits_g, bits_u, kXPrep, &waves, &two);
+  skinny_shape(M > kGemvMaxM ? kGemvMaxM : M, H, bits_g, bits_u, kXPrep, &waves, &two);
   return (H / 32 + 3) / 4 > (two ? 2 : 1) * waves;
 }
 #endif
@@ -1418,17 +1430,18 @@ bool skinny_needs_kexp(int M, int H, int bits_g, int bits_u) {
 // Column tiles per block of the few-row kernel: two (with one chunk quad per
 // wave, the row in one pass of at most kSkinnyMaxWaves waves) when each wave
 // converts x itself, the codes are narrow, and the 16-column tiles are more
-// than the device's CUs but at most twice as many: one round of blocks of 32
-// columns, each conversion of x serving both tiles, instead of some CUs
-// taking a second block of 16 (measured at H = 2048: I = 5632, M = 8 / 16:
-// 9.04 / 10.12 -> 8.59 / 9.21 us; one tile stays ahead at most one round of
-// tiles and at 3.5 rounds).  SWIGLU_Q_SKINNY_CT=1 or 2 (read on every call)
-// overrides where two are possible, for comparisons and tests.
-static int skinny_ct(int64_t I, int xs, bool narrow, int quads) {
+// than the device's CUs -- with one row tile, at most twice as many: each
+// conversion of x serves both tiles, instead of some CUs taking a second
+// block of 16 (measured at H = 2048: I = 5632, M = 8 / 16: 9.04 / 10.12 ->
+// 8.59 / 9.21 us; one tile stays ahead at most one round of tiles, and with
+// one row tile at 3.5 rounds, where two of its blocks share a CU).
+// SWIGLU_Q_SKINNY_CT=1 or 2 (read on every call) overrides where two are
+// possible, for comparisons and tests.
+static int skinny_ct(int64_t I, int xs, bool narrow, int quads, int rt) {
   if (xs != kXSelf || !narrow || quads > kSkinnyMaxWaves) return 1;
   if (const char* s = getenv("SWIGLU_Q_SKINNY_CT"); s && (s[0] == '1' || s[0] == '2') && s[1] == 0) return s[0] - '0';
   const int64_t tiles = (I + 15) / 16, cus = device_cus();
-  return tiles > cus && tiles <= 2 * cus ? 2 : 1;
+  return tiles > cus && (rt == 2 || tiles <= 2 * cus) ? 2 : 1;
 }
 
 // Two row tiles with x converted by the waves: regions past 64 KB of
@@ -1467,29 +1480,32 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
     if (cpl == 1) return full ? launch_gemv1_rows_t<BG, BU, 1, true, ACT>(p, r, stream) : hipErrorInvalidValue;   // H = 2048
     return full ? launch_gemv1_rows_t<BG, BU, 2, true, ACT>(p, r, stream) : launch_gemv1_rows_t<BG, BU, 2, false, ACT>(p, r, stream);
   }
-  if (p.M < 1 || p.M > kGemvMaxM) return hipErrorInvalidValue;
+  if (p.M < 1 || p.M > kGemvGroupsMaxM) return hipErrorInvalidValue;
+  // row groups of kGemvMaxM rows (grid y); Mg: the rows of a full group
+  const int groups = (p.M + kGemvMaxM - 1) / kGemvMaxM;
+  const int Mg = groups > 1 ? kGemvMaxM : p.M;
   // one wave per chunk quad (or pair of quads), at most kSkinnyMaxWaves per
   // block of 16 columns
   constexpr bool kNarrow = BG <= 4 && BU <= 4 && BG == BU;
   const int xs = p.xa != nullptr ? kXPrep : skinny_x_source(p.M, p.H, BG, BU);
   int waves;
   bool two;
-  skinny_shape(p.M, p.H, BG, BU, xs, &waves, &two);
+  skinny_shape(Mg, p.H, BG, BU, xs, &waves, &two);
   const int quads = (p.H / 32 + 3) / 4;
   if (xs == kXPrep && (p.xa == nullptr || (p.kexp == nullptr && skinny_needs_kexp(p.M, p.H, BG, BU))))
     return hipErrorInvalidValue;
-  if (xs == kXStage && (int64_t)p.M * p.H > kSkinnyStageMax) return hipErrorInvalidValue;
-  const int ct = skinny_ct(p.I, xs, kNarrow, quads);
+  if (xs == kXStage && (groups > 1 || (int64_t)p.M * p.H > kSkinnyStageMax)) return hipErrorInvalidValue;
+  const int rt = Mg > 16 ? 2 : 1;
+  const int ct = skinny_ct(p.I, xs, kNarrow, quads, rt);
   if (ct == 2) {   // one quad per wave
     two = false;
     waves = quads;
   }
-  const int rt = p.M > 16 ? 2 : 1;
-  const int lds = xs == kXSelf ? waves * skinny_self_region(p.M, two ? 8 : 4, ct * rt) : 0;
-  if (xs == kXSelf && (p.M > 32 || quads > (two ? 2 : 1) * waves || (rt == 2 && (two || !kNarrow)) ||
+  const int lds = xs == kXSelf ? waves * skinny_self_region(Mg, two ? 8 : 4, ct * rt) : 0;
+  if (xs == kXSelf && (quads > (two ? 2 : 1) * waves || (rt == 2 && (two || !kNarrow)) ||
                        lds > (rt == 2 ? kSkinnySelfRt2MaxLds : kSkinnySelfMaxLds)))
     return hipErrorInvalidValue;   // one pass, regions within bounds; two row tiles: one quad per wave
-  const dim3 g((p.I + 16 * ct - 1) / (16 * ct)), b(64 * waves);
+  const dim3 g((p.I + 16 * ct - 1) / (16 * ct), groups), b(64 * waves);
   auto go = [&](auto xs_tag, auto two_tag) {
     constexpr int XS = decltype(xs_tag)::value;
     constexpr bool TWO = decltype(two_tag)::value;
@@ -1504,7 +1520,7 @@ static hipError_t launch_gemv_bits(const GemvParams& p, hipStream_t stream) {
       }
     } else if constexpr (XS == kXSelf) {
       hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, lds, stream, p);
-    } else if (p.M <= 16) {
+    } else if (Mg <= 16) {
       hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 1, TWO, ACT, 1>), g, b, 0, stream, p);
     } else {
       hipLaunchKernelGGL((swq_skinny_kernel<BG, BU, XS, 2, TWO, ACT, 1>), g, b, 0, stream, p);

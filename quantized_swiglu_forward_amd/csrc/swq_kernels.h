@@ -114,8 +114,14 @@ constexpr int kMfmaConfigs = 2;
 constexpr int kMfmaBM[kMfmaConfigs] = {256, 128};
 constexpr int kMfmaBN[kMfmaConfigs] = {128, 128};
 
-// Largest M the matrix-vector path takes (two 16-row MFMA tiles).
+// Rows of one launch group of the few-row kernel (two 16-row MFMA tiles).
 constexpr int kGemvMaxM = 32;
+// ... the few-row kernel takes up to kGemvGroupsMaxM rows as row groups of
+// kGemvMaxM (one grid row per group; x' and the weights read once per group)
+constexpr int kGemvGroupsMaxM = 128;
+// 16-row tiles of x' the prep kernel stages for the few-row kernel: one for
+// M <= 16, else two per row group
+inline int64_t gemv_x_tiles(int64_t M) { return M > 16 ? 2 * ((M + kGemvMaxM - 1) / kGemvMaxM) : 1; }
 // Where the few-row kernel's x' comes from (skinny_x_source): the prep
 // kernel (staged in the workspace), the block's own LDS (M*H up to
 // kSkinnyStageMax), or each wave's own registers (a row fits one pass of the

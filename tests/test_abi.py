@@ -190,8 +190,9 @@ def test_threshold_roundtrip():
 
 
 def test_dispatcher_choice_given_m_and_threshold():
-    """M < T takes the matrix-vector path while it fits (M <= 32), else the
-    MFMA path; T <= 1 sends everything to MFMA; invalid sizes give -1."""
+    """M < T takes the matrix-vector path while it fits (M <= 128, row groups
+    of 32 past 32 rows), else the MFMA path; T <= 1 sends everything to
+    MFMA; invalid sizes give -1."""
     old = swq.swiglu_q_get_m_threshold()
     try:
         swq.swiglu_q_set_m_threshold(33)
@@ -202,9 +203,10 @@ def test_dispatcher_choice_given_m_and_threshold():
         swq.swiglu_q_set_m_threshold(9)
         assert swq.swiglu_q_path_for(8, 4096) == swq.SWQ_PATH_GEMV
         assert swq.swiglu_q_path_for(9, 4096) == swq.SWQ_PATH_MFMA
-        swq.swiglu_q_set_m_threshold(100)
+        swq.swiglu_q_set_m_threshold(200)
         assert swq.swiglu_q_path_for(32, 256) == swq.SWQ_PATH_GEMV
-        assert swq.swiglu_q_path_for(33, 256) == swq.SWQ_PATH_MFMA   # past the matrix-vector limit
+        assert swq.swiglu_q_path_for(128, 256) == swq.SWQ_PATH_GEMV  # four row groups of 32
+        assert swq.swiglu_q_path_for(129, 256) == swq.SWQ_PATH_MFMA   # past the matrix-vector limit
         swq.swiglu_q_set_m_threshold(1)
         assert swq.swiglu_q_path_for(1, 2048) == swq.SWQ_PATH_MFMA
         assert swq.swiglu_q_path_for(0, 2048) == -1 and swq.swiglu_q_path_for(4, 0) == -1
@@ -221,7 +223,7 @@ def test_threshold_default_from_environment():
     env = dict(os.environ, SWIGLU_Q_MMIN="junk")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
                          check=True).stdout.strip()
-    assert out == "33"
+    assert out == "65"
 
 
 def test_strerror_and_version():
@@ -265,7 +267,8 @@ def test_few_row_x_source_and_workspace():
 
     def prep_bytes(M, H):   # x' in lane order, row exponents, weight-row exponents
         a = lambda v: (v + 255) // 256 * 256
-        return a((H + 127) // 128 * (2 if M > 16 else 1) * 256 * 16) + a(M * 4) + a(2 * 5632 * 4)
+        tiles = 2 * ((M + 31) // 32) if M > 16 else 1   # 16-row tiles: two per row group of 32
+        return a((H + 127) // 128 * tiles * 256 * 16) + a(M * 4) + a(2 * 5632 * 4)
 
     for M, H in ((5, 2048), (8, 2048), (16, 2048), (8, 4096), (2, 1024), (16, 1056)):
         assert ws(M, H) == 0, (M, H)
@@ -275,6 +278,10 @@ def test_few_row_x_source_and_workspace():
     assert ws(17, 2048) == 0 and ws(32, 1024) == 0 and ws(32, 2048, 2, 2) == 0 and ws(24, 512) == 0
     assert ws(17, 2048, 8, 4) == prep_bytes(17, 2048)   # codes not narrow
     assert ws(24, 4096) == prep_bytes(24, 4096)         # 32 quads: no one pass of one quad per wave
+    # row groups of 32 past 32 rows: converted by the waves, or staged for every group
+    gemv = lambda M, H: swq.swiglu_q_staging_bytes(M, H, 5632, 4, 64, 4, 64, swq.SWQ_PATH_GEMV)
+    assert ws(33, 2048) == 0 and ws(64, 2048, 2, 2) == 0 and gemv(128, 1024) == 0
+    assert ws(40, 2048, 8, 4) == prep_bytes(40, 2048) and gemv(128, 4096) == prep_bytes(128, 4096)
     assert ws(8, 8192) == prep_bytes(8, 8192)
     os.environ["SWIGLU_Q_SKINNY_X"] = "prep"
     try:
@@ -288,7 +295,7 @@ def test_few_row_x_source_and_workspace():
         swq.swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64)
     assert swq.swiglu_q_staging_bytes(8, 2048, 5632, 4, 64, 4, 64, swq.SWQ_PATH_MFMA) == \
         swq.swiglu_q_workspace_bytes(8, 2048, 5632, 4, 64, 4, 64)
-    assert swq.swiglu_q_staging_bytes(33, 2048, 5632, 4, 64, 4, 64, swq.SWQ_PATH_GEMV) == 0   # no such call
+    assert swq.swiglu_q_staging_bytes(129, 2048, 5632, 4, 64, 4, 64, swq.SWQ_PATH_GEMV) == 0   # no such call
     assert swq.swiglu_q_staging_bytes(8, 2048, 5632, 3, 64, 4, 64) == 0
 
 

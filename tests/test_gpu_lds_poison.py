@@ -69,6 +69,18 @@ def test_few_row_two_column_tiles_under_poison(M, H, I):
     check(y, o, 1, f"poison two column tiles M{M} H{H} I{I}")
 
 
+@pytest.mark.parametrize("source", [None, "prep"])
+def test_few_row_row_groups_under_poison(source):
+    """Two row groups of 32 on the matrix-vector path, x converted by each
+    group's waves or staged for both groups by the prep kernel."""
+    p = make_custom(48, 2048, 300, 4, 64, 4, 64, seed=48)
+    o = oracle_full(p, 1)
+    say("poison row groups", source or "default")
+    with skinny_x(source):
+        y = device_forward(p, 1, GEMV_PATH)
+    check(y, o, 1, f"poison row groups x source {source}")
+
+
 def test_split_launch_under_poison():
     """256 x 128 tiles over whole rounds and 128 x 128 tiles for the rest."""
     p = make_custom(512, 256, 38400, 4, 64, 4, 64, seed=41)

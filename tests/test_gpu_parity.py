@@ -501,6 +501,38 @@ def test_few_row_two_column_tiles(M, H, I, spec, act):
     assert np.array_equal(ys["default"], ys["two tiles" if cus < tiles <= 2 * cus else "one tile"])
 
 
+# row groups of 32 (33 <= M <= 128 on the matrix-vector path): x converted by
+# the waves of each group or staged by the prep kernel for every group (8-bit
+# or mixed codes, H past one pass, or forced), 2 to 4 groups, a last group of
+# one row, ragged widths, both activation types; every output against the
+# oracle (sampled at the decode width)
+ROW_GROUP_CASES = [(33, 2048, 300, (4, 64, 4, 64), "bf16"), (48, 1024, 1000, (4, 64, 4, 64), "bf16"),
+                   (64, 2048, 5632, (4, 64, 4, 64), "bf16"), (96, 512, 200, (2, 32, 2, 32), "f16"),
+                   (128, 2048, 130, (4, 128, 4, 128), "bf16"), (40, 2048, 257, (8, 32, 4, 64), "bf16"),
+                   (70, 4096, 100, (4, 64, 4, 64), "bf16"), (100, 1024, 77, (2, 64, 8, 128), "f16"),
+                   (65, 256, 97, (4, 64, 4, 64), "bf16")]
+
+
+@pytest.mark.parametrize("M,H,I,spec,act", ROW_GROUP_CASES, ids=[f"M{m}-H{h}-I{i}-{a}" for m, h, i, _, a in ROW_GROUP_CASES])
+def test_few_row_row_groups(M, H, I, spec, act):
+    mode = (M + I) % 3
+    p = make_custom(M, H, I, *spec, seed=M * 3 + I, act=act)
+    dev = swq.to_device(p)
+    if M * I > 100000:
+        rng = np.random.default_rng(M)
+        ms = np.concatenate([np.arange(M), rng.integers(0, M, 3000)])
+        ns = np.concatenate([rng.integers(0, I, M), rng.integers(0, I, 3000)])
+        ref = oracle_pairs(p, mode, ms, ns)
+    else:
+        ms = ns = None
+        ref = oracle_full(p, mode)
+    for source in (None, "prep"):
+        say("row groups", M, H, I, spec, act, "mode", mode, "x source", source or "default")
+        with skinny_x(source):
+            y = device_forward(p, mode, GEMV, dev=dev)
+        check(y if ms is None else y[ms, ns], ref, mode, f"row groups M{M} H{H} I{I} {act} x source {source}")
+
+
 # ------------------------------------------------- tile shapes and splits --
 
 def test_tile_shapes_and_column_split_agree_bitwise():
