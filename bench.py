@@ -916,7 +916,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-linear", action="store_true")
-    ap.add_argument("--no-small-batch", action="store_true", help="skip the decode shape at 2 and 4 rows")
+    ap.add_argument("--no-small-batch", action="store_true", help="skip the decode shape at 2 to 64 rows")
     ap.add_argument("--no-mlp", action="store_true", help="skip the whole-MLP measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true")
@@ -952,7 +952,7 @@ def main():
                      "dtype": r["dtype"], "config": r["config"], "roofline": r["roofline"]})
     if args.workload == "decode" and not args.no_small_batch:
         log("decode, a few rows per call: timing ...")
-        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32)}
+        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32, 64)}
         torch.cuda.empty_cache()
     if not args.no_prefill:
         log("MFMA probe: sustained f16 rate ...")
