@@ -504,13 +504,15 @@ def test_few_row_two_column_tiles(M, H, I, spec, act):
 # row groups of 32 (33 <= M <= 128 on the matrix-vector path): x converted by
 # the waves of each group or staged by the prep kernel for every group (8-bit
 # or mixed codes, H past one pass, or forced), 2 to 4 groups, a last group of
-# one row, ragged widths, both activation types; every output against the
-# oracle (sampled at the decode width)
+# one row, ragged widths and ragged H (a partial last chunk quad), both
+# activation types; every output against the oracle (sampled at the decode
+# width)
 ROW_GROUP_CASES = [(33, 2048, 300, (4, 64, 4, 64), "bf16"), (48, 1024, 1000, (4, 64, 4, 64), "bf16"),
                    (64, 2048, 5632, (4, 64, 4, 64), "bf16"), (96, 512, 200, (2, 32, 2, 32), "f16"),
                    (128, 2048, 130, (4, 128, 4, 128), "bf16"), (40, 2048, 257, (8, 32, 4, 64), "bf16"),
                    (70, 4096, 100, (4, 64, 4, 64), "bf16"), (100, 1024, 77, (2, 64, 8, 128), "f16"),
-                   (65, 256, 97, (4, 64, 4, 64), "bf16")]
+                   (65, 256, 97, (4, 64, 4, 64), "bf16"), (40, 1056, 77, (2, 32, 2, 32), "bf16"),
+                   (72, 1184, 50, (8, 32, 4, 32), "f16"), (120, 1504, 33, (4, 32, 4, 32), "bf16")]
 
 
 @pytest.mark.parametrize("M,H,I,spec,act", ROW_GROUP_CASES, ids=[f"M{m}-H{h}-I{i}-{a}" for m, h, i, _, a in ROW_GROUP_CASES])
@@ -671,9 +673,11 @@ def test_m_zero_launches_nothing():
 
 @pytest.mark.parametrize("M,H,I,spec", [(1, 2048, 600, (4, 64, 4, 64)), (3, 2048, 600, (4, 64, 4, 64)),
                                         (6, 256, 300, (8, 32, 4, 64)), (12, 2048, 200, (4, 64, 4, 64)),
-                                        (24, 1024, 300, (4, 64, 4, 64)), (300, 512, 384, (4, 64, 8, 32))],
-                         ids=["decode", "decode-rows", "few-row-in-kernel", "few-row-prep", "few-row-two-tiles",
-                              "mfma"])
+                                        (24, 1024, 300, (4, 64, 4, 64)), (20, 2048, 200, (8, 32, 4, 64)),
+                                        (48, 2048, 600, (4, 64, 4, 64)), (40, 2048, 300, (8, 32, 4, 64)),
+                                        (300, 512, 384, (4, 64, 8, 32))],
+                         ids=["decode", "decode-rows", "few-row-in-block", "few-row-waves", "few-row-two-row-tiles",
+                              "few-row-prep", "row-groups", "row-groups-prep", "mfma"])
 def test_graph_replays_match_eager(M, H, I, spec):
     """The forward recorded into a HIP graph (after an eager call, so the
     workspace exists) and replayed several times, with other eager work and
