@@ -37,7 +37,8 @@
  * them.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  * and the call returns without synchronising.  A matrix-vector call whose
  * kernel cannot convert x itself needs a device workspace for the staged x
- * (swiglu_q_staging_bytes says how much; most calls with M <= 32 need none),
+ * (swiglu_q_staging_bytes says how much; most calls with 4-bit or 2-bit
+ * codes, H <= 2048 and M <= 128 need none),
  * and every matrix-matrix call needs one for x and the weights' extra rows,
  * scale tiles and row exponents: the library keeps one per (device, stream),
  * allocated on
@@ -101,7 +102,7 @@ extern "C" {
 #define SWQ_F32_BF16OUT  2  /* as SWQ_F32, rounded once to bf16 at the store       */
 
 /* Kernel paths chosen by the M-threshold dispatcher. */
-#define SWQ_PATH_GEMV    0  /* M < threshold (M <= 32): matrix-vector kernels      */
+#define SWQ_PATH_GEMV    0  /* M < threshold (M <= 128): matrix-vector kernels     */
 #define SWQ_PATH_MFMA    1  /* M >= threshold: dequantizing bf16/f16 MFMA GEMM      */
 #define SWQ_PATH_AUTO   -1
 
