@@ -1400,7 +1400,7 @@ static void skinny_shape(int64_t M, int64_t H, int bits_g, int bits_u, int xs, i
 int skinny_x_source(int64_t M, int64_t H, int bits_g, int bits_u) {
   const char* env = getenv("SWIGLU_Q_SKINNY_X");
   if (env && strcmp(env, "prep") == 0) return kXPrep;
-  if (env && strcmp(env, "stage") == 0 && M * H <= kSkinnyStageMax) return kXStage;
+  if (env && strcmp(env, "stage") == 0 && M <= kGemvMaxM && M * H <= kSkinnyStageMax) return kXStage;
   // (more than kGemvMaxM rows: row groups of kGemvMaxM, never built in the block)
   const int64_t Mg = M > kGemvMaxM ? kGemvMaxM : M;
   int waves;
