@@ -120,6 +120,36 @@ def test_random_specs_and_magnitudes(case):
     check(y, oracle_full(p, mode), mode, f"random case {case}")
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_few_row_forms(case):
+    """Seeded random problems on the matrix-vector path for 2 <= M <= 128:
+    any code widths and group sizes, H from 64 to 2560 (ragged in chunk
+    quads), ragged I, both activation types, every mode, with the library's
+    choice or a forced column-tile count, x source and quads per wave."""
+    rng = np.random.default_rng(900 + case)
+    narrow = case % 3 != 0
+    if narrow:
+        bits_g = bits_u = int(rng.choice([2, 4]))
+    else:
+        bits_g, bits_u = (int(b) for b in rng.choice([2, 4, 8], 2))
+    gs_g, gs_u = (int(g) for g in rng.choice([32, 64, 128], 2))
+    step = max(gs_g, gs_u)
+    M = int(rng.choice([2, 5, 8, 11, 16, 17, 25, 32, 33, 47, 64, 65, 100, 128]))
+    H = step * int(rng.integers(1, 2560 // step + 1))
+    I = int(rng.integers(1, 700))
+    act = "f16" if case % 4 == 1 else "bf16"
+    mode = case % 3
+    ct = [None, 1, 2][case % 3]
+    quads = 1 if case % 5 == 2 else None
+    source = "prep" if case % 7 == 3 else None
+    p = make_custom(M, H, I, bits_g, gs_g, bits_u, gs_u, seed=1000 + case, act=act)
+    say("random few-row", M, H, I, (bits_g, gs_g, bits_u, gs_u), act, "mode", mode, "ct", ct, "quads", quads,
+        "x source", source)
+    with skinny_ct(ct, quads), skinny_x(source):
+        y = device_forward(p, mode, GEMV)
+    check(y, oracle_full(p, mode), mode, f"random few-row case {case}")
+
+
 # ------------------------------------------- scale and bias magnitudes --
 
 # Scales and biases anywhere in bf16's range: each weight row's scales and
