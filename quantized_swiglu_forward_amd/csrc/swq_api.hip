@@ -20,6 +20,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -186,12 +187,43 @@ int choose_column_split(int64_t M, int64_t I, int cfg, int bits_g, int bits_u) {
   return (int)(128 * nt1);
 }
 
+// K split of the MFMA path: with few 128 x 128 tiles (at most half the CUs)
+// and H >= 2048, each tile's code K-steps are split across blocks in whole
+// super-steps (at least four per split), up to 8 ways, within 24 MB of
+// float32 partial sums; a second kernel adds the splits in order and runs
+// the epilogue.  Shorter splits, or more partial sums, measured slower (at
+// H = 1024 the split loses from M = 128 on).  Forward
+// precision modes only.  SWIGLU_Q_MFMA_KSPLIT=n caps the splits at n (0 or 1:
+// no split).
+struct KSplit {
+  int n = 1;       // splits (1: none)
+  int chunk = 0;   // code K-steps per split
+};
+KSplit choose_ksplit(int64_t M, int64_t H, int64_t I, int cfg, int n_split) {
+  KSplit k;
+  int64_t cap = 8;
+  if (const char* s = getenv("SWIGLU_Q_MFMA_KSPLIT"); s && *s) cap = std::min<int64_t>(cap, atol(s));
+  if (cap < 2 || cfg != 1 || n_split != 0 || M <= 0 || I <= 0) return k;
+  const int64_t cus = device_cus();
+  const int64_t tiles = ((M + 127) / 128) * ((I + 127) / 128), steps = H / 32;
+  if (2 * tiles > cus || steps < 64) return k;
+  int64_t n = std::min<int64_t>(std::min<int64_t>(cus / tiles, steps / 16), cap);
+  while (n > 1 && n * 2 * M * I * 4 > (int64_t(24) << 20)) --n;
+  if (n < 2) return k;
+  const int64_t chunk = ((steps + n - 1) / n + 3) / 4 * 4;
+  const int64_t nn = (steps + chunk - 1) / chunk;
+  if (nn < 2) return k;
+  k.n = (int)nn;
+  k.chunk = (int)chunk;
+  return k;
+}
+
 // Workspace of the matrix-matrix path, in order: x' rows [M, H + kext]
 // (binary16), row exponents [M] (int32), the extra-column B rows [I, kext]
 // (binary16) of the gate and of the up matrix, the scale tiles (4 KB per
 // 128 columns and 128 inputs), then the weight rows' exponents k [2][I] (int32).
 struct WsLayout {
-  int64_t xa, xexp, eg, eu, sc, kx, total;
+  int64_t xa, xexp, eg, eu, sc, kx, part, total;
 };
 
 int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -207,9 +239,11 @@ WsLayout ws_layout(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g, int bi
   w.sc = w.eu + plane;
   const int64_t tiles = (I + kScaleTileCols - 1) / kScaleTileCols * ((H + 127) / 128);
   w.kx = w.sc + align256(tiles * kScaleTileWords * 4);
-  w.total = w.kx + align256(2 * I * 4);
-  (void)bits_g;
-  (void)bits_u;
+  w.part = w.kx + align256(2 * I * 4);
+  // the K split's float32 partial sums (gate, up) per split, when it applies
+  const int cfg = choose_mfma_config(M, I);
+  const KSplit ks = choose_ksplit(M, H, I, cfg, choose_column_split(M, I, cfg, bits_g, bits_u));
+  w.total = w.part + (ks.n > 1 ? align256(2 * (int64_t)ks.n * M * I * 4) : 0);
   return w;
 }
 
@@ -377,6 +411,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   p.kexp = pp.kexp;
   p.mode = mode; p.out = out; p.dbg_g = dbg_g; p.dbg_u = dbg_u; p.res = (const uint16_t*)res;
   p.act = act;
+  p.kchunk = 0;
   {
     const auto a16 = [](const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; };
     p.vec = (I % 4 == 0) && (ldo % 4 == 0) && a16(out) && a16(dbg_g) && a16(dbg_u);
@@ -387,9 +422,24 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) split %d M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
             cfg, kMfmaBM[cfg], kMfmaBN[cfg], n_split, (long long)M, (long long)H, (long long)I, bits_g, bits_u,
             gs_g, gs_u, mode);
+  // the forward's modes may split K (choose_ksplit): partial sums in the
+  // workspace, then the second pass writes the output
+  const KSplit ks = (mode >= SWQ_MATCH && mode <= SWQ_F32_BF16OUT && !dbg_g) ? choose_ksplit(M, H, I, cfg, n_split)
+                                                                              : KSplit{};
   (void)hipGetLastError();
   if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
-  if (launch_mfma(p, cfg, n_split, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
+  if (ks.n > 1) {
+    MfmaParams q = p;
+    q.dbg_g = (float*)(wsb + L.part);
+    q.dbg_u = q.dbg_g + (int64_t)ks.n * M * ldo;
+    q.kchunk = ks.chunk;
+    q.vec = (I % 4 == 0) && (ldo % 4 == 0);
+    if (logging()) fprintf(stderr, "[swiglu_q] mfma K split %d x %d K-steps\n", ks.n, ks.chunk);
+    if (launch_mfma(q, cfg, 0, ks.n, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
+    if (launch_ksplit_epilogue(q, ks.n, stream) != hipSuccess) return SWQ_ERR_HIP;
+  } else if (launch_mfma(p, cfg, n_split, 1, bits_g, bits_u, stream) != hipSuccess) {
+    return SWQ_ERR_HIP;
+  }
   g_calls[SWQ_PATH_MFMA].fetch_add(1, std::memory_order_relaxed);
   return SWQ_OK;
 }

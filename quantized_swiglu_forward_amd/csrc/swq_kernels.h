@@ -76,6 +76,7 @@ struct MfmaParams {
   const uint16_t* res; // the linear only: bf16 [M, ldo] added to its sums before the store, or null
   int vec;             // 1: the output rows allow 16-byte (f32) / 8-byte (bf16) stores of 4 features
   int act;             // kActBf16 or kActF16 (output type of modes 0 and 2, MATCH rounding)
+  int kchunk;          // K split: code K-steps per split (a multiple of 4), else 0
 };
 
 struct GemvParams {
@@ -163,7 +164,12 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // cfg: tile shape (kMfmaBM/kMfmaBN); n_split > 0 with cfg 0: columns
 // [0, n_split) as 256 x 128 tiles and [n_split, I) as 128 x 128 tiles, two launches.
-hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream);
+// ksplit > 1: 128 x 128 tiles with the code K-steps split ksplit ways
+// (p.kchunk each), the float32 sums of split k at dbg_g / dbg_u + k M ldo.
+hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int ksplit, int bits_g, int bits_u,
+                       hipStream_t stream);
+// The K split's second pass: out = epilogue(sum over the splits), forward modes.
+hipError_t launch_ksplit_epilogue(const MfmaParams& p, int ksplit, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
 // the instances of one activation type (kActBf16 / kActF16), each compiled in
 // its own translation unit

@@ -474,7 +474,7 @@ __device__ __forceinline__ void dequant_block(const uint32_t* w, f16x2 s2, f16x8
 template <int BITS, bool A16>
 inline constexpr int kPlanes = (kCodeWidth<BITS> == 8 ? 2 : 1) + (A16 ? 1 : 0);
 
-template <int BITS_G, int BITS_U, int BM, int WN, int OCC, bool A16>
+template <int BITS_G, int BITS_U, int BM, int WN, int OCC, bool A16, bool KSPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void swq_mfma_kernel(MfmaParams p) {
   constexpr int NT = 256;
   constexpr int STAGES = 4;                            // x' / extra-column ring: K-steps in flight
@@ -542,6 +542,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   const int s_main = p.H / 32;
   const int s_ext = p.kext / 32;
   const int s_total = s_main + 2 * s_ext;              // extra-column steps: gate then up, per 32 columns
+  // K split (KSPLIT; grid y = the splits): this block runs the code K-steps
+  // [kb0, kb1) (p.kchunk per split, whole super-steps) and, in the last
+  // split, the extra columns; its float32 sums go to its own slice of the
+  // partial buffers (dbg_g, dbg_u), which swq_ksplit_epilogue adds in split
+  // order and finishes
+  const int kb0 = KSPLIT ? (int)blockIdx.y * p.kchunk : 0;
+  const int kb1 = KSPLIT ? min(s_main, kb0 + p.kchunk) : s_main;
+  const bool klast = !KSPLIT || kb1 == s_main;
   const int rw_g = p.H * BITS_G / 32, rw_u = p.H * BITS_U / 32;
 
   // x' tile rows of K-step s: (s * M + m0 + row) * 64 bytes from the start of x'
@@ -834,29 +842,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   };
 
   // ---- prologue: super-step 0 and K-steps 0 .. 2 in flight, step 0 complete, its first operands read
-  issue_ss(0);
-  issue(0, 0, 0 >= s_main);
-  issue(1, 1, 1 >= s_main);
-  issue(2, 2, 2 >= s_main);
-  if (2 < s_main) {
+  issue_ss(kb0 / SS);
+  issue(0, kb0, kb0 >= s_main);
+  issue(1, kb0 + 1, kb0 + 1 >= s_main);
+  issue(2, kb0 + 2, kb0 + 2 >= s_main);
+  if (kb0 + 2 < s_main) {
     wait_vmcnt<2 * N_MAIN>();
-  } else if (1 < s_main) {
+  } else if (kb0 + 1 < s_main) {
     wait_vmcnt<N_MAIN + N_EXT>();
   } else {
     wait_vmcnt<2 * N_EXT>();
   }
   block_barrier();
   read_a(0, 0, a0);
-  if (0 < s_main) {
-    load_codes(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0]);
+  if (kb0 < s_main) {
+    load_codes(kb0, cw_g[0], cw_u[0], s_g2[0], s_u2[0]);
     dequant(0, cw_g[0], cw_u[0], s_g2[0], s_u2[0], g0a, g0b, g0c, u0a, u0b, u0c);
   } else {
     read_ext(0, 0, g0a);
   }
 
   // ---- K loop: code steps, the last three code steps, extra-column steps in gate/up pairs
-  const int t_code = max(0, s_main - 3);
-  int t = 0;
+  const int t_code = max(kb0, kb1 - 3);
+  int t = kb0;
   for (; t + STAGES <= t_code; t += STAGES) {
     step.template operator()<0, 0, false>(t, 0);
     step.template operator()<0, 1, false>(t + 1, 1);
@@ -864,12 +872,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     step.template operator()<0, 1, false>(t + 3, 3);
   }
   for (; t < t_code; ++t) step.template operator()<0>(t, t % STAGES);
-  if (s_main >= 3) step.template operator()<3>(s_main - 3, (s_main - 3) % STAGES);
-  if (s_main >= 2) step.template operator()<2>(s_main - 2, (s_main - 2) % STAGES);
-  step.template operator()<1>(s_main - 1, (s_main - 1) % STAGES);
-  for (t = s_main; t < s_total; t += 2) {
-    step.template operator()<-1>(t, t % STAGES);
-    step.template operator()<-2>(t + 1, (t + 1) % STAGES);
+  if (kb1 - kb0 >= 3) step.template operator()<3>(kb1 - 3, (kb1 - 3) % STAGES);
+  if (kb1 - kb0 >= 2) step.template operator()<2>(kb1 - 2, (kb1 - 2) % STAGES);
+  step.template operator()<1>(kb1 - 1, (kb1 - 1) % STAGES);
+  if (klast) {
+    for (t = s_main; t < s_total; t += 2) {
+      step.template operator()<-1>(t, t % STAGES);
+      step.template operator()<-2>(t + 1, (t + 1) % STAGES);
+    }
   }
   wait_vmcnt<0>();                                   // nothing left in flight at exit
   if (tid < BM) rexp[tid] = my_exp;
@@ -927,8 +937,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
           if (!row_ok) continue;
           const int64_t o = orow + c0;
           if constexpr (MODE == 3) {
-            put4(p.dbg_g, o, c0, p.n_end, g);
-            put4(p.dbg_u, o, c0, p.n_end, u);
+            const int64_t ko = KSPLIT ? (int64_t)blockIdx.y * p.M * p.ldo : 0;   // this split's slice
+            put4(p.dbg_g + ko, o, c0, p.n_end, g);
+            put4(p.dbg_u + ko, o, c0, p.n_end, u);
           } else if constexpr (LIN) {
             if (p.res) {   // the residual of a whole MLP, added in float32 before the one rounding
               const int lg_ = p.n_end - c0, lu_ = min(p.n_end, p.I_u) - c0;
@@ -966,22 +977,50 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The K split's second pass: for each output (m, n) the splits' float32
+// gate and up sums (true scale), added in split order, then the epilogue of
+// the precision mode (the forward's modes only).
+__global__ __launch_bounds__(256) void swq_ksplit_epilogue(MfmaParams p, int ksplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)p.M * p.I) return;
+  const int m = (int)(i / p.I), n = (int)(i - (int64_t)m * p.I);
+  const int64_t o = (int64_t)m * p.ldo + n, slice = (int64_t)p.M * p.ldo;
+  float g = p.dbg_g[o], u = p.dbg_u[o];
+  for (int k = 1; k < ksplit; ++k) {
+    g += p.dbg_g[k * slice + o];
+    u += p.dbg_u[k * slice + o];
+  }
+  const float h = swiglu_epilogue(g, u, p.mode, p.act);
+  if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
+  else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(h, p.act);
+}
+
+hipError_t launch_ksplit_epilogue(const MfmaParams& p, int ksplit, hipStream_t stream) {
+  const int64_t n = (int64_t)p.M * p.I;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swq_ksplit_epilogue, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, ksplit);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream) {
   const int64_t blocks = p.M + (p.k_only ? prep_row_blocks(p.I, p.kext) : 0);
   hipLaunchKernelGGL(swq_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int BG, int BU, int BM, int WN, int OCC, bool A16 = false>
-static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream) {
+template <int BG, int BU, int BM, int WN, int OCC, bool A16 = false, bool KSPLIT = false>
+static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream, int ksplit = 1) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.n_end - p.n_begin + 4 * WN - 1) / (4 * WN));
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC, A16>), dim3(tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((swq_mfma_kernel<BG, BU, BM, WN, OCC, A16, KSPLIT>), dim3(tiles, KSPLIT ? ksplit : 1), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 
 template <int BG, int BU, bool A16>
-static hipError_t launch_mfma_cfg(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
+static hipError_t launch_mfma_cfg(const MfmaParams& p, int cfg, int n_split, int ksplit, hipStream_t stream) {
+  // K split: 128-row tiles, the splits along grid y (the host's choice: few tiles)
+  if (ksplit > 1) return launch_mfma_t<BG, BU, 128, 32, 1, A16, true>(p, stream, ksplit);
   // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
   if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1, A16>(p, stream);
   if constexpr (!(BG == 8 && BU == 8)) {
@@ -999,23 +1038,24 @@ static hipError_t launch_mfma_cfg(const MfmaParams& p, int cfg, int n_split, hip
 
 // binary16 activations take the instances with the split-scale planes
 template <int BG, int BU>
-static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, hipStream_t stream) {
-  if (p.act == kActF16) return launch_mfma_cfg<BG, BU, true>(p, cfg, n_split, stream);
-  return launch_mfma_cfg<BG, BU, false>(p, cfg, n_split, stream);
+static hipError_t launch_mfma_bits(const MfmaParams& p, int cfg, int n_split, int ksplit, hipStream_t stream) {
+  if (p.act == kActF16) return launch_mfma_cfg<BG, BU, true>(p, cfg, n_split, ksplit, stream);
+  return launch_mfma_cfg<BG, BU, false>(p, cfg, n_split, ksplit, stream);
 }
 
 template <int BG>
-static hipError_t launch_mfma_g(const MfmaParams& p, int cfg, int n_split, int bits_u, hipStream_t stream) {
-  if (bits_u == 2) return launch_mfma_bits<BG, 2>(p, cfg, n_split, stream);
-  if (bits_u == 4) return launch_mfma_bits<BG, 4>(p, cfg, n_split, stream);
-  if (bits_u == 8) return launch_mfma_bits<BG, 8>(p, cfg, n_split, stream);
+static hipError_t launch_mfma_g(const MfmaParams& p, int cfg, int n_split, int ksplit, int bits_u, hipStream_t stream) {
+  if (bits_u == 2) return launch_mfma_bits<BG, 2>(p, cfg, n_split, ksplit, stream);
+  if (bits_u == 4) return launch_mfma_bits<BG, 4>(p, cfg, n_split, ksplit, stream);
+  if (bits_u == 8) return launch_mfma_bits<BG, 8>(p, cfg, n_split, ksplit, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int bits_g, int bits_u, hipStream_t stream) {
-  if (bits_g == 2) return launch_mfma_g<2>(p, cfg, n_split, bits_u, stream);
-  if (bits_g == 4) return launch_mfma_g<4>(p, cfg, n_split, bits_u, stream);
-  if (bits_g == 8) return launch_mfma_g<8>(p, cfg, n_split, bits_u, stream);
+hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int ksplit, int bits_g, int bits_u,
+                       hipStream_t stream) {
+  if (bits_g == 2) return launch_mfma_g<2>(p, cfg, n_split, ksplit, bits_u, stream);
+  if (bits_g == 4) return launch_mfma_g<4>(p, cfg, n_split, ksplit, bits_u, stream);
+  if (bits_g == 8) return launch_mfma_g<8>(p, cfg, n_split, ksplit, bits_u, stream);
   return hipErrorInvalidValue;
 }
 

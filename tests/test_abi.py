@@ -253,6 +253,36 @@ def test_workspace_bytes():
     assert swq.swiglu_q_workspace_bytes(4, 2048, 64, 3, 64, 4, 64) == 0
 
 
+def test_workspace_bytes_k_split(monkeypatch):
+    # few 128 x 128 tiles (at most half of 256 CUs) and H >= 2048: the K
+    # split's float32 partial sums (gate and up, [splits, M, I]) follow,
+    # min(256 / tiles, K-steps / 16, 8) splits within 24 MB
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    def base(M, H, I):
+        ext = (3 * (H // 64) + 31) // 32 * 32
+        tiles = (I + 127) // 128 * ((H + 127) // 128)
+        return a256(M * (H + ext) * 2) + a256(M * 4) + 2 * a256(I * ext * 2) + a256(tiles * 4096) + a256(2 * I * 4)
+
+    ws = lambda M, H, I: swq.swiglu_q_workspace_bytes(M, H, I, 4, 64, 4, 64)
+    monkeypatch.delenv("SWIGLU_Q_MFMA_KSPLIT", raising=False)
+    # 44 tiles, 64 K-steps: four splits
+    assert ws(65, 2048, 5632) == base(65, 2048, 5632) + a256(2 * 4 * 65 * 5632 * 4)
+    # 64 tiles, 128 K-steps: four splits of 33.5 MB lower to three
+    assert ws(128, 4096, 8192) == base(128, 4096, 8192) + a256(2 * 3 * 128 * 8192 * 4)
+    # 3 tiles at H = 4096: eight splits
+    assert ws(96, 4096, 384) == base(96, 4096, 384) + a256(2 * 8 * 96 * 384 * 4)
+    # H = 1024 (32 K-steps) and 2 x 112 tiles: none
+    assert ws(65, 1024, 4096) == base(65, 1024, 4096)
+    assert ws(256, 4096, 14336) == base(256, 4096, 14336)
+    # capped by the environment: three, then none
+    monkeypatch.setenv("SWIGLU_Q_MFMA_KSPLIT", "3")
+    assert ws(96, 4096, 384) == base(96, 4096, 384) + a256(2 * 3 * 96 * 384 * 4)
+    monkeypatch.setenv("SWIGLU_Q_MFMA_KSPLIT", "0")
+    assert ws(96, 4096, 384) == base(96, 4096, 384)
+
+
 def test_few_row_x_source_and_workspace():
     """The few-row kernel converts x itself (no prep launch, no workspace)
     for M <= 16 when a row fits one pass of its waves and their LDS regions
