@@ -40,7 +40,8 @@
  * (swiglu_q_staging_bytes says how much; most calls with 4-bit or 2-bit
  * codes, H <= 2048 and M <= 128 need none),
  * and every matrix-matrix call needs one for x and the weights' extra rows,
- * scale tiles and row exponents: the library keeps one per (device, stream),
+ * scale tiles and row exponents (and, where few output tiles split K across
+ * blocks, the float32 partial sums): the library keeps one per (device, stream),
  * allocated on
  * first use and replaced by a larger one (at least twice the size) when a call
  * needs more.  Growth never synchronises: a replaced buffer is kept, not freed,
@@ -240,9 +241,9 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
  * the MFMA path.  The default comes from the environment variable
  * SWIGLU_Q_MMIN when set to a positive integer, else the built-in default 65
  * (measured: the matrix-vector path is faster for every M <= 32 on every
- * weight shape measured; for 33 <= M <= 64 it is 20-45 % faster with
- * intermediate sizes up to 8192, level at H = 2048, I = 14336, and up to
- * 19 % slower at H = 4096, I = 14336, where T = 33 suits better).
+ * weight shape measured; for 33 <= M <= 64 it is 17-67 % faster where
+ * H * I is below about 2^24, e.g. H = 2048, I = 5632, and 18-57 % slower
+ * above, e.g. H = 4096, I = 14336, where T = 33 suits better).
  * T <= 1 sends every M >= 1 to the MFMA path. */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);
@@ -292,7 +293,9 @@ int swiglu_q_debug_gemm(const void *x,
                         int path, float *gate_out, float *up_out, void *stream);
 
 /* Bytes of workspace the MFMA path uses for this shape (0 when M == 0 or
- * the arguments are invalid). */
+ * the arguments are invalid), including the K split's float32 partial sums
+ * where the shape takes it (the choice depends on the current device's CU
+ * count and on SWIGLU_Q_MFMA_KSPLIT). */
 int64_t swiglu_q_workspace_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int gs_g,
                                  int bits_u, int gs_u);
 

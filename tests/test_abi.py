@@ -256,7 +256,7 @@ def test_workspace_bytes():
 def test_workspace_bytes_k_split(monkeypatch):
     # few 128 x 128 tiles (at most half of 256 CUs) and H >= 2048: the K
     # split's float32 partial sums (gate and up, [splits, M, I]) follow,
-    # min(256 / tiles, K-steps / 16, 8) splits below 32 MB
+    # min(256 / tiles, K-steps / 16, 8) splits, more than two only below 32 MB
     def a256(v):
         return (v + 255) // 256 * 256
 
@@ -276,7 +276,8 @@ def test_workspace_bytes_k_split(monkeypatch):
     # H = 1024 (32 K-steps) and 2 x 112 tiles: none
     assert ws(65, 1024, 4096) == base(65, 1024, 4096)
     assert ws(256, 4096, 14336) == base(256, 4096, 14336)
-    # 112 tiles: two splits (29.4 MB)
+    # 112 tiles: two splits (29.4 MB); 128 tiles: two splits (32 MiB)
+    assert ws(256, 4096, 8192) == base(256, 4096, 8192) + a256(2 * 2 * 256 * 8192 * 4)
     assert ws(128, 4096, 14336) == base(128, 4096, 14336) + a256(2 * 2 * 128 * 14336 * 4)
     # capped by the environment: three, then none
     monkeypatch.setenv("SWIGLU_Q_MFMA_KSPLIT", "3")
