@@ -422,21 +422,27 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
     fprintf(stderr, "[swiglu_q] mfma cfg %d (%dx%d) split %d M=%lld H=%lld I=%lld bits %d/%d gs %d/%d mode %d\n",
             cfg, kMfmaBM[cfg], kMfmaBN[cfg], n_split, (long long)M, (long long)H, (long long)I, bits_g, bits_u,
             gs_g, gs_u, mode);
-  // the forward's modes may split K (choose_ksplit): partial sums in the
-  // workspace, then the second pass writes the output
-  const KSplit ks = (mode >= SWQ_MATCH && mode <= SWQ_F32_BF16OUT && !dbg_g) ? choose_ksplit(M, H, I, cfg, n_split)
-                                                                              : KSplit{};
+  // the forward's and the linear's modes may split K (choose_ksplit): partial
+  // sums in the workspace ([split][M][I], rows of I), then the second pass
+  // writes the output
+  const bool can_split = mode == SWQ_MATCH || mode == SWQ_F32 || mode == SWQ_F32_BF16OUT || mode == kLinBf16 ||
+                         mode == kLinF32;
+  const KSplit ks = (can_split && !dbg_g) ? choose_ksplit(M, H, I, cfg, n_split) : KSplit{};
   (void)hipGetLastError();
   if (launch_prep(pp, stream) != hipSuccess) return SWQ_ERR_HIP;
   if (ks.n > 1) {
     MfmaParams q = p;
-    q.dbg_g = (float*)(wsb + L.part);
-    q.dbg_u = q.dbg_g + (int64_t)ks.n * M * ldo;
+    float* part_g = (float*)(wsb + L.part);
+    float* part_u = part_g + (int64_t)ks.n * M * I;
+    q.dbg_g = part_g;
+    q.dbg_u = part_u;
+    q.ldo = (int)I;
+    q.res = nullptr;
     q.kchunk = ks.chunk;
-    q.vec = (I % 4 == 0) && (ldo % 4 == 0);
+    q.vec = (I % 4 == 0);
     if (logging()) fprintf(stderr, "[swiglu_q] mfma K split %d x %d K-steps\n", ks.n, ks.chunk);
     if (launch_mfma(q, cfg, 0, ks.n, bits_g, bits_u, stream) != hipSuccess) return SWQ_ERR_HIP;
-    if (launch_ksplit_epilogue(q, ks.n, stream) != hipSuccess) return SWQ_ERR_HIP;
+    if (launch_ksplit_epilogue(p, part_g, part_u, ks.n, stream) != hipSuccess) return SWQ_ERR_HIP;
   } else if (launch_mfma(p, cfg, n_split, 1, bits_g, bits_u, stream) != hipSuccess) {
     return SWQ_ERR_HIP;
   }

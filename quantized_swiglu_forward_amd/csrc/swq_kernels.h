@@ -168,8 +168,10 @@ hipError_t launch_prep_rows(const PrepParams& p, hipStream_t stream);
 // (p.kchunk each), the float32 sums of split k at dbg_g / dbg_u + k M ldo.
 hipError_t launch_mfma(const MfmaParams& p, int cfg, int n_split, int ksplit, int bits_g, int bits_u,
                        hipStream_t stream);
-// The K split's second pass: out = epilogue(sum over the splits), forward modes.
-hipError_t launch_ksplit_epilogue(const MfmaParams& p, int ksplit, hipStream_t stream);
+// The K split's second pass: out = epilogue(sum over the splits) for p.mode
+// (forward or linear), the splits' sums in [ksplit][M][p.I] planes.
+hipError_t launch_ksplit_epilogue(const MfmaParams& p, const float* part_g, const float* part_u, int ksplit,
+                                  hipStream_t stream);
 hipError_t launch_gemv(const GemvParams& p, int bits_g, int bits_u, hipStream_t stream);
 // the instances of one activation type (kActBf16 / kActF16), each compiled in
 // its own translation unit

@@ -977,28 +977,49 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The K split's second pass: for each output (m, n) the splits' float32
-// gate and up sums (true scale), added in split order, then the epilogue of
-// the precision mode (the forward's modes only).
-__global__ __launch_bounds__(256) void swq_ksplit_epilogue(MfmaParams p, int ksplit) {
+// The K split's second pass: for each output feature n < p.I of row m the
+// splits' float32 gate and up sums (true scale; [split][M][p.I] planes),
+// added in split order, then the epilogue of p.mode: the forward's SwiGLU,
+// or the linear's two output columns n and p.I + n (the residual added in
+// float32 before the one rounding).
+__global__ __launch_bounds__(256) void swq_ksplit_epilogue(MfmaParams p, const float* __restrict__ part_g,
+                                                           const float* __restrict__ part_u, int ksplit) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)p.M * p.I) return;
   const int m = (int)(i / p.I), n = (int)(i - (int64_t)m * p.I);
-  const int64_t o = (int64_t)m * p.ldo + n, slice = (int64_t)p.M * p.ldo;
-  float g = p.dbg_g[o], u = p.dbg_u[o];
+  const int64_t slice = (int64_t)p.M * p.I;
+  float g = part_g[i], u = part_u[i];
   for (int k = 1; k < ksplit; ++k) {
-    g += p.dbg_g[k * slice + o];
-    u += p.dbg_u[k * slice + o];
+    g += part_g[k * slice + i];
+    u += part_u[k * slice + i];
+  }
+  const int64_t o = (int64_t)m * p.ldo + n;
+  if (p.mode == kLinBf16 || p.mode == kLinF32) {
+    const bool up = n < p.I_u;
+    if (p.res) {
+      g += bf16_to_f32(p.res[o]);
+      if (up) u += bf16_to_f32(p.res[o + p.I]);
+    }
+    if (p.mode == kLinF32) {
+      reinterpret_cast<float*>(p.out)[o] = g;
+      if (up) reinterpret_cast<float*>(p.out)[o + p.I] = u;
+    } else {
+      reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(g, p.act);
+      if (up) reinterpret_cast<uint16_t*>(p.out)[o + p.I] = f32_to_act(u, p.act);
+    }
+    return;
   }
   const float h = swiglu_epilogue(g, u, p.mode, p.act);
   if (p.mode == kF32) reinterpret_cast<float*>(p.out)[o] = h;
   else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_act(h, p.act);
 }
 
-hipError_t launch_ksplit_epilogue(const MfmaParams& p, int ksplit, hipStream_t stream) {
+hipError_t launch_ksplit_epilogue(const MfmaParams& p, const float* part_g, const float* part_u, int ksplit,
+                                  hipStream_t stream) {
   const int64_t n = (int64_t)p.M * p.I;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swq_ksplit_epilogue, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, ksplit);
+  hipLaunchKernelGGL(swq_ksplit_epilogue, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, part_g,
+                     part_u, ksplit);
   return hipGetLastError();
 }
 

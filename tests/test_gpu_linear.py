@@ -53,14 +53,16 @@ def check_linear(y, p, out_mode, what, ms=None, ns=None):
 
 # (M, K, N, bits, gs, path): N even and odd, N = 1 and 2 (an empty or one-row
 # up slot), tiles past M and N, both paths and bit widths, row groups of 32 on
-# the matrix-vector path
+# the matrix-vector path, the MFMA path's K split
 CASES = [(300, 256, 200, 4, 64, MFMA), (129, 512, 77, 8, 32, MFMA), (64, 1024, 1, 4, 128, MFMA),
          (257, 256, 2, 4, 64, MFMA), (512, 1024, 1000, 4, 64, MFMA), (33, 384, 129, 8, 64, MFMA),
          (1, 2048, 300, 4, 64, GEMV), (1, 5632, 257, 4, 64, GEMV), (3, 1024, 77, 8, 32, GEMV),
          (16, 2048, 130, 4, 64, GEMV), (1, 256, 1, 4, 32, GEMV), (7, 512, 2, 8, 128, GEMV),
          (129, 512, 77, 2, 64, MFMA), (1, 2048, 133, 2, 32, GEMV), (9, 1024, 65, 2, 128, GEMV),
          (4, 2048, 131, 4, 64, GEMV), (2, 4096, 1, 2, 32, GEMV), (3, 3072, 2, 8, 64, GEMV),
-         (40, 2048, 301, 4, 64, GEMV), (100, 1024, 77, 8, 32, GEMV)]
+         (40, 2048, 301, 4, 64, GEMV), (100, 1024, 77, 8, 32, GEMV),
+         # few MFMA tiles with H >= 2048: K split over blocks (odd N: element stores; 4 | Ig: vector stores)
+         (100, 2048, 301, 4, 64, MFMA), (96, 4096, 512, 8, 32, MFMA), (80, 2560, 3, 2, 64, MFMA)]
 
 
 @pytest.mark.parametrize("M,K,N,bits,gs,path", CASES,

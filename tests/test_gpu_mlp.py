@@ -74,6 +74,9 @@ CASES = [
     (129, 256, 320, 201, (2, 64), (2, 64), (2, 32), False, 0),
     (17, 1024, 2048, 1023, (4, 128), (8, 64), (4, 128), True, 0),
     (64, 2048, 4096, 2048, (4, 64), (4, 64), (4, 64), True, 1),
+    # both halves with the MFMA path's K split (few tiles, H and I >= 2048)
+    (100, 2048, 2048, 1001, (4, 64), (4, 64), (4, 64), True, 0),
+    (80, 2048, 2560, 600, (4, 64), (8, 32), (4, 64), True, 1),
 ]
 
 
@@ -93,7 +96,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("M,H,I,Ho", [(1, 2048, 2048, 2048), (3, 2048, 1024, 1024), (9, 512, 1024, 515),
-                                      (300, 512, 768, 512)])
+                                      (300, 512, 768, 512), (100, 2048, 2048, 1001)])
 def test_mlp_equals_forward_then_linear_bitwise(M, H, I, Ho):
     """The whole MLP is the forward in MATCH followed by the linear of the
     down matrix; the residual is added to the linear's float32 sums before
