@@ -564,7 +564,9 @@ def bench_decode_spec(c, steps, warmup):
 def bench_decode_rows(M, steps, warmup):
     """The decode shape (H=2048, I=5632, 4-bit gs64) at a few rows per call:
     1000 calls per step on fresh x rows over the 40 rotating weight sets,
-    recorded into a HIP graph; per-call time and weight bytes per second."""
+    recorded into a HIP graph; per-call time and weight bytes per second.
+    Each call takes the dispatcher's path (the matrix-matrix one, with its K
+    split, at 128 rows)."""
     import torch
 
     import quantized_swiglu_forward_amd as swq
@@ -580,7 +582,8 @@ def bench_decode_rows(M, steps, warmup):
     L = swq.lib()
     ptrs = [tuple(t.data_ptr() for t in s) for s in sets]
     x0, o0 = x.data_ptr(), out.data_ptr()
-    before = swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV)
+    path = swq.swiglu_q_path_for(M, c.H)
+    before = swq.swiglu_q_call_count(path)
 
     def step(sh):
         for i in range(CALLS):
@@ -595,7 +598,7 @@ def bench_decode_rows(M, steps, warmup):
     with torch.cuda.stream(stream):
         step(stream.cuda_stream)
     torch.cuda.synchronize()
-    assert swq.swiglu_q_call_count(swq.SWQ_PATH_GEMV) - before == CALLS, "not the matrix-vector path"
+    assert swq.swiglu_q_call_count(path) - before == CALLS, "not the dispatcher's path"
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         step(torch.cuda.current_stream().cuda_stream)
@@ -614,6 +617,8 @@ def bench_decode_rows(M, steps, warmup):
     alg = wb + M * (c.H + c.I) * 2
     return {"config": f"decode shape M={M} H={c.H} I={c.I}, 4-bit gs64 gate and up, fresh x per call, "
                       f"{ROTATING_SETS} rotating weight sets, hip graph",
+            "path": "matrix-vector" if path == swq.SWQ_PATH_GEMV else
+                    "matrix-matrix (prep, MFMA GEMM with its K split, split epilogue: three launches per call)",
             "avg_launch_us": round(us, 3), "weight_GB_per_s": round(wb / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": alg}
 
@@ -952,7 +957,7 @@ def main():
                      "dtype": r["dtype"], "config": r["config"], "roofline": r["roofline"]})
     if args.workload == "decode" and not args.no_small_batch:
         log("decode, a few rows per call: timing ...")
-        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32, 64)}
+        line["decode_small_batch"] = {f"M{m}": bench_decode_rows(m, max(1, args.steps // 4), 2) for m in (2, 4, 8, 16, 32, 64, 128)}
         torch.cuda.empty_cache()
     if not args.no_prefill:
         log("MFMA probe: sustained f16 rate ...")

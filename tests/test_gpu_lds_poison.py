@@ -4,7 +4,9 @@ use, so a kernel that read LDS it had not written would fail here.  One case
 per kernel and branch: the M = 1 kernel and its several-row form, the
 few-row kernel (x' converted by each wave, built in the block, from the
 prep kernel, two row tiles, two column tiles, rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
-column split, a partial last super-step), the linear and the whole MLP."""
+column split, a partial last super-step, the K split: M = 300, H = 2080
+takes four splits of 20, 20, 20 and 5 K-steps), the linear and the whole
+MLP."""
 import os
 
 import numpy as np
