@@ -582,7 +582,7 @@ def bench_decode_rows(M, steps, warmup):
     L = swq.lib()
     ptrs = [tuple(t.data_ptr() for t in s) for s in sets]
     x0, o0 = x.data_ptr(), out.data_ptr()
-    path = swq.swiglu_q_path_for(M, c.H)
+    path = swq.swiglu_q_path_for(M, c.H, c.I)
     before = swq.swiglu_q_call_count(path)
 
     def step(sh):

@@ -238,21 +238,26 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
 /* M threshold T of the dispatcher: M < T takes SWQ_PATH_GEMV, M >= T takes
  * SWQ_PATH_MFMA; the matrix-vector path takes at most 128 rows (past 32, as
  * row groups of 32 that each read the weights once), so M > 128 always runs
- * the MFMA path.  The default comes from the environment variable
- * SWIGLU_Q_MMIN when set to a positive integer, else the built-in default 65
- * (measured: the matrix-vector path is faster for every M <= 32 on every
- * weight shape measured; for 33 <= M <= 64 it is 17-67 % faster where
- * H * I is below about 2^24, e.g. H = 2048, I = 5632, and 18-57 % slower
- * above, e.g. H = 4096, I = 14336, where T = 33 suits better).
- * T <= 1 sends every M >= 1 to the MFMA path. */
+ * the MFMA path.  T is the value given to swiglu_q_set_m_threshold (T >= 0),
+ * else the environment variable SWIGLU_Q_MMIN when set to a positive integer,
+ * and applies to every weight shape.  Without either, the default rule
+ * applies: T = 65, or T = 33 for weights with H * I >= 2^24.
+ * (Measured: the matrix-vector path is faster for every M <= 32 on every
+ * weight shape measured. For 33 <= M <= 64 it is 17-67 % faster where
+ * H * I is below 2^24, e.g. H = 2048, I = 5632, and 18-57 % slower above,
+ * e.g. H = 4096, I = 14336, where the MFMA path splits K.)
+ * swiglu_q_set_m_threshold with T < 0 restores the default rule; T <= 1
+ * sends every M >= 1 to the MFMA path.  swiglu_q_get_m_threshold returns the
+ * threshold set, else 65 (the default rule's value below 2^24 weights). */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);
 
-/* The path (SWQ_PATH_GEMV or SWQ_PATH_MFMA) a call with M rows and hidden
- * size H takes under the current threshold, by the same rule as the calls
- * (M < T and M <= 128 take the matrix-vector path); -1 for M < 1 or H < 1.
+/* The path (SWQ_PATH_GEMV or SWQ_PATH_MFMA) a call with M rows, hidden size
+ * H and intermediate size I takes under the current threshold, by the same
+ * rule as the calls (M < T and M <= 128 take the matrix-vector path; the
+ * linear's rule is that of I = ceil(N / 2)); -1 for M, H or I below 1.
  * Host only: touches no device. */
-int swiglu_q_path_for(int64_t M, int64_t H);
+int swiglu_q_path_for(int64_t M, int64_t H, int64_t I);
 
 /* Number of forward (and debug) calls that launched each path since load
  * or the last reset.  path: SWQ_PATH_GEMV or SWQ_PATH_MFMA.  Mirrors the

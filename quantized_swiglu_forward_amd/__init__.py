@@ -67,7 +67,7 @@ def load_library(path):
     L.swiglu_q_supported.restype = i32
     L.swiglu_q_set_m_threshold.argtypes = [i32]
     L.swiglu_q_set_m_threshold.restype = None
-    L.swiglu_q_path_for.argtypes = [i64, i64]
+    L.swiglu_q_path_for.argtypes = [i64, i64, i64]
     L.swiglu_q_path_for.restype = i32
     L.swiglu_q_get_m_threshold.argtypes = []
     L.swiglu_q_get_m_threshold.restype = i32
@@ -144,8 +144,8 @@ def swiglu_q_mlp(x, Wg, sg, bg, Wu, su, bu, Wd, sd, bd, residual, M, H, I, Ho, b
                               gs_d, out_mode, _ptr(out), _stream(stream))
 
 
-def swiglu_q_path_for(M, H) -> int:
-    return lib().swiglu_q_path_for(M, H)
+def swiglu_q_path_for(M, H, I) -> int:
+    return lib().swiglu_q_path_for(M, H, I)
 
 
 def swiglu_q_debug_gemm(x, Wg, sg, bg, Wu, su, bu, M, H, I, bits_g, gs_g, bits_u, gs_u, path,

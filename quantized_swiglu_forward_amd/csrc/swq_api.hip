@@ -9,13 +9,14 @@
 // threshold defaults to 2 there, benchmarks are to set it, and it can be set
 // from the environment) and the support predicate of the same file (bf16
 // activations, affine biases, 2-, 4- or 8-bit codes, group size a multiple
-// of 32, H a multiple of 32).  Here the default is 65: measured on this GPU,
-// the matrix-vector kernels beat the matrix-matrix kernel for every M <= 32
-// on every weight shape measured (2-3x on the decode and prefill weight
-// shapes for M <= 16), and with two row groups of 32 (33 <= M <= 64) by
-// 20-45 % on decode-width weights (I up to 8192), level at H = 2048,
-// I = 14336 and up to 19 % behind at H = 4096, I = 14336; the few-row
-// kernel takes at most 128 rows (four groups).
+// of 32, H a multiple of 32).  Here the default is 65, or 33 for weights of
+// at least 2^24 elements (H * I).  Measured on this GPU, the matrix-vector
+// kernels beat the matrix-matrix kernel for every M <= 32 on every weight
+// shape measured (2-3x on the decode and prefill weight shapes for M <= 16).
+// With two row groups of 32 (33 <= M <= 64) they are 17-67 % faster below
+// 2^24 weights.  Above it they are 18-57 % slower than the matrix-matrix
+// kernel with its K split.  The few-row kernel takes at most 128 rows (four
+// groups).  A threshold set by API or environment applies to every shape.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,8 +52,12 @@ int swq::device_cus() {
 
 namespace {
 
-// Default M threshold: the matrix-vector path up to two row groups (M <= 64).
+// Default M thresholds: the matrix-vector path up to two row groups (M <= 64),
+// or up to one (M <= 32) for weights of at least 2^24 elements (H * I), where
+// the MFMA path with its K split is faster from 33 rows on.
 constexpr int kDefaultThreshold = 2 * kGemvMaxM + 1;
+constexpr int kDefaultThresholdWide = kGemvMaxM + 1;
+constexpr int64_t kWideWeights = int64_t(1) << 24;
 
 std::atomic<int> g_threshold{-1};
 std::atomic<uint64_t> g_calls[2];
@@ -85,18 +90,27 @@ std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;
 // graphs captured while they were current, may still read and write them.
 std::vector<std::pair<int, void*>> g_retired;
 
-int threshold_now() {
-  int t = g_threshold.load(std::memory_order_relaxed);
+// The threshold set by swiglu_q_set_m_threshold, else by SWIGLU_Q_MMIN (read
+// once), else -1 (the default rule).
+int explicit_threshold() {
+  const int t = g_threshold.load(std::memory_order_relaxed);
   if (t >= 0) return t;
-  t = kDefaultThreshold;
-  if (const char* s = getenv("SWIGLU_Q_MMIN")) {
-    char* end = nullptr;
-    long v = strtol(s, &end, 10);
-    if (end != s && v > 0 && v < (1L << 30)) t = (int)v;
-  }
-  int expected = -1;
-  g_threshold.compare_exchange_strong(expected, t);
-  return g_threshold.load();
+  static const int env = [] {
+    if (const char* s = getenv("SWIGLU_Q_MMIN")) {
+      char* end = nullptr;
+      long v = strtol(s, &end, 10);
+      if (end != s && v > 0 && v < (1L << 30)) return (int)v;
+    }
+    return -1;
+  }();
+  return env;
+}
+
+// The threshold for weights of H x I.
+int threshold_for(int64_t H, int64_t I) {
+  const int t = explicit_threshold();
+  if (t >= 0) return t;
+  return H * I >= kWideWeights ? kDefaultThresholdWide : kDefaultThreshold;
 }
 
 bool logging() {
@@ -136,8 +150,8 @@ int validate(const void* x, const uint32_t* Wg, const void* sg, const void* bg, 
 bool gemv_fits(int64_t M, int64_t H);
 
 // The dispatcher's rule.
-int auto_path(int64_t M, int64_t H) {
-  return (M < threshold_now() && gemv_fits(M, H)) ? SWQ_PATH_GEMV : SWQ_PATH_MFMA;
+int auto_path(int64_t M, int64_t H, int64_t I) {
+  return (M < threshold_for(H, I) && gemv_fits(M, H)) ? SWQ_PATH_GEMV : SWQ_PATH_MFMA;
 }
 
 bool gemv_fits(int64_t M, int64_t H) {
@@ -313,7 +327,7 @@ int run(const void* x, const uint32_t* Wg, const void* sg, const void* bg, const
   hipStream_t stream = (hipStream_t)stream_v;
   if (M == 0) return SWQ_OK;
   if (path == SWQ_PATH_AUTO) {
-    path = auto_path(M, H);
+    path = auto_path(M, H, I);
   }
   if (path == SWQ_PATH_GEMV && !gemv_fits(M, H)) return SWQ_ERR_UNSUPPORTED;
 
@@ -549,7 +563,7 @@ int swiglu_q_forward_noalloc(const void* x, const uint32_t* Wg, const void* sg, 
   if (!aligned(out, precision_mode == SWQ_F32 ? 4 : 2)) return SWQ_ERR_ALIGN;
   if (M == 0) return SWQ_OK;
   // the size check comes before any HIP call
-  const int path = auto_path(M, H);
+  const int path = auto_path(M, H, I);
   if (staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path) > (int64_t)kScratchBytes) return SWQ_ERR_TOO_LARGE;
   void* ptr = nullptr;
   rc = scratch_address(&ptr);
@@ -605,13 +619,16 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u, in
   return 1;
 }
 
-void swiglu_q_set_m_threshold(int T) { g_threshold.store(T < 0 ? 0 : T); }
+void swiglu_q_set_m_threshold(int T) { g_threshold.store(T < 0 ? -1 : T); }
 
-int swiglu_q_get_m_threshold(void) { return threshold_now(); }
+int swiglu_q_get_m_threshold(void) {
+  const int t = explicit_threshold();
+  return t >= 0 ? t : kDefaultThreshold;
+}
 
-int swiglu_q_path_for(int64_t M, int64_t H) {
-  if (M < 1 || H < 1) return -1;
-  return auto_path(M, H);
+int swiglu_q_path_for(int64_t M, int64_t H, int64_t I) {
+  if (M < 1 || H < 1 || I < 1) return -1;
+  return auto_path(M, H, I);
 }
 
 uint64_t swiglu_q_call_count(int path) {
@@ -656,7 +673,7 @@ int64_t swiglu_q_staging_bytes(int64_t M, int64_t H, int64_t I, int bits_g, int 
                                int path) {
   if (M <= 0 || H <= 0 || I <= 0 || !spec_ok(bits_g, gs_g) || !spec_ok(bits_u, gs_u)) return 0;
   if (H % 32 != 0 || H % gs_g != 0 || H % gs_u != 0) return 0;
-  if (path == SWQ_PATH_AUTO) path = auto_path(M, H);
+  if (path == SWQ_PATH_AUTO) path = auto_path(M, H, I);
   if (path == SWQ_PATH_GEMV && !gemv_fits(M, H)) return 0;
   if (path != SWQ_PATH_GEMV && path != SWQ_PATH_MFMA) return 0;
   return staging_bytes(M, H, I, bits_g, gs_g, bits_u, gs_u, path);

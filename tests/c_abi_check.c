@@ -79,11 +79,11 @@ int main(void) {
     t = swiglu_q_get_m_threshold();
     swiglu_q_set_m_threshold(9);
     expect(swiglu_q_get_m_threshold(), 9, "threshold round trip");
-    expect(swiglu_q_path_for(8, 2048), SWQ_PATH_GEMV, "path of M = 8 under T = 9");
-    expect(swiglu_q_path_for(9, 2048), SWQ_PATH_MFMA, "path of M = 9 under T = 9");
-    expect(swiglu_q_path_for(0, 2048), -1, "path of M = 0");
-    swiglu_q_set_m_threshold(t);
-    expect(swiglu_q_get_m_threshold(), t, "threshold restored");
+    expect(swiglu_q_path_for(8, 2048, 5632), SWQ_PATH_GEMV, "path of M = 8 under T = 9");
+    expect(swiglu_q_path_for(9, 2048, 5632), SWQ_PATH_MFMA, "path of M = 9 under T = 9");
+    expect(swiglu_q_path_for(0, 2048, 5632), -1, "path of M = 0");
+    swiglu_q_set_m_threshold(-1);
+    expect(swiglu_q_get_m_threshold(), t, "default rule restored");
     if (swiglu_q_workspace_bytes(512, 2048, 8192, 4, 64, 4, 64) <= 0) {
         fprintf(stderr, "no workspace size for a valid shape\n");
         ++failures;

@@ -21,8 +21,8 @@ def say(*a):
 
 @contextlib.contextmanager
 def forced_path(path, M):
-    """Make the dispatcher pick ``path`` for M rows via the threshold setter."""
-    old = swq.swiglu_q_get_m_threshold()
+    """Make the dispatcher pick ``path`` for M rows via the threshold setter
+    (the default rule afterwards)."""
     if path == swq.SWQ_PATH_GEMV:
         swq.swiglu_q_set_m_threshold(M + 1)
     elif path == swq.SWQ_PATH_MFMA:
@@ -30,7 +30,7 @@ def forced_path(path, M):
     try:
         yield
     finally:
-        swq.swiglu_q_set_m_threshold(old)
+        swq.swiglu_q_set_m_threshold(-1)
 
 
 @contextlib.contextmanager

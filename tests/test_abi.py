@@ -179,39 +179,63 @@ def test_supported_predicate():
 
 
 def test_threshold_roundtrip():
-    old = swq.swiglu_q_get_m_threshold()
     try:
         swq.swiglu_q_set_m_threshold(9)
         assert swq.swiglu_q_get_m_threshold() == 9
-        swq.swiglu_q_set_m_threshold(-5)
+        swq.swiglu_q_set_m_threshold(0)
         assert swq.swiglu_q_get_m_threshold() == 0
+        swq.swiglu_q_set_m_threshold(-5)   # back to the default rule
+        assert swq.swiglu_q_get_m_threshold() == 65
     finally:
-        swq.swiglu_q_set_m_threshold(old)
+        swq.swiglu_q_set_m_threshold(-1)
+
+
+def test_default_rule_by_weight_size():
+    """Without a threshold set, M < 65 takes the matrix-vector path for
+    weights below 2^24 elements (H * I) and M < 33 for larger ones; a
+    threshold set by API applies to every shape."""
+    swq.swiglu_q_set_m_threshold(-1)
+    try:
+        for M in (1, 17, 32, 33, 48, 64):
+            assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_GEMV, M
+            assert swq.swiglu_q_path_for(M, 2048, 8191) == swq.SWQ_PATH_GEMV, M   # just below 2^24
+        for M in (65, 128, 129):
+            assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_MFMA, M
+        for M in (1, 16, 32):
+            assert swq.swiglu_q_path_for(M, 4096, 14336) == swq.SWQ_PATH_GEMV, M
+            assert swq.swiglu_q_path_for(M, 2048, 8192) == swq.SWQ_PATH_GEMV, M   # exactly 2^24
+        for M in (33, 48, 64, 128):
+            assert swq.swiglu_q_path_for(M, 4096, 14336) == swq.SWQ_PATH_MFMA, M
+            assert swq.swiglu_q_path_for(M, 2048, 8192) == swq.SWQ_PATH_MFMA, M
+        swq.swiglu_q_set_m_threshold(65)
+        assert swq.swiglu_q_path_for(64, 4096, 14336) == swq.SWQ_PATH_GEMV
+    finally:
+        swq.swiglu_q_set_m_threshold(-1)
 
 
 def test_dispatcher_choice_given_m_and_threshold():
     """M < T takes the matrix-vector path while it fits (M <= 128, row groups
     of 32 past 32 rows), else the MFMA path; T <= 1 sends everything to
     MFMA; invalid sizes give -1."""
-    old = swq.swiglu_q_get_m_threshold()
     try:
         swq.swiglu_q_set_m_threshold(33)
         for M in (1, 2, 4, 5, 16, 17, 32):
-            assert swq.swiglu_q_path_for(M, 2048) == swq.SWQ_PATH_GEMV, M
+            assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_GEMV, M
         for M in (33, 64, 2048):
-            assert swq.swiglu_q_path_for(M, 2048) == swq.SWQ_PATH_MFMA, M
+            assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_MFMA, M
         swq.swiglu_q_set_m_threshold(9)
-        assert swq.swiglu_q_path_for(8, 4096) == swq.SWQ_PATH_GEMV
-        assert swq.swiglu_q_path_for(9, 4096) == swq.SWQ_PATH_MFMA
+        assert swq.swiglu_q_path_for(8, 4096, 14336) == swq.SWQ_PATH_GEMV
+        assert swq.swiglu_q_path_for(9, 4096, 14336) == swq.SWQ_PATH_MFMA
         swq.swiglu_q_set_m_threshold(200)
-        assert swq.swiglu_q_path_for(32, 256) == swq.SWQ_PATH_GEMV
-        assert swq.swiglu_q_path_for(128, 256) == swq.SWQ_PATH_GEMV  # four row groups of 32
-        assert swq.swiglu_q_path_for(129, 256) == swq.SWQ_PATH_MFMA   # past the matrix-vector limit
+        assert swq.swiglu_q_path_for(32, 256, 768) == swq.SWQ_PATH_GEMV
+        assert swq.swiglu_q_path_for(128, 256, 768) == swq.SWQ_PATH_GEMV  # four row groups of 32
+        assert swq.swiglu_q_path_for(129, 256, 768) == swq.SWQ_PATH_MFMA   # past the matrix-vector limit
         swq.swiglu_q_set_m_threshold(1)
-        assert swq.swiglu_q_path_for(1, 2048) == swq.SWQ_PATH_MFMA
-        assert swq.swiglu_q_path_for(0, 2048) == -1 and swq.swiglu_q_path_for(4, 0) == -1
+        assert swq.swiglu_q_path_for(1, 2048, 5632) == swq.SWQ_PATH_MFMA
+        assert swq.swiglu_q_path_for(0, 2048, 5632) == -1 and swq.swiglu_q_path_for(4, 0, 5632) == -1
+        assert swq.swiglu_q_path_for(4, 2048, 0) == -1
     finally:
-        swq.swiglu_q_set_m_threshold(old)
+        swq.swiglu_q_set_m_threshold(-1)
 
 
 def test_threshold_default_from_environment():

@@ -108,7 +108,6 @@ def test_ksplit_graph_replays():
     p = make_custom(80, 2048, 600, 4, 64, 4, 64, seed=9)
     assert splits(p)
     x, wg, sg, bg, wu, su, bu = swq.to_device(p)
-    old = swq.swiglu_q_get_m_threshold()
     swq.swiglu_q_set_m_threshold(1)
     try:
         say("K split eager")
@@ -132,4 +131,4 @@ def test_ksplit_graph_replays():
             torch.cuda.synchronize()
             del other
     finally:
-        swq.swiglu_q_set_m_threshold(old)
+        swq.swiglu_q_set_m_threshold(-1)

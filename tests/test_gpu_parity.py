@@ -40,7 +40,7 @@ def test_config0_full(mode, path):
 def test_config0_default_dispatch():
     p = make_problem(0)
     say("config0 default dispatch")
-    expect = GEMV if p.M < swq.swiglu_q_get_m_threshold() else MFMA
+    expect = swq.swiglu_q_path_for(p.M, p.H, p.I)
     y = device_forward(p, 0, None, expect_path=expect)
     check(y, oracle_full(p, 0), 0, "c0 default")
 
@@ -298,7 +298,7 @@ def test_decode_rows_match_single_row_calls(M, H, I):
 def test_config1_decode_full(mode):
     p = make_problem(1)
     say("config1 decode full", "mode", mode)
-    y = device_forward(p, mode, None, expect_path=GEMV if 1 < swq.swiglu_q_get_m_threshold() else MFMA)
+    y = device_forward(p, mode, None, expect_path=swq.swiglu_q_path_for(1, p.H, p.I))
     check(y, oracle_full(p, mode), mode, f"c1 mode{mode}")
 
 
