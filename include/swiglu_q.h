@@ -241,14 +241,16 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
  * the MFMA path.  T is the value given to swiglu_q_set_m_threshold (T >= 0),
  * else the environment variable SWIGLU_Q_MMIN when set to a positive integer,
  * and applies to every weight shape.  Without either, the default rule
- * applies: T = 65, or T = 33 for weights with H * I >= 2^24.
+ * applies: T = 65, or T = 33 for wide weights (H * I >= 3 * 2^23 with
+ * I >= 4096; the linear's I is ceil(N / 2)).
  * (Measured: the matrix-vector path is faster for every M <= 32 on every
- * weight shape measured. For 33 <= M <= 64 it is 17-67 % faster where
- * H * I is below 2^24, e.g. H = 2048, I = 5632, and 18-57 % slower above,
- * e.g. H = 4096, I = 14336, where the MFMA path splits K.)
+ * weight shape measured.  For 33 <= M <= 64 it is 17-67 % faster up to
+ * H * I = 2^24, e.g. H = 2048, I = 5632, and on fewer columns.  It is
+ * 18-57 % slower on wide weights, e.g. H = 4096, I = 14336, where the MFMA
+ * path splits K.)
  * swiglu_q_set_m_threshold with T < 0 restores the default rule; T <= 1
  * sends every M >= 1 to the MFMA path.  swiglu_q_get_m_threshold returns the
- * threshold set, else 65 (the default rule's value below 2^24 weights). */
+ * threshold set, else 65 (the default rule's value for weights that are not wide). */
 void swiglu_q_set_m_threshold(int T);
 int swiglu_q_get_m_threshold(void);
 

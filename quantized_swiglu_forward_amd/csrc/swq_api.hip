@@ -9,13 +9,14 @@
 // threshold defaults to 2 there, benchmarks are to set it, and it can be set
 // from the environment) and the support predicate of the same file (bf16
 // activations, affine biases, 2-, 4- or 8-bit codes, group size a multiple
-// of 32, H a multiple of 32).  Here the default is 65, or 33 for weights of
-// at least 2^24 elements (H * I).  Measured on this GPU, the matrix-vector
-// kernels beat the matrix-matrix kernel for every M <= 32 on every weight
-// shape measured (2-3x on the decode and prefill weight shapes for M <= 16).
-// With two row groups of 32 (33 <= M <= 64) they are 17-67 % faster below
-// 2^24 weights.  Above it they are 18-57 % slower than the matrix-matrix
-// kernel with its K split.  The few-row kernel takes at most 128 rows (four
+// of 32, H a multiple of 32).  Here the default is 65, or 33 for wide
+// weights (H * I >= 3 * 2^23 with I >= 4096).  Measured on this GPU, the
+// matrix-vector kernels beat the matrix-matrix kernel for every M <= 32 on
+// every weight shape measured (2-3x on the decode and prefill weight shapes
+// for M <= 16).  With two row groups of 32 (33 <= M <= 64) they are faster
+// on weights up to 2^24 elements (17-67 %) and on fewer than 4096 columns.
+// On wide weights they are 18-57 % slower than the matrix-matrix kernel with
+// its K split.  The few-row kernel takes at most 128 rows (four
 // groups).  A threshold set by API or environment applies to every shape.
 #include <stdio.h>
 #include <stdlib.h>
@@ -53,11 +54,14 @@ int swq::device_cus() {
 namespace {
 
 // Default M thresholds: the matrix-vector path up to two row groups (M <= 64),
-// or up to one (M <= 32) for weights of at least 2^24 elements (H * I), where
-// the MFMA path with its K split is faster from 33 rows on.
+// or up to one (M <= 32) for wide weights (H * I >= 3 * 2^23 and I >= 4096),
+// where the MFMA path with its K split is faster from 33 rows on.  With
+// fewer columns its split blocks do not fill the chip (a linear of 2048
+// columns per slot and K = 14336: 57.5 against 41.5 us at M = 48).
 constexpr int kDefaultThreshold = 2 * kGemvMaxM + 1;
 constexpr int kDefaultThresholdWide = kGemvMaxM + 1;
-constexpr int64_t kWideWeights = int64_t(1) << 24;
+constexpr int64_t kWideWeights = int64_t(3) << 23;
+constexpr int64_t kWideColumns = 4096;
 
 std::atomic<int> g_threshold{-1};
 std::atomic<uint64_t> g_calls[2];
@@ -110,7 +114,7 @@ int explicit_threshold() {
 int threshold_for(int64_t H, int64_t I) {
   const int t = explicit_threshold();
   if (t >= 0) return t;
-  return H * I >= kWideWeights ? kDefaultThresholdWide : kDefaultThreshold;
+  return (H * I >= kWideWeights && I >= kWideColumns) ? kDefaultThresholdWide : kDefaultThreshold;
 }
 
 bool logging() {

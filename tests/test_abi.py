@@ -191,22 +191,25 @@ def test_threshold_roundtrip():
 
 
 def test_default_rule_by_weight_size():
-    """Without a threshold set, M < 65 takes the matrix-vector path for
-    weights below 2^24 elements (H * I) and M < 33 for larger ones; a
-    threshold set by API applies to every shape."""
+    """Without a threshold set, M < 65 takes the matrix-vector path, or
+    M < 33 for wide weights (H * I >= 3 * 2^23 with I >= 4096); a threshold
+    set by API applies to every shape."""
     swq.swiglu_q_set_m_threshold(-1)
     try:
         for M in (1, 17, 32, 33, 48, 64):
             assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_GEMV, M
-            assert swq.swiglu_q_path_for(M, 2048, 8191) == swq.SWQ_PATH_GEMV, M   # just below 2^24
+            assert swq.swiglu_q_path_for(M, 2048, 8192) == swq.SWQ_PATH_GEMV, M    # 2^24
+            assert swq.swiglu_q_path_for(M, 2048, 12287) == swq.SWQ_PATH_GEMV, M   # just below 3 * 2^23
+            assert swq.swiglu_q_path_for(M, 14336, 2048) == swq.SWQ_PATH_GEMV, M   # 2048 columns
         for M in (65, 128, 129):
             assert swq.swiglu_q_path_for(M, 2048, 5632) == swq.SWQ_PATH_MFMA, M
         for M in (1, 16, 32):
             assert swq.swiglu_q_path_for(M, 4096, 14336) == swq.SWQ_PATH_GEMV, M
-            assert swq.swiglu_q_path_for(M, 2048, 8192) == swq.SWQ_PATH_GEMV, M   # exactly 2^24
+            assert swq.swiglu_q_path_for(M, 2048, 12288) == swq.SWQ_PATH_GEMV, M
         for M in (33, 48, 64, 128):
             assert swq.swiglu_q_path_for(M, 4096, 14336) == swq.SWQ_PATH_MFMA, M
-            assert swq.swiglu_q_path_for(M, 2048, 8192) == swq.SWQ_PATH_MFMA, M
+            assert swq.swiglu_q_path_for(M, 2048, 12288) == swq.SWQ_PATH_MFMA, M   # 3 * 2^23
+            assert swq.swiglu_q_path_for(M, 6144, 4096) == swq.SWQ_PATH_MFMA, M
         swq.swiglu_q_set_m_threshold(65)
         assert swq.swiglu_q_path_for(64, 4096, 14336) == swq.SWQ_PATH_GEMV
     finally:
