@@ -207,8 +207,8 @@ int choose_column_split(int64_t M, int64_t I, int cfg, int bits_g, int bits_u) {
 
 // K split of the MFMA path: with few 128 x 128 tiles (at most half the CUs)
 // and H >= 2048, each tile's code K-steps are split across blocks in whole
-// super-steps (at least four per split), up to 8 ways (more than two only
-// while their float32 partial sums stay below 32 MB); a second kernel adds the splits in order and runs
+// super-steps (at least four per split), up to 8 ways, 16 from H = 8192 on
+// (more than two only while their float32 partial sums stay below 32 MB); a second kernel adds the splits in order and runs
 // the epilogue.  Shorter splits, or more partial sums, measured slower (at
 // H = 1024 the split loses from M = 128 on).  Forward
 // precision modes only.  SWIGLU_Q_MFMA_KSPLIT=n caps the splits at n (0 or 1:
@@ -219,11 +219,12 @@ struct KSplit {
 };
 KSplit choose_ksplit(int64_t M, int64_t H, int64_t I, int cfg, int n_split) {
   KSplit k;
-  int64_t cap = 8;
+  const int64_t steps = H / 32;
+  int64_t cap = steps >= 256 ? 16 : 8;
   if (const char* s = getenv("SWIGLU_Q_MFMA_KSPLIT"); s && *s) cap = std::min<int64_t>(cap, atol(s));
   if (cap < 2 || cfg != 1 || n_split != 0 || M <= 0 || I <= 0) return k;
   const int64_t cus = device_cus();
-  const int64_t tiles = ((M + 127) / 128) * ((I + 127) / 128), steps = H / 32;
+  const int64_t tiles = ((M + 127) / 128) * ((I + 127) / 128);
   if (2 * tiles > cus || steps < 64) return k;
   int64_t n = std::min<int64_t>(std::min<int64_t>(cus / tiles, steps / 16), cap);
   while (n > 2 && n * 2 * M * I * 4 >= (int64_t(32) << 20)) --n;

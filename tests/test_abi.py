@@ -283,7 +283,8 @@ def test_workspace_bytes():
 def test_workspace_bytes_k_split(monkeypatch):
     # few 128 x 128 tiles (at most half of 256 CUs) and H >= 2048: the K
     # split's float32 partial sums (gate and up, [splits, M, I]) follow,
-    # min(256 / tiles, K-steps / 16, 8) splits, more than two only below 32 MB
+    # min(256 / tiles, K-steps / 16, 8 or from 256 K-steps 16) splits, more
+    # than two only below 32 MB
     def a256(v):
         return (v + 255) // 256 * 256
 
@@ -298,8 +299,9 @@ def test_workspace_bytes_k_split(monkeypatch):
     assert ws(65, 2048, 5632) == base(65, 2048, 5632) + a256(2 * 4 * 65 * 5632 * 4)
     # 64 tiles, 128 K-steps: four splits (32 MiB of partial sums) lower to three
     assert ws(128, 4096, 8192) == base(128, 4096, 8192) + a256(2 * 3 * 128 * 8192 * 4)
-    # 3 tiles at H = 4096: eight splits
+    # 3 tiles at H = 4096: eight splits; 16 tiles at H = 14336 (448 K-steps): sixteen
     assert ws(96, 4096, 384) == base(96, 4096, 384) + a256(2 * 8 * 96 * 384 * 4)
+    assert ws(48, 14336, 2048) == base(48, 14336, 2048) + a256(2 * 16 * 48 * 2048 * 4)
     # H = 1024 (32 K-steps) and 2 x 112 tiles: none
     assert ws(65, 1024, 4096) == base(65, 1024, 4096)
     assert ws(256, 4096, 14336) == base(256, 4096, 14336)
