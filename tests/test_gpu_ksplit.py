@@ -59,6 +59,7 @@ CASES = [
     (300, 3072, 130, 4, 32, 8, 64),     # three row tiles, I just past one column tile
     (70, 2592, 200, 4, 32, 4, 32),      # 81 K-steps: splits of 20, the last of one step
     (70, 8192, 256, 4, 64, 8, 32),      # 256 K-steps: sixteen splits of 16
+    (66, 2048, 1, 4, 64, 4, 64),        # one output column
 ]
 
 

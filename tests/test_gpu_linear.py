@@ -63,7 +63,7 @@ CASES = [(300, 256, 200, 4, 64, MFMA), (129, 512, 77, 8, 32, MFMA), (64, 1024, 1
          (40, 2048, 301, 4, 64, GEMV), (100, 1024, 77, 8, 32, GEMV),
          # few MFMA tiles with H >= 2048: K split over blocks (odd N: element stores; 4 | Ig: vector stores)
          (100, 2048, 301, 4, 64, MFMA), (96, 4096, 512, 8, 32, MFMA), (80, 2560, 3, 2, 64, MFMA),
-         (70, 8192, 300, 4, 64, MFMA)]
+         (70, 8192, 300, 4, 64, MFMA), (70, 2048, 1, 4, 64, MFMA)]
 
 
 @pytest.mark.parametrize("M,K,N,bits,gs,path", CASES,
