@@ -1040,8 +1040,12 @@ static hipError_t launch_mfma_t(const MfmaParams& p, hipStream_t stream, int ksp
 
 template <int BG, int BU, bool A16>
 static hipError_t launch_mfma_cfg(const MfmaParams& p, int cfg, int n_split, int ksplit, hipStream_t stream) {
-  // K split: 128-row tiles, the splits along grid y (the host's choice: few tiles)
-  if (ksplit > 1) return launch_mfma_t<BG, BU, 128, 32, 1, A16, true>(p, stream, ksplit);
+  // K split: 128-row tiles (64-row ones for at most 64 rows), the splits
+  // along grid y (the host's choice: few tiles)
+  if (ksplit > 1) {
+    if (p.M <= 64) return launch_mfma_t<BG, BU, 64, 32, 1, A16, true>(p, stream, ksplit);
+    return launch_mfma_t<BG, BU, 128, 32, 1, A16, true>(p, stream, ksplit);
+  }
   // 8-bit codes in both matrices need the larger code ring: 128-row tiles only
   if (cfg == 1 || (BG == 8 && BU == 8)) return launch_mfma_t<BG, BU, 128, 32, 1, A16>(p, stream);
   if constexpr (!(BG == 8 && BU == 8)) {

@@ -60,6 +60,11 @@ CASES = [
     (70, 2592, 200, 4, 32, 4, 32),      # 81 K-steps: splits of 20, the last of one step
     (70, 8192, 256, 4, 64, 8, 32),      # 256 K-steps: sixteen splits of 16
     (66, 2048, 1, 4, 64, 4, 64),        # one output column
+    # at most 64 rows: 64-row tiles
+    (64, 2048, 300, 4, 64, 4, 64),
+    (33, 4096, 520, 8, 32, 4, 128),
+    (40, 2560, 256, 2, 64, 8, 32),
+    (1, 8192, 130, 4, 64, 4, 64),
 ]
 
 
