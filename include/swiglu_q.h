@@ -246,7 +246,7 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
  * (Measured: the matrix-vector path is faster for every M <= 32 on every
  * weight shape measured.  For 33 <= M <= 64 it is 17-67 % faster up to
  * H * I = 2^24, e.g. H = 2048, I = 5632, and on fewer columns.  It is
- * 18-57 % slower on wide weights, e.g. H = 4096, I = 14336, where the MFMA
+ * 24-66 % slower on wide weights, e.g. H = 4096, I = 14336, where the MFMA
  * path splits K.)
  * swiglu_q_set_m_threshold with T < 0 restores the default rule; T <= 1
  * sends every M >= 1 to the MFMA path.  swiglu_q_get_m_threshold returns the

@@ -15,7 +15,7 @@
 // every weight shape measured (2-3x on the decode and prefill weight shapes
 // for M <= 16).  With two row groups of 32 (33 <= M <= 64) they are faster
 // on weights up to 2^24 elements (17-67 %) and on fewer than 4096 columns.
-// On wide weights they are 18-57 % slower than the matrix-matrix kernel with
+// On wide weights they are 24-66 % slower than the matrix-matrix kernel with
 // its K split.  The few-row kernel takes at most 128 rows (four
 // groups).  A threshold set by API or environment applies to every shape.
 #include <stdio.h>
