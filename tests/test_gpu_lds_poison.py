@@ -5,8 +5,8 @@ per kernel and branch: the M = 1 kernel and its several-row form, the
 few-row kernel (x' converted by each wave, built in the block, from the
 prep kernel, two row tiles, two column tiles, rows longer than one pass), the prep and MFMA kernels (both tile shapes, the
 column split, a partial last super-step, the K split: M = 300, H = 2080
-takes four splits of 20, 20, 20 and 5 K-steps), the linear and the whole
-MLP."""
+takes four splits of 20, 20, 20 and 5 K-steps, M = 48 four splits in
+64-row tiles), the linear and the whole MLP."""
 import os
 
 import numpy as np
@@ -43,6 +43,7 @@ CASES = [
     (9, 2048, 300, (4, 64, 4, 64), GEMV_PATH), (20, 1024, 130, (4, 64, 4, 64), GEMV_PATH),
     (12, 8192, 64, (4, 64, 8, 32), GEMV_PATH), (6, 256, 768, (4, 64, 4, 64), MFMA_PATH),
     (300, 2080, 257, (8, 32, 4, 32), MFMA_PATH), (700, 1024, 600, (4, 64, 4, 64), MFMA_PATH),
+    (48, 2048, 300, (4, 64, 2, 64), MFMA_PATH),   # K split in 64-row tiles
 ]
 
 
