@@ -242,7 +242,8 @@ int swiglu_q_supported(int64_t H, int bits_g, int gs_g, int bits_u, int gs_u,
  * else the environment variable SWIGLU_Q_MMIN when set to a positive integer,
  * and applies to every weight shape.  Without either, the default rule
  * applies: T = 65, or T = 33 for wide weights (H * I >= 3 * 2^23 with
- * I >= 4096; the linear's I is ceil(N / 2)).
+ * I >= 4096), or T = 129 for small weights (H * I <= 2^23; the matrix-vector
+ * path up to its 128 rows); the linear's I is ceil(N / 2).
  * (Measured: the matrix-vector path is faster for every M <= 32 on every
  * weight shape measured.  For 33 <= M <= 64 it is 17-67 % faster up to
  * H * I = 2^24, e.g. H = 2048, I = 5632, and on fewer columns.  It is

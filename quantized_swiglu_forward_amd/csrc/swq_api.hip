@@ -10,7 +10,8 @@
 // from the environment) and the support predicate of the same file (bf16
 // activations, affine biases, 2-, 4- or 8-bit codes, group size a multiple
 // of 32, H a multiple of 32).  Here the default is 65, or 33 for wide
-// weights (H * I >= 3 * 2^23 with I >= 4096).  Measured on this GPU, the
+// weights (H * I >= 3 * 2^23 with I >= 4096), or 129 for small ones
+// (H * I <= 2^23).  Measured on this GPU, the
 // matrix-vector kernels beat the matrix-matrix kernel for every M <= 32 on
 // every weight shape measured (2-3x on the decode and prefill weight shapes
 // for M <= 16).  With two row groups of 32 (33 <= M <= 64) they are faster
@@ -58,8 +59,12 @@ namespace {
 // where the MFMA path with its K split is faster from 33 rows on.  With
 // fewer columns its split blocks do not fill the chip (a linear of 2048
 // columns per slot and K = 14336: 57.5 against 41.5 us at M = 48).
+// Small weights (H * I <= 2^23) keep the matrix-vector path up to its 128
+// rows (H = 1024, I = 4096: 15.6 against 25.6 us at M = 128).
 constexpr int kDefaultThreshold = 2 * kGemvMaxM + 1;
 constexpr int kDefaultThresholdWide = kGemvMaxM + 1;
+constexpr int kDefaultThresholdSmall = kGemvGroupsMaxM + 1;
+constexpr int64_t kSmallWeights = int64_t(1) << 23;
 constexpr int64_t kWideWeights = int64_t(3) << 23;
 constexpr int64_t kWideColumns = 4096;
 
@@ -114,6 +119,7 @@ int explicit_threshold() {
 int threshold_for(int64_t H, int64_t I) {
   const int t = explicit_threshold();
   if (t >= 0) return t;
+  if (H * I <= kSmallWeights) return kDefaultThresholdSmall;
   return (H * I >= kWideWeights && I >= kWideColumns) ? kDefaultThresholdWide : kDefaultThreshold;
 }
 

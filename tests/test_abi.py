@@ -210,8 +210,15 @@ def test_default_rule_by_weight_size():
             assert swq.swiglu_q_path_for(M, 4096, 14336) == swq.SWQ_PATH_MFMA, M
             assert swq.swiglu_q_path_for(M, 2048, 12288) == swq.SWQ_PATH_MFMA, M   # 3 * 2^23
             assert swq.swiglu_q_path_for(M, 6144, 4096) == swq.SWQ_PATH_MFMA, M
+        # small weights (H * I <= 2^23): the matrix-vector path up to 128 rows
+        for M in (65, 100, 128):
+            assert swq.swiglu_q_path_for(M, 1024, 4096) == swq.SWQ_PATH_GEMV, M
+            assert swq.swiglu_q_path_for(M, 2048, 4096) == swq.SWQ_PATH_GEMV, M   # exactly 2^23
+            assert swq.swiglu_q_path_for(M, 2048, 4097) == swq.SWQ_PATH_MFMA, M
+        assert swq.swiglu_q_path_for(129, 1024, 4096) == swq.SWQ_PATH_MFMA
         swq.swiglu_q_set_m_threshold(65)
         assert swq.swiglu_q_path_for(64, 4096, 14336) == swq.SWQ_PATH_GEMV
+        assert swq.swiglu_q_path_for(65, 1024, 4096) == swq.SWQ_PATH_MFMA
     finally:
         swq.swiglu_q_set_m_threshold(-1)
 
